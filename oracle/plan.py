@@ -1,0 +1,96 @@
+"""The CSA2 layer plan (Full / Reindex / Reuse) for one sequence, and the Full-layer prefill.
+
+[zaikei] "■CSA2とFP4でキャッシュを圧縮": each CSA2 layer is fixed to one of Full,
+Reindex, Reuse. Full computes KV data and reference positions afresh; Reindex
+reuses the preceding layers' KV data and re-selects positions; Reuse inherits
+both KV data and positions. [jiwasawa] CSA2: modes are assigned statically;
+Full computes the main KV and its own indexer Q and fresh Top-K indices;
+Reindex shares main KV and indexer K from an earlier layer and re-scores with
+its own Q; Reuse shares main KV and the Top-K indices and skips the indexer.
+Hierarchical Sparse Indexer: the first Full layer picks a candidate pool from
+the whole context and later Reindex layers search only inside it.
+
+Readings:
+  * the pool is the top-P of the first Full layer's scores under the same
+    order as top-K (so it contains that layer's top-K);
+  * a Reindex layer scores the pool positions with its own indexer query and
+    the first Full layer's indexer keys, and selects top-K from the pool;
+  * a Reuse layer takes the positions of the immediately preceding layer;
+  * all layers read the one shared main KV cache (one KV head);
+  * plan validity: the first layer is Full; a Reindex needs an earlier Full
+    (and a pool, so P >= K); a Reuse needs a predecessor.
+"""
+
+import numpy as np
+
+from .attention import sparse_attn
+from .scores import index_scores, pool_scores
+from .topk import topk
+
+FULL, REINDEX, REUSE = "full", "reindex", "reuse"
+
+
+def validate_plan(modes, K, P=None):
+    modes = list(modes)
+    if not modes or modes[0] != FULL:
+        raise ValueError("first layer must be Full")
+    for m in modes:
+        if m not in (FULL, REINDEX, REUSE):
+            raise ValueError(f"unknown mode {m}")
+    if REINDEX in modes:
+        if P is None or P < K:
+            raise ValueError("a Reindex layer needs a pool with P >= K")
+    return modes
+
+
+def run_decode(modes, cache, layers, K, P=None, softmax_scale=None):
+    """One decode step of the stack for ONE sequence.
+
+    cache: dict with 'k_codes', 'k_scales', 'v_codes', 'v_scales' (main KV,
+    [N][d/2] and [N][d/16]), 'k_idx' ([N][d_idx] stored), 'k_idx_dtype'.
+    layers: list (one per layer) of dicts with 'q' ((H, d) bf16 bits) and, for
+    Full and Reindex layers, 'q_idx' ((d_idx,) stored) and 'q_idx_dtype'.
+    Returns a list of dicts per layer: 'idx' (K,), 'out' (H, d) fp64 and, for
+    the first Full layer when the plan has a Reindex, 'pool' (P,).
+    """
+    modes = validate_plan(modes, K, P)
+    need_pool = REINDEX in modes
+    pool = None
+    prev_idx = None
+    results = []
+    for mode, layer in zip(modes, layers):
+        res = {}
+        if mode == FULL:
+            s = index_scores(layer["q_idx"], layer["q_idx_dtype"], cache["k_idx"], cache["k_idx_dtype"])
+            if need_pool and pool is None:
+                pool, _ = topk(s, P)
+                res["pool"] = pool
+            idx, _ = topk(s, K)
+        elif mode == REINDEX:
+            s = pool_scores(layer["q_idx"], layer["q_idx_dtype"], cache["k_idx"], cache["k_idx_dtype"], pool)
+            idx, _ = topk(s, K, positions=pool)
+        else:
+            idx = prev_idx.copy()
+        res["idx"] = idx
+        res["out"] = sparse_attn(layer["q"], cache, idx, softmax_scale)
+        results.append(res)
+        prev_idx = idx
+    return results
+
+
+def prefill_full(q_idx, q_idx_dtype, q_pos, q, cache, K, softmax_scale=None, queries=None):
+    """Full-layer prefill for a chunk of queries of ONE sequence.
+
+    q_idx: (Q, d_idx) stored; q_pos: (Q,) positions; q: (Q, H, d) bf16 bits.
+    Reading (causal): query i may select only positions <= q_pos[i].
+    `queries` restricts the work to a subset of query rows (sampling).
+    Returns (idx (Q', K), out (Q', H, d)).
+    """
+    rows = range(len(q_pos)) if queries is None else list(queries)
+    idx_all, out_all = [], []
+    for i in rows:
+        s = index_scores(q_idx[i], q_idx_dtype, cache["k_idx"], cache["k_idx_dtype"], q_pos=int(q_pos[i]))
+        idx, _ = topk(s, K)
+        idx_all.append(idx)
+        out_all.append(sparse_attn(q[i], cache, idx, softmax_scale))
+    return np.stack(idx_all), np.stack(out_all)
