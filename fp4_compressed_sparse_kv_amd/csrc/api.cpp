@@ -1,0 +1,489 @@
+// C ABI of libcsa2: argument validation, the layer plan and kernel dispatch.
+// Every check here runs on the host before any HIP call, so invalid calls are
+// rejected on a machine without a GPU.
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "csa2.h"
+#include "internal.hpp"
+
+namespace csa2 {
+
+static thread_local std::string g_err;
+
+int fail(int code, const std::string& msg) {
+    g_err = msg;
+    return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+    g_err = std::string(what) + ": " + hipGetErrorString(e);
+    return HIP;
+}
+
+int device_info(DeviceInfo* out) {
+    static std::mutex mu;
+    static std::vector<DeviceInfo> cache;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    std::lock_guard<std::mutex> lock(mu);
+    for (const auto& d : cache)
+        if (d.device == dev) {
+            *out = d;
+            return OK;
+        }
+    DeviceInfo d;
+    d.device = dev;
+    e = hipDeviceGetAttribute(&d.num_cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute(CUs)");
+    int lds = 0, lds_optin = 0;
+    e = hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
+    if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute(LDS)");
+    if (hipDeviceGetAttribute(&lds_optin, hipDeviceAttributeSharedMemPerBlockOptin, dev) != hipSuccess) lds_optin = 0;
+    (void)hipGetLastError();
+    d.max_lds = (size_t)(lds_optin > lds ? lds_optin : lds);
+    cache.push_back(d);
+    *out = d;
+    return OK;
+}
+
+}  // namespace csa2
+
+using namespace csa2;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool q_dtype_ok(int32_t t) { return t == CSA2_F32 || t == CSA2_BF16; }
+bool k_dtype_ok(int32_t t) { return t == CSA2_F32 || t == CSA2_BF16 || t == CSA2_E4M3; }
+int k_elem_bytes(int32_t t) { return t == CSA2_F32 ? 4 : (t == CSA2_BF16 ? 2 : 1); }
+
+int check_ws(void* ws, size_t have, size_t need, const char* who) {
+    if (need == 0) return OK;
+    if (!ws) return fail(WORKSPACE, std::string(who) + ": workspace is null");
+    if (!aligned(ws, kAlign)) return fail(WORKSPACE, std::string(who) + ": workspace must be 256-byte aligned");
+    if (have < need)
+        return fail(WORKSPACE, std::string(who) + ": workspace of " + std::to_string(have) + " bytes, need " +
+                                   std::to_string(need));
+    return OK;
+}
+
+int check_quant_layout(int64_t rows, int32_t C, int64_t x_stride, int64_t cs, int64_t ss, const void* x,
+                       const void* codes, const void* scales, const char* who) {
+    const std::string w(who);
+    if (rows < 0) return fail(INVALID, w + ": rows < 0");
+    if (C <= 0 || C % 16 != 0) return fail(INVALID, w + ": C must be a positive multiple of 16");
+    if (x_stride < C) return fail(INVALID, w + ": bf16 row stride < C");
+    if (cs < C / 2) return fail(INVALID, w + ": code row stride < C/2 bytes");
+    if (ss < C / 16) return fail(INVALID, w + ": scale row stride < C/16 bytes");
+    if (rows == 0) return OK;
+    if (!x || !codes || !scales) return fail(INVALID, w + ": null pointer");
+    if (!aligned(x, 16) || (x_stride * 2) % 16 != 0) return fail(INVALID, w + ": bf16 rows must be 16-byte aligned");
+    if (!aligned(codes, 8) || cs % 8 != 0) return fail(INVALID, w + ": code rows must be 8-byte aligned");
+    return OK;
+}
+
+int check_scan(const void* q_idx, int32_t q_dtype, const void* k_idx, int32_t k_dtype, int32_t d_idx, const char* who) {
+    const std::string w(who);
+    if (!q_dtype_ok(q_dtype)) return fail(DTYPE, w + ": indexer query dtype must be CSA2_F32 or CSA2_BF16");
+    if (!k_dtype_ok(k_dtype)) return fail(DTYPE, w + ": indexer key dtype must be CSA2_F32, CSA2_BF16 or CSA2_E4M3");
+    if (d_idx != 64 && d_idx != 128) return fail(INVALID, w + ": d_idx must be 64 or 128");
+    if (!q_idx || !k_idx) return fail(INVALID, w + ": null indexer pointer");
+    if (!aligned(k_idx, 16)) return fail(INVALID, w + ": indexer keys must be 16-byte aligned");
+    if (!aligned(q_idx, q_dtype == CSA2_F32 ? 4 : 2)) return fail(INVALID, w + ": indexer query misaligned");
+    return OK;
+}
+
+int check_attn(const uint16_t* q, int32_t H, int32_t d, const uint8_t* kc, const uint8_t* ks, const uint8_t* vc,
+               const uint8_t* vs, int64_t N, int64_t cs, int64_t ss, int32_t K, const char* who) {
+    const std::string w(who);
+    if (H < 1 || H > 16) return fail(INVALID, w + ": H must be in 1..16");
+    if (d != 128) return fail(INVALID, w + ": head dim d must be 128");
+    if (K < 1) return fail(INVALID, w + ": K must be >= 1");
+    if (N < 1) return fail(INVALID, w + ": N must be >= 1");
+    if (cs < d / 2 || ss < d / 16) return fail(INVALID, w + ": KV code/scale stride smaller than one row");
+    if (!q || !kc || !ks || !vc || !vs) return fail(INVALID, w + ": null pointer");
+    if (!aligned(kc, 8) || !aligned(vc, 8) || cs % 8 != 0) return fail(INVALID, w + ": KV codes must be 8-byte aligned");
+    if (!aligned(q, 2)) return fail(INVALID, w + ": query misaligned");
+    return OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* csa2_last_error(void) { return g_err.c_str(); }
+
+int csa2_version(void) { return 100; }
+
+int kv_quant_fp4(const uint16_t* x, int64_t rows, int32_t C, int64_t x_stride, uint8_t* codes,
+                 int64_t code_stride_bytes, uint8_t* scales, int64_t scale_stride_bytes, hipStream_t stream) {
+    g_err.clear();
+    if (int e = check_quant_layout(rows, C, x_stride, code_stride_bytes, scale_stride_bytes, x, codes, scales,
+                                   "kv_quant_fp4"))
+        return e;
+    return launch_quant(x, rows, C, x_stride, codes, code_stride_bytes, scales, scale_stride_bytes, stream);
+}
+
+int kv_dequant_fp4(const uint8_t* codes, int64_t code_stride_bytes, const uint8_t* scales, int64_t scale_stride_bytes,
+                   int64_t rows, int32_t C, uint16_t* y, int64_t y_stride, hipStream_t stream) {
+    g_err.clear();
+    if (int e = check_quant_layout(rows, C, y_stride, code_stride_bytes, scale_stride_bytes, y, codes, scales,
+                                   "kv_dequant_fp4"))
+        return e;
+    return launch_dequant(codes, code_stride_bytes, scales, scale_stride_bytes, rows, C, y, y_stride, stream);
+}
+
+int csa2_index_full(const void* q_idx, int32_t q_dtype, const void* k_idx, int32_t k_dtype, int32_t B, int32_t Q,
+                    int64_t N, int32_t d_idx, const int64_t* q_pos, float* scores, hipStream_t stream) {
+    g_err.clear();
+    if (B < 0 || Q < 0 || N < 0) return fail(INVALID, "csa2_index_full: negative size");
+    if ((int64_t)B * Q > 65535) return fail(INVALID, "csa2_index_full: B*Q must be <= 65535");
+    if ((int64_t)B * Q == 0 || N == 0) return OK;
+    if (int e = check_scan(q_idx, q_dtype, k_idx, k_dtype, d_idx, "csa2_index_full")) return e;
+    if (!scores) return fail(INVALID, "csa2_index_full: scores is null");
+    ScanArgs a;
+    a.q = q_idx;
+    a.k = reinterpret_cast<const uint8_t*>(k_idx);
+    a.N = N;
+    a.q_pos = q_pos;
+    a.q_dtype = q_dtype;
+    a.k_dtype = k_dtype;
+    a.d_idx = d_idx;
+    return launch_index_dense(a, B, Q, scores, stream);
+}
+
+int csa2_index_reindex(const void* q_idx, int32_t q_dtype, const void* k_idx, int32_t k_dtype, int32_t B, int64_t N,
+                       int32_t d_idx, const int32_t* pool, int32_t P, float* scores, hipStream_t stream) {
+    g_err.clear();
+    if (B < 0 || N < 0 || P < 0) return fail(INVALID, "csa2_index_reindex: negative size");
+    if (B > 65535) return fail(INVALID, "csa2_index_reindex: B must be <= 65535");
+    if (B == 0 || P == 0) return OK;
+    if (int e = check_scan(q_idx, q_dtype, k_idx, k_dtype, d_idx, "csa2_index_reindex")) return e;
+    if (!pool || !scores) return fail(INVALID, "csa2_index_reindex: null pointer");
+    ScanArgs a;
+    a.q = q_idx;
+    a.k = reinterpret_cast<const uint8_t*>(k_idx);
+    a.N = N;
+    a.pool = pool;
+    a.q_dtype = q_dtype;
+    a.k_dtype = k_dtype;
+    a.d_idx = d_idx;
+    return launch_index_pool(a, B, P, scores, stream);
+}
+
+int csa2_topk_workspace_bytes(int64_t rows, int64_t n, int32_t K, size_t* bytes) {
+    g_err.clear();
+    if (!bytes) return fail(INVALID, "csa2_topk_workspace_bytes: bytes is null");
+    if (rows < 0 || n < 1 || n >= (int64_t(1) << 31) || K < 1)
+        return fail(INVALID, "csa2_topk_workspace_bytes: need rows >= 0, 1 <= n < 2^31, K >= 1");
+    SelPlan p;
+    if (int e = plan_select(rows, n, 1024, &p)) return e;
+    *bytes = align_up(p.ws_bytes);
+    return OK;
+}
+
+int csa2_topk(const float* scores, int64_t rows, int64_t n, int64_t score_stride, const int32_t* cand, int32_t K,
+              int32_t* idx, float* sel_scores, void* ws, size_t ws_bytes, hipStream_t stream) {
+    g_err.clear();
+    if (rows < 0 || n < 1 || n >= (int64_t(1) << 31) || K < 1)
+        return fail(INVALID, "csa2_topk: need rows >= 0, 1 <= n < 2^31, K >= 1");
+    if (score_stride < n) return fail(INVALID, "csa2_topk: score_stride < n");
+    if (rows == 0) return OK;
+    if (!scores || !idx) return fail(INVALID, "csa2_topk: null pointer");
+    SelPlan p;
+    if (int e = plan_select(rows, n, 1024, &p)) return e;
+    if (int e = check_ws(ws, ws_bytes, p.ws_bytes, "csa2_topk")) return e;
+    ScanArgs scan;
+    ScoresArgs sc;
+    sc.scores = scores;
+    sc.stride = score_stride;
+    sc.cand = cand;
+    SelOutput o;
+    o.idx = idx;
+    o.score = sel_scores;
+    o.stride = K;
+    o.M = K;
+    return run_select(p, SRC_SCORES, scan, sc, &o, 1, ws, stream);
+}
+
+int csa2_sparse_attn_workspace_bytes(int32_t B, int32_t Q, int32_t H, int32_t d, int32_t K, size_t* bytes) {
+    g_err.clear();
+    if (!bytes) return fail(INVALID, "csa2_sparse_attn_workspace_bytes: bytes is null");
+    if (B < 0 || Q < 0 || H < 1 || H > 16 || d != 128 || K < 1)
+        return fail(INVALID, "csa2_sparse_attn_workspace_bytes: bad sizes");
+    *bytes = align_up(attn_workspace_bytes((int64_t)B * Q, H, d, K));
+    return OK;
+}
+
+int csa2_sparse_attn_fp4(const uint16_t* q, int32_t B, int32_t Q, int32_t H, int32_t d, const uint8_t* k_codes,
+                         const uint8_t* k_scales, const uint8_t* v_codes, const uint8_t* v_scales, int64_t N,
+                         int64_t code_stride_bytes, int64_t scale_stride_bytes, const int32_t* idx, int32_t K,
+                         float softmax_scale, float* out, void* ws, size_t ws_bytes, hipStream_t stream) {
+    g_err.clear();
+    if (B < 0 || Q < 0) return fail(INVALID, "csa2_sparse_attn_fp4: negative size");
+    if ((int64_t)B * Q == 0) return OK;
+    if (int e = check_attn(q, H, d, k_codes, k_scales, v_codes, v_scales, N, code_stride_bytes, scale_stride_bytes, K,
+                           "csa2_sparse_attn_fp4"))
+        return e;
+    if (!idx || !out) return fail(INVALID, "csa2_sparse_attn_fp4: null pointer");
+    if (!(softmax_scale > 0.f) || !isfinite(softmax_scale))
+        return fail(INVALID, "csa2_sparse_attn_fp4: softmax_scale must be positive and finite");
+    const size_t need = attn_workspace_bytes((int64_t)B * Q, H, d, K);
+    if (int e = check_ws(ws, ws_bytes, need, "csa2_sparse_attn_fp4")) return e;
+    AttnArgs a;
+    a.q = q;
+    a.rows = (int64_t)B * Q;
+    a.rows_per_seq = Q;
+    a.H = H;
+    a.d = d;
+    a.k_codes = k_codes;
+    a.k_scales = k_scales;
+    a.v_codes = v_codes;
+    a.v_scales = v_scales;
+    a.N = N;
+    a.code_stride = code_stride_bytes;
+    a.scale_stride = scale_stride_bytes;
+    a.idx = idx;
+    a.idx_stride = K;
+    a.K = K;
+    a.scale = softmax_scale;
+    a.out = out;
+    return launch_attn(a, ws, ws_bytes, stream);
+}
+
+// ------------------------------------------------------------------- plan
+
+struct csa2_plan {
+    std::vector<int32_t> modes;
+    csa2_plan_params p;
+    bool has_reindex = false;
+};
+
+int csa2_plan_create(const int32_t* modes, int32_t L, const csa2_plan_params* params, csa2_plan** out) {
+    g_err.clear();
+    if (!out) return fail(INVALID, "csa2_plan_create: out is null");
+    *out = nullptr;
+    if (!modes || !params || L < 1) return fail(INVALID, "csa2_plan_create: need modes, params and L >= 1");
+    const csa2_plan_params& p = *params;
+    for (int32_t l = 0; l < L; ++l)
+        if (modes[l] != CSA2_FULL && modes[l] != CSA2_REINDEX && modes[l] != CSA2_REUSE)
+            return fail(BAD_PLAN, "csa2_plan_create: unknown mode at layer " + std::to_string(l));
+    if (modes[0] != CSA2_FULL) return fail(BAD_PLAN, "csa2_plan_create: the first layer must be Full");
+    bool has_reindex = false;
+    for (int32_t l = 0; l < L; ++l) has_reindex |= modes[l] == CSA2_REINDEX;
+    if (p.K < 1) return fail(INVALID, "csa2_plan_create: K must be >= 1");
+    if (has_reindex && p.P < p.K) return fail(BAD_PLAN, "csa2_plan_create: a Reindex layer needs P >= K");
+    if (p.H < 1 || p.H > 16) return fail(INVALID, "csa2_plan_create: H must be in 1..16");
+    if (p.d != 128) return fail(INVALID, "csa2_plan_create: d must be 128");
+    if (p.d_idx != 64 && p.d_idx != 128) return fail(INVALID, "csa2_plan_create: d_idx must be 64 or 128");
+    if (!q_dtype_ok(p.q_idx_dtype)) return fail(DTYPE, "csa2_plan_create: indexer query dtype");
+    if (!k_dtype_ok(p.k_idx_dtype)) return fail(DTYPE, "csa2_plan_create: indexer key dtype");
+    if (!(p.softmax_scale >= 0.f) || !isfinite(p.softmax_scale))
+        return fail(INVALID, "csa2_plan_create: softmax_scale must be >= 0 and finite");
+    csa2_plan* plan = new csa2_plan;
+    plan->modes.assign(modes, modes + L);
+    plan->p = p;
+    if (plan->p.softmax_scale == 0.f) plan->p.softmax_scale = 1.0f / sqrtf((float)p.d);
+    plan->has_reindex = has_reindex;
+    *out = plan;
+    return OK;
+}
+
+void csa2_plan_destroy(csa2_plan* plan) { delete plan; }
+
+namespace {
+
+struct PlanLayout {
+    SelPlan full, pool;
+    size_t off_full = 0, off_pool = 0, off_attn = 0, off_idx = 0, off_poolbuf = 0, total = 0;
+};
+
+int plan_layout(const csa2_plan* plan, int32_t B, int64_t N, PlanLayout* lay) {
+    if (int e = plan_select(B, N, 1024, &lay->full)) return e;
+    size_t off = 0;
+    lay->off_full = off;
+    off += align_up(lay->full.ws_bytes);
+    if (plan->has_reindex) {
+        if (int e = plan_select(B, plan->p.P, 512, &lay->pool)) return e;
+        lay->off_pool = off;
+        off += align_up(lay->pool.ws_bytes);
+        lay->off_poolbuf = off;
+        off += align_up((size_t)B * plan->p.P * 4);
+    }
+    lay->off_attn = off;
+    off += align_up(attn_workspace_bytes(B, plan->p.H, plan->p.d, plan->p.K));
+    lay->off_idx = off;
+    off += align_up((size_t)B * plan->p.K * 4);
+    lay->total = off;
+    return OK;
+}
+
+}  // namespace
+
+int csa2_plan_workspace_bytes(const csa2_plan* plan, int32_t B, int64_t N, size_t* bytes) {
+    g_err.clear();
+    if (!plan || !bytes) return fail(INVALID, "csa2_plan_workspace_bytes: null pointer");
+    if (B < 1 || N < 1) return fail(INVALID, "csa2_plan_workspace_bytes: B and N must be >= 1");
+    PlanLayout lay;
+    if (int e = plan_layout(plan, B, N, &lay)) return e;
+    *bytes = lay.total;
+    return OK;
+}
+
+int csa2_plan_run_decode(const csa2_plan* plan, const csa2_cache* cache, const csa2_layer_io* io, int32_t B, int64_t N,
+                         void* ws, size_t ws_bytes, hipStream_t stream) {
+    g_err.clear();
+    if (!plan || !cache || !io) return fail(INVALID, "csa2_plan_run_decode: null pointer");
+    if (B < 1 || N < 1) return fail(INVALID, "csa2_plan_run_decode: B and N must be >= 1");
+    if (B > 65535) return fail(INVALID, "csa2_plan_run_decode: B must be <= 65535");
+    const csa2_plan_params& p = plan->p;
+    const int L = (int)plan->modes.size();
+    if (plan->has_reindex && p.P > N) return fail(INVALID, "csa2_plan_run_decode: pool size P exceeds N");
+    if (int e = check_attn(io[0].q, p.H, p.d, cache->k_codes, cache->k_scales, cache->v_codes, cache->v_scales, N,
+                           cache->code_stride_bytes, cache->scale_stride_bytes, p.K, "csa2_plan_run_decode"))
+        return e;
+    if (!cache->k_idx || !aligned(cache->k_idx, 16))
+        return fail(INVALID, "csa2_plan_run_decode: indexer keys null or not 16-byte aligned");
+    for (int l = 0; l < L; ++l) {
+        if (!io[l].q || !io[l].out) return fail(INVALID, "csa2_plan_run_decode: layer " + std::to_string(l) + " needs q and out");
+        if (plan->modes[l] != CSA2_REUSE && !io[l].q_idx)
+            return fail(INVALID, "csa2_plan_run_decode: layer " + std::to_string(l) + " needs q_idx");
+    }
+    PlanLayout lay;
+    if (int e = plan_layout(plan, B, N, &lay)) return e;
+    if (int e = check_ws(ws, ws_bytes, lay.total, "csa2_plan_run_decode")) return e;
+    uint8_t* wsb = reinterpret_cast<uint8_t*>(ws);
+
+    const int32_t* cur_idx = nullptr;
+    const int32_t* pool = nullptr;
+    for (int l = 0; l < L; ++l) {
+        const int32_t mode = plan->modes[l];
+        if (mode == CSA2_FULL || mode == CSA2_REINDEX) {
+            int32_t* idx_dst = io[l].idx_out ? io[l].idx_out : reinterpret_cast<int32_t*>(wsb + lay.off_idx);
+            ScanArgs a;
+            a.q = io[l].q_idx;
+            a.k = reinterpret_cast<const uint8_t*>(cache->k_idx);
+            a.N = N;
+            a.q_dtype = p.q_idx_dtype;
+            a.k_dtype = p.k_idx_dtype;
+            a.d_idx = p.d_idx;
+            ScoresArgs none;
+            SelOutput o[2];
+            int nt = 1;
+            int e;
+            if (mode == CSA2_FULL) {
+                if (plan->has_reindex && !pool) {
+                    int32_t* pool_dst = io[l].pool_out ? io[l].pool_out : reinterpret_cast<int32_t*>(wsb + lay.off_poolbuf);
+                    o[0] = SelOutput{pool_dst, nullptr, p.P, p.P};
+                    o[1] = SelOutput{idx_dst, nullptr, p.K, p.K};
+                    nt = 2;
+                    pool = pool_dst;
+                } else {
+                    o[0] = SelOutput{idx_dst, nullptr, p.K, p.K};
+                }
+                e = run_select(lay.full, SRC_SCAN, a, none, o, nt, wsb + lay.off_full, stream);
+            } else {
+                a.pool = pool;
+                o[0] = SelOutput{idx_dst, nullptr, p.K, p.K};
+                e = run_select(lay.pool, SRC_POOL, a, none, o, 1, wsb + lay.off_pool, stream);
+            }
+            if (e) return e;
+            cur_idx = idx_dst;
+        }
+        AttnArgs at;
+        at.q = io[l].q;
+        at.rows = B;
+        at.rows_per_seq = 1;
+        at.H = p.H;
+        at.d = p.d;
+        at.k_codes = cache->k_codes;
+        at.k_scales = cache->k_scales;
+        at.v_codes = cache->v_codes;
+        at.v_scales = cache->v_scales;
+        at.N = N;
+        at.code_stride = cache->code_stride_bytes;
+        at.scale_stride = cache->scale_stride_bytes;
+        at.idx = cur_idx;
+        at.idx_stride = p.K;
+        at.K = p.K;
+        at.scale = p.softmax_scale;
+        at.out = io[l].out;
+        if (int e = launch_attn(at, wsb + lay.off_attn, ws_bytes - lay.off_attn, stream)) return e;
+    }
+    return OK;
+}
+
+int csa2_prefill_workspace_bytes(const csa2_plan* plan, int32_t B, int32_t Q, int64_t N, size_t* bytes) {
+    g_err.clear();
+    if (!plan || !bytes) return fail(INVALID, "csa2_prefill_workspace_bytes: null pointer");
+    if (B < 1 || Q < 1 || N < 1) return fail(INVALID, "csa2_prefill_workspace_bytes: sizes must be >= 1");
+    SelPlan sp;
+    if (int e = plan_select((int64_t)B * Q, N, 1024, &sp)) return e;
+    *bytes = align_up(sp.ws_bytes) + align_up(attn_workspace_bytes((int64_t)B * Q, plan->p.H, plan->p.d, plan->p.K));
+    return OK;
+}
+
+int csa2_prefill_full(const csa2_plan* plan, const csa2_cache* cache, const void* q_idx, const uint16_t* q,
+                      const int64_t* q_pos, int32_t B, int32_t Q, int64_t N, int32_t* idx_out, float* out, void* ws,
+                      size_t ws_bytes, hipStream_t stream) {
+    g_err.clear();
+    if (!plan || !cache) return fail(INVALID, "csa2_prefill_full: null pointer");
+    if (B < 1 || Q < 1 || N < 1) return fail(INVALID, "csa2_prefill_full: sizes must be >= 1");
+    const csa2_plan_params& p = plan->p;
+    if (int e = check_attn(q, p.H, p.d, cache->k_codes, cache->k_scales, cache->v_codes, cache->v_scales, N,
+                           cache->code_stride_bytes, cache->scale_stride_bytes, p.K, "csa2_prefill_full"))
+        return e;
+    if (int e = check_scan(q_idx, p.q_idx_dtype, cache->k_idx, p.k_idx_dtype, p.d_idx, "csa2_prefill_full")) return e;
+    if (!q_pos || !idx_out || !out) return fail(INVALID, "csa2_prefill_full: null pointer");
+    const int64_t rows = (int64_t)B * Q;
+    SelPlan sp;
+    if (int e = plan_select(rows, N, 1024, &sp)) return e;
+    const size_t sel_bytes = align_up(sp.ws_bytes);
+    const size_t need = sel_bytes + align_up(attn_workspace_bytes(rows, p.H, p.d, p.K));
+    if (int e = check_ws(ws, ws_bytes, need, "csa2_prefill_full")) return e;
+    uint8_t* wsb = reinterpret_cast<uint8_t*>(ws);
+    ScanArgs a;
+    a.q = q_idx;
+    a.k = reinterpret_cast<const uint8_t*>(cache->k_idx);
+    a.N = N;
+    a.rows_per_seq = Q;
+    a.q_pos = q_pos;
+    a.q_dtype = p.q_idx_dtype;
+    a.k_dtype = p.k_idx_dtype;
+    a.d_idx = p.d_idx;
+    ScoresArgs none;
+    SelOutput o{idx_out, nullptr, p.K, p.K};
+    if (int e = run_select(sp, SRC_SCAN, a, none, &o, 1, wsb, stream)) return e;
+    AttnArgs at;
+    at.q = q;
+    at.rows = rows;
+    at.rows_per_seq = Q;
+    at.H = p.H;
+    at.d = p.d;
+    at.k_codes = cache->k_codes;
+    at.k_scales = cache->k_scales;
+    at.v_codes = cache->v_codes;
+    at.v_scales = cache->v_scales;
+    at.N = N;
+    at.code_stride = cache->code_stride_bytes;
+    at.scale_stride = cache->scale_stride_bytes;
+    at.idx = idx_out;
+    at.idx_stride = p.K;
+    at.K = p.K;
+    at.scale = p.softmax_scale;
+    at.out = out;
+    return launch_attn(at, wsb + sel_bytes, ws_bytes - sel_bytes, stream);
+}
+
+}  // extern "C"

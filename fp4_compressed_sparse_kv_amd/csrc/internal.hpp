@@ -1,0 +1,96 @@
+// Host-side interfaces between the C ABI (api.cpp) and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include <string>
+
+namespace csa2 {
+
+// Status codes mirror csa2.h.
+enum Status : int { OK = 0, INVALID = 1, DTYPE = 2, BAD_PLAN = 3, WORKSPACE = 4, HIP = 5, DEVICE = 6 };
+
+// Set the thread-local error message; returns `code` for convenience.
+int fail(int code, const std::string& msg);
+int hip_fail(hipError_t e, const char* what);
+
+// Device facts cached per device ordinal.
+struct DeviceInfo {
+    int device = -1;
+    int num_cus = 0;
+    size_t max_lds = 0;     // bytes of LDS one workgroup may allocate
+};
+int device_info(DeviceInfo* out);
+
+// ------------------------------------------------------------- selection
+// Geometry of one selection problem: `rows` rows of `n` entries split into S
+// chunks of `chunk` entries, one workgroup per chunk, all chunks of a row
+// co-resident; `rows_per_launch` rows per cooperative launch.
+struct SelPlan {
+    int64_t rows = 0, n = 0;
+    int32_t S = 1, chunk = 0, rows_per_launch = 0, launches = 0;
+    int32_t row_words = 0;          // exchange words per row in the workspace
+    size_t lds_bytes = 0;
+    size_t ws_bytes = 0;            // workspace bytes (header + rows_per_launch rows)
+};
+
+enum SelSource : int { SRC_SCORES = 0, SRC_SCAN = 1, SRC_POOL = 2 };
+
+// Plan a selection. `min_chunk` bounds how finely a row may be split.
+int plan_select(int64_t rows, int64_t n, int32_t min_chunk, SelPlan* out);
+
+struct SelOutput {
+    int32_t* idx = nullptr;         // [rows][stride] positions
+    float* score = nullptr;         // optional selected scores
+    int64_t stride = 0;
+    int32_t M = 0;
+};
+
+struct ScanArgs {                   // indexer keys scored inside the select kernel
+    const void* q = nullptr;        // [rows][d_idx] indexer queries (q_dtype)
+    const uint8_t* k = nullptr;     // [seqs][N][d_idx] keys (k_dtype)
+    int64_t N = 0;                  // positions per sequence
+    int32_t rows_per_seq = 1;       // row r reads sequence r / rows_per_seq
+    const int64_t* q_pos = nullptr; // causal limit per row, or null
+    const int32_t* pool = nullptr;  // SRC_POOL: [rows][n] positions to score
+    int32_t q_dtype = 0, k_dtype = 0, d_idx = 64;
+};
+
+struct ScoresArgs {                 // precomputed scores
+    const float* scores = nullptr;
+    int64_t stride = 0;
+    const int32_t* cand = nullptr;  // [rows][n] positions or null
+};
+
+// Run a planned selection for all rows (several launches if needed).
+// nt = number of targets (1 or 2, out[0].M >= out[1].M).
+int run_select(const SelPlan& p, int source, const ScanArgs& scan, const ScoresArgs& sc,
+               const SelOutput* out, int nt, void* ws, hipStream_t stream);
+
+// ---------------------------------------------------------- other kernels
+int launch_quant(const uint16_t* x, int64_t rows, int32_t C, int64_t x_stride, uint8_t* codes,
+                 int64_t cs, uint8_t* scales, int64_t ss, hipStream_t stream);
+int launch_dequant(const uint8_t* codes, int64_t cs, const uint8_t* scales, int64_t ss, int64_t rows,
+                   int32_t C, uint16_t* y, int64_t y_stride, hipStream_t stream);
+int launch_index_dense(const ScanArgs& a, int32_t B, int32_t Q, float* scores, hipStream_t stream);
+int launch_index_pool(const ScanArgs& a, int32_t B, int32_t P, float* scores, hipStream_t stream);
+
+struct AttnArgs {
+    const uint16_t* q = nullptr;    // [rows][H][d]
+    int64_t rows = 0;               // B*Q query rows
+    int32_t rows_per_seq = 1;       // row r reads sequence r / rows_per_seq
+    int32_t H = 0, d = 128;
+    const uint8_t *k_codes = nullptr, *k_scales = nullptr, *v_codes = nullptr, *v_scales = nullptr;
+    int64_t N = 0, code_stride = 0, scale_stride = 0;
+    const int32_t* idx = nullptr;   // [rows][idx_stride]
+    int64_t idx_stride = 0;
+    int32_t K = 0;
+    float scale = 0.f;
+    float* out = nullptr;           // [rows][H][d]
+};
+size_t attn_workspace_bytes(int64_t rows, int32_t H, int32_t d, int32_t K);
+int launch_attn(const AttnArgs& a, void* ws, size_t ws_bytes, hipStream_t stream);
+
+}  // namespace csa2

@@ -1,0 +1,273 @@
+/*
+ * csa2.h - C ABI of libcsa2: the decode-time CSA2 step (Compressed Sparse
+ * Attention 2) over an FP4 E2M1 main KV cache with one E4M3 scale per 16
+ * channels, for AMD Instinct MI355X (gfx950).
+ *
+ * Pages this interface follows (titles and sections):
+ *   [ezic]     "DeepSeek-V4.1-Flash: KVキャッシュ1トークン890バイト" (ai2.x.ezic.info),
+ *              "先に要点だけ" and "KVを捨てる、共有する、作り直す".
+ *   [zaikei]   "DeepSeek-V4.1-Flash、KVキャッシュを約4分の1に圧縮" (zaikei.co.jp),
+ *              "■CSA2とFP4でキャッシュを圧縮".
+ *   [jiwasawa] "DeepSeek-V4.1-Flash" report digest (jiwasawa.github.io),
+ *              "Compressed Sparse Attention 2 (CSA2) による極限のKV cache圧縮" and
+ *              "FP4 メイン KV Cache と SWA Bounded Replay".
+ *
+ * Conventions for every call:
+ *   - Buffers named as device buffers are device pointers owned by the caller;
+ *     the library never allocates, frees or retains device memory. Scratch
+ *     comes from a caller-provided workspace sized by the matching
+ *     *_workspace_bytes call.
+ *   - Workspaces must be zero-filled before their first use. Every call that
+ *     completes normally leaves the workspace's control words zero again, so
+ *     one zero-fill at allocation is enough. One workspace must not be used by
+ *     two calls that can run at the same time.
+ *   - All work is enqueued on `stream` (a hipStream_t; NULL = default stream).
+ *     No call synchronizes the host with the device.
+ *   - Arguments are validated on the host before any HIP call. Device data
+ *     (positions, code bytes) is not validated except where stated; positions
+ *     outside [0, N) are treated as padding by every kernel that reads them.
+ *   - Return value: CSA2_OK or one of the error codes below; on error nothing
+ *     was enqueued (except CSA2_ERR_HIP, reported by the launch itself) and
+ *     csa2_last_error() describes the failure (thread-local string).
+ *   - Element counts and strides are in elements of the named dtype unless
+ *     the argument name ends in _bytes or the comment says bytes.
+ *
+ * Storage formats (readings where the pages are silent are marked R):
+ *   FP4 codes: one byte holds two E2M1 codes; channel 2j in the low nibble,
+ *     channel 2j+1 in the high nibble of byte j (R). Code bit 3 is the sign;
+ *     magnitudes {0, .5, 1, 1.5, 2, 3, 4, 6} ([jiwasawa] FP4: OCP E2M1).
+ *   Scales: one E4M3FN byte (bias 7, max 448, 0x7F/0xFF = NaN) per 16
+ *     channels ([ezic] key points), byte g covers channels 16g..16g+15.
+ *   Main KV cache of a sequence with N positions: for position t, the K codes
+ *     start at k_codes + t*code_stride_bytes, the K scales at
+ *     k_scales + t*scale_stride_bytes, likewise for V. Sequence b starts at
+ *     position b*N. The recommended record layout is code_stride = 128 with
+ *     v_codes = k_codes + 64 and scale_stride = 16 with v_scales = k_scales + 8:
+ *     144 bytes per token for K and V of 128 channels.
+ */
+#ifndef CSA2_H_
+#define CSA2_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define CSA2_OK 0
+#define CSA2_ERR_INVALID_ARG 1      /* null pointer, bad size, stride or alignment */
+#define CSA2_ERR_UNSUPPORTED_DTYPE 2
+#define CSA2_ERR_BAD_PLAN 3         /* layer modes violate the plan rules */
+#define CSA2_ERR_WORKSPACE 4        /* workspace null, misaligned or too small */
+#define CSA2_ERR_HIP 5              /* a HIP call failed; see csa2_last_error() */
+#define CSA2_ERR_DEVICE 6           /* the device reported a failed in-kernel wait */
+
+/* Element types of indexer queries and keys. */
+#define CSA2_F32 0                  /* IEEE fp32 */
+#define CSA2_BF16 1                 /* bfloat16, stored as uint16 bit patterns */
+#define CSA2_E4M3 2                 /* OCP E4M3FN byte, no scale */
+
+/* Layer modes ([zaikei] CSA2とFP4; [jiwasawa] CSA2). */
+#define CSA2_FULL 0
+#define CSA2_REINDEX 1
+#define CSA2_REUSE 2
+
+/* Message for the last failing call on this thread ("" if none). */
+const char* csa2_last_error(void);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int csa2_version(void);
+
+/*
+ * kv_quant_fp4 - S1: quantize bf16 rows to FP4 E2M1 codes with one E4M3 scale
+ * per 16 channels ([ezic] key points and "KVを捨てる、共有する、作り直す";
+ * [zaikei] CSA2とFP4: the main KV cache is stored in FP4 E2M1).
+ *
+ * Per row r and 16-channel group g (R: the pages do not say how the scale is
+ * chosen): amax = max |x|; S = RNE_E4M3(amax / 6) saturating at 448; if S is
+ * 0 every code of the group is 0x0, else code_i = RNE_E2M1(x_i / S) with the
+ * sign of x_i kept (a negative value rounding to zero gives 0x8).
+ *
+ *   x             device, bf16 bit patterns; row r starts at x + r*x_stride
+ *   rows          number of rows (>= 0; 0 is a no-op)
+ *   C             channels per row, a positive multiple of 16
+ *   x_stride      elements between row starts (>= C)
+ *   codes         device; row r's C/2 code bytes start at codes + r*code_stride_bytes
+ *   scales        device; row r's C/16 scale bytes start at scales + r*scale_stride_bytes
+ * Alignment: x and x_stride*2 bytes to 16 bytes; codes and code_stride_bytes
+ * to 8 bytes. Inputs must be finite (NaN/Inf give unspecified codes).
+ */
+int kv_quant_fp4(const uint16_t* x, int64_t rows, int32_t C, int64_t x_stride,
+                 uint8_t* codes, int64_t code_stride_bytes,
+                 uint8_t* scales, int64_t scale_stride_bytes, hipStream_t stream);
+
+/*
+ * kv_dequant_fp4 - inverse image of kv_quant_fp4 ([zaikei] CSA2とFP4: the cache
+ * is dequantized before attention): y = E2M1(code) * E4M3(scale), which is
+ * exact in bf16. Same layouts and alignment rules as kv_quant_fp4 (y like x).
+ */
+int kv_dequant_fp4(const uint8_t* codes, int64_t code_stride_bytes,
+                   const uint8_t* scales, int64_t scale_stride_bytes,
+                   int64_t rows, int32_t C, uint16_t* y, int64_t y_stride, hipStream_t stream);
+
+/*
+ * csa2_index_full - S2a, dense form: indexer scores of Q queries per sequence
+ * against all N indexer keys of that sequence ([jiwasawa] CSA2: a Full layer
+ * computes its own indexer Q and scores the whole context; [zaikei] CSA2とFP4:
+ * the retrieval keys are shared across layers).
+ *
+ * Score (R: the pages give no formula) = the exact dot product q . k rounded
+ * once to fp32 (nearest-even); the kernel accumulates exact products in fp64,
+ * which is exact whenever the terms share a 2^53-wide window. With q_pos
+ * given, positions t > q_pos[b*Q + i] score -inf (causal prefill).
+ *
+ *   q_idx    device [B][Q][d_idx] of q_dtype (CSA2_F32 or CSA2_BF16)
+ *   k_idx    device [B][N][d_idx] of k_dtype (CSA2_F32, CSA2_BF16 or CSA2_E4M3)
+ *   d_idx    64 or 128
+ *   q_pos    device [B][Q] int64 or NULL (no mask)
+ *   scores   device [B][Q][N] fp32 (output)
+ * k_idx must be 16-byte aligned.
+ */
+int csa2_index_full(const void* q_idx, int32_t q_dtype, const void* k_idx, int32_t k_dtype,
+                    int32_t B, int32_t Q, int64_t N, int32_t d_idx, const int64_t* q_pos,
+                    float* scores, hipStream_t stream);
+
+/*
+ * csa2_index_reindex - S2b: a Reindex layer's scores over the candidate pool
+ * only ([jiwasawa] CSA2, Hierarchical Sparse Indexer: the first Full layer
+ * picks a pool from the whole context and Reindex layers search only inside
+ * it; a Reindex layer re-scores with its own Q against the shared indexer K).
+ *
+ *   q_idx    device [B][d_idx]; k_idx device [B][N][d_idx] (shared keys)
+ *   pool     device [B][P] int32 positions; entries outside [0, N) score -inf
+ *   scores   device [B][P] fp32 (output), same score definition as csa2_index_full
+ */
+int csa2_index_reindex(const void* q_idx, int32_t q_dtype, const void* k_idx, int32_t k_dtype,
+                       int32_t B, int64_t N, int32_t d_idx, const int32_t* pool, int32_t P,
+                       float* scores, hipStream_t stream);
+
+/*
+ * csa2_topk - S3: top-K positions per row ([jiwasawa] CSA2: Full and Reindex
+ * layers produce fresh Top-K indices; [zaikei] CSA2とFP4: the selected token
+ * positions are shared across layers).
+ *
+ * Order (R): higher score first, equal scores by lower position; -0 == +0;
+ * NaN and -inf are never selected. The first min(K, #selectable) entries are
+ * written sorted by ascending position, then -1 up to K.
+ *
+ *   scores       device; row r's n scores start at scores + r*score_stride
+ *   cand         device [rows][n] int32 positions of the entries, or NULL
+ *                (position = entry index)
+ *   idx          device [rows][K] int32 (output)
+ *   sel_scores   device [rows][K] fp32 (output, NaN in padding slots) or NULL
+ *   ws           workspace of csa2_topk_workspace_bytes(rows, n, K) bytes, 256-byte aligned
+ * Limits: 1 <= K <= n, n < 2^31.
+ */
+int csa2_topk_workspace_bytes(int64_t rows, int64_t n, int32_t K, size_t* bytes);
+int csa2_topk(const float* scores, int64_t rows, int64_t n, int64_t score_stride,
+              const int32_t* cand, int32_t K, int32_t* idx, float* sel_scores,
+              void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * csa2_sparse_attn_fp4 - S4 + S5: gather the FP4 K and V rows at the selected
+ * positions, dequantize them in registers and run softmax attention
+ * ([jiwasawa] CSA2: sparse attention over the Top-K positions; [zaikei]
+ * CSA2とFP4: dequantize before attention).
+ *
+ * R: all H query heads share the one KV head and one position list; logits
+ * are (q_h . K_j) * softmax_scale; no mask beyond the position list; a query
+ * whose list has no valid position gets zeros.
+ *
+ *   q          device [B][Q][H][d] bf16 bit patterns
+ *   H          1..16 query heads;  d = 128
+ *   k_codes, k_scales, v_codes, v_scales, code_stride_bytes, scale_stride_bytes:
+ *              the main KV cache of B sequences of N positions (see the top)
+ *   idx        device [B][Q][K] int32 positions; -1 or >= N = padding
+ *   out        device [B][Q][H][d] fp32 (output)
+ *   ws         workspace of csa2_sparse_attn_workspace_bytes(...) bytes
+ * Alignment: code pointers and code_stride_bytes to 8 bytes.
+ */
+int csa2_sparse_attn_workspace_bytes(int32_t B, int32_t Q, int32_t H, int32_t d, int32_t K, size_t* bytes);
+int csa2_sparse_attn_fp4(const uint16_t* q, int32_t B, int32_t Q, int32_t H, int32_t d,
+                         const uint8_t* k_codes, const uint8_t* k_scales,
+                         const uint8_t* v_codes, const uint8_t* v_scales,
+                         int64_t N, int64_t code_stride_bytes, int64_t scale_stride_bytes,
+                         const int32_t* idx, int32_t K, float softmax_scale,
+                         float* out, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Layer plan - S6: a static per-layer mode table ([zaikei] CSA2とFP4: each
+ * CSA2 layer is fixed to Full, Reindex or Reuse; [jiwasawa] CSA2: modes are
+ * assigned statically; Full computes its indexer Q and fresh Top-K; Reindex
+ * shares main KV and indexer K and re-scores with its own Q; Reuse shares main
+ * KV and Top-K indices and skips the indexer; Hierarchical Sparse Indexer:
+ * the first Full layer picks the candidate pool that Reindex layers search).
+ *
+ * Plan rules (checked at creation): the first layer is Full; a Reindex layer
+ * needs an earlier Full layer and P >= K; a Reuse layer takes the positions of
+ * the immediately preceding layer (R). The pool is the top-P of the first
+ * Full layer's scores, in the top-K order (R), so it holds that layer's top-K.
+ * ------------------------------------------------------------------------- */
+typedef struct csa2_plan csa2_plan;
+
+typedef struct {
+    int32_t K;              /* positions attended per query */
+    int32_t P;              /* pool size (used when the plan has a Reindex layer) */
+    int32_t H;              /* query heads (1..16) */
+    int32_t d;              /* head dim (128) */
+    int32_t d_idx;          /* indexer dim (64 or 128) */
+    int32_t q_idx_dtype;    /* CSA2_F32 or CSA2_BF16 */
+    int32_t k_idx_dtype;    /* CSA2_F32, CSA2_BF16 or CSA2_E4M3 */
+    float softmax_scale;    /* 0 selects 1/sqrt(d) */
+} csa2_plan_params;
+
+typedef struct {
+    const uint8_t* k_codes; /* main KV cache of B sequences x N positions */
+    const uint8_t* k_scales;
+    const uint8_t* v_codes;
+    const uint8_t* v_scales;
+    int64_t code_stride_bytes;
+    int64_t scale_stride_bytes;
+    const void* k_idx;      /* device [B][N][d_idx] indexer keys, k_idx_dtype */
+} csa2_cache;
+
+typedef struct {
+    const uint16_t* q;      /* device [B][H][d] bf16 attention query of this layer */
+    const void* q_idx;      /* device [B][d_idx] indexer query (Full, Reindex); ignored for Reuse */
+    float* out;             /* device [B][H][d] fp32 attention output */
+    int32_t* idx_out;       /* device [B][K] positions selected by this layer (Full, Reindex)
+                               or NULL to keep them in the workspace; ignored for Reuse */
+    int32_t* pool_out;      /* device [B][P] pool of the first Full layer, or NULL */
+} csa2_layer_io;
+
+int csa2_plan_create(const int32_t* modes, int32_t L, const csa2_plan_params* params, csa2_plan** out);
+void csa2_plan_destroy(csa2_plan* plan);
+int csa2_plan_workspace_bytes(const csa2_plan* plan, int32_t B, int64_t N, size_t* bytes);
+/* One decode step of the whole stack for B sequences, one query each; layers
+ * run in order on `stream`. io has one entry per layer. */
+int csa2_plan_run_decode(const csa2_plan* plan, const csa2_cache* cache, const csa2_layer_io* io,
+                         int32_t B, int64_t N, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * csa2_prefill_full - a chunk of Q queries per sequence through the plan's
+ * first (Full) layer: indexer scores over the whole context with the causal
+ * rule that query i selects only positions <= q_pos[b][i] (R), top-K, and
+ * sparse FP4 attention per query.
+ *
+ *   q_idx   device [B][Q][d_idx];  q device [B][Q][H][d] bf16
+ *   q_pos   device [B][Q] int64 positions of the queries
+ *   idx_out device [B][Q][K] int32 (output);  out device [B][Q][H][d] fp32 (output)
+ */
+int csa2_prefill_workspace_bytes(const csa2_plan* plan, int32_t B, int32_t Q, int64_t N, size_t* bytes);
+int csa2_prefill_full(const csa2_plan* plan, const csa2_cache* cache, const void* q_idx,
+                      const uint16_t* q, const int64_t* q_pos, int32_t B, int32_t Q, int64_t N,
+                      int32_t* idx_out, float* out, void* ws, size_t ws_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CSA2_H_ */

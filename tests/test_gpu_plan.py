@@ -1,0 +1,163 @@
+"""GPU parity of the layer plan (Full / Reindex / Reuse) and the Full-layer prefill
+against the oracle, end to end from bf16 KV rows and indexer inputs."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import fp4_compressed_sparse_kv_amd as C
+import synth
+from oracle import plan as OP
+from oracle import quant as OQ
+from oracle import scores as OS
+from oracle.attention import sparse_attn as o_attn
+from tests.parity import ATTN_TOL, compare_topk, dev_bf16, dev_key, host, max_rel_err_rows
+
+pytestmark = pytest.mark.gpu
+
+
+def build_case(cfg, B=None, with_oracle=True):
+    """Device cache + per-layer inputs for a workload, and the oracle's view of the same inputs."""
+    B = cfg["B"] if B is None else B
+    N, L = cfg["N"], len(cfg["modes"])
+    kidx = np.stack([synth.k_idx(cfg, b) for b in range(B)])
+    cache = C.KVCache(B, N, k_idx=dev_key(kidx, cfg["k_idx_dtype"]))
+    ocache = []
+    for b in range(B):
+        kb, vb = synth.kv_bf16(cfg, b)
+        cache.fill(dev_bf16(kb), dev_bf16(vb), row0=b * N)
+        if with_oracle:
+            kc, ks = OQ.quant_fp4(kb)
+            vc, vs = OQ.quant_fp4(vb)
+            ocache.append(dict(k_codes=kc, k_scales=ks, v_codes=vc, v_scales=vs, k_idx=kidx[b],
+                               k_idx_dtype=cfg["k_idx_dtype"]))
+    layers, olayers = [], []
+    for li in range(L):
+        q = np.stack([synth.q_bf16(cfg, li, b)[0] for b in range(B)])          # [B][H][d]
+        qi = np.stack([synth.q_idx(cfg, li, b)[0] for b in range(B)])          # [B][d_idx]
+        layers.append(dict(q=dev_bf16(q), q_idx=dev_key(qi, cfg["q_idx_dtype"]),
+                           out=torch.empty(B, cfg["H"], cfg["d"], dtype=torch.float32, device="cuda"),
+                           idx_out=torch.empty(B, cfg["K"], dtype=torch.int32, device="cuda")))
+        olayers.append([dict(q=q[b], q_idx=qi[b], q_idx_dtype=cfg["q_idx_dtype"]) for b in range(B)])
+    if cfg.get("P"):
+        layers[0]["pool_out"] = torch.empty(B, cfg["P"], dtype=torch.int32, device="cuda")
+    return cache, layers, ocache, olayers
+
+
+def make_plan(cfg):
+    return C.Plan(cfg["modes"], K=cfg["K"], P=cfg.get("P") or 0, H=cfg["H"], d=cfg["d"], d_idx=cfg["d_idx"],
+                  q_idx_dtype=cfg["q_idx_dtype"], k_idx_dtype=cfg["k_idx_dtype"])
+
+
+SCALE = float(np.float32(1 / math.sqrt(128)))
+
+
+def check_against_oracle(cfg, layers, ocache, olayers, seqs):
+    stats = {"exact": 0, "excused": 0}
+    modes = list(cfg["modes"])
+    for b in seqs:
+        res = OP.run_decode(modes, ocache[b], [olayers[li][b] for li in range(len(modes))], cfg["K"], cfg.get("P"),
+                            softmax_scale=SCALE)
+        pool = None
+        for li, mode in enumerate(modes):
+            g_idx = host(layers[li]["idx_out"][b]) if mode != "reuse" else None
+            if mode == "full" and "pool" in res[li]:
+                pool = res[li]["pool"]
+                g_pool = host(layers[li]["pool_out"][b])
+                s_full = OS.index_scores(olayers[li][b]["q_idx"], cfg["q_idx_dtype"], ocache[b]["k_idx"],
+                                         cfg["k_idx_dtype"])
+                stats[compare_topk(g_pool, pool, lambda p: s_full[p], cfg["P"])] += 1
+            if mode == "full":
+                s = OS.index_scores(olayers[li][b]["q_idx"], cfg["q_idx_dtype"], ocache[b]["k_idx"], cfg["k_idx_dtype"])
+                stats[compare_topk(g_idx, res[li]["idx"], lambda p: s[p], cfg["K"])] += 1
+            elif mode == "reindex":
+                s = OS.index_scores(olayers[li][b]["q_idx"], cfg["q_idx_dtype"], ocache[b]["k_idx"], cfg["k_idx_dtype"])
+                stats[compare_topk(g_idx, res[li]["idx"], lambda p: s[p], cfg["K"])] += 1
+            # attention rows are compared where the positions agree exactly
+            if mode != "reuse" and not np.array_equal(g_idx, res[li]["idx"]):
+                continue
+            err = max_rel_err_rows(host(layers[li]["out"][b]), res[li]["out"])
+            assert err <= ATTN_TOL, (b, li, err)
+    return stats
+
+
+def test_full_layer_n2048_end_to_end():
+    cfg = synth.WORKLOADS["full_n2048"]
+    cache, layers, ocache, olayers = build_case(cfg)
+    plan = make_plan(cfg)
+    plan.run_decode(cache, layers)
+    torch.cuda.synchronize()
+    stats = check_against_oracle(cfg, layers, ocache, olayers, range(cfg["B"]))
+    assert stats["exact"] == 1, stats
+
+
+@pytest.mark.parametrize("B,N,K,P", [(3, 20000, 64, 512), (2, 70001, 2048, 8192), (1, 5000, 100, 100)])
+def test_stack_full_reindex_reuse(B, N, K, P):
+    cfg = synth.small("stack_b32_n262144", B=B, N=N, K=K, P=P)
+    cache, layers, ocache, olayers = build_case(cfg)
+    plan = make_plan(cfg)
+    plan.run_decode(cache, layers)
+    torch.cuda.synchronize()
+    stats = check_against_oracle(cfg, layers, ocache, olayers, range(B))
+    assert stats["excused"] == 0, stats
+    # Reuse layers inherit the Reindex layer's positions bit for bit ...
+    idx1 = layers[1]["idx_out"]
+    for li in (2, 3):
+        direct = C.sparse_attn_fp4(layers[li]["q"][:, None], cache, idx1[:, None], softmax_scale=SCALE)
+        assert torch.equal(direct[:, 0], layers[li]["out"])
+    # ... Reindex positions lie inside the pool, and so do the Full layer's
+    pool = host(layers[0]["pool_out"])
+    for b in range(B):
+        ps = set(pool[b].tolist())
+        assert set(host(idx1[b]).tolist()) - {-1} <= ps
+        assert set(host(layers[0]["idx_out"][b]).tolist()) - {-1} <= ps
+
+
+def test_reindex_over_whole_context_equals_full():
+    cfg = synth.small("stack_b32_n262144", B=2, N=3000, K=50, P=3000, modes=("full", "reindex"))
+    cache, layers, _, _ = build_case(cfg, with_oracle=False)
+    plan = make_plan(cfg)
+    plan.run_decode(cache, layers)
+    full_only = make_plan(dict(cfg, modes=("full",)))
+    l2 = [dict(layers[1], out=torch.empty_like(layers[1]["out"]), idx_out=torch.empty_like(layers[1]["idx_out"]))]
+    full_only.run_decode(cache, l2)
+    torch.cuda.synchronize()
+    assert torch.equal(layers[0]["pool_out"], torch.arange(3000, dtype=torch.int32, device="cuda").expand(2, -1))
+    assert torch.equal(layers[1]["idx_out"], l2[0]["idx_out"])
+    assert torch.equal(layers[1]["out"], l2[0]["out"])
+
+
+def test_plan_is_deterministic():
+    cfg = synth.small("stack_b32_n262144", B=4, N=40000, K=256, P=1024)
+    cache, layers, _, _ = build_case(cfg, with_oracle=False)
+    plan = make_plan(cfg)
+    plan.run_decode(cache, layers)
+    first = [(L["idx_out"].clone(), L["out"].clone()) for L in layers]
+    for _ in range(2):
+        plan.run_decode(cache, layers)
+    torch.cuda.synchronize()
+    for (i0, o0), L in zip(first, layers):
+        assert torch.equal(i0, L["idx_out"]) and torch.equal(o0, L["out"])
+
+
+def test_prefill_full_causal():
+    cfg = synth.small("stack_b4_n1m", B=2, N=5000, K=32, modes=("full",))
+    cache, layers, ocache, _ = build_case(cfg)
+    Q = 12
+    q_pos = np.array([[0, 5, 31, 32, 100, 1000, 2500, 4000, 4990, 4997, 4998, 4999]] * 2, dtype=np.int64)
+    qi = np.stack([synth.prefill_q_idx(cfg, b, Q) for b in range(2)])
+    qb = np.stack([synth.prefill_q_bf16(cfg, b, Q) for b in range(2)])
+    plan = make_plan(cfg)
+    idx, out = plan.prefill_full(cache, dev_key(qi, cfg["q_idx_dtype"]), dev_bf16(qb), torch.from_numpy(q_pos).cuda())
+    torch.cuda.synchronize()
+    idx, out = host(idx), host(out)
+    for b in range(2):
+        r_idx, r_out = OP.prefill_full(qi[b], cfg["q_idx_dtype"], q_pos[b], qb[b], ocache[b], cfg["K"],
+                                       softmax_scale=SCALE)
+        for i in range(Q):
+            s = OS.index_scores(qi[b, i], cfg["q_idx_dtype"], ocache[b]["k_idx"], cfg["k_idx_dtype"], q_pos=int(q_pos[b, i]))
+            assert compare_topk(idx[b, i], r_idx[i], lambda p: s[p], cfg["K"]) == "exact"
+            assert max_rel_err_rows(out[b, i], r_out[i]) <= ATTN_TOL
+        assert (idx[b, 0] >= 0).sum() == 1 and idx[b, 0, 0] == 0       # query at position 0 sees only itself
