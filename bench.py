@@ -1,0 +1,289 @@
+#!/usr/bin/env python3
+"""Benchmark of one decode step of the CSA2 layer stack over an FP4 E2M1 KV cache on one MI355X.
+
+Default workload: stack_b32_n262144 - layers Full, Reindex, Reuse, Reuse; 32
+sequences x 262,144 positions; 16 query heads of dim 128 on one shared FP4 KV
+head (E4M3 scale per 16 channels); indexer dim 64 with E4M3 keys and bf16
+queries; pool P = 8192; top-K = 2048. One step = the whole stack for all 32
+sequences (one query each), inputs resident in HBM.
+
+Prints ONE JSON line: queries/s, ms per step, algorithmic HBM GB/s of the step,
+a roofline entry for the dominant kernel (the Full layer's fused scan + select,
+timed with HIP events on its own stream inside this process) and the CPU
+oracle timed on a bounded sample of the same workload (cpu_baseline).
+
+  python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
+  python bench.py --copy-calibration   # also runs a known-size copy kernel (for PMC scaling)
+"""
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "decode queries/s per CSA2 layer stack + achieved HBM GB/s (% of peak)"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_full_select_stack_b32_n262144.json")
+KERNEL_SOURCES = ["select.hip", "dot.hpp", "device.hpp"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def alg_bytes(cfg):
+    """Algorithmic bytes of one step (per sequence sums x B) and of the Full selection kernel.
+
+    Full    = 2*d_I + N*d_I*b_k + 4P (when a Reindex follows) + 4K + A
+    Reindex = 2*d_I + 4P + P*d_I*b_k + 4K + A
+    Reuse   = A,  A = 4K + 2*H*d + K*2*(d/2 + d/16) + 4*H*d
+    """
+    B, N, K, H, d, dI = cfg["B"], cfg["N"], cfg["K"], cfg["H"], cfg["d"], cfg["d_idx"]
+    P = cfg.get("P") or 0
+    bk = {"e4m3": 1, "bf16": 2, "f32": 4}[cfg["k_idx_dtype"]]
+    bq = {"bf16": 2, "f32": 4}[cfg["q_idx_dtype"]]
+    modes = list(cfg["modes"])
+    has_re = "reindex" in modes
+    A = 4 * K + 2 * H * d + K * 2 * (d // 2 + d // 16) + 4 * H * d
+    per_seq = 0
+    full_sel = 0
+    first_full = True
+    for m in modes:
+        if m == "full":
+            sel = bq * dI + N * dI * bk + (4 * P if (has_re and first_full) else 0) + 4 * K
+            if first_full:
+                full_sel = sel
+            first_full = False
+            per_seq += sel + A
+        elif m == "reindex":
+            per_seq += bq * dI + 4 * P + P * dI * bk + 4 * K + A
+        else:
+            per_seq += A
+    return B * per_seq, B * full_sel
+
+
+def kernel_hash():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "fp4_compressed_sparse_kv_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch of the Full selection kernel from the committed PMC runs, or None
+    when they were taken on other kernel sources or another workload."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as fh:
+        t = json.load(fh)
+    if t.get("kernel_hash") != kernel_hash() or t.get("workload") != workload:
+        return None
+    return t.get("traffic_bytes_per_launch")
+
+
+def build_inputs(cfg, dev):
+    import numpy as np
+    import torch
+
+    import fp4_compressed_sparse_kv_amd as C
+    import synth
+
+    B, N, L = cfg["B"], cfg["N"], len(cfg["modes"])
+
+    def bf(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    def key_t(a, dt):
+        t = torch.from_numpy(np.ascontiguousarray(a))
+        if dt == "e4m3":
+            return t.to(dev).view(torch.float8_e4m3fn)
+        if dt == "bf16":
+            return t.view(torch.int16).to(dev).view(torch.bfloat16)
+        return t.to(dev)
+
+    dI = cfg["d_idx"]
+    kdt = {"e4m3": torch.uint8, "bf16": torch.int16, "f32": torch.float32}[cfg["k_idx_dtype"]]
+    kidx = torch.empty(B, N, dI, dtype=kdt, device=dev)
+    cache = C.KVCache(B, N, device=dev)
+    for b in range(B):
+        kb, vb = synth.kv_bf16(cfg, b)
+        cache.fill(bf(kb), bf(vb), row0=b * N)
+        ki = synth.k_idx(cfg, b)
+        kidx[b].copy_(torch.from_numpy(np.ascontiguousarray(ki).view(
+            {"e4m3": np.uint8, "bf16": np.int16, "f32": np.float32}[cfg["k_idx_dtype"]])))
+    if cfg["k_idx_dtype"] == "e4m3":
+        cache.k_idx = kidx.view(torch.float8_e4m3fn)
+    elif cfg["k_idx_dtype"] == "bf16":
+        cache.k_idx = kidx.view(torch.bfloat16)
+    else:
+        cache.k_idx = kidx
+    layers = []
+    for li in range(L):
+        q = np.stack([synth.q_bf16(cfg, li, b)[0] for b in range(B)])
+        qi = np.stack([synth.q_idx(cfg, li, b)[0] for b in range(B)])
+        layers.append(dict(q=bf(q), q_idx=key_t(qi, cfg["q_idx_dtype"]),
+                           out=torch.empty(B, cfg["H"], cfg["d"], dtype=torch.float32, device=dev),
+                           idx_out=torch.empty(B, cfg["K"], dtype=torch.int32, device=dev)))
+    if cfg.get("P") and "reindex" in cfg["modes"]:
+        layers[0]["pool_out"] = torch.empty(B, cfg["P"], dtype=torch.int32, device=dev)
+    torch.cuda.synchronize()
+    return cache, layers
+
+
+def cpu_baseline(cfg, budget_s):
+    """The oracle, as it stands, on whole sequences of the same workload until ~budget_s of CPU work."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import synth
+    from oracle import plan as OP
+
+    modes = list(cfg["modes"])
+    scale = float(np.float32(1 / math.sqrt(cfg["d"])))
+    done, spent = 0, 0.0
+    with threadpool_limits(limits=1):
+        for b in range(cfg["B"]):
+            kb, vb = synth.kv_bf16(cfg, b)                           # untimed: input generation
+            cache = dict(k_bf16=kb, v_bf16=vb, k_idx=synth.k_idx(cfg, b), k_idx_dtype=cfg["k_idx_dtype"])
+            layers = [dict(q=synth.q_bf16(cfg, li, b)[0], q_idx=synth.q_idx(cfg, li, b)[0],
+                           q_idx_dtype=cfg["q_idx_dtype"]) for li in range(len(modes))]
+            t0 = time.perf_counter()
+            OP.run_decode(modes, cache, layers, cfg["K"], cfg.get("P"), softmax_scale=scale)
+            spent += time.perf_counter() - t0
+            done += 1
+            if spent >= budget_s:
+                break
+    return {"value": done / spent, "unit": "queries/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} of {cfg['B']} sequences, one decode step of the whole stack each "
+                      f"(N={cfg['N']}), {spent:.1f} s on 1 host core (BLAS limited to 1 thread); "
+                      f"KV rows quantized by the oracle only where attention reads them"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="stack_b32_n262144")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU only; the stack shards by sequence "
+                                   "(see DESIGN.md) and no multi-GPU run is provided", "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+
+    import fp4_compressed_sparse_kv_amd as C
+    import synth
+
+    cfg = dict(synth.WORKLOADS[args.workload])
+    if "modes" not in cfg:
+        raise SystemExit(f"{args.workload} is not a decode workload")
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    t0 = time.perf_counter()
+    cache, layers = build_inputs(cfg, dev)
+    log(f"inputs ready in {time.perf_counter() - t0:.1f} s")
+    plan = C.Plan(cfg["modes"], K=cfg["K"], P=cfg.get("P") or 0, H=cfg["H"], d=cfg["d"], d_idx=cfg["d_idx"],
+                  q_idx_dtype=cfg["q_idx_dtype"], k_idx_dtype=cfg["k_idx_dtype"])
+    stream = torch.cuda.current_stream()
+
+    for _ in range(args.warmup):
+        plan.run_decode(cache, layers)
+    torch.cuda.synchronize()
+
+    # timed region: exactly K steps between two events, synchronized on both sides
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        plan.run_decode(cache, layers)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    log(f"step {ms * 1e3:.1f} us")
+
+    # per-kernel durations over a second pass of K steps (events around each kernel, same stream)
+    plan.profile_begin(args.steps)
+    for _ in range(args.steps):
+        plan.run_decode(cache, layers)
+    torch.cuda.synchronize()
+    slot_ms, runs = plan.profile_read()
+    plan.profile_begin(0)
+    log("kernel slots (ms): " + ", ".join(f"{s:.4f}" for s in slot_ms))
+
+    # cold-cache steps: a 1 GiB write between steps evicts L2 and MALL; each step timed alone
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    cold = []
+    for _ in range(min(args.steps, 10)):
+        flush.fill_(1)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        plan.run_decode(cache, layers)
+        b.record(stream)
+        torch.cuda.synchronize()
+        cold.append(a.elapsed_time(b))
+    del flush
+
+    if args.copy_calibration:
+        # known-size copy kernel for scaling PMC byte counters: reads and writes 1 GiB
+        x = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        y = torch.empty_like(x)
+        torch.add(x, 0.0, out=y)
+        torch.cuda.synchronize()
+        del x, y
+
+    step_bytes, sel_bytes = alg_bytes(cfg)
+    qps = cfg["B"] / (ms * 1e-3)
+    sel_ms = slot_ms[0]
+    achieved = sel_bytes / (sel_ms * 1e-3) / 1e9
+    traffic = measured_traffic(args.workload)
+    out = {
+        "metric": METRIC,
+        "value": round(qps, 1),
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f64/f32",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "B": cfg["B"], "N": cfg["N"], "modes": list(cfg["modes"]),
+                   "H": cfg["H"], "d": cfg["d"], "d_idx": cfg["d_idx"], "K": cfg["K"], "P": cfg.get("P"),
+                   "kv": "fp4_e2m1 + e4m3 scale per 16 ch", "indexer_keys": cfg["k_idx_dtype"],
+                   "indexer_query": cfg["q_idx_dtype"]},
+        "hbm_gbs_step": round(step_bytes / (ms * 1e-3) / 1e9, 1),
+        "hbm_frac_step": round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "alg_bytes_step": step_bytes,
+        "cold_ms_per_step": round(sorted(cold)[len(cold) // 2], 5) if cold else None,
+        "kernel_ms": {"full_select": round(sel_ms, 5),
+                      **{f"slot{i}": round(v, 5) for i, v in enumerate(slot_ms) if i > 0 and v > 0}},
+        "roofline": {"bound": "hbm", "kernel": "k_select<SrcScan> (Full layer: scan + pool/top-K select)",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "alg_bytes_per_launch": sel_bytes,
+                     "traffic": traffic},
+    }
+    if not args.no_cpu:
+        t0 = time.perf_counter()
+        out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
+        log(f"cpu baseline in {time.perf_counter() - t0:.1f} s")
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

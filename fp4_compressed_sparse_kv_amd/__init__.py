@@ -69,6 +69,8 @@ _SIGS = {
     "csa2_plan_workspace_bytes": (ctypes.c_int, [_vp, _c_i32, _c_i64, ctypes.POINTER(_c_sz)]),
     "csa2_plan_run_decode": (ctypes.c_int, [_vp, ctypes.POINTER(CacheDesc), ctypes.POINTER(LayerIO), _c_i32, _c_i64,
                                             _vp, _c_sz, _vp]),
+    "csa2_plan_profile_begin": (ctypes.c_int, [_vp, _c_i32]),
+    "csa2_plan_profile_read": (ctypes.c_int, [_vp, ctypes.POINTER(_c_f32), ctypes.POINTER(_c_i32)]),
     "csa2_prefill_workspace_bytes": (ctypes.c_int, [_vp, _c_i32, _c_i32, _c_i64, ctypes.POINTER(_c_sz)]),
     "csa2_prefill_full": (ctypes.c_int, [_vp, ctypes.POINTER(CacheDesc), _vp, _vp, _vp, _c_i32, _c_i32, _c_i64, _vp,
                                          _vp, _vp, _c_sz, _vp]),
@@ -306,6 +308,18 @@ class Plan:
         desc = cache.desc()
         _check(lib().csa2_plan_run_decode(self._h, ctypes.byref(desc), io, B, N, _ptr(ws), ws.numel(),
                                           _stream(stream)), "csa2_plan_run_decode")
+
+    def profile_begin(self, max_runs):
+        """Record HIP events around every kernel of the next max_runs run_decode calls."""
+        _check(lib().csa2_plan_profile_begin(self._h, max_runs), "csa2_plan_profile_begin")
+
+    def profile_read(self):
+        """Average ms per launch for each kernel slot (2*l: selection of layer l, 2*l+1: attention)."""
+        n = 2 * len(self.modes)
+        arr = (_c_f32 * n)()
+        runs = _c_i32(0)
+        _check(lib().csa2_plan_profile_read(self._h, arr, ctypes.byref(runs)), "csa2_plan_profile_read")
+        return list(arr), runs.value
 
     def prefill_workspace_bytes(self, B, Q, N):
         nb = ctypes.c_size_t(0)

@@ -113,8 +113,9 @@ int check_attn(const uint16_t* q, int32_t H, int32_t d, const uint8_t* kc, const
     if (N < 1) return fail(INVALID, w + ": N must be >= 1");
     if (cs < d / 2 || ss < d / 16) return fail(INVALID, w + ": KV code/scale stride smaller than one row");
     if (!q || !kc || !ks || !vc || !vs) return fail(INVALID, w + ": null pointer");
-    if (!aligned(kc, 8) || !aligned(vc, 8) || cs % 8 != 0) return fail(INVALID, w + ": KV codes must be 8-byte aligned");
-    if (!aligned(q, 2)) return fail(INVALID, w + ": query misaligned");
+    if (!aligned(kc, 16) || !aligned(vc, 16) || cs % 16 != 0)
+        return fail(INVALID, w + ": KV code rows must be 16-byte aligned");
+    if (!aligned(q, 16)) return fail(INVALID, w + ": query must be 16-byte aligned");
     return OK;
 }
 
@@ -268,7 +269,90 @@ struct csa2_plan {
     std::vector<int32_t> modes;
     csa2_plan_params p;
     bool has_reindex = false;
+    // timing aid: events[(run * 2L + slot) * 2 + {0 start, 1 stop}]
+    mutable std::vector<hipEvent_t> events;
+    mutable std::vector<uint8_t> used;        // [run][slot] recorded?
+    mutable int32_t max_runs = 0, runs = 0;
+
+    void drop_events() const {
+        for (hipEvent_t e : events)
+            if (e) (void)hipEventDestroy(e);
+        events.clear();
+        used.clear();
+        max_runs = runs = 0;
+    }
+    ~csa2_plan() { drop_events(); }
 };
+
+namespace {
+
+// Records the start/stop events of one kernel slot when profiling is on.
+struct SlotTimer {
+    const csa2_plan* plan;
+    int slot;
+    hipStream_t stream;
+    bool on;
+    SlotTimer(const csa2_plan* pl, int s, hipStream_t st) : plan(pl), slot(s), stream(st) {
+        on = pl->runs < pl->max_runs;
+        if (on) {
+            const size_t L2 = 2 * pl->modes.size();
+            (void)hipEventRecord(pl->events[((size_t)pl->runs * L2 + slot) * 2 + 0], stream);
+            pl->used[(size_t)pl->runs * L2 + slot] = 1;
+        }
+    }
+    ~SlotTimer() {
+        if (on) {
+            const size_t L2 = 2 * plan->modes.size();
+            (void)hipEventRecord(plan->events[((size_t)plan->runs * L2 + slot) * 2 + 1], stream);
+        }
+    }
+};
+
+}  // namespace
+
+int csa2_plan_profile_begin(csa2_plan* plan, int32_t max_runs) {
+    g_err.clear();
+    if (!plan || max_runs < 0) return fail(INVALID, "csa2_plan_profile_begin: bad arguments");
+    plan->drop_events();
+    if (max_runs == 0) return OK;
+    const size_t n = (size_t)max_runs * 2 * plan->modes.size() * 2;
+    plan->events.assign(n, nullptr);
+    for (size_t i = 0; i < n; ++i) {
+        hipError_t e = hipEventCreate(&plan->events[i]);
+        if (e != hipSuccess) {
+            plan->drop_events();
+            return hip_fail(e, "hipEventCreate");
+        }
+    }
+    plan->used.assign((size_t)max_runs * 2 * plan->modes.size(), 0);
+    plan->max_runs = max_runs;
+    plan->runs = 0;
+    return OK;
+}
+
+int csa2_plan_profile_read(csa2_plan* plan, float* avg_ms, int32_t* runs) {
+    g_err.clear();
+    if (!plan || !avg_ms || !runs) return fail(INVALID, "csa2_plan_profile_read: null pointer");
+    const size_t L2 = 2 * plan->modes.size();
+    for (size_t s = 0; s < L2; ++s) {
+        double sum = 0.0;
+        int n = 0;
+        for (int32_t r = 0; r < plan->runs; ++r) {
+            if (!plan->used[(size_t)r * L2 + s]) continue;
+            hipEvent_t a = plan->events[((size_t)r * L2 + s) * 2 + 0], b = plan->events[((size_t)r * L2 + s) * 2 + 1];
+            hipError_t e = hipEventSynchronize(b);
+            if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+            float ms = 0.f;
+            e = hipEventElapsedTime(&ms, a, b);
+            if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
+            sum += ms;
+            ++n;
+        }
+        avg_ms[s] = n ? (float)(sum / n) : 0.f;
+    }
+    *runs = plan->runs;
+    return OK;
+}
 
 int csa2_plan_create(const int32_t* modes, int32_t L, const csa2_plan_params* params, csa2_plan** out) {
     g_err.clear();
@@ -382,6 +466,7 @@ int csa2_plan_run_decode(const csa2_plan* plan, const csa2_cache* cache, const c
             SelOutput o[2];
             int nt = 1;
             int e;
+            SlotTimer timer(plan, 2 * l, stream);
             if (mode == CSA2_FULL) {
                 if (plan->has_reindex && !pool) {
                     int32_t* pool_dst = io[l].pool_out ? io[l].pool_out : reinterpret_cast<int32_t*>(wsb + lay.off_poolbuf);
@@ -419,8 +504,10 @@ int csa2_plan_run_decode(const csa2_plan* plan, const csa2_cache* cache, const c
         at.K = p.K;
         at.scale = p.softmax_scale;
         at.out = io[l].out;
+        SlotTimer timer(plan, 2 * l + 1, stream);
         if (int e = launch_attn(at, wsb + lay.off_attn, ws_bytes - lay.off_attn, stream)) return e;
     }
+    if (plan->runs < plan->max_runs) plan->runs += 1;
     return OK;
 }
 

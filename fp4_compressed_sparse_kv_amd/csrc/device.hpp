@@ -115,21 +115,37 @@ __device__ __forceinline__ uint32_t add_rlx(uint32_t* p, uint32_t v) {
 constexpr uint32_t kSpinLimit = 1u << 20;
 constexpr uint32_t kStatusBarrierTimeout = 1u;
 
+__device__ __forceinline__ void st_rlx_f32(float* p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_rlx_f32(const float* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Wait until every memory operation this wave has issued - including
+// non-returning atomics and stores - has completed.
+__device__ __forceinline__ void wave_drain() { __builtin_amdgcn_s_waitcnt(0); }
+
+// Cross-workgroup data in this library moves only through device-scope
+// atomics and device-scope (coherent, "sc1") loads and stores, never through
+// ordinary cached accesses. Publishing therefore needs no L2 write-back and
+// consuming no L2 invalidate: a writer drains its own operations (wave_drain)
+// before the flag RMW that announces them, and readers read with coherent
+// loads. On this multi-XCD part an agent-scope fence costs an L2 write-back
+// or invalidate of the whole XCD, which is what this protocol avoids.
+//
 // Barrier among the S workgroups that share one row. `ctrl` is a counter that
 // starts at 0 for the launch; the g-th barrier waits until it reaches g*S.
-// Data exchanged across it is written with device-scope atomics and read with
-// device-scope atomic loads, so no cache maintenance beyond the
-// release/acquire pair on the counter is needed.
 __device__ __forceinline__ void row_barrier(uint32_t* ctrl, uint32_t S, uint32_t& gen, uint32_t* status) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    wave_drain();
     __syncthreads();
     gen += 1;
     if (threadIdx.x == 0) {
-        __hip_atomic_fetch_add(ctrl, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        add_rlx(ctrl, 1u);
         const uint32_t target = gen * S;
         uint32_t spins = 0;
-        while (ld_acq(ctrl) < target) {
-            __builtin_amdgcn_s_sleep(2);
+        while (ld_rlx(ctrl) < target) {
+            __builtin_amdgcn_s_sleep(1);
             if (++spins > kSpinLimit) {
                 __hip_atomic_fetch_or(status, kStatusBarrierTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 break;
@@ -137,7 +153,6 @@ __device__ __forceinline__ void row_barrier(uint32_t* ctrl, uint32_t S, uint32_t
         }
     }
     __syncthreads();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 }
 
 }  // namespace csa2

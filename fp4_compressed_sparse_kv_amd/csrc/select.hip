@@ -12,8 +12,9 @@
 // The K-th largest key T is found with three radix passes over the LDS keys
 // (digits of 11, 11 and 10 bits). Each pass builds a per-chunk histogram with
 // LDS atomics, adds it into the row's histogram in the workspace with
-// device-scope atomics, waits at a barrier of the row's S workgroups (all of
-// them co-resident: cooperative launch) and reads the row total back. Ties at
+// device-scope atomics, waits at a barrier of the row's S workgroups (all
+// resident at once: a launch never holds more workgroups than CUs, and the
+// kernel fits one per CU) and reads the row total back. Ties at
 // T are resolved by position: every chunk publishes its counts of keys > T and
 // == T, and chunks take their share of the ==T entries in chunk order. Each
 // chunk then compacts its selected entries in position order straight into
@@ -339,21 +340,23 @@ __global__ void __launch_bounds__(kSelThreads) k_select(Src src, SelDev g, SelTg
     if (multi) row_barrier(ctrl, g.S, gen, status);
     else __syncthreads();
 
-    // ---- offsets: this chunk's output base and its share of the == T entries
+    // ---- offsets: this chunk's output base and its share of the == T entries.
+    // The counts of all chunks are staged in LDS by one lane each (the pass-2/3
+    // histogram space is free now), so no lane walks them with serial loads.
+    uint32_t* cnts = lh2;                       // [S][2 targets][gt, eq]
+    if (multi) {
+        for (int i = tid; i < g.S * 4; i += kSelThreads) cnts[i] = ld_rlx(&gcnt[i]);
+    } else if (tid < 4) {
+        cnts[tid] = sm[16 + tid];
+    }
+    __syncthreads();
     uint32_t* wbase = sm + 128;                 // [2][16][base, eq_before]
     uint32_t* tinfo = sm + 192;                 // [2][take_eq, total_sel]
     if (tid < nt) {
         const int j = tid;
         uint32_t off = 0, eq_before = 0, total_sel = 0, my_take = 0;
         for (int s = 0; s < g.S; ++s) {
-            uint32_t gt, eq;
-            if (multi) {
-                gt = ld_rlx(&gcnt[(s * 2 + j) * 2 + 0]);
-                eq = ld_rlx(&gcnt[(s * 2 + j) * 2 + 1]);
-            } else {
-                gt = sm[16 + j * 2 + 0];
-                eq = sm[16 + j * 2 + 1];
-            }
+            const uint32_t gt = cnts[(s * 2 + j) * 2 + 0], eq = cnts[(s * 2 + j) * 2 + 1];
             const uint32_t left = need[j] > eq_before ? need[j] - eq_before : 0u;
             const uint32_t take = eq < left ? eq : left;
             if (s < split) off += gt + take;
@@ -412,7 +415,7 @@ __global__ void __launch_bounds__(kSelThreads) k_select(Src src, SelDev g, SelTg
     if (multi) {
         __syncthreads();
         if (tid == 0) {
-            const uint32_t old = __hip_atomic_fetch_add(exitc, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+            const uint32_t old = add_rlx(exitc, 1u);
             sm[0] = (old == (uint32_t)g.S - 1) ? 1u : 0u;
         }
         __syncthreads();
@@ -488,14 +491,29 @@ int launch_rows(const SelPlan& p, const Src& src, const SelOutput* out, int nt, 
     g.nt = nt;
     g.row_words = p.row_words;
     g.ws = reinterpret_cast<uint32_t*>(ws);
+    // The workgroups of a row wait for each other, so every workgroup of a
+    // launch must be resident at once. A launch holds at most rows_per_launch
+    // * S <= #CUs workgroups; check that the kernel fits one workgroup per CU
+    // with this LDS size (the occupancy query accounts for registers too).
+    // Kernels on one stream run one after another, so the CUs are free when
+    // the launch starts; a wait that still cannot finish gives up after a
+    // bounded number of polls and flags the workspace status word.
+    static size_t checked_lds = 0;
+    if (checked_lds != p.lds_bytes) {
+        int per_cu = 0;
+        hipError_t he = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kSelThreads, p.lds_bytes);
+        if (he != hipSuccess) return hip_fail(he, "hipOccupancyMaxActiveBlocksPerMultiprocessor(select)");
+        if (per_cu < 1) return fail(INVALID, "select: kernel does not fit on a CU with this LDS size");
+        checked_lds = p.lds_bytes;
+    }
     Src s = src;
     for (int64_t r0 = 0; r0 < p.rows; r0 += p.rows_per_launch) {
         const int64_t nr = (p.rows - r0) < p.rows_per_launch ? (p.rows - r0) : p.rows_per_launch;
         g.row0 = (int32_t)r0;
         void* args[] = {&s, &g, &t[0], &t[1]};
-        hipError_t he = hipLaunchCooperativeKernel(fn, dim3((unsigned)(nr * p.S)), dim3(kSelThreads), args,
-                                                   (unsigned)p.lds_bytes, stream);
-        if (he != hipSuccess) return hip_fail(he, "hipLaunchCooperativeKernel(select)");
+        hipError_t he = hipLaunchKernel(fn, dim3((unsigned)(nr * p.S)), dim3(kSelThreads), args,
+                                        (unsigned)p.lds_bytes, stream);
+        if (he != hipSuccess) return hip_fail(he, "hipLaunchKernel(select)");
     }
     return OK;
 }

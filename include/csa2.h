@@ -188,7 +188,10 @@ int csa2_topk(const float* scores, int64_t rows, int64_t n, int64_t score_stride
  *   idx        device [B][Q][K] int32 positions; -1 or >= N = padding
  *   out        device [B][Q][H][d] fp32 (output)
  *   ws         workspace of csa2_sparse_attn_workspace_bytes(...) bytes
- * Alignment: code pointers and code_stride_bytes to 8 bytes.
+ * Alignment: code pointers and code_stride_bytes to 16 bytes.
+ * Numerics: the query is used in f16 (exact for |q| in [2^-14, 65504]), the
+ * dequantized K and V are exact in f16, each softmax weight is carried as
+ * two f16 terms (about 22 significant bits), products accumulate in fp32.
  */
 int csa2_sparse_attn_workspace_bytes(int32_t B, int32_t Q, int32_t H, int32_t d, int32_t K, size_t* bytes);
 int csa2_sparse_attn_fp4(const uint16_t* q, int32_t B, int32_t Q, int32_t H, int32_t d,
@@ -250,6 +253,20 @@ int csa2_plan_workspace_bytes(const csa2_plan* plan, int32_t B, int64_t N, size_
  * run in order on `stream`. io has one entry per layer. */
 int csa2_plan_run_decode(const csa2_plan* plan, const csa2_cache* cache, const csa2_layer_io* io,
                          int32_t B, int64_t N, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Per-kernel timing of csa2_plan_run_decode (a measurement aid). After
+ * csa2_plan_profile_begin(plan, max_runs), each of the next max_runs calls of
+ * csa2_plan_run_decode records a HIP event on `stream` before and after each
+ * kernel it launches. Kernel slot 2*l is layer l's indexer/selection kernel
+ * (none for Reuse), slot 2*l+1 its attention kernel. csa2_plan_profile_read
+ * waits for the recorded events and writes the average milliseconds per
+ * launch of every slot (0 for a slot that never ran) into avg_ms[2*L] and the
+ * number of profiled runs into *runs. max_runs = 0 stops profiling. Events are
+ * host-side HIP objects owned by the plan; no device memory is allocated.
+ */
+int csa2_plan_profile_begin(csa2_plan* plan, int32_t max_runs);
+int csa2_plan_profile_read(csa2_plan* plan, float* avg_ms, int32_t* runs);
 
 /*
  * csa2_prefill_full - a chunk of Q queries per sequence through the plan's
