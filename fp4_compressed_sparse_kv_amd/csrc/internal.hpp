@@ -30,7 +30,7 @@ int device_info(DeviceInfo* out);
 // co-resident; `rows_per_launch` rows per cooperative launch.
 struct SelPlan {
     int64_t rows = 0, n = 0;
-    int32_t S = 1, chunk = 0, rows_per_launch = 0, launches = 0;
+    int32_t S = 1, chunk = 0, chunk_pad = 0, rows_per_launch = 0, launches = 0;
     int32_t row_words = 0;          // exchange words per row in the workspace
     size_t lds_bytes = 0;
     size_t ws_bytes = 0;            // workspace bytes (header + rows_per_launch rows)

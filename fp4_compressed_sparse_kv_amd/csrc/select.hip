@@ -9,20 +9,27 @@
 //               Full layer: scan and select fused, scores never leave LDS);
 //   SrcPool   - indexer keys gathered at candidate-pool positions and scored
 //               (a Reindex layer).
-// The K-th largest key T is found with three radix passes over the LDS keys
-// (digits of 11, 11 and 10 bits). Each pass builds a per-chunk histogram with
-// LDS atomics, adds it into the row's histogram in the workspace with
-// device-scope atomics, waits at a barrier of the row's S workgroups (all
-// resident at once: a launch never holds more workgroups than CUs, and the
-// kernel fits one per CU) and reads the row total back. Ties at
-// T are resolved by position: every chunk publishes its counts of keys > T and
-// == T, and chunks take their share of the ==T entries in chunk order. Each
-// chunk then compacts its selected entries in position order straight into
-// the output, so the output is sorted by position without a sort. Up to two
-// targets (pool size P and K) are selected from the same keys in one launch.
-//
-// The last workgroup of a row to leave zeroes the row's histograms and
-// counters, so the workspace is ready for the next launch without a memset.
+// The source also builds the chunk's histogram of the top 11 key bits while
+// it writes the keys. The histograms of a row's chunks are summed in the
+// workspace with device-scope atomics; after a barrier of the row's S
+// workgroups (all resident at once: a launch never holds more workgroups
+// than CUs, and the kernel fits one per CU) every chunk knows the bin b1 that
+// holds the M-th largest key.
+//   List path (S > 1 and at most kCandCap keys in bin b1 row-wide): each
+//     chunk appends its bin-b1 entries (index, key) to a per-row list, at
+//     slots reserved with one atomic per chunk, and publishes its count of
+//     keys above the bin. After a second barrier every chunk reads the short
+//     list and resolves the exact threshold key T, how many entries equal to
+//     T are taken, and every chunk's counts, with no further exchange.
+//   Radix path (otherwise): two more radix passes over the LDS keys (11 and
+//     10 bits), each with a row-wide histogram exchange, then an exchange of
+//     the per-chunk counts of keys > T and == T.
+// Ties at T go to the lowest entry index (chunks in order, entries in order
+// within a chunk). Each chunk compacts its selected entries in index order
+// straight into the output, so the output is sorted without a sort. Up to
+// two targets (pool size P and K) are selected from the same keys in one
+// launch. The last workgroup of a row to leave resets the row's counters and
+// histograms, so the workspace is ready for the next launch without a memset.
 #include "dot.hpp"
 #include "internal.hpp"
 
@@ -31,16 +38,19 @@ namespace csa2 {
 constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / kWave;
 constexpr int kB1 = 2048, kB2 = 2048, kB3 = 1024;   // radix digits 11 | 11 | 10 bits
-constexpr int kRowHdr = 16;                          // [0] barrier counter, [1] exit counter
-constexpr int kRowFixed = kRowHdr + kB1 + 2 * kB2 + 2 * kB3;
+constexpr int kRowHdr = 16;                          // [0] barrier, [1] exit, [2 + j] list length of target j
+constexpr int kCandCap = 16384;                      // list entries per (row, target)
+constexpr int kMaxS = 256;                           // chunks per row (<= CUs)
 constexpr int kWsHeaderWords = 64;                   // [0] device status word
 constexpr int kScratchWords = 256;
-constexpr int kLdsFixedWords = kB1 + 2 * kB2 + kScratchWords;
+constexpr int kLdsFixedWords = kB1 + 2 * kB2 + 4 * kMaxS + kScratchWords;
 constexpr int kMaxChunk = 32768;
+constexpr int kPadTo = 256;                          // keys per wave step of the count/compaction passes
+constexpr int kMaxSteps = kMaxChunk / kSelWaves / kPadTo;   // steps per wave (8)
 
 struct SelDev {
     int64_t n;
-    int32_t S, chunk, row0, nt, row_words;
+    int32_t S, chunk, chunk_pad, row0, nt, row_words;
     uint32_t* ws;
 };
 
@@ -51,6 +61,15 @@ struct SelTgt {
     int32_t M;
 };
 
+__device__ __forceinline__ void put_key(uint32_t* keys, uint32_t* hist, int i, uint32_t key) {
+    keys[i] = key;
+    if (key) atomicAdd(&hist[key >> 21], 1u);
+}
+
+__device__ __forceinline__ void pad_keys(uint32_t* keys, int cnt, int cpad) {
+    for (int i = cnt + (int)threadIdx.x; i < cpad; i += kSelThreads) keys[i] = 0u;
+}
+
 // ------------------------------------------------------------------ sources
 
 struct SrcScores {
@@ -59,9 +78,11 @@ struct SrcScores {
     const int32_t* cand;
     int64_t n;
 
-    __device__ __forceinline__ void fill(int64_t row, int64_t begin, int cnt, uint32_t* keys) const {
+    __device__ __forceinline__ void fill(int64_t row, int64_t begin, int cnt, int cpad, uint32_t* keys,
+                                         uint32_t* hist) const {
         const float* p = scores + row * stride + begin;
-        for (int i = threadIdx.x; i < cnt; i += kSelThreads) keys[i] = score_key(p[i]);
+        for (int i = threadIdx.x; i < cnt; i += kSelThreads) put_key(keys, hist, i, score_key(p[i]));
+        pad_keys(keys, cnt, cpad);
         __syncthreads();
     }
     __device__ __forceinline__ int32_t position(int64_t row, int64_t i) const {
@@ -77,7 +98,8 @@ struct SrcScan {
     int32_t rows_per_seq;
     const int64_t* q_pos;
 
-    __device__ __forceinline__ void fill(int64_t row, int64_t begin, int cnt, uint32_t* keys) const {
+    __device__ __forceinline__ void fill(int64_t row, int64_t begin, int cnt, int cpad, uint32_t* keys,
+                                         uint32_t* hist) const {
         using KS = KeySlice<KT, D>;
         constexpr int QB = (QT == kBF16) ? 2 : 4;
         constexpr int U = KS::RAW >= 4 ? 1 : 4 / KS::RAW;   // 64 bytes in flight per lane
@@ -103,9 +125,10 @@ struct SrcScan {
             for (int u = 0; u < U; ++u) {
                 const int i = base + u * (kSelThreads / 4) + quad;
                 const double v = quad_sum(s[u].dot(qd));
-                if (lq == 0 && i < cnt) keys[i] = (i < lim) ? score_key((float)v) : 0u;
+                if (lq == 0 && i < cnt) put_key(keys, hist, i, (i < lim) ? score_key((float)v) : 0u);
             }
         }
+        pad_keys(keys, cnt, cpad);
         __syncthreads();
     }
     __device__ __forceinline__ int32_t position(int64_t, int64_t i) const { return (int32_t)i; }
@@ -119,7 +142,8 @@ struct SrcPool {
     const int32_t* pool;
     int64_t P;
 
-    __device__ __forceinline__ void fill(int64_t row, int64_t begin, int cnt, uint32_t* keys) const {
+    __device__ __forceinline__ void fill(int64_t row, int64_t begin, int cnt, int cpad, uint32_t* keys,
+                                         uint32_t* hist) const {
         using KS = KeySlice<KT, D>;
         constexpr int QB = (QT == kBF16) ? 2 : 4;
         constexpr int U = KS::RAW >= 4 ? 1 : 4 / KS::RAW;
@@ -143,9 +167,10 @@ struct SrcPool {
             for (int u = 0; u < U; ++u) {
                 const int i = base + u * (kSelThreads / 4) + quad;
                 const double v = quad_sum(s[u].dot(qd));
-                if (lq == 0 && i < cnt) keys[i] = ok[u] ? score_key((float)v) : 0u;
+                if (lq == 0 && i < cnt) put_key(keys, hist, i, ok[u] ? score_key((float)v) : 0u);
             }
         }
+        pad_keys(keys, cnt, cpad);
         __syncthreads();
     }
     __device__ __forceinline__ int32_t position(int64_t row, int64_t i) const { return pool[row * P + i]; }
@@ -207,160 +232,320 @@ __device__ __forceinline__ void pull_hist(uint32_t* lh, const uint32_t* gh, int 
 
 // ------------------------------------------------------------------ kernel
 
+enum : int { kPathAll = 0, kPathList = 1, kPathRadix = 2 };
+
+__device__ __forceinline__ void st_rlx_u64(uint64_t* p, uint64_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ld_rlx_u64(const uint64_t* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 template <class Src>
 __global__ void __launch_bounds__(kSelThreads) k_select(Src src, SelDev g, SelTgt t0, SelTgt t1) {
     extern __shared__ uint32_t lds[];
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
-    const int lrow = blockIdx.x / g.S;
-    const int split = blockIdx.x - lrow * g.S;
+    const int S = g.S;
+    const int lrow = blockIdx.x / S;
+    const int split = blockIdx.x - lrow * S;
     const int64_t row = (int64_t)g.row0 + lrow;
     const int64_t begin = (int64_t)split * g.chunk;
     const int cnt = (int)min((int64_t)g.chunk, g.n - begin);
+    const int cpad = g.chunk_pad;
     const int nt = g.nt;
-    const bool multi = g.S > 1;
+    const bool multi = S > 1;
 
-    uint32_t* keys = lds;
-    uint32_t* lh1 = lds + g.chunk;
-    uint32_t* lh2 = lh1 + kB1;                 // [2][kB2]; pass 3 reuses it as [2][kB3]
-    uint32_t* sm = lh2 + 2 * kB2;
+    uint32_t* keys = lds;                       // [cpad] score keys, 0 past cnt
+    uint32_t* lh1 = lds + cpad;                 // [kB1] this chunk's top-digit histogram
+    uint32_t* lh2 = lh1 + kB1;                  // [2*kB2] row histogram, then later histograms
+    uint32_t* cnts = lh2 + 2 * kB2;             // [S][2 targets][> T, == T]
+    uint32_t* sm = cnts + 4 * kMaxS;            // scratch
     uint32_t* status = g.ws;
     uint32_t* rw = g.ws + kWsHeaderWords + (size_t)lrow * g.row_words;
     uint32_t* ctrl = rw;
     uint32_t* exitc = rw + 1;
+    uint32_t* llen = rw + 2;                    // [2] list lengths
     uint32_t* gh1 = rw + kRowHdr;
     uint32_t* gh2 = gh1 + kB1;
     uint32_t* gh3 = gh2 + 2 * kB2;
-    uint32_t* gcnt = gh3 + 2 * kB3;             // [S][2 targets][gt, eq]
+    uint32_t* gtab = gh3 + 2 * kB3;             // [S][2] keys above bin b1 per chunk
+    uint32_t* gcnt = gtab + 2 * S;              // [S][2][> T, == T]
+    uint64_t* glist = reinterpret_cast<uint64_t*>(gcnt + 4 * S);   // [2][kCandCap] (index << 32 | key)
     uint32_t gen = 0;
 
     const uint32_t M[2] = {(uint32_t)t0.M, (uint32_t)t1.M};
 
-    for (int i = tid; i < kB1 + 2 * kB2; i += kSelThreads) lh1[i] = 0u;
-    src.fill(row, begin, cnt, keys);            // ends with a block barrier
-
-    // ---- pass 1: bits 31..21
-    for (int i = tid; i < cnt; i += kSelThreads) {
-        const uint32_t k = keys[i];
-        if (k) atomicAdd(&lh1[k >> 21], 1u);
-    }
+    for (int i = tid; i < kB1; i += kSelThreads) lh1[i] = 0u;
     __syncthreads();
+    src.fill(row, begin, cnt, cpad, keys, lh1);  // keys + lh1; ends with a block barrier
+
+    // ---- row histogram of the top 11 bits
+    const uint32_t* G = lh1;
     if (multi) {
         push_hist(lh1, gh1, kB1);
-        row_barrier(ctrl, g.S, gen, status);
-        pull_hist(lh1, gh1, kB1);
+        row_barrier(ctrl, S, gen, status);
+        for (int b = tid; b < kB1; b += kSelThreads) lh2[b] = ld_rlx(&gh1[b]);
+        __syncthreads();
+        G = lh2;
     }
-    bool all[2] = {true, true};
-    uint32_t b1[2] = {0, 0}, rem[2] = {0, 0}, T[2] = {0, 0}, need[2] = {0, 0};
+    int path[2] = {kPathAll, kPathAll};
+    uint32_t b1[2] = {0, 0}, rem[2] = {0, 0}, C[2] = {0, 0}, T[2] = {0, 0}, need[2] = {0, 0};
     for (int j = 0; j < nt; ++j) {
-        const Found f = block_find(lh1, kB1, M[j], sm);
-        all[j] = f.total <= M[j];
-        b1[j] = f.bin;
-        rem[j] = f.rem;
+        const Found f = block_find(G, kB1, M[j], sm);
+        if (f.total > M[j]) {
+            b1[j] = f.bin;
+            rem[j] = f.rem;
+            C[j] = G[f.bin];
+            path[j] = (multi && C[j] <= (uint32_t)kCandCap) ? kPathList : kPathRadix;
+        }
     }
-    const bool any_pass = !all[0] || (nt > 1 && !all[1]);
-    if (any_pass) {
-        // ---- pass 2: bits 20..10 within the chosen top digit
-        for (int i = tid; i < cnt; i += kSelThreads) {
-            const uint32_t k = keys[i];
-            for (int j = 0; j < nt; ++j)
-                if (!all[j] && (k >> 21) == b1[j]) atomicAdd(&lh2[j * kB2 + ((k >> 10) & 2047u)], 1u);
+    __syncthreads();                            // G (lh2) may be overwritten below
+    const bool any_list = path[0] == kPathList || (nt > 1 && path[1] == kPathList);
+    const bool any_radix = path[0] == kPathRadix || (nt > 1 && path[1] == kPathRadix);
+    const bool any_other = path[0] != kPathList || (nt > 1 && path[1] != kPathList);
+
+    // ---- each wave owns a contiguous span of kPadTo-key steps; its lanes keep
+    // the span's keys in registers (4 per lane per step) for every later pass
+    int span = (cpad + kSelWaves - 1) / kSelWaves;
+    span = (span + kPadTo - 1) / kPadTo * kPadTo;
+    const int w0 = min(cpad, wave * span), w1 = min(cpad, w0 + span);
+    const int nst = (w1 - w0) / kPadTo;         // steps of this wave (<= kMaxSteps)
+    uint4 kreg[kMaxSteps];
+    auto load_kreg = [&]() {
+#pragma unroll
+        for (int t = 0; t < kMaxSteps; ++t)
+            kreg[t] = (t < nst) ? *reinterpret_cast<const uint4*>(&keys[w0 + t * kPadTo + 4 * lane])
+                                : make_uint4(0, 0, 0, 0);
+    };
+    if (any_list) load_kreg();
+
+    // ---- list path, part 1: append this chunk's bin-b1 entries, count the keys above the bin
+    if (any_list) {
+        uint32_t* wl = sm + 32;                 // [2][16] per-wave candidate counts, then bases
+        uint32_t above[2] = {0u, 0u}, ncand[2] = {0u, 0u};
+#pragma unroll
+        for (int t = 0; t < kMaxSteps; ++t) {
+            if (t >= nst) break;
+            const uint32_t kv[4] = {kreg[t].x, kreg[t].y, kreg[t].z, kreg[t].w};
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const uint32_t d = kv[u] >> 21;
+                for (int j = 0; j < nt; ++j) {
+                    above[j] += (uint32_t)(d > b1[j]);
+                    ncand[j] += (uint32_t)__popcll(__ballot(kv[u] != 0u && d == b1[j]));
+                }
+            }
+        }
+        for (int j = 0; j < nt; ++j) {
+            const uint32_t a = wave_sum(above[j]);
+            if (lane == 0) {
+                sm[96 + j * kSelWaves + wave] = a;
+                wl[j * kSelWaves + wave] = ncand[j];
+            }
         }
         __syncthreads();
-        if (multi) {
-            for (int j = 0; j < nt; ++j)
-                if (!all[j]) push_hist(lh2 + j * kB2, gh2 + j * kB2, kB2);
-            row_barrier(ctrl, g.S, gen, status);
-            for (int j = 0; j < nt; ++j)
-                if (!all[j]) pull_hist(lh2 + j * kB2, gh2 + j * kB2, kB2);
+        if (tid < nt && path[tid] == kPathList) {
+            uint32_t a = 0, c = 0;
+            for (int w = 0; w < kSelWaves; ++w) {
+                a += sm[96 + tid * kSelWaves + w];
+                c += wl[tid * kSelWaves + w];
+            }
+            st_rlx(&gtab[split * 2 + tid], a);
+            uint32_t base = add_rlx(&llen[tid], c);    // this chunk's slots in the row's list
+            for (int w = 0; w < kSelWaves; ++w) {
+                const uint32_t n = wl[tid * kSelWaves + w];
+                wl[tid * kSelWaves + w] = base;
+                base += n;
+            }
         }
-        uint32_t pre2[2] = {0, 0};
+        __syncthreads();
         for (int j = 0; j < nt; ++j) {
-            if (all[j]) continue;
-            const Found f = block_find(lh2 + j * kB2, kB2, rem[j], sm);
-            pre2[j] = (b1[j] << 11) | f.bin;
-            rem[j] = f.rem;
+            if (path[j] != kPathList) continue;
+            uint32_t run = wl[j * kSelWaves + wave];
+            uint64_t* lst = glist + (size_t)j * kCandCap;
+#pragma unroll
+            for (int t = 0; t < kMaxSteps; ++t) {
+                if (t >= nst) break;
+                const uint32_t kv[4] = {kreg[t].x, kreg[t].y, kreg[t].z, kreg[t].w};
+                const uint32_t ib = (uint32_t)(begin + w0 + t * kPadTo + 4 * lane);
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const bool c = kv[u] != 0u && (kv[u] >> 21) == b1[j];
+                    const uint64_t m = __ballot(c);
+                    const uint32_t slot = run + lanes_below(m);
+                    if (c && slot < (uint32_t)kCandCap)     // holds: the slots of a row sum to C[j] <= kCandCap
+                        st_rlx_u64(&lst[slot], ((uint64_t)(ib + u) << 32) | kv[u]);
+                    run += (uint32_t)__popcll(m);
+                }
+            }
         }
-        // ---- pass 3: bits 9..0 within the chosen 22-bit prefix
+    }
+
+    // ---- radix path: two more digit passes over the LDS keys with row exchanges
+    if (any_radix) {
         for (int i = tid; i < 2 * kB2; i += kSelThreads) lh2[i] = 0u;
         __syncthreads();
         for (int i = tid; i < cnt; i += kSelThreads) {
             const uint32_t k = keys[i];
             for (int j = 0; j < nt; ++j)
-                if (!all[j] && (k >> 10) == pre2[j]) atomicAdd(&lh2[j * kB3 + (k & 1023u)], 1u);
+                if (path[j] == kPathRadix && (k >> 21) == b1[j]) atomicAdd(&lh2[j * kB2 + ((k >> 10) & 2047u)], 1u);
         }
         __syncthreads();
         if (multi) {
             for (int j = 0; j < nt; ++j)
-                if (!all[j]) push_hist(lh2 + j * kB3, gh3 + j * kB3, kB3);
-            row_barrier(ctrl, g.S, gen, status);
+                if (path[j] == kPathRadix) push_hist(lh2 + j * kB2, gh2 + j * kB2, kB2);
+            row_barrier(ctrl, S, gen, status);
             for (int j = 0; j < nt; ++j)
-                if (!all[j]) pull_hist(lh2 + j * kB3, gh3 + j * kB3, kB3);
+                if (path[j] == kPathRadix) pull_hist(lh2 + j * kB2, gh2 + j * kB2, kB2);
+        }
+        uint32_t pre2[2] = {0, 0};
+        for (int j = 0; j < nt; ++j) {
+            if (path[j] != kPathRadix) continue;
+            const Found f = block_find(lh2 + j * kB2, kB2, rem[j], sm);
+            pre2[j] = (b1[j] << 11) | f.bin;
+            rem[j] = f.rem;
+        }
+        for (int i = tid; i < 2 * kB2; i += kSelThreads) lh2[i] = 0u;
+        __syncthreads();
+        for (int i = tid; i < cnt; i += kSelThreads) {
+            const uint32_t k = keys[i];
+            for (int j = 0; j < nt; ++j)
+                if (path[j] == kPathRadix && (k >> 10) == pre2[j]) atomicAdd(&lh2[j * kB3 + (k & 1023u)], 1u);
+        }
+        __syncthreads();
+        if (multi) {
+            for (int j = 0; j < nt; ++j)
+                if (path[j] == kPathRadix) push_hist(lh2 + j * kB3, gh3 + j * kB3, kB3);
+            row_barrier(ctrl, S, gen, status);
+            for (int j = 0; j < nt; ++j)
+                if (path[j] == kPathRadix) pull_hist(lh2 + j * kB3, gh3 + j * kB3, kB3);
         }
         for (int j = 0; j < nt; ++j) {
-            if (all[j]) continue;
+            if (path[j] != kPathRadix) continue;
             const Found f = block_find(lh2 + j * kB3, kB3, rem[j], sm);
             T[j] = (pre2[j] << 10) | f.bin;
-            need[j] = f.rem;                   // entries equal to T that are taken, row-wide
+            need[j] = f.rem;
         }
     }
 
-    // ---- counts of > T and == T per wave (each wave owns a contiguous span)
-    int span = (cnt + kSelWaves - 1) / kSelWaves;
-    span = (span + kWave - 1) & ~(kWave - 1);
-    const int w0 = min(cnt, wave * span), w1 = min(cnt, w0 + span);
-    uint32_t* wcnt = sm + 32;                   // [2][16][gt, eq]
+    // ---- list path, part 2: resolve T and every chunk's counts from the list
+    if (any_list) {
+        row_barrier(ctrl, S, gen, status);
+        for (int i = tid; i < S * 2; i += kSelThreads) {
+            const int j = i & 1;
+            cnts[i * 2 + 0] = (j < nt && path[j] == kPathList) ? ld_rlx(&gtab[i]) : 0u;
+            cnts[i * 2 + 1] = 0u;
+        }
+        for (int j = 0; j < nt; ++j) {
+            if (path[j] != kPathList) continue;
+            constexpr int R = kCandCap / kSelThreads;
+            uint64_t ent[R];
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const int e = tid + r * kSelThreads;
+                ent[r] = (e < (int)C[j]) ? ld_rlx_u64(&glist[(size_t)j * kCandCap + e]) : 0ull;
+            }
+            for (int i = tid; i < kB2; i += kSelThreads) lh2[i] = 0u;
+            __syncthreads();
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const uint32_t k = (uint32_t)ent[r];
+                if (k) atomicAdd(&lh2[(k >> 10) & 2047u], 1u);
+            }
+            __syncthreads();
+            const Found f2 = block_find(lh2, kB2, rem[j], sm);
+            for (int i = tid; i < kB3; i += kSelThreads) lh2[i] = 0u;
+            __syncthreads();
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const uint32_t k = (uint32_t)ent[r];
+                if (k && ((k >> 10) & 2047u) == f2.bin) atomicAdd(&lh2[k & 1023u], 1u);
+            }
+            __syncthreads();
+            const Found f3 = block_find(lh2, kB3, f2.rem, sm);
+            T[j] = (b1[j] << 21) | (f2.bin << 10) | f3.bin;
+            need[j] = f3.rem;
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const uint32_t k = (uint32_t)ent[r];
+                if (!k) continue;
+                const int s = (int)((uint32_t)(ent[r] >> 32) / (uint32_t)g.chunk);
+                if (k > T[j]) atomicAdd(&cnts[(s * 2 + j) * 2 + 0], 1u);
+                else if (k == T[j]) atomicAdd(&cnts[(s * 2 + j) * 2 + 1], 1u);
+            }
+        }
+        __syncthreads();
+    }
+
+    // ---- per-wave counts of keys > T and == T (keys reloaded into registers:
+    // their first live range ended before the list resolution, which needs the
+    // registers for list entries)
+    load_kreg();
+    uint32_t* wcnt = sm + 64;                   // [2][16][gt, eq]
     for (int j = 0; j < nt; ++j) {
         uint32_t gt = 0, eq = 0;
-        for (int i = w0 + lane; i < w1; i += kWave) {
-            const uint32_t k = keys[i];
-            gt += k > T[j];
-            eq += (k == T[j]) && k != 0u;
+        const uint32_t Tj = T[j];
+#pragma unroll
+        for (int t = 0; t < kMaxSteps; ++t) {
+            if (t >= nst) break;
+            const uint32_t kv[4] = {kreg[t].x, kreg[t].y, kreg[t].z, kreg[t].w};
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                gt += (uint32_t)__popcll(__ballot(kv[u] > Tj));
+                eq += (uint32_t)__popcll(__ballot(kv[u] == Tj && kv[u] != 0u));
+            }
         }
-        gt = wave_sum(gt);
-        eq = wave_sum(eq);
         if (lane == 0) {
             wcnt[(j * kSelWaves + wave) * 2 + 0] = gt;
             wcnt[(j * kSelWaves + wave) * 2 + 1] = eq;
         }
     }
     __syncthreads();
-    if (tid < nt) {
-        uint32_t gt = 0, eq = 0;
-        for (int w = 0; w < kSelWaves; ++w) {
-            gt += wcnt[(tid * kSelWaves + w) * 2 + 0];
-            eq += wcnt[(tid * kSelWaves + w) * 2 + 1];
+
+    // ---- targets resolved without the list exchange their per-chunk counts
+    if (any_other) {
+        if (tid < nt && path[tid] != kPathList) {
+            uint32_t gt = 0, eq = 0;
+            for (int w = 0; w < kSelWaves; ++w) {
+                gt += wcnt[(tid * kSelWaves + w) * 2 + 0];
+                eq += wcnt[(tid * kSelWaves + w) * 2 + 1];
+            }
+            if (multi) {
+                st_rlx(&gcnt[(split * 2 + tid) * 2 + 0], gt);
+                st_rlx(&gcnt[(split * 2 + tid) * 2 + 1], eq);
+            } else {
+                cnts[tid * 2 + 0] = gt;
+                cnts[tid * 2 + 1] = eq;
+            }
         }
         if (multi) {
-            st_rlx(&gcnt[(split * 2 + tid) * 2 + 0], gt);
-            st_rlx(&gcnt[(split * 2 + tid) * 2 + 1], eq);
+            row_barrier(ctrl, S, gen, status);
+            for (int i = tid; i < S * 2; i += kSelThreads) {
+                const int j = i & 1;
+                if (j < nt && path[j] != kPathList) {
+                    cnts[i * 2 + 0] = ld_rlx(&gcnt[i * 2 + 0]);
+                    cnts[i * 2 + 1] = ld_rlx(&gcnt[i * 2 + 1]);
+                }
+            }
         }
-        sm[16 + tid * 2 + 0] = gt;
-        sm[16 + tid * 2 + 1] = eq;
+        __syncthreads();
     }
-    if (multi) row_barrier(ctrl, g.S, gen, status);
-    else __syncthreads();
 
-    // ---- offsets: this chunk's output base and its share of the == T entries.
-    // The counts of all chunks are staged in LDS by one lane each (the pass-2/3
-    // histogram space is free now), so no lane walks them with serial loads.
-    uint32_t* cnts = lh2;                       // [S][2 targets][gt, eq]
-    if (multi) {
-        for (int i = tid; i < g.S * 4; i += kSelThreads) cnts[i] = ld_rlx(&gcnt[i]);
-    } else if (tid < 4) {
-        cnts[tid] = sm[16 + tid];
-    }
-    __syncthreads();
+    // ---- offsets: this chunk's output base and its share of the == T entries
     uint32_t* wbase = sm + 128;                 // [2][16][base, eq_before]
-    uint32_t* tinfo = sm + 192;                 // [2][take_eq, total_sel]
+    uint32_t* tinfo = sm + 192;                 // [2][take_eq, total_sel, eq_chunk, -]
     if (tid < nt) {
         const int j = tid;
-        uint32_t off = 0, eq_before = 0, total_sel = 0, my_take = 0;
-        for (int s = 0; s < g.S; ++s) {
+        uint32_t off = 0, eq_before = 0, total_sel = 0, my_take = 0, my_eq = 0;
+        for (int s = 0; s < S; ++s) {
             const uint32_t gt = cnts[(s * 2 + j) * 2 + 0], eq = cnts[(s * 2 + j) * 2 + 1];
             const uint32_t left = need[j] > eq_before ? need[j] - eq_before : 0u;
             const uint32_t take = eq < left ? eq : left;
             if (s < split) off += gt + take;
-            if (s == split) my_take = take;
+            if (s == split) {
+                my_take = take;
+                my_eq = eq;
+            }
             total_sel += gt + take;
             eq_before += eq;
         }
@@ -373,38 +558,80 @@ __global__ void __launch_bounds__(kSelThreads) k_select(Src src, SelDev g, SelTg
             wb += gt + (eq < left ? eq : left);
             web += eq;
         }
-        tinfo[j * 2 + 0] = my_take;
-        tinfo[j * 2 + 1] = total_sel;
+        tinfo[j * 4 + 0] = my_take;
+        tinfo[j * 4 + 1] = total_sel;
+        tinfo[j * 4 + 2] = my_eq;
     }
     __syncthreads();
 
-    // ---- compaction in position order
-    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+    // ---- compaction in index order, 4 keys per lane per step
     for (int j = 0; j < nt; ++j) {
         const SelTgt& t = j ? t1 : t0;
-        const uint32_t take_eq = tinfo[j * 2 + 0];
+        const uint32_t Tj = T[j];
+        const uint32_t take_eq = tinfo[j * 4 + 0];
+        const bool eq_all = take_eq >= tinfo[j * 4 + 2];
         uint32_t run_sel = wbase[(j * kSelWaves + wave) * 2 + 0];
         uint32_t run_eq = wbase[(j * kSelWaves + wave) * 2 + 1];
         int32_t* out_idx = t.idx + row * t.stride;
         float* out_sc = t.score ? t.score + row * t.stride : nullptr;
-        for (int i0 = w0; i0 < w1; i0 += kWave) {
-            const int i = i0 + lane;
-            const uint32_t k = (i < w1) ? keys[i] : 0u;
-            const bool is_eq = (i < w1) && k == T[j] && k != 0u;
-            const uint64_t m_eq = __ballot(is_eq);
-            const uint32_t r_eq = run_eq + (uint32_t)__popcll(m_eq & lt_mask);
-            const bool sel = (i < w1) && (k > T[j] || (is_eq && r_eq < take_eq));
-            const uint64_t m_sel = __ballot(sel);
-            const uint32_t slot = run_sel + (uint32_t)__popcll(m_sel & lt_mask);
-            if (sel && slot < M[j]) {                   // the bound holds whenever the counts agree
-                out_idx[slot] = src.position(row, begin + i);
-                if (out_sc) out_sc[slot] = key_score(k);
+        // Entry (lane, u) of a step has index i0 + 4*lane + u; its rank among the
+        // step's selected entries is the count over all u of selected entries in
+        // lower lanes (one ballot per u, counted with mbcnt) plus those at u' < u
+        // in its own lane - no cross-lane data movement.
+#pragma unroll
+        for (int t = 0; t < kMaxSteps; ++t) {
+            if (t >= nst) break;
+            const int ib = w0 + t * kPadTo + 4 * lane;
+            const uint32_t kv[4] = {kreg[t].x, kreg[t].y, kreg[t].z, kreg[t].w};
+            uint32_t selm = 0, below = 0, total = 0;
+            if (eq_all || take_eq == 0) {
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const bool s = kv[u] > Tj || (eq_all && kv[u] == Tj && kv[u] != 0u);
+                    const uint64_t m = __ballot(s);
+                    selm |= (uint32_t)s << u;
+                    below += lanes_below(m);
+                    total += (uint32_t)__popcll(m);
+                }
+            } else {                            // ties at T split inside this chunk: rank them in index order
+                uint32_t eqm = 0, eq_below = 0, eq_total = 0;
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const bool e = kv[u] == Tj && kv[u] != 0u;
+                    const uint64_t m = __ballot(e);
+                    eqm |= (uint32_t)e << u;
+                    eq_below += lanes_below(m);
+                    eq_total += (uint32_t)__popcll(m);
+                }
+                uint32_t r = run_eq + eq_below;
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    bool s = kv[u] > Tj;
+                    if ((eqm >> u) & 1u) {
+                        s = r < take_eq;
+                        ++r;
+                    }
+                    const uint64_t m = __ballot(s);
+                    selm |= (uint32_t)s << u;
+                    below += lanes_below(m);
+                    total += (uint32_t)__popcll(m);
+                }
+                run_eq += eq_total;
             }
-            run_eq += (uint32_t)__popcll(m_eq);
-            run_sel += (uint32_t)__popcll(m_sel);
+            uint32_t slot = run_sel + below;
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                if ((selm >> u) & 1u) {
+                    if (slot < M[j]) {          // the bound holds whenever the counts agree
+                        out_idx[slot] = src.position(row, begin + ib + u);
+                        if (out_sc) out_sc[slot] = key_score(kv[u]);
+                    }
+                    ++slot;
+                }
+            run_sel += total;
         }
-        if (split == g.S - 1) {
-            for (uint32_t s = tinfo[j * 2 + 1] + tid; s < M[j]; s += kSelThreads) {
+        if (split == S - 1) {
+            for (uint32_t s = tinfo[j * 4 + 1] + tid; s < M[j]; s += kSelThreads) {
                 out_idx[s] = -1;
                 if (out_sc) out_sc[s] = __uint_as_float(0x7FC00000u);
             }
@@ -416,12 +643,15 @@ __global__ void __launch_bounds__(kSelThreads) k_select(Src src, SelDev g, SelTg
         __syncthreads();
         if (tid == 0) {
             const uint32_t old = add_rlx(exitc, 1u);
-            sm[0] = (old == (uint32_t)g.S - 1) ? 1u : 0u;
+            sm[0] = (old == (uint32_t)S - 1) ? 1u : 0u;
         }
         __syncthreads();
         if (sm[0]) {
-            for (int i = tid; i < kB1 + 2 * kB2 + 2 * kB3; i += kSelThreads) st_rlx(&gh1[i], 0u);
+            const int nz = any_radix ? kB1 + 2 * kB2 + 2 * kB3 : kB1;
+            for (int i = tid; i < nz; i += kSelThreads) st_rlx(&gh1[i], 0u);
             if (tid == 0) {
+                st_rlx(&llen[0], 0u);
+                st_rlx(&llen[1], 0u);
                 st_rlx(ctrl, 0u);
                 st_rlx(exitc, 0u);
             }
@@ -437,6 +667,7 @@ int plan_select(int64_t rows, int64_t n, int32_t min_chunk, SelPlan* out) {
     if (rows < 0 || n < 1 || n >= (int64_t(1) << 31)) return fail(INVALID, "select: n must be in [1, 2^31)");
     int64_t cap = (int64_t)(di.max_lds / 4) - kLdsFixedWords;
     cap = cap / 1024 * 1024;
+    if (di.num_cus > kMaxS) return fail(INVALID, "select: more CUs than the kernel's chunk table holds");
     if (cap > kMaxChunk) cap = kMaxChunk;
     if (cap < 1024) return fail(INVALID, "select: device LDS too small");
     const int64_t s_min = (n + cap - 1) / cap;
@@ -458,9 +689,10 @@ int plan_select(int64_t rows, int64_t n, int32_t min_chunk, SelPlan* out) {
     if (rows > 0 && p.rows_per_launch > rows) p.rows_per_launch = (int32_t)rows;
     if (p.rows_per_launch < 1) p.rows_per_launch = 1;
     p.launches = rows > 0 ? (int32_t)((rows + p.rows_per_launch - 1) / p.rows_per_launch) : 0;
-    p.row_words = kRowFixed + 4 * (int32_t)S;
+    p.row_words = kRowHdr + kB1 + 2 * kB2 + 2 * kB3 + 6 * (int32_t)S + 2 * 2 * kCandCap;
     p.row_words = (p.row_words + 63) / 64 * 64;
-    p.lds_bytes = (size_t)(chunk + kLdsFixedWords) * 4;
+    p.chunk_pad = (int32_t)((chunk + kPadTo - 1) / kPadTo * kPadTo);
+    p.lds_bytes = (size_t)(p.chunk_pad + kLdsFixedWords) * 4;
     p.ws_bytes = (size_t)(kWsHeaderWords + (size_t)p.rows_per_launch * p.row_words) * 4;
     *out = p;
     return OK;
@@ -488,6 +720,7 @@ int launch_rows(const SelPlan& p, const Src& src, const SelOutput* out, int nt, 
     g.n = p.n;
     g.S = p.S;
     g.chunk = p.chunk;
+    g.chunk_pad = p.chunk_pad;
     g.nt = nt;
     g.row_words = p.row_words;
     g.ws = reinterpret_cast<uint32_t*>(ws);
