@@ -116,6 +116,8 @@ int check_attn(const uint16_t* q, int32_t H, int32_t d, const uint8_t* kc, const
     if (!aligned(kc, 16) || !aligned(vc, 16) || cs % 16 != 0)
         return fail(INVALID, w + ": KV code rows must be 16-byte aligned");
     if (!aligned(q, 16)) return fail(INVALID, w + ": query must be 16-byte aligned");
+    if (!aligned(ks, 8) || !aligned(vs, 8) || ss % 8 != 0)
+        return fail(INVALID, w + ": KV scale rows must be 8-byte aligned");
     return OK;
 }
 

@@ -1,30 +1,40 @@
 // Sparse softmax attention over gathered FP4 KV rows on gfx950 matrix cores.
 //
 // One query row (all H <= 16 heads, which share one KV head and one position
-// list) is split over NS workgroups of 4 waves; each wave walks blocks of 32
-// positions of its slice. Per block, a wave:
-//   1. gathers, per lane, the K code bytes and scales it feeds to the matrix
-//      core (16 contiguous code bytes of one position) and the V code dword /
-//      scale of 8 positions, straight from HBM;
-//   2. dequantizes in registers: the FP4 pairs are widened to f16 with the
-//      hardware convert at unit scale (exact), then multiplied by the E4M3
-//      scale as a packed f16 product (E2M1 x E4M3 has at most 6 significant
-//      bits and lies in [2^-10, 2688], so it is exact in f16);
-//   3. S^T = K_hat Q^T with 8 MFMA 16x16x32 f16 (M = positions, N = heads,
+// list) is split over NS workgroups of kAttnWaves waves; each wave walks
+// blocks of 32 positions of its slice, with the next block's gathers (and the
+// position list of the block after it) in flight while the current block is
+// computed. Per block, a wave:
+//   1. gathers, with 16-byte loads, the 64 K code bytes and 64 V code bytes of
+//      each of its 32 positions (4 lanes per position and plane) and the
+//      position's 8 + 8 E4M3 scale bytes, straight from HBM;
+//   2. stages the V codes and all scales in its own LDS area, from which each
+//      lane reads the bytes its matrix-core operands need;
+//   3. dequantizes in registers: the FP4 pairs are widened to f16 with the
+//      hardware convert at unit scale (exact - the instruction applies only
+//      the exponent of its scale operand), then multiplied by the E4M3 scale
+//      as a packed f16 product (E2M1 x E4M3 has at most 6 significant bits
+//      and lies in [2^-10, 2688], so it is exact in f16);
+//   4. S^T = K_hat Q^T with 8 MFMA 16x16x32 f16 (M = positions, N = heads,
 //      contraction over the 128 channels in a lane-friendly channel order);
-//   4. an online softmax per head on the accumulator registers;
-//   5. out^T += V_hat^T P^T with 8 more MFMAs. The contraction index of this
-//      product is ordered so that each lane's softmax weights are exactly the
-//      ones it holds from step 3 (no cross-lane movement), and output channel
-//      8m + t of MFMA t lands in accumulator row m, so each lane dequantizes
-//      only the 8 channels 8n..8n+7 of its 8 positions.
+//   5. an online softmax per head on the accumulator registers;
+//   6. out^T += V_hat^T P^T. The contraction index of this product is ordered
+//      so that each lane's softmax weights are exactly the ones it holds from
+//      step 4 (no cross-lane movement), and output channel 8m + t of MFMA t
+//      lands in accumulator row m, so each lane dequantizes only the 8
+//      channels 8n..8n+7 of its 8 positions.
 // The query is converted to f16 once (exact for |q| in [2^-14, 65504]; smaller
 // magnitudes round to f16 subnormals, an absolute error below 2^-25). Each
 // softmax weight p (fp32) enters the matrix core as two f16 terms hi + lo
 // (about 22 significant bits together); accumulation is fp32.
-// The 4 waves are merged through LDS; the NS slices of a row are written to
-// the workspace and merged in slice order by a second, small kernel, so the
-// result does not depend on scheduling.
+//
+// The waves of a workgroup are merged through LDS in wave order. With NS > 1
+// each workgroup writes its (max, sum, acc) state to the workspace with
+// device-coherent stores, and the last workgroup of the row to arrive (one
+// device-scope counter per row) merges the NS states in slice order and
+// writes the output, then resets the counter. Workgroups are numbered row
+// fastest, so all slices of a row run on the same XCD whenever the row count
+// is a multiple of 8. The result does not depend on scheduling.
 #include "device.hpp"
 #include "internal.hpp"
 
@@ -33,20 +43,27 @@ namespace csa2 {
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kAttnThreads = 256;
-constexpr int kAttnWaves = 4;
+constexpr int kAttnWaves = 8;
+constexpr int kAttnThreads = kAttnWaves * kWave;
 constexpr int kBlk = 32;
 constexpr int kMaxHeads = 16;
 constexpr int kD = 128;
-constexpr int kAttnWsHeader = 64;               // words; [0] device status word
-constexpr int kAttnTargetBlocks = 512;
-constexpr int kMaxSplits = 16;                  // slices per query row (bounded for the merge)
+constexpr int kAttnWsHeader = 64;               // words; [0] device status word (unused here)
+constexpr int kAttnTargetGroups = 256;          // one workgroup per CU of a 256-CU part
+constexpr int kMaxSplits = 16;
+constexpr int kPartFloats = kMaxHeads * kD + 2 * kMaxHeads;   // per (row, slice): acc [16][128], (m, l) [16][2]
+constexpr int kVRowBytes = 80;                  // staged V row: 64 code bytes + pad (conflict-free dword reads)
+constexpr int kMergeStride = kD + 4;
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr uint32_t kRsrcWord3 = 0x00020000u;    // raw buffer resource (byte-addressed, 32-bit data format)
+constexpr int kCoherent = 16;                   // buffer cache policy sc1: device-coherent access
 
 static int attn_splits(int64_t rows, int32_t K) {
     const int64_t nblk = (K + kBlk - 1) / kBlk;
-    int64_t ns = (kAttnTargetBlocks + rows - 1) / (rows > 0 ? rows : 1);
+    int64_t ns = (kAttnTargetGroups + rows - 1) / (rows > 0 ? rows : 1);
     const int64_t max_ns = (nblk + kAttnWaves - 1) / kAttnWaves;   // at least one block per wave
     if (ns > max_ns) ns = max_ns;
     if (ns > kMaxSplits) ns = kMaxSplits;
@@ -54,12 +71,15 @@ static int attn_splits(int64_t rows, int32_t K) {
     return (int)ns;
 }
 
+__host__ __device__ inline int64_t counter_words(int64_t rows) { return (rows + 63) / 64 * 64; }
+
 size_t attn_workspace_bytes(int64_t rows, int32_t H, int32_t d, int32_t K) {
-    const int ns = attn_splits(rows, K);
-    const size_t part = (size_t)rows * ns * (size_t)kMaxHeads * (kD + 2);
     (void)H;
     (void)d;
-    return (kAttnWsHeader + part) * 4;
+    const int ns = attn_splits(rows, K);
+    size_t words = kAttnWsHeader;
+    if (ns > 1) words += (size_t)counter_words(rows) + (size_t)rows * ns * kPartFloats;
+    return words * 4;
 }
 
 // 8 FP4 codes (one dword, channel 2j in the low nibble of byte j) times a scale -> 8 f16.
@@ -74,178 +94,281 @@ __device__ __forceinline__ f16x8 dq8(uint32_t w, _Float16 s) {
 
 __device__ __forceinline__ _Float16 scale_f16(uint32_t b) { return (_Float16)e4m3_to_f32(b); }
 
+struct KvBase {
+    const uint8_t *kc, *ks, *vc, *vs;           // this sequence's planes
+    int64_t cs, ss;
+};
+
+// One lane's loads for a block of 32 positions. Lane (n, g) holds bytes
+// 16g..16g+15 of the K and V code rows of positions n and 16 + n; lanes < 32
+// hold the K and V scale bytes of position `lane`.
+struct BlockRaw {
+    uint4 k[2], v[2];
+    uint2 ks, vs;
+    int32_t pos;                                // lanes < 32: position of entry `lane`, -1 if none
+};
+
+struct Stage {                                  // one wave's LDS staging area
+    uint8_t v[kBlk][kVRowBytes];
+    uint8_t ks[kBlk][8];
+    uint8_t vs[kBlk][8];
+};
+
+struct MergeArea {
+    float acc[kAttnWaves][kMaxHeads][kMergeStride];
+    float m[kAttnWaves][kMaxHeads];
+    float l[kAttnWaves][kMaxHeads];
+};
+
+union AttnLds {
+    Stage st[kAttnWaves];
+    MergeArea mg;
+};
+
+// Raw position-list entry of lane `lane` of block `blk` (lanes >= 32 and
+// entries past K read a clamped in-range entry and are discarded later). The
+// load is unconditional and its value is checked only where it is consumed,
+// so it can stay in flight.
+__device__ __forceinline__ int32_t load_pos(const int32_t* ip, int blk, int K, int lane) {
+    return ip[min(blk * kBlk + (lane & (kBlk - 1)), K - 1)];
+}
+
+// Issue the gathers of one block. Every load is unconditional: an entry that
+// is padding (past K, negative or >= N) reads position 0 of the sequence
+// instead, and its scales are zeroed when the block is staged, so it
+// dequantizes to exact zeros and is masked out of the softmax.
+__device__ __forceinline__ void gather(BlockRaw& r, int32_t raw_pos, int blk, int K, const KvBase& kv, int64_t N,
+                                       int lane, int n, int g) {
+    const bool ok = lane < kBlk && blk * kBlk + lane < K && raw_pos >= 0 && (int64_t)raw_pos < N;
+    const int32_t safe = ok ? raw_pos : 0;
+    const int32_t p0 = __shfl(safe, n), p1 = __shfl(safe, 16 + n);
+    r.k[0] = *reinterpret_cast<const uint4*>(kv.kc + p0 * kv.cs + 16 * g);
+    r.v[0] = *reinterpret_cast<const uint4*>(kv.vc + p0 * kv.cs + 16 * g);
+    r.k[1] = *reinterpret_cast<const uint4*>(kv.kc + p1 * kv.cs + 16 * g);
+    r.v[1] = *reinterpret_cast<const uint4*>(kv.vc + p1 * kv.cs + 16 * g);
+    r.ks = *reinterpret_cast<const uint2*>(kv.ks + safe * kv.ss);
+    r.vs = *reinterpret_cast<const uint2*>(kv.vs + safe * kv.ss);
+    r.pos = ok ? raw_pos : -1;
+}
+
+struct WaveState {
+    float m, l;                                 // head n (same in the 4 lane groups), log2 units
+    f32x4 acc[8];                               // acc[t][i] = unnormalized out[n][8*(4g+i) + t]
+};
+
+__device__ __forceinline__ void attend_block(WaveState& st, const BlockRaw& r, Stage& sg, const f16x8 (&qb)[4],
+                                             float sl2, int lane, int n, int g) {
+    // ---- stage V codes and scales; this wave alone uses `sg`, and its LDS
+    // accesses complete in order, so no barrier is needed
+    *reinterpret_cast<uint4*>(&sg.v[n][16 * g]) = r.v[0];
+    *reinterpret_cast<uint4*>(&sg.v[16 + n][16 * g]) = r.v[1];
+    if (lane < kBlk) {
+        const bool ok = r.pos >= 0;
+        *reinterpret_cast<uint2*>(&sg.ks[lane][0]) = ok ? r.ks : make_uint2(0, 0);
+        *reinterpret_cast<uint2*>(&sg.vs[lane][0]) = ok ? r.vs : make_uint2(0, 0);
+    }
+    __builtin_amdgcn_wave_barrier();
+    // positions of this lane's softmax columns: 4g + i (i < 4), 16 + 4g + i - 4 (i >= 4)
+    uint32_t vw[8], vsb[8];
+    bool valid[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int p = (i < 4) ? (4 * g + i) : (16 + 4 * g + i - 4);
+        vw[i] = *reinterpret_cast<const uint32_t*>(&sg.v[p][4 * n]);
+        vsb[i] = sg.vs[p][n >> 1];
+        valid[i] = __shfl(r.pos, p) >= 0;
+    }
+    const uint32_t k0s = *reinterpret_cast<const uint16_t*>(&sg.ks[n][2 * g]);
+    const uint32_t k1s = *reinterpret_cast<const uint16_t*>(&sg.ks[16 + n][2 * g]);
+
+    // ---- S^T = K_hat Q^T
+    f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+        const uint32_t ksc = mb == 0 ? k0s : k1s;
+        const _Float16 s_lo = scale_f16(ksc & 0xFFu), s_hi = scale_f16(ksc >> 8);
+        const uint32_t w[4] = {r.k[mb].x, r.k[mb].y, r.k[mb].z, r.k[mb].w};
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+            sacc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(dq8(w[s], s < 2 ? s_lo : s_hi), qb[s], sacc[mb], 0, 0, 0);
+    }
+
+    // ---- online softmax for head n over the 8 positions this lane holds
+    float lg[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float sv = (i < 4) ? sacc[0][i] : sacc[1][i - 4];
+        lg[i] = valid[i] ? sv * sl2 : -INFINITY;
+    }
+    float mx = lg[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) mx = fmaxf(mx, lg[i]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(st.m, mx);
+    f16x8 pb_hi, pb_lo;                         // p = hi + lo, both f16: ~22 significant bits
+    float psum = 0.f, alpha = 1.f;
+    if (m_new != -INFINITY) {
+        alpha = exp2f(st.m - m_new);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float p = exp2f(lg[i] - m_new);
+            const _Float16 hi = (_Float16)p;
+            pb_hi[i] = hi;
+            pb_lo[i] = (_Float16)(p - (float)hi);
+            psum += p;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) pb_hi[i] = pb_lo[i] = (_Float16)0.f;
+    }
+    psum += __shfl_xor(psum, 16);
+    psum += __shfl_xor(psum, 32);
+    st.l = st.l * alpha + psum;
+    st.m = m_new;
+
+    // ---- out^T += V_hat^T P^T: MFMA t covers channels 8m + t
+    f16x2 hv[8][4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const _Float16 sv = scale_f16(vsb[i]);
+        const f16x2 sp = {sv, sv};
+        hv[i][0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(vw[i], 1.0f, 0) * sp;
+        hv[i][1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(vw[i], 1.0f, 1) * sp;
+        hv[i][2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(vw[i], 1.0f, 2) * sp;
+        hv[i][3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(vw[i], 1.0f, 3) * sp;
+    }
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        f16x8 va;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) va[i] = hv[i][t >> 1][t & 1];
+        st.acc[t] = st.acc[t] * alpha;
+        st.acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb_hi, st.acc[t], 0, 0, 0);
+        st.acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb_lo, st.acc[t], 0, 0, 0);
+    }
+}
+
 __global__ void __launch_bounds__(kAttnThreads)
 k_sparse_attn(const uint16_t* __restrict__ q, int32_t rows_per_seq, int32_t H, const uint8_t* __restrict__ k_codes,
               const uint8_t* __restrict__ k_scales, const uint8_t* __restrict__ v_codes,
               const uint8_t* __restrict__ v_scales, int64_t N, int64_t cs, int64_t ss, const int32_t* __restrict__ idx,
               int64_t idx_stride, int32_t K, float scale, float* __restrict__ out, int32_t NS,
               uint32_t* __restrict__ ws, int64_t rows) {
-    __shared__ float s_m[kAttnWaves][kMaxHeads];
-    __shared__ float s_l[kAttnWaves][kMaxHeads];
-    __shared__ float s_acc[kAttnWaves][kMaxHeads][kD + 1];
+    __shared__ AttnLds lds;
+    __shared__ int s_last;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n = lane & 15, g = lane >> 4;
-    const int64_t row = blockIdx.x / NS;
-    const int split = blockIdx.x - (int)(row * NS);
+    const int64_t row = (int64_t)blockIdx.x % rows;            // row fastest: a row's slices share an XCD
+    const int split = (int)((int64_t)blockIdx.x / rows);
     const int64_t seq = row / rows_per_seq;
     const int nblk = (K + kBlk - 1) / kBlk;
-    const int bps = (nblk + NS - 1) / NS;              // blocks per slice
+    const int bps = (nblk + NS - 1) / NS;                       // blocks per slice
     const int b0 = split * bps, b1 = min(nblk, b0 + bps);
     const float sl2 = scale * kLog2e;
 
     // query as the B operand of S^T = K_hat Q^T: lane (n, g), k-step s holds
-    // q[head n][channel 32g + 8s + i], i = 0..7
+    // q[head n][channel 32g + 8s + i], i = 0..7; heads >= H read head H - 1
+    // and are zeroed when converted
+    uint4 qraw[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+        qraw[s] = *reinterpret_cast<const uint4*>(q + (row * H + min(n, H - 1)) * (int64_t)kD + 32 * g + 8 * s);
     f16x8 qb[4];
+    auto convert_q = [&]() {
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-        uint4 raw = make_uint4(0, 0, 0, 0);
-        if (n < H) raw = *reinterpret_cast<const uint4*>(q + (row * H + n) * (int64_t)kD + 32 * g + 8 * s);
-        const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+        for (int s = 0; s < 4; ++s) {
+            const uint32_t w[4] = {qraw[s].x, qraw[s].y, qraw[s].z, qraw[s].w};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            qb[s][2 * i + 0] = (_Float16)bf16_bits_to_f32(w[i] & 0xFFFFu);
-            qb[s][2 * i + 1] = (_Float16)bf16_bits_to_f32(w[i] >> 16);
+            for (int i = 0; i < 4; ++i) {
+                qb[s][2 * i + 0] = n < H ? (_Float16)bf16_bits_to_f32(w[i] & 0xFFFFu) : (_Float16)0.f;
+                qb[s][2 * i + 1] = n < H ? (_Float16)bf16_bits_to_f32(w[i] >> 16) : (_Float16)0.f;
+            }
         }
-    }
+    };
 
     const int32_t* ip = idx + row * idx_stride;
-    const uint8_t* kc_base = k_codes + seq * N * cs;
-    const uint8_t* ks_base = k_scales + seq * N * ss;
-    const uint8_t* vc_base = v_codes + seq * N * cs;
-    const uint8_t* vs_base = v_scales + seq * N * ss;
+    const KvBase kv{k_codes + seq * N * cs, k_scales + seq * N * ss, v_codes + seq * N * cs,
+                    v_scales + seq * N * ss, cs, ss};
 
-    float m_run = -INFINITY, l_run = 0.f;             // per head n, in log2 units of the scaled logits
-    f32x4 acc[8];
+    WaveState st;
+    st.m = -INFINITY;
+    st.l = 0.f;
 #pragma unroll
-    for (int t = 0; t < 8; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < 8; ++t) st.acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    for (int blk = b0 + wave; blk < b1; blk += kAttnWaves) {
-        const int jb = blk * kBlk;
-        int32_t my_pos = -1;
-        if (lane < kBlk && jb + lane < K) {
-            const int32_t p = ip[jb + lane];
-            my_pos = (p >= 0 && (int64_t)p < N) ? p : -1;
+    // ---- this wave's blocks k = 0 .. nb-1: block first + k*W. Issue order per
+    // step k: position list of block k+2, gathers of block k+1, then the math
+    // of block k - so two blocks of gathers are in flight and no load is waited
+    // for before it is needed. Even and odd blocks use separate registers (the
+    // loop is unrolled by two) and every load in the steady-state loop is
+    // unconditional, so nothing in flight is copied and the compiler's wait
+    // counts stay exact; the last one to three blocks are peeled.
+    const int first = b0 + wave;
+    const int nb = first < b1 ? (b1 - first + kAttnWaves - 1) / kAttnWaves : 0;
+    if (nb > 0) {
+        BlockRaw r0, r1;
+        int32_t p0 = load_pos(ip, first, K, lane);
+        int32_t p1 = load_pos(ip, first + min(1, nb - 1) * kAttnWaves, K, lane);
+        gather(r0, p0, first, K, kv, N, lane, n, g);
+        convert_q();
+        int k = 0;
+        for (; k + 3 < nb; k += 2) {
+            const int bk = first + k * kAttnWaves;
+            p0 = load_pos(ip, bk + 2 * kAttnWaves, K, lane);
+            gather(r1, p1, bk + kAttnWaves, K, kv, N, lane, n, g);
+            attend_block(st, r0, lds.st[wave], qb, sl2, lane, n, g);
+            p1 = load_pos(ip, bk + 3 * kAttnWaves, K, lane);
+            gather(r0, p0, bk + 2 * kAttnWaves, K, kv, N, lane, n, g);
+            attend_block(st, r1, lds.st[wave], qb, sl2, lane, n, g);
         }
-        // K rows: positions n and 16 + n of the block; V rows / softmax columns:
-        // positions 4g + i (i < 4) and 16 + 4g + (i - 4) (i >= 4)
-        const int32_t kp0 = __shfl(my_pos, n), kp1 = __shfl(my_pos, 16 + n);
-        int32_t vp[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) vp[i] = __shfl(my_pos, (i < 4) ? (4 * g + i) : (16 + 4 * g + i - 4));
-
-        uint4 kraw[2] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0)};
-        uint32_t ksc[2] = {0, 0};
-        if (kp0 >= 0) {
-            kraw[0] = *reinterpret_cast<const uint4*>(kc_base + kp0 * cs + 16 * g);
-            ksc[0] = (uint32_t)ks_base[kp0 * ss + 2 * g] | ((uint32_t)ks_base[kp0 * ss + 2 * g + 1] << 8);
-        }
-        if (kp1 >= 0) {
-            kraw[1] = *reinterpret_cast<const uint4*>(kc_base + kp1 * cs + 16 * g);
-            ksc[1] = (uint32_t)ks_base[kp1 * ss + 2 * g] | ((uint32_t)ks_base[kp1 * ss + 2 * g + 1] << 8);
-        }
-        uint32_t vraw[8], vsc[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            vraw[i] = 0;
-            vsc[i] = 0;
-            if (vp[i] >= 0) {
-                vraw[i] = *reinterpret_cast<const uint32_t*>(vc_base + vp[i] * cs + 4 * n);
-                vsc[i] = vs_base[vp[i] * ss + (n >> 1)];
-            }
-        }
-
-        // ---- S^T = K_hat Q^T
-        f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
-            const _Float16 s_lo = scale_f16(ksc[mb] & 0xFFu), s_hi = scale_f16(ksc[mb] >> 8);
-            const uint32_t w[4] = {kraw[mb].x, kraw[mb].y, kraw[mb].z, kraw[mb].w};
-#pragma unroll
-            for (int s = 0; s < 4; ++s)
-                sacc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(dq8(w[s], s < 2 ? s_lo : s_hi), qb[s], sacc[mb], 0, 0, 0);
-        }
-
-        // ---- online softmax for head n over the 8 positions this lane holds
-        float lg[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const float sv = (i < 4) ? sacc[0][i] : sacc[1][i - 4];
-            lg[i] = (vp[i] >= 0) ? sv * sl2 : -INFINITY;
-        }
-        float mx = lg[0];
-#pragma unroll
-        for (int i = 1; i < 8; ++i) mx = fmaxf(mx, lg[i]);
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(m_run, mx);
-        f16x8 pb_hi, pb_lo;                         // p = hi + lo, both f16: ~22 significant bits
-        float psum = 0.f, alpha = 1.f;
-        if (m_new != -INFINITY) {
-            alpha = exp2f(m_run - m_new);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const float p = exp2f(lg[i] - m_new);
-                const _Float16 hi = (_Float16)p;
-                pb_hi[i] = hi;
-                pb_lo[i] = (_Float16)(p - (float)hi);
-                psum += p;
-            }
+        const int bk = first + k * kAttnWaves;
+        const int rem = nb - k;                 // 1, 2 or 3
+        if (rem == 1) {
+            attend_block(st, r0, lds.st[wave], qb, sl2, lane, n, g);
+        } else if (rem == 2) {
+            gather(r1, p1, bk + kAttnWaves, K, kv, N, lane, n, g);
+            attend_block(st, r0, lds.st[wave], qb, sl2, lane, n, g);
+            attend_block(st, r1, lds.st[wave], qb, sl2, lane, n, g);
         } else {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) pb_hi[i] = pb_lo[i] = (_Float16)0.f;
-        }
-        psum += __shfl_xor(psum, 16);
-        psum += __shfl_xor(psum, 32);
-        l_run = l_run * alpha + psum;
-        m_run = m_new;
-
-        // ---- out^T += V_hat^T P^T: MFMA t covers channels 8m + t
-        f16x2 hv[8][4];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const _Float16 sv = scale_f16(vsc[i]);
-            const f16x2 sp = {sv, sv};
-            hv[i][0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(vraw[i], 1.0f, 0) * sp;
-            hv[i][1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(vraw[i], 1.0f, 1) * sp;
-            hv[i][2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(vraw[i], 1.0f, 2) * sp;
-            hv[i][3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(vraw[i], 1.0f, 3) * sp;
-        }
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            f16x8 va;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) va[i] = hv[i][t >> 1][t & 1];
-            acc[t] = acc[t] * alpha;
-            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb_hi, acc[t], 0, 0, 0);
-            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb_lo, acc[t], 0, 0, 0);
+            p0 = load_pos(ip, bk + 2 * kAttnWaves, K, lane);
+            gather(r1, p1, bk + kAttnWaves, K, kv, N, lane, n, g);
+            attend_block(st, r0, lds.st[wave], qb, sl2, lane, n, g);
+            gather(r0, p0, bk + 2 * kAttnWaves, K, kv, N, lane, n, g);
+            attend_block(st, r1, lds.st[wave], qb, sl2, lane, n, g);
+            attend_block(st, r0, lds.st[wave], qb, sl2, lane, n, g);
         }
     }
 
-    // ---- merge the 4 waves through LDS: lane (n, g) holds out[n][8*(4g+i) + t] in acc[t][i]
+    // ---- merge the waves in wave order (the staging areas are reused)
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        float* dst = &lds.mg.acc[wave][n][8 * (4 * g + i)];
+        *reinterpret_cast<f32x4*>(dst) = f32x4{st.acc[0][i], st.acc[1][i], st.acc[2][i], st.acc[3][i]};
+        *reinterpret_cast<f32x4*>(dst + 4) = f32x4{st.acc[4][i], st.acc[5][i], st.acc[6][i], st.acc[7][i]};
+    }
     if (g == 0) {
-        s_m[wave][n] = m_run;
-        s_l[wave][n] = l_run;
+        lds.mg.m[wave][n] = st.m;
+        lds.mg.l[wave][n] = st.l;
     }
-#pragma unroll
-    for (int t = 0; t < 8; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) s_acc[wave][n][8 * (4 * g + i) + t] = acc[t][i];
     __syncthreads();
 
-    const int h = tid >> 4;                              // this thread's head and 8 channels
-    const int c0 = (tid & 15) * 8;
+    const int h = tid >> 5;                     // this thread's head and 4 channels
+    const int c0 = (tid & 31) * 4;
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kAttnWaves; ++w) M = fmaxf(M, s_m[w][h]);
-    float L = 0.f, o[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int w = 0; w < kAttnWaves; ++w) M = fmaxf(M, lds.mg.m[w][h]);
+    float L = 0.f;
+    f32x4 o = {0.f, 0.f, 0.f, 0.f};
     if (M != -INFINITY) {
 #pragma unroll
         for (int w = 0; w < kAttnWaves; ++w) {
-            const float wt = (s_m[w][h] == -INFINITY) ? 0.f : exp2f(s_m[w][h] - M);
-            L += wt * s_l[w][h];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) o[i] = fmaf(wt, s_acc[w][h][c0 + i], o[i]);
+            const float mw = lds.mg.m[w][h];
+            const float wt = (mw == -INFINITY) ? 0.f : exp2f(mw - M);
+            L += wt * lds.mg.l[w][h];
+            o += wt * *reinterpret_cast<const f32x4*>(&lds.mg.acc[w][h][c0]);
         }
     }
 
@@ -253,86 +376,69 @@ k_sparse_attn(const uint16_t* __restrict__ q, int32_t rows_per_seq, int32_t H, c
     if (NS == 1) {
         if (h < H) {
             const float inv = L > 0.f ? 1.f / L : 0.f;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) orow[h * kD + c0 + i] = o[i] * inv;
+            *reinterpret_cast<f32x4*>(orow + h * kD + c0) = o * inv;
         }
         return;
     }
 
-    // ---- slices -> workspace (plain stores); k_attn_merge combines them in slice order
-    float* part = reinterpret_cast<float*>(ws + kAttnWsHeader);
-    const int64_t pstride = (int64_t)kMaxHeads * (kD + 2);
-    float* mine = part + (row * NS + split) * pstride;
-    *reinterpret_cast<float4*>(mine + h * kD + c0) = make_float4(o[0], o[1], o[2], o[3]);
-    *reinterpret_cast<float4*>(mine + h * kD + c0 + 4) = make_float4(o[4], o[5], o[6], o[7]);
-    if ((tid & 15) == 0) {
-        mine[kMaxHeads * kD + 2 * h + 0] = M;
-        mine[kMaxHeads * kD + 2 * h + 1] = L;
+    // ---- NS > 1: publish this slice's state, the last slice of the row merges
+    uint32_t* ctr = ws + kAttnWsHeader + row;
+    float* part_row = reinterpret_cast<float*>(ws + kAttnWsHeader + counter_words(rows)) + row * NS * kPartFloats;
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(part_row, (short)0, NS * kPartFloats * 4, kRsrcWord3);
+    const int mine = split * kPartFloats * 4;
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o), rs, mine + (h * kD + c0) * 4, 0, kCoherent);
+    if ((tid & 31) == 0) {
+        const f32x2 ml = {M, L};
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, ml), rs,
+                                             mine + (kMaxHeads * kD + 2 * h) * 4, 0, kCoherent);
     }
-}
+    wave_drain();
+    __syncthreads();
+    if (tid == 0) s_last = (add_rlx(ctr, 1u) == (uint32_t)(NS - 1));
+    __syncthreads();
+    if (!s_last) return;
 
-// Merge of the NS slices of each query row (launched after k_sparse_attn on the
-// same stream, so the kernel boundary orders the partials before these reads):
-// out = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s, in slice order.
-__global__ void __launch_bounds__(kAttnThreads)
-k_attn_merge(const uint32_t* __restrict__ ws, int32_t H, int32_t NS, float* __restrict__ out) {
-    const int64_t row = blockIdx.x;
-    const int tid = threadIdx.x;
-    const int h = tid >> 4, c0 = (tid & 15) * 8;
-    if (h >= H) return;
-    const float* part = reinterpret_cast<const float*>(ws + kAttnWsHeader);
-    const int64_t pstride = (int64_t)kMaxHeads * (kD + 2);
-    const float* base = part + row * NS * pstride;
-    float ms[kMaxSplits];
-    float MM = -INFINITY;
+    // slices beyond NS read past the resource's range and return zeros
+    u32x4 pa[kMaxSplits];
+    u32x2 pml[kMaxSplits];
 #pragma unroll
     for (int s = 0; s < kMaxSplits; ++s) {
-        ms[s] = (s < NS) ? base[s * pstride + kMaxHeads * kD + 2 * h] : -INFINITY;
-        MM = fmaxf(MM, ms[s]);
+        pa[s] = __builtin_amdgcn_raw_buffer_load_b128(rs, (s * kPartFloats + h * kD + c0) * 4, 0, kCoherent);
+        pml[s] = __builtin_amdgcn_raw_buffer_load_b64(rs, (s * kPartFloats + kMaxHeads * kD + 2 * h) * 4, 0, kCoherent);
     }
-    float LL = 0.f, oo[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    float MM = -INFINITY;
+#pragma unroll
+    for (int s = 0; s < kMaxSplits; ++s) MM = fmaxf(MM, s < NS ? __uint_as_float(pml[s].x) : -INFINITY);
+    float LL = 0.f;
+    f32x4 oo = {0.f, 0.f, 0.f, 0.f};
     if (MM != -INFINITY) {
-#pragma unroll 4
-        for (int s = 0; s < NS; ++s) {
-            const float* b = base + s * pstride;
-            const float4 a0 = *reinterpret_cast<const float4*>(b + h * kD + c0);
-            const float4 a1 = *reinterpret_cast<const float4*>(b + h * kD + c0 + 4);
-            const float ls = b[kMaxHeads * kD + 2 * h + 1];
-            const float wt = (ms[s] == -INFINITY) ? 0.f : exp2f(ms[s] - MM);
-            LL += wt * ls;
-            oo[0] = fmaf(wt, a0.x, oo[0]);
-            oo[1] = fmaf(wt, a0.y, oo[1]);
-            oo[2] = fmaf(wt, a0.z, oo[2]);
-            oo[3] = fmaf(wt, a0.w, oo[3]);
-            oo[4] = fmaf(wt, a1.x, oo[4]);
-            oo[5] = fmaf(wt, a1.y, oo[5]);
-            oo[6] = fmaf(wt, a1.z, oo[6]);
-            oo[7] = fmaf(wt, a1.w, oo[7]);
+#pragma unroll
+        for (int s = 0; s < kMaxSplits; ++s) {
+            const float ms = __uint_as_float(pml[s].x);
+            const float wt = (s >= NS || ms == -INFINITY) ? 0.f : exp2f(ms - MM);
+            LL += wt * __uint_as_float(pml[s].y);
+            oo += wt * __builtin_bit_cast(f32x4, pa[s]);
         }
     }
-    const float inv = LL > 0.f ? 1.f / LL : 0.f;
-    float* orow = out + row * (int64_t)H * kD + h * kD + c0;
-    *reinterpret_cast<float4*>(orow) = make_float4(oo[0] * inv, oo[1] * inv, oo[2] * inv, oo[3] * inv);
-    *reinterpret_cast<float4*>(orow + 4) = make_float4(oo[4] * inv, oo[5] * inv, oo[6] * inv, oo[7] * inv);
+    if (h < H) {
+        const float inv = LL > 0.f ? 1.f / LL : 0.f;
+        *reinterpret_cast<f32x4*>(orow + h * kD + c0) = oo * inv;
+    }
+    if (tid == 0) st_rlx(ctr, 0u);              // ready for the next launch
 }
 
 int launch_attn(const AttnArgs& a, void* ws, size_t ws_bytes, hipStream_t stream) {
     if (a.rows == 0) return OK;
     const int ns = attn_splits(a.rows, a.K);
     if (ws_bytes < attn_workspace_bytes(a.rows, a.H, a.d, a.K)) return fail(WORKSPACE, "attention workspace too small");
-    hipLaunchKernelGGL(k_sparse_attn, dim3((unsigned)(a.rows * ns)), dim3(kAttnThreads), 0, stream, a.q,
-                       a.rows_per_seq, a.H, a.k_codes, a.k_scales, a.v_codes, a.v_scales, a.N, a.code_stride,
-                       a.scale_stride, a.idx, a.idx_stride, a.K, a.scale, a.out, ns,
-                       reinterpret_cast<uint32_t*>(ws), a.rows);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return hip_fail(e, "launch k_sparse_attn");
-    if (ns > 1) {
-        hipLaunchKernelGGL(k_attn_merge, dim3((unsigned)a.rows), dim3(kAttnThreads), 0, stream,
-                           reinterpret_cast<const uint32_t*>(ws), a.H, ns, a.out);
-        e = hipGetLastError();
-        if (e != hipSuccess) return hip_fail(e, "launch k_attn_merge");
-    }
-    return OK;
+    const int64_t groups = a.rows * ns;
+    if (groups > 0x7FFFFFFFll) return fail(INVALID, "attention: too many query rows");
+    hipLaunchKernelGGL(k_sparse_attn, dim3((unsigned)groups), dim3(kAttnThreads), 0, stream, a.q, a.rows_per_seq,
+                       a.H, a.k_codes, a.k_scales, a.v_codes, a.v_scales, a.N, a.code_stride, a.scale_stride, a.idx,
+                       a.idx_stride, a.K, a.scale, a.out, ns, reinterpret_cast<uint32_t*>(ws), a.rows);
+    const hipError_t e = hipGetLastError();
+    return e == hipSuccess ? OK : hip_fail(e, "launch k_sparse_attn");
 }
 
 }  // namespace csa2

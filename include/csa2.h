@@ -188,7 +188,9 @@ int csa2_topk(const float* scores, int64_t rows, int64_t n, int64_t score_stride
  *   idx        device [B][Q][K] int32 positions; -1 or >= N = padding
  *   out        device [B][Q][H][d] fp32 (output)
  *   ws         workspace of csa2_sparse_attn_workspace_bytes(...) bytes
- * Alignment: code pointers and code_stride_bytes to 16 bytes.
+ * Alignment: code pointers and code_stride_bytes to 16 bytes; scale
+ * pointers and scale_stride_bytes to 8 bytes (each position's 8 K and 8 V
+ * scale bytes are read as one 8-byte word each).
  * Numerics: the query is used in f16 (exact for |q| in [2^-14, 65504]), the
  * dequantized K and V are exact in f16, each softmax weight is carried as
  * two f16 terms (about 22 significant bits), products accumulate in fp32.
