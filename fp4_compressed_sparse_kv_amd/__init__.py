@@ -192,8 +192,9 @@ def index_reindex(q_idx, k_idx, pool, scores=None, stream=None):
     return scores
 
 
-def topk(scores, K, cand=None, idx=None, sel_scores=None, want_scores=False, stream=None):
-    """Top-K positions per row of scores [rows][n] (stride allowed): idx [rows][K] ascending, -1 padded."""
+def topk(scores, K, cand=None, idx=None, sel_scores=None, want_scores=False, stream=None, ws=None):
+    """Top-K positions per row of scores [rows][n] (stride allowed): idx [rows][K] ascending, -1 padded.
+    ws: optional zero-filled uint8 workspace (default: a cached one)."""
     _need_cuda(scores, cand)
     rows, n = scores.shape
     dev = scores.device
@@ -203,7 +204,8 @@ def topk(scores, K, cand=None, idx=None, sel_scores=None, want_scores=False, str
         sel_scores = torch.empty(rows, K, dtype=torch.float32, device=dev)
     nb = ctypes.c_size_t(0)
     _check(lib().csa2_topk_workspace_bytes(rows, n, K, ctypes.byref(nb)), "csa2_topk_workspace_bytes")
-    ws = workspace(nb.value, dev, "topk")
+    if ws is None:
+        ws = workspace(nb.value, dev, "topk")
     _check(lib().csa2_topk(_ptr(scores), rows, n, scores.stride(0), _ptr(cand), K, _ptr(idx), _ptr(sel_scores),
                            _ptr(ws), ws.numel(), _stream(stream)), "csa2_topk")
     return (idx, sel_scores) if want_scores else idx
@@ -250,8 +252,9 @@ class KVCache:
                          None if self.k_idx is None else self.k_idx.data_ptr())
 
 
-def sparse_attn_fp4(q, cache, idx, softmax_scale=None, out=None, stream=None):
-    """Sparse FP4 attention. q [B][Q][H][d] bf16, idx [B][Q][K] int32 -> out [B][Q][H][d] fp32."""
+def sparse_attn_fp4(q, cache, idx, softmax_scale=None, out=None, stream=None, ws=None):
+    """Sparse FP4 attention. q [B][Q][H][d] bf16, idx [B][Q][K] int32 -> out [B][Q][H][d] fp32.
+    ws: optional zero-filled uint8 workspace (default: a cached one)."""
     _need_cuda(q, idx)
     B, Q, H, d = q.shape
     K = idx.shape[-1]
@@ -260,7 +263,8 @@ def sparse_attn_fp4(q, cache, idx, softmax_scale=None, out=None, stream=None):
     scale = 1.0 / math.sqrt(d) if softmax_scale is None else softmax_scale
     nb = ctypes.c_size_t(0)
     _check(lib().csa2_sparse_attn_workspace_bytes(B, Q, H, d, K, ctypes.byref(nb)), "csa2_sparse_attn_workspace_bytes")
-    ws = workspace(nb.value, q.device, "attn")
+    if ws is None:
+        ws = workspace(nb.value, q.device, "attn")
     c = cache.desc()
     _check(lib().csa2_sparse_attn_fp4(_ptr(q), B, Q, H, d, c.k_codes, c.k_scales, c.v_codes, c.v_scales, cache.N,
                                       c.code_stride_bytes, c.scale_stride_bytes, _ptr(idx), K, scale, _ptr(out),

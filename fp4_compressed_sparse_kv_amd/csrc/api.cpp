@@ -217,7 +217,7 @@ int csa2_topk(const float* scores, int64_t rows, int64_t n, int64_t score_stride
     o.score = sel_scores;
     o.stride = K;
     o.M = K;
-    return run_select(p, SRC_SCORES, scan, sc, &o, 1, ws, stream);
+    return run_select(p, SRC_SCORES, scan, sc, &o, 1, ws, static_cast<uint8_t*>(ws) + kCtrlBytes, stream);
 }
 
 int csa2_sparse_attn_workspace_bytes(int32_t B, int32_t Q, int32_t H, int32_t d, int32_t K, size_t* bytes) {
@@ -225,7 +225,7 @@ int csa2_sparse_attn_workspace_bytes(int32_t B, int32_t Q, int32_t H, int32_t d,
     if (!bytes) return fail(INVALID, "csa2_sparse_attn_workspace_bytes: bytes is null");
     if (B < 0 || Q < 0 || H < 1 || H > 16 || d != 128 || K < 1)
         return fail(INVALID, "csa2_sparse_attn_workspace_bytes: bad sizes");
-    *bytes = align_up(attn_workspace_bytes((int64_t)B * Q, H, d, K));
+    *bytes = align_up(kCtrlBytes + attn_data_bytes((int64_t)B * Q, K));
     return OK;
 }
 
@@ -242,7 +242,7 @@ int csa2_sparse_attn_fp4(const uint16_t* q, int32_t B, int32_t Q, int32_t H, int
     if (!idx || !out) return fail(INVALID, "csa2_sparse_attn_fp4: null pointer");
     if (!(softmax_scale > 0.f) || !isfinite(softmax_scale))
         return fail(INVALID, "csa2_sparse_attn_fp4: softmax_scale must be positive and finite");
-    const size_t need = attn_workspace_bytes((int64_t)B * Q, H, d, K);
+    const size_t need = kCtrlBytes + attn_data_bytes((int64_t)B * Q, K);
     if (int e = check_ws(ws, ws_bytes, need, "csa2_sparse_attn_fp4")) return e;
     AttnArgs a;
     a.q = q;
@@ -262,7 +262,7 @@ int csa2_sparse_attn_fp4(const uint16_t* q, int32_t B, int32_t Q, int32_t H, int
     a.K = K;
     a.scale = softmax_scale;
     a.out = out;
-    return launch_attn(a, ws, ws_bytes, stream);
+    return launch_attn(a, ws, static_cast<uint8_t*>(ws) + kCtrlBytes, ws_bytes - kCtrlBytes, stream);
 }
 
 // ------------------------------------------------------------------- plan
@@ -390,6 +390,8 @@ void csa2_plan_destroy(csa2_plan* plan) { delete plan; }
 
 namespace {
 
+// Plan workspace: the shared control region, then the data regions of the
+// Full select, the Reindex select, the pool, the attention and the positions.
 struct PlanLayout {
     SelPlan full, pool;
     size_t off_full = 0, off_pool = 0, off_attn = 0, off_idx = 0, off_poolbuf = 0, total = 0;
@@ -397,18 +399,18 @@ struct PlanLayout {
 
 int plan_layout(const csa2_plan* plan, int32_t B, int64_t N, PlanLayout* lay) {
     if (int e = plan_select(B, N, 1024, &lay->full)) return e;
-    size_t off = 0;
+    size_t off = align_up(kCtrlBytes);
     lay->off_full = off;
-    off += align_up(lay->full.ws_bytes);
+    off += align_up(lay->full.data_bytes);
     if (plan->has_reindex) {
         if (int e = plan_select(B, plan->p.P, 512, &lay->pool)) return e;
         lay->off_pool = off;
-        off += align_up(lay->pool.ws_bytes);
+        off += align_up(lay->pool.data_bytes);
         lay->off_poolbuf = off;
         off += align_up((size_t)B * plan->p.P * 4);
     }
     lay->off_attn = off;
-    off += align_up(attn_workspace_bytes(B, plan->p.H, plan->p.d, plan->p.K));
+    off += align_up(attn_data_bytes(B, plan->p.K));
     lay->off_idx = off;
     off += align_up((size_t)B * plan->p.K * 4);
     lay->total = off;
@@ -479,11 +481,11 @@ int csa2_plan_run_decode(const csa2_plan* plan, const csa2_cache* cache, const c
                 } else {
                     o[0] = SelOutput{idx_dst, nullptr, p.K, p.K};
                 }
-                e = run_select(lay.full, SRC_SCAN, a, none, o, nt, wsb + lay.off_full, stream);
+                e = run_select(lay.full, SRC_SCAN, a, none, o, nt, wsb, wsb + lay.off_full, stream);
             } else {
                 a.pool = pool;
                 o[0] = SelOutput{idx_dst, nullptr, p.K, p.K};
-                e = run_select(lay.pool, SRC_POOL, a, none, o, 1, wsb + lay.off_pool, stream);
+                e = run_select(lay.pool, SRC_POOL, a, none, o, 1, wsb, wsb + lay.off_pool, stream);
             }
             if (e) return e;
             cur_idx = idx_dst;
@@ -507,7 +509,7 @@ int csa2_plan_run_decode(const csa2_plan* plan, const csa2_cache* cache, const c
         at.scale = p.softmax_scale;
         at.out = io[l].out;
         SlotTimer timer(plan, 2 * l + 1, stream);
-        if (int e = launch_attn(at, wsb + lay.off_attn, ws_bytes - lay.off_attn, stream)) return e;
+        if (int e = launch_attn(at, wsb, wsb + lay.off_attn, lay.off_idx - lay.off_attn, stream)) return e;
     }
     if (plan->runs < plan->max_runs) plan->runs += 1;
     return OK;
@@ -519,7 +521,7 @@ int csa2_prefill_workspace_bytes(const csa2_plan* plan, int32_t B, int32_t Q, in
     if (B < 1 || Q < 1 || N < 1) return fail(INVALID, "csa2_prefill_workspace_bytes: sizes must be >= 1");
     SelPlan sp;
     if (int e = plan_select((int64_t)B * Q, N, 1024, &sp)) return e;
-    *bytes = align_up(sp.ws_bytes) + align_up(attn_workspace_bytes((int64_t)B * Q, plan->p.H, plan->p.d, plan->p.K));
+    *bytes = align_up(kCtrlBytes) + align_up(sp.data_bytes) + align_up(attn_data_bytes((int64_t)B * Q, plan->p.K));
     return OK;
 }
 
@@ -538,8 +540,8 @@ int csa2_prefill_full(const csa2_plan* plan, const csa2_cache* cache, const void
     const int64_t rows = (int64_t)B * Q;
     SelPlan sp;
     if (int e = plan_select(rows, N, 1024, &sp)) return e;
-    const size_t sel_bytes = align_up(sp.ws_bytes);
-    const size_t need = sel_bytes + align_up(attn_workspace_bytes(rows, p.H, p.d, p.K));
+    const size_t sel_off = align_up(kCtrlBytes), attn_off = sel_off + align_up(sp.data_bytes);
+    const size_t need = attn_off + align_up(attn_data_bytes(rows, p.K));
     if (int e = check_ws(ws, ws_bytes, need, "csa2_prefill_full")) return e;
     uint8_t* wsb = reinterpret_cast<uint8_t*>(ws);
     ScanArgs a;
@@ -553,7 +555,7 @@ int csa2_prefill_full(const csa2_plan* plan, const csa2_cache* cache, const void
     a.d_idx = p.d_idx;
     ScoresArgs none;
     SelOutput o{idx_out, nullptr, p.K, p.K};
-    if (int e = run_select(sp, SRC_SCAN, a, none, &o, 1, wsb, stream)) return e;
+    if (int e = run_select(sp, SRC_SCAN, a, none, &o, 1, wsb, wsb + sel_off, stream)) return e;
     AttnArgs at;
     at.q = q;
     at.rows = rows;
@@ -572,7 +574,7 @@ int csa2_prefill_full(const csa2_plan* plan, const csa2_cache* cache, const void
     at.K = p.K;
     at.scale = p.softmax_scale;
     at.out = out;
-    return launch_attn(at, wsb + sel_bytes, ws_bytes - sel_bytes, stream);
+    return launch_attn(at, wsb, wsb + attn_off, ws_bytes - attn_off, stream);
 }
 
 }  // extern "C"

@@ -51,7 +51,6 @@ constexpr int kAttnThreads = kAttnWaves * kWave;
 constexpr int kBlk = 32;
 constexpr int kMaxHeads = 16;
 constexpr int kD = 128;
-constexpr int kAttnWsHeader = 64;               // words; [0] device status word (unused here)
 constexpr int kAttnTargetGroups = 256;          // one workgroup per CU of a 256-CU part
 constexpr int kMaxSplits = 16;
 constexpr int kPartFloats = kMaxHeads * kD + 2 * kMaxHeads;   // per (row, slice): acc [16][128], (m, l) [16][2]
@@ -71,15 +70,9 @@ static int attn_splits(int64_t rows, int32_t K) {
     return (int)ns;
 }
 
-__host__ __device__ inline int64_t counter_words(int64_t rows) { return (rows + 63) / 64 * 64; }
-
-size_t attn_workspace_bytes(int64_t rows, int32_t H, int32_t d, int32_t K) {
-    (void)H;
-    (void)d;
+size_t attn_data_bytes(int64_t rows, int32_t K) {
     const int ns = attn_splits(rows, K);
-    size_t words = kAttnWsHeader;
-    if (ns > 1) words += (size_t)counter_words(rows) + (size_t)rows * ns * kPartFloats;
-    return words * 4;
+    return ns > 1 ? (size_t)rows * ns * kPartFloats * 4 : 0;
 }
 
 // 8 FP4 codes (one dword, channel 2j in the low nibble of byte j) times a scale -> 8 f16.
@@ -156,6 +149,13 @@ struct WaveState {
     f32x4 acc[8];                               // acc[t][i] = unnormalized out[n][8*(4g+i) + t]
 };
 
+// Two E4M3 bytes (bits 0..15 of w) -> two f16, exactly (the hardware decode
+// to fp32 is exact and every E4M3 value is an f16 value).
+__device__ __forceinline__ f16x2 e4m3x2_to_f16(uint32_t w) {
+    const f32x2 f = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
+    return __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(f.x, f.y));
+}
+
 __device__ __forceinline__ void attend_block(WaveState& st, const BlockRaw& r, Stage& sg, const f16x8 (&qb)[4],
                                              float sl2, int lane, int n, int g) {
     // ---- stage V codes and scales; this wave alone uses `sg`, and its LDS
@@ -163,89 +163,108 @@ __device__ __forceinline__ void attend_block(WaveState& st, const BlockRaw& r, S
     *reinterpret_cast<uint4*>(&sg.v[n][16 * g]) = r.v[0];
     *reinterpret_cast<uint4*>(&sg.v[16 + n][16 * g]) = r.v[1];
     if (lane < kBlk) {
-        const bool ok = r.pos >= 0;
-        *reinterpret_cast<uint2*>(&sg.ks[lane][0]) = ok ? r.ks : make_uint2(0, 0);
-        *reinterpret_cast<uint2*>(&sg.vs[lane][0]) = ok ? r.vs : make_uint2(0, 0);
+        *reinterpret_cast<uint2*>(&sg.ks[lane][0]) = r.ks;
+        *reinterpret_cast<uint2*>(&sg.vs[lane][0]) = r.vs;
     }
     __builtin_amdgcn_wave_barrier();
-    // positions of this lane's softmax columns: 4g + i (i < 4), 16 + 4g + i - 4 (i >= 4)
+    // bit p: position p of the block is a real entry (padding is masked out of
+    // the softmax; its codes and scales are those of position 0, all finite)
+    const uint32_t vmask = (uint32_t)__builtin_amdgcn_ballot_w64(r.pos >= 0);
+    // this lane's softmax columns i: positions 4g + i (i < 4), 16 + 4g + i - 4 (i >= 4)
     uint32_t vw[8], vsb[8];
-    bool valid[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const int p = (i < 4) ? (4 * g + i) : (16 + 4 * g + i - 4);
         vw[i] = *reinterpret_cast<const uint32_t*>(&sg.v[p][4 * n]);
         vsb[i] = sg.vs[p][n >> 1];
-        valid[i] = __shfl(r.pos, p) >= 0;
     }
-    const uint32_t k0s = *reinterpret_cast<const uint16_t*>(&sg.ks[n][2 * g]);
-    const uint32_t k1s = *reinterpret_cast<const uint16_t*>(&sg.ks[16 + n][2 * g]);
+    const f16x2 ks0 = e4m3x2_to_f16(*reinterpret_cast<const uint16_t*>(&sg.ks[n][2 * g]));
+    const f16x2 ks1 = e4m3x2_to_f16(*reinterpret_cast<const uint16_t*>(&sg.ks[16 + n][2 * g]));
 
     // ---- S^T = K_hat Q^T
     f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
-        const uint32_t ksc = mb == 0 ? k0s : k1s;
-        const _Float16 s_lo = scale_f16(ksc & 0xFFu), s_hi = scale_f16(ksc >> 8);
+        const f16x2 ks = mb == 0 ? ks0 : ks1;
         const uint32_t w[4] = {r.k[mb].x, r.k[mb].y, r.k[mb].z, r.k[mb].w};
 #pragma unroll
         for (int s = 0; s < 4; ++s)
-            sacc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(dq8(w[s], s < 2 ? s_lo : s_hi), qb[s], sacc[mb], 0, 0, 0);
+            sacc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(dq8(w[s], s < 2 ? ks.x : ks.y), qb[s], sacc[mb], 0, 0, 0);
     }
 
     // ---- online softmax for head n over the 8 positions this lane holds
+    const uint32_t mlo = vmask >> (4 * g), mhi = vmask >> (16 + 4 * g);
     float lg[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const float sv = (i < 4) ? sacc[0][i] : sacc[1][i - 4];
-        lg[i] = valid[i] ? sv * sl2 : -INFINITY;
+        const uint32_t bit = (i < 4) ? (mlo >> i) & 1u : (mhi >> (i - 4)) & 1u;
+        lg[i] = bit ? sv * sl2 : -INFINITY;
     }
-    float mx = lg[0];
-#pragma unroll
-    for (int i = 1; i < 8; ++i) mx = fmaxf(mx, lg[i]);
+    float mx = fmaxf(fmaxf(fmaxf(lg[0], lg[1]), fmaxf(lg[2], lg[3])), fmaxf(fmaxf(lg[4], lg[5]), fmaxf(lg[6], lg[7])));
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(st.m, mx);
+    const float m_old = st.m;
+    const float m_new = fmaxf(m_old, mx);
+    // weights 2^(lg - m_new): the hardware exp2 flushes results below 2^-126
+    // to zero, far below what can matter against the maximum weight 1
+    const float mref = m_new == -INFINITY ? 0.f : m_new;
+    float p[8], psum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        p[i] = __builtin_amdgcn_exp2f(lg[i] - mref);
+        psum += p[i];
+    }
     f16x8 pb_hi, pb_lo;                         // p = hi + lo, both f16: ~22 significant bits
-    float psum = 0.f, alpha = 1.f;
-    if (m_new != -INFINITY) {
-        alpha = exp2f(st.m - m_new);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const float p = exp2f(lg[i] - m_new);
-            const _Float16 hi = (_Float16)p;
-            pb_hi[i] = hi;
-            pb_lo[i] = (_Float16)(p - (float)hi);
-            psum += p;
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) pb_hi[i] = pb_lo[i] = (_Float16)0.f;
+    for (int i = 0; i < 8; i += 2) {
+        const f16x2 hi = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(p[i], p[i + 1]));
+        const f16x2 lo = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(p[i] - (float)hi.x, p[i + 1] - (float)hi.y));
+        pb_hi[i] = hi.x;
+        pb_hi[i + 1] = hi.y;
+        pb_lo[i] = lo.x;
+        pb_lo[i + 1] = lo.y;
     }
     psum += __shfl_xor(psum, 16);
     psum += __shfl_xor(psum, 32);
+    const float alpha = m_old == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_old - mref);
     st.l = st.l * alpha + psum;
     st.m = m_new;
-
-    // ---- out^T += V_hat^T P^T: MFMA t covers channels 8m + t
-    f16x2 hv[8][4];
+    // the running sums need rescaling only where the maximum grew after the
+    // first block (before it they are zero)
+    if (__builtin_amdgcn_ballot_w64(m_old != -INFINITY && alpha != 1.f) != 0) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const _Float16 sv = scale_f16(vsb[i]);
-        const f16x2 sp = {sv, sv};
-        hv[i][0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(vw[i], 1.0f, 0) * sp;
-        hv[i][1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(vw[i], 1.0f, 1) * sp;
-        hv[i][2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(vw[i], 1.0f, 2) * sp;
-        hv[i][3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(vw[i], 1.0f, 3) * sp;
+        for (int t = 0; t < 8; ++t) st.acc[t] = st.acc[t] * alpha;
+    }
+
+    // ---- out^T += V_hat^T P^T: MFMA t covers channels 8m + t; its operand
+    // element i is channel 8n + t of position column i. Codes of columns
+    // 2k and 2k+1 are interleaved nibble-wise so that one convert yields the
+    // (column 2k, column 2k+1) pair of a channel, scaled by the packed scale
+    // pair of the two positions.
+    f16x2 va[8][4];                             // va[t][k] = (V[2k][8n+t], V[2k+1][8n+t])
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const uint32_t wa = vw[2 * k], wb = vw[2 * k + 1];
+        const f16x2 sp = e4m3x2_to_f16(vsb[2 * k] | (vsb[2 * k + 1] << 8));
+        const uint32_t ev = (wa & 0x0F0F0F0Fu) | ((wb << 4) & 0xF0F0F0F0u);   // byte j: channel 2j of a | of b
+        const uint32_t od = ((wa >> 4) & 0x0F0F0F0Fu) | (wb & 0xF0F0F0F0u);  // byte j: channel 2j+1
+        va[0][k] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(ev, 1.0f, 0) * sp;
+        va[2][k] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(ev, 1.0f, 1) * sp;
+        va[4][k] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(ev, 1.0f, 2) * sp;
+        va[6][k] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(ev, 1.0f, 3) * sp;
+        va[1][k] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(od, 1.0f, 0) * sp;
+        va[3][k] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(od, 1.0f, 1) * sp;
+        va[5][k] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(od, 1.0f, 2) * sp;
+        va[7][k] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(od, 1.0f, 3) * sp;
     }
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-        f16x8 va;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) va[i] = hv[i][t >> 1][t & 1];
-        st.acc[t] = st.acc[t] * alpha;
-        st.acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb_hi, st.acc[t], 0, 0, 0);
-        st.acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb_lo, st.acc[t], 0, 0, 0);
+        const f16x8 a = __builtin_shufflevector(__builtin_shufflevector(va[t][0], va[t][1], 0, 1, 2, 3),
+                                                __builtin_shufflevector(va[t][2], va[t][3], 0, 1, 2, 3), 0, 1, 2, 3,
+                                                4, 5, 6, 7);
+        st.acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pb_hi, st.acc[t], 0, 0, 0);
+        st.acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pb_lo, st.acc[t], 0, 0, 0);
     }
 }
 
@@ -254,7 +273,7 @@ k_sparse_attn(const uint16_t* __restrict__ q, int32_t rows_per_seq, int32_t H, c
               const uint8_t* __restrict__ k_scales, const uint8_t* __restrict__ v_codes,
               const uint8_t* __restrict__ v_scales, int64_t N, int64_t cs, int64_t ss, const int32_t* __restrict__ idx,
               int64_t idx_stride, int32_t K, float scale, float* __restrict__ out, int32_t NS,
-              uint32_t* __restrict__ ws, int64_t rows) {
+              uint32_t* __restrict__ counters, float* __restrict__ parts, int64_t rows) {
     __shared__ AttnLds lds;
     __shared__ int s_last;
 
@@ -382,8 +401,8 @@ k_sparse_attn(const uint16_t* __restrict__ q, int32_t rows_per_seq, int32_t H, c
     }
 
     // ---- NS > 1: publish this slice's state, the last slice of the row merges
-    uint32_t* ctr = ws + kAttnWsHeader + row;
-    float* part_row = reinterpret_cast<float*>(ws + kAttnWsHeader + counter_words(rows)) + row * NS * kPartFloats;
+    uint32_t* ctr = counters + row;
+    float* part_row = parts + row * NS * kPartFloats;
     const __amdgpu_buffer_rsrc_t rs =
         __builtin_amdgcn_make_buffer_rsrc(part_row, (short)0, NS * kPartFloats * 4, kRsrcWord3);
     const int mine = split * kPartFloats * 4;
@@ -428,15 +447,17 @@ k_sparse_attn(const uint16_t* __restrict__ q, int32_t rows_per_seq, int32_t H, c
     if (tid == 0) st_rlx(ctr, 0u);              // ready for the next launch
 }
 
-int launch_attn(const AttnArgs& a, void* ws, size_t ws_bytes, hipStream_t stream) {
+int launch_attn(const AttnArgs& a, void* ws_ctrl, void* ws_data, size_t data_bytes, hipStream_t stream) {
     if (a.rows == 0) return OK;
     const int ns = attn_splits(a.rows, a.K);
-    if (ws_bytes < attn_workspace_bytes(a.rows, a.H, a.d, a.K)) return fail(WORKSPACE, "attention workspace too small");
+    if (data_bytes < attn_data_bytes(a.rows, a.K)) return fail(WORKSPACE, "attention workspace too small");
+    if (ns > 1 && a.rows > kAttnCtrlWords) return fail(INVALID, "attention: split rows exceed the counter table");
     const int64_t groups = a.rows * ns;
     if (groups > 0x7FFFFFFFll) return fail(INVALID, "attention: too many query rows");
+    uint32_t* counters = reinterpret_cast<uint32_t*>(ws_ctrl) + kAttnCtrlOffsetWords;
     hipLaunchKernelGGL(k_sparse_attn, dim3((unsigned)groups), dim3(kAttnThreads), 0, stream, a.q, a.rows_per_seq,
                        a.H, a.k_codes, a.k_scales, a.v_codes, a.v_scales, a.N, a.code_stride, a.scale_stride, a.idx,
-                       a.idx_stride, a.K, a.scale, a.out, ns, reinterpret_cast<uint32_t*>(ws), a.rows);
+                       a.idx_stride, a.K, a.scale, a.out, ns, counters, reinterpret_cast<float*>(ws_data), a.rows);
     const hipError_t e = hipGetLastError();
     return e == hipSuccess ? OK : hip_fail(e, "launch k_sparse_attn");
 }

@@ -24,6 +24,23 @@ struct DeviceInfo {
 };
 int device_info(DeviceInfo* out);
 
+// ------------------------------------------------------------ workspaces
+// Every workspace starts with one control region whose layout is the same for
+// every call and every problem shape: a header, the select kernels' per-row
+// barrier and exit counters and histogram accumulators, and the attention
+// kernel's per-row merge counters. Each call leaves the words it used zero,
+// so one zero-filled buffer can serve calls of any kind and shape in turn.
+// The region of data that a call writes (lists, partial results, outputs
+// kept in the workspace) follows it; data never lands on a control word.
+constexpr int kCtrlHeaderWords = 64;        // [0] device status word
+constexpr int kSelCtrlRowWords = 8256;      // barrier, exit, 2048 + 2*2048 + 2*1024 histogram bins, padded
+constexpr int kSelCtrlRows = 256;           // rows per select launch (at most one workgroup per CU)
+constexpr int kAttnCtrlWords = 256;         // rows whose attention is split over workgroups (< 256)
+constexpr size_t kCtrlWords = kCtrlHeaderWords + (size_t)kSelCtrlRows * kSelCtrlRowWords + kAttnCtrlWords;
+constexpr size_t kCtrlBytes = kCtrlWords * 4;
+constexpr size_t kSelCtrlOffsetWords = kCtrlHeaderWords;
+constexpr size_t kAttnCtrlOffsetWords = kCtrlHeaderWords + (size_t)kSelCtrlRows * kSelCtrlRowWords;
+
 // ------------------------------------------------------------- selection
 // Geometry of one selection problem: `rows` rows of `n` entries split into S
 // chunks of `chunk` entries, one workgroup per chunk, all chunks of a row
@@ -31,9 +48,10 @@ int device_info(DeviceInfo* out);
 struct SelPlan {
     int64_t rows = 0, n = 0;
     int32_t S = 1, chunk = 0, chunk_pad = 0, rows_per_launch = 0, launches = 0;
-    int32_t row_words = 0;          // exchange words per row in the workspace
+    int32_t row_words = 0;          // data words per row in the workspace
     size_t lds_bytes = 0;
-    size_t ws_bytes = 0;            // workspace bytes (header + rows_per_launch rows)
+    size_t data_bytes = 0;          // data region bytes (rows_per_launch rows)
+    size_t ws_bytes = 0;            // control region + data region
 };
 
 enum SelSource : int { SRC_SCORES = 0, SRC_SCAN = 1, SRC_POOL = 2 };
@@ -66,8 +84,10 @@ struct ScoresArgs {                 // precomputed scores
 
 // Run a planned selection for all rows (several launches if needed).
 // nt = number of targets (1 or 2, out[0].M >= out[1].M).
+// ws_ctrl: start of the workspace (its control region); ws_data: this call's
+// data region of p.data_bytes bytes.
 int run_select(const SelPlan& p, int source, const ScanArgs& scan, const ScoresArgs& sc,
-               const SelOutput* out, int nt, void* ws, hipStream_t stream);
+               const SelOutput* out, int nt, void* ws_ctrl, void* ws_data, hipStream_t stream);
 
 // ---------------------------------------------------------- other kernels
 int launch_quant(const uint16_t* x, int64_t rows, int32_t C, int64_t x_stride, uint8_t* codes,
@@ -90,7 +110,7 @@ struct AttnArgs {
     float scale = 0.f;
     float* out = nullptr;           // [rows][H][d]
 };
-size_t attn_workspace_bytes(int64_t rows, int32_t H, int32_t d, int32_t K);
-int launch_attn(const AttnArgs& a, void* ws, size_t ws_bytes, hipStream_t stream);
+size_t attn_data_bytes(int64_t rows, int32_t K);     // data region of one attention call
+int launch_attn(const AttnArgs& a, void* ws_ctrl, void* ws_data, size_t data_bytes, hipStream_t stream);
 
 }  // namespace csa2

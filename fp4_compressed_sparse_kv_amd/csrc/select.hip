@@ -11,16 +11,19 @@
 //               (a Reindex layer).
 // The source also builds the chunk's histogram of the top 11 key bits while
 // it writes the keys. The histograms of a row's chunks are summed in the
-// workspace with device-scope atomics; after a barrier of the row's S
+// workspace with device-scope atomics, and each chunk also publishes the
+// suffix sums of its own histogram; after a barrier of the row's S
 // workgroups (all resident at once: a launch never holds more workgroups
 // than CUs, and the kernel fits one per CU) every chunk knows the bin b1 that
-// holds the M-th largest key.
+// holds the M-th largest key, and every chunk's count of keys above b1 and
+// in it.
 //   List path (S > 1 and at most kCandCap keys in bin b1 row-wide): each
-//     chunk appends its bin-b1 entries (index, key) to a per-row list, at
-//     slots reserved with one atomic per chunk, and publishes its count of
-//     keys above the bin. After a second barrier every chunk reads the short
-//     list and resolves the exact threshold key T, how many entries equal to
-//     T are taken, and every chunk's counts, with no further exchange.
+//     chunk writes its bin-b1 entries (index, key) to a per-row list, at
+//     slots that follow from those counts (chunks in order, entries in index
+//     order). After a second barrier every chunk reads the short list and
+//     resolves the exact threshold key T, how many entries equal to T are
+//     taken, and every chunk's (and its own waves') counts of entries > T
+//     and == T, with no further exchange.
 //   Radix path (otherwise): two more radix passes over the LDS keys (11 and
 //     10 bits), each with a row-wide histogram exchange, then an exchange of
 //     the per-chunk counts of keys > T and == T.
@@ -38,10 +41,9 @@ namespace csa2 {
 constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / kWave;
 constexpr int kB1 = 2048, kB2 = 2048, kB3 = 1024;   // radix digits 11 | 11 | 10 bits
-constexpr int kRowHdr = 16;                          // [0] barrier, [1] exit, [2 + j] list length of target j
+constexpr int kRowHdr = 16;                          // control words of a row: [0] barrier, [1] exit
 constexpr int kCandCap = 16384;                      // list entries per (row, target)
 constexpr int kMaxS = 256;                           // chunks per row (<= CUs)
-constexpr int kWsHeaderWords = 64;                   // [0] device status word
 constexpr int kScratchWords = 256;
 constexpr int kLdsFixedWords = kB1 + 2 * kB2 + 4 * kMaxS + kScratchWords;
 constexpr int kMaxChunk = 32768;
@@ -51,8 +53,12 @@ constexpr int kMaxSteps = kMaxChunk / kSelWaves / kPadTo;   // steps per wave (8
 struct SelDev {
     int64_t n;
     int32_t S, chunk, chunk_pad, row0, nt, row_words;
-    uint32_t* ws;
+    uint32_t* ctrl;                             // workspace control region
+    uint32_t* data;                             // this call's data region
 };
+
+static_assert(kRowHdr + kB1 + 2 * kB2 + 2 * kB3 <= kSelCtrlRowWords, "select control words per row");
+static_assert(kMaxS <= kSelCtrlRows, "select rows per launch");
 
 struct SelTgt {
     int32_t* idx;
@@ -241,7 +247,14 @@ __device__ __forceinline__ uint64_t ld_rlx_u64(const uint64_t* p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <class Src>
+// Element j of a per-target pair, as a select on values (an indexed access
+// would force the pair into scratch memory).
+template <int NT, class T>
+__device__ __forceinline__ T pick(T a0, T a1, int j) {
+    return (NT > 1 && j) ? a1 : a0;
+}
+
+template <class Src, int NT>
 __global__ void __launch_bounds__(kSelThreads) k_select(Src src, SelDev g, SelTgt t0, SelTgt t1) {
     extern __shared__ uint32_t lds[];
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
@@ -252,7 +265,6 @@ __global__ void __launch_bounds__(kSelThreads) k_select(Src src, SelDev g, SelTg
     const int64_t begin = (int64_t)split * g.chunk;
     const int cnt = (int)min((int64_t)g.chunk, g.n - begin);
     const int cpad = g.chunk_pad;
-    const int nt = g.nt;
     const bool multi = S > 1;
 
     uint32_t* keys = lds;                       // [cpad] score keys, 0 past cnt
@@ -260,17 +272,17 @@ __global__ void __launch_bounds__(kSelThreads) k_select(Src src, SelDev g, SelTg
     uint32_t* lh2 = lh1 + kB1;                  // [2*kB2] row histogram, then later histograms
     uint32_t* cnts = lh2 + 2 * kB2;             // [S][2 targets][> T, == T]
     uint32_t* sm = cnts + 4 * kMaxS;            // scratch
-    uint32_t* status = g.ws;
-    uint32_t* rw = g.ws + kWsHeaderWords + (size_t)lrow * g.row_words;
-    uint32_t* ctrl = rw;
-    uint32_t* exitc = rw + 1;
-    uint32_t* llen = rw + 2;                    // [2] list lengths
-    uint32_t* gh1 = rw + kRowHdr;
+    uint32_t* status = g.ctrl;
+    uint32_t* rc = g.ctrl + kSelCtrlOffsetWords + (size_t)lrow * kSelCtrlRowWords;   // zero between calls
+    uint32_t* ctrl = rc;
+    uint32_t* exitc = rc + 1;
+    uint32_t* gh1 = rc + kRowHdr;
     uint32_t* gh2 = gh1 + kB1;
     uint32_t* gh3 = gh2 + 2 * kB2;
-    uint32_t* gtab = gh3 + 2 * kB3;             // [S][2] keys above bin b1 per chunk
-    uint32_t* gcnt = gtab + 2 * S;              // [S][2][> T, == T]
-    uint64_t* glist = reinterpret_cast<uint64_t*>(gcnt + 4 * S);   // [2][kCandCap] (index << 32 | key)
+    uint32_t* rw = g.data + (size_t)lrow * g.row_words;                              // data, any content
+    uint32_t* gcnt = rw;                        // [S][2][> T, == T]
+    uint32_t* gsuf = gcnt + 4 * S;              // [S][kB1] per-chunk suffix sums of the top-digit histogram
+    uint64_t* glist = reinterpret_cast<uint64_t*>(gsuf + (size_t)S * kB1);   // [2][kCandCap] (index << 32 | key)
     uint32_t gen = 0;
 
     const uint32_t M[2] = {(uint32_t)t0.M, (uint32_t)t1.M};
@@ -279,10 +291,24 @@ __global__ void __launch_bounds__(kSelThreads) k_select(Src src, SelDev g, SelTg
     __syncthreads();
     src.fill(row, begin, cnt, cpad, keys, lh1);  // keys + lh1; ends with a block barrier
 
-    // ---- row histogram of the top 11 bits
+    // ---- row histogram of the top 11 bits; each chunk also publishes the
+    // suffix sums of its own histogram (keys at or above each bin)
     const uint32_t* G = lh1;
     if (multi) {
         push_hist(lh1, gh1, kB1);
+        {
+            // bins 2047 - 2*tid and 2046 - 2*tid, scanned from the top
+            const int hi = kB1 - 1 - 2 * tid;
+            const uint32_t a = lh1[hi], b = lh1[hi - 1];
+            const uint32_t inc = wave_incl_scan(a + b);
+            if (lane == kWave - 1) sm[wave] = inc;
+            __syncthreads();
+            uint32_t before = inc - (a + b);
+            for (int w = 0; w < wave; ++w) before += sm[w];
+            uint32_t* mine = gsuf + (size_t)split * kB1;
+            st_rlx(&mine[hi], before + a);
+            st_rlx(&mine[hi - 1], before + a + b);
+        }
         row_barrier(ctrl, S, gen, status);
         for (int b = tid; b < kB1; b += kSelThreads) lh2[b] = ld_rlx(&gh1[b]);
         __syncthreads();
@@ -290,7 +316,8 @@ __global__ void __launch_bounds__(kSelThreads) k_select(Src src, SelDev g, SelTg
     }
     int path[2] = {kPathAll, kPathAll};
     uint32_t b1[2] = {0, 0}, rem[2] = {0, 0}, C[2] = {0, 0}, T[2] = {0, 0}, need[2] = {0, 0};
-    for (int j = 0; j < nt; ++j) {
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
         const Found f = block_find(G, kB1, M[j], sm);
         if (f.total > M[j]) {
             b1[j] = f.bin;
@@ -300,9 +327,9 @@ __global__ void __launch_bounds__(kSelThreads) k_select(Src src, SelDev g, SelTg
         }
     }
     __syncthreads();                            // G (lh2) may be overwritten below
-    const bool any_list = path[0] == kPathList || (nt > 1 && path[1] == kPathList);
-    const bool any_radix = path[0] == kPathRadix || (nt > 1 && path[1] == kPathRadix);
-    const bool any_other = path[0] != kPathList || (nt > 1 && path[1] != kPathList);
+    const bool any_list = path[0] == kPathList || (NT > 1 && path[1] == kPathList);
+    const bool any_radix = path[0] == kPathRadix || (NT > 1 && path[1] == kPathRadix);
+    const bool any_other = path[0] != kPathList || (NT > 1 && path[1] != kPathList);
 
     // ---- each wave owns a contiguous span of kPadTo-key steps; its lanes keep
     // the span's keys in registers (4 per lane per step) for every later pass
@@ -317,11 +344,26 @@ __global__ void __launch_bounds__(kSelThreads) k_select(Src src, SelDev g, SelTg
             kreg[t] = (t < nst) ? *reinterpret_cast<const uint4*>(&keys[w0 + t * kPadTo + 4 * lane])
                                 : make_uint4(0, 0, 0, 0);
     };
-    if (any_list) load_kreg();
+    uint32_t* wcnt = sm + 64;                   // [2][16][gt, eq] per-wave counts of this chunk
 
-    // ---- list path, part 1: append this chunk's bin-b1 entries, count the keys above the bin
+    // ---- list path, part 1: every chunk's counts above bin b1 and in it come
+    // from the published suffix sums, so each chunk knows its slots in the
+    // row's list (chunks in order) without an atomic; it appends its bin-b1
+    // entries there in index order.
     if (any_list) {
-        uint32_t* wl = sm + 32;                 // [2][16] per-wave candidate counts, then bases
+        load_kreg();
+        // cnts[s][j] = (keys above b1, keys in b1) of chunk s
+        for (int i = tid; i < S * NT; i += kSelThreads) {
+            const int s = i / NT, j = i - s * NT;
+            if (pick<NT>(path[0], path[1], j) != kPathList) continue;
+            const uint32_t bj = pick<NT>(b1[0], b1[1], j);
+            const uint32_t* su = gsuf + (size_t)s * kB1;
+            const uint32_t at = ld_rlx(&su[bj]);
+            const uint32_t ab = bj + 1 < (uint32_t)kB1 ? ld_rlx(&su[bj + 1]) : 0u;
+            cnts[(s * 2 + j) * 2 + 0] = ab;
+            cnts[(s * 2 + j) * 2 + 1] = at - ab;
+        }
+        // per-wave counts of keys above the bin and in it
         uint32_t above[2] = {0u, 0u}, ncand[2] = {0u, 0u};
 #pragma unroll
         for (int t = 0; t < kMaxSteps; ++t) {
@@ -330,28 +372,27 @@ __global__ void __launch_bounds__(kSelThreads) k_select(Src src, SelDev g, SelTg
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const uint32_t d = kv[u] >> 21;
-                for (int j = 0; j < nt; ++j) {
+#pragma unroll
+                for (int j = 0; j < NT; ++j) {
                     above[j] += (uint32_t)(d > b1[j]);
                     ncand[j] += (uint32_t)__popcll(__ballot(kv[u] != 0u && d == b1[j]));
                 }
             }
         }
-        for (int j = 0; j < nt; ++j) {
+        uint32_t* wl = sm + 32;                 // [2][16] per-wave list bases
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
             const uint32_t a = wave_sum(above[j]);
             if (lane == 0) {
-                sm[96 + j * kSelWaves + wave] = a;
+                wcnt[(j * kSelWaves + wave) * 2 + 0] = a;
+                wcnt[(j * kSelWaves + wave) * 2 + 1] = 0u;
                 wl[j * kSelWaves + wave] = ncand[j];
             }
         }
         __syncthreads();
-        if (tid < nt && path[tid] == kPathList) {
-            uint32_t a = 0, c = 0;
-            for (int w = 0; w < kSelWaves; ++w) {
-                a += sm[96 + tid * kSelWaves + w];
-                c += wl[tid * kSelWaves + w];
-            }
-            st_rlx(&gtab[split * 2 + tid], a);
-            uint32_t base = add_rlx(&llen[tid], c);    // this chunk's slots in the row's list
+        if (tid < NT && pick<NT>(path[0], path[1], tid) == kPathList) {
+            uint32_t base = 0;
+            for (int s = 0; s < split; ++s) base += cnts[(s * 2 + tid) * 2 + 1];
             for (int w = 0; w < kSelWaves; ++w) {
                 const uint32_t n = wl[tid * kSelWaves + w];
                 wl[tid * kSelWaves + w] = base;
@@ -359,7 +400,14 @@ __global__ void __launch_bounds__(kSelThreads) k_select(Src src, SelDev g, SelTg
             }
         }
         __syncthreads();
-        for (int j = 0; j < nt; ++j) {
+        // from here on cnts[s][j] counts (> T, == T): keys above the bin count
+        // as > T, and the list adds its entries once T is known
+        for (int i = tid; i < S * NT; i += kSelThreads) {
+            const int s = i / NT, j = i - s * NT;
+            if (pick<NT>(path[0], path[1], j) == kPathList) cnts[(s * 2 + j) * 2 + 1] = 0u;
+        }
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
             if (path[j] != kPathList) continue;
             uint32_t run = wl[j * kSelWaves + wave];
             uint64_t* lst = glist + (size_t)j * kCandCap;
@@ -387,19 +435,23 @@ __global__ void __launch_bounds__(kSelThreads) k_select(Src src, SelDev g, SelTg
         __syncthreads();
         for (int i = tid; i < cnt; i += kSelThreads) {
             const uint32_t k = keys[i];
-            for (int j = 0; j < nt; ++j)
+#pragma unroll
+            for (int j = 0; j < NT; ++j)
                 if (path[j] == kPathRadix && (k >> 21) == b1[j]) atomicAdd(&lh2[j * kB2 + ((k >> 10) & 2047u)], 1u);
         }
         __syncthreads();
         if (multi) {
-            for (int j = 0; j < nt; ++j)
+#pragma unroll
+            for (int j = 0; j < NT; ++j)
                 if (path[j] == kPathRadix) push_hist(lh2 + j * kB2, gh2 + j * kB2, kB2);
             row_barrier(ctrl, S, gen, status);
-            for (int j = 0; j < nt; ++j)
+#pragma unroll
+            for (int j = 0; j < NT; ++j)
                 if (path[j] == kPathRadix) pull_hist(lh2 + j * kB2, gh2 + j * kB2, kB2);
         }
         uint32_t pre2[2] = {0, 0};
-        for (int j = 0; j < nt; ++j) {
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
             if (path[j] != kPathRadix) continue;
             const Found f = block_find(lh2 + j * kB2, kB2, rem[j], sm);
             pre2[j] = (b1[j] << 11) | f.bin;
@@ -409,18 +461,22 @@ __global__ void __launch_bounds__(kSelThreads) k_select(Src src, SelDev g, SelTg
         __syncthreads();
         for (int i = tid; i < cnt; i += kSelThreads) {
             const uint32_t k = keys[i];
-            for (int j = 0; j < nt; ++j)
+#pragma unroll
+            for (int j = 0; j < NT; ++j)
                 if (path[j] == kPathRadix && (k >> 10) == pre2[j]) atomicAdd(&lh2[j * kB3 + (k & 1023u)], 1u);
         }
         __syncthreads();
         if (multi) {
-            for (int j = 0; j < nt; ++j)
+#pragma unroll
+            for (int j = 0; j < NT; ++j)
                 if (path[j] == kPathRadix) push_hist(lh2 + j * kB3, gh3 + j * kB3, kB3);
             row_barrier(ctrl, S, gen, status);
-            for (int j = 0; j < nt; ++j)
+#pragma unroll
+            for (int j = 0; j < NT; ++j)
                 if (path[j] == kPathRadix) pull_hist(lh2 + j * kB3, gh3 + j * kB3, kB3);
         }
-        for (int j = 0; j < nt; ++j) {
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
             if (path[j] != kPathRadix) continue;
             const Found f = block_find(lh2 + j * kB3, kB3, rem[j], sm);
             T[j] = (pre2[j] << 10) | f.bin;
@@ -428,28 +484,29 @@ __global__ void __launch_bounds__(kSelThreads) k_select(Src src, SelDev g, SelTg
         }
     }
 
-    // ---- list path, part 2: resolve T and every chunk's counts from the list
+    // ---- list path, part 2: after the row barrier every chunk reads the
+    // row's lists, resolves T and the tie count, and adds the entries > T and
+    // == T to the counts of their chunk (and, for its own chunk, of their wave)
     if (any_list) {
         row_barrier(ctrl, S, gen, status);
-        for (int i = tid; i < S * 2; i += kSelThreads) {
-            const int j = i & 1;
-            cnts[i * 2 + 0] = (j < nt && path[j] == kPathList) ? ld_rlx(&gtab[i]) : 0u;
-            cnts[i * 2 + 1] = 0u;
-        }
-        for (int j = 0; j < nt; ++j) {
-            if (path[j] != kPathList) continue;
-            constexpr int R = kCandCap / kSelThreads;
-            uint64_t ent[R];
+        constexpr int R = kCandCap / kSelThreads;
+        uint64_t ent[2][R];
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
 #pragma unroll
             for (int r = 0; r < R; ++r) {
                 const int e = tid + r * kSelThreads;
-                ent[r] = (e < (int)C[j]) ? ld_rlx_u64(&glist[(size_t)j * kCandCap + e]) : 0ull;
+                ent[j][r] = (path[j] == kPathList && e < (int)C[j]) ? ld_rlx_u64(&glist[(size_t)j * kCandCap + e]) : 0ull;
             }
+        }
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+            if (path[j] != kPathList) continue;
             for (int i = tid; i < kB2; i += kSelThreads) lh2[i] = 0u;
             __syncthreads();
 #pragma unroll
             for (int r = 0; r < R; ++r) {
-                const uint32_t k = (uint32_t)ent[r];
+                const uint32_t k = (uint32_t)ent[j][r];
                 if (k) atomicAdd(&lh2[(k >> 10) & 2047u], 1u);
             }
             __syncthreads();
@@ -458,7 +515,7 @@ __global__ void __launch_bounds__(kSelThreads) k_select(Src src, SelDev g, SelTg
             __syncthreads();
 #pragma unroll
             for (int r = 0; r < R; ++r) {
-                const uint32_t k = (uint32_t)ent[r];
+                const uint32_t k = (uint32_t)ent[j][r];
                 if (k && ((k >> 10) & 2047u) == f2.bin) atomicAdd(&lh2[k & 1023u], 1u);
             }
             __syncthreads();
@@ -467,44 +524,45 @@ __global__ void __launch_bounds__(kSelThreads) k_select(Src src, SelDev g, SelTg
             need[j] = f3.rem;
 #pragma unroll
             for (int r = 0; r < R; ++r) {
-                const uint32_t k = (uint32_t)ent[r];
-                if (!k) continue;
-                const int s = (int)((uint32_t)(ent[r] >> 32) / (uint32_t)g.chunk);
-                if (k > T[j]) atomicAdd(&cnts[(s * 2 + j) * 2 + 0], 1u);
-                else if (k == T[j]) atomicAdd(&cnts[(s * 2 + j) * 2 + 1], 1u);
+                const uint32_t k = (uint32_t)ent[j][r];
+                if (!k || k < T[j]) continue;
+                const uint32_t ix = (uint32_t)(ent[j][r] >> 32);
+                const int s = (int)(ix / (uint32_t)g.chunk);
+                const int side = k > T[j] ? 0 : 1;
+                atomicAdd(&cnts[(s * 2 + j) * 2 + side], 1u);
+                if (s == split) atomicAdd(&wcnt[(j * kSelWaves + (int)(ix - (uint32_t)begin) / span) * 2 + side], 1u);
             }
         }
         __syncthreads();
     }
 
-    // ---- per-wave counts of keys > T and == T (keys reloaded into registers:
-    // their first live range ended before the list resolution, which needs the
-    // registers for list entries)
-    load_kreg();
-    uint32_t* wcnt = sm + 64;                   // [2][16][gt, eq]
-    for (int j = 0; j < nt; ++j) {
-        uint32_t gt = 0, eq = 0;
-        const uint32_t Tj = T[j];
+    // ---- targets not resolved from a list: per-wave counts of keys > T and
+    // == T from the register-resident keys, then (radix path) an exchange of
+    // the per-chunk counts
+    if (any_other) {
+        load_kreg();
 #pragma unroll
-        for (int t = 0; t < kMaxSteps; ++t) {
-            if (t >= nst) break;
-            const uint32_t kv[4] = {kreg[t].x, kreg[t].y, kreg[t].z, kreg[t].w};
+        for (int j = 0; j < NT; ++j) {
+            if (path[j] == kPathList) continue;
+            uint32_t gt = 0, eq = 0;
+            const uint32_t Tj = T[j];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                gt += (uint32_t)__popcll(__ballot(kv[u] > Tj));
-                eq += (uint32_t)__popcll(__ballot(kv[u] == Tj && kv[u] != 0u));
+            for (int t = 0; t < kMaxSteps; ++t) {
+                if (t >= nst) break;
+                const uint32_t kv[4] = {kreg[t].x, kreg[t].y, kreg[t].z, kreg[t].w};
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    gt += (uint32_t)__popcll(__ballot(kv[u] > Tj));
+                    eq += (uint32_t)__popcll(__ballot(kv[u] == Tj && kv[u] != 0u));
+                }
+            }
+            if (lane == 0) {
+                wcnt[(j * kSelWaves + wave) * 2 + 0] = gt;
+                wcnt[(j * kSelWaves + wave) * 2 + 1] = eq;
             }
         }
-        if (lane == 0) {
-            wcnt[(j * kSelWaves + wave) * 2 + 0] = gt;
-            wcnt[(j * kSelWaves + wave) * 2 + 1] = eq;
-        }
-    }
-    __syncthreads();
-
-    // ---- targets resolved without the list exchange their per-chunk counts
-    if (any_other) {
-        if (tid < nt && path[tid] != kPathList) {
+        __syncthreads();
+        if (tid < NT && pick<NT>(path[0], path[1], tid) != kPathList) {
             uint32_t gt = 0, eq = 0;
             for (int w = 0; w < kSelWaves; ++w) {
                 gt += wcnt[(tid * kSelWaves + w) * 2 + 0];
@@ -522,7 +580,7 @@ __global__ void __launch_bounds__(kSelThreads) k_select(Src src, SelDev g, SelTg
             row_barrier(ctrl, S, gen, status);
             for (int i = tid; i < S * 2; i += kSelThreads) {
                 const int j = i & 1;
-                if (j < nt && path[j] != kPathList) {
+                if (j < NT && pick<NT>(path[0], path[1], j) != kPathList) {
                     cnts[i * 2 + 0] = ld_rlx(&gcnt[i * 2 + 0]);
                     cnts[i * 2 + 1] = ld_rlx(&gcnt[i * 2 + 1]);
                 }
@@ -530,16 +588,18 @@ __global__ void __launch_bounds__(kSelThreads) k_select(Src src, SelDev g, SelTg
         }
         __syncthreads();
     }
+    if (!any_other) load_kreg();
 
     // ---- offsets: this chunk's output base and its share of the == T entries
     uint32_t* wbase = sm + 128;                 // [2][16][base, eq_before]
     uint32_t* tinfo = sm + 192;                 // [2][take_eq, total_sel, eq_chunk, -]
-    if (tid < nt) {
+    if (tid < NT) {
         const int j = tid;
+        const uint32_t nj = pick<NT>(need[0], need[1], j);
         uint32_t off = 0, eq_before = 0, total_sel = 0, my_take = 0, my_eq = 0;
         for (int s = 0; s < S; ++s) {
             const uint32_t gt = cnts[(s * 2 + j) * 2 + 0], eq = cnts[(s * 2 + j) * 2 + 1];
-            const uint32_t left = need[j] > eq_before ? need[j] - eq_before : 0u;
+            const uint32_t left = nj > eq_before ? nj - eq_before : 0u;
             const uint32_t take = eq < left ? eq : left;
             if (s < split) off += gt + take;
             if (s == split) {
@@ -565,7 +625,8 @@ __global__ void __launch_bounds__(kSelThreads) k_select(Src src, SelDev g, SelTg
     __syncthreads();
 
     // ---- compaction in index order, 4 keys per lane per step
-    for (int j = 0; j < nt; ++j) {
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
         const SelTgt& t = j ? t1 : t0;
         const uint32_t Tj = T[j];
         const uint32_t take_eq = tinfo[j * 4 + 0];
@@ -650,8 +711,6 @@ __global__ void __launch_bounds__(kSelThreads) k_select(Src src, SelDev g, SelTg
             const int nz = any_radix ? kB1 + 2 * kB2 + 2 * kB3 : kB1;
             for (int i = tid; i < nz; i += kSelThreads) st_rlx(&gh1[i], 0u);
             if (tid == 0) {
-                st_rlx(&llen[0], 0u);
-                st_rlx(&llen[1], 0u);
                 st_rlx(ctrl, 0u);
                 st_rlx(exitc, 0u);
             }
@@ -689,11 +748,13 @@ int plan_select(int64_t rows, int64_t n, int32_t min_chunk, SelPlan* out) {
     if (rows > 0 && p.rows_per_launch > rows) p.rows_per_launch = (int32_t)rows;
     if (p.rows_per_launch < 1) p.rows_per_launch = 1;
     p.launches = rows > 0 ? (int32_t)((rows + p.rows_per_launch - 1) / p.rows_per_launch) : 0;
-    p.row_words = kRowHdr + kB1 + 2 * kB2 + 2 * kB3 + 6 * (int32_t)S + 2 * 2 * kCandCap;
+    p.row_words = 4 * (int32_t)S + (int32_t)S * kB1 + 2 * 2 * kCandCap;
     p.row_words = (p.row_words + 63) / 64 * 64;
     p.chunk_pad = (int32_t)((chunk + kPadTo - 1) / kPadTo * kPadTo);
     p.lds_bytes = (size_t)(p.chunk_pad + kLdsFixedWords) * 4;
-    p.ws_bytes = (size_t)(kWsHeaderWords + (size_t)p.rows_per_launch * p.row_words) * 4;
+    if (p.rows_per_launch > kSelCtrlRows) return fail(INVALID, "select: too many rows per launch");
+    p.data_bytes = (size_t)p.rows_per_launch * p.row_words * 4;
+    p.ws_bytes = kCtrlBytes + p.data_bytes;
     *out = p;
     return OK;
 }
@@ -701,15 +762,16 @@ int plan_select(int64_t rows, int64_t n, int32_t min_chunk, SelPlan* out) {
 namespace {
 
 template <class Src>
-int launch_rows(const SelPlan& p, const Src& src, const SelOutput* out, int nt, void* ws, hipStream_t stream) {
-    auto fn = reinterpret_cast<const void*>(&k_select<Src>);
-    static bool attr_set = false;
-    if (!attr_set) {
+int launch_rows(const SelPlan& p, const Src& src, const SelOutput* out, int nt, void* ws_ctrl, void* ws_data,
+                hipStream_t stream) {
+    auto fn = nt == 2 ? reinterpret_cast<const void*>(&k_select<Src, 2>) : reinterpret_cast<const void*>(&k_select<Src, 1>);
+    static bool attr_set[2] = {false, false};
+    if (!attr_set[nt - 1]) {
         DeviceInfo di;
         if (int e = device_info(&di)) return e;
         hipError_t he = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)di.max_lds);
         if (he != hipSuccess) return hip_fail(he, "hipFuncSetAttribute(select)");
-        attr_set = true;
+        attr_set[nt - 1] = true;
     }
     SelTgt t[2];
     for (int j = 0; j < 2; ++j) {
@@ -723,7 +785,8 @@ int launch_rows(const SelPlan& p, const Src& src, const SelOutput* out, int nt, 
     g.chunk_pad = p.chunk_pad;
     g.nt = nt;
     g.row_words = p.row_words;
-    g.ws = reinterpret_cast<uint32_t*>(ws);
+    g.ctrl = reinterpret_cast<uint32_t*>(ws_ctrl);
+    g.data = reinterpret_cast<uint32_t*>(ws_data);
     // The workgroups of a row wait for each other, so every workgroup of a
     // launch must be resident at once. A launch holds at most rows_per_launch
     // * S <= #CUs workgroups; check that the kernel fits one workgroup per CU
@@ -731,13 +794,13 @@ int launch_rows(const SelPlan& p, const Src& src, const SelOutput* out, int nt, 
     // Kernels on one stream run one after another, so the CUs are free when
     // the launch starts; a wait that still cannot finish gives up after a
     // bounded number of polls and flags the workspace status word.
-    static size_t checked_lds = 0;
-    if (checked_lds != p.lds_bytes) {
+    static size_t checked_lds[2] = {0, 0};
+    if (checked_lds[nt - 1] != p.lds_bytes) {
         int per_cu = 0;
         hipError_t he = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kSelThreads, p.lds_bytes);
         if (he != hipSuccess) return hip_fail(he, "hipOccupancyMaxActiveBlocksPerMultiprocessor(select)");
         if (per_cu < 1) return fail(INVALID, "select: kernel does not fit on a CU with this LDS size");
-        checked_lds = p.lds_bytes;
+        checked_lds[nt - 1] = p.lds_bytes;
     }
     Src s = src;
     for (int64_t r0 = 0; r0 < p.rows; r0 += p.rows_per_launch) {
@@ -752,45 +815,45 @@ int launch_rows(const SelPlan& p, const Src& src, const SelOutput* out, int nt, 
 }
 
 template <int KT, int QT, int D>
-int run_scan_typed(const SelPlan& p, int source, const ScanArgs& a, const SelOutput* out, int nt, void* ws,
-                   hipStream_t stream) {
+int run_scan_typed(const SelPlan& p, int source, const ScanArgs& a, const SelOutput* out, int nt, void* wc,
+                   void* wd, hipStream_t stream) {
     if (source == SRC_SCAN) {
         SrcScan<KT, QT, D> s{a.q, a.k, a.N, a.rows_per_seq, a.q_pos};
-        return launch_rows(p, s, out, nt, ws, stream);
+        return launch_rows(p, s, out, nt, wc, wd, stream);
     }
     SrcPool<KT, QT, D> s{a.q, a.k, a.N, a.pool, p.n};
-    return launch_rows(p, s, out, nt, ws, stream);
+    return launch_rows(p, s, out, nt, wc, wd, stream);
 }
 
 template <int KT, int QT>
-int run_scan_d(const SelPlan& p, int source, const ScanArgs& a, const SelOutput* out, int nt, void* ws,
-               hipStream_t stream) {
-    if (a.d_idx == 64) return run_scan_typed<KT, QT, 64>(p, source, a, out, nt, ws, stream);
-    if (a.d_idx == 128) return run_scan_typed<KT, QT, 128>(p, source, a, out, nt, ws, stream);
+int run_scan_d(const SelPlan& p, int source, const ScanArgs& a, const SelOutput* out, int nt, void* wc,
+               void* wd, hipStream_t stream) {
+    if (a.d_idx == 64) return run_scan_typed<KT, QT, 64>(p, source, a, out, nt, wc, wd, stream);
+    if (a.d_idx == 128) return run_scan_typed<KT, QT, 128>(p, source, a, out, nt, wc, wd, stream);
     return fail(INVALID, "d_idx must be 64 or 128");
 }
 
 template <int KT>
-int run_scan_q(const SelPlan& p, int source, const ScanArgs& a, const SelOutput* out, int nt, void* ws,
-               hipStream_t stream) {
-    if (a.q_dtype == kF32) return run_scan_d<KT, kF32>(p, source, a, out, nt, ws, stream);
-    if (a.q_dtype == kBF16) return run_scan_d<KT, kBF16>(p, source, a, out, nt, ws, stream);
+int run_scan_q(const SelPlan& p, int source, const ScanArgs& a, const SelOutput* out, int nt, void* wc,
+               void* wd, hipStream_t stream) {
+    if (a.q_dtype == kF32) return run_scan_d<KT, kF32>(p, source, a, out, nt, wc, wd, stream);
+    if (a.q_dtype == kBF16) return run_scan_d<KT, kBF16>(p, source, a, out, nt, wc, wd, stream);
     return fail(DTYPE, "indexer query dtype must be F32 or BF16");
 }
 
 }  // namespace
 
 int run_select(const SelPlan& p, int source, const ScanArgs& scan, const ScoresArgs& sc, const SelOutput* out,
-               int nt, void* ws, hipStream_t stream) {
+               int nt, void* ws_ctrl, void* ws_data, hipStream_t stream) {
     if (p.rows == 0) return OK;
     if (source == SRC_SCORES) {
         SrcScores s{sc.scores, sc.stride, sc.cand, p.n};
-        return launch_rows(p, s, out, nt, ws, stream);
+        return launch_rows(p, s, out, nt, ws_ctrl, ws_data, stream);
     }
     switch (scan.k_dtype) {
-        case kF32: return run_scan_q<kF32>(p, source, scan, out, nt, ws, stream);
-        case kBF16: return run_scan_q<kBF16>(p, source, scan, out, nt, ws, stream);
-        case kE4M3: return run_scan_q<kE4M3>(p, source, scan, out, nt, ws, stream);
+        case kF32: return run_scan_q<kF32>(p, source, scan, out, nt, ws_ctrl, ws_data, stream);
+        case kBF16: return run_scan_q<kBF16>(p, source, scan, out, nt, ws_ctrl, ws_data, stream);
+        case kE4M3: return run_scan_q<kE4M3>(p, source, scan, out, nt, ws_ctrl, ws_data, stream);
         default: return fail(DTYPE, "indexer key dtype must be F32, BF16 or E4M3");
     }
 }

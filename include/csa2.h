@@ -17,10 +17,13 @@
  *     the library never allocates, frees or retains device memory. Scratch
  *     comes from a caller-provided workspace sized by the matching
  *     *_workspace_bytes call.
- *   - Workspaces must be zero-filled before their first use. Every call that
- *     completes normally leaves the workspace's control words zero again, so
- *     one zero-fill at allocation is enough. One workspace must not be used by
- *     two calls that can run at the same time.
+ *   - Workspaces must be zero-filled before their first use. Every workspace
+ *     starts with a control region of fixed layout (about 8 MiB: counters and
+ *     histogram accumulators), and every call that completes normally leaves
+ *     it zero again, so one zero-fill at allocation is enough and one buffer
+ *     may serve calls of any kind and shape in turn, as long as it is large
+ *     enough for each. One workspace must not be used by two calls that can
+ *     run at the same time.
  *   - All work is enqueued on `stream` (a hipStream_t; NULL = default stream).
  *     No call synchronizes the host with the device.
  *   - Arguments are validated on the host before any HIP call. Device data

@@ -1,6 +1,7 @@
 """GPU parity of each libcsa2 call against the oracle, at sizes that span several
 tiles / chunks and a ragged tail, plus the edge cases of each step."""
 
+import ctypes
 import math
 
 import numpy as np
@@ -194,6 +195,45 @@ def test_topk_repeat_calls_reuse_workspace():
         assert np.array_equal(host(C.topk(s, 512)), a)
     ws = C.workspace(0, s.device, "topk")
     assert int(ws.view(torch.int32)[:64].abs().sum().item()) == 0        # status word clean
+
+
+def test_one_workspace_serves_calls_of_any_shape():
+    """One zero-filled buffer used in turn by top-K and attention calls of different shapes: the control
+    words sit at fixed offsets and every call leaves them zero, so no call sees another's data as counters."""
+    rng = np.random.default_rng(21)
+    cases = [(2, 65536, 100, "equal"), (6, 50000, 512, "normal"), (1, 300000, 8192, "normal"),
+             (40, 9000, 64, "ties"), (2, 65536, 100, "equal")]
+    scores = [_scores_with_ties(rng, r, n, kind) for r, n, _, kind in cases]
+    N = 6000
+    cache, okv = _kv_case(N, 77)
+    attn_cases = []
+    for Q, K in ((3, 2048), (300, 256), (2, 100)):
+        qb = synth.to_bf16_bits(rng.standard_normal((1, Q, 16, 128)).astype(np.float32))
+        idx = np.stack([np.sort(rng.choice(N, K, replace=False)) for _ in range(Q)]).astype(np.int32)[None]
+        attn_cases.append((qb, idx))
+    need = []
+    for (r, n, K, _) in cases:
+        nb = ctypes.c_size_t(0)
+        C.lib().csa2_topk_workspace_bytes(r, n, K, ctypes.byref(nb))
+        need.append(nb.value)
+    for qb, idx in attn_cases:
+        nb = ctypes.c_size_t(0)
+        C.lib().csa2_sparse_attn_workspace_bytes(1, qb.shape[1], 16, 128, idx.shape[-1], ctypes.byref(nb))
+        need.append(nb.value)
+    ws = torch.zeros(max(need), dtype=torch.uint8, device="cuda")
+    scale = float(np.float32(1 / math.sqrt(128)))
+    for i, ((r, n, K, _), s) in enumerate(zip(cases, scores)):
+        idx_t = host(C.topk(dev_f32(s), K, ws=ws))
+        for row in range(r):
+            ri, _ = o_topk(s[row], K)
+            assert np.array_equal(idx_t[row], ri), (i, row)
+        qb, idx = attn_cases[i % len(attn_cases)]
+        out = host(C.sparse_attn_fp4(dev_bf16(qb), cache, torch.from_numpy(idx).cuda(), softmax_scale=scale, ws=ws))
+        for qi in (0, qb.shape[1] - 1):
+            err = max_rel_err_rows(out[0, qi], o_attn(qb[0, qi], okv, idx[0, qi], scale))
+            assert err <= ATTN_TOL, (i, qi, err)
+    ctrl_bytes = (64 + 256 * 8256 + 256) * 4                               # the fixed control region
+    assert int(ws[:ctrl_bytes].view(torch.int32).abs().sum().item()) == 0
 
 
 # --------------------------------------------------------------- attention
