@@ -224,6 +224,53 @@ __device__ Found block_find(const uint32_t* hist, int nb, uint32_t need, uint32_
     return f;
 }
 
+// block_find over NT histograms at once (histogram j at hist + j * hstride,
+// target need[j]; need[j] = 0 skips it) with three block barriers in all.
+template <int NT>
+__device__ __forceinline__ void block_find_multi(const uint32_t* hist, int nb, int hstride, const uint32_t (&need)[2],
+                                                 uint32_t* sm, Found (&out)[2]) {
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
+    const int per = nb / kSelThreads;
+    const int top = nb - 1 - tid * per;
+    uint32_t s[2] = {0u, 0u}, inc[2] = {0u, 0u};
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+        for (int i = 0; i < per; ++i) s[j] += hist[j * hstride + top - i];
+        inc[j] = wave_incl_scan(s[j]);
+        if (lane == kWave - 1) sm[j * kSelWaves + wave] = inc[j];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+        uint32_t before = inc[j] - s[j], total = 0;
+        for (int w = 0; w < kSelWaves; ++w) {
+            const uint32_t t = sm[j * kSelWaves + w];
+            total += t;
+            if (w < wave) before += t;
+        }
+        out[j].total = total;
+        if (before < need[j] && need[j] <= before + s[j]) {
+            uint32_t c = before;
+            for (int i = 0; i < per; ++i) {
+                const uint32_t h = hist[j * hstride + top - i];
+                if (c + h >= need[j]) {
+                    sm[2 * kSelWaves + 2 * j] = (uint32_t)(top - i);
+                    sm[2 * kSelWaves + 2 * j + 1] = need[j] - c;
+                    break;
+                }
+                c += h;
+            }
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+        out[j].bin = sm[2 * kSelWaves + 2 * j];
+        out[j].rem = sm[2 * kSelWaves + 2 * j + 1];
+    }
+    __syncthreads();
+}
+
 __device__ __forceinline__ void push_hist(const uint32_t* lh, uint32_t* gh, int nb) {
     for (int b = threadIdx.x; b < nb; b += kSelThreads) {
         const uint32_t c = lh[b];
@@ -316,14 +363,17 @@ __global__ void __launch_bounds__(kSelThreads) k_select(Src src, SelDev g, SelTg
     }
     int path[2] = {kPathAll, kPathAll};
     uint32_t b1[2] = {0, 0}, rem[2] = {0, 0}, C[2] = {0, 0}, T[2] = {0, 0}, need[2] = {0, 0};
+    {
+        Found f[2];
+        block_find_multi<NT>(G, kB1, 0, M, sm, f);
 #pragma unroll
-    for (int j = 0; j < NT; ++j) {
-        const Found f = block_find(G, kB1, M[j], sm);
-        if (f.total > M[j]) {
-            b1[j] = f.bin;
-            rem[j] = f.rem;
-            C[j] = G[f.bin];
-            path[j] = (multi && C[j] <= (uint32_t)kCandCap) ? kPathList : kPathRadix;
+        for (int j = 0; j < NT; ++j) {
+            if (f[j].total > M[j]) {
+                b1[j] = f[j].bin;
+                rem[j] = f[j].rem;
+                C[j] = G[f[j].bin];
+                path[j] = (multi && C[j] <= (uint32_t)kCandCap) ? kPathList : kPathRadix;
+            }
         }
     }
     __syncthreads();                            // G (lh2) may be overwritten below
@@ -352,16 +402,17 @@ __global__ void __launch_bounds__(kSelThreads) k_select(Src src, SelDev g, SelTg
     // entries there in index order.
     if (any_list) {
         load_kreg();
-        // cnts[s][j] = (keys above b1, keys in b1) of chunk s
-        for (int i = tid; i < S * NT; i += kSelThreads) {
-            const int s = i / NT, j = i - s * NT;
-            if (pick<NT>(path[0], path[1], j) != kPathList) continue;
-            const uint32_t bj = pick<NT>(b1[0], b1[1], j);
-            const uint32_t* su = gsuf + (size_t)s * kB1;
-            const uint32_t at = ld_rlx(&su[bj]);
-            const uint32_t ab = bj + 1 < (uint32_t)kB1 ? ld_rlx(&su[bj + 1]) : 0u;
-            cnts[(s * 2 + j) * 2 + 0] = ab;
-            cnts[(s * 2 + j) * 2 + 1] = at - ab;
+        // cnts[s][j] = (keys above b1, keys in b1) of chunk s; the loads
+        // (S * NT <= 512 pairs, one per thread) stay in flight during the pass
+        const int si = tid / NT, sj = tid - si * NT;
+        const bool sl = tid < S * NT && pick<NT>(path[0], path[1], sj) == kPathList;
+        uint32_t s_at = 0u, s_ab = 0u;
+        if (sl) {
+            const uint32_t bj = pick<NT>(b1[0], b1[1], sj);
+            const uint32_t* su = gsuf + (size_t)si * kB1;
+            s_at = ld_rlx(&su[bj]);
+            s_ab = ld_rlx(&su[bj + 1 < (uint32_t)kB1 ? bj + 1 : bj]);
+            if (bj + 1 >= (uint32_t)kB1) s_ab = 0u;
         }
         // per-wave counts of keys above the bin and in it
         uint32_t above[2] = {0u, 0u}, ncand[2] = {0u, 0u};
@@ -379,6 +430,10 @@ __global__ void __launch_bounds__(kSelThreads) k_select(Src src, SelDev g, SelTg
                 }
             }
         }
+        if (sl) {
+            cnts[(si * 2 + sj) * 2 + 0] = s_ab;
+            cnts[(si * 2 + sj) * 2 + 1] = s_at - s_ab;
+        }
         uint32_t* wl = sm + 32;                 // [2][16] per-wave list bases
 #pragma unroll
         for (int j = 0; j < NT; ++j) {
@@ -393,19 +448,15 @@ __global__ void __launch_bounds__(kSelThreads) k_select(Src src, SelDev g, SelTg
         if (tid < NT && pick<NT>(path[0], path[1], tid) == kPathList) {
             uint32_t base = 0;
             for (int s = 0; s < split; ++s) base += cnts[(s * 2 + tid) * 2 + 1];
+            sm[200 + 2 * tid] = base;           // this chunk's range [lo, hi) of the row's list
             for (int w = 0; w < kSelWaves; ++w) {
                 const uint32_t n = wl[tid * kSelWaves + w];
                 wl[tid * kSelWaves + w] = base;
                 base += n;
             }
+            sm[201 + 2 * tid] = base;
         }
         __syncthreads();
-        // from here on cnts[s][j] counts (> T, == T): keys above the bin count
-        // as > T, and the list adds its entries once T is known
-        for (int i = tid; i < S * NT; i += kSelThreads) {
-            const int s = i / NT, j = i - s * NT;
-            if (pick<NT>(path[0], path[1], j) == kPathList) cnts[(s * 2 + j) * 2 + 1] = 0u;
-        }
 #pragma unroll
         for (int j = 0; j < NT; ++j) {
             if (path[j] != kPathList) continue;
@@ -415,14 +466,13 @@ __global__ void __launch_bounds__(kSelThreads) k_select(Src src, SelDev g, SelTg
             for (int t = 0; t < kMaxSteps; ++t) {
                 if (t >= nst) break;
                 const uint32_t kv[4] = {kreg[t].x, kreg[t].y, kreg[t].z, kreg[t].w};
-                const uint32_t ib = (uint32_t)(begin + w0 + t * kPadTo + 4 * lane);
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
                     const bool c = kv[u] != 0u && (kv[u] >> 21) == b1[j];
                     const uint64_t m = __ballot(c);
                     const uint32_t slot = run + lanes_below(m);
                     if (c && slot < (uint32_t)kCandCap)     // holds: the slots of a row sum to C[j] <= kCandCap
-                        st_rlx_u64(&lst[slot], ((uint64_t)(ib + u) << 32) | kv[u]);
+                        st_rlx_u64(&lst[slot], ((uint64_t)wave << 32) | kv[u]);   // (writer wave, key)
                     run += (uint32_t)__popcll(m);
                 }
             }
@@ -499,38 +549,78 @@ __global__ void __launch_bounds__(kSelThreads) k_select(Src src, SelDev g, SelTg
                 ent[j][r] = (path[j] == kPathList && e < (int)C[j]) ? ld_rlx_u64(&glist[(size_t)j * kCandCap + e]) : 0ull;
             }
         }
+        // both targets' digit histograms side by side: bits 10..20, then bits 0..9
+        uint32_t nd[2] = {0u, 0u};
+#pragma unroll
+        for (int j = 0; j < NT; ++j) nd[j] = path[j] == kPathList ? rem[j] : 0u;
+        for (int i = tid; i < NT * kB2; i += kSelThreads) lh2[i] = 0u;
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const uint32_t k = (uint32_t)ent[j][r];
+                if (k) atomicAdd(&lh2[j * kB2 + ((k >> 10) & 2047u)], 1u);
+            }
+        }
+        __syncthreads();
+        Found f2[2], f3[2];
+        block_find_multi<NT>(lh2, kB2, kB2, nd, sm, f2);
+        for (int i = tid; i < NT * kB3; i += kSelThreads) lh2[i] = 0u;
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+            nd[j] = path[j] == kPathList ? f2[j].rem : 0u;
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const uint32_t k = (uint32_t)ent[j][r];
+                if (k && ((k >> 10) & 2047u) == f2[j].bin) atomicAdd(&lh2[j * kB3 + (k & 1023u)], 1u);
+            }
+        }
+        __syncthreads();
+        block_find_multi<NT>(lh2, kB3, kB3, nd, sm, f3);
+        // Entries > T and == T, counted by list position with ballots: before
+        // this chunk's range (earlier chunks), anywhere (all chunks), and -
+        // attributed to the writer wave - inside this chunk's range. The
+        // per-wave sums go to lh2 (free once T is known).
 #pragma unroll
         for (int j = 0; j < NT; ++j) {
             if (path[j] != kPathList) continue;
-            for (int i = tid; i < kB2; i += kSelThreads) lh2[i] = 0u;
-            __syncthreads();
+            T[j] = (b1[j] << 21) | (f2[j].bin << 10) | f3[j].bin;
+            need[j] = f3[j].rem;
+            const uint32_t lo = sm[200 + 2 * j], hi = sm[201 + 2 * j];
+            uint32_t gt_before = 0, eq_before = 0, gt_all = 0, eq_all = 0;
 #pragma unroll
             for (int r = 0; r < R; ++r) {
+                const uint32_t e = (uint32_t)(tid + r * kSelThreads);
                 const uint32_t k = (uint32_t)ent[j][r];
-                if (k) atomicAdd(&lh2[(k >> 10) & 2047u], 1u);
+                const uint64_t mg = __ballot(k > T[j]), me = __ballot(k == T[j]);   // padding keys are 0 < T
+                if ((mg | me) == 0ull) continue;
+                const uint64_t mlo = __ballot(e < lo), mown = __ballot(e >= lo && e < hi);
+                gt_before += (uint32_t)__popcll(mg & mlo);
+                eq_before += (uint32_t)__popcll(me & mlo);
+                gt_all += (uint32_t)__popcll(mg);
+                eq_all += (uint32_t)__popcll(me);
+                const uint64_t mo = mown & (mg | me);
+                if (mo == 0ull) continue;
+                const uint32_t wt = (uint32_t)(ent[j][r] >> 32);
+                const uint32_t w0l = (uint32_t)__builtin_amdgcn_readlane((int)wt, (int)__builtin_ctzll(mo));
+                if ((__ballot(wt != w0l) & mo) == 0ull) {
+                    if (lane == 0) {
+                        const uint32_t ng = (uint32_t)__popcll(mg & mown), ne = (uint32_t)__popcll(me & mown);
+                        if (ng) atomicAdd(&wcnt[(j * kSelWaves + (int)w0l) * 2 + 0], ng);
+                        if (ne) atomicAdd(&wcnt[(j * kSelWaves + (int)w0l) * 2 + 1], ne);
+                    }
+                } else if ((mo >> lane) & 1ull) {
+                    atomicAdd(&wcnt[(j * kSelWaves + (int)wt) * 2 + (((mg >> lane) & 1ull) ? 0 : 1)], 1u);
+                }
             }
-            __syncthreads();
-            const Found f2 = block_find(lh2, kB2, rem[j], sm);
-            for (int i = tid; i < kB3; i += kSelThreads) lh2[i] = 0u;
-            __syncthreads();
-#pragma unroll
-            for (int r = 0; r < R; ++r) {
-                const uint32_t k = (uint32_t)ent[j][r];
-                if (k && ((k >> 10) & 2047u) == f2.bin) atomicAdd(&lh2[k & 1023u], 1u);
-            }
-            __syncthreads();
-            const Found f3 = block_find(lh2, kB3, f2.rem, sm);
-            T[j] = (b1[j] << 21) | (f2.bin << 10) | f3.bin;
-            need[j] = f3.rem;
-#pragma unroll
-            for (int r = 0; r < R; ++r) {
-                const uint32_t k = (uint32_t)ent[j][r];
-                if (!k || k < T[j]) continue;
-                const uint32_t ix = (uint32_t)(ent[j][r] >> 32);
-                const int s = (int)(ix / (uint32_t)g.chunk);
-                const int side = k > T[j] ? 0 : 1;
-                atomicAdd(&cnts[(s * 2 + j) * 2 + side], 1u);
-                if (s == split) atomicAdd(&wcnt[(j * kSelWaves + (int)(ix - (uint32_t)begin) / span) * 2 + side], 1u);
+            if (lane == 0) {
+                uint32_t* agg = lh2 + (j * kSelWaves + wave) * 4;
+                agg[0] = gt_before;
+                agg[1] = eq_before;
+                agg[2] = gt_all;
+                agg[3] = eq_all;
             }
         }
         __syncthreads();
@@ -597,17 +687,41 @@ __global__ void __launch_bounds__(kSelThreads) k_select(Src src, SelDev g, SelTg
         const int j = tid;
         const uint32_t nj = pick<NT>(need[0], need[1], j);
         uint32_t off = 0, eq_before = 0, total_sel = 0, my_take = 0, my_eq = 0;
-        for (int s = 0; s < S; ++s) {
-            const uint32_t gt = cnts[(s * 2 + j) * 2 + 0], eq = cnts[(s * 2 + j) * 2 + 1];
-            const uint32_t left = nj > eq_before ? nj - eq_before : 0u;
-            const uint32_t take = eq < left ? eq : left;
-            if (s < split) off += gt + take;
-            if (s == split) {
-                my_take = take;
-                my_eq = eq;
+        if (pick<NT>(path[0], path[1], j) == kPathList) {
+            // keys above bin b1 per chunk (cnts), plus the list counts by position;
+            // ties are taken in chunk order, so only the totals before this
+            // chunk and over all chunks matter
+            uint32_t ab_before = 0, ab_all = 0, lg_before = 0, le_before = 0, lg_all = 0, le_all = 0;
+            for (int s = 0; s < S; ++s) {
+                const uint32_t a = cnts[(s * 2 + j) * 2 + 0];
+                if (s < split) ab_before += a;
+                ab_all += a;
             }
-            total_sel += gt + take;
-            eq_before += eq;
+            for (int w = 0; w < kSelWaves; ++w) {
+                const uint32_t* agg = lh2 + (j * kSelWaves + w) * 4;
+                lg_before += agg[0];
+                le_before += agg[1];
+                lg_all += agg[2];
+                le_all += agg[3];
+            }
+            for (int w = 0; w < kSelWaves; ++w) my_eq += wcnt[(j * kSelWaves + w) * 2 + 1];
+            off = ab_before + lg_before + (le_before < nj ? le_before : nj);
+            my_take = nj > le_before ? nj - le_before : 0u;
+            if (my_take > my_eq) my_take = my_eq;
+            total_sel = ab_all + lg_all + (le_all < nj ? le_all : nj);
+        } else {
+            for (int s = 0; s < S; ++s) {
+                const uint32_t gt = cnts[(s * 2 + j) * 2 + 0], eq = cnts[(s * 2 + j) * 2 + 1];
+                const uint32_t left = nj > eq_before ? nj - eq_before : 0u;
+                const uint32_t take = eq < left ? eq : left;
+                if (s < split) off += gt + take;
+                if (s == split) {
+                    my_take = take;
+                    my_eq = eq;
+                }
+                total_sel += gt + take;
+                eq_before += eq;
+            }
         }
         uint32_t wb = off, web = 0;
         for (int w = 0; w < kSelWaves; ++w) {
