@@ -793,16 +793,17 @@ __global__ void __launch_bounds__(kSelThreads) k_select(Src src, SelDev g, SelTg
                 }
                 run_eq += eq_total;
             }
+            // one store per selected entry of the lane (usually none or one)
             uint32_t slot = run_sel + below;
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-                if ((selm >> u) & 1u) {
-                    if (slot < M[j]) {          // the bound holds whenever the counts agree
-                        out_idx[slot] = src.position(row, begin + ib + u);
-                        if (out_sc) out_sc[slot] = key_score(kv[u]);
-                    }
-                    ++slot;
+            while (selm) {
+                const int u = __builtin_ctz(selm);
+                selm &= selm - 1u;
+                if (slot < M[j]) {              // the bound holds whenever the counts agree
+                    out_idx[slot] = src.position(row, begin + ib + u);
+                    if (out_sc) out_sc[slot] = key_score(u == 0 ? kv[0] : u == 1 ? kv[1] : u == 2 ? kv[2] : kv[3]);
                 }
+                ++slot;
+            }
             run_sel += total;
         }
         if (split == S - 1) {
