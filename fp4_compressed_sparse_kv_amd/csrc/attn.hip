@@ -46,16 +46,19 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kAttnWaves = 8;
+constexpr int kAttnWaves = 4;
 constexpr int kAttnThreads = kAttnWaves * kWave;
 constexpr int kBlk = 32;
 constexpr int kMaxHeads = 16;
 constexpr int kD = 128;
 constexpr int kAttnTargetGroups = 256;          // one workgroup per CU of a 256-CU part
-constexpr int kMaxSplits = 16;
+constexpr int kMaxSplits = 8;
 constexpr int kPartFloats = kMaxHeads * kD + 2 * kMaxHeads;   // per (row, slice): acc [16][128], (m, l) [16][2]
 constexpr int kVRowBytes = 80;                  // staged V row: 64 code bytes + pad (conflict-free dword reads)
 constexpr int kMergeStride = kD + 4;
+constexpr int kCh = kMaxHeads * kD / kAttnThreads;  // output channels per thread in the merges
+constexpr int kV4 = kCh / 4;
+static_assert(kCh % 4 == 0 && kD % kCh == 0, "merge tiling");
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr uint32_t kRsrcWord3 = 0x00020000u;    // raw buffer resource (byte-addressed, 32-bit data format)
 constexpr int kCoherent = 16;                   // buffer cache policy sc1: device-coherent access
@@ -268,7 +271,7 @@ __device__ __forceinline__ void attend_block(WaveState& st, const BlockRaw& r, S
     }
 }
 
-__global__ void __launch_bounds__(kAttnThreads)
+__global__ void __launch_bounds__(kAttnThreads, 2)
 k_sparse_attn(const uint16_t* __restrict__ q, int32_t rows_per_seq, int32_t H, const uint8_t* __restrict__ k_codes,
               const uint8_t* __restrict__ k_scales, const uint8_t* __restrict__ v_codes,
               const uint8_t* __restrict__ v_scales, int64_t N, int64_t cs, int64_t ss, const int32_t* __restrict__ idx,
@@ -374,20 +377,24 @@ k_sparse_attn(const uint16_t* __restrict__ q, int32_t rows_per_seq, int32_t H, c
     }
     __syncthreads();
 
-    const int h = tid >> 5;                     // this thread's head and 4 channels
-    const int c0 = (tid & 31) * 4;
+    // this thread's head h and channels c0 .. c0 + kCh - 1
+    const int h = tid / (kD / kCh);
+    const int c0 = (tid % (kD / kCh)) * kCh;
     float M = -INFINITY;
 #pragma unroll
     for (int w = 0; w < kAttnWaves; ++w) M = fmaxf(M, lds.mg.m[w][h]);
     float L = 0.f;
-    f32x4 o = {0.f, 0.f, 0.f, 0.f};
+    f32x4 o[kV4];
+#pragma unroll
+    for (int v = 0; v < kV4; ++v) o[v] = f32x4{0.f, 0.f, 0.f, 0.f};
     if (M != -INFINITY) {
 #pragma unroll
         for (int w = 0; w < kAttnWaves; ++w) {
             const float mw = lds.mg.m[w][h];
             const float wt = (mw == -INFINITY) ? 0.f : exp2f(mw - M);
             L += wt * lds.mg.l[w][h];
-            o += wt * *reinterpret_cast<const f32x4*>(&lds.mg.acc[w][h][c0]);
+#pragma unroll
+            for (int v = 0; v < kV4; ++v) o[v] += wt * *reinterpret_cast<const f32x4*>(&lds.mg.acc[w][h][c0 + 4 * v]);
         }
     }
 
@@ -395,7 +402,8 @@ k_sparse_attn(const uint16_t* __restrict__ q, int32_t rows_per_seq, int32_t H, c
     if (NS == 1) {
         if (h < H) {
             const float inv = L > 0.f ? 1.f / L : 0.f;
-            *reinterpret_cast<f32x4*>(orow + h * kD + c0) = o * inv;
+#pragma unroll
+            for (int v = 0; v < kV4; ++v) *reinterpret_cast<f32x4*>(orow + h * kD + c0 + 4 * v) = o[v] * inv;
         }
         return;
     }
@@ -406,8 +414,11 @@ k_sparse_attn(const uint16_t* __restrict__ q, int32_t rows_per_seq, int32_t H, c
     const __amdgpu_buffer_rsrc_t rs =
         __builtin_amdgcn_make_buffer_rsrc(part_row, (short)0, NS * kPartFloats * 4, kRsrcWord3);
     const int mine = split * kPartFloats * 4;
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o), rs, mine + (h * kD + c0) * 4, 0, kCoherent);
-    if ((tid & 31) == 0) {
+#pragma unroll
+    for (int v = 0; v < kV4; ++v)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o[v]), rs, mine + (h * kD + c0 + 4 * v) * 4, 0,
+                                               kCoherent);
+    if (c0 == 0) {
         const f32x2 ml = {M, L};
         __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, ml), rs,
                                              mine + (kMaxHeads * kD + 2 * h) * 4, 0, kCoherent);
@@ -419,30 +430,36 @@ k_sparse_attn(const uint16_t* __restrict__ q, int32_t rows_per_seq, int32_t H, c
     if (!s_last) return;
 
     // slices beyond NS read past the resource's range and return zeros
-    u32x4 pa[kMaxSplits];
+    u32x4 pa[kMaxSplits][kV4];
     u32x2 pml[kMaxSplits];
 #pragma unroll
     for (int s = 0; s < kMaxSplits; ++s) {
-        pa[s] = __builtin_amdgcn_raw_buffer_load_b128(rs, (s * kPartFloats + h * kD + c0) * 4, 0, kCoherent);
+#pragma unroll
+        for (int v = 0; v < kV4; ++v)
+            pa[s][v] = __builtin_amdgcn_raw_buffer_load_b128(rs, (s * kPartFloats + h * kD + c0 + 4 * v) * 4, 0, kCoherent);
         pml[s] = __builtin_amdgcn_raw_buffer_load_b64(rs, (s * kPartFloats + kMaxHeads * kD + 2 * h) * 4, 0, kCoherent);
     }
     float MM = -INFINITY;
 #pragma unroll
     for (int s = 0; s < kMaxSplits; ++s) MM = fmaxf(MM, s < NS ? __uint_as_float(pml[s].x) : -INFINITY);
     float LL = 0.f;
-    f32x4 oo = {0.f, 0.f, 0.f, 0.f};
+    f32x4 oo[kV4];
+#pragma unroll
+    for (int v = 0; v < kV4; ++v) oo[v] = f32x4{0.f, 0.f, 0.f, 0.f};
     if (MM != -INFINITY) {
 #pragma unroll
         for (int s = 0; s < kMaxSplits; ++s) {
             const float ms = __uint_as_float(pml[s].x);
             const float wt = (s >= NS || ms == -INFINITY) ? 0.f : exp2f(ms - MM);
             LL += wt * __uint_as_float(pml[s].y);
-            oo += wt * __builtin_bit_cast(f32x4, pa[s]);
+#pragma unroll
+            for (int v = 0; v < kV4; ++v) oo[v] += wt * __builtin_bit_cast(f32x4, pa[s][v]);
         }
     }
     if (h < H) {
         const float inv = LL > 0.f ? 1.f / LL : 0.f;
-        *reinterpret_cast<f32x4*>(orow + h * kD + c0) = oo * inv;
+#pragma unroll
+        for (int v = 0; v < kV4; ++v) *reinterpret_cast<f32x4*>(orow + h * kD + c0 + 4 * v) = oo[v] * inv;
     }
     if (tid == 0) st_rlx(ctr, 0u);              // ready for the next launch
 }
