@@ -330,6 +330,14 @@ class Plan:
         _check(lib().csa2_prefill_workspace_bytes(self._h, B, Q, N, ctypes.byref(nb)), "csa2_prefill_workspace_bytes")
         return nb.value
 
+    def prefill_status(self, cache, Q):
+        """Device status word of the cached prefill workspace (synchronizes): 0 = clean; bit 1 = more rows
+        failed the candidate check than the exact repair pass holds (their top-K is not guaranteed)."""
+        nb = self.prefill_workspace_bytes(cache.B, Q, cache.N)
+        ws = workspace(nb, cache.codes.device, ("prefill", id(self)))
+        torch.cuda.synchronize(ws.device)
+        return int(ws[:4].view(torch.int32).item())
+
     def prefill_full(self, cache, q_idx, q, q_pos, idx_out=None, out=None, ws=None, stream=None):
         """Full-layer prefill: q_idx [B][Q][d_idx], q [B][Q][H][d] bf16, q_pos [B][Q] int64."""
         B, Q = q_pos.shape

@@ -515,13 +515,94 @@ int csa2_plan_run_decode(const csa2_plan* plan, const csa2_cache* cache, const c
     return OK;
 }
 
+}  // extern "C"
+
+namespace {
+
+// Prefill workspace: the control region, then (matrix-core indexer path) the
+// key maxima, the sample scores (later reused for the candidate lists), the
+// sample top-R, the thresholds and counters, the repair list and map, one
+// data region shared by the three select calls (they run one after another)
+// and the attention data; or (exact path) one select region and the attention.
+constexpr int32_t kSampleStride = 64;           // every 64th position is sampled
+constexpr int32_t kRepairRows = 64;             // rows the exact repair pass holds
+
+struct PrefillLayout {
+    bool mfma = false;
+    int64_t rows = 0, ns = 0;
+    int32_t R = 0, nr = 0, nrd = 0, cap = 0;
+    SelPlan sel_sample, sel_cand, sel_exact;
+    size_t off_kmax = 0, off_dense = 0, off_sidx = 0, off_ssc = 0, off_thr = 0, off_hi = 0, off_cnt = 0,
+           off_rep = 0, off_sel = 0, off_attn = 0, total = 0;
+};
+
+bool prefill_uses_mfma(const csa2_plan_params& p, int64_t N) {
+    return p.q_idx_dtype == CSA2_BF16 && (p.k_idx_dtype == CSA2_E4M3 || p.k_idx_dtype == CSA2_BF16) && p.d_idx == 64 &&
+           N >= 65536 && (int64_t)p.K * 16 <= N;
+}
+
+int prefill_layout(const csa2_plan* plan, int32_t B, int32_t Q, int64_t N, PrefillLayout* lay) {
+    const csa2_plan_params& p = plan->p;
+    lay->rows = (int64_t)B * Q;
+    lay->mfma = prefill_uses_mfma(p, N);
+    size_t off = align_up(kCtrlBytes);
+    if (!lay->mfma) {
+        if (int e = plan_select(lay->rows, N, 1024, &lay->sel_exact)) return e;
+        lay->off_sel = off;
+        off += align_up(lay->sel_exact.data_bytes);
+    } else {
+        const int64_t rows = lay->rows;
+        lay->ns = (N - kSampleStride / 2 + kSampleStride - 1) / kSampleStride;
+        lay->R = (int32_t)((2 * (int64_t)p.K * lay->ns + N - 1) / N);
+        if (lay->R < 1) lay->R = 1;
+        lay->nr = (int32_t)(N / 65536 < 1 ? 1 : (N / 65536 > 16 ? 16 : N / 65536));
+        lay->nrd = (int32_t)(lay->ns / 2048 < 1 ? 1 : (lay->ns / 2048 > 8 ? 8 : lay->ns / 2048));
+        int64_t cap = 4 * 2 * (int64_t)p.K / lay->nr;
+        if (cap < 512) cap = 512;
+        lay->cap = (int32_t)((cap + 63) / 64 * 64);
+        if (int e = plan_select(rows, lay->ns, 1024, &lay->sel_sample)) return e;
+        if (int e = plan_select(rows, (int64_t)lay->nr * lay->cap, 1024, &lay->sel_cand)) return e;
+        if (int e = plan_select(kRepairRows, N, 1024, &lay->sel_exact)) return e;
+        lay->off_kmax = off;
+        off += align_up(pf_kmax_floats(B) * 4);
+        lay->off_dense = off;                   // sample scores, then candidate lists
+        const size_t dense = (size_t)rows * lay->ns * 4, cand = (size_t)rows * lay->nr * lay->cap * 4;
+        off += align_up(dense > cand ? dense : cand);
+        lay->off_sidx = off;
+        off += align_up((size_t)rows * lay->R * 4);
+        lay->off_ssc = off;
+        off += align_up((size_t)rows * lay->R * 4);
+        lay->off_thr = off;
+        off += align_up((size_t)rows * 2 * 4);
+        lay->off_hi = off;
+        off += align_up((size_t)rows * 4);
+        lay->off_cnt = off;
+        off += align_up((size_t)rows * lay->nr * 4);
+        lay->off_rep = off;                     // [count][pad][kRepairRows rows][kRepairRows map]
+        off += align_up((size_t)(64 + 2 * kRepairRows) * 4);
+        lay->off_sel = off;
+        size_t sel = lay->sel_sample.data_bytes;
+        if (lay->sel_cand.data_bytes > sel) sel = lay->sel_cand.data_bytes;
+        if (lay->sel_exact.data_bytes > sel) sel = lay->sel_exact.data_bytes;
+        off += align_up(sel);
+    }
+    lay->off_attn = off;
+    off += align_up(attn_data_bytes(lay->rows, p.K));
+    lay->total = off;
+    return OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 int csa2_prefill_workspace_bytes(const csa2_plan* plan, int32_t B, int32_t Q, int64_t N, size_t* bytes) {
     g_err.clear();
     if (!plan || !bytes) return fail(INVALID, "csa2_prefill_workspace_bytes: null pointer");
     if (B < 1 || Q < 1 || N < 1) return fail(INVALID, "csa2_prefill_workspace_bytes: sizes must be >= 1");
-    SelPlan sp;
-    if (int e = plan_select((int64_t)B * Q, N, 1024, &sp)) return e;
-    *bytes = align_up(kCtrlBytes) + align_up(sp.data_bytes) + align_up(attn_data_bytes((int64_t)B * Q, plan->p.K));
+    PrefillLayout lay;
+    if (int e = prefill_layout(plan, B, Q, N, &lay)) return e;
+    *bytes = lay.total;
     return OK;
 }
 
@@ -537,13 +618,12 @@ int csa2_prefill_full(const csa2_plan* plan, const csa2_cache* cache, const void
         return e;
     if (int e = check_scan(q_idx, p.q_idx_dtype, cache->k_idx, p.k_idx_dtype, p.d_idx, "csa2_prefill_full")) return e;
     if (!q_pos || !idx_out || !out) return fail(INVALID, "csa2_prefill_full: null pointer");
-    const int64_t rows = (int64_t)B * Q;
-    SelPlan sp;
-    if (int e = plan_select(rows, N, 1024, &sp)) return e;
-    const size_t sel_off = align_up(kCtrlBytes), attn_off = sel_off + align_up(sp.data_bytes);
-    const size_t need = attn_off + align_up(attn_data_bytes(rows, p.K));
-    if (int e = check_ws(ws, ws_bytes, need, "csa2_prefill_full")) return e;
+    PrefillLayout lay;
+    if (int e = prefill_layout(plan, B, Q, N, &lay)) return e;
+    if (int e = check_ws(ws, ws_bytes, lay.total, "csa2_prefill_full")) return e;
+    if (lay.mfma && !aligned(q_idx, 16)) return fail(INVALID, "csa2_prefill_full: indexer query must be 16-byte aligned");
     uint8_t* wsb = reinterpret_cast<uint8_t*>(ws);
+    const int64_t rows = lay.rows;
     ScanArgs a;
     a.q = q_idx;
     a.k = reinterpret_cast<const uint8_t*>(cache->k_idx);
@@ -555,7 +635,67 @@ int csa2_prefill_full(const csa2_plan* plan, const csa2_cache* cache, const void
     a.d_idx = p.d_idx;
     ScoresArgs none;
     SelOutput o{idx_out, nullptr, p.K, p.K};
-    if (int e = run_select(sp, SRC_SCAN, a, none, &o, 1, wsb, wsb + sel_off, stream)) return e;
+    if (!lay.mfma) {
+        if (int e = run_select(lay.sel_exact, SRC_SCAN, a, none, &o, 1, wsb, wsb + lay.off_sel, stream)) return e;
+    } else {
+        const uint16_t* qb = reinterpret_cast<const uint16_t*>(q_idx);
+        float* kmax = reinterpret_cast<float*>(wsb + lay.off_kmax);
+        float* dense = reinterpret_cast<float*>(wsb + lay.off_dense);
+        int32_t* sidx = reinterpret_cast<int32_t*>(wsb + lay.off_sidx);
+        float* ssc = reinterpret_cast<float*>(wsb + lay.off_ssc);
+        float* thr = reinterpret_cast<float*>(wsb + lay.off_thr);
+        uint32_t* hi = reinterpret_cast<uint32_t*>(wsb + lay.off_hi);
+        uint32_t* cnt = reinterpret_cast<uint32_t*>(wsb + lay.off_cnt);
+        uint32_t* rep_count = reinterpret_cast<uint32_t*>(wsb + lay.off_rep);
+        int32_t* rep_rows = reinterpret_cast<int32_t*>(wsb + lay.off_rep) + 64;
+        int32_t* rep_map = rep_rows + kRepairRows;
+        int32_t* cand = reinterpret_cast<int32_t*>(wsb + lay.off_dense);   // reuses the sample scores
+        uint32_t* status = reinterpret_cast<uint32_t*>(wsb);
+        if (int e = launch_pf_kmax(a.k, p.k_idx_dtype, B, N, kmax, stream)) return e;
+        PfTiles t;
+        t.q = qb;
+        t.k = a.k;
+        t.N = N;
+        t.B = B;
+        t.Q = Q;
+        t.q_pos = q_pos;
+        t.key_off = kSampleStride / 2;
+        t.key_stride = kSampleStride;
+        t.nkeys = lay.ns;
+        t.nranges = lay.nrd;
+        t.dense = dense;
+        if (int e = launch_pf_tiles(t, p.k_idx_dtype, true, stream)) return e;
+        ScoresArgs sa;
+        sa.scores = dense;
+        sa.stride = lay.ns;
+        SelOutput so{sidx, ssc, lay.R, lay.R};
+        if (int e = run_select(lay.sel_sample, SRC_SCORES, a, sa, &so, 1, wsb, wsb + lay.off_sel, stream)) return e;
+        if (int e = launch_pf_thresholds(qb, rows, Q, ssc, lay.R, kmax, thr, hi, rep_count, stream)) return e;
+        t.key_off = 0;
+        t.key_stride = 1;
+        t.nkeys = N;
+        t.nranges = lay.nr;
+        t.dense = nullptr;
+        t.thr = thr;
+        t.cand = cand;
+        t.cap = lay.cap;
+        t.cnt = cnt;
+        t.hi = hi;
+        if (int e = launch_pf_tiles(t, p.k_idx_dtype, false, stream)) return e;
+        ScanArgs ca = a;
+        ca.cand = cand;
+        ca.cnt = cnt;
+        ca.nranges = lay.nr;
+        ca.cap = lay.cap;
+        if (int e = run_select(lay.sel_cand, SRC_CAND, ca, none, &o, 1, wsb, wsb + lay.off_sel, stream)) return e;
+        if (int e = launch_pf_verify(rows, lay.nr, lay.cap, cnt, hi, q_pos, N, p.K, rep_rows, rep_count, kRepairRows,
+                                     status, stream))
+            return e;
+        if (int e = launch_pf_repair_map(rep_rows, rep_count, 0, kRepairRows, rep_map, stream)) return e;
+        ScanArgs ra = a;
+        ra.rowmap = rep_map;
+        if (int e = run_select(lay.sel_exact, SRC_SCAN, ra, none, &o, 1, wsb, wsb + lay.off_sel, stream)) return e;
+    }
     AttnArgs at;
     at.q = q;
     at.rows = rows;
@@ -574,7 +714,7 @@ int csa2_prefill_full(const csa2_plan* plan, const csa2_cache* cache, const void
     at.K = p.K;
     at.scale = p.softmax_scale;
     at.out = out;
-    return launch_attn(at, wsb, wsb + attn_off, ws_bytes - attn_off, stream);
+    return launch_attn(at, wsb, wsb + lay.off_attn, lay.total - lay.off_attn, stream);
 }
 
 }  // extern "C"

@@ -123,6 +123,7 @@ __device__ __forceinline__ uint32_t add_rlx(uint32_t* p, uint32_t v) {
 // flags the status word and lets the kernel run to its end.
 constexpr uint32_t kSpinLimit = 1u << 20;
 constexpr uint32_t kStatusBarrierTimeout = 1u;
+constexpr uint32_t kStatusRepairOverflow = 2u;  // more prefill rows failed verification than the repair pass holds
 
 __device__ __forceinline__ void st_rlx_f32(float* p, float v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -54,7 +54,7 @@ struct SelPlan {
     size_t ws_bytes = 0;            // control region + data region
 };
 
-enum SelSource : int { SRC_SCORES = 0, SRC_SCAN = 1, SRC_POOL = 2 };
+enum SelSource : int { SRC_SCORES = 0, SRC_SCAN = 1, SRC_POOL = 2, SRC_CAND = 3 };
 
 // Plan a selection. `min_chunk` bounds how finely a row may be split.
 int plan_select(int64_t rows, int64_t n, int32_t min_chunk, SelPlan* out);
@@ -73,6 +73,10 @@ struct ScanArgs {                   // indexer keys scored inside the select ker
     int32_t rows_per_seq = 1;       // row r reads sequence r / rows_per_seq
     const int64_t* q_pos = nullptr; // causal limit per row, or null
     const int32_t* pool = nullptr;  // SRC_POOL: [rows][n] positions to score
+    const int32_t* cand = nullptr;  // SRC_CAND: [rows][nranges][cap] positions, valid below cnt
+    const uint32_t* cnt = nullptr;  //           [rows][nranges]
+    int32_t nranges = 0, cap = 0;
+    const int32_t* rowmap = nullptr;// scan sources: launch row -> query row (-1: none), or null
     int32_t q_dtype = 0, k_dtype = 0, d_idx = 64;
 };
 
@@ -88,6 +92,34 @@ struct ScoresArgs {                 // precomputed scores
 // data region of p.data_bytes bytes.
 int run_select(const SelPlan& p, int source, const ScanArgs& scan, const ScoresArgs& sc,
                const SelOutput* out, int nt, void* ws_ctrl, void* ws_data, hipStream_t stream);
+
+// --------------------------------------------------------- prefill indexer
+struct PfTiles {
+    const uint16_t* q = nullptr;    // [B*Q][64] bf16 indexer queries
+    const uint8_t* k = nullptr;     // [B][N][64] indexer keys
+    int64_t N = 0;
+    int32_t B = 0, Q = 0;
+    const int64_t* q_pos = nullptr;
+    int64_t key_off = 0, key_stride = 1, nkeys = 0;
+    int32_t nranges = 1;
+    float* dense = nullptr;         // dense mode output [B*Q][nkeys]
+    const float* thr = nullptr;     // candidate mode: [B*Q][2] (lo, hi)
+    int32_t* cand = nullptr;
+    int32_t cap = 0;
+    uint32_t* cnt = nullptr;
+    uint32_t* hi = nullptr;
+};
+size_t pf_kmax_floats(int32_t B);
+int launch_pf_kmax(const uint8_t* k, int k_dtype, int32_t B, int64_t N, float* partial, hipStream_t stream);
+int launch_pf_tiles(const PfTiles& t, int k_dtype, bool dense, hipStream_t stream);
+int launch_pf_thresholds(const uint16_t* q, int64_t rows, int32_t Q, const float* sel, int32_t R,
+                         const float* kmax_partial, float* thr, uint32_t* hi, uint32_t* repair_count,
+                         hipStream_t stream);
+int launch_pf_verify(int64_t rows, int32_t nranges, int32_t cap, const uint32_t* cnt, const uint32_t* hi,
+                     const int64_t* q_pos, int64_t N, int32_t K, int32_t* repair_rows, uint32_t* repair_count,
+                     int32_t repair_cap, uint32_t* status, hipStream_t stream);
+int launch_pf_repair_map(const int32_t* repair_rows, const uint32_t* repair_count, int32_t first, int32_t n,
+                         int32_t* map, hipStream_t stream);
 
 // ---------------------------------------------------------- other kernels
 int launch_quant(const uint16_t* x, int64_t rows, int32_t C, int64_t x_stride, uint8_t* codes,

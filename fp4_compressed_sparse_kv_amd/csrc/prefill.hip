@@ -1,0 +1,383 @@
+// Prefill indexer on gfx950 matrix cores: candidate positions for the top-K of
+// many queries per sequence (a chunk of Q queries scoring all N keys), for the
+// Full layer of a prefill.
+//
+// The exact score of a position is the dot product of the bf16 indexer query
+// and the key, rounded once to fp32; the exact top-K of each query is taken
+// by the select kernel over a short candidate list per query. The matrix
+// cores only decide which positions are candidates:
+//   1. k_pf_kmax: per sequence and channel, the largest |key| (partials).
+//   2. k_pf_tiles, dense mode: approximate scores s~ of every query against a
+//      sample of the keys (every 64th position); the select kernel then gives
+//      each query's R-th largest sample score t.
+//   3. k_pf_thresholds: per query, the margin e = 2^-14 * sum_i |q_i| kmax_i
+//      (+ 2^-120), which bounds twice the error of s~ plus one fp32 rounding
+//      with room to spare (the products bf16 x bf16 are exact in fp32 and the
+//      64 terms are summed in fp32: |s~ - s| <= 68 * 2^-23 * sum |q_i k_i|),
+//      and the thresholds lo = t - e, hi = t.
+//   4. k_pf_tiles, candidate mode: s~ of every query against every causal
+//      position; positions with s~ >= lo are appended, in position order, to
+//      one list per (query, key range); positions with s~ >= hi are counted.
+//   5. k_pf_verify: a query whose count of s~ >= hi is at least
+//      min(K, causal positions) has every member of its exact top-K (ties
+//      included) in its lists: such members have s >= s_K >= hi - e/2, hence
+//      s~ >= lo. Queries that fail this, or whose lists overflowed, are
+//      queued for the exact full-scan select.
+// Matrix-core tiles: a workgroup of 4 waves owns 128 queries of one sequence
+// and one key range; wave w owns query rows 32w..32w+31 and runs
+// v_mfma_f32_32x32x16_bf16 over 128-key tiles staged in LDS as bf16 (E4M3
+// keys convert exactly). The K dimension is permuted (lane group g holds
+// channels 32g..32g+31) so each lane reads 32 contiguous key bytes; the dot
+// product does not depend on the order of its terms beyond the bound above.
+#include "dot.hpp"
+#include "internal.hpp"
+
+namespace csa2 {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kPfThreads = 256;
+constexpr int kPfRows = 128;                    // query rows per workgroup
+constexpr int kPfKeys = 128;                    // keys per LDS tile
+constexpr int kPfDim = 64;                      // indexer dim of this path
+constexpr int kPfLdsStride = 72;                // bf16 per staged key row (64 + 8: conflict-free reads)
+constexpr int kKmaxBlocks = 64;                 // partial-max blocks per sequence
+
+// ------------------------------------------------------------------ kmax
+
+template <int KT>
+__global__ void __launch_bounds__(256) k_pf_kmax(const uint8_t* __restrict__ k, int64_t N, float* __restrict__ partial) {
+    // thread t reads 16 channels (16 * elem bytes) of keys t/4, t/4 + 64, ...
+    constexpr int EB = ElemBytes<KT>::v;
+    __shared__ float red[256][16];
+    const int seq = blockIdx.y, blk = blockIdx.x, t = threadIdx.x;
+    const int cg = t & 3;
+    const int64_t per = (N + kKmaxBlocks - 1) / kKmaxBlocks;
+    const int64_t t0 = blk * per, t1 = min(N, t0 + per);
+    float m[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) m[i] = 0.f;
+    const uint8_t* base = k + (size_t)seq * N * kPfDim * EB;
+    for (int64_t r = t0 + (t >> 2); r < t1; r += 64) {
+        const uint8_t* p = base + (size_t)r * kPfDim * EB + cg * 16 * EB;
+        if constexpr (KT == kE4M3) {
+            const uint4 w = *reinterpret_cast<const uint4*>(p);
+            const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)ws[j], false);
+                const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)ws[j], true);
+                m[4 * j + 0] = fmaxf(m[4 * j + 0], fabsf(a.x));
+                m[4 * j + 1] = fmaxf(m[4 * j + 1], fabsf(a.y));
+                m[4 * j + 2] = fmaxf(m[4 * j + 2], fabsf(b.x));
+                m[4 * j + 3] = fmaxf(m[4 * j + 3], fabsf(b.y));
+            }
+        } else {
+            const uint4 w0 = *reinterpret_cast<const uint4*>(p), w1 = *reinterpret_cast<const uint4*>(p + 16);
+            const uint32_t ws[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                m[2 * j + 0] = fmaxf(m[2 * j + 0], fabsf(__uint_as_float(ws[j] << 16)));
+                m[2 * j + 1] = fmaxf(m[2 * j + 1], fabsf(__uint_as_float(ws[j] & 0xFFFF0000u)));
+            }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) red[t][i] = m[i];
+    __syncthreads();
+    if (t < kPfDim) {
+        const int g = t / 16, i = t % 16;
+        float r = 0.f;
+        for (int u = g; u < 256; u += 4) r = fmaxf(r, red[u][i]);
+        partial[((size_t)seq * kKmaxBlocks + blk) * kPfDim + t] = r;
+    }
+}
+
+// ----------------------------------------------------------------- tiles
+
+struct PfTileArgs {
+    const uint16_t* q;                          // [rows][64] bf16 indexer queries
+    const uint8_t* k;                           // [seqs][N][64] keys
+    int64_t N;
+    int32_t Q;                                  // queries per sequence (row = seq * Q + i)
+    const int64_t* q_pos;                       // [rows] causal limit
+    int64_t key_off, key_stride, nkeys;         // key j of the set is position key_off + j * key_stride
+    int32_t nranges;
+    int64_t range_len;                          // keys per range (a multiple of kPfKeys)
+    float* dense;                               // dense mode: [rows][nkeys] scores (s~, -inf past q_pos)
+    const float* thr;                           // candidate mode: [rows][2] (lo, hi)
+    int32_t* cand;                              // [rows][nranges][cap] positions
+    int32_t cap;
+    uint32_t* cnt;                              // [rows][nranges] candidates found (may exceed cap)
+    uint32_t* hi;                               // [rows] count of s~ >= hi (accumulated)
+};
+
+template <int KT, bool DENSE>
+__global__ void __launch_bounds__(kPfThreads, 2) k_pf_tiles(PfTileArgs a) {
+    constexpr int EB = ElemBytes<KT>::v;
+    __shared__ __attribute__((aligned(16))) uint16_t tile[kPfKeys * kPfLdsStride];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = lane >> 5, ln = lane & 31;
+    const int qtiles = (a.Q + kPfRows - 1) / kPfRows;
+    const int seq = blockIdx.x / qtiles, qt = blockIdx.x - seq * qtiles;
+    const int range = blockIdx.y;
+    const int q0 = qt * kPfRows + wave * 32;    // this wave's first query (within the sequence)
+    const int64_t rbase = (int64_t)seq * a.Q;
+
+    // A operand: query q0 + ln, channels 32g + 8s .. 32g + 8s + 7 for k-step s
+    bf16x8 qa[4];
+    {
+        const int qi = min(q0 + ln, a.Q - 1);
+        const uint4* p = reinterpret_cast<const uint4*>(a.q + (rbase + qi) * kPfDim + 32 * g);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            uint4 w = p[s];
+            if (q0 + ln >= a.Q) w = make_uint4(0, 0, 0, 0);
+            qa[s] = __builtin_bit_cast(bf16x8, w);
+        }
+    }
+    // accumulator element i of this lane is query row rr(i) = 8*(i/4) + 4g + i%4 of the wave
+    float tlo[16], thi[16];
+    int32_t qp[16];
+    uint32_t cur[16], hic[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int qi = q0 + 8 * (i / 4) + 4 * g + (i % 4);
+        const bool ok = qi < a.Q;
+        const int64_t r = rbase + (ok ? qi : 0);
+        const int64_t pq = a.q_pos ? a.q_pos[r] : INT64_MAX;
+        qp[i] = ok ? (int32_t)(pq < 0 ? -1 : (pq >= a.N ? a.N - 1 : pq)) : -1;
+        if constexpr (!DENSE) {
+            tlo[i] = ok ? a.thr[2 * r + 0] : INFINITY;
+            thi[i] = ok ? a.thr[2 * r + 1] : INFINITY;
+        }
+        cur[i] = 0u;
+        hic[i] = 0u;
+    }
+
+    const uint8_t* kbase = a.k + (size_t)seq * a.N * kPfDim * EB;
+    const int64_t j0 = (int64_t)range * a.range_len;
+    const int64_t j1 = min(a.nkeys, j0 + a.range_len);
+    for (int64_t jt = j0; jt < j1; jt += kPfKeys) {
+        // ---- stage 128 keys as bf16: thread t converts half (t & 1) of key t / 2
+        {
+            const int64_t j = jt + (tid >> 1);
+            const int64_t pos = j < j1 ? a.key_off + j * a.key_stride : 0;
+            const uint8_t* src = kbase + (size_t)pos * kPfDim * EB + (tid & 1) * 32 * EB;
+            uint4* dst = reinterpret_cast<uint4*>(&tile[(tid >> 1) * kPfLdsStride + (tid & 1) * 32]);
+            if constexpr (KT == kE4M3) {
+                const uint4 w0 = *reinterpret_cast<const uint4*>(src), w1 = *reinterpret_cast<const uint4*>(src + 16);
+                const uint32_t ws[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+                uint32_t o[16];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)ws[u], false);
+                    const f32x2 hi2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)ws[u], true);
+                    // E4M3 values are exact in bf16: keep the top 16 bits of each fp32
+                    o[2 * u + 0] = (__float_as_uint(lo.x) >> 16) | (__float_as_uint(lo.y) & 0xFFFF0000u);
+                    o[2 * u + 1] = (__float_as_uint(hi2.x) >> 16) | (__float_as_uint(hi2.y) & 0xFFFF0000u);
+                }
+#pragma unroll
+                for (int u = 0; u < 4; ++u) dst[u] = make_uint4(o[4 * u], o[4 * u + 1], o[4 * u + 2], o[4 * u + 3]);
+            } else {
+#pragma unroll
+                for (int u = 0; u < 4; ++u) dst[u] = *reinterpret_cast<const uint4*>(src + 16 * u);
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int c = 0; c < kPfKeys / 32; ++c) {
+            f32x16 acc = {};
+            const uint16_t* brow = &tile[(32 * c + ln) * kPfLdsStride + 32 * g];
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const bf16x8 b = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(brow + 8 * s));
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[s], b, acc, 0, 0, 0);
+            }
+            const int64_t jk = jt + 32 * c + ln;
+            const bool kvalid = jk < j1;
+            const int64_t pos = a.key_off + jk * a.key_stride;
+            if constexpr (DENSE) {
+                if (kvalid) {
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const int qi = q0 + 8 * (i / 4) + 4 * g + (i % 4);
+                        if (qi < a.Q)
+                            a.dense[(size_t)(rbase + qi) * a.nkeys + jk] = pos <= (int64_t)qp[i] ? acc[i] : -INFINITY;
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const bool pass = kvalid && pos <= (int64_t)qp[i] && acc[i] >= tlo[i];
+                    const uint64_t m = __ballot(pass);
+                    if (m == 0ull) continue;
+                    const uint32_t mlo = (uint32_t)m, half = g ? (uint32_t)(m >> 32) : mlo;
+                    const uint32_t below = lanes_below(m) - (g ? (uint32_t)__popc(mlo) : 0u);
+                    const uint32_t slot = cur[i] + below;
+                    if (pass && slot < (uint32_t)a.cap) {
+                        const int qi = q0 + 8 * (i / 4) + 4 * g + (i % 4);
+                        a.cand[((size_t)(rbase + qi) * a.nranges + range) * a.cap + slot] = (int32_t)pos;
+                    }
+                    cur[i] += (uint32_t)__popc(half);
+                    const uint64_t mh = __ballot(pass && acc[i] >= thi[i]);
+                    hic[i] += (uint32_t)__popc(g ? (uint32_t)(mh >> 32) : (uint32_t)mh);
+                }
+            }
+        }
+        __syncthreads();
+    }
+    if constexpr (!DENSE) {
+        if (ln == 0) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int qi = q0 + 8 * (i / 4) + 4 * g + (i % 4);
+                if (qi < a.Q) {
+                    const int64_t r = rbase + qi;
+                    a.cnt[(size_t)r * a.nranges + range] = cur[i];
+                    if (hic[i]) atomicAdd(&a.hi[r], hic[i]);
+                }
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------ thresholds
+
+// One thread per query row: t = R-th largest sample score (the minimum of the
+// select's R outputs; -inf if fewer than R samples are causal), the margin
+// from the query and the per-channel key maxima, and a cleared hi counter.
+__global__ void __launch_bounds__(256)
+k_pf_thresholds(const uint16_t* __restrict__ q, int64_t rows, int32_t Q, const float* __restrict__ sel, int32_t R,
+                const float* __restrict__ kmax_partial, float* __restrict__ thr, uint32_t* __restrict__ hi,
+                uint32_t* __restrict__ repair_count) {
+    const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (r == 0) *repair_count = 0u;
+    if (r >= rows) return;
+    const int64_t seq = r / Q;
+    float t = INFINITY;
+    int n = 0;
+    for (int j = 0; j < R; ++j) {
+        const float v = sel[r * R + j];
+        if (v == v) {                           // the select pads with NaN
+            t = fminf(t, v);
+            ++n;
+        }
+    }
+    if (n < R) t = -INFINITY;
+    const float* kp = kmax_partial + (size_t)seq * kKmaxBlocks * kPfDim;
+    double s = 0.0;
+    for (int i = 0; i < kPfDim; ++i) {
+        float km = 0.f;
+        for (int b = 0; b < kKmaxBlocks; ++b) km = fmaxf(km, kp[b * kPfDim + i]);
+        s += fabs((double)bf16_bits_to_f32(q[r * kPfDim + i])) * (double)km;
+    }
+    const double e = s * 0x1p-14 + 0x1p-120;
+    thr[2 * r + 0] = t == -INFINITY ? -INFINITY : (float)((double)t - e);
+    thr[2 * r + 1] = t;
+    hi[r] = 0u;
+}
+
+// ----------------------------------------------------------------- verify
+
+// A query passes when its count of s~ >= hi reaches min(K, causal positions)
+// and no list of it overflowed; the others are appended to the repair list.
+__global__ void __launch_bounds__(256)
+k_pf_verify(int64_t rows, int32_t nranges, int32_t cap, const uint32_t* __restrict__ cnt,
+            const uint32_t* __restrict__ hi, const int64_t* __restrict__ q_pos, int64_t N, int32_t K,
+            int32_t* __restrict__ repair_rows, uint32_t* __restrict__ repair_count, int32_t repair_cap,
+            uint32_t* __restrict__ status) {
+    const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (r >= rows) return;
+    const int64_t pq = q_pos ? q_pos[r] : N - 1;
+    const int64_t valid = pq < 0 ? 0 : (pq >= N ? N : pq + 1);
+    bool ok = (int64_t)hi[r] >= (valid < K ? valid : (int64_t)K);
+    for (int j = 0; j < nranges; ++j) ok = ok && cnt[r * nranges + j] <= (uint32_t)cap;
+    if (!ok) {
+        const uint32_t slot = atomicAdd(repair_count, 1u);
+        if (slot < (uint32_t)repair_cap) repair_rows[slot] = (int32_t)r;
+        else __hip_atomic_fetch_or(status, kStatusRepairOverflow, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+// Repair map for one launch of the exact select: slots [first, first + n) of
+// the repair list, -1 where the list is shorter.
+__global__ void k_pf_repair_map(const int32_t* __restrict__ repair_rows, const uint32_t* __restrict__ repair_count,
+                                int32_t first, int32_t n, int32_t* __restrict__ map) {
+    const int i = threadIdx.x;
+    if (i < n) map[i] = (uint32_t)(first + i) < *repair_count ? repair_rows[first + i] : -1;
+}
+
+// ------------------------------------------------------------------- host
+
+size_t pf_kmax_floats(int32_t B) { return (size_t)B * kKmaxBlocks * kPfDim; }
+
+int launch_pf_kmax(const uint8_t* k, int k_dtype, int32_t B, int64_t N, float* partial, hipStream_t stream) {
+    const dim3 grid(kKmaxBlocks, (unsigned)B);
+    if (k_dtype == kE4M3) hipLaunchKernelGGL(k_pf_kmax<kE4M3>, grid, dim3(256), 0, stream, k, N, partial);
+    else hipLaunchKernelGGL(k_pf_kmax<kBF16>, grid, dim3(256), 0, stream, k, N, partial);
+    const hipError_t e = hipGetLastError();
+    return e == hipSuccess ? OK : hip_fail(e, "launch k_pf_kmax");
+}
+
+int launch_pf_tiles(const PfTiles& t, int k_dtype, bool dense, hipStream_t stream) {
+    PfTileArgs a;
+    a.q = t.q;
+    a.k = t.k;
+    a.N = t.N;
+    a.Q = t.Q;
+    a.q_pos = t.q_pos;
+    a.key_off = t.key_off;
+    a.key_stride = t.key_stride;
+    a.nkeys = t.nkeys;
+    a.nranges = t.nranges;
+    a.range_len = (t.nkeys + t.nranges - 1) / t.nranges;
+    a.range_len = (a.range_len + kPfKeys - 1) / kPfKeys * kPfKeys;
+    a.dense = t.dense;
+    a.thr = t.thr;
+    a.cand = t.cand;
+    a.cap = t.cap;
+    a.cnt = t.cnt;
+    a.hi = t.hi;
+    const int qtiles = (t.Q + kPfRows - 1) / kPfRows;
+    const dim3 grid((unsigned)((int64_t)t.B * qtiles), (unsigned)t.nranges);
+    if (k_dtype == kE4M3) {
+        if (dense) hipLaunchKernelGGL((k_pf_tiles<kE4M3, true>), grid, dim3(kPfThreads), 0, stream, a);
+        else hipLaunchKernelGGL((k_pf_tiles<kE4M3, false>), grid, dim3(kPfThreads), 0, stream, a);
+    } else {
+        if (dense) hipLaunchKernelGGL((k_pf_tiles<kBF16, true>), grid, dim3(kPfThreads), 0, stream, a);
+        else hipLaunchKernelGGL((k_pf_tiles<kBF16, false>), grid, dim3(kPfThreads), 0, stream, a);
+    }
+    const hipError_t e = hipGetLastError();
+    return e == hipSuccess ? OK : hip_fail(e, "launch k_pf_tiles");
+}
+
+int launch_pf_thresholds(const uint16_t* q, int64_t rows, int32_t Q, const float* sel, int32_t R,
+                         const float* kmax_partial, float* thr, uint32_t* hi, uint32_t* repair_count,
+                         hipStream_t stream) {
+    const unsigned blocks = (unsigned)((rows + 255) / 256);
+    hipLaunchKernelGGL(k_pf_thresholds, dim3(blocks > 0 ? blocks : 1), dim3(256), 0, stream, q, rows, Q, sel, R,
+                       kmax_partial, thr, hi, repair_count);
+    const hipError_t e = hipGetLastError();
+    return e == hipSuccess ? OK : hip_fail(e, "launch k_pf_thresholds");
+}
+
+int launch_pf_verify(int64_t rows, int32_t nranges, int32_t cap, const uint32_t* cnt, const uint32_t* hi,
+                     const int64_t* q_pos, int64_t N, int32_t K, int32_t* repair_rows, uint32_t* repair_count,
+                     int32_t repair_cap, uint32_t* status, hipStream_t stream) {
+    const unsigned blocks = (unsigned)((rows + 255) / 256);
+    hipLaunchKernelGGL(k_pf_verify, dim3(blocks > 0 ? blocks : 1), dim3(256), 0, stream, rows, nranges, cap, cnt, hi,
+                       q_pos, N, K, repair_rows, repair_count, repair_cap, status);
+    const hipError_t e = hipGetLastError();
+    return e == hipSuccess ? OK : hip_fail(e, "launch k_pf_verify");
+}
+
+int launch_pf_repair_map(const int32_t* repair_rows, const uint32_t* repair_count, int32_t first, int32_t n,
+                         int32_t* map, hipStream_t stream) {
+    hipLaunchKernelGGL(k_pf_repair_map, dim3(1), dim3(256), 0, stream, repair_rows, repair_count, first, n, map);
+    const hipError_t e = hipGetLastError();
+    return e == hipSuccess ? OK : hip_fail(e, "launch k_pf_repair_map");
+}
+
+}  // namespace csa2

@@ -55,6 +55,7 @@ struct SelDev {
     int32_t S, chunk, chunk_pad, row0, nt, row_words;
     uint32_t* ctrl;                             // workspace control region
     uint32_t* data;                             // this call's data region
+    const int32_t* rowmap;                      // launch row -> row (-1: nothing to do), or null
 };
 
 static_assert(kRowHdr + kB1 + 2 * kB2 + 2 * kB3 <= kSelCtrlRowWords, "select control words per row");
@@ -180,6 +181,57 @@ struct SrcPool {
         __syncthreads();
     }
     __device__ __forceinline__ int32_t position(int64_t row, int64_t i) const { return pool[row * P + i]; }
+};
+
+// Candidate lists of the prefill indexer: entry i of a row is slot i % cap of
+// list i / cap, valid below that list's count; entries are in position order.
+template <int KT, int QT, int D>
+struct SrcCand {
+    const void* q;
+    const uint8_t* k;
+    int64_t N;
+    int32_t rows_per_seq;
+    const int32_t* cand;
+    const uint32_t* cnt;
+    int32_t nranges, cap;
+
+    __device__ __forceinline__ int32_t entry(int64_t row, int i) const {
+        const int r = i / cap, sl = i - r * cap;
+        const uint32_t c = cnt[row * nranges + r];
+        return (uint32_t)sl < (c < (uint32_t)cap ? c : (uint32_t)cap) ? cand[(row * nranges + r) * cap + sl] : -1;
+    }
+
+    __device__ __forceinline__ void fill(int64_t row, int64_t begin, int cnt_, int cpad, uint32_t* keys,
+                                         uint32_t* hist) const {
+        using KS = KeySlice<KT, D>;
+        constexpr int QB = (QT == kBF16) ? 2 : 4;
+        constexpr int U = KS::RAW >= 4 ? 1 : 4 / KS::RAW;
+        const int quad = threadIdx.x >> 2, lq = threadIdx.x & 3;
+        double qd[D / 4];
+        load_query_slice<QT, D>(reinterpret_cast<const uint8_t*>(q) + row * (int64_t)(D * QB), lq, qd);
+        const uint8_t* kb = k + (row / rows_per_seq) * N * (int64_t)KS::ROW_BYTES;
+        for (int base = 0; base < cnt_; base += (kSelThreads / 4) * U) {
+            KS s[U];
+            bool ok[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int i = base + u * (kSelThreads / 4) + quad;
+                const int32_t pos = (i < cnt_) ? entry(row, (int)begin + i) : -1;
+                ok[u] = pos >= 0 && (int64_t)pos < N;
+                if (ok[u]) s[u].load(kb + (int64_t)pos * KS::ROW_BYTES, lq);
+                else for (int j = 0; j < KS::RAW; ++j) s[u].raw[j] = make_uint4(0, 0, 0, 0);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int i = base + u * (kSelThreads / 4) + quad;
+                const double v = quad_sum(s[u].dot(qd));
+                if (lq == 0 && i < cnt_) put_key(keys, hist, i, ok[u] ? score_key((float)v) : 0u);
+            }
+        }
+        pad_keys(keys, cnt_, cpad);
+        __syncthreads();
+    }
+    __device__ __forceinline__ int32_t position(int64_t row, int64_t i) const { return entry(row, (int)i); }
 };
 
 // ------------------------------------------------------------ block helpers
@@ -308,7 +360,8 @@ __global__ void __launch_bounds__(kSelThreads) k_select(Src src, SelDev g, SelTg
     const int S = g.S;
     const int lrow = blockIdx.x / S;
     const int split = blockIdx.x - lrow * S;
-    const int64_t row = (int64_t)g.row0 + lrow;
+    const int64_t row = g.rowmap ? (int64_t)g.rowmap[g.row0 + lrow] : (int64_t)g.row0 + lrow;
+    if (row < 0) return;                        // the same for every workgroup of the launch row
     const int64_t begin = (int64_t)split * g.chunk;
     const int cnt = (int)min((int64_t)g.chunk, g.n - begin);
     const int cpad = g.chunk_pad;
@@ -878,7 +931,7 @@ namespace {
 
 template <class Src>
 int launch_rows(const SelPlan& p, const Src& src, const SelOutput* out, int nt, void* ws_ctrl, void* ws_data,
-                hipStream_t stream) {
+                hipStream_t stream, const int32_t* rowmap = nullptr) {
     auto fn = nt == 2 ? reinterpret_cast<const void*>(&k_select<Src, 2>) : reinterpret_cast<const void*>(&k_select<Src, 1>);
     static bool attr_set[2] = {false, false};
     if (!attr_set[nt - 1]) {
@@ -902,6 +955,7 @@ int launch_rows(const SelPlan& p, const Src& src, const SelOutput* out, int nt, 
     g.row_words = p.row_words;
     g.ctrl = reinterpret_cast<uint32_t*>(ws_ctrl);
     g.data = reinterpret_cast<uint32_t*>(ws_data);
+    g.rowmap = rowmap;
     // The workgroups of a row wait for each other, so every workgroup of a
     // launch must be resident at once. A launch holds at most rows_per_launch
     // * S <= #CUs workgroups; check that the kernel fits one workgroup per CU
@@ -934,6 +988,10 @@ int run_scan_typed(const SelPlan& p, int source, const ScanArgs& a, const SelOut
                    void* wd, hipStream_t stream) {
     if (source == SRC_SCAN) {
         SrcScan<KT, QT, D> s{a.q, a.k, a.N, a.rows_per_seq, a.q_pos};
+        return launch_rows(p, s, out, nt, wc, wd, stream, a.rowmap);
+    }
+    if (source == SRC_CAND) {
+        SrcCand<KT, QT, D> s{a.q, a.k, a.N, a.rows_per_seq, a.cand, a.cnt, a.nranges, a.cap};
         return launch_rows(p, s, out, nt, wc, wd, stream);
     }
     SrcPool<KT, QT, D> s{a.q, a.k, a.N, a.pool, p.n};

@@ -13,6 +13,7 @@ from oracle import plan as OP
 from oracle import quant as OQ
 from oracle import scores as OS
 from oracle.attention import sparse_attn as o_attn
+from oracle.topk import topk as o_topk
 from tests.parity import ATTN_TOL, compare_topk, dev_bf16, dev_key, host, max_rel_err_rows
 
 pytestmark = pytest.mark.gpu
@@ -161,3 +162,72 @@ def test_prefill_full_causal():
             assert compare_topk(idx[b, i], r_idx[i], lambda p: s[p], cfg["K"]) == "exact"
             assert max_rel_err_rows(out[b, i], r_out[i]) <= ATTN_TOL
         assert (idx[b, 0] >= 0).sum() == 1 and idx[b, 0, 0] == 0       # query at position 0 sees only itself
+
+
+def _prefill_inputs(cfg, B, Q, q_pos):
+    qi = np.stack([synth.prefill_q_idx(cfg, b, Q) for b in range(B)])
+    qb = np.stack([synth.prefill_q_bf16(cfg, b, Q) for b in range(B)])
+    return qi, qb, torch.from_numpy(np.ascontiguousarray(q_pos)).cuda()
+
+
+def test_prefill_matrix_core_indexer_matches_oracle():
+    """N >= 65536 with bf16 queries and E4M3 keys takes the matrix-core candidate path; every row is
+    compared with the oracle's exact top-K (near-ties excused and counted) and sampled rows' attention."""
+    cfg = synth.small("stack_b4_n1m", B=2, N=70001, K=256, modes=("full",))
+    cache, _, ocache, _ = build_case(cfg)
+    B, Q, N, K = 2, 160, cfg["N"], cfg["K"]
+    rng = np.random.default_rng(5)
+    q_pos = np.stack([np.concatenate([[0, 10, 31, 32, 100, 255, 256, 4000, 40000, N - 1],
+                                      np.sort(rng.integers(N - 3000, N, Q - 10))]) for _ in range(B)]).astype(np.int64)
+    qi, qb, qp = _prefill_inputs(cfg, B, Q, q_pos)
+    plan = make_plan(cfg)
+    idx, out = plan.prefill_full(cache, dev_key(qi, cfg["q_idx_dtype"]), dev_bf16(qb), qp)
+    assert plan.prefill_status(cache, Q) == 0
+    idx, out = host(idx), host(out)
+    stats = {"exact": 0, "excused": 0}
+    for b in range(B):
+        for i in range(Q):
+            s = OS.index_scores(qi[b, i], cfg["q_idx_dtype"], ocache[b]["k_idx"], cfg["k_idx_dtype"],
+                                q_pos=int(q_pos[b, i]))
+            r_idx, _ = o_topk(s, K)
+            res = compare_topk(idx[b, i], r_idx, lambda p: s[p], K)
+            assert res in stats, (b, i, res)
+            stats[res] += 1
+            if i % 16 == 0:
+                ref = o_attn(qb[b, i], ocache[b], r_idx if res == "exact" else idx[b, i], SCALE)
+                assert max_rel_err_rows(out[b, i], ref) <= ATTN_TOL, (b, i)
+    assert stats["exact"] >= B * Q - 2, stats
+
+
+def _tied_cache(N, B=1):
+    """Indexer keys all equal (every score of a query ties): candidate lists overflow."""
+    kb = np.zeros((N, 128), dtype=np.uint16)
+    cache = C.KVCache(B, N, k_idx=dev_key(np.full((B, N, 64), 0x38, dtype=np.uint8), "e4m3"))   # 1.0 everywhere
+    for b in range(B):
+        cache.fill(dev_bf16(kb), dev_bf16(kb), row0=b * N)
+    return cache
+
+
+def test_prefill_repair_pass_takes_lowest_positions_on_ties():
+    cfg = synth.small("stack_b4_n1m", B=1, N=70001, K=256, modes=("full",))
+    N, K, Q = cfg["N"], cfg["K"], 40
+    cache = _tied_cache(N)
+    q_pos = np.array([[N - 1 - 7 * i for i in range(Q)]], dtype=np.int64)
+    qi, qb, qp = _prefill_inputs(cfg, 1, Q, q_pos)
+    plan = make_plan(cfg)
+    idx, _ = plan.prefill_full(cache, dev_key(qi, "bf16"), dev_bf16(qb), qp)
+    assert plan.prefill_status(cache, Q) == 0
+    idx = host(idx)
+    for i in range(Q):
+        assert np.array_equal(idx[0, i], np.arange(K)), i          # ties go to the lowest positions
+
+
+def test_prefill_reports_rows_beyond_the_repair_pass():
+    cfg = synth.small("stack_b4_n1m", B=1, N=70001, K=256, modes=("full",))
+    N, Q = cfg["N"], 100                                            # 100 failing rows > 64 repair slots
+    cache = _tied_cache(N)
+    q_pos = np.full((1, Q), N - 1, dtype=np.int64)
+    qi, qb, qp = _prefill_inputs(cfg, 1, Q, q_pos)
+    plan = make_plan(cfg)
+    plan.prefill_full(cache, dev_key(qi, "bf16"), dev_bf16(qb), qp)
+    assert plan.prefill_status(cache, Q) & 2
