@@ -532,7 +532,7 @@ struct PrefillLayout {
     int64_t rows = 0, ns = 0;
     int32_t R = 0, nr = 0, nrd = 0, cap = 0;
     SelPlan sel_sample, sel_cand, sel_exact;
-    size_t off_kmax = 0, off_dense = 0, off_sidx = 0, off_ssc = 0, off_thr = 0, off_hi = 0, off_cnt = 0,
+    size_t off_kmax = 0, off_dense = 0, off_sidx = 0, off_ssc = 0, off_thr = 0, off_csc = 0, off_cnt = 0,
            off_rep = 0, off_sel = 0, off_attn = 0, total = 0;
 };
 
@@ -574,8 +574,8 @@ int prefill_layout(const csa2_plan* plan, int32_t B, int32_t Q, int64_t N, Prefi
         off += align_up((size_t)rows * lay->R * 4);
         lay->off_thr = off;
         off += align_up((size_t)rows * 2 * 4);
-        lay->off_hi = off;
-        off += align_up((size_t)rows * 4);
+        lay->off_csc = off;                     // exact scores of the selected candidates
+        off += align_up((size_t)rows * p.K * 4);
         lay->off_cnt = off;
         off += align_up((size_t)rows * lay->nr * 4);
         lay->off_rep = off;                     // [count][pad][kRepairRows rows][kRepairRows map]
@@ -644,7 +644,7 @@ int csa2_prefill_full(const csa2_plan* plan, const csa2_cache* cache, const void
         int32_t* sidx = reinterpret_cast<int32_t*>(wsb + lay.off_sidx);
         float* ssc = reinterpret_cast<float*>(wsb + lay.off_ssc);
         float* thr = reinterpret_cast<float*>(wsb + lay.off_thr);
-        uint32_t* hi = reinterpret_cast<uint32_t*>(wsb + lay.off_hi);
+        float* csc = reinterpret_cast<float*>(wsb + lay.off_csc);
         uint32_t* cnt = reinterpret_cast<uint32_t*>(wsb + lay.off_cnt);
         uint32_t* rep_count = reinterpret_cast<uint32_t*>(wsb + lay.off_rep);
         int32_t* rep_rows = reinterpret_cast<int32_t*>(wsb + lay.off_rep) + 64;
@@ -670,7 +670,7 @@ int csa2_prefill_full(const csa2_plan* plan, const csa2_cache* cache, const void
         sa.stride = lay.ns;
         SelOutput so{sidx, ssc, lay.R, lay.R};
         if (int e = run_select(lay.sel_sample, SRC_SCORES, a, sa, &so, 1, wsb, wsb + lay.off_sel, stream)) return e;
-        if (int e = launch_pf_thresholds(qb, rows, Q, ssc, lay.R, kmax, thr, hi, rep_count, stream)) return e;
+        if (int e = launch_pf_thresholds(qb, rows, Q, ssc, lay.R, kmax, thr, rep_count, stream)) return e;
         t.key_off = 0;
         t.key_stride = 1;
         t.nkeys = N;
@@ -680,16 +680,16 @@ int csa2_prefill_full(const csa2_plan* plan, const csa2_cache* cache, const void
         t.cand = cand;
         t.cap = lay.cap;
         t.cnt = cnt;
-        t.hi = hi;
         if (int e = launch_pf_tiles(t, p.k_idx_dtype, false, stream)) return e;
         ScanArgs ca = a;
         ca.cand = cand;
         ca.cnt = cnt;
         ca.nranges = lay.nr;
         ca.cap = lay.cap;
-        if (int e = run_select(lay.sel_cand, SRC_CAND, ca, none, &o, 1, wsb, wsb + lay.off_sel, stream)) return e;
-        if (int e = launch_pf_verify(rows, lay.nr, lay.cap, cnt, hi, q_pos, N, p.K, rep_rows, rep_count, kRepairRows,
-                                     status, stream))
+        SelOutput oc{idx_out, csc, p.K, p.K};
+        if (int e = run_select(lay.sel_cand, SRC_CAND, ca, none, &oc, 1, wsb, wsb + lay.off_sel, stream)) return e;
+        if (int e = launch_pf_verify(rows, lay.nr, lay.cap, cnt, csc, thr, q_pos, N, p.K, rep_rows, rep_count,
+                                     kRepairRows, status, stream))
             return e;
         if (int e = launch_pf_repair_map(rep_rows, rep_count, 0, kRepairRows, rep_map, stream)) return e;
         ScanArgs ra = a;

@@ -103,21 +103,19 @@ struct PfTiles {
     int64_t key_off = 0, key_stride = 1, nkeys = 0;
     int32_t nranges = 1;
     float* dense = nullptr;         // dense mode output [B*Q][nkeys]
-    const float* thr = nullptr;     // candidate mode: [B*Q][2] (lo, hi)
+    const float* thr = nullptr;     // candidate mode: [B*Q][2] (lo, check bound)
     int32_t* cand = nullptr;
     int32_t cap = 0;
     uint32_t* cnt = nullptr;
-    uint32_t* hi = nullptr;
 };
 size_t pf_kmax_floats(int32_t B);
 int launch_pf_kmax(const uint8_t* k, int k_dtype, int32_t B, int64_t N, float* partial, hipStream_t stream);
 int launch_pf_tiles(const PfTiles& t, int k_dtype, bool dense, hipStream_t stream);
 int launch_pf_thresholds(const uint16_t* q, int64_t rows, int32_t Q, const float* sel, int32_t R,
-                         const float* kmax_partial, float* thr, uint32_t* hi, uint32_t* repair_count,
-                         hipStream_t stream);
-int launch_pf_verify(int64_t rows, int32_t nranges, int32_t cap, const uint32_t* cnt, const uint32_t* hi,
-                     const int64_t* q_pos, int64_t N, int32_t K, int32_t* repair_rows, uint32_t* repair_count,
-                     int32_t repair_cap, uint32_t* status, hipStream_t stream);
+                         const float* kmax_partial, float* thr, uint32_t* repair_count, hipStream_t stream);
+int launch_pf_verify(int64_t rows, int32_t nranges, int32_t cap, const uint32_t* cnt, const float* sel,
+                     const float* thr, const int64_t* q_pos, int64_t N, int32_t K, int32_t* repair_rows,
+                     uint32_t* repair_count, int32_t repair_cap, uint32_t* status, hipStream_t stream);
 int launch_pf_repair_map(const int32_t* repair_rows, const uint32_t* repair_count, int32_t first, int32_t n,
                          int32_t* map, hipStream_t stream);
 

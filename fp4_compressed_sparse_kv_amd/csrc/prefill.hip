@@ -11,18 +11,22 @@
 //      sample of the keys (every 64th position); the select kernel then gives
 //      each query's R-th largest sample score t.
 //   3. k_pf_thresholds: per query, the margin e = 2^-14 * sum_i |q_i| kmax_i
-//      (+ 2^-120), which bounds twice the error of s~ plus one fp32 rounding
-//      with room to spare (the products bf16 x bf16 are exact in fp32 and the
-//      64 terms are summed in fp32: |s~ - s| <= 68 * 2^-23 * sum |q_i k_i|),
-//      and the thresholds lo = t - e, hi = t.
+//      (+ 2^-120), which exceeds four times the error of s~ plus one fp32
+//      rounding (the products bf16 x bf16 are exact in fp32 and the 64 terms
+//      are summed in fp32: |s~ - S| <= 68 * 2^-23 * sum |q_i k_i| for the
+//      exact real dot S), the candidate threshold lo = t - e and the check
+//      bound v = t - e/2.
 //   4. k_pf_tiles, candidate mode: s~ of every query against every causal
 //      position; positions with s~ >= lo are appended, in position order, to
-//      one list per (query, key range); positions with s~ >= hi are counted.
-//   5. k_pf_verify: a query whose count of s~ >= hi is at least
-//      min(K, causal positions) has every member of its exact top-K (ties
-//      included) in its lists: such members have s >= s_K >= hi - e/2, hence
-//      s~ >= lo. Queries that fail this, or whose lists overflowed, are
-//      queued for the exact full-scan select.
+//      one list per (query, key range).
+//   5. The select kernel ranks each query's candidates by their exact scores.
+//   6. k_pf_verify: a position that is not a candidate has s~ < lo, so its
+//      exact fp32 score is below lo + e/2 = v. If the K-th largest exact
+//      score among the candidates is above v, no other position can enter
+//      the top-K or tie with its last member, so the result is the exact
+//      top-K; so it is too when the lists hold every causal position. Queries
+//      that fail both tests, or whose lists overflowed, are queued for the
+//      exact full-scan select.
 // Matrix-core tiles: a workgroup of 4 waves owns 128 queries of one sequence
 // and one key range; wave w owns query rows 32w..32w+31 and runs
 // v_mfma_f32_32x32x16_bf16 over 128-key tiles staged in LDS as bf16 (E4M3
@@ -106,17 +110,23 @@ struct PfTileArgs {
     int32_t nranges;
     int64_t range_len;                          // keys per range (a multiple of kPfKeys)
     float* dense;                               // dense mode: [rows][nkeys] scores (s~, -inf past q_pos)
-    const float* thr;                           // candidate mode: [rows][2] (lo, hi)
+    const float* thr;                           // candidate mode: [rows][2] (lo, v)
     int32_t* cand;                              // [rows][nranges][cap] positions
     int32_t cap;
     uint32_t* cnt;                              // [rows][nranges] candidates found (may exceed cap)
-    uint32_t* hi;                               // [rows] count of s~ >= hi (accumulated)
+};
+
+// Raw bytes of one thread's share of a 128-key tile: half (t & 1) of key t / 2.
+template <int KT>
+struct TileRaw {
+    static constexpr int W = 2 * ElemBytes<KT>::v;   // 16-byte words (32 channels)
+    uint4 w[W];
 };
 
 template <int KT, bool DENSE>
 __global__ void __launch_bounds__(kPfThreads, 2) k_pf_tiles(PfTileArgs a) {
     constexpr int EB = ElemBytes<KT>::v;
-    __shared__ __attribute__((aligned(16))) uint16_t tile[kPfKeys * kPfLdsStride];
+    __shared__ __attribute__((aligned(16))) uint16_t tile[2][kPfKeys * kPfLdsStride];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 5, ln = lane & 31;
     const int qtiles = (a.Q + kPfRows - 1) / kPfRows;
@@ -138,9 +148,10 @@ __global__ void __launch_bounds__(kPfThreads, 2) k_pf_tiles(PfTileArgs a) {
         }
     }
     // accumulator element i of this lane is query row rr(i) = 8*(i/4) + 4g + i%4 of the wave
-    float tlo[16], thi[16];
+    float tlo[16];
     int32_t qp[16];
-    uint32_t cur[16], hic[16];
+    uint32_t cur0[16], cur1[16];                // list lengths of the rows rr(i) of lane group 0 and 1 (uniform)
+    int32_t qmin = INT32_MAX, qmax = -1;        // over this wave's valid rows
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
         const int qi = q0 + 8 * (i / 4) + 4 * g + (i % 4);
@@ -148,96 +159,152 @@ __global__ void __launch_bounds__(kPfThreads, 2) k_pf_tiles(PfTileArgs a) {
         const int64_t r = rbase + (ok ? qi : 0);
         const int64_t pq = a.q_pos ? a.q_pos[r] : INT64_MAX;
         qp[i] = ok ? (int32_t)(pq < 0 ? -1 : (pq >= a.N ? a.N - 1 : pq)) : -1;
-        if constexpr (!DENSE) {
-            tlo[i] = ok ? a.thr[2 * r + 0] : INFINITY;
-            thi[i] = ok ? a.thr[2 * r + 1] : INFINITY;
+        if (ok) {
+            qmin = min(qmin, qp[i]);
+            qmax = max(qmax, qp[i]);
         }
-        cur[i] = 0u;
-        hic[i] = 0u;
+        if constexpr (!DENSE) tlo[i] = ok ? a.thr[2 * r + 0] : INFINITY;
+        cur0[i] = 0u;
+        cur1[i] = 0u;
+    }
+    for (int o = 32; o >= 1; o >>= 1) {
+        qmin = min(qmin, __shfl_xor(qmin, o));
+        qmax = max(qmax, __shfl_xor(qmax, o));
     }
 
     const uint8_t* kbase = a.k + (size_t)seq * a.N * kPfDim * EB;
+    // candidate list of row rr(i): cand_base + (8*(i/4) + i%4) * row_step
+    const size_t row_step = (size_t)a.nranges * a.cap;
+    const size_t cand_base = ((size_t)(rbase + q0 + 4 * g) * a.nranges + range) * a.cap;
     const int64_t j0 = (int64_t)range * a.range_len;
     const int64_t j1 = min(a.nkeys, j0 + a.range_len);
-    for (int64_t jt = j0; jt < j1; jt += kPfKeys) {
-        // ---- stage 128 keys as bf16: thread t converts half (t & 1) of key t / 2
-        {
-            const int64_t j = jt + (tid >> 1);
-            const int64_t pos = j < j1 ? a.key_off + j * a.key_stride : 0;
-            const uint8_t* src = kbase + (size_t)pos * kPfDim * EB + (tid & 1) * 32 * EB;
-            uint4* dst = reinterpret_cast<uint4*>(&tile[(tid >> 1) * kPfLdsStride + (tid & 1) * 32]);
-            if constexpr (KT == kE4M3) {
-                const uint4 w0 = *reinterpret_cast<const uint4*>(src), w1 = *reinterpret_cast<const uint4*>(src + 16);
-                const uint32_t ws[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-                uint32_t o[16];
+    const int64_t ntile = j1 > j0 ? (j1 - j0 + kPfKeys - 1) / kPfKeys : 0;
+
+    // Loads are unconditional (a tile past the range reloads the last one) so
+    // the compiler's wait counts stay exact across the two register sets.
+    auto load_raw = [&](int64_t t, TileRaw<KT>& r) {
+        const int64_t tt = t < ntile ? t : ntile - 1;
+        const int64_t j = j0 + tt * kPfKeys + (tid >> 1);
+        const int64_t pos = j < j1 ? a.key_off + j * a.key_stride : 0;
+        const uint8_t* src = kbase + (size_t)pos * kPfDim * EB + (tid & 1) * 32 * EB;
 #pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)ws[u], false);
-                    const f32x2 hi2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)ws[u], true);
-                    // E4M3 values are exact in bf16: keep the top 16 bits of each fp32
-                    o[2 * u + 0] = (__float_as_uint(lo.x) >> 16) | (__float_as_uint(lo.y) & 0xFFFF0000u);
-                    o[2 * u + 1] = (__float_as_uint(hi2.x) >> 16) | (__float_as_uint(hi2.y) & 0xFFFF0000u);
-                }
+        for (int u = 0; u < TileRaw<KT>::W; ++u) r.w[u] = *reinterpret_cast<const uint4*>(src + 16 * u);
+    };
+    auto stage = [&](const TileRaw<KT>& r, uint16_t* buf) {
+        uint4* dst = reinterpret_cast<uint4*>(&buf[(tid >> 1) * kPfLdsStride + (tid & 1) * 32]);
+        if constexpr (KT == kE4M3) {
+            const uint32_t ws[8] = {r.w[0].x, r.w[0].y, r.w[0].z, r.w[0].w, r.w[1].x, r.w[1].y, r.w[1].z, r.w[1].w};
+            uint32_t o[16];
 #pragma unroll
-                for (int u = 0; u < 4; ++u) dst[u] = make_uint4(o[4 * u], o[4 * u + 1], o[4 * u + 2], o[4 * u + 3]);
-            } else {
-#pragma unroll
-                for (int u = 0; u < 4; ++u) dst[u] = *reinterpret_cast<const uint4*>(src + 16 * u);
+            for (int u = 0; u < 8; ++u) {
+                const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)ws[u], false);
+                const f32x2 hi2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)ws[u], true);
+                // E4M3 values are exact in bf16: keep the top 16 bits of each fp32
+                o[2 * u + 0] = (__float_as_uint(lo.x) >> 16) | (__float_as_uint(lo.y) & 0xFFFF0000u);
+                o[2 * u + 1] = (__float_as_uint(hi2.x) >> 16) | (__float_as_uint(hi2.y) & 0xFFFF0000u);
             }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) dst[u] = make_uint4(o[4 * u], o[4 * u + 1], o[4 * u + 2], o[4 * u + 3]);
+        } else {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) dst[u] = r.w[u];
         }
-        __syncthreads();
+    };
+    auto compute = [&](const uint16_t* buf, int64_t t) {
+        const int64_t jt = j0 + t * kPfKeys;
+        const int64_t p_first = a.key_off + jt * a.key_stride;
+        const int64_t p_last = a.key_off + min(jt + kPfKeys - 1, j1 - 1) * a.key_stride;
+        if (!DENSE && p_first > (int64_t)qmax) return;           // no causal key for any row of the wave
+        const bool masked = p_last > (int64_t)qmin;              // some key is past some row's limit
+        const bool full = jt + kPfKeys <= j1;                    // every key of the tile is in the range
+        // all B operands of the tile first, then the four 32-key blocks' MFMA
+        // chains interleaved (independent accumulators keep the matrix core busy)
+        constexpr int NC = kPfKeys / 32;
+        bf16x8 bop[NC][4];
 #pragma unroll
-        for (int c = 0; c < kPfKeys / 32; ++c) {
-            f32x16 acc = {};
-            const uint16_t* brow = &tile[(32 * c + ln) * kPfLdsStride + 32 * g];
+        for (int c = 0; c < NC; ++c)
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const bf16x8 b = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(brow + 8 * s));
-                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[s], b, acc, 0, 0, 0);
-            }
+            for (int s = 0; s < 4; ++s)
+                bop[c][s] = __builtin_bit_cast(
+                    bf16x8, *reinterpret_cast<const uint4*>(&buf[(32 * c + ln) * kPfLdsStride + 32 * g + 8 * s]));
+        f32x16 accs[NC];
+#pragma unroll
+        for (int c = 0; c < NC; ++c) accs[c] = f32x16{};
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int c = 0; c < NC; ++c) accs[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[s], bop[c][s], accs[c], 0, 0, 0);
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            const f32x16 acc = accs[c];
             const int64_t jk = jt + 32 * c + ln;
             const bool kvalid = jk < j1;
-            const int64_t pos = a.key_off + jk * a.key_stride;
+            const int32_t pos = (int32_t)(a.key_off + jk * a.key_stride);
             if constexpr (DENSE) {
                 if (kvalid) {
 #pragma unroll
                     for (int i = 0; i < 16; ++i) {
                         const int qi = q0 + 8 * (i / 4) + 4 * g + (i % 4);
-                        if (qi < a.Q)
-                            a.dense[(size_t)(rbase + qi) * a.nkeys + jk] = pos <= (int64_t)qp[i] ? acc[i] : -INFINITY;
+                        if (qi < a.Q) a.dense[(size_t)(rbase + qi) * a.nkeys + jk] = pos <= qp[i] ? acc[i] : -INFINITY;
                     }
                 }
             } else {
+                // lanes 0..31 hold row rr(i) of lane group 0, lanes 32..63 that of group 1;
+                // each half appends its passing keys in lane (= position) order
+                auto emit = [&](int i, uint64_t m, bool pass) {
+                    const uint32_t n0 = (uint32_t)__popc((uint32_t)m), n1 = (uint32_t)__popc((uint32_t)(m >> 32));
+                    const uint32_t slot = (g ? cur1[i] : cur0[i]) + lanes_below(m) - (g ? n0 : 0u);
+                    if (pass && slot < (uint32_t)a.cap)
+                        a.cand[cand_base + (size_t)(8 * (i / 4) + (i % 4)) * row_step + slot] = pos;
+                    cur0[i] += n0;
+                    cur1[i] += n1;
+                };
+                if (full && !masked) {          // every key valid and causal for every row: one compare each
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const bool pass = kvalid && pos <= (int64_t)qp[i] && acc[i] >= tlo[i];
-                    const uint64_t m = __ballot(pass);
-                    if (m == 0ull) continue;
-                    const uint32_t mlo = (uint32_t)m, half = g ? (uint32_t)(m >> 32) : mlo;
-                    const uint32_t below = lanes_below(m) - (g ? (uint32_t)__popc(mlo) : 0u);
-                    const uint32_t slot = cur[i] + below;
-                    if (pass && slot < (uint32_t)a.cap) {
-                        const int qi = q0 + 8 * (i / 4) + 4 * g + (i % 4);
-                        a.cand[((size_t)(rbase + qi) * a.nranges + range) * a.cap + slot] = (int32_t)pos;
+                    for (int i = 0; i < 16; ++i) {
+                        const bool pass = acc[i] >= tlo[i];
+                        const uint64_t m = __ballot(pass);
+                        if (m != 0ull) emit(i, m, pass);
                     }
-                    cur[i] += (uint32_t)__popc(half);
-                    const uint64_t mh = __ballot(pass && acc[i] >= thi[i]);
-                    hic[i] += (uint32_t)__popc(g ? (uint32_t)(mh >> 32) : (uint32_t)mh);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const bool pass = (int)kvalid & (int)(pos <= qp[i]) & (int)(acc[i] >= tlo[i]);
+                        const uint64_t m = __ballot(pass);
+                        if (m != 0ull) emit(i, m, pass);
+                    }
                 }
             }
         }
+    };
+
+    // Pipeline: tile t is computed from LDS buffer t & 1 while the raw bytes
+    // of tile t + 2 load into one register set and those of tile t + 1 (loaded
+    // one tile earlier, in the other set) are converted into the other buffer.
+    if (ntile > 0) {
+        TileRaw<KT> r0, r1;
+        load_raw(0, r0);
+        load_raw(1, r1);
+        stage(r0, tile[0]);
         __syncthreads();
+        for (int64_t t = 0; t < ntile; t += 2) {
+            load_raw(t + 2, r0);
+            compute(tile[0], t);
+            if (t + 1 < ntile) stage(r1, tile[1]);
+            __syncthreads();
+            if (t + 1 >= ntile) break;
+            load_raw(t + 3, r1);
+            compute(tile[1], t + 1);
+            if (t + 2 < ntile) stage(r0, tile[0]);
+            __syncthreads();
+        }
     }
     if constexpr (!DENSE) {
         if (ln == 0) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const int qi = q0 + 8 * (i / 4) + 4 * g + (i % 4);
-                if (qi < a.Q) {
-                    const int64_t r = rbase + qi;
-                    a.cnt[(size_t)r * a.nranges + range] = cur[i];
-                    if (hic[i]) atomicAdd(&a.hi[r], hic[i]);
-                }
+                if (qi < a.Q) a.cnt[(size_t)(rbase + qi) * a.nranges + range] = g ? cur1[i] : cur0[i];
             }
         }
     }
@@ -247,11 +314,10 @@ __global__ void __launch_bounds__(kPfThreads, 2) k_pf_tiles(PfTileArgs a) {
 
 // One thread per query row: t = R-th largest sample score (the minimum of the
 // select's R outputs; -inf if fewer than R samples are causal), the margin
-// from the query and the per-channel key maxima, and a cleared hi counter.
+// from the query and the per-channel key maxima, lo and v.
 __global__ void __launch_bounds__(256)
 k_pf_thresholds(const uint16_t* __restrict__ q, int64_t rows, int32_t Q, const float* __restrict__ sel, int32_t R,
-                const float* __restrict__ kmax_partial, float* __restrict__ thr, uint32_t* __restrict__ hi,
-                uint32_t* __restrict__ repair_count) {
+                const float* __restrict__ kmax_partial, float* __restrict__ thr, uint32_t* __restrict__ repair_count) {
     const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (r == 0) *repair_count = 0u;
     if (r >= rows) return;
@@ -275,25 +341,45 @@ k_pf_thresholds(const uint16_t* __restrict__ q, int64_t rows, int32_t Q, const f
     }
     const double e = s * 0x1p-14 + 0x1p-120;
     thr[2 * r + 0] = t == -INFINITY ? -INFINITY : (float)((double)t - e);
-    thr[2 * r + 1] = t;
-    hi[r] = 0u;
+    thr[2 * r + 1] = t == -INFINITY ? -INFINITY : (float)((double)t - 0.5 * e);
 }
 
 // ----------------------------------------------------------------- verify
 
-// A query passes when its count of s~ >= hi reaches min(K, causal positions)
-// and no list of it overflowed; the others are appended to the repair list.
+// See step 6 above; sel holds the exact scores the select returned ([rows][K],
+// NaN past the selected ones). One wave per query row.
 __global__ void __launch_bounds__(256)
-k_pf_verify(int64_t rows, int32_t nranges, int32_t cap, const uint32_t* __restrict__ cnt,
-            const uint32_t* __restrict__ hi, const int64_t* __restrict__ q_pos, int64_t N, int32_t K,
+k_pf_verify(int64_t rows, int32_t nranges, int32_t cap, const uint32_t* __restrict__ cnt, const float* __restrict__ sel,
+            const float* __restrict__ thr, const int64_t* __restrict__ q_pos, int64_t N, int32_t K,
             int32_t* __restrict__ repair_rows, uint32_t* __restrict__ repair_count, int32_t repair_cap,
             uint32_t* __restrict__ status) {
-    const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int lane = threadIdx.x & 63;
+    const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (r >= rows) return;
+    float sk = INFINITY;
+    uint32_t n = 0;
+    for (int j = lane; j < K; j += 64) {
+        const float v = sel[r * K + j];
+        if (v == v) {
+            sk = fminf(sk, v);
+            ++n;
+        }
+    }
+    for (int o = 32; o >= 1; o >>= 1) {
+        sk = fminf(sk, __shfl_xor(sk, o));
+        n += __shfl_xor(n, o);
+    }
+    if (lane != 0) return;
     const int64_t pq = q_pos ? q_pos[r] : N - 1;
     const int64_t valid = pq < 0 ? 0 : (pq >= N ? N : pq + 1);
-    bool ok = (int64_t)hi[r] >= (valid < K ? valid : (int64_t)K);
-    for (int j = 0; j < nranges; ++j) ok = ok && cnt[r * nranges + j] <= (uint32_t)cap;
+    int64_t total = 0;
+    bool overflow = false;
+    for (int j = 0; j < nranges; ++j) {
+        const uint32_t c = cnt[r * nranges + j];
+        total += c;
+        overflow = overflow || c > (uint32_t)cap;
+    }
+    const bool ok = !overflow && (total == valid || (n == (uint32_t)K && sk > thr[2 * r + 1]));
     if (!ok) {
         const uint32_t slot = atomicAdd(repair_count, 1u);
         if (slot < (uint32_t)repair_cap) repair_rows[slot] = (int32_t)r;
@@ -339,7 +425,6 @@ int launch_pf_tiles(const PfTiles& t, int k_dtype, bool dense, hipStream_t strea
     a.cand = t.cand;
     a.cap = t.cap;
     a.cnt = t.cnt;
-    a.hi = t.hi;
     const int qtiles = (t.Q + kPfRows - 1) / kPfRows;
     const dim3 grid((unsigned)((int64_t)t.B * qtiles), (unsigned)t.nranges);
     if (k_dtype == kE4M3) {
@@ -354,21 +439,20 @@ int launch_pf_tiles(const PfTiles& t, int k_dtype, bool dense, hipStream_t strea
 }
 
 int launch_pf_thresholds(const uint16_t* q, int64_t rows, int32_t Q, const float* sel, int32_t R,
-                         const float* kmax_partial, float* thr, uint32_t* hi, uint32_t* repair_count,
-                         hipStream_t stream) {
+                         const float* kmax_partial, float* thr, uint32_t* repair_count, hipStream_t stream) {
     const unsigned blocks = (unsigned)((rows + 255) / 256);
     hipLaunchKernelGGL(k_pf_thresholds, dim3(blocks > 0 ? blocks : 1), dim3(256), 0, stream, q, rows, Q, sel, R,
-                       kmax_partial, thr, hi, repair_count);
+                       kmax_partial, thr, repair_count);
     const hipError_t e = hipGetLastError();
     return e == hipSuccess ? OK : hip_fail(e, "launch k_pf_thresholds");
 }
 
-int launch_pf_verify(int64_t rows, int32_t nranges, int32_t cap, const uint32_t* cnt, const uint32_t* hi,
-                     const int64_t* q_pos, int64_t N, int32_t K, int32_t* repair_rows, uint32_t* repair_count,
-                     int32_t repair_cap, uint32_t* status, hipStream_t stream) {
-    const unsigned blocks = (unsigned)((rows + 255) / 256);
-    hipLaunchKernelGGL(k_pf_verify, dim3(blocks > 0 ? blocks : 1), dim3(256), 0, stream, rows, nranges, cap, cnt, hi,
-                       q_pos, N, K, repair_rows, repair_count, repair_cap, status);
+int launch_pf_verify(int64_t rows, int32_t nranges, int32_t cap, const uint32_t* cnt, const float* sel,
+                     const float* thr, const int64_t* q_pos, int64_t N, int32_t K, int32_t* repair_rows,
+                     uint32_t* repair_count, int32_t repair_cap, uint32_t* status, hipStream_t stream) {
+    const unsigned blocks = (unsigned)((rows + 3) / 4);
+    hipLaunchKernelGGL(k_pf_verify, dim3(blocks > 0 ? blocks : 1), dim3(256), 0, stream, rows, nranges, cap, cnt, sel,
+                       thr, q_pos, N, K, repair_rows, repair_count, repair_cap, status);
     const hipError_t e = hipGetLastError();
     return e == hipSuccess ? OK : hip_fail(e, "launch k_pf_verify");
 }

@@ -201,34 +201,70 @@ struct SrcCand {
         return (uint32_t)sl < (c < (uint32_t)cap ? c : (uint32_t)cap) ? cand[(row * nranges + r) * cap + sl] : -1;
     }
 
+    // Only the valid slots are visited: the chunk's keys start at 0 (padding)
+    // and each valid slot (list r, slot sl) writes its key at entry r*cap + sl.
     __device__ __forceinline__ void fill(int64_t row, int64_t begin, int cnt_, int cpad, uint32_t* keys,
                                          uint32_t* hist) const {
         using KS = KeySlice<KT, D>;
         constexpr int QB = (QT == kBF16) ? 2 : 4;
-        constexpr int U = KS::RAW >= 4 ? 1 : 4 / KS::RAW;
+        constexpr int U = KS::RAW >= 4 ? 2 : 8 / KS::RAW;
+        constexpr int kMaxLists = 16;
         const int quad = threadIdx.x >> 2, lq = threadIdx.x & 3;
+        for (int i = threadIdx.x; i < cpad; i += kSelThreads) keys[i] = 0u;
         double qd[D / 4];
         load_query_slice<QT, D>(reinterpret_cast<const uint8_t*>(q) + row * (int64_t)(D * QB), lq, qd);
         const uint8_t* kb = k + (row / rows_per_seq) * N * (int64_t)KS::ROW_BYTES;
-        for (int base = 0; base < cnt_; base += (kSelThreads / 4) * U) {
+        // entries [begin, begin + cnt_) of the row cover lists r0 .. r1 - 1 (a chunk is whole lists or a part of one)
+        uint32_t lo[kMaxLists], nv[kMaxLists];  // per list: first valid entry, number of valid entries in this chunk
+        uint32_t total = 0;
+#pragma unroll
+        for (int r = 0; r < kMaxLists; ++r) {
+            lo[r] = 0u;
+            nv[r] = 0u;
+            if (r < nranges) {
+                const uint32_t c = cnt[row * nranges + r];
+                const int64_t e0 = (int64_t)r * cap, e1 = e0 + (c < (uint32_t)cap ? c : (uint32_t)cap);
+                const int64_t a0 = e0 > begin ? e0 : begin, a1 = e1 < begin + cnt_ ? e1 : begin + cnt_;
+                if (a1 > a0) {
+                    lo[r] = (uint32_t)(a0 - begin);
+                    nv[r] = (uint32_t)(a1 - a0);
+                }
+            }
+            total += nv[r];
+        }
+        __syncthreads();                        // the zero fill is complete before valid keys land
+        for (uint32_t base = 0; base < total; base += (kSelThreads / 4) * U) {
             KS s[U];
-            bool ok[U];
+            int32_t ent[U];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const int i = base + u * (kSelThreads / 4) + quad;
-                const int32_t pos = (i < cnt_) ? entry(row, (int)begin + i) : -1;
-                ok[u] = pos >= 0 && (int64_t)pos < N;
-                if (ok[u]) s[u].load(kb + (int64_t)pos * KS::ROW_BYTES, lq);
-                else for (int j = 0; j < KS::RAW; ++j) s[u].raw[j] = make_uint4(0, 0, 0, 0);
+                const uint32_t v = base + u * (kSelThreads / 4) + quad;     // v-th valid entry of the chunk
+                ent[u] = -1;
+                int32_t pos = -1;
+                if (v < total) {
+                    uint32_t rest = v;
+#pragma unroll
+                    for (int r = 0; r < kMaxLists; ++r) {
+                        if (ent[u] < 0 && rest < nv[r]) ent[u] = (int32_t)(lo[r] + rest);
+                        else if (ent[u] < 0) rest -= nv[r];
+                    }
+                    const int64_t e = begin + ent[u];
+                    const int r = (int)(e / cap), sl = (int)(e - (int64_t)r * cap);
+                    pos = cand[(row * nranges + r) * cap + sl];
+                }
+                if (pos >= 0 && (int64_t)pos < N) {
+                    s[u].load(kb + (int64_t)pos * KS::ROW_BYTES, lq);
+                } else {
+                    for (int j = 0; j < KS::RAW; ++j) s[u].raw[j] = make_uint4(0, 0, 0, 0);
+                    ent[u] = -1;                // no position: the entry stays padding
+                }
             }
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const int i = base + u * (kSelThreads / 4) + quad;
                 const double v = quad_sum(s[u].dot(qd));
-                if (lq == 0 && i < cnt_) put_key(keys, hist, i, ok[u] ? score_key((float)v) : 0u);
+                if (lq == 0 && ent[u] >= 0) put_key(keys, hist, ent[u], score_key((float)v));
             }
         }
-        pad_keys(keys, cnt_, cpad);
         __syncthreads();
     }
     __device__ __forceinline__ int32_t position(int64_t row, int64_t i) const { return entry(row, (int)i); }
@@ -912,15 +948,16 @@ int plan_select(int64_t rows, int64_t n, int32_t min_chunk, SelPlan* out) {
     p.n = n;
     p.S = (int32_t)S;
     p.chunk = (int32_t)chunk;
-    p.rows_per_launch = (int32_t)(di.num_cus / S);
+    // rows of one chunk need no co-residency (no row barrier): one launch holds them all
+    p.rows_per_launch = S == 1 ? (int32_t)(rows < (int64_t(1) << 24) ? rows : (int64_t(1) << 24)) : (int32_t)(di.num_cus / S);
     if (rows > 0 && p.rows_per_launch > rows) p.rows_per_launch = (int32_t)rows;
     if (p.rows_per_launch < 1) p.rows_per_launch = 1;
     p.launches = rows > 0 ? (int32_t)((rows + p.rows_per_launch - 1) / p.rows_per_launch) : 0;
-    p.row_words = 4 * (int32_t)S + (int32_t)S * kB1 + 2 * 2 * kCandCap;
+    p.row_words = S == 1 ? 0 : 4 * (int32_t)S + (int32_t)S * kB1 + 2 * 2 * kCandCap;
     p.row_words = (p.row_words + 63) / 64 * 64;
     p.chunk_pad = (int32_t)((chunk + kPadTo - 1) / kPadTo * kPadTo);
     p.lds_bytes = (size_t)(p.chunk_pad + kLdsFixedWords) * 4;
-    if (p.rows_per_launch > kSelCtrlRows) return fail(INVALID, "select: too many rows per launch");
+    if (S > 1 && p.rows_per_launch > kSelCtrlRows) return fail(INVALID, "select: too many rows per launch");
     p.data_bytes = (size_t)p.rows_per_launch * p.row_words * 4;
     p.ws_bytes = kCtrlBytes + p.data_bytes;
     *out = p;
@@ -991,8 +1028,12 @@ int run_scan_typed(const SelPlan& p, int source, const ScanArgs& a, const SelOut
         return launch_rows(p, s, out, nt, wc, wd, stream, a.rowmap);
     }
     if (source == SRC_CAND) {
-        SrcCand<KT, QT, D> s{a.q, a.k, a.N, a.rows_per_seq, a.cand, a.cnt, a.nranges, a.cap};
-        return launch_rows(p, s, out, nt, wc, wd, stream);
+        if constexpr (D == 64 && KT != kF32 && QT == kBF16) {      // the matrix-core prefill path's inputs
+            SrcCand<KT, QT, D> s{a.q, a.k, a.N, a.rows_per_seq, a.cand, a.cnt, a.nranges, a.cap};
+            return launch_rows(p, s, out, nt, wc, wd, stream);
+        } else {
+            return fail(INVALID, "candidate select needs bf16 queries, 64 channels and E4M3 or bf16 keys");
+        }
     }
     SrcPool<KT, QT, D> s{a.q, a.k, a.N, a.pool, p.n};
     return launch_rows(p, s, out, nt, wc, wd, stream);
