@@ -14,6 +14,7 @@ oracle timed on a bounded sample of the same workload (cpu_baseline).
 
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
   python bench.py --copy-calibration   # also runs a known-size copy kernel (for PMC scaling)
+  python bench.py --workload stack_b4_n1m --prefill --steps 3 --warmup 1   # the prefill chunk
 """
 
 import argparse
@@ -166,6 +167,56 @@ def cpu_baseline(cfg, budget_s):
                       f"KV rows quantized by the oracle only where attention reads them"}
 
 
+def run_prefill(args, cfg, dev):
+    """Full-layer prefill of the workload's chunk: prefill_Q queries per sequence at the last
+    positions of the context (causal), through the matrix-core indexer, exact top-K and attention."""
+    import numpy as np
+    import torch
+
+    import fp4_compressed_sparse_kv_amd as C
+    import synth
+
+    B, N, Q, K = cfg["B"], cfg["N"], cfg["prefill_Q"], cfg["K"]
+    t0 = time.perf_counter()
+    cache, _ = build_inputs(cfg, dev)
+    qi = np.stack([synth.prefill_q_idx(cfg, b, Q) for b in range(B)])
+    qb = np.stack([synth.prefill_q_bf16(cfg, b, Q) for b in range(B)])
+    qi_t = torch.from_numpy(np.ascontiguousarray(qi).view(np.int16)).view(torch.bfloat16).to(dev)
+    qb_t = torch.from_numpy(np.ascontiguousarray(qb).view(np.int16)).view(torch.bfloat16).to(dev)
+    q_pos = torch.arange(N - Q, N, dtype=torch.int64, device=dev).repeat(B, 1).contiguous()
+    log(f"inputs ready in {time.perf_counter() - t0:.1f} s")
+    plan = C.Plan(("full",), K=K, P=0, H=cfg["H"], d=cfg["d"], d_idx=cfg["d_idx"],
+                  q_idx_dtype=cfg["q_idx_dtype"], k_idx_dtype=cfg["k_idx_dtype"])
+    idx = torch.empty(B, Q, K, dtype=torch.int32, device=dev)
+    out = torch.empty(B, Q, cfg["H"], cfg["d"], dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        plan.prefill_full(cache, qi_t, qb_t, q_pos, idx_out=idx, out=out)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        plan.prefill_full(cache, qi_t, qb_t, q_pos, idx_out=idx, out=out)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    status = plan.prefill_status(cache, Q)
+    causal = float((q_pos + 1).sum().item())
+    flop = 2.0 * cfg["d_idx"] * causal                  # indexer dot products, causal positions only
+    res = {
+        "metric": "Full-layer prefill queries/s (indexer + exact top-K + FP4 sparse attention)",
+        "value": round(B * Q / (ms * 1e-3), 1), "unit": "queries/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16 MFMA (candidates) / f64 (exact scores) / f32", "data": "synthetic",
+        "config": {"workload": args.workload + ":prefill", "B": B, "N": N, "Q": Q, "K": K, "H": cfg["H"],
+                   "d_idx": cfg["d_idx"], "indexer_keys": cfg["k_idx_dtype"], "indexer_query": cfg["q_idx_dtype"]},
+        "indexer_tflop": round(flop / 1e12, 3),
+        "indexer_mfma_frac_of_whole_prefill": round(flop / (ms * 1e-3) / 2.5e15, 4),
+        "status_word": status,
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -175,6 +226,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--prefill", action="store_true",
+                    help="time the workload's Full-layer prefill chunk instead of the decode step")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -189,6 +242,11 @@ def main():
     import synth
 
     cfg = dict(synth.WORKLOADS[args.workload])
+    if args.prefill:
+        if "prefill_Q" not in cfg:
+            raise SystemExit(f"{args.workload} has no prefill chunk")
+        torch.cuda.set_device(0)
+        return run_prefill(args, cfg, torch.device("cuda", 0))
     if "modes" not in cfg:
         raise SystemExit(f"{args.workload} is not a decode workload")
     dev = torch.device("cuda", 0)
