@@ -18,12 +18,14 @@
 // holds the M-th largest key, and every chunk's count of keys above b1 and
 // in it.
 //   List path (S > 1 and at most kCandCap keys in bin b1 row-wide): each
-//     chunk writes its bin-b1 entries (index, key) to a per-row list, at
-//     slots that follow from those counts (chunks in order, entries in index
-//     order). After a second barrier every chunk reads the short list and
+//     wave first copies its keys in bin b1 or above (a few percent of them)
+//     with their indices, in index order, to the start of its own LDS span;
+//     the later steps visit only these. Each chunk writes its bin-b1 keys to
+//     its segment of a per-row list (segments in chunk order, placed by those
+//     counts). After a second barrier every chunk reads the short list and
 //     resolves the exact threshold key T, how many entries equal to T are
-//     taken, and every chunk's (and its own waves') counts of entries > T
-//     and == T, with no further exchange.
+//     taken, and the counts of entries > T and == T in earlier chunks and in
+//     all chunks, with no further exchange.
 //   Radix path (otherwise): two more radix passes over the LDS keys (11 and
 //     10 bits), each with a row-wide histogram exchange, then an exchange of
 //     the per-chunk counts of keys > T and == T.
@@ -375,13 +377,6 @@ __device__ __forceinline__ void pull_hist(uint32_t* lh, const uint32_t* gh, int 
 
 enum : int { kPathAll = 0, kPathList = 1, kPathRadix = 2 };
 
-__device__ __forceinline__ void st_rlx_u64(uint64_t* p, uint64_t v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint64_t ld_rlx_u64(const uint64_t* p) {
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 // Element j of a per-target pair, as a select on values (an indexed access
 // would force the pair into scratch memory).
 template <int NT, class T>
@@ -418,12 +413,13 @@ __global__ void __launch_bounds__(kSelThreads) k_select(Src src, SelDev g, SelTg
     uint32_t* rw = g.data + (size_t)lrow * g.row_words;                              // data, any content
     uint32_t* gcnt = rw;                        // [S][2][> T, == T]
     uint32_t* gsuf = gcnt + 4 * S;              // [S][kB1] per-chunk suffix sums of the top-digit histogram
-    uint64_t* glist = reinterpret_cast<uint64_t*>(gsuf + (size_t)S * kB1);   // [2][kCandCap] (index << 32 | key)
+    uint32_t* glist = gsuf + (size_t)S * kB1;  // [2][kCandCap] bin-b1 keys, one segment per chunk in chunk order
     uint32_t gen = 0;
 
     const uint32_t M[2] = {(uint32_t)t0.M, (uint32_t)t1.M};
 
     for (int i = tid; i < kB1; i += kSelThreads) lh1[i] = 0u;
+    if (tid < 2) sm[204 + tid] = 0u;          // list slot cursors of the two targets
     __syncthreads();
     src.fill(row, begin, cnt, cpad, keys, lh1);  // keys + lh1; ends with a block barrier
 
@@ -471,7 +467,7 @@ __global__ void __launch_bounds__(kSelThreads) k_select(Src src, SelDev g, SelTg
     const bool any_other = path[0] != kPathList || (NT > 1 && path[1] != kPathList);
 
     // ---- each wave owns a contiguous span of kPadTo-key steps; its lanes keep
-    // the span's keys in registers (4 per lane per step) for every later pass
+    // the span's keys in registers (4 per lane per step) for the passes below
     int span = (cpad + kSelWaves - 1) / kSelWaves;
     span = (span + kPadTo - 1) / kPadTo * kPadTo;
     const int w0 = min(cpad, wave * span), w1 = min(cpad, w0 + span);
@@ -485,14 +481,80 @@ __global__ void __launch_bounds__(kSelThreads) k_select(Src src, SelDev g, SelTg
     };
     uint32_t* wcnt = sm + 64;                   // [2][16][gt, eq] per-wave counts of this chunk
 
-    // ---- list path, part 1: every chunk's counts above bin b1 and in it come
-    // from the published suffix sums, so each chunk knows its slots in the
-    // row's list (chunks in order) without an atomic; it appends its bin-b1
-    // entries there in index order.
-    if (any_list) {
+    // ---- extraction: when every target takes the list path, each wave copies
+    // its keys in bin min(b1) or above - the only keys any later step needs -
+    // as (key, chunk index) pairs in index order to the start of its own LDS
+    // span. A wave whose pairs would not fit its span restores the span and
+    // keeps working on all its keys (ext = false); so do all waves on the
+    // other paths, which read the LDS keys of the whole chunk.
+    uint2* pairs = reinterpret_cast<uint2*>(keys + w0);
+    uint32_t npair = 0;                         // wave-uniform
+    bool ext = false;
+    if (any_list && !any_other) {
         load_kreg();
+        const uint32_t bmin = (NT > 1 && b1[1] < b1[0]) ? b1[1] : b1[0];
+        const uint32_t lowk = (bmin << 21) > 1u ? (bmin << 21) : 1u;
+        const uint32_t cap = (uint32_t)(w1 - w0) >> 1;
+#pragma unroll
+        for (int t = 0; t < kMaxSteps; ++t) {
+            if (t >= nst) break;
+            const int ib = w0 + t * kPadTo + 4 * lane;
+            const uint32_t kv[4] = {kreg[t].x, kreg[t].y, kreg[t].z, kreg[t].w};
+            uint32_t cm = 0, below = 0, total = 0;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const bool c = kv[u] >= lowk;
+                const uint64_t m = __ballot(c);
+                cm |= (uint32_t)c << u;
+                below += lanes_below(m);
+                total += (uint32_t)__popcll(m);
+            }
+            uint32_t slot = npair + below;
+            while (cm) {
+                const int u = __builtin_ctz(cm);
+                cm &= cm - 1u;
+                if (slot < cap) pairs[slot] = make_uint2(u == 0 ? kv[0] : u == 1 ? kv[1] : u == 2 ? kv[2] : kv[3], (uint32_t)(ib + u));
+                ++slot;
+            }
+            npair += total;
+        }
+        ext = npair <= cap;
+        if (!ext) {
+#pragma unroll
+            for (int t = 0; t < kMaxSteps; ++t)
+                if (t < nst) *reinterpret_cast<uint4*>(&keys[w0 + t * kPadTo + 4 * lane]) = kreg[t];
+        }
+    }
+    // Visit this wave's keys in index order, 64 at a time: f(key, chunk index,
+    // valid) is called by every lane with wave-uniform control flow.
+    auto for_keys = [&](auto&& f) {
+        if (ext) {
+            for (uint32_t i0 = 0; i0 < npair; i0 += kWave) {
+                const uint32_t i = i0 + (uint32_t)lane;
+                const uint2 pr = i < npair ? pairs[i] : make_uint2(0u, 0u);
+                f(pr.x, pr.y, i < npair);
+            }
+        } else {
+            load_kreg();
+#pragma unroll
+            for (int t = 0; t < kMaxSteps; ++t) {
+                if (t >= nst) break;
+                const int ib = w0 + t * kPadTo + 4 * lane;
+                f(kreg[t].x, (uint32_t)ib, true);
+                f(kreg[t].y, (uint32_t)ib + 1u, true);
+                f(kreg[t].z, (uint32_t)ib + 2u, true);
+                f(kreg[t].w, (uint32_t)ib + 3u, true);
+            }
+        }
+    };
+
+    // ---- list path, part 1: every chunk's counts above bin b1 and in it come
+    // from the published suffix sums, so each chunk knows its segment of the
+    // row's list (chunks in order) without an atomic; its waves reserve slots
+    // inside the segment and write their bin-b1 keys there.
+    if (any_list) {
         // cnts[s][j] = (keys above b1, keys in b1) of chunk s; the loads
-        // (S * NT <= 512 pairs, one per thread) stay in flight during the pass
+        // (S * NT <= 512 pairs, one per thread) stay in flight meanwhile
         const int si = tid / NT, sj = tid - si * NT;
         const bool sl = tid < S * NT && pick<NT>(path[0], path[1], sj) == kPathList;
         uint32_t s_at = 0u, s_ab = 0u;
@@ -503,69 +565,48 @@ __global__ void __launch_bounds__(kSelThreads) k_select(Src src, SelDev g, SelTg
             s_ab = ld_rlx(&su[bj + 1 < (uint32_t)kB1 ? bj + 1 : bj]);
             if (bj + 1 >= (uint32_t)kB1) s_ab = 0u;
         }
-        // per-wave counts of keys above the bin and in it
-        uint32_t above[2] = {0u, 0u}, ncand[2] = {0u, 0u};
+        uint32_t inb[2] = {0u, 0u};
+        for_keys([&](uint32_t k, uint32_t, bool v) {
 #pragma unroll
-        for (int t = 0; t < kMaxSteps; ++t) {
-            if (t >= nst) break;
-            const uint32_t kv[4] = {kreg[t].x, kreg[t].y, kreg[t].z, kreg[t].w};
+            for (int j = 0; j < NT; ++j) inb[j] += (uint32_t)__popcll(__ballot(v && k != 0u && (k >> 21) == b1[j]));
+        });
+        uint32_t off[2] = {0u, 0u};             // this wave's first slot in the chunk's segment
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const uint32_t d = kv[u] >> 21;
-#pragma unroll
-                for (int j = 0; j < NT; ++j) {
-                    above[j] += (uint32_t)(d > b1[j]);
-                    ncand[j] += (uint32_t)__popcll(__ballot(kv[u] != 0u && d == b1[j]));
-                }
-            }
+        for (int j = 0; j < NT; ++j) {
+            if (path[j] == kPathList && lane == 0 && inb[j]) off[j] = atomicAdd(&sm[204 + j], inb[j]);
+            off[j] = (uint32_t)__builtin_amdgcn_readfirstlane((int)off[j]);
         }
         if (sl) {
             cnts[(si * 2 + sj) * 2 + 0] = s_ab;
             cnts[(si * 2 + sj) * 2 + 1] = s_at - s_ab;
         }
-        uint32_t* wl = sm + 32;                 // [2][16] per-wave list bases
-#pragma unroll
-        for (int j = 0; j < NT; ++j) {
-            const uint32_t a = wave_sum(above[j]);
-            if (lane == 0) {
-                wcnt[(j * kSelWaves + wave) * 2 + 0] = a;
-                wcnt[(j * kSelWaves + wave) * 2 + 1] = 0u;
-                wl[j * kSelWaves + wave] = ncand[j];
-            }
-        }
         __syncthreads();
-        if (tid < NT && pick<NT>(path[0], path[1], tid) == kPathList) {
-            uint32_t base = 0;
-            for (int s = 0; s < split; ++s) base += cnts[(s * 2 + tid) * 2 + 1];
-            sm[200 + 2 * tid] = base;           // this chunk's range [lo, hi) of the row's list
-            for (int w = 0; w < kSelWaves; ++w) {
-                const uint32_t n = wl[tid * kSelWaves + w];
-                wl[tid * kSelWaves + w] = base;
-                base += n;
-            }
-            sm[201 + 2 * tid] = base;
-        }
-        __syncthreads();
+        uint32_t lo[2] = {0u, 0u}, hi[2] = {0u, 0u};
 #pragma unroll
         for (int j = 0; j < NT; ++j) {
             if (path[j] != kPathList) continue;
-            uint32_t run = wl[j * kSelWaves + wave];
-            uint64_t* lst = glist + (size_t)j * kCandCap;
-#pragma unroll
-            for (int t = 0; t < kMaxSteps; ++t) {
-                if (t >= nst) break;
-                const uint32_t kv[4] = {kreg[t].x, kreg[t].y, kreg[t].z, kreg[t].w};
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const bool c = kv[u] != 0u && (kv[u] >> 21) == b1[j];
-                    const uint64_t m = __ballot(c);
-                    const uint32_t slot = run + lanes_below(m);
-                    if (c && slot < (uint32_t)kCandCap)     // holds: the slots of a row sum to C[j] <= kCandCap
-                        st_rlx_u64(&lst[slot], ((uint64_t)wave << 32) | kv[u]);   // (writer wave, key)
-                    run += (uint32_t)__popcll(m);
-                }
+            uint32_t b = 0;
+            for (int s = lane; s < split; s += kWave) b += cnts[(s * 2 + j) * 2 + 1];
+            lo[j] = wave_sum(b);
+            hi[j] = lo[j] + cnts[(split * 2 + j) * 2 + 1];
+            if (wave == 0 && lane == 0) {
+                sm[200 + 2 * j] = lo[j];        // this chunk's range [lo, hi) of the row's list
+                sm[201 + 2 * j] = hi[j];
             }
         }
+        uint32_t run[2] = {lo[0] + off[0], lo[1] + off[1]};
+        for_keys([&](uint32_t k, uint32_t, bool v) {
+#pragma unroll
+            for (int j = 0; j < NT; ++j) {
+                if (path[j] != kPathList) continue;
+                const bool c = v && k != 0u && (k >> 21) == b1[j];
+                const uint64_t m = __ballot(c);
+                const uint32_t slot = run[j] + lanes_below(m);
+                if (c && slot < hi[j] && slot < (uint32_t)kCandCap)   // holds: the waves' counts sum to hi - lo
+                    st_rlx(&glist[(size_t)j * kCandCap + slot], k);
+                run[j] += (uint32_t)__popcll(m);
+            }
+        });
     }
 
     // ---- radix path: two more digit passes over the LDS keys with row exchanges
@@ -624,18 +665,18 @@ __global__ void __launch_bounds__(kSelThreads) k_select(Src src, SelDev g, SelTg
     }
 
     // ---- list path, part 2: after the row barrier every chunk reads the
-    // row's lists, resolves T and the tie count, and adds the entries > T and
-    // == T to the counts of their chunk (and, for its own chunk, of their wave)
+    // row's lists, resolves T and the tie count, and counts the entries > T
+    // and == T before its own segment and in all segments
     if (any_list) {
         row_barrier(ctrl, S, gen, status);
         constexpr int R = kCandCap / kSelThreads;
-        uint64_t ent[2][R];
+        uint32_t ent[2][R];
 #pragma unroll
         for (int j = 0; j < NT; ++j) {
 #pragma unroll
             for (int r = 0; r < R; ++r) {
                 const int e = tid + r * kSelThreads;
-                ent[j][r] = (path[j] == kPathList && e < (int)C[j]) ? ld_rlx_u64(&glist[(size_t)j * kCandCap + e]) : 0ull;
+                ent[j][r] = (path[j] == kPathList && e < (int)C[j]) ? ld_rlx(&glist[(size_t)j * kCandCap + e]) : 0u;
             }
         }
         // both targets' digit histograms side by side: bits 10..20, then bits 0..9
@@ -648,7 +689,7 @@ __global__ void __launch_bounds__(kSelThreads) k_select(Src src, SelDev g, SelTg
         for (int j = 0; j < NT; ++j) {
 #pragma unroll
             for (int r = 0; r < R; ++r) {
-                const uint32_t k = (uint32_t)ent[j][r];
+                const uint32_t k = ent[j][r];
                 if (k) atomicAdd(&lh2[j * kB2 + ((k >> 10) & 2047u)], 1u);
             }
         }
@@ -662,47 +703,32 @@ __global__ void __launch_bounds__(kSelThreads) k_select(Src src, SelDev g, SelTg
             nd[j] = path[j] == kPathList ? f2[j].rem : 0u;
 #pragma unroll
             for (int r = 0; r < R; ++r) {
-                const uint32_t k = (uint32_t)ent[j][r];
+                const uint32_t k = ent[j][r];
                 if (k && ((k >> 10) & 2047u) == f2[j].bin) atomicAdd(&lh2[j * kB3 + (k & 1023u)], 1u);
             }
         }
         __syncthreads();
         block_find_multi<NT>(lh2, kB3, kB3, nd, sm, f3);
         // Entries > T and == T, counted by list position with ballots: before
-        // this chunk's range (earlier chunks), anywhere (all chunks), and -
-        // attributed to the writer wave - inside this chunk's range. The
+        // this chunk's segment (earlier chunks) and anywhere (all chunks). The
         // per-wave sums go to lh2 (free once T is known).
 #pragma unroll
         for (int j = 0; j < NT; ++j) {
             if (path[j] != kPathList) continue;
             T[j] = (b1[j] << 21) | (f2[j].bin << 10) | f3[j].bin;
             need[j] = f3[j].rem;
-            const uint32_t lo = sm[200 + 2 * j], hi = sm[201 + 2 * j];
+            const uint32_t lo = sm[200 + 2 * j];
             uint32_t gt_before = 0, eq_before = 0, gt_all = 0, eq_all = 0;
 #pragma unroll
             for (int r = 0; r < R; ++r) {
                 const uint32_t e = (uint32_t)(tid + r * kSelThreads);
-                const uint32_t k = (uint32_t)ent[j][r];
+                const uint32_t k = ent[j][r];
                 const uint64_t mg = __ballot(k > T[j]), me = __ballot(k == T[j]);   // padding keys are 0 < T
-                if ((mg | me) == 0ull) continue;
-                const uint64_t mlo = __ballot(e < lo), mown = __ballot(e >= lo && e < hi);
+                const uint64_t mlo = __ballot(e < lo);
                 gt_before += (uint32_t)__popcll(mg & mlo);
                 eq_before += (uint32_t)__popcll(me & mlo);
                 gt_all += (uint32_t)__popcll(mg);
                 eq_all += (uint32_t)__popcll(me);
-                const uint64_t mo = mown & (mg | me);
-                if (mo == 0ull) continue;
-                const uint32_t wt = (uint32_t)(ent[j][r] >> 32);
-                const uint32_t w0l = (uint32_t)__builtin_amdgcn_readlane((int)wt, (int)__builtin_ctzll(mo));
-                if ((__ballot(wt != w0l) & mo) == 0ull) {
-                    if (lane == 0) {
-                        const uint32_t ng = (uint32_t)__popcll(mg & mown), ne = (uint32_t)__popcll(me & mown);
-                        if (ng) atomicAdd(&wcnt[(j * kSelWaves + (int)w0l) * 2 + 0], ng);
-                        if (ne) atomicAdd(&wcnt[(j * kSelWaves + (int)w0l) * 2 + 1], ne);
-                    }
-                } else if ((mo >> lane) & 1ull) {
-                    atomicAdd(&wcnt[(j * kSelWaves + (int)wt) * 2 + (((mg >> lane) & 1ull) ? 0 : 1)], 1u);
-                }
             }
             if (lane == 0) {
                 uint32_t* agg = lh2 + (j * kSelWaves + wave) * 4;
@@ -712,35 +738,25 @@ __global__ void __launch_bounds__(kSelThreads) k_select(Src src, SelDev g, SelTg
                 agg[3] = eq_all;
             }
         }
-        __syncthreads();
     }
 
-    // ---- targets not resolved from a list: per-wave counts of keys > T and
-    // == T from the register-resident keys, then (radix path) an exchange of
-    // the per-chunk counts
-    if (any_other) {
-        load_kreg();
+    // ---- per-wave counts of keys > T and == T for every target; targets not
+    // resolved from a list then exchange their per-chunk counts
 #pragma unroll
-        for (int j = 0; j < NT; ++j) {
-            if (path[j] == kPathList) continue;
-            uint32_t gt = 0, eq = 0;
-            const uint32_t Tj = T[j];
-#pragma unroll
-            for (int t = 0; t < kMaxSteps; ++t) {
-                if (t >= nst) break;
-                const uint32_t kv[4] = {kreg[t].x, kreg[t].y, kreg[t].z, kreg[t].w};
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    gt += (uint32_t)__popcll(__ballot(kv[u] > Tj));
-                    eq += (uint32_t)__popcll(__ballot(kv[u] == Tj && kv[u] != 0u));
-                }
-            }
-            if (lane == 0) {
-                wcnt[(j * kSelWaves + wave) * 2 + 0] = gt;
-                wcnt[(j * kSelWaves + wave) * 2 + 1] = eq;
-            }
+    for (int j = 0; j < NT; ++j) {
+        uint32_t gt = 0, eq = 0;
+        const uint32_t Tj = T[j];
+        for_keys([&](uint32_t k, uint32_t, bool v) {
+            gt += (uint32_t)__popcll(__ballot(v && k > Tj));
+            eq += (uint32_t)__popcll(__ballot(v && k == Tj && k != 0u));
+        });
+        if (lane == 0) {
+            wcnt[(j * kSelWaves + wave) * 2 + 0] = gt;
+            wcnt[(j * kSelWaves + wave) * 2 + 1] = eq;
         }
-        __syncthreads();
+    }
+    __syncthreads();
+    if (any_other) {
         if (tid < NT && pick<NT>(path[0], path[1], tid) != kPathList) {
             uint32_t gt = 0, eq = 0;
             for (int w = 0; w < kSelWaves; ++w) {
@@ -767,7 +783,6 @@ __global__ void __launch_bounds__(kSelThreads) k_select(Src src, SelDev g, SelTg
         }
         __syncthreads();
     }
-    if (!any_other) load_kreg();
 
     // ---- offsets: this chunk's output base and its share of the == T entries
     uint32_t* wbase = sm + 128;                 // [2][16][base, eq_before]
@@ -827,7 +842,8 @@ __global__ void __launch_bounds__(kSelThreads) k_select(Src src, SelDev g, SelTg
     }
     __syncthreads();
 
-    // ---- compaction in index order, 4 keys per lane per step
+    // ---- compaction in index order: the selected entries of the wave's keys
+    // get consecutive output slots from the wave's base
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
         const SelTgt& t = j ? t1 : t0;
@@ -838,62 +854,87 @@ __global__ void __launch_bounds__(kSelThreads) k_select(Src src, SelDev g, SelTg
         uint32_t run_eq = wbase[(j * kSelWaves + wave) * 2 + 1];
         int32_t* out_idx = t.idx + row * t.stride;
         float* out_sc = t.score ? t.score + row * t.stride : nullptr;
-        // Entry (lane, u) of a step has index i0 + 4*lane + u; its rank among the
-        // step's selected entries is the count over all u of selected entries in
-        // lower lanes (one ballot per u, counted with mbcnt) plus those at u' < u
-        // in its own lane - no cross-lane data movement.
-#pragma unroll
-        for (int t = 0; t < kMaxSteps; ++t) {
-            if (t >= nst) break;
-            const int ib = w0 + t * kPadTo + 4 * lane;
-            const uint32_t kv[4] = {kreg[t].x, kreg[t].y, kreg[t].z, kreg[t].w};
-            uint32_t selm = 0, below = 0, total = 0;
-            if (eq_all || take_eq == 0) {
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const bool s = kv[u] > Tj || (eq_all && kv[u] == Tj && kv[u] != 0u);
-                    const uint64_t m = __ballot(s);
-                    selm |= (uint32_t)s << u;
-                    below += lanes_below(m);
-                    total += (uint32_t)__popcll(m);
+        if (ext) {
+            for (uint32_t i0 = 0; i0 < npair; i0 += kWave) {
+                const uint32_t i = i0 + (uint32_t)lane;
+                const bool v = i < npair;
+                const uint2 pr = v ? pairs[i] : make_uint2(0u, 0u);
+                bool s = v && pr.x > Tj;
+                if (eq_all) {
+                    s = s || (v && pr.x == Tj);
+                } else if (take_eq) {           // ties at T split inside this chunk: ranked in index order
+                    const bool e = v && pr.x == Tj;
+                    const uint64_t me = __ballot(e);
+                    s = s || (e && run_eq + lanes_below(me) < take_eq);
+                    run_eq += (uint32_t)__popcll(me);
                 }
-            } else {                            // ties at T split inside this chunk: rank them in index order
-                uint32_t eqm = 0, eq_below = 0, eq_total = 0;
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const bool e = kv[u] == Tj && kv[u] != 0u;
-                    const uint64_t m = __ballot(e);
-                    eqm |= (uint32_t)e << u;
-                    eq_below += lanes_below(m);
-                    eq_total += (uint32_t)__popcll(m);
+                const uint64_t m = __ballot(s);
+                const uint32_t slot = run_sel + lanes_below(m);
+                if (s && slot < M[j]) {         // the bound holds whenever the counts agree
+                    out_idx[slot] = src.position(row, begin + (int64_t)pr.y);
+                    if (out_sc) out_sc[slot] = key_score(pr.x);
                 }
-                uint32_t r = run_eq + eq_below;
+                run_sel += (uint32_t)__popcll(m);
+            }
+        } else {
+            load_kreg();
+            // Entry (lane, u) of a step has index i0 + 4*lane + u; its rank among the
+            // step's selected entries is the count over all u of selected entries in
+            // lower lanes (one ballot per u, counted with mbcnt) plus those at u' < u
+            // in its own lane - no cross-lane data movement.
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    bool s = kv[u] > Tj;
-                    if ((eqm >> u) & 1u) {
-                        s = r < take_eq;
-                        ++r;
+            for (int t = 0; t < kMaxSteps; ++t) {
+                if (t >= nst) break;
+                const int ib = w0 + t * kPadTo + 4 * lane;
+                const uint32_t kv[4] = {kreg[t].x, kreg[t].y, kreg[t].z, kreg[t].w};
+                uint32_t selm = 0, below = 0, total = 0;
+                if (eq_all || take_eq == 0) {
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const bool s = kv[u] > Tj || (eq_all && kv[u] == Tj && kv[u] != 0u);
+                        const uint64_t m = __ballot(s);
+                        selm |= (uint32_t)s << u;
+                        below += lanes_below(m);
+                        total += (uint32_t)__popcll(m);
                     }
-                    const uint64_t m = __ballot(s);
-                    selm |= (uint32_t)s << u;
-                    below += lanes_below(m);
-                    total += (uint32_t)__popcll(m);
+                } else {                        // ties at T split inside this chunk: rank them in index order
+                    uint32_t eqm = 0, eq_below = 0, eq_total = 0;
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const bool e = kv[u] == Tj && kv[u] != 0u;
+                        const uint64_t m = __ballot(e);
+                        eqm |= (uint32_t)e << u;
+                        eq_below += lanes_below(m);
+                        eq_total += (uint32_t)__popcll(m);
+                    }
+                    uint32_t r = run_eq + eq_below;
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        bool s = kv[u] > Tj;
+                        if ((eqm >> u) & 1u) {
+                            s = r < take_eq;
+                            ++r;
+                        }
+                        const uint64_t m = __ballot(s);
+                        selm |= (uint32_t)s << u;
+                        below += lanes_below(m);
+                        total += (uint32_t)__popcll(m);
+                    }
+                    run_eq += eq_total;
                 }
-                run_eq += eq_total;
-            }
-            // one store per selected entry of the lane (usually none or one)
-            uint32_t slot = run_sel + below;
-            while (selm) {
-                const int u = __builtin_ctz(selm);
-                selm &= selm - 1u;
-                if (slot < M[j]) {              // the bound holds whenever the counts agree
-                    out_idx[slot] = src.position(row, begin + ib + u);
-                    if (out_sc) out_sc[slot] = key_score(u == 0 ? kv[0] : u == 1 ? kv[1] : u == 2 ? kv[2] : kv[3]);
+                // one store per selected entry of the lane (usually none or one)
+                uint32_t slot = run_sel + below;
+                while (selm) {
+                    const int u = __builtin_ctz(selm);
+                    selm &= selm - 1u;
+                    if (slot < M[j]) {          // the bound holds whenever the counts agree
+                        out_idx[slot] = src.position(row, begin + ib + u);
+                        if (out_sc) out_sc[slot] = key_score(u == 0 ? kv[0] : u == 1 ? kv[1] : u == 2 ? kv[2] : kv[3]);
+                    }
+                    ++slot;
                 }
-                ++slot;
+                run_sel += total;
             }
-            run_sel += total;
         }
         if (split == S - 1) {
             for (uint32_t s = tinfo[j * 4 + 1] + tid; s < M[j]; s += kSelThreads) {
@@ -953,7 +994,7 @@ int plan_select(int64_t rows, int64_t n, int32_t min_chunk, SelPlan* out) {
     if (rows > 0 && p.rows_per_launch > rows) p.rows_per_launch = (int32_t)rows;
     if (p.rows_per_launch < 1) p.rows_per_launch = 1;
     p.launches = rows > 0 ? (int32_t)((rows + p.rows_per_launch - 1) / p.rows_per_launch) : 0;
-    p.row_words = S == 1 ? 0 : 4 * (int32_t)S + (int32_t)S * kB1 + 2 * 2 * kCandCap;
+    p.row_words = S == 1 ? 0 : 4 * (int32_t)S + (int32_t)S * kB1 + 2 * kCandCap;
     p.row_words = (p.row_words + 63) / 64 * 64;
     p.chunk_pad = (int32_t)((chunk + kPadTo - 1) / kPadTo * kPadTo);
     p.lds_bytes = (size_t)(p.chunk_pad + kLdsFixedWords) * 4;
