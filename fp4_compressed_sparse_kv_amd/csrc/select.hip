@@ -315,7 +315,10 @@ __device__ Found block_find(const uint32_t* hist, int nb, uint32_t need, uint32_
 }
 
 // block_find over NT histograms at once (histogram j at hist + j * hstride,
-// target need[j]; need[j] = 0 skips it) with three block barriers in all.
+// target need[j]; need[j] = 0 skips it) with two block barriers. The
+// histograms are not read after the second one, and a later call rewrites the
+// scratch words only after its own first barrier, when every thread has read
+// this call's result.
 template <int NT>
 __device__ __forceinline__ void block_find_multi(const uint32_t* hist, int nb, int hstride, const uint32_t (&need)[2],
                                                  uint32_t* sm, Found (&out)[2]) {
@@ -358,7 +361,6 @@ __device__ __forceinline__ void block_find_multi(const uint32_t* hist, int nb, i
         out[j].bin = sm[2 * kSelWaves + 2 * j];
         out[j].rem = sm[2 * kSelWaves + 2 * j + 1];
     }
-    __syncthreads();
 }
 
 __device__ __forceinline__ void push_hist(const uint32_t* lh, uint32_t* gh, int nb) {
@@ -419,7 +421,7 @@ __global__ void __launch_bounds__(kSelThreads) k_select(Src src, SelDev g, SelTg
     const uint32_t M[2] = {(uint32_t)t0.M, (uint32_t)t1.M};
 
     for (int i = tid; i < kB1; i += kSelThreads) lh1[i] = 0u;
-    if (tid < 2) sm[204 + tid] = 0u;          // list slot cursors of the two targets
+    if (tid < 4) sm[204 + tid] = 0u;          // list slot cursors and tie counters of the two targets
     __syncthreads();
     src.fill(row, begin, cnt, cpad, keys, lh1);  // keys + lh1; ends with a block barrier
 
@@ -487,6 +489,19 @@ __global__ void __launch_bounds__(kSelThreads) k_select(Src src, SelDev g, SelTg
     // span. A wave whose pairs would not fit its span restores the span and
     // keeps working on all its keys (ext = false); so do all waves on the
     // other paths, which read the LDS keys of the whole chunk.
+    // cnts[s][j] = (keys above b1, keys in b1) of chunk s, from the suffix
+    // sums at b1 and b1 + 1 (S * NT <= 512 pairs, one per thread); the loads
+    // stay in flight during the extraction pass
+    const int si = tid / NT, sj = tid - si * NT;
+    const bool sl = any_list && tid < S * NT && pick<NT>(path[0], path[1], sj) == kPathList;
+    uint32_t s_at = 0u, s_ab = 0u;
+    if (sl) {
+        const uint32_t bj = pick<NT>(b1[0], b1[1], sj);
+        const uint32_t* su = gsuf + (size_t)si * kB1;
+        s_at = ld_rlx(&su[bj]);
+        s_ab = ld_rlx(&su[bj + 1 < (uint32_t)kB1 ? bj + 1 : bj]);
+        if (bj + 1 >= (uint32_t)kB1) s_ab = 0u;
+    }
     uint2* pairs = reinterpret_cast<uint2*>(keys + w0);
     uint32_t npair = 0;                         // wave-uniform
     bool ext = false;
@@ -553,18 +568,6 @@ __global__ void __launch_bounds__(kSelThreads) k_select(Src src, SelDev g, SelTg
     // row's list (chunks in order) without an atomic; its waves reserve slots
     // inside the segment and write their bin-b1 keys there.
     if (any_list) {
-        // cnts[s][j] = (keys above b1, keys in b1) of chunk s; the loads
-        // (S * NT <= 512 pairs, one per thread) stay in flight meanwhile
-        const int si = tid / NT, sj = tid - si * NT;
-        const bool sl = tid < S * NT && pick<NT>(path[0], path[1], sj) == kPathList;
-        uint32_t s_at = 0u, s_ab = 0u;
-        if (sl) {
-            const uint32_t bj = pick<NT>(b1[0], b1[1], sj);
-            const uint32_t* su = gsuf + (size_t)si * kB1;
-            s_at = ld_rlx(&su[bj]);
-            s_ab = ld_rlx(&su[bj + 1 < (uint32_t)kB1 ? bj + 1 : bj]);
-            if (bj + 1 >= (uint32_t)kB1) s_ab = 0u;
-        }
         uint32_t inb[2] = {0u, 0u};
         for_keys([&](uint32_t k, uint32_t, bool v) {
 #pragma unroll
@@ -667,16 +670,20 @@ __global__ void __launch_bounds__(kSelThreads) k_select(Src src, SelDev g, SelTg
     // ---- list path, part 2: after the row barrier every chunk reads the
     // row's lists, resolves T and the tie count, and counts the entries > T
     // and == T before its own segment and in all segments
+    uint32_t lgt_all[2] = {0u, 0u}, leq_all[2] = {0u, 0u};   // list entries > T and == T (list targets)
     if (any_list) {
         row_barrier(ctrl, S, gen, status);
         constexpr int R = kCandCap / kSelThreads;
         uint32_t ent[2][R];
+        int rn[2] = {0, 0};                     // list slots per thread in use (uniform)
 #pragma unroll
         for (int j = 0; j < NT; ++j) {
+            if (path[j] == kPathList) rn[j] = ((int)C[j] + kSelThreads - 1) / kSelThreads;
 #pragma unroll
             for (int r = 0; r < R; ++r) {
                 const int e = tid + r * kSelThreads;
-                ent[j][r] = (path[j] == kPathList && e < (int)C[j]) ? ld_rlx(&glist[(size_t)j * kCandCap + e]) : 0u;
+                ent[j][r] = 0u;
+                if (r < rn[j] && e < (int)C[j]) ent[j][r] = ld_rlx(&glist[(size_t)j * kCandCap + e]);
             }
         }
         // both targets' digit histograms side by side: bits 10..20, then bits 0..9
@@ -689,53 +696,117 @@ __global__ void __launch_bounds__(kSelThreads) k_select(Src src, SelDev g, SelTg
         for (int j = 0; j < NT; ++j) {
 #pragma unroll
             for (int r = 0; r < R; ++r) {
+                if (r >= rn[j]) break;
                 const uint32_t k = ent[j][r];
                 if (k) atomicAdd(&lh2[j * kB2 + ((k >> 10) & 2047u)], 1u);
             }
         }
         __syncthreads();
-        Found f2[2], f3[2];
+        Found f2[2];
         block_find_multi<NT>(lh2, kB2, kB2, nd, sm, f2);
-        for (int i = tid; i < NT * kB3; i += kSelThreads) lh2[i] = 0u;
-        __syncthreads();
+        // The entries of bin (b1, b2) - usually a handful - are collected and
+        // ranked directly: T is the key k with (# > k) < rem <= (# >= k). A
+        // target with more of them than one per thread takes a histogram of
+        // the low 10 bits instead.
+        uint32_t* tie = lh2;                    // [2][kSelThreads] (the histogram is no longer read)
 #pragma unroll
         for (int j = 0; j < NT; ++j) {
-            nd[j] = path[j] == kPathList ? f2[j].rem : 0u;
 #pragma unroll
             for (int r = 0; r < R; ++r) {
+                if (r >= rn[j]) break;
                 const uint32_t k = ent[j][r];
-                if (k && ((k >> 10) & 2047u) == f2[j].bin) atomicAdd(&lh2[j * kB3 + (k & 1023u)], 1u);
+                if (k && ((k >> 10) & 2047u) == f2[j].bin) {
+                    const uint32_t slot = atomicAdd(&sm[206 + j], 1u);
+                    if (slot < (uint32_t)kSelThreads) tie[j * kSelThreads + slot] = k;
+                }
             }
         }
         __syncthreads();
-        block_find_multi<NT>(lh2, kB3, kB3, nd, sm, f3);
-        // Entries > T and == T, counted by list position with ballots: before
-        // this chunk's segment (earlier chunks) and anywhere (all chunks). The
-        // per-wave sums go to lh2 (free once T is known).
+        uint32_t ntie[2] = {0u, 0u};
+        bool big = false;
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+            ntie[j] = sm[206 + j];
+            big = big || (path[j] == kPathList && ntie[j] > (uint32_t)kSelThreads);
+        }
+        uint32_t tbin[2] = {0u, 0u}, gt_t[2] = {0u, 0u}, eq_t[2] = {0u, 0u};   // in bin (b1, b2): > T, == T
+        if (!big) {
+#pragma unroll
+            for (int j = 0; j < NT; ++j) {
+                if (path[j] != kPathList || (uint32_t)tid >= ntie[j]) continue;
+                const uint32_t k = tie[j * kSelThreads + tid];
+                uint32_t gt = 0, ge = 0;
+                for (uint32_t i = 0; i < ntie[j]; ++i) {
+                    const uint32_t v = tie[j * kSelThreads + i];
+                    gt += (uint32_t)(v > k);
+                    ge += (uint32_t)(v >= k);
+                }
+                if (gt < f2[j].rem && f2[j].rem <= ge) {   // every thread holding T writes the same values
+                    sm[208 + 4 * j] = k & 1023u;
+                    sm[209 + 4 * j] = f2[j].rem - gt;
+                    sm[210 + 4 * j] = gt;
+                    sm[211 + 4 * j] = ge - gt;
+                }
+            }
+            __syncthreads();
+#pragma unroll
+            for (int j = 0; j < NT; ++j) {
+                tbin[j] = sm[208 + 4 * j];
+                need[j] = sm[209 + 4 * j];
+                gt_t[j] = sm[210 + 4 * j];
+                eq_t[j] = sm[211 + 4 * j];
+            }
+        } else {
+            Found f3[2];
+            for (int i = tid; i < NT * kB3; i += kSelThreads) lh2[i] = 0u;
+            __syncthreads();
+#pragma unroll
+            for (int j = 0; j < NT; ++j) {
+                nd[j] = path[j] == kPathList ? f2[j].rem : 0u;
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    if (r >= rn[j]) break;
+                    const uint32_t k = ent[j][r];
+                    if (k && ((k >> 10) & 2047u) == f2[j].bin) atomicAdd(&lh2[j * kB3 + (k & 1023u)], 1u);
+                }
+            }
+            __syncthreads();
+            block_find_multi<NT>(lh2, kB3, kB3, nd, sm, f3);
+#pragma unroll
+            for (int j = 0; j < NT; ++j) {
+                tbin[j] = f3[j].bin;
+                need[j] = f3[j].rem;
+                gt_t[j] = nd[j] - f3[j].rem;
+                eq_t[j] = path[j] == kPathList ? lh2[j * kB3 + f3[j].bin] : 0u;
+            }
+        }
+        __syncthreads();                        // lh2 is rewritten below
+        // Entries > T and == T in the whole list follow from the finds (bins
+        // above b2, then the ranking inside it); those before this chunk's
+        // segment (earlier chunks) are counted by list position with ballots.
+        // The per-wave sums go to lh2 (free once T is known).
 #pragma unroll
         for (int j = 0; j < NT; ++j) {
             if (path[j] != kPathList) continue;
-            T[j] = (b1[j] << 21) | (f2[j].bin << 10) | f3[j].bin;
-            need[j] = f3[j].rem;
+            T[j] = (b1[j] << 21) | (f2[j].bin << 10) | tbin[j];
+            lgt_all[j] = (rem[j] - f2[j].rem) + gt_t[j];
+            leq_all[j] = eq_t[j];
             const uint32_t lo = sm[200 + 2 * j];
-            uint32_t gt_before = 0, eq_before = 0, gt_all = 0, eq_all = 0;
+            const int rlo = ((int)lo + kSelThreads - 1) / kSelThreads;
+            uint32_t gt_before = 0, eq_before = 0;
 #pragma unroll
             for (int r = 0; r < R; ++r) {
+                if (r >= rlo) break;
                 const uint32_t e = (uint32_t)(tid + r * kSelThreads);
                 const uint32_t k = ent[j][r];
-                const uint64_t mg = __ballot(k > T[j]), me = __ballot(k == T[j]);   // padding keys are 0 < T
-                const uint64_t mlo = __ballot(e < lo);
-                gt_before += (uint32_t)__popcll(mg & mlo);
-                eq_before += (uint32_t)__popcll(me & mlo);
-                gt_all += (uint32_t)__popcll(mg);
-                eq_all += (uint32_t)__popcll(me);
+                const bool b = e < lo;
+                gt_before += (uint32_t)__popcll(__ballot(b && k > T[j]));   // padding keys are 0 < T
+                eq_before += (uint32_t)__popcll(__ballot(b && k == T[j]));
             }
             if (lane == 0) {
-                uint32_t* agg = lh2 + (j * kSelWaves + wave) * 4;
+                uint32_t* agg = lh2 + (j * kSelWaves + wave) * 2;
                 agg[0] = gt_before;
                 agg[1] = eq_before;
-                agg[2] = gt_all;
-                agg[3] = eq_all;
             }
         }
     }
@@ -802,12 +873,12 @@ __global__ void __launch_bounds__(kSelThreads) k_select(Src src, SelDev g, SelTg
                 ab_all += a;
             }
             for (int w = 0; w < kSelWaves; ++w) {
-                const uint32_t* agg = lh2 + (j * kSelWaves + w) * 4;
+                const uint32_t* agg = lh2 + (j * kSelWaves + w) * 2;
                 lg_before += agg[0];
                 le_before += agg[1];
-                lg_all += agg[2];
-                le_all += agg[3];
             }
+            lg_all = pick<NT>(lgt_all[0], lgt_all[1], j);
+            le_all = pick<NT>(leq_all[0], leq_all[1], j);
             for (int w = 0; w < kSelWaves; ++w) my_eq += wcnt[(j * kSelWaves + w) * 2 + 1];
             off = ab_before + lg_before + (le_before < nj ? le_before : nj);
             my_take = nj > le_before ? nj - le_before : 0u;
