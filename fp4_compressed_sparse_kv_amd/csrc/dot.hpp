@@ -87,4 +87,27 @@ __device__ __forceinline__ double quad_sum(double v) {
     return v;
 }
 
+// fp64 value of the quad lane named by the DPP quad permutation CTRL.
+template <int CTRL>
+__device__ __forceinline__ double quad_perm_f64(double v) {
+    const int2 p = __builtin_bit_cast(int2, v);
+    int2 r;
+    r.x = __builtin_amdgcn_mov_dpp(p.x, CTRL, 0xF, 0xF, false);
+    r.y = __builtin_amdgcn_mov_dpp(p.y, CTRL, 0xF, 0xF, false);
+    return __builtin_bit_cast(double, r);
+}
+
+// Transposed quad reduction: lane lq (0..3) of a quad holds partial sums
+// acc[0..3] of four keys; it returns the sum over the quad of key lq. Step 1
+// exchanges with lane lq ^ 1 (each lane keeps the keys whose bit 0 is its
+// own), step 2 with lane lq ^ 2; 6 cross-lane moves instead of 16.
+__device__ __forceinline__ double quad_transpose_sum(const double (&acc)[4], int lq) {
+    constexpr int kXor1 = 0xB1;                 // quad_perm [1, 0, 3, 2]
+    constexpr int kXor2 = 0x4E;                 // quad_perm [2, 3, 0, 1]
+    const bool b0 = lq & 1, b1 = lq & 2;
+    const double t0 = (b0 ? acc[1] : acc[0]) + quad_perm_f64<kXor1>(b0 ? acc[0] : acc[1]);   // key b0
+    const double t1 = (b0 ? acc[3] : acc[2]) + quad_perm_f64<kXor1>(b0 ? acc[2] : acc[3]);   // key 2 + b0
+    return (b1 ? t1 : t0) + quad_perm_f64<kXor2>(b1 ? t0 : t1);
+}
+
 }  // namespace csa2

@@ -122,6 +122,58 @@ struct SrcScan {
             const int64_t v = q_pos[row] - begin + 1;
             lim = (int)(v < 0 ? 0 : (v > cnt ? cnt : v));
         }
+        if constexpr (KS::RAW == 1) {
+            // One 16-byte load per lane and key: batches of 1024 keys, key
+            // base + 256u + quad in slot u of its quad's lanes; after the
+            // transposed reduction lane lq owns key base + 256 lq + quad. Whole
+            // unmasked batches run software-pipelined (the next batch's loads
+            // are issued before this one is scored; two register sets, loads
+            // unconditional with the batch index clamped), the rest predicated.
+            constexpr int kB = kSelThreads;
+            const uint8_t* kq = kb + (int64_t)quad * KS::ROW_BYTES + lq * (KS::ROW_BYTES / 4);
+            const int nfull = lim / kB;
+            auto load_batch = [&](int bi, uint4 (&r)[4]) {
+#pragma unroll
+                for (int u = 0; u < 4; ++u) r[u] = ld_stream16(kq + (int64_t)(bi * kB + u * 256) * KS::ROW_BYTES);
+            };
+            auto score_batch = [&](const uint4 (&r)[4], int base, bool masked) {
+                double acc[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    KS sl;
+                    sl.raw[0] = r[u];
+                    acc[u] = sl.dot(qd);
+                }
+                const double v = quad_transpose_sum(acc, lq);
+                const int i = base + lq * 256 + quad;
+                if (!masked) put_key(keys, hist, i, score_key((float)v));
+                else if (i < cnt) put_key(keys, hist, i, (i < lim) ? score_key((float)v) : 0u);
+            };
+            if (nfull > 0) {
+                uint4 ra[4], rb[4];
+                load_batch(0, ra);
+                int bi = 0;
+                for (; bi + 2 <= nfull; bi += 2) {
+                    load_batch(bi + 1, rb);
+                    score_batch(ra, bi * kB, false);
+                    load_batch(min(bi + 2, nfull - 1), ra);
+                    score_batch(rb, (bi + 1) * kB, false);
+                }
+                if (bi < nfull) score_batch(ra, bi * kB, false);
+            }
+            for (int base = nfull * kB; base < cnt; base += kB) {
+                uint4 r[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int i = base + u * 256 + quad;
+                    r[u] = (i < lim) ? ld_stream16(kq + (int64_t)(base + u * 256) * KS::ROW_BYTES) : make_uint4(0, 0, 0, 0);
+                }
+                score_batch(r, base, true);
+            }
+            pad_keys(keys, cnt, cpad);
+            __syncthreads();
+            return;
+        }
         for (int base = 0; base < cnt; base += (kSelThreads / 4) * U) {
             KS s[U];
 #pragma unroll
