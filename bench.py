@@ -15,6 +15,7 @@ oracle timed on a bounded sample of the same workload (cpu_baseline).
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
   python bench.py --copy-calibration   # also runs a known-size copy kernel (for PMC scaling)
   python bench.py --workload stack_b4_n1m --prefill --steps 3 --warmup 1   # the prefill chunk
+  python bench.py --workload quant_1m_x512 --steps 20                       # kv_quant_fp4 / dequant
 """
 
 import argparse
@@ -167,6 +168,77 @@ def cpu_baseline(cfg, budget_s):
                       f"KV rows quantized by the oracle only where attention reads them"}
 
 
+def run_quant(args, cfg, dev):
+    """The quantize workload: kv_quant_fp4 and kv_dequant_fp4 over T x C bf16 rows (each call timed alone,
+    back to back, K calls between two events), with the oracle's quantizer on a bounded sample of rows."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_limits
+
+    import fp4_compressed_sparse_kv_amd as C
+    import synth
+    from oracle import quant as OQ
+
+    T, Cc, rb = cfg["T"], cfg["C"], cfg["row_block"]
+    t0 = time.perf_counter()
+    x = torch.empty(T, Cc, dtype=torch.bfloat16, device=dev)
+    for blk in range(T // rb):
+        xb = synth.quant_rows(cfg, blk)
+        x[blk * rb:(blk + 1) * rb].copy_(torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16))
+    log(f"inputs ready in {time.perf_counter() - t0:.1f} s")
+    codes = torch.empty(T, Cc // 2, dtype=torch.uint8, device=dev)
+    scales = torch.empty(T, Cc // 16, dtype=torch.uint8, device=dev)
+    y = torch.empty_like(x)
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    q_ms = timed(lambda: C.kv_quant_fp4(x, codes, scales))
+    d_ms = timed(lambda: C.kv_dequant_fp4(codes, scales, Cc, y))
+    nbytes = T * Cc * 2 + T * (Cc // 2 + Cc // 16)            # bf16 rows + codes + scales, each direction
+    groups = T * Cc // 16
+    s_zero = int((scales == 0).sum().item())
+    s_sat = int((scales == 0x7E).sum().item())
+    out = {
+        "metric": "kv_quant_fp4 HBM GB/s (bf16 rows in, FP4 codes + E4M3 scales out)",
+        "value": round(nbytes / (q_ms * 1e-3) / 1e9, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(q_ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32 compares / u8", "data": "synthetic",
+        "config": {"workload": args.workload, "T": T, "C": Cc},
+        "rows_per_s": round(T / (q_ms * 1e-3), 1),
+        "dequant_ms": round(d_ms, 5), "dequant_gbs": round(nbytes / (d_ms * 1e-3) / 1e9, 1),
+        "alg_bytes_per_call": nbytes, "groups": groups, "groups_scale_zero": s_zero, "groups_scale_448": s_sat,
+        "roofline": {"bound": "hbm", "kernel": "k_quant", "achieved": round(nbytes / (q_ms * 1e-3) / 1e9, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(nbytes / (q_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "traffic": None},
+    }
+    if not args.no_cpu:
+        done, spent = 0, 0.0
+        with threadpool_limits(limits=1):
+            for blk in range(T // rb):
+                xb = synth.quant_rows(cfg, blk)                   # untimed: input generation
+                t1 = time.perf_counter()
+                OQ.quant_fp4(xb)
+                spent += time.perf_counter() - t1
+                done += rb
+                if spent >= args.cpu_seconds:
+                    break
+        out["cpu_baseline"] = {"value": round(done / spent, 1), "unit": "rows/s", "cores": 1, "kind": "oracle",
+                               "sample": f"{done} of {T} rows ({done // rb} blocks of {rb}), {spent:.1f} s on 1 host "
+                                         f"core (BLAS limited to 1 thread)"}
+    print(json.dumps(out), flush=True)
+
+
 def run_prefill(args, cfg, dev):
     """Full-layer prefill of the workload's chunk: prefill_Q queries per sequence at the last
     positions of the context (causal), through the matrix-core indexer, exact top-K and attention."""
@@ -236,6 +308,7 @@ def main():
                                    "(see DESIGN.md) and no multi-GPU run is provided", "n_gpus": args.gpus}))
         sys.exit(2)
 
+    import numpy as np
     import torch
 
     import fp4_compressed_sparse_kv_amd as C
@@ -247,6 +320,9 @@ def main():
             raise SystemExit(f"{args.workload} has no prefill chunk")
         torch.cuda.set_device(0)
         return run_prefill(args, cfg, torch.device("cuda", 0))
+    if "T" in cfg:
+        torch.cuda.set_device(0)
+        return run_quant(args, cfg, torch.device("cuda", 0))
     if "modes" not in cfg:
         raise SystemExit(f"{args.workload} is not a decode workload")
     dev = torch.device("cuda", 0)
@@ -295,6 +371,19 @@ def main():
         cold.append(a.elapsed_time(b))
     del flush
 
+    # achievable reference: a device-to-device copy of 1 GiB (2 GiB moved)
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(5):
+        dst.copy_(src)
+    b.record(stream)
+    torch.cuda.synchronize()
+    copy_gbs = 2 * (1 << 30) * 5 / (a.elapsed_time(b) * 1e-3) / 1e9
+    del src, dst
+
     if args.copy_calibration:
         # known-size copy kernel for scaling PMC byte counters: reads and writes 1 GiB
         x = torch.ones(1 << 28, dtype=torch.float32, device=dev)
@@ -329,6 +418,8 @@ def main():
         "hbm_frac_step": round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "alg_bytes_step": step_bytes,
         "cold_ms_per_step": round(sorted(cold)[len(cold) // 2], 5) if cold else None,
+        "cold_ms_p10_p90": [round(float(np.percentile(cold, 10)), 5), round(float(np.percentile(cold, 90)), 5)] if cold else None,
+        "achievable_copy_gbs": round(copy_gbs, 1),
         "kernel_ms": {"full_select": round(sel_ms, 5),
                       **{f"slot{i}": round(v, 5) for i, v in enumerate(slot_ms) if i > 0 and v > 0}},
         "roofline": {"bound": "hbm", "kernel": "k_select<SrcScan> (Full layer: scan + pool/top-K select)",

@@ -1,87 +1,180 @@
 // FP4 E2M1 quantization with one E4M3 scale per 16 channels, and the inverse.
 //
-// One lane owns one 16-channel group: it loads the group's 32 bytes of bf16
-// with two 16-byte loads (a wave covers 2 KiB of a row contiguously), finds
-// amax, rounds amax/6 to E4M3 (round-to-nearest-even, saturating at 448),
-// and picks each E2M1 code by comparing |x| with the scaled rounding
-// thresholds t*S, t in {0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5}. Each t*S has at
-// most 7 significant bits, so it is exact in fp32 and the comparison decides
-// exactly as rounding the real quotient x/S would: strict '>' at thresholds
-// whose lower neighbour has the even code, '>=' where the upper one does.
+// One lane owns one 16-channel group (two groups per pass, their loads issued
+// together): it loads the group's 32 bytes of bf16 with two 16-byte loads (a
+// wave covers 2 KiB of a row contiguously), finds amax and rounds amax/6 to
+// E4M3 (round-to-nearest-even, saturating at 448). Each E2M1 code is the
+// round-to-nearest-even of x/S onto {0, .5, 1, 1.5, 2, 3, 4, 6} with
+// saturation and the sign of x. That rounding is done by the hardware FP4
+// convert on y = x * RN(1/S) with y rounded to 12 significant bits first.
+// Exactness: for bf16 x and E4M3 S the real quotient x/S either equals a
+// rounding midpoint t exactly (x = t*S) or lies at least 2^-8 (relative) away
+// from every midpoint; y is within 2^-23 of x/S, so rounding it to 12 bits
+// gives exactly t in the first case and stays on the same side of every
+// midpoint in the second (checked on the device for every finite bf16 x and
+// every positive finite E4M3 S). Groups holding an Inf or NaN take the
+// threshold form of the same rule: |x| compared with t*S, each product exact
+// in fp32 (NaN codes to a signed zero, Inf to 6).
 // The 16 codes leave as one 8-byte store, the scale as one byte.
 #include "device.hpp"
 #include "internal.hpp"
 
 namespace csa2 {
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
 constexpr int kQuantThreads = 256;
 
-__global__ void __launch_bounds__(kQuantThreads)
-k_quant(const uint16_t* __restrict__ x, int64_t rows, int32_t gpr, int64_t x_stride, uint8_t* __restrict__ codes,
-        int64_t cs, uint8_t* __restrict__ scales, int64_t ss) {
-    const int64_t total = rows * gpr;
-    for (int64_t gid = (int64_t)blockIdx.x * kQuantThreads + threadIdx.x; gid < total;
-         gid += (int64_t)gridDim.x * kQuantThreads) {
-        const int64_t r = gid / gpr;
-        const int32_t g = (int32_t)(gid - r * gpr);
-        const uint4* src = reinterpret_cast<const uint4*>(x + r * x_stride + (int64_t)g * 16);
-        const uint4 a = ld_stream16(src);
-        const uint4 b = ld_stream16(src + 1);
-        const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-        uint32_t amax_bits = 0;                 // |x| of non-NaN bf16 orders like its bits
+// E2M1 code by thresholds t*S (t = 0.25 .. 5): strict '>' where the lower
+// neighbour has the even code, '>=' where the upper one does.
+__device__ __forceinline__ uint32_t code_by_thresholds(uint32_t hb, float S) {
+    const float v = bf16_bits_to_f32(hb & 0x7FFFu);
+    uint32_t c = (uint32_t)(v > 0.25f * S) + (uint32_t)(v >= 0.75f * S) + (uint32_t)(v > 1.25f * S) +
+                 (uint32_t)(v >= 1.75f * S) + (uint32_t)(v > 2.5f * S) + (uint32_t)(v >= 3.5f * S) +
+                 (uint32_t)(v > 5.0f * S);
+    return c | ((hb >> 12) & 8u);               // sign bit of the bf16 -> code bit 3
+}
+
+// y rounded to 12 significant bits (half away from zero on the magnitude).
+__device__ __forceinline__ float round12(float y) { return __uint_as_float((__float_as_uint(y) + 0x400u) & ~0x7FFu); }
+
+// Codes of the bf16 pair in w (channels 2j, 2j+1), times r, into byte J of acc.
+template <int J>
+__device__ __forceinline__ uint32_t put_pair(uint32_t acc, uint32_t w, float r) {
+    return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(acc, round12(bf16_bits_to_f32(w & 0xFFFFu) * r),
+                                                    round12(__uint_as_float(w & 0xFFFF0000u) * r), 1.0f, J);
+}
+
+// E2M1 values (unit scale) of the two codes in byte J of w.
+template <int J>
+__device__ __forceinline__ f32x2 fp4_pair(uint32_t w) {
+    return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, J);
+}
+
+// 16 bf16 values (w[j]: channels 2j, 2j+1) -> packed codes and the scale byte.
+__device__ __forceinline__ uint2 quant_group(const uint32_t (&w)[8], uint32_t& sc) {
+    uint32_t amax_bits = 0;                     // |x| of non-NaN bf16 orders like its bits
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            amax_bits = max(amax_bits, w[i] & 0x7FFFu);
-            amax_bits = max(amax_bits, (w[i] >> 16) & 0x7FFFu);
-        }
-        const float amax = bf16_bits_to_f32(amax_bits);
-        const uint32_t sc = f32_to_e4m3_sat(__fdiv_rn(amax, 6.0f));
-        const float S = e4m3_to_f32(sc);
-        uint32_t lo = 0, hi = 0;
-        if (S > 0.0f) {
-            const float t0 = 0.25f * S, t1 = 0.75f * S, t2 = 1.25f * S, t3 = 1.75f * S;
-            const float t4 = 2.5f * S, t5 = 3.5f * S, t6 = 5.0f * S;
+    for (int i = 0; i < 8; ++i) {
+        amax_bits = max(amax_bits, w[i] & 0x7FFFu);
+        amax_bits = max(amax_bits, (w[i] >> 16) & 0x7FFFu);
+    }
+    const float amax = bf16_bits_to_f32(amax_bits);
+    sc = f32_to_e4m3_sat(__fdiv_rn(amax, 6.0f));
+    const float S = e4m3_to_f32(sc);
+    uint32_t lo = 0, hi = 0;
+    if (S > 0.0f && amax_bits < 0x7F80u) {
+        const float r = __frcp_rn(S);
+        lo = put_pair<0>(lo, w[0], r);
+        lo = put_pair<1>(lo, w[1], r);
+        lo = put_pair<2>(lo, w[2], r);
+        lo = put_pair<3>(lo, w[3], r);
+        hi = put_pair<0>(hi, w[4], r);
+        hi = put_pair<1>(hi, w[5], r);
+        hi = put_pair<2>(hi, w[6], r);
+        hi = put_pair<3>(hi, w[7], r);
+    } else if (S > 0.0f) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const uint32_t hb = (i & 1) ? (w[i >> 1] >> 16) : (w[i >> 1] & 0xFFFFu);
-                const float v = bf16_bits_to_f32(hb & 0x7FFFu);
-                uint32_t c = (uint32_t)(v > t0) + (uint32_t)(v >= t1) + (uint32_t)(v > t2) + (uint32_t)(v >= t3) +
-                             (uint32_t)(v > t4) + (uint32_t)(v >= t5) + (uint32_t)(v > t6);
-                c |= (hb >> 12) & 8u;           // sign bit of the bf16 -> code bit 3
-                if (i < 8) lo |= c << (4 * i);
-                else hi |= c << (4 * (i - 8));
-            }
+        for (int i = 0; i < 16; ++i) {
+            const uint32_t hb = (i & 1) ? (w[i >> 1] >> 16) : (w[i >> 1] & 0xFFFFu);
+            const uint32_t c = code_by_thresholds(hb, S);
+            if (i < 8) lo |= c << (4 * i);
+            else hi |= c << (4 * (i - 8));
         }
-        *reinterpret_cast<uint2*>(codes + r * cs + (int64_t)g * 8) = make_uint2(lo, hi);
-        scales[r * ss + g] = (uint8_t)sc;
+    }
+    return make_uint2(lo, hi);
+}
+
+// Row and group of group index gid: shifts when the groups per row are a power of two.
+__device__ __forceinline__ void row_group(int64_t gid, int32_t gpr, int32_t gshift, int64_t& r, int32_t& g) {
+    if (gshift >= 0) {
+        r = gid >> gshift;
+        g = (int32_t)(gid & (gpr - 1));
+    } else {
+        r = gid / gpr;
+        g = (int32_t)(gid - r * gpr);
     }
 }
 
 __global__ void __launch_bounds__(kQuantThreads)
-k_dequant(const uint8_t* __restrict__ codes, int64_t cs, const uint8_t* __restrict__ scales, int64_t ss,
-          int64_t rows, int32_t gpr, uint16_t* __restrict__ y, int64_t y_stride) {
+k_quant(const uint16_t* __restrict__ x, int64_t rows, int32_t gpr, int32_t gshift, int64_t x_stride,
+        uint8_t* __restrict__ codes, int64_t cs, uint8_t* __restrict__ scales, int64_t ss) {
     const int64_t total = rows * gpr;
-    for (int64_t gid = (int64_t)blockIdx.x * kQuantThreads + threadIdx.x; gid < total;
-         gid += (int64_t)gridDim.x * kQuantThreads) {
-        const int64_t r = gid / gpr;
-        const int32_t g = (int32_t)(gid - r * gpr);
-        const uint2 c = *reinterpret_cast<const uint2*>(codes + r * cs + (int64_t)g * 8);
-        const float S = e4m3_to_f32(scales[r * ss + g]);
-        uint32_t o[8];
+    const int64_t stride = (int64_t)gridDim.x * kQuantThreads;
+    for (int64_t gid = (int64_t)blockIdx.x * kQuantThreads + threadIdx.x; gid < total; gid += 2 * stride) {
+        int64_t r[2];
+        int32_t g[2];
+        bool ok[2];
+        uint32_t w[2][8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const uint32_t word = (i < 4) ? c.x : c.y;
-            const uint32_t byte = (word >> (8 * (i & 3))) & 0xFFu;
-            const uint32_t c0 = byte & 0xFu, c1 = byte >> 4;
-            // E2M1 * E4M3 is exact in fp32 and in bf16, so the top half is the bf16.
-            const uint32_t v0 = __float_as_uint(e2m1_mag_to_f32(c0 & 7u) * S) | ((c0 & 8u) << 28);
-            const uint32_t v1 = __float_as_uint(e2m1_mag_to_f32(c1 & 7u) * S) | ((c1 & 8u) << 28);
-            o[i] = (v0 >> 16) | (v1 & 0xFFFF0000u);
+        for (int k = 0; k < 2; ++k) {
+            const int64_t id = gid + k * stride;
+            ok[k] = id < total;
+            row_group(ok[k] ? id : gid, gpr, gshift, r[k], g[k]);
+            const uint4* src = reinterpret_cast<const uint4*>(x + r[k] * x_stride + (int64_t)g[k] * 16);
+            const uint4 a = ld_stream16(src), b = ld_stream16(src + 1);
+            w[k][0] = a.x; w[k][1] = a.y; w[k][2] = a.z; w[k][3] = a.w;
+            w[k][4] = b.x; w[k][5] = b.y; w[k][6] = b.z; w[k][7] = b.w;
         }
-        uint4* dst = reinterpret_cast<uint4*>(y + r * y_stride + (int64_t)g * 16);
-        dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
-        dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            uint32_t sc;
+            const uint2 c = quant_group(w[k], sc);
+            if (ok[k]) {
+                *reinterpret_cast<uint2*>(codes + r[k] * cs + (int64_t)g[k] * 8) = c;
+                scales[r[k] * ss + g[k]] = (uint8_t)sc;
+            }
+        }
     }
+}
+
+// Dequantization: the hardware FP4 convert gives the E2M1 values (signed, at
+// unit scale), times the E4M3 scale in fp32. E2M1 x E4M3 has at most 6
+// significant bits and lies in [2^-10, 2688], so the product is exact and its
+// top half is the bf16.
+__global__ void __launch_bounds__(kQuantThreads)
+k_dequant(const uint8_t* __restrict__ codes, int64_t cs, const uint8_t* __restrict__ scales, int64_t ss,
+          int64_t rows, int32_t gpr, int32_t gshift, uint16_t* __restrict__ y, int64_t y_stride) {
+    const int64_t total = rows * gpr;
+    const int64_t stride = (int64_t)gridDim.x * kQuantThreads;
+    for (int64_t gid = (int64_t)blockIdx.x * kQuantThreads + threadIdx.x; gid < total; gid += 2 * stride) {
+        int64_t r[2];
+        int32_t g[2];
+        bool ok[2];
+        uint2 c[2];
+        uint32_t sb[2];
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int64_t id = gid + k * stride;
+            ok[k] = id < total;
+            row_group(ok[k] ? id : gid, gpr, gshift, r[k], g[k]);
+            c[k] = *reinterpret_cast<const uint2*>(codes + r[k] * cs + (int64_t)g[k] * 8);
+            sb[k] = scales[r[k] * ss + g[k]];
+        }
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const float S = e4m3_to_f32(sb[k]);
+            const f32x2 v[8] = {fp4_pair<0>(c[k].x), fp4_pair<1>(c[k].x), fp4_pair<2>(c[k].x), fp4_pair<3>(c[k].x),
+                                fp4_pair<0>(c[k].y), fp4_pair<1>(c[k].y), fp4_pair<2>(c[k].y), fp4_pair<3>(c[k].y)};
+            uint32_t o[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                o[j] = (__float_as_uint(v[j].x * S) >> 16) | (__float_as_uint(v[j].y * S) & 0xFFFF0000u);
+            if (ok[k]) {
+                uint4* dst = reinterpret_cast<uint4*>(y + r[k] * y_stride + (int64_t)g[k] * 16);
+                dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
+                dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
+            }
+        }
+    }
+}
+
+// log2(n) when n is a power of two, else -1.
+static int32_t pow2_shift(int32_t n) {
+    if (n <= 0 || (n & (n - 1))) return -1;
+    int32_t sh = 0;
+    while ((1 << sh) < n) ++sh;
+    return sh;
 }
 
 static unsigned grid_for(int64_t items, int threads) {
@@ -96,7 +189,7 @@ int launch_quant(const uint16_t* x, int64_t rows, int32_t C, int64_t x_stride, u
     if (rows == 0) return OK;
     const int32_t gpr = C / 16;
     hipLaunchKernelGGL(k_quant, dim3(grid_for(rows * gpr, kQuantThreads)), dim3(kQuantThreads), 0, stream, x, rows,
-                       gpr, x_stride, codes, cs, scales, ss);
+                       gpr, pow2_shift(gpr), x_stride, codes, cs, scales, ss);
     const hipError_t e = hipGetLastError();
     return e == hipSuccess ? OK : hip_fail(e, "launch k_quant");
 }
@@ -106,7 +199,7 @@ int launch_dequant(const uint8_t* codes, int64_t cs, const uint8_t* scales, int6
     if (rows == 0) return OK;
     const int32_t gpr = C / 16;
     hipLaunchKernelGGL(k_dequant, dim3(grid_for(rows * gpr, kQuantThreads)), dim3(kQuantThreads), 0, stream, codes,
-                       cs, scales, ss, rows, gpr, y, y_stride);
+                       cs, scales, ss, rows, gpr, pow2_shift(gpr), y, y_stride);
     const hipError_t e = hipGetLastError();
     return e == hipSuccess ? OK : hip_fail(e, "launch k_dequant");
 }
