@@ -60,6 +60,34 @@ def test_quant_bit_exact_all_bf16_values(C_):
     assert np.array_equal(host(codes), rc)
 
 
+def test_quant_every_scale_with_every_value_up_to_its_group_max():
+    """Every (x, S) pair the quantizer can meet: for each positive finite E4M3 scale S, groups whose
+    maximum is 6*S (so the group's scale is S) hold, in their other 15 slots, every finite bf16 x with
+    |x| <= 6*S, both signs. Codes and scales must equal the oracle's bit for bit."""
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    finite = (bits & 0x7F80) != 0x7F80
+    mag = F.bf16_decode(np.where(finite, bits & np.uint16(0x7FFF), 0).astype(np.uint16))
+    groups = []
+    for sc in range(1, 0x7F):
+        S = float(F.e4m3_decode(np.array([sc], dtype=np.uint8))[0])
+        top = np.float32(6.0 * S)
+        tb = synth.to_bf16_bits(np.array([top], dtype=np.float32))[0]
+        if F.bf16_decode(np.array([tb]))[0] != top:      # 6*S not a bf16: this scale is not reached this way
+            continue
+        vals = bits[finite & (mag <= top)]
+        pad = (-vals.size) % 15
+        vals = np.concatenate([vals, np.zeros(pad, dtype=np.uint16)]).reshape(-1, 15)
+        groups.append(np.concatenate([np.full((vals.shape[0], 1), tb, dtype=np.uint16), vals], axis=1))
+    g = np.concatenate(groups)
+    rows = (g.shape[0] + 31) // 32
+    g = np.concatenate([g, np.zeros((rows * 32 - g.shape[0], 16), dtype=np.uint16)]).reshape(rows, 512)
+    codes, scales = C.kv_quant_fp4(dev_bf16(g))
+    rc, rs = OQ.quant_fp4(g)
+    assert np.array_equal(host(scales), rs)
+    assert np.array_equal(host(codes), rc)
+    assert len(set(rs.ravel().tolist())) >= 100            # nearly every scale code occurs
+
+
 def test_quant_bit_exact_log_uniform_rows_and_dequant():
     cfg = synth.small("quant_1m_x512", row_block=2048)
     x = np.concatenate([synth.quant_rows(cfg, 0), synth.quant_rows(cfg, 7)])[:3001]   # ragged row count
