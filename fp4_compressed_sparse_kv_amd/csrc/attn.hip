@@ -1,7 +1,8 @@
 // Sparse softmax attention over gathered FP4 KV rows on gfx950 matrix cores.
 //
 // One query row (all H <= 16 heads, which share one KV head and one position
-// list) is split over NS workgroups of kAttnWaves waves; each wave walks
+// list) is split over NS workgroups of W waves (8, or 4 when every row has a
+// workgroup of its own); each wave walks
 // blocks of 32 positions of its slice, with the next block's gathers (and the
 // position list of the block after it) in flight while the current block is
 // computed. Per block, a wave:
@@ -46,8 +47,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kAttnWaves = 4;
-constexpr int kAttnThreads = kAttnWaves * kWave;
 constexpr int kBlk = 32;
 constexpr int kMaxHeads = 16;
 constexpr int kD = 128;
@@ -56,25 +55,34 @@ constexpr int kMaxSplits = 8;
 constexpr int kPartFloats = kMaxHeads * kD + 2 * kMaxHeads;   // per (row, slice): acc [16][128], (m, l) [16][2]
 constexpr int kVRowBytes = 80;                  // staged V row: 64 code bytes + pad (conflict-free dword reads)
 constexpr int kMergeStride = kD + 4;
-constexpr int kCh = kMaxHeads * kD / kAttnThreads;  // output channels per thread in the merges
-constexpr int kV4 = kCh / 4;
-static_assert(kCh % 4 == 0 && kD % kCh == 0, "merge tiling");
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr uint32_t kRsrcWord3 = 0x00020000u;    // raw buffer resource (byte-addressed, 32-bit data format)
 constexpr int kCoherent = 16;                   // buffer cache policy sc1: device-coherent access
 
-static int attn_splits(int64_t rows, int32_t K) {
+static int attn_splits(int64_t rows, int32_t K, int waves) {
     const int64_t nblk = (K + kBlk - 1) / kBlk;
     int64_t ns = (kAttnTargetGroups + rows - 1) / (rows > 0 ? rows : 1);
-    const int64_t max_ns = (nblk + kAttnWaves - 1) / kAttnWaves;   // at least one block per wave
+    const int64_t max_ns = (nblk + waves - 1) / waves;   // at least one block per wave
     if (ns > max_ns) ns = max_ns;
     if (ns > kMaxSplits) ns = kMaxSplits;
     if (ns < 1) ns = 1;
     return (int)ns;
 }
 
+// Launch shape: rows that fill the device one workgroup each run 4-wave
+// workgroups (more of them resident per CU); rows split over several
+// workgroups run 8-wave ones (fewer, shorter slices to merge).
+struct AttnShape {
+    int waves, ns;
+};
+static AttnShape attn_shape(int64_t rows, int32_t K) {
+    const int ns4 = attn_splits(rows, K, 4);
+    if (ns4 == 1) return AttnShape{4, 1};
+    return AttnShape{8, attn_splits(rows, K, 8)};
+}
+
 size_t attn_data_bytes(int64_t rows, int32_t K) {
-    const int ns = attn_splits(rows, K);
+    const int ns = attn_shape(rows, K).ns;
     return ns > 1 ? (size_t)rows * ns * kPartFloats * 4 : 0;
 }
 
@@ -110,15 +118,17 @@ struct Stage {                                  // one wave's LDS staging area
     uint8_t vs[kBlk][8];
 };
 
+template <int W>
 struct MergeArea {
-    float acc[kAttnWaves][kMaxHeads][kMergeStride];
-    float m[kAttnWaves][kMaxHeads];
-    float l[kAttnWaves][kMaxHeads];
+    float acc[W][kMaxHeads][kMergeStride];
+    float m[W][kMaxHeads];
+    float l[W][kMaxHeads];
 };
 
+template <int W>
 union AttnLds {
-    Stage st[kAttnWaves];
-    MergeArea mg;
+    Stage st[W];
+    MergeArea<W> mg;
 };
 
 // Raw position-list entry of lane `lane` of block `blk` (lanes >= 32 and
@@ -271,13 +281,19 @@ __device__ __forceinline__ void attend_block(WaveState& st, const BlockRaw& r, S
     }
 }
 
-__global__ void __launch_bounds__(kAttnThreads, 2)
+template <int W>
+__global__ void __launch_bounds__(W * kWave, W == 4 ? 2 : 1)
 k_sparse_attn(const uint16_t* __restrict__ q, int32_t rows_per_seq, int32_t H, const uint8_t* __restrict__ k_codes,
               const uint8_t* __restrict__ k_scales, const uint8_t* __restrict__ v_codes,
               const uint8_t* __restrict__ v_scales, int64_t N, int64_t cs, int64_t ss, const int32_t* __restrict__ idx,
               int64_t idx_stride, int32_t K, float scale, float* __restrict__ out, int32_t NS,
               uint32_t* __restrict__ counters, float* __restrict__ parts, int64_t rows) {
-    __shared__ AttnLds lds;
+    constexpr int kAttnWaves = W;
+    constexpr int kAttnThreads = W * kWave;
+    constexpr int kCh = kMaxHeads * kD / kAttnThreads;  // output channels per thread in the merges
+    constexpr int kV4 = kCh / 4;
+    static_assert(kCh % 4 == 0 && kD % kCh == 0, "merge tiling");
+    __shared__ AttnLds<W> lds;
     __shared__ int s_last;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -466,13 +482,15 @@ k_sparse_attn(const uint16_t* __restrict__ q, int32_t rows_per_seq, int32_t H, c
 
 int launch_attn(const AttnArgs& a, void* ws_ctrl, void* ws_data, size_t data_bytes, hipStream_t stream) {
     if (a.rows == 0) return OK;
-    const int ns = attn_splits(a.rows, a.K);
+    const AttnShape sh = attn_shape(a.rows, a.K);
+    const int ns = sh.ns;
     if (data_bytes < attn_data_bytes(a.rows, a.K)) return fail(WORKSPACE, "attention workspace too small");
     if (ns > 1 && a.rows > kAttnCtrlWords) return fail(INVALID, "attention: split rows exceed the counter table");
     const int64_t groups = a.rows * ns;
     if (groups > 0x7FFFFFFFll) return fail(INVALID, "attention: too many query rows");
     uint32_t* counters = reinterpret_cast<uint32_t*>(ws_ctrl) + kAttnCtrlOffsetWords;
-    hipLaunchKernelGGL(k_sparse_attn, dim3((unsigned)groups), dim3(kAttnThreads), 0, stream, a.q, a.rows_per_seq,
+    auto fn = sh.waves == 4 ? k_sparse_attn<4> : k_sparse_attn<8>;
+    hipLaunchKernelGGL(fn, dim3((unsigned)groups), dim3(sh.waves * kWave), 0, stream, a.q, a.rows_per_seq,
                        a.H, a.k_codes, a.k_scales, a.v_codes, a.v_scales, a.N, a.code_stride, a.scale_stride, a.idx,
                        a.idx_stride, a.K, a.scale, a.out, ns, counters, reinterpret_cast<float*>(ws_data), a.rows);
     const hipError_t e = hipGetLastError();

@@ -55,6 +55,7 @@ constexpr int kMaxSteps = kMaxChunk / kSelWaves / kPadTo;   // steps per wave (8
 struct SelDev {
     int64_t n;
     int32_t S, chunk, chunk_pad, row0, nt, row_words;
+    int32_t pos_lds;                            // the source keeps each key's position in LDS
     uint32_t* ctrl;                             // workspace control region
     uint32_t* data;                             // this call's data region
     const int32_t* rowmap;                      // launch row -> row (-1: nothing to do), or null
@@ -87,8 +88,9 @@ struct SrcScores {
     const int32_t* cand;
     int64_t n;
 
+    static constexpr bool kPosLds = false;
     __device__ __forceinline__ void fill(int64_t row, int64_t begin, int cnt, int cpad, uint32_t* keys,
-                                         uint32_t* hist) const {
+                                         uint32_t* hist, uint32_t*) const {
         const float* p = scores + row * stride + begin;
         for (int i = threadIdx.x; i < cnt; i += kSelThreads) put_key(keys, hist, i, score_key(p[i]));
         pad_keys(keys, cnt, cpad);
@@ -107,8 +109,9 @@ struct SrcScan {
     int32_t rows_per_seq;
     const int64_t* q_pos;
 
+    static constexpr bool kPosLds = false;       // position = index
     __device__ __forceinline__ void fill(int64_t row, int64_t begin, int cnt, int cpad, uint32_t* keys,
-                                         uint32_t* hist) const {
+                                         uint32_t* hist, uint32_t*) const {
         using KS = KeySlice<KT, D>;
         constexpr int QB = (QT == kBF16) ? 2 : 4;
         constexpr int U = KS::RAW >= 4 ? 1 : 4 / KS::RAW;   // 64 bytes in flight per lane
@@ -203,8 +206,9 @@ struct SrcPool {
     const int32_t* pool;
     int64_t P;
 
+    static constexpr bool kPosLds = true;        // positions come from the pool: kept in LDS when they fit
     __device__ __forceinline__ void fill(int64_t row, int64_t begin, int cnt, int cpad, uint32_t* keys,
-                                         uint32_t* hist) const {
+                                         uint32_t* hist, uint32_t* posl) const {
         using KS = KeySlice<KT, D>;
         constexpr int QB = (QT == kBF16) ? 2 : 4;
         constexpr int U = KS::RAW >= 4 ? 1 : 4 / KS::RAW;
@@ -216,19 +220,23 @@ struct SrcPool {
         for (int base = 0; base < cnt; base += (kSelThreads / 4) * U) {
             KS s[U];
             bool ok[U];
+            int32_t pv[U];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int i = base + u * (kSelThreads / 4) + quad;
-                const int32_t pos = (i < cnt) ? pr[i] : -1;
-                ok[u] = pos >= 0 && (int64_t)pos < N;
-                if (ok[u]) s[u].load(kb + (int64_t)pos * KS::ROW_BYTES, lq);
+                pv[u] = (i < cnt) ? pr[i] : -1;
+                ok[u] = pv[u] >= 0 && (int64_t)pv[u] < N;
+                if (ok[u]) s[u].load(kb + (int64_t)pv[u] * KS::ROW_BYTES, lq);
                 else for (int j = 0; j < KS::RAW; ++j) s[u].raw[j] = make_uint4(0, 0, 0, 0);
             }
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int i = base + u * (kSelThreads / 4) + quad;
                 const double v = quad_sum(s[u].dot(qd));
-                if (lq == 0 && i < cnt) put_key(keys, hist, i, ok[u] ? score_key((float)v) : 0u);
+                if (lq == 0 && i < cnt) {
+                    put_key(keys, hist, i, ok[u] ? score_key((float)v) : 0u);
+                    if (posl) posl[i] = (uint32_t)pv[u];
+                }
             }
         }
         pad_keys(keys, cnt, cpad);
@@ -257,8 +265,9 @@ struct SrcCand {
 
     // Only the valid slots are visited: the chunk's keys start at 0 (padding)
     // and each valid slot (list r, slot sl) writes its key at entry r*cap + sl.
+    static constexpr bool kPosLds = true;        // positions come from the lists: kept in LDS when they fit
     __device__ __forceinline__ void fill(int64_t row, int64_t begin, int cnt_, int cpad, uint32_t* keys,
-                                         uint32_t* hist) const {
+                                         uint32_t* hist, uint32_t* posl) const {
         using KS = KeySlice<KT, D>;
         constexpr int QB = (QT == kBF16) ? 2 : 4;
         constexpr int U = KS::RAW >= 4 ? 2 : 8 / KS::RAW;
@@ -289,7 +298,7 @@ struct SrcCand {
         __syncthreads();                        // the zero fill is complete before valid keys land
         for (uint32_t base = 0; base < total; base += (kSelThreads / 4) * U) {
             KS s[U];
-            int32_t ent[U];
+            int32_t ent[U], pv[U];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const uint32_t v = base + u * (kSelThreads / 4) + quad;     // v-th valid entry of the chunk
@@ -306,6 +315,7 @@ struct SrcCand {
                     const int r = (int)(e / cap), sl = (int)(e - (int64_t)r * cap);
                     pos = cand[(row * nranges + r) * cap + sl];
                 }
+                pv[u] = pos;
                 if (pos >= 0 && (int64_t)pos < N) {
                     s[u].load(kb + (int64_t)pos * KS::ROW_BYTES, lq);
                 } else {
@@ -316,7 +326,10 @@ struct SrcCand {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const double v = quad_sum(s[u].dot(qd));
-                if (lq == 0 && ent[u] >= 0) put_key(keys, hist, ent[u], score_key((float)v));
+                if (lq == 0 && ent[u] >= 0) {
+                    put_key(keys, hist, ent[u], score_key((float)v));
+                    if (posl) posl[ent[u]] = (uint32_t)pv[u];
+                }
             }
         }
         __syncthreads();
@@ -453,7 +466,9 @@ __global__ void __launch_bounds__(kSelThreads) k_select(Src src, SelDev g, SelTg
     const bool multi = S > 1;
 
     uint32_t* keys = lds;                       // [cpad] score keys, 0 past cnt
-    uint32_t* lh1 = lds + cpad;                 // [kB1] this chunk's top-digit histogram
+    const bool pos_lds = Src::kPosLds && g.pos_lds;
+    uint32_t* posl = pos_lds ? lds + cpad : nullptr;     // [cpad] positions of the keys (sources that keep them)
+    uint32_t* lh1 = lds + cpad * (pos_lds ? 2 : 1);     // [kB1] this chunk's top-digit histogram
     uint32_t* lh2 = lh1 + kB1;                  // [2*kB2] row histogram, then later histograms
     uint32_t* cnts = lh2 + 2 * kB2;             // [S][2 targets][> T, == T]
     uint32_t* sm = cnts + 4 * kMaxS;            // scratch
@@ -475,7 +490,7 @@ __global__ void __launch_bounds__(kSelThreads) k_select(Src src, SelDev g, SelTg
     for (int i = tid; i < kB1; i += kSelThreads) lh1[i] = 0u;
     if (tid < 4) sm[204 + tid] = 0u;          // list slot cursors and tie counters of the two targets
     __syncthreads();
-    src.fill(row, begin, cnt, cpad, keys, lh1);  // keys + lh1; ends with a block barrier
+    src.fill(row, begin, cnt, cpad, keys, lh1, posl);   // keys + lh1 (+ positions); ends with a block barrier
 
     // ---- row histogram of the top 11 bits; each chunk also publishes the
     // suffix sums of its own histogram (keys at or above each bin)
@@ -994,7 +1009,7 @@ __global__ void __launch_bounds__(kSelThreads) k_select(Src src, SelDev g, SelTg
                 const uint64_t m = __ballot(s);
                 const uint32_t slot = run_sel + lanes_below(m);
                 if (s && slot < M[j]) {         // the bound holds whenever the counts agree
-                    out_idx[slot] = src.position(row, begin + (int64_t)pr.y);
+                    out_idx[slot] = pos_lds ? (int32_t)posl[pr.y] : src.position(row, begin + (int64_t)pr.y);
                     if (out_sc) out_sc[slot] = key_score(pr.x);
                 }
                 run_sel += (uint32_t)__popcll(m);
@@ -1051,7 +1066,7 @@ __global__ void __launch_bounds__(kSelThreads) k_select(Src src, SelDev g, SelTg
                     const int u = __builtin_ctz(selm);
                     selm &= selm - 1u;
                     if (slot < M[j]) {          // the bound holds whenever the counts agree
-                        out_idx[slot] = src.position(row, begin + ib + u);
+                        out_idx[slot] = pos_lds ? (int32_t)posl[ib + u] : src.position(row, begin + ib + u);
                         if (out_sc) out_sc[slot] = key_score(u == 0 ? kv[0] : u == 1 ? kv[1] : u == 2 ? kv[2] : kv[3]);
                     }
                     ++slot;
@@ -1142,6 +1157,11 @@ int launch_rows(const SelPlan& p, const Src& src, const SelOutput* out, int nt, 
         if (he != hipSuccess) return hip_fail(he, "hipFuncSetAttribute(select)");
         attr_set[nt - 1] = true;
     }
+    // Sources whose positions are indirect keep them in LDS next to the keys when both fit.
+    DeviceInfo dinfo;
+    if (int e = device_info(&dinfo)) return e;
+    const bool pos_lds = Src::kPosLds && (size_t)(2 * p.chunk_pad + kLdsFixedWords) * 4 <= dinfo.max_lds;
+    const size_t lds_bytes = (size_t)(p.chunk_pad * (pos_lds ? 2 : 1) + kLdsFixedWords) * 4;
     SelTgt t[2];
     for (int j = 0; j < 2; ++j) {
         const SelOutput& o = out[j < nt ? j : 0];
@@ -1152,6 +1172,7 @@ int launch_rows(const SelPlan& p, const Src& src, const SelOutput* out, int nt, 
     g.S = p.S;
     g.chunk = p.chunk;
     g.chunk_pad = p.chunk_pad;
+    g.pos_lds = pos_lds ? 1 : 0;
     g.nt = nt;
     g.row_words = p.row_words;
     g.ctrl = reinterpret_cast<uint32_t*>(ws_ctrl);
@@ -1165,12 +1186,12 @@ int launch_rows(const SelPlan& p, const Src& src, const SelOutput* out, int nt, 
     // the launch starts; a wait that still cannot finish gives up after a
     // bounded number of polls and flags the workspace status word.
     static size_t checked_lds[2] = {0, 0};
-    if (checked_lds[nt - 1] != p.lds_bytes) {
+    if (checked_lds[nt - 1] != lds_bytes) {
         int per_cu = 0;
-        hipError_t he = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kSelThreads, p.lds_bytes);
+        hipError_t he = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kSelThreads, lds_bytes);
         if (he != hipSuccess) return hip_fail(he, "hipOccupancyMaxActiveBlocksPerMultiprocessor(select)");
         if (per_cu < 1) return fail(INVALID, "select: kernel does not fit on a CU with this LDS size");
-        checked_lds[nt - 1] = p.lds_bytes;
+        checked_lds[nt - 1] = lds_bytes;
     }
     Src s = src;
     for (int64_t r0 = 0; r0 < p.rows; r0 += p.rows_per_launch) {
@@ -1178,7 +1199,7 @@ int launch_rows(const SelPlan& p, const Src& src, const SelOutput* out, int nt, 
         g.row0 = (int32_t)r0;
         void* args[] = {&s, &g, &t[0], &t[1]};
         hipError_t he = hipLaunchKernel(fn, dim3((unsigned)(nr * p.S)), dim3(kSelThreads), args,
-                                        (unsigned)p.lds_bytes, stream);
+                                        (unsigned)lds_bytes, stream);
         if (he != hipSuccess) return hip_fail(he, "hipLaunchKernel(select)");
     }
     return OK;
