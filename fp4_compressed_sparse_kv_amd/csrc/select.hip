@@ -89,12 +89,13 @@ struct SrcScores {
     int64_t n;
 
     static constexpr bool kPosLds = false;
-    __device__ __forceinline__ void fill(int64_t row, int64_t begin, int cnt, int cpad, uint32_t* keys,
-                                         uint32_t* hist, uint32_t*) const {
+    __device__ __forceinline__ int fill(int64_t row, int64_t begin, int cnt, int cpad, uint32_t* keys,
+                                        uint32_t* hist, uint32_t*) const {
         const float* p = scores + row * stride + begin;
         for (int i = threadIdx.x; i < cnt; i += kSelThreads) put_key(keys, hist, i, score_key(p[i]));
         pad_keys(keys, cnt, cpad);
         __syncthreads();
+        return cnt;
     }
     __device__ __forceinline__ int32_t position(int64_t row, int64_t i) const {
         return cand ? cand[row * n + i] : (int32_t)i;
@@ -110,8 +111,8 @@ struct SrcScan {
     const int64_t* q_pos;
 
     static constexpr bool kPosLds = false;       // position = index
-    __device__ __forceinline__ void fill(int64_t row, int64_t begin, int cnt, int cpad, uint32_t* keys,
-                                         uint32_t* hist, uint32_t*) const {
+    __device__ __forceinline__ int fill(int64_t row, int64_t begin, int cnt, int cpad, uint32_t* keys,
+                                        uint32_t* hist, uint32_t*) const {
         using KS = KeySlice<KT, D>;
         constexpr int QB = (QT == kBF16) ? 2 : 4;
         constexpr int U = KS::RAW >= 4 ? 1 : 4 / KS::RAW;   // 64 bytes in flight per lane
@@ -175,7 +176,7 @@ struct SrcScan {
             }
             pad_keys(keys, cnt, cpad);
             __syncthreads();
-            return;
+            return cnt;
         }
         for (int base = 0; base < cnt; base += (kSelThreads / 4) * U) {
             KS s[U];
@@ -194,6 +195,7 @@ struct SrcScan {
         }
         pad_keys(keys, cnt, cpad);
         __syncthreads();
+        return cnt;
     }
     __device__ __forceinline__ int32_t position(int64_t, int64_t i) const { return (int32_t)i; }
 };
@@ -207,8 +209,8 @@ struct SrcPool {
     int64_t P;
 
     static constexpr bool kPosLds = true;        // positions come from the pool: kept in LDS when they fit
-    __device__ __forceinline__ void fill(int64_t row, int64_t begin, int cnt, int cpad, uint32_t* keys,
-                                         uint32_t* hist, uint32_t* posl) const {
+    __device__ __forceinline__ int fill(int64_t row, int64_t begin, int cnt, int cpad, uint32_t* keys,
+                                        uint32_t* hist, uint32_t* posl) const {
         using KS = KeySlice<KT, D>;
         constexpr int QB = (QT == kBF16) ? 2 : 4;
         constexpr int U = KS::RAW >= 4 ? 1 : 4 / KS::RAW;
@@ -241,12 +243,16 @@ struct SrcPool {
         }
         pad_keys(keys, cnt, cpad);
         __syncthreads();
+        return cnt;
     }
     __device__ __forceinline__ int32_t position(int64_t row, int64_t i) const { return pool[row * P + i]; }
 };
 
 // Candidate lists of the prefill indexer: entry i of a row is slot i % cap of
 // list i / cap, valid below that list's count; entries are in position order.
+// When positions are kept in LDS the chunk's valid entries are stored densely
+// (key v = the v-th valid entry, still in position order) and the select runs
+// over those only; otherwise key i is entry begin + i.
 template <int KT, int QT, int D>
 struct SrcCand {
     const void* q;
@@ -266,14 +272,14 @@ struct SrcCand {
     // Only the valid slots are visited: the chunk's keys start at 0 (padding)
     // and each valid slot (list r, slot sl) writes its key at entry r*cap + sl.
     static constexpr bool kPosLds = true;        // positions come from the lists: kept in LDS when they fit
-    __device__ __forceinline__ void fill(int64_t row, int64_t begin, int cnt_, int cpad, uint32_t* keys,
-                                         uint32_t* hist, uint32_t* posl) const {
+    __device__ __forceinline__ int fill(int64_t row, int64_t begin, int cnt_, int cpad, uint32_t* keys,
+                                        uint32_t* hist, uint32_t* posl) const {
         using KS = KeySlice<KT, D>;
         constexpr int QB = (QT == kBF16) ? 2 : 4;
         constexpr int U = KS::RAW >= 4 ? 2 : 8 / KS::RAW;
         constexpr int kMaxLists = 16;
         const int quad = threadIdx.x >> 2, lq = threadIdx.x & 3;
-        for (int i = threadIdx.x; i < cpad; i += kSelThreads) keys[i] = 0u;
+        const bool dense = posl != nullptr;
         double qd[D / 4];
         load_query_slice<QT, D>(reinterpret_cast<const uint8_t*>(q) + row * (int64_t)(D * QB), lq, qd);
         const uint8_t* kb = k + (row / rows_per_seq) * N * (int64_t)KS::ROW_BYTES;
@@ -294,6 +300,11 @@ struct SrcCand {
                 }
             }
             total += nv[r];
+        }
+        {
+            const int zfrom = dense ? (int)total : 0;
+            const int zto = dense ? (int)((total + kPadTo - 1) / kPadTo * kPadTo) : cpad;
+            for (int i = zfrom + (int)threadIdx.x; i < zto; i += kSelThreads) keys[i] = 0u;
         }
         __syncthreads();                        // the zero fill is complete before valid keys land
         for (uint32_t base = 0; base < total; base += (kSelThreads / 4) * U) {
@@ -325,14 +336,21 @@ struct SrcCand {
             }
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const double v = quad_sum(s[u].dot(qd));
-                if (lq == 0 && ent[u] >= 0) {
-                    put_key(keys, hist, ent[u], score_key((float)v));
-                    if (posl) posl[ent[u]] = (uint32_t)pv[u];
+                const double sv = quad_sum(s[u].dot(qd));
+                const uint32_t v = base + u * (kSelThreads / 4) + quad;
+                if (lq != 0) continue;
+                if (dense) {
+                    if (v < total) {            // an entry without a valid position is padding (key 0)
+                        put_key(keys, hist, (int)v, ent[u] >= 0 ? score_key((float)sv) : 0u);
+                        posl[v] = (uint32_t)pv[u];
+                    }
+                } else if (ent[u] >= 0) {
+                    put_key(keys, hist, ent[u], score_key((float)sv));
                 }
             }
         }
         __syncthreads();
+        return dense ? (int)total : cnt_;
     }
     __device__ __forceinline__ int32_t position(int64_t row, int64_t i) const { return entry(row, (int)i); }
 };
@@ -461,8 +479,8 @@ __global__ void __launch_bounds__(kSelThreads) k_select(Src src, SelDev g, SelTg
     const int64_t row = g.rowmap ? (int64_t)g.rowmap[g.row0 + lrow] : (int64_t)g.row0 + lrow;
     if (row < 0) return;                        // the same for every workgroup of the launch row
     const int64_t begin = (int64_t)split * g.chunk;
-    const int cnt = (int)min((int64_t)g.chunk, g.n - begin);
-    const int cpad = g.chunk_pad;
+    int cnt = (int)min((int64_t)g.chunk, g.n - begin);
+    int cpad = g.chunk_pad;                     // LDS key area; after the fill: the keys written, rounded up
     const bool multi = S > 1;
 
     uint32_t* keys = lds;                       // [cpad] score keys, 0 past cnt
@@ -490,7 +508,8 @@ __global__ void __launch_bounds__(kSelThreads) k_select(Src src, SelDev g, SelTg
     for (int i = tid; i < kB1; i += kSelThreads) lh1[i] = 0u;
     if (tid < 4) sm[204 + tid] = 0u;          // list slot cursors and tie counters of the two targets
     __syncthreads();
-    src.fill(row, begin, cnt, cpad, keys, lh1, posl);   // keys + lh1 (+ positions); ends with a block barrier
+    cnt = src.fill(row, begin, cnt, cpad, keys, lh1, posl);   // keys + lh1 (+ positions); ends with a block barrier
+    cpad = (cnt + kPadTo - 1) / kPadTo * kPadTo;
 
     // ---- row histogram of the top 11 bits; each chunk also publishes the
     // suffix sums of its own histogram (keys at or above each bin)
