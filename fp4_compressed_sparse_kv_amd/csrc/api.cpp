@@ -526,6 +526,7 @@ namespace {
 // and the attention data; or (exact path) one select region and the attention.
 constexpr int32_t kSampleStride = 64;           // every 64th position is sampled
 constexpr int32_t kRepairRows = 64;             // rows the exact repair pass holds
+constexpr int64_t kRthMaxSamples = 16384;       // sample rows the threshold kernel holds in registers
 
 struct PrefillLayout {
     bool mfma = false;
@@ -665,12 +666,18 @@ int csa2_prefill_full(const csa2_plan* plan, const csa2_cache* cache, const void
         t.nranges = lay.nrd;
         t.dense = dense;
         if (int e = launch_pf_tiles(t, p.k_idx_dtype, true, stream)) return e;
-        ScoresArgs sa;
-        sa.scores = dense;
-        sa.stride = lay.ns;
-        SelOutput so{sidx, ssc, lay.R, lay.R};
-        if (int e = run_select(lay.sel_sample, SRC_SCORES, a, sa, &so, 1, wsb, wsb + lay.off_sel, stream)) return e;
-        if (int e = launch_pf_thresholds(qb, rows, Q, ssc, lay.R, kmax, thr, rep_count, stream)) return e;
+        if (lay.ns <= kRthMaxSamples) {
+            // the R-th largest sample score of each row (exact) straight from the dense scores
+            if (int e = launch_pf_rth(dense, rows, (int32_t)lay.ns, lay.R, ssc, stream)) return e;
+            if (int e = launch_pf_thresholds(qb, rows, Q, ssc, 1, kmax, thr, rep_count, stream)) return e;
+        } else {
+            ScoresArgs sa;
+            sa.scores = dense;
+            sa.stride = lay.ns;
+            SelOutput so{sidx, ssc, lay.R, lay.R};
+            if (int e = run_select(lay.sel_sample, SRC_SCORES, a, sa, &so, 1, wsb, wsb + lay.off_sel, stream)) return e;
+            if (int e = launch_pf_thresholds(qb, rows, Q, ssc, lay.R, kmax, thr, rep_count, stream)) return e;
+        }
         t.key_off = 0;
         t.key_stride = 1;
         t.nkeys = N;

@@ -111,6 +111,8 @@ struct PfTiles {
 size_t pf_kmax_floats(int32_t B);
 int launch_pf_kmax(const uint8_t* k, int k_dtype, int32_t B, int64_t N, float* partial, hipStream_t stream);
 int launch_pf_tiles(const PfTiles& t, int k_dtype, bool dense, hipStream_t stream);
+// R-th largest of each of `rows` rows of n sample scores (n <= 16384) -> tval[rows].
+int launch_pf_rth(const float* dense, int64_t rows, int32_t n, int32_t R, float* tval, hipStream_t stream);
 int launch_pf_thresholds(const uint16_t* q, int64_t rows, int32_t Q, const float* sel, int32_t R,
                          const float* kmax_partial, float* thr, uint32_t* repair_count, hipStream_t stream);
 int launch_pf_verify(int64_t rows, int32_t nranges, int32_t cap, const uint32_t* cnt, const float* sel,

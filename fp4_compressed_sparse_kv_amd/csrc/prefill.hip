@@ -8,8 +8,9 @@
 // cores only decide which positions are candidates:
 //   1. k_pf_kmax: per sequence and channel, the largest |key| (partials).
 //   2. k_pf_tiles, dense mode: approximate scores s~ of every query against a
-//      sample of the keys (every 64th position); the select kernel then gives
-//      each query's R-th largest sample score t.
+//      sample of the keys (every 64th position); k_pf_rth (or, for longer
+//      sample rows, the select kernel) then gives each query's R-th largest
+//      sample score t.
 //   3. k_pf_thresholds: per query, the margin e = 2^-14 * sum_i |q_i| kmax_i
 //      (+ 2^-120), which exceeds four times the error of s~ plus one fp32
 //      rounding (the products bf16 x bf16 are exact in fp32 and the 64 terms
@@ -310,6 +311,80 @@ __global__ void __launch_bounds__(kPfThreads, 2) k_pf_tiles(PfTileArgs a) {
     }
 }
 
+// ------------------------------------------------------- sample threshold
+
+// The R-th largest of each row's n sample scores, exactly (-inf when fewer
+// than R are finite): the row's order-preserving keys stay in registers (256
+// threads, up to kRthPer keys each) and three radix passes over 11, 11 and 10
+// key bits narrow the bin that holds the R-th key, counting from the top.
+constexpr int kRthThreads = 256;
+constexpr int kRthPer = 64;                     // rows of up to 16384 samples
+
+__global__ void __launch_bounds__(kRthThreads)
+k_pf_rth(const float* __restrict__ dense, int32_t n, int32_t R, float* __restrict__ tval) {
+    __shared__ uint32_t hist[2048];
+    __shared__ uint32_t wsum[kRthThreads / kWave];
+    __shared__ uint32_t res[2];
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
+    const float* p = dense + (size_t)blockIdx.x * n;
+    uint32_t kv[kRthPer];
+#pragma unroll
+    for (int j = 0; j < kRthPer; ++j) {
+        const int i = j * kRthThreads + tid;
+        kv[j] = i < n ? score_key(p[i]) : 0u;
+    }
+    uint32_t prefix = 0, need = (uint32_t)R;
+#pragma unroll
+    for (int d = 0; d < 3; ++d) {
+        const int lo = d == 0 ? 21 : (d == 1 ? 10 : 0);
+        const int w = d == 2 ? 10 : 11;
+        const int nb = 1 << w;
+        for (int b = tid; b < nb; b += kRthThreads) hist[b] = 0u;
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < kRthPer; ++j) {
+            const uint32_t k = kv[j];
+            if (k != 0u && (d == 0 || (k >> (lo + w)) == prefix)) atomicAdd(&hist[(k >> lo) & (uint32_t)(nb - 1)], 1u);
+        }
+        __syncthreads();
+        // thread t owns bins top - per + 1 .. top (top = nb - 1 - per * t), scanned from the top
+        const int per = nb / kRthThreads;
+        const int top = nb - 1 - tid * per;
+        uint32_t sum = 0;
+        for (int i = 0; i < per; ++i) sum += hist[top - i];
+        const uint32_t inc = wave_incl_scan(sum);
+        if (lane == kWave - 1) wsum[wave] = inc;
+        __syncthreads();
+        uint32_t before = inc - sum, total = 0;
+#pragma unroll
+        for (int v = 0; v < kRthThreads / kWave; ++v) {
+            total += wsum[v];
+            if (v < wave) before += wsum[v];
+        }
+        if (d == 0 && total < need) {           // the same for every thread
+            if (tid == 0) tval[blockIdx.x] = -INFINITY;
+            return;
+        }
+        if (before < need && need <= before + sum) {
+            uint32_t c = before;
+            for (int i = 0; i < per; ++i) {
+                const uint32_t h = hist[top - i];
+                if (c + h >= need) {
+                    res[0] = (uint32_t)(top - i);
+                    res[1] = need - c;
+                    break;
+                }
+                c += h;
+            }
+        }
+        __syncthreads();
+        prefix = (prefix << w) | res[0];
+        need = res[1];
+        __syncthreads();                        // hist, wsum and res are rewritten by the next pass
+    }
+    if (tid == 0) tval[blockIdx.x] = key_score(prefix);
+}
+
 // ------------------------------------------------------------ thresholds
 
 // One thread per query row: t = R-th largest sample score (the minimum of the
@@ -436,6 +511,14 @@ int launch_pf_tiles(const PfTiles& t, int k_dtype, bool dense, hipStream_t strea
     }
     const hipError_t e = hipGetLastError();
     return e == hipSuccess ? OK : hip_fail(e, "launch k_pf_tiles");
+}
+
+int launch_pf_rth(const float* dense, int64_t rows, int32_t n, int32_t R, float* tval, hipStream_t stream) {
+    if (rows == 0) return OK;
+    if (n > kRthThreads * kRthPer || R < 1) return fail(INVALID, "prefill: sample row too long for the threshold kernel");
+    hipLaunchKernelGGL(k_pf_rth, dim3((unsigned)rows), dim3(kRthThreads), 0, stream, dense, n, R, tval);
+    const hipError_t e = hipGetLastError();
+    return e == hipSuccess ? OK : hip_fail(e, "launch k_pf_rth");
 }
 
 int launch_pf_thresholds(const uint16_t* q, int64_t rows, int32_t Q, const float* sel, int32_t R,
