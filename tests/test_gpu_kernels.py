@@ -174,6 +174,8 @@ def test_index_reindex_scores_with_padding():
 def _scores_with_ties(rng, rows, n, kind):
     if kind == "ties":
         s = rng.integers(-50, 50, (rows, n)).astype(np.float32)
+    elif kind == "few":                                     # thousands of copies of each of 7 values
+        s = rng.integers(-3, 4, (rows, n)).astype(np.float32)
     elif kind == "equal":
         s = np.full((rows, n), 1.25, dtype=np.float32)
     else:
@@ -189,7 +191,9 @@ def _scores_with_ties(rng, rows, n, kind):
 @pytest.mark.parametrize("rows,n,K,kind", [
     (1, 100, 10, "ties"), (3, 5000, 64, "ties"), (2, 70001, 2048, "normal"), (2, 70001, 2048, "ties"),
     (1, 300000, 8192, "normal"), (4, 40000, 40000, "ties"), (2, 1000, 1500, "normal"),
-    (2, 65536, 100, "equal"), (5, 33, 1, "normal")])
+    (2, 65536, 100, "equal"), (5, 33, 1, "normal"),
+    (2, 70001, 50000, "normal"),    # most keys are candidates: waves fall back from extraction
+    (2, 70001, 2048, "few")])       # > 1024 keys equal to the threshold: low-bit histogram fallback
 def test_topk_matches_oracle(rows, n, K, kind):
     rng = np.random.default_rng(rows * 1000 + n + K)
     s = _scores_with_ties(rng, rows, n, kind)
