@@ -306,6 +306,39 @@ struct SrcCand {
             const int zto = dense ? (int)((total + kPadTo - 1) / kPadTo * kPadTo) : cpad;
             for (int i = zfrom + (int)threadIdx.x; i < zto; i += kSelThreads) keys[i] = 0u;
         }
+        if (dense) {
+            // Pass 1: every list's valid positions to LDS (independent, coalesced loads).
+            // Pass 2: quads take U entries each, read their positions from LDS, issue
+            // all U key loads, then score them.
+            uint32_t v0 = 0;
+#pragma unroll
+            for (int r = 0; r < kMaxLists; ++r) {
+                const int32_t* lst = cand + (row * nranges + r) * (int64_t)cap + (int64_t)(begin + lo[r] - (int64_t)r * cap);
+                for (uint32_t sl = threadIdx.x; sl < nv[r]; sl += kSelThreads) posl[v0 + sl] = (uint32_t)lst[sl];
+                v0 += nv[r];
+            }
+            __syncthreads();
+            for (uint32_t base = 0; base < total; base += (kSelThreads / 4) * U) {
+                KS sk[U];
+                int32_t pv[U];
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const uint32_t v = base + u * (kSelThreads / 4) + quad;
+                    pv[u] = v < total ? (int32_t)posl[v] : -1;
+                    if (pv[u] >= 0 && (int64_t)pv[u] < N) sk[u].load(kb + (int64_t)pv[u] * KS::ROW_BYTES, lq);
+                    else for (int j = 0; j < KS::RAW; ++j) sk[u].raw[j] = make_uint4(0, 0, 0, 0);
+                }
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const double sv = quad_sum(sk[u].dot(qd));
+                    const uint32_t v = base + u * (kSelThreads / 4) + quad;
+                    if (lq == 0 && v < total)   // an entry without a valid position is padding (key 0)
+                        put_key(keys, hist, (int)v, (pv[u] >= 0 && (int64_t)pv[u] < N) ? score_key((float)sv) : 0u);
+                }
+            }
+            __syncthreads();
+            return (int)total;
+        }
         __syncthreads();                        // the zero fill is complete before valid keys land
         for (uint32_t base = 0; base < total; base += (kSelThreads / 4) * U) {
             KS s[U];
