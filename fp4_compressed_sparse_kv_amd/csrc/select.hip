@@ -231,13 +231,28 @@ struct SrcPool {
                 if (ok[u]) s[u].load(kb + (int64_t)pv[u] * KS::ROW_BYTES, lq);
                 else for (int j = 0; j < KS::RAW; ++j) s[u].raw[j] = make_uint4(0, 0, 0, 0);
             }
+            if constexpr (U == 4) {
+                // transposed quad reduction: lane lq ends with the sum of slot lq's key
+                double acc[4];
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int i = base + u * (kSelThreads / 4) + quad;
-                const double v = quad_sum(s[u].dot(qd));
-                if (lq == 0 && i < cnt) {
-                    put_key(keys, hist, i, ok[u] ? score_key((float)v) : 0u);
-                    if (posl) posl[i] = (uint32_t)pv[u];
+                for (int u = 0; u < 4; ++u) acc[u] = s[u].dot(qd);
+                const double v = quad_transpose_sum(acc, lq);
+                const int i = base + lq * (kSelThreads / 4) + quad;
+                const bool okl = lq == 0 ? ok[0] : lq == 1 ? ok[1] : lq == 2 ? ok[2] : ok[3];
+                const int32_t pvl = lq == 0 ? pv[0] : lq == 1 ? pv[1] : lq == 2 ? pv[2] : pv[3];
+                if (i < cnt) {
+                    put_key(keys, hist, i, okl ? score_key((float)v) : 0u);
+                    if (posl) posl[i] = (uint32_t)pvl;
+                }
+            } else {
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int i = base + u * (kSelThreads / 4) + quad;
+                    const double v = quad_sum(s[u].dot(qd));
+                    if (lq == 0 && i < cnt) {
+                        put_key(keys, hist, i, ok[u] ? score_key((float)v) : 0u);
+                        if (posl) posl[i] = (uint32_t)pv[u];
+                    }
                 }
             }
         }
@@ -328,12 +343,27 @@ struct SrcCand {
                     if (pv[u] >= 0 && (int64_t)pv[u] < N) sk[u].load(kb + (int64_t)pv[u] * KS::ROW_BYTES, lq);
                     else for (int j = 0; j < KS::RAW; ++j) sk[u].raw[j] = make_uint4(0, 0, 0, 0);
                 }
+                if constexpr (U == 8) {
+                    // two groups of four slots, transposed quad reduction: lane lq writes slot 4h + lq
+                    auto group = [&](const KS& a, const KS& b, const KS& c, const KS& d, int32_t p0, int32_t p1,
+                                     int32_t p2, int32_t p3, int h) {
+                        const double acc[4] = {a.dot(qd), b.dot(qd), c.dot(qd), d.dot(qd)};
+                        const double sv = quad_transpose_sum(acc, lq);
+                        const int32_t p = lq == 0 ? p0 : lq == 1 ? p1 : lq == 2 ? p2 : p3;
+                        const uint32_t v = base + (4 * h + lq) * (kSelThreads / 4) + quad;
+                        if (v < total)          // an entry without a valid position is padding (key 0)
+                            put_key(keys, hist, (int)v, (p >= 0 && (int64_t)p < N) ? score_key((float)sv) : 0u);
+                    };
+                    group(sk[0], sk[1], sk[2], sk[3], pv[0], pv[1], pv[2], pv[3], 0);
+                    group(sk[4], sk[5], sk[6], sk[7], pv[4], pv[5], pv[6], pv[7], 1);
+                } else {
 #pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const double sv = quad_sum(sk[u].dot(qd));
-                    const uint32_t v = base + u * (kSelThreads / 4) + quad;
-                    if (lq == 0 && v < total)   // an entry without a valid position is padding (key 0)
-                        put_key(keys, hist, (int)v, (pv[u] >= 0 && (int64_t)pv[u] < N) ? score_key((float)sv) : 0u);
+                    for (int u = 0; u < U; ++u) {
+                        const double sv = quad_sum(sk[u].dot(qd));
+                        const uint32_t v = base + u * (kSelThreads / 4) + quad;
+                        if (lq == 0 && v < total)
+                            put_key(keys, hist, (int)v, (pv[u] >= 0 && (int64_t)pv[u] < N) ? score_key((float)sv) : 0u);
+                    }
                 }
             }
             __syncthreads();
