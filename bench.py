@@ -285,8 +285,47 @@ def run_prefill(args, cfg, dev):
         "indexer_tflop": round(flop / 1e12, 3),
         "indexer_mfma_frac_of_whole_prefill": round(flop / (ms * 1e-3) / 2.5e15, 4),
         "status_word": status,
+        # conservative: the indexer's FLOP over the whole prefill time (all kernels), dense bf16 peak
+        "roofline": {"bound": "mfma", "kernel": "k_pf_tiles (indexer candidates), whole-prefill time",
+                     "achieved": round(flop / (ms * 1e-3) / 1e12, 1), "peak": 2500.0, "unit": "TFLOP/s",
+                     "frac": round(flop / (ms * 1e-3) / 2.5e15, 4), "traffic": None},
     }
+    if not args.no_cpu:
+        res["cpu_baseline"] = prefill_cpu_baseline(cfg, args.cpu_seconds)
     print(json.dumps(res), flush=True)
+
+
+def prefill_cpu_baseline(cfg, budget_s):
+    """The oracle on sampled prefill queries of sequence 0 (exact causal scores over the whole context,
+    top-K, fp64 attention) until ~budget_s of CPU work."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import synth
+    from oracle import scores as OS
+    from oracle.attention import sparse_attn as o_attn
+    from oracle.topk import topk as o_topk
+
+    N, Q, K = cfg["N"], cfg["prefill_Q"], cfg["K"]
+    scale = float(np.float32(1 / math.sqrt(cfg["d"])))
+    kb, vb = synth.kv_bf16(cfg, 0)                                   # untimed: input generation
+    cache = dict(k_bf16=kb, v_bf16=vb, k_idx=synth.k_idx(cfg, 0), k_idx_dtype=cfg["k_idx_dtype"])
+    qi = synth.prefill_q_idx(cfg, 0, Q)
+    qb = synth.prefill_q_bf16(cfg, 0, Q)
+    done, spent = 0, 0.0
+    with threadpool_limits(limits=1):
+        for i in range(0, Q, 97):                                    # a spread of query positions
+            t0 = time.perf_counter()
+            s = OS.index_scores(qi[i], cfg["q_idx_dtype"], cache["k_idx"], cfg["k_idx_dtype"], q_pos=N - Q + i)
+            idx, _ = o_topk(s, K)
+            o_attn(qb[i], cache, idx, scale)
+            spent += time.perf_counter() - t0
+            done += 1
+            if spent >= budget_s:
+                break
+    return {"value": done / spent, "unit": "queries/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} of {Q} queries of sequence 0 (every 97th position), N={N}, {spent:.1f} s on 1 host "
+                      f"core (BLAS limited to 1 thread); KV rows quantized by the oracle only where attention reads them"}
 
 
 def main():
