@@ -343,8 +343,9 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(json.dumps({"error": "this benchmark runs on one GPU only; the stack shards by sequence "
-                                   "(see DESIGN.md) and no multi-GPU run is provided", "n_gpus": args.gpus}))
+        print(json.dumps({"error": "this benchmark runs on one GPU only: the decode stack shards by sequence "
+                                   "(each GPU runs the same kernels on its own sequences) and no multi-GPU run "
+                                   "is provided", "n_gpus": args.gpus}))
         sys.exit(2)
 
     import numpy as np

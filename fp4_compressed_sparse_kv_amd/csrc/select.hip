@@ -3,12 +3,14 @@
 //
 // Each row (one query's score list) is cut into S chunks; one workgroup of
 // 1024 threads owns one chunk and keeps its order-preserving u32 score keys
-// in LDS for the whole kernel. The keys come from one of three sources:
+// in LDS for the whole kernel. The keys come from one of four sources:
 //   SrcScores - precomputed fp32 scores in HBM (the standalone top-K call);
 //   SrcScan   - indexer keys streamed from HBM and scored in the kernel (a
 //               Full layer: scan and select fused, scores never leave LDS);
 //   SrcPool   - indexer keys gathered at candidate-pool positions and scored
-//               (a Reindex layer).
+//               (a Reindex layer);
+//   SrcCand   - indexer keys gathered at the prefill indexer's candidate
+//               positions and scored exactly.
 // The source also builds the chunk's histogram of the top 11 key bits while
 // it writes the keys. The histograms of a row's chunks are summed in the
 // workspace with device-scope atomics, and each chunk also publishes the
