@@ -666,16 +666,15 @@ __global__ void __launch_bounds__(kSelThreads) k_select(Src src, SelDev g, SelTg
             if (t >= nst) break;
             const int ib = w0 + t * kPadTo + 4 * lane;
             const uint32_t kv[4] = {kreg[t].x, kreg[t].y, kreg[t].z, kreg[t].w};
-            uint32_t cm = 0, below = 0, total = 0;
+            // this lane's candidates (bit u: key 4*lane + u), their count, and the
+            // count in lower lanes by one wave scan: slots follow index order
+            uint32_t cm = 0;
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const bool c = kv[u] >= lowk;
-                const uint64_t m = __ballot(c);
-                cm |= (uint32_t)c << u;
-                below += lanes_below(m);
-                total += (uint32_t)__popcll(m);
-            }
-            uint32_t slot = npair + below;
+            for (int u = 0; u < 4; ++u) cm |= (uint32_t)(kv[u] >= lowk) << u;
+            const uint32_t mine = (uint32_t)__popc(cm);
+            const uint32_t incl = wave_incl_scan(mine);
+            const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)incl, kWave - 1);
+            uint32_t slot = npair + incl - mine;
             while (cm) {
                 const int u = __builtin_ctz(cm);
                 cm &= cm - 1u;
