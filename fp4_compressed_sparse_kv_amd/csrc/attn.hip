@@ -56,8 +56,6 @@ constexpr int kPartFloats = kMaxHeads * kD + 2 * kMaxHeads;   // per (row, slice
 constexpr int kVRowBytes = 80;                  // staged V row: 64 code bytes + pad (conflict-free dword reads)
 constexpr int kMergeStride = kD + 4;
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr uint32_t kRsrcWord3 = 0x00020000u;    // raw buffer resource (byte-addressed, 32-bit data format)
-constexpr int kCoherent = 16;                   // buffer cache policy sc1: device-coherent access
 
 static int attn_splits(int64_t rows, int32_t K, int waves) {
     const int64_t nblk = (K + kBlk - 1) / kBlk;

@@ -131,6 +131,13 @@ __device__ __forceinline__ float ld_rlx_f32(const float* p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Raw buffer resources: word 3 of a byte-addressed resource with a 32-bit data
+// format; a load past the resource's range returns 0 without a memory access.
+// Cache policy sc1 makes a buffer access device-coherent, like the relaxed
+// agent-scope atomics above.
+constexpr uint32_t kRsrcWord3 = 0x00020000u;
+constexpr int kCoherent = 16;
+
 // Wait until every memory operation this wave has issued - including
 // non-returning atomics and stores - has completed.
 __device__ __forceinline__ void wave_drain() { __builtin_amdgcn_s_waitcnt(0); }

@@ -518,8 +518,15 @@ __device__ __forceinline__ void push_hist(const uint32_t* lh, uint32_t* gh, int 
     }
 }
 
-__device__ __forceinline__ void pull_hist(uint32_t* lh, const uint32_t* gh, int nb) {
-    for (int b = threadIdx.x; b < nb; b += kSelThreads) lh[b] = ld_rlx(&gh[b]);
+template <int NB>
+__device__ __forceinline__ void pull_hist(uint32_t* lh, const uint32_t* gh) {
+    static_assert(NB % kSelThreads == 0, "whole bins per thread");
+    constexpr int P = NB / kSelThreads;
+    uint32_t v[P];
+#pragma unroll
+    for (int i = 0; i < P; ++i) v[i] = ld_rlx(&gh[threadIdx.x + i * kSelThreads]);   // all in flight
+#pragma unroll
+    for (int i = 0; i < P; ++i) lh[threadIdx.x + i * kSelThreads] = v[i];
     __syncthreads();
 }
 
@@ -595,7 +602,13 @@ __global__ void __launch_bounds__(kSelThreads) k_select(Src src, SelDev g, SelTg
             st_rlx(&mine[hi - 1], before + a + b);
         }
         row_barrier(ctrl, S, gen, status);
-        for (int b = tid; b < kB1; b += kSelThreads) lh2[b] = ld_rlx(&gh1[b]);
+        {
+            // both loads in flight before either is stored (a loop would wait on each)
+            static_assert(kB1 == 2 * kSelThreads, "two row-histogram bins per thread");
+            const uint32_t h0 = ld_rlx(&gh1[tid]), h1 = ld_rlx(&gh1[tid + kSelThreads]);
+            lh2[tid] = h0;
+            lh2[tid + kSelThreads] = h1;
+        }
         __syncthreads();
         G = lh2;
     }
@@ -645,13 +658,16 @@ __global__ void __launch_bounds__(kSelThreads) k_select(Src src, SelDev g, SelTg
     // stay in flight during the extraction pass
     const int si = tid / NT, sj = tid - si * NT;
     const bool sl = any_list && tid < S * NT && pick<NT>(path[0], path[1], sj) == kPathList;
+    // (bin b1 + 1 exists: the largest score key, that of +inf, is in bin
+    // 0xFF800000 >> 21 = 2044; the values are used as loaded, so nothing
+    // here waits for the loads)
+    static_assert((0xFF800000u >> 21) + 1 < (uint32_t)kB1, "a bin above every score key's");
     uint32_t s_at = 0u, s_ab = 0u;
     if (sl) {
         const uint32_t bj = pick<NT>(b1[0], b1[1], sj);
         const uint32_t* su = gsuf + (size_t)si * kB1;
         s_at = ld_rlx(&su[bj]);
-        s_ab = ld_rlx(&su[bj + 1 < (uint32_t)kB1 ? bj + 1 : bj]);
-        if (bj + 1 >= (uint32_t)kB1) s_ab = 0u;
+        s_ab = ld_rlx(&su[min(bj + 1, (uint32_t)kB1 - 1)]);
     }
     uint2* pairs = reinterpret_cast<uint2*>(keys + w0);
     uint32_t npair = 0;                         // wave-uniform
@@ -780,7 +796,7 @@ __global__ void __launch_bounds__(kSelThreads) k_select(Src src, SelDev g, SelTg
             row_barrier(ctrl, S, gen, status);
 #pragma unroll
             for (int j = 0; j < NT; ++j)
-                if (path[j] == kPathRadix) pull_hist(lh2 + j * kB2, gh2 + j * kB2, kB2);
+                if (path[j] == kPathRadix) pull_hist<kB2>(lh2 + j * kB2, gh2 + j * kB2);
         }
         uint32_t pre2[2] = {0, 0};
 #pragma unroll
@@ -806,7 +822,7 @@ __global__ void __launch_bounds__(kSelThreads) k_select(Src src, SelDev g, SelTg
             row_barrier(ctrl, S, gen, status);
 #pragma unroll
             for (int j = 0; j < NT; ++j)
-                if (path[j] == kPathRadix) pull_hist(lh2 + j * kB3, gh3 + j * kB3, kB3);
+                if (path[j] == kPathRadix) pull_hist<kB3>(lh2 + j * kB3, gh3 + j * kB3);
         }
 #pragma unroll
         for (int j = 0; j < NT; ++j) {
@@ -826,15 +842,19 @@ __global__ void __launch_bounds__(kSelThreads) k_select(Src src, SelDev g, SelTg
         constexpr int R = kCandCap / kSelThreads;
         uint32_t ent[2][R];
         int rn[2] = {0, 0};                     // list slots per thread in use (uniform)
+        // coherent buffer loads: entries past C read 0 (a padding key) without
+        // a branch, so all of a thread's loads are in flight together
 #pragma unroll
         for (int j = 0; j < NT; ++j) {
             if (path[j] == kPathList) rn[j] = ((int)C[j] + kSelThreads - 1) / kSelThreads;
+            const __amdgpu_buffer_rsrc_t lr = __builtin_amdgcn_make_buffer_rsrc(
+                glist + (size_t)j * kCandCap, (short)0, (int)(path[j] == kPathList ? C[j] * 4u : 0u), kRsrcWord3);
+            // (ent[j][r] is read only for r < rn[j]; left unset otherwise, so
+            // the loads need no merge with a default and stay in flight)
 #pragma unroll
-            for (int r = 0; r < R; ++r) {
-                const int e = tid + r * kSelThreads;
-                ent[j][r] = 0u;
-                if (r < rn[j] && e < (int)C[j]) ent[j][r] = ld_rlx(&glist[(size_t)j * kCandCap + e]);
-            }
+            for (int r = 0; r < R; ++r)
+                if (r < rn[j])                  // uniform
+                    ent[j][r] = __builtin_amdgcn_raw_buffer_load_b32(lr, (tid + r * kSelThreads) * 4, 0, kCoherent);
         }
         // both targets' digit histograms side by side: bits 10..20, then bits 0..9
         uint32_t nd[2] = {0u, 0u};
@@ -997,8 +1017,9 @@ __global__ void __launch_bounds__(kSelThreads) k_select(Src src, SelDev g, SelTg
             for (int i = tid; i < S * 2; i += kSelThreads) {
                 const int j = i & 1;
                 if (j < NT && pick<NT>(path[0], path[1], j) != kPathList) {
-                    cnts[i * 2 + 0] = ld_rlx(&gcnt[i * 2 + 0]);
-                    cnts[i * 2 + 1] = ld_rlx(&gcnt[i * 2 + 1]);
+                    const uint32_t gt = ld_rlx(&gcnt[i * 2 + 0]), eq = ld_rlx(&gcnt[i * 2 + 1]);
+                    cnts[i * 2 + 0] = gt;
+                    cnts[i * 2 + 1] = eq;
                 }
             }
         }

@@ -178,6 +178,9 @@ def _scores_with_ties(rng, rows, n, kind):
         s = rng.integers(-3, 4, (rows, n)).astype(np.float32)
     elif kind == "equal":
         s = np.full((rows, n), 1.25, dtype=np.float32)
+    elif kind == "inf":                                     # the top-K is a subset of many +inf
+        s = rng.standard_normal((rows, n)).astype(np.float32)
+        s[rng.random((rows, n)) < 0.3] = np.inf
     else:
         s = rng.standard_normal((rows, n)).astype(np.float32)
     m = rng.random((rows, n))
@@ -193,7 +196,10 @@ def _scores_with_ties(rng, rows, n, kind):
     (1, 300000, 8192, "normal"), (4, 40000, 40000, "ties"), (2, 1000, 1500, "normal"),
     (2, 65536, 100, "equal"), (5, 33, 1, "normal"),
     (2, 70001, 50000, "normal"),    # most keys are candidates: waves fall back from extraction
-    (2, 70001, 2048, "few")])       # > 1024 keys equal to the threshold: low-bit histogram fallback
+    (2, 70001, 2048, "few"),        # > 1024 keys equal to the threshold: low-bit histogram fallback
+    # rows of 2..16 chunks, which exchange suffix sums only
+    (32, 70001, 2048, "normal"), (32, 70001, 50000, "normal"), (32, 70001, 2048, "few"),
+    (32, 70001, 2048, "inf"), (16, 262144, 100, "equal"), (20, 100000, 3000, "ties")])
 def test_topk_matches_oracle(rows, n, K, kind):
     rng = np.random.default_rng(rows * 1000 + n + K)
     s = _scores_with_ties(rng, rows, n, kind)
