@@ -21,7 +21,7 @@ OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libcsa2.so")
 ARCH = os.environ.get("CSA2_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["api.cpp", "quant.hip", "index.hip", "select.hip", "attn.hip", "prefill.hip"]
+SOURCES = ["api.cpp", "quant.hip", "index.hip", "select.hip", "poolsel.hip", "attn.hip", "prefill.hip"]
 
 COMMON = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

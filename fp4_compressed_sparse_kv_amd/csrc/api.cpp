@@ -394,6 +394,8 @@ namespace {
 // Full select, the Reindex select, the pool, the attention and the positions.
 struct PlanLayout {
     SelPlan full, pool;
+    PoolSelPlan psel;               // Reindex select when the pool has at most kPoolSelMaxN entries
+    bool use_psel = false;
     size_t off_full = 0, off_pool = 0, off_attn = 0, off_idx = 0, off_poolbuf = 0, total = 0;
 };
 
@@ -403,9 +405,17 @@ int plan_layout(const csa2_plan* plan, int32_t B, int64_t N, PlanLayout* lay) {
     lay->off_full = off;
     off += align_up(lay->full.data_bytes);
     if (plan->has_reindex) {
-        if (int e = plan_select(B, plan->p.P, 512, &lay->pool)) return e;
+        lay->use_psel = plan->p.P <= kPoolSelMaxN;
+        size_t pool_data = 0;
+        if (lay->use_psel) {
+            if (int e = plan_pool_select(B, plan->p.P, &lay->psel)) return e;
+            pool_data = lay->psel.data_bytes;
+        } else {
+            if (int e = plan_select(B, plan->p.P, 512, &lay->pool)) return e;
+            pool_data = lay->pool.data_bytes;
+        }
         lay->off_pool = off;
-        off += align_up(lay->pool.data_bytes);
+        off += align_up(pool_data);
         lay->off_poolbuf = off;
         off += align_up((size_t)B * plan->p.P * 4);
     }
@@ -482,6 +492,19 @@ int csa2_plan_run_decode(const csa2_plan* plan, const csa2_cache* cache, const c
                     o[0] = SelOutput{idx_dst, nullptr, p.K, p.K};
                 }
                 e = run_select(lay.full, SRC_SCAN, a, none, o, nt, wsb, wsb + lay.off_full, stream);
+            } else if (lay.use_psel) {
+                PoolSelArgs ps;
+                ps.q = io[l].q_idx;
+                ps.k = a.k;
+                ps.N = N;
+                ps.pool = pool;
+                ps.q_dtype = p.q_idx_dtype;
+                ps.k_dtype = p.k_idx_dtype;
+                ps.d_idx = p.d_idx;
+                ps.K = p.K;
+                ps.idx = idx_dst;
+                ps.idx_stride = p.K;
+                e = run_pool_select(lay.psel, ps, wsb, wsb + lay.off_pool, lay.psel.data_bytes, stream);
             } else {
                 a.pool = pool;
                 o[0] = SelOutput{idx_dst, nullptr, p.K, p.K};

@@ -93,6 +93,28 @@ struct ScoresArgs {                 // precomputed scores
 int run_select(const SelPlan& p, int source, const ScanArgs& scan, const ScoresArgs& sc,
                const SelOutput* out, int nt, void* ws_ctrl, void* ws_data, hipStream_t stream);
 
+// Reindex selection (pool of at most 16,384 entries per row): score the pool
+// and select top-K with one all-keys exchange per row (poolsel.hip).
+struct PoolSelPlan {
+    int64_t rows = 0;
+    int32_t n = 0, n4 = 0, S = 1, rows_per_launch = 0;
+    size_t data_bytes = 0;          // published keys, rows_per_launch rows of n4 words
+};
+struct PoolSelArgs {
+    const void* q = nullptr;        // [rows][d_idx] indexer queries (q_dtype)
+    const uint8_t* k = nullptr;     // [rows][N][d_idx] keys (k_dtype); row r reads sequence r
+    int64_t N = 0;
+    const int32_t* pool = nullptr;  // [rows][n] ascending positions
+    int32_t q_dtype = 0, k_dtype = 0, d_idx = 64, K = 0;
+    int32_t* idx = nullptr;         // [rows][idx_stride] ascending positions, -1 padding
+    int64_t idx_stride = 0;
+    float* score = nullptr;         // optional selected scores
+};
+constexpr int64_t kPoolSelMaxN = 16384;
+int plan_pool_select(int64_t rows, int64_t n, PoolSelPlan* out);
+int run_pool_select(const PoolSelPlan& p, const PoolSelArgs& a, void* ws_ctrl, void* ws_data, size_t data_bytes,
+                    hipStream_t stream);
+
 // --------------------------------------------------------- prefill indexer
 struct PfTiles {
     const uint16_t* q = nullptr;    // [B*Q][64] bf16 indexer queries

@@ -116,6 +116,32 @@ def test_stack_full_reindex_reuse(B, N, K, P):
         assert set(host(layers[0]["idx_out"][b]).tolist()) - {-1} <= ps
 
 
+@pytest.mark.parametrize("N,P,K,zero_q", [(20000, 3001, 1500, False), (20000, 3001, 1500, True),
+                                           (9000, 1025, 1025, True), (40000, 16384, 2048, False),
+                                           (40000, 16384, 2048, True), (5000, 1030, 7, False)])
+def test_reindex_pool_shapes_and_ties(N, P, K, zero_q):
+    """Reindex over pools with a ragged tail (P not a multiple of 4 or of 1024), the largest pool
+    the single-exchange select takes, K = P, and an all-zero Reindex query, whose scores all tie:
+    then the positions are the K lowest pool positions."""
+    cfg = synth.small("stack_b32_n262144", B=2, N=N, K=K, P=P, modes=("full", "reindex", "reuse"))
+    cache, layers, ocache, olayers = build_case(cfg)
+    if zero_q:
+        layers[1]["q_idx"].zero_()
+        for b in range(2):
+            olayers[1][b]["q_idx"] = np.zeros_like(olayers[1][b]["q_idx"])
+    plan = make_plan(cfg)
+    plan.run_decode(cache, layers)
+    torch.cuda.synchronize()
+    stats = check_against_oracle(cfg, layers, ocache, olayers, range(2))
+    assert stats["excused"] == 0, stats
+    if zero_q:
+        pool = layers[0]["pool_out"]
+        assert torch.equal(layers[1]["idx_out"], pool[:, :K])
+    idx1 = layers[1]["idx_out"]
+    direct = C.sparse_attn_fp4(layers[2]["q"][:, None], cache, idx1[:, None], softmax_scale=SCALE)
+    assert torch.equal(direct[:, 0], layers[2]["out"])
+
+
 def test_reindex_over_whole_context_equals_full():
     cfg = synth.small("stack_b32_n262144", B=2, N=3000, K=50, P=3000, modes=("full", "reindex"))
     cache, layers, _, _ = build_case(cfg, with_oracle=False)
