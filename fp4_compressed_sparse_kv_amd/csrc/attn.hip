@@ -96,6 +96,24 @@ __device__ __forceinline__ f16x8 dq8(uint32_t w, _Float16 s) {
 
 __device__ __forceinline__ _Float16 scale_f16(uint32_t b) { return (_Float16)e4m3_to_f32(b); }
 
+// Over the four rows of 16 lanes (lanes n, 16 + n, 32 + n, 48 + n): the
+// maximum and the sum, in every lane of the group. v_permlane16_swap and
+// v_permlane32_swap hand each lane the value of lane ^ 16 and lane ^ 32 as one
+// of the pair they return (the other is its own), so op(pair) is the combine
+// with that lane; both lanes of a pair compute the same value.
+__device__ __forceinline__ float rows_max(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float rows_sum(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 struct KvBase {
     const uint8_t *kc, *ks, *vc, *vs;           // this sequence's planes
     int64_t cs, ss;
@@ -129,30 +147,41 @@ union AttnLds {
     MergeArea<W> mg;
 };
 
-// Raw position-list entry of lane `lane` of block `blk` (lanes >= 32 and
-// entries past K read a clamped in-range entry and are discarded later). The
-// load is unconditional and its value is checked only where it is consumed,
-// so it can stay in flight.
-__device__ __forceinline__ int32_t load_pos(const int32_t* ip, int blk, int K, int lane) {
-    return ip[min(blk * kBlk + (lane & (kBlk - 1)), K - 1)];
+// Raw position-list entries a lane of block `blk` needs: entries n and 16 + n
+// (its code rows) and entry lane % 32 (the scale record it loads). Each lane
+// loads them itself - lanes with the same entry read the same word - so no
+// cross-lane move waits on the list. Entries past K read a clamped in-range
+// entry and are discarded later. The loads are unconditional and their values
+// are checked only where they are consumed, so they can stay in flight.
+struct BlockPos {
+    int32_t a, b, s;
+};
+__device__ __forceinline__ BlockPos load_pos(const int32_t* ip, int blk, int K, int lane) {
+    const int n = lane & 15;
+    BlockPos p;
+    p.a = ip[min(blk * kBlk + n, K - 1)];
+    p.b = ip[min(blk * kBlk + 16 + n, K - 1)];
+    p.s = ip[min(blk * kBlk + (lane & (kBlk - 1)), K - 1)];
+    return p;
 }
 
 // Issue the gathers of one block. Every load is unconditional: an entry that
 // is padding (past K, negative or >= N) reads position 0 of the sequence
 // instead, and its scales are zeroed when the block is staged, so it
 // dequantizes to exact zeros and is masked out of the softmax.
-__device__ __forceinline__ void gather(BlockRaw& r, int32_t raw_pos, int blk, int K, const KvBase& kv, int64_t N,
+__device__ __forceinline__ void gather(BlockRaw& r, const BlockPos& bp, int blk, int K, const KvBase& kv, int64_t N,
                                        int lane, int n, int g) {
-    const bool ok = lane < kBlk && blk * kBlk + lane < K && raw_pos >= 0 && (int64_t)raw_pos < N;
-    const int32_t safe = ok ? raw_pos : 0;
-    const int32_t p0 = __shfl(safe, n), p1 = __shfl(safe, 16 + n);
+    const bool ok = lane < kBlk && blk * kBlk + lane < K && bp.s >= 0 && (int64_t)bp.s < N;
+    const int32_t safe = ok ? bp.s : 0;
+    const int32_t p0 = (blk * kBlk + n < K && bp.a >= 0 && (int64_t)bp.a < N) ? bp.a : 0;
+    const int32_t p1 = (blk * kBlk + 16 + n < K && bp.b >= 0 && (int64_t)bp.b < N) ? bp.b : 0;
     r.k[0] = *reinterpret_cast<const uint4*>(kv.kc + p0 * kv.cs + 16 * g);
     r.v[0] = *reinterpret_cast<const uint4*>(kv.vc + p0 * kv.cs + 16 * g);
     r.k[1] = *reinterpret_cast<const uint4*>(kv.kc + p1 * kv.cs + 16 * g);
     r.v[1] = *reinterpret_cast<const uint4*>(kv.vc + p1 * kv.cs + 16 * g);
     r.ks = *reinterpret_cast<const uint2*>(kv.ks + safe * kv.ss);
     r.vs = *reinterpret_cast<const uint2*>(kv.vs + safe * kv.ss);
-    r.pos = ok ? raw_pos : -1;
+    r.pos = ok ? bp.s : -1;
 }
 
 struct WaveState {
@@ -213,8 +242,7 @@ __device__ __forceinline__ void attend_block(WaveState& st, const BlockRaw& r, S
         lg[i] = bit ? sv * sl2 : -INFINITY;
     }
     float mx = fmaxf(fmaxf(fmaxf(lg[0], lg[1]), fmaxf(lg[2], lg[3])), fmaxf(fmaxf(lg[4], lg[5]), fmaxf(lg[6], lg[7])));
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = rows_max(mx);
     const float m_old = st.m;
     const float m_new = fmaxf(m_old, mx);
     // weights 2^(lg - m_new): the hardware exp2 flushes results below 2^-126
@@ -236,8 +264,7 @@ __device__ __forceinline__ void attend_block(WaveState& st, const BlockRaw& r, S
         pb_lo[i] = lo.x;
         pb_lo[i + 1] = lo.y;
     }
-    psum += __shfl_xor(psum, 16);
-    psum += __shfl_xor(psum, 32);
+    psum = rows_sum(psum);
     const float alpha = m_old == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_old - mref);
     st.l = st.l * alpha + psum;
     st.m = m_new;
@@ -306,11 +333,14 @@ k_sparse_attn(const uint16_t* __restrict__ q, int32_t rows_per_seq, int32_t H, c
 
     // query as the B operand of S^T = K_hat Q^T: lane (n, g), k-step s holds
     // q[head n][channel 32g + 8s + i], i = 0..7; heads >= H read head H - 1
-    // and are zeroed when converted
+    // and are zeroed when converted. Loaded after the first block's position
+    // list, so the first gathers do not wait for it.
     uint4 qraw[4];
+    auto load_q = [&]() {
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
-        qraw[s] = *reinterpret_cast<const uint4*>(q + (row * H + min(n, H - 1)) * (int64_t)kD + 32 * g + 8 * s);
+        for (int s = 0; s < 4; ++s)
+            qraw[s] = *reinterpret_cast<const uint4*>(q + (row * H + min(n, H - 1)) * (int64_t)kD + 32 * g + 8 * s);
+    };
     f16x8 qb[4];
     auto convert_q = [&]() {
 #pragma unroll
@@ -345,8 +375,9 @@ k_sparse_attn(const uint16_t* __restrict__ q, int32_t rows_per_seq, int32_t H, c
     const int nb = first < b1 ? (b1 - first + kAttnWaves - 1) / kAttnWaves : 0;
     if (nb > 0) {
         BlockRaw r0, r1;
-        int32_t p0 = load_pos(ip, first, K, lane);
-        int32_t p1 = load_pos(ip, first + min(1, nb - 1) * kAttnWaves, K, lane);
+        BlockPos p0 = load_pos(ip, first, K, lane);
+        load_q();
+        BlockPos p1 = load_pos(ip, first + min(1, nb - 1) * kAttnWaves, K, lane);
         gather(r0, p0, first, K, kv, N, lane, n, g);
         convert_q();
         int k = 0;
@@ -405,7 +436,7 @@ k_sparse_attn(const uint16_t* __restrict__ q, int32_t rows_per_seq, int32_t H, c
 #pragma unroll
         for (int w = 0; w < kAttnWaves; ++w) {
             const float mw = lds.mg.m[w][h];
-            const float wt = (mw == -INFINITY) ? 0.f : exp2f(mw - M);
+            const float wt = (mw == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw - M);
             L += wt * lds.mg.l[w][h];
 #pragma unroll
             for (int v = 0; v < kV4; ++v) o[v] += wt * *reinterpret_cast<const f32x4*>(&lds.mg.acc[w][h][c0 + 4 * v]);
@@ -464,7 +495,7 @@ k_sparse_attn(const uint16_t* __restrict__ q, int32_t rows_per_seq, int32_t H, c
 #pragma unroll
         for (int s = 0; s < kMaxSplits; ++s) {
             const float ms = __uint_as_float(pml[s].x);
-            const float wt = (s >= NS || ms == -INFINITY) ? 0.f : exp2f(ms - MM);
+            const float wt = (s >= NS || ms == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ms - MM);
             LL += wt * __uint_as_float(pml[s].y);
 #pragma unroll
             for (int v = 0; v < kV4; ++v) oo[v] += wt * __builtin_bit_cast(f32x4, pa[s][v]);
