@@ -12,8 +12,9 @@
 //   2. waits at the row barrier, then loads the whole row's keys (16-byte
 //      coherent loads; thread t holds entries t*NK .. t*NK + NK - 1);
 //   3. finds the exact threshold key T (the K-th largest key, or the smallest
-//      valid one when the row has fewer than K) by three radix passes of 11,
-//      11 and 10 bits over LDS histograms; every workgroup of the row computes
+//      valid one when the row has fewer than K) by radix passes of 11, 11 and
+//      10 bits over LDS histograms - the third only when the bin found by the
+//      second holds more than one key; every workgroup of the row computes
 //      the same T from the same keys;
 //   4. writes the positions of its own chunk's selected entries straight to
 //      their output slots: an entry is selected if its key is above T, or
@@ -65,11 +66,11 @@ __device__ __forceinline__ uint32_t ps_block_scan(uint32_t v, uint32_t* wsum, ui
 }
 
 // Bins h[NB-1] (highest) down to h[0]: the bin holding the M-th largest key,
-// M = min(M_req, total). Every thread gets (bin, keys in higher bins, M); M == 0
-// when the histogram is empty.
+// M = min(M_req, total). Every thread gets (bin, keys in higher bins, keys in
+// the bin, M); M == 0 when the histogram is empty.
 template <int NB>
 __device__ __forceinline__ void ps_find(const uint32_t* h, uint32_t M_req, PsLds& L, uint32_t& bin, uint32_t& above,
-                                        uint32_t& M) {
+                                        uint32_t& in_bin, uint32_t& M) {
     static_assert(NB == 2 * kPsThreads || NB == kPsThreads, "bins per thread");
     const int tid = threadIdx.x;
     const int hi = NB - 1 - (NB == 2 * kPsThreads ? 2 * tid : tid);
@@ -82,10 +83,12 @@ __device__ __forceinline__ void ps_find(const uint32_t* h, uint32_t M_req, PsLds
         const bool in_hi = before + a >= m;
         L.sh[0] = in_hi ? (uint32_t)hi : (uint32_t)(hi - 1);
         L.sh[1] = in_hi ? before : before + a;
+        L.sh[2] = in_hi ? a : b;
     }
     __syncthreads();
     bin = L.sh[0];
     above = L.sh[1];
+    in_bin = L.sh[2];
     M = m;
 }
 
@@ -184,8 +187,8 @@ __global__ void __launch_bounds__(kPsThreads) k_pool_select(const void* __restri
     for (int j = 0; j < NK; ++j)
         if (kv[j]) atomicAdd(&L.hist[kv[j] >> 21], 1u);
     __syncthreads();
-    uint32_t b1, a1, M;
-    ps_find<2048>(L.hist, (uint32_t)g.K, L, b1, a1, M);
+    uint32_t b1, a1, c1, M;
+    ps_find<2048>(L.hist, (uint32_t)g.K, L, b1, a1, c1, M);
     uint32_t T = 0u, gt = 0u, need = 0u;
     if (M > 0) {
         for (int i = tid; i < 2048; i += kPsThreads) L.hist[i] = 0u;
@@ -194,19 +197,29 @@ __global__ void __launch_bounds__(kPsThreads) k_pool_select(const void* __restri
         for (int j = 0; j < NK; ++j)
             if (kv[j] && (kv[j] >> 21) == b1) atomicAdd(&L.hist[(kv[j] >> 10) & 2047u], 1u);
         __syncthreads();
-        uint32_t b2, a2, m2;
-        ps_find<2048>(L.hist, M - a1, L, b2, a2, m2);
-        for (int i = tid; i < 1024; i += kPsThreads) L.hist[i] = 0u;
-        __syncthreads();
+        uint32_t b2, a2, c2, m2;
+        ps_find<2048>(L.hist, M - a1, L, b2, a2, c2, m2);
         const uint32_t p21 = (b1 << 11) | b2;
+        if (c2 == 1u) {
+            // a single key with these 22 leading bits: it is T, and it is taken
 #pragma unroll
-        for (int j = 0; j < NK; ++j)
-            if (kv[j] && (kv[j] >> 10) == p21) atomicAdd(&L.hist[kv[j] & 1023u], 1u);
-        __syncthreads();
-        uint32_t b3, a3, m3;
-        ps_find<1024>(L.hist, M - a1 - a2, L, b3, a3, m3);
-        T = (p21 << 10) | b3;
-        gt = a1 + a2 + a3;
+            for (int j = 0; j < NK; ++j)
+                if (kv[j] && (kv[j] >> 10) == p21) L.sh[3] = kv[j];
+            __syncthreads();
+            T = L.sh[3];
+            gt = a1 + a2;
+        } else {
+            for (int i = tid; i < 1024; i += kPsThreads) L.hist[i] = 0u;
+            __syncthreads();
+#pragma unroll
+            for (int j = 0; j < NK; ++j)
+                if (kv[j] && (kv[j] >> 10) == p21) atomicAdd(&L.hist[kv[j] & 1023u], 1u);
+            __syncthreads();
+            uint32_t b3, a3, c3, m3;
+            ps_find<1024>(L.hist, M - a1 - a2, L, b3, a3, c3, m3);
+            T = (p21 << 10) | b3;
+            gt = a1 + a2 + a3;
+        }
         need = M - gt;                          // >= 1 keys equal to T are taken
     }
 

@@ -131,40 +131,42 @@ k_quant(const uint16_t* __restrict__ x, int64_t rows, int32_t gpr, int32_t gshif
 // Dequantization: the hardware FP4 convert gives the E2M1 values (signed, at
 // unit scale), times the E4M3 scale in fp32. E2M1 x E4M3 has at most 6
 // significant bits and lies in [2^-10, 2688], so the product is exact and its
-// top half is the bf16.
+// top half is the bf16. One lane owns half a group (8 channels: 4 code bytes
+// in, 16 bytes of bf16 out), so a wave's stores cover 1 KiB contiguously;
+// four half-groups per pass have their loads issued together.
+constexpr int kDqInFlight = 4;
+
 __global__ void __launch_bounds__(kQuantThreads)
 k_dequant(const uint8_t* __restrict__ codes, int64_t cs, const uint8_t* __restrict__ scales, int64_t ss,
           int64_t rows, int32_t gpr, int32_t gshift, uint16_t* __restrict__ y, int64_t y_stride) {
-    const int64_t total = rows * gpr;
+    const int64_t total = rows * gpr * 2;       // half-groups
     const int64_t stride = (int64_t)gridDim.x * kQuantThreads;
-    for (int64_t gid = (int64_t)blockIdx.x * kQuantThreads + threadIdx.x; gid < total; gid += 2 * stride) {
-        int64_t r[2];
-        int32_t g[2];
-        bool ok[2];
-        uint2 c[2];
-        uint32_t sb[2];
+    for (int64_t hid = (int64_t)blockIdx.x * kQuantThreads + threadIdx.x; hid < total; hid += kDqInFlight * stride) {
+        int64_t r[kDqInFlight];
+        int32_t g[kDqInFlight], half[kDqInFlight];
+        bool ok[kDqInFlight];
+        uint32_t c[kDqInFlight], sb[kDqInFlight];
 #pragma unroll
-        for (int k = 0; k < 2; ++k) {
-            const int64_t id = gid + k * stride;
+        for (int k = 0; k < kDqInFlight; ++k) {
+            const int64_t id = hid + k * stride;
             ok[k] = id < total;
-            row_group(ok[k] ? id : gid, gpr, gshift, r[k], g[k]);
-            c[k] = *reinterpret_cast<const uint2*>(codes + r[k] * cs + (int64_t)g[k] * 8);
+            const int64_t h = ok[k] ? id : hid;
+            half[k] = (int32_t)(h & 1);
+            row_group(h >> 1, gpr, gshift, r[k], g[k]);
+            c[k] = *reinterpret_cast<const uint32_t*>(codes + r[k] * cs + (int64_t)g[k] * 8 + half[k] * 4);
             sb[k] = scales[r[k] * ss + g[k]];
         }
 #pragma unroll
-        for (int k = 0; k < 2; ++k) {
+        for (int k = 0; k < kDqInFlight; ++k) {
             const float S = e4m3_to_f32(sb[k]);
-            const f32x2 v[8] = {fp4_pair<0>(c[k].x), fp4_pair<1>(c[k].x), fp4_pair<2>(c[k].x), fp4_pair<3>(c[k].x),
-                                fp4_pair<0>(c[k].y), fp4_pair<1>(c[k].y), fp4_pair<2>(c[k].y), fp4_pair<3>(c[k].y)};
-            uint32_t o[8];
+            const f32x2 v[4] = {fp4_pair<0>(c[k]), fp4_pair<1>(c[k]), fp4_pair<2>(c[k]), fp4_pair<3>(c[k])};
+            uint32_t o[4];
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
+            for (int j = 0; j < 4; ++j)
                 o[j] = (__float_as_uint(v[j].x * S) >> 16) | (__float_as_uint(v[j].y * S) & 0xFFFF0000u);
-            if (ok[k]) {
-                uint4* dst = reinterpret_cast<uint4*>(y + r[k] * y_stride + (int64_t)g[k] * 16);
-                dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
-                dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
-            }
+            if (ok[k])
+                *reinterpret_cast<uint4*>(y + r[k] * y_stride + (int64_t)g[k] * 16 + half[k] * 8) =
+                    make_uint4(o[0], o[1], o[2], o[3]);
         }
     }
 }
@@ -198,7 +200,7 @@ int launch_dequant(const uint8_t* codes, int64_t cs, const uint8_t* scales, int6
                    uint16_t* y, int64_t y_stride, hipStream_t stream) {
     if (rows == 0) return OK;
     const int32_t gpr = C / 16;
-    hipLaunchKernelGGL(k_dequant, dim3(grid_for(rows * gpr, kQuantThreads)), dim3(kQuantThreads), 0, stream, codes,
+    hipLaunchKernelGGL(k_dequant, dim3(grid_for(rows * gpr * 2, kQuantThreads)), dim3(kQuantThreads), 0, stream, codes,
                        cs, scales, ss, rows, gpr, pow2_shift(gpr), y, y_stride);
     const hipError_t e = hipGetLastError();
     return e == hipSuccess ? OK : hip_fail(e, "launch k_dequant");
