@@ -331,8 +331,9 @@ def prefill_cpu_baseline(cfg, budget_s):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=300)
+    ap.add_argument("--warmup", type=int, default=300,
+                    help="untimed steps first: a few hundred bring the GPU from idle clocks to steady state")
     ap.add_argument("--workload", default="stack_b32_n262144")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -389,9 +390,10 @@ def main():
     ms = e0.elapsed_time(e1) / args.steps
     log(f"step {ms * 1e3:.1f} us")
 
-    # per-kernel durations over a second pass of K steps (events around each kernel, same stream)
-    plan.profile_begin(args.steps)
-    for _ in range(args.steps):
+    # per-kernel durations over a second pass of up to 100 steps (events around each kernel, same stream)
+    prof_steps = min(args.steps, 100)
+    plan.profile_begin(prof_steps)
+    for _ in range(prof_steps):
         plan.run_decode(cache, layers)
     torch.cuda.synchronize()
     slot_ms, runs = plan.profile_read()
