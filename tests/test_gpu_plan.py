@@ -143,6 +143,29 @@ def test_reindex_pool_shapes_and_ties(N, P, K, zero_q):
     assert torch.equal(direct[:, 0], layers[2]["out"])
 
 
+def test_pool_with_padding_when_most_scores_are_nan():
+    """Keys whose rows hold E4M3 NaN score NaN and are never selected: with 1000 finite scores per row,
+    the Full layer's pool (P = 2048) is 1000 positions then -1 padding, and both the Full and the
+    Reindex top-K (K = 1500) are 1000 positions then -1."""
+    cfg = synth.small("stack_b32_n262144", B=2, N=3000, K=1500, P=2048, modes=("full", "reindex", "reuse"))
+    cache, layers, ocache, olayers = build_case(cfg)
+    rng = np.random.default_rng(11)
+    kdev = cache.k_idx.view(torch.uint8)
+    for b in range(2):
+        nan_pos = np.sort(rng.choice(3000, size=2000, replace=False))
+        ocache[b]["k_idx"] = ocache[b]["k_idx"].copy()
+        ocache[b]["k_idx"][nan_pos] = 0x7F
+        kdev[b, torch.from_numpy(nan_pos).cuda()] = 0x7F
+    plan = make_plan(cfg)
+    plan.run_decode(cache, layers)
+    torch.cuda.synchronize()
+    stats = check_against_oracle(cfg, layers, ocache, olayers, range(2))
+    assert stats["excused"] == 0, stats
+    for li, name in ((0, "pool_out"), (0, "idx_out"), (1, "idx_out")):
+        got = host(layers[li][name])
+        assert (got[:, :1000] >= 0).all() and (got[:, 1000:] == -1).all(), (li, name)
+
+
 def test_reindex_over_whole_context_equals_full():
     cfg = synth.small("stack_b32_n262144", B=2, N=3000, K=50, P=3000, modes=("full", "reindex"))
     cache, layers, _, _ = build_case(cfg, with_oracle=False)
