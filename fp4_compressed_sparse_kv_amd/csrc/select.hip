@@ -132,15 +132,25 @@ struct SrcScan {
             // One 16-byte load per lane and key: batches of 1024 keys, key
             // base + 256u + quad in slot u of its quad's lanes; after the
             // transposed reduction lane lq owns key base + 256 lq + quad. Whole
-            // unmasked batches run software-pipelined (the next batch's loads
-            // are issued before this one is scored; two register sets, loads
-            // unconditional with the batch index clamped), the rest predicated.
+            // unmasked batches run software-pipelined over three register
+            // sets: while a batch is scored the loads of the next two are in
+            // flight. The loads are streaming buffer loads bounded by the
+            // chunk's causal limit, so the look-ahead past the last batch
+            // returns zeros without touching memory, and every load is
+            // unconditional (the compiler's wait counts stay exact). The
+            // rest is predicated.
             constexpr int kB = kSelThreads;
+            constexpr int kStreaming = 2;       // cache policy: non-temporal
+            const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<uint8_t*>(kb), (short)0, lim * KS::ROW_BYTES, kRsrcWord3);
+            const int qoff = quad * KS::ROW_BYTES + lq * (KS::ROW_BYTES / 4);
             const uint8_t* kq = kb + (int64_t)quad * KS::ROW_BYTES + lq * (KS::ROW_BYTES / 4);
             const int nfull = lim / kB;
             auto load_batch = [&](int bi, uint4 (&r)[4]) {
 #pragma unroll
-                for (int u = 0; u < 4; ++u) r[u] = ld_stream16(kq + (int64_t)(bi * kB + u * 256) * KS::ROW_BYTES);
+                for (int u = 0; u < 4; ++u)
+                    r[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                         kr, (bi * kB + u * 256) * KS::ROW_BYTES + qoff, 0, kStreaming));
             };
             auto score_batch = [&](const uint4 (&r)[4], int base, bool masked) {
                 double acc[4];
@@ -156,16 +166,20 @@ struct SrcScan {
                 else if (i < cnt) put_key(keys, hist, i, (i < lim) ? score_key((float)v) : 0u);
             };
             if (nfull > 0) {
-                uint4 ra[4], rb[4];
+                uint4 ra[4], rb[4], rc[4];
                 load_batch(0, ra);
+                load_batch(1, rb);
                 int bi = 0;
-                for (; bi + 2 <= nfull; bi += 2) {
-                    load_batch(bi + 1, rb);
+                for (; bi + 3 <= nfull; bi += 3) {
+                    load_batch(bi + 2, rc);
                     score_batch(ra, bi * kB, false);
-                    load_batch(min(bi + 2, nfull - 1), ra);
+                    load_batch(bi + 3, ra);
                     score_batch(rb, (bi + 1) * kB, false);
+                    load_batch(bi + 4, rb);
+                    score_batch(rc, (bi + 2) * kB, false);
                 }
                 if (bi < nfull) score_batch(ra, bi * kB, false);
+                if (bi + 1 < nfull) score_batch(rb, (bi + 1) * kB, false);
             }
             for (int base = nfull * kB; base < cnt; base += kB) {
                 uint4 r[4];
