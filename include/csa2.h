@@ -34,6 +34,14 @@
  *     csa2_last_error() describes the failure (thread-local string).
  *   - Element counts and strides are in elements of the named dtype unless
  *     the argument name ends in _bytes or the comment says bytes.
+ *   - Selection kernels (csa2_topk, csa2_plan_run_decode, csa2_prefill_full)
+ *     split a row over several workgroups that wait for each other, at most
+ *     one workgroup per compute unit, so they expect the compute units to be
+ *     free when they start (kernels of other streams that hold compute units
+ *     can delay them). Every such wait is bounded: after 2^20 polls it gives
+ *     up, sets bit 0 of the workspace's first 32-bit word (the status word)
+ *     and lets the kernel finish; the outputs of that call are then
+ *     unspecified. The status word is never cleared by the library.
  *
  * Storage formats (readings where the pages are silent are marked R):
  *   FP4 codes: one byte holds two E2M1 codes; channel 2j in the low nibble,
@@ -282,6 +290,15 @@ int csa2_plan_profile_read(csa2_plan* plan, float* avg_ms, int32_t* runs);
  *   q_idx   device [B][Q][d_idx];  q device [B][Q][H][d] bf16
  *   q_pos   device [B][Q] int64 positions of the queries
  *   idx_out device [B][Q][K] int32 (output);  out device [B][Q][H][d] fp32 (output)
+ *
+ * With bf16 indexer queries, E4M3 or bf16 keys, d_idx = 64 and long contexts
+ * the indexer runs on the matrix cores and only nominates candidates; their
+ * exact scores decide the top-K. A query whose result the candidates cannot
+ * certify (ties or near-ties at its threshold, an overflowing candidate list)
+ * is re-selected by an exact scan of its whole causal range, up to 64 such
+ * queries per call; beyond that, bit 1 (value 2) of the workspace status word
+ * is set and the remaining ones keep the candidate result, which is then not
+ * guaranteed to be the exact top-K.
  */
 int csa2_prefill_workspace_bytes(const csa2_plan* plan, int32_t B, int32_t Q, int64_t N, size_t* bytes);
 int csa2_prefill_full(const csa2_plan* plan, const csa2_cache* cache, const void* q_idx,
