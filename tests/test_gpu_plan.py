@@ -95,7 +95,8 @@ def test_full_layer_n2048_end_to_end():
 
 
 @pytest.mark.parametrize("B,N,K,P", [(3, 20000, 64, 512), (2, 70001, 2048, 8192), (1, 5000, 100, 100),
-                                     (2, 40000, 512, 20000)])   # a pool above 16,384: the general select
+                                     (2, 40000, 512, 20000),    # a pool above 16,384: the general select
+                                     (20, 20000, 512, 16384)])  # 16 chunks per pool row: two select launches
 def test_stack_full_reindex_reuse(B, N, K, P):
     cfg = synth.small("stack_b32_n262144", B=B, N=N, K=K, P=P)
     cache, layers, ocache, olayers = build_case(cfg)
