@@ -1040,61 +1040,77 @@ __global__ void __launch_bounds__(kSelThreads) k_select(Src src, SelDev g, SelTg
         __syncthreads();
     }
 
-    // ---- offsets: this chunk's output base and its share of the == T entries
+    // ---- offsets: this chunk's output base and its share of the == T entries.
+    // Wave j works out target j with its 64 lanes (lane s: chunk s, lane w:
+    // wave w of this chunk), by wave sums and scans in registers.
     uint32_t* wbase = sm + 128;                 // [2][16][base, eq_before]
     uint32_t* tinfo = sm + 192;                 // [2][take_eq, total_sel, eq_chunk, -]
-    if (tid < NT) {
-        const int j = tid;
+    static_assert(kSelWaves <= kWave, "one lane per wave of the workgroup");
+    if (wave < NT) {
+        const int j = wave;
         const uint32_t nj = pick<NT>(need[0], need[1], j);
-        uint32_t off = 0, eq_before = 0, total_sel = 0, my_take = 0, my_eq = 0;
+        uint32_t off = 0, total_sel = 0, my_take = 0, my_eq = 0;
+        const bool lw = lane < kSelWaves;
+        const uint32_t wgt = lw ? wcnt[(j * kSelWaves + lane) * 2 + 0] : 0u;   // this chunk's wave `lane`
+        const uint32_t weq = lw ? wcnt[(j * kSelWaves + lane) * 2 + 1] : 0u;
         if (pick<NT>(path[0], path[1], j) == kPathList) {
             // keys above bin b1 per chunk (cnts), plus the list counts by position;
             // ties are taken in chunk order, so only the totals before this
             // chunk and over all chunks matter
-            uint32_t ab_before = 0, ab_all = 0, lg_before = 0, le_before = 0, lg_all = 0, le_all = 0;
-            for (int s = 0; s < S; ++s) {
+            uint32_t ab_before = 0, ab_all = 0;
+            for (int s = lane; s < S; s += kWave) {
                 const uint32_t a = cnts[(s * 2 + j) * 2 + 0];
-                if (s < split) ab_before += a;
                 ab_all += a;
+                if (s < split) ab_before += a;
             }
-            for (int w = 0; w < kSelWaves; ++w) {
-                const uint32_t* agg = lh2 + (j * kSelWaves + w) * 2;
-                lg_before += agg[0];
-                le_before += agg[1];
-            }
-            lg_all = pick<NT>(lgt_all[0], lgt_all[1], j);
-            le_all = pick<NT>(leq_all[0], leq_all[1], j);
-            for (int w = 0; w < kSelWaves; ++w) my_eq += wcnt[(j * kSelWaves + w) * 2 + 1];
+            ab_before = wave_sum(ab_before);
+            ab_all = wave_sum(ab_all);
+            const uint32_t lg_before = wave_sum(lw ? lh2[(j * kSelWaves + lane) * 2 + 0] : 0u);
+            const uint32_t le_before = wave_sum(lw ? lh2[(j * kSelWaves + lane) * 2 + 1] : 0u);
+            const uint32_t lg_all = pick<NT>(lgt_all[0], lgt_all[1], j);
+            const uint32_t le_all = pick<NT>(leq_all[0], leq_all[1], j);
+            my_eq = wave_sum(weq);
             off = ab_before + lg_before + (le_before < nj ? le_before : nj);
             my_take = nj > le_before ? nj - le_before : 0u;
             if (my_take > my_eq) my_take = my_eq;
             total_sel = ab_all + lg_all + (le_all < nj ? le_all : nj);
         } else {
-            for (int s = 0; s < S; ++s) {
-                const uint32_t gt = cnts[(s * 2 + j) * 2 + 0], eq = cnts[(s * 2 + j) * 2 + 1];
-                const uint32_t left = nj > eq_before ? nj - eq_before : 0u;
+            // chunks in order: chunk s takes min(eq_s, nj - (ties in chunks before s)) of its ties
+            uint32_t run_eq = 0;
+            for (int s0 = 0; s0 < S; s0 += kWave) {
+                const int s = s0 + lane;
+                const uint32_t gt = s < S ? cnts[(s * 2 + j) * 2 + 0] : 0u;
+                const uint32_t eq = s < S ? cnts[(s * 2 + j) * 2 + 1] : 0u;
+                const uint32_t inc = wave_incl_scan(eq);
+                const uint32_t before = run_eq + inc - eq;
+                const uint32_t left = nj > before ? nj - before : 0u;
                 const uint32_t take = eq < left ? eq : left;
-                if (s < split) off += gt + take;
-                if (s == split) {
-                    my_take = take;
-                    my_eq = eq;
+                const uint32_t sel = gt + take;
+                off += wave_sum(s < split ? sel : 0u);
+                total_sel += wave_sum(sel);
+                if (split >= s0 && split < s0 + kWave) {   // uniform
+                    my_take = (uint32_t)__builtin_amdgcn_readlane((int)take, split - s0);
+                    my_eq = (uint32_t)__builtin_amdgcn_readlane((int)eq, split - s0);
                 }
-                total_sel += gt + take;
-                eq_before += eq;
+                run_eq += (uint32_t)__builtin_amdgcn_readlane((int)inc, kWave - 1);
             }
         }
-        uint32_t wb = off, web = 0;
-        for (int w = 0; w < kSelWaves; ++w) {
-            const uint32_t gt = wcnt[(j * kSelWaves + w) * 2 + 0], eq = wcnt[(j * kSelWaves + w) * 2 + 1];
-            const uint32_t left = my_take > web ? my_take - web : 0u;
-            wbase[(j * kSelWaves + w) * 2 + 0] = wb;
-            wbase[(j * kSelWaves + w) * 2 + 1] = web;
-            wb += gt + (eq < left ? eq : left);
-            web += eq;
+        // wave w of this chunk: base = off + the entries its earlier waves select,
+        // where wave w takes min(eq_w, my_take - ties of earlier waves) of its ties
+        const uint32_t einc = wave_incl_scan(weq);
+        const uint32_t web = einc - weq;
+        const uint32_t left = my_take > web ? my_take - web : 0u;
+        const uint32_t sel = wgt + (weq < left ? weq : left);
+        const uint32_t sinc = wave_incl_scan(sel);
+        if (lw) {
+            wbase[(j * kSelWaves + lane) * 2 + 0] = off + sinc - sel;
+            wbase[(j * kSelWaves + lane) * 2 + 1] = web;
         }
-        tinfo[j * 4 + 0] = my_take;
-        tinfo[j * 4 + 1] = total_sel;
-        tinfo[j * 4 + 2] = my_eq;
+        if (lane == 0) {
+            tinfo[j * 4 + 0] = my_take;
+            tinfo[j * 4 + 1] = total_sel;
+            tinfo[j * 4 + 2] = my_eq;
+        }
     }
     __syncthreads();
 
