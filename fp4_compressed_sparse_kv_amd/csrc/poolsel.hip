@@ -32,12 +32,12 @@ namespace csa2 {
 constexpr int kPsThreads = 1024;
 constexpr int kPsWaves = kPsThreads / kWave;
 constexpr int kPsChunk = kPsThreads;            // pool entries per workgroup (4 per lane quad)
-constexpr int kPsMaxN = (int)kPoolSelMaxN;         // pool entries per row (16 per thread)
+constexpr int kPsMaxN = (int)kPoolSelMaxN;      // pool entries per row (16 per thread)
 
 struct PsDev {
     int32_t n, n4, S, K, row0;                  // n4: n rounded up to a multiple of 4 (key buffer row stride)
     uint32_t* ctrl;                             // workspace control region
-    uint32_t* keys;                             // [rows of the launch][n] published keys
+    uint32_t* keys;                             // [rows of the launch][n4] published keys
 };
 
 struct PsLds {
@@ -287,6 +287,16 @@ namespace {
 template <int KT, int QT, int D>
 int launch_ps_typed(const PoolSelPlan& p, const PoolSelArgs& a, void* ws_ctrl, void* ws_data, hipStream_t stream) {
     auto fn = p.n <= 8 * kPsThreads ? k_pool_select<KT, QT, D, 8> : k_pool_select<KT, QT, D, 16>;
+    // the chunks of a row wait for each other: check once that a workgroup fits on a CU
+    static bool fits[2] = {false, false};
+    const int which = p.n <= 8 * kPsThreads ? 0 : 1;
+    if (!fits[which]) {
+        int per_cu = 0;
+        const hipError_t he = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kPsThreads, 0);
+        if (he != hipSuccess) return hip_fail(he, "hipOccupancyMaxActiveBlocksPerMultiprocessor(pool select)");
+        if (per_cu < 1) return fail(INVALID, "pool select: kernel does not fit on a CU");
+        fits[which] = true;
+    }
     PsDev g;
     g.n = p.n;
     g.n4 = p.n4;
