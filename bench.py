@@ -90,7 +90,7 @@ def measured_traffic(workload):
     return t.get("traffic_bytes_per_launch")
 
 
-def build_inputs(cfg, dev):
+def build_inputs(cfg, dev, query_set=0):
     import numpy as np
     import torch
 
@@ -128,8 +128,9 @@ def build_inputs(cfg, dev):
         cache.k_idx = kidx
     layers = []
     for li in range(L):
-        q = np.stack([synth.q_bf16(cfg, li, b)[0] for b in range(B)])
-        qi = np.stack([synth.q_idx(cfg, li, b)[0] for b in range(B)])
+        ql = query_set * L + li                 # set 0 is the workload's own queries (the parity tests' set)
+        q = np.stack([synth.q_bf16(cfg, ql, b)[0] for b in range(B)])
+        qi = np.stack([synth.q_idx(cfg, ql, b)[0] for b in range(B)])
         layers.append(dict(q=bf(q), q_idx=key_t(qi, cfg["q_idx_dtype"]),
                            out=torch.empty(B, cfg["H"], cfg["d"], dtype=torch.float32, device=dev),
                            idx_out=torch.empty(B, cfg["K"], dtype=torch.int32, device=dev)))
@@ -137,6 +138,53 @@ def build_inputs(cfg, dev):
         layers[0]["pool_out"] = torch.empty(B, cfg["P"], dtype=torch.int32, device=dev)
     torch.cuda.synchronize()
     return cache, layers
+
+
+def query_sets(cfg, dev, layers, nsets):
+    """nsets sets of per-layer queries (set 0 = `layers`), each another seeded draw of the same
+    distribution, sharing the output buffers of `layers`. Timed steps rotate through them so that
+    consecutive steps select different positions and the gathers are not served from caches warmed
+    by the previous step with the same queries."""
+    import numpy as np
+
+    import synth
+
+    B, L = cfg["B"], len(cfg["modes"])
+    sets = [layers]
+    for qs in range(1, nsets):
+        cur = []
+        for li in range(L):
+            ql = qs * L + li
+            q = np.stack([synth.q_bf16(cfg, ql, b)[0] for b in range(B)])
+            qi = np.stack([synth.q_idx(cfg, ql, b)[0] for b in range(B)])
+            d = dict(layers[li])
+            d["q"] = _to_dev_bf16(q, dev)
+            d["q_idx"] = _to_dev_key(qi, cfg["q_idx_dtype"], dev)
+            cur.append(d)
+        sets.append(cur)
+    return sets
+
+
+def _to_dev_bf16(bits, dev):
+    import numpy as np
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+
+def _to_dev_key(a, dt, dev):
+    import numpy as np
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if dt == "e4m3":
+        return t.to(dev).view(torch.float8_e4m3fn)
+    if dt == "bf16":
+        return t.view(torch.int16).to(dev).view(torch.bfloat16)
+    return t.to(dev)
+
+
+def host_cores():
+    """Host threads this process may run on (its CPU affinity)."""
+    return len(os.sched_getaffinity(0))
 
 
 def cpu_baseline(cfg, budget_s):
@@ -150,7 +198,8 @@ def cpu_baseline(cfg, budget_s):
     modes = list(cfg["modes"])
     scale = float(np.float32(1 / math.sqrt(cfg["d"])))
     done, spent = 0, 0.0
-    with threadpool_limits(limits=1):
+    cores = host_cores()
+    with threadpool_limits(limits=cores):
         for b in range(cfg["B"]):
             kb, vb = synth.kv_bf16(cfg, b)                           # untimed: input generation
             cache = dict(k_bf16=kb, v_bf16=vb, k_idx=synth.k_idx(cfg, b), k_idx_dtype=cfg["k_idx_dtype"])
@@ -162,10 +211,26 @@ def cpu_baseline(cfg, budget_s):
             done += 1
             if spent >= budget_s:
                 break
-    return {"value": done / spent, "unit": "queries/s", "cores": 1, "kind": "oracle",
+    return {"value": done / spent, "unit": "queries/s", "cores": cores, "kind": "oracle",
             "sample": f"{done} of {cfg['B']} sequences, one decode step of the whole stack each "
-                      f"(N={cfg['N']}), {spent:.1f} s on 1 host core (BLAS limited to 1 thread); "
-                      f"KV rows quantized by the oracle only where attention reads them"}
+                      f"(N={cfg['N']}), {spent:.1f} s with BLAS on {cores} host threads (the process's CPU "
+                      f"affinity); KV rows quantized by the oracle only where attention reads them"}
+
+
+def build_quant_input(cfg, dev):
+    """The quantize workload's T x C bf16 rows on the device, block by block from the seeded generator."""
+    import numpy as np
+    import torch
+
+    import synth
+
+    T, Cc, rb = cfg["T"], cfg["C"], cfg["row_block"]
+    x = torch.empty(T, Cc, dtype=torch.bfloat16, device=dev)
+    for blk in range(T // rb):
+        xb = synth.quant_rows(cfg, blk)
+        x[blk * rb:(blk + 1) * rb].copy_(torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16))
+    torch.cuda.synchronize()
+    return x
 
 
 def run_quant(args, cfg, dev):
@@ -181,10 +246,7 @@ def run_quant(args, cfg, dev):
 
     T, Cc, rb = cfg["T"], cfg["C"], cfg["row_block"]
     t0 = time.perf_counter()
-    x = torch.empty(T, Cc, dtype=torch.bfloat16, device=dev)
-    for blk in range(T // rb):
-        xb = synth.quant_rows(cfg, blk)
-        x[blk * rb:(blk + 1) * rb].copy_(torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16))
+    x = build_quant_input(cfg, dev)
     log(f"inputs ready in {time.perf_counter() - t0:.1f} s")
     codes = torch.empty(T, Cc // 2, dtype=torch.uint8, device=dev)
     scales = torch.empty(T, Cc // 16, dtype=torch.uint8, device=dev)
@@ -224,7 +286,8 @@ def run_quant(args, cfg, dev):
     }
     if not args.no_cpu:
         done, spent = 0, 0.0
-        with threadpool_limits(limits=1):
+        cores = host_cores()
+        with threadpool_limits(limits=cores):
             for blk in range(T // rb):
                 xb = synth.quant_rows(cfg, blk)                   # untimed: input generation
                 t1 = time.perf_counter()
@@ -233,9 +296,9 @@ def run_quant(args, cfg, dev):
                 done += rb
                 if spent >= args.cpu_seconds:
                     break
-        out["cpu_baseline"] = {"value": round(done / spent, 1), "unit": "rows/s", "cores": 1, "kind": "oracle",
-                               "sample": f"{done} of {T} rows ({done // rb} blocks of {rb}), {spent:.1f} s on 1 host "
-                                         f"core (BLAS limited to 1 thread)"}
+        out["cpu_baseline"] = {"value": round(done / spent, 1), "unit": "rows/s", "cores": cores, "kind": "oracle",
+                               "sample": f"{done} of {T} rows ({done // rb} blocks of {rb}), {spent:.1f} s with "
+                                         f"BLAS on {cores} host threads (numpy's elementwise work runs on one)"}
     print(json.dumps(out), flush=True)
 
 
@@ -263,12 +326,12 @@ def run_prefill(args, cfg, dev):
     out = torch.empty(B, Q, cfg["H"], cfg["d"], dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
     for _ in range(args.warmup):
-        plan.prefill_full(cache, qi_t, qb_t, q_pos, idx_out=idx, out=out)
+        plan.prefill_full(cache, qi_t, qb_t, q_pos, idx_out=idx, out=out, check=False)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     for _ in range(args.steps):
-        plan.prefill_full(cache, qi_t, qb_t, q_pos, idx_out=idx, out=out)
+        plan.prefill_full(cache, qi_t, qb_t, q_pos, idx_out=idx, out=out, check=False)
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
@@ -277,7 +340,7 @@ def run_prefill(args, cfg, dev):
     flop = 2.0 * cfg["d_idx"] * causal                  # indexer dot products, causal positions only
     res = {
         "metric": "Full-layer prefill queries/s (indexer + exact top-K + FP4 sparse attention)",
-        "value": round(B * Q / (ms * 1e-3), 1), "unit": "queries/s", "n_gpus": 1, "steps": args.steps,
+        "value": round(B * Q / (ms * 1e-3), 1) if status == 0 else None, "unit": "queries/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16 MFMA (candidates) / f64 (exact scores) / f32", "data": "synthetic",
         "config": {"workload": args.workload + ":prefill", "B": B, "N": N, "Q": Q, "K": K, "H": cfg["H"],
@@ -313,7 +376,8 @@ def prefill_cpu_baseline(cfg, budget_s):
     qi = synth.prefill_q_idx(cfg, 0, Q)
     qb = synth.prefill_q_bf16(cfg, 0, Q)
     done, spent = 0, 0.0
-    with threadpool_limits(limits=1):
+    cores = host_cores()
+    with threadpool_limits(limits=cores):
         for i in range(0, Q, 97):                                    # a spread of query positions
             t0 = time.perf_counter()
             s = OS.index_scores(qi[i], cfg["q_idx_dtype"], cache["k_idx"], cfg["k_idx_dtype"], q_pos=N - Q + i)
@@ -323,9 +387,9 @@ def prefill_cpu_baseline(cfg, budget_s):
             done += 1
             if spent >= budget_s:
                 break
-    return {"value": done / spent, "unit": "queries/s", "cores": 1, "kind": "oracle",
-            "sample": f"{done} of {Q} queries of sequence 0 (every 97th position), N={N}, {spent:.1f} s on 1 host "
-                      f"core (BLAS limited to 1 thread); KV rows quantized by the oracle only where attention reads them"}
+    return {"value": done / spent, "unit": "queries/s", "cores": cores, "kind": "oracle",
+            "sample": f"{done} of {Q} queries of sequence 0 (every 97th position), N={N}, {spent:.1f} s with BLAS "
+                      f"on {cores} host threads; KV rows quantized by the oracle only where attention reads them"}
 
 
 def main():
@@ -337,6 +401,8 @@ def main():
     ap.add_argument("--workload", default="stack_b32_n262144")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--query-sets", type=int, default=4,
+                    help="decode: timed steps rotate through this many seeded query sets")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--prefill", action="store_true",
                     help="time the workload's Full-layer prefill chunk instead of the decode step")
@@ -374,27 +440,30 @@ def main():
     plan = C.Plan(cfg["modes"], K=cfg["K"], P=cfg.get("P") or 0, H=cfg["H"], d=cfg["d"], d_idx=cfg["d_idx"],
                   q_idx_dtype=cfg["q_idx_dtype"], k_idx_dtype=cfg["k_idx_dtype"])
     stream = torch.cuda.current_stream()
+    sets = query_sets(cfg, dev, layers, args.query_sets)
+    ws = plan.decode_workspace(cache)
 
-    for _ in range(args.warmup):
-        plan.run_decode(cache, layers)
+    for i in range(args.warmup):
+        plan.run_decode(cache, sets[i % len(sets)], ws=ws, check=False)
     torch.cuda.synchronize()
 
     # timed region: exactly K steps between two events, synchronized on both sides
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record(stream)
-    for _ in range(args.steps):
-        plan.run_decode(cache, layers)
+    for i in range(args.steps):
+        plan.run_decode(cache, sets[i % len(sets)], ws=ws, check=False)
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
-    log(f"step {ms * 1e3:.1f} us")
+    status = C.status_word(ws)
+    log(f"step {ms * 1e3:.1f} us, status word {status}")
 
     # per-kernel durations over a second pass of up to 100 steps (events around each kernel, same stream)
     prof_steps = min(args.steps, 100)
     plan.profile_begin(prof_steps)
-    for _ in range(prof_steps):
-        plan.run_decode(cache, layers)
+    for i in range(prof_steps):
+        plan.run_decode(cache, sets[i % len(sets)], ws=ws, check=False)
     torch.cuda.synchronize()
     slot_ms, runs = plan.profile_read()
     plan.profile_begin(0)
@@ -403,15 +472,16 @@ def main():
     # cold-cache steps: a 1 GiB write between steps evicts L2 and MALL; each step timed alone
     flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     cold = []
-    for _ in range(min(args.steps, 10)):
+    for i in range(min(args.steps, 10)):
         flush.fill_(1)
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record(stream)
-        plan.run_decode(cache, layers)
+        plan.run_decode(cache, sets[i % len(sets)], ws=ws, check=False)
         b.record(stream)
         torch.cuda.synchronize()
         cold.append(a.elapsed_time(b))
     del flush
+    status |= C.status_word(ws)
 
     # achievable reference: a device-to-device copy of 1 GiB (2 GiB moved)
     src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -441,7 +511,7 @@ def main():
     traffic = measured_traffic(args.workload)
     out = {
         "metric": METRIC,
-        "value": round(qps, 1),
+        "value": round(qps, 1) if status == 0 else None,
         "unit": "queries/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -456,6 +526,9 @@ def main():
                    "H": cfg["H"], "d": cfg["d"], "d_idx": cfg["d_idx"], "K": cfg["K"], "P": cfg.get("P"),
                    "kv": "fp4_e2m1 + e4m3 scale per 16 ch", "indexer_keys": cfg["k_idx_dtype"],
                    "indexer_query": cfg["q_idx_dtype"]},
+        "status_word": status,
+        "query_sets": len(sets),
+        "hbm_frac_basis": f"ms_per_step: timed steps rotate through {len(sets)} seeded query sets",
         "hbm_gbs_step": round(step_bytes / (ms * 1e-3) / 1e9, 1),
         "hbm_frac_step": round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "alg_bytes_step": step_bytes,

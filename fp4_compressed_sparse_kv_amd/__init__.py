@@ -11,7 +11,6 @@ Build first:  python -m fp4_compressed_sparse_kv_amd.build
 """
 
 import ctypes
-import math
 import os
 import threading
 
@@ -20,7 +19,7 @@ import torch
 __all__ = [
     "Csa2Error", "lib", "F32", "BF16", "E4M3", "FULL", "REINDEX", "REUSE",
     "kv_quant_fp4", "kv_dequant_fp4", "index_full", "index_reindex", "topk",
-    "sparse_attn_fp4", "KVCache", "Plan",
+    "sparse_attn_fp4", "KVCache", "Plan", "status_word",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcsa2.so")
@@ -139,6 +138,23 @@ def workspace(nbytes, device, key="default"):
         ws = torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device)
         _ws_cache[k] = ws
     return ws
+
+
+STATUS_BARRIER_TIMEOUT = 1      # a selection kernel's in-kernel wait gave up: that call's outputs are unspecified
+
+
+def status_word(ws):
+    """The device status word of a workspace (its first 32-bit word; synchronizes with the device).
+    0 = every call that used this workspace completed normally; the library never clears it."""
+    torch.cuda.synchronize(ws.device)
+    return int(ws[:4].view(torch.int32).item())
+
+
+def _check_status(ws, what):
+    st = status_word(ws)
+    if st:
+        raise Csa2Error(f"{what}: device status word {st:#x} (bit 0: a selection kernel's in-kernel wait "
+                        f"timed out) - the outputs are not valid")
 
 
 # ------------------------------------------------------------------- calls
@@ -260,7 +276,7 @@ def sparse_attn_fp4(q, cache, idx, softmax_scale=None, out=None, stream=None, ws
     K = idx.shape[-1]
     if out is None:
         out = torch.empty(B, Q, H, d, dtype=torch.float32, device=q.device)
-    scale = 1.0 / math.sqrt(d) if softmax_scale is None else softmax_scale
+    scale = 0.0 if softmax_scale is None else softmax_scale     # 0: the library's default 1/sqrt(d)
     nb = ctypes.c_size_t(0)
     _check(lib().csa2_sparse_attn_workspace_bytes(B, Q, H, d, K, ctypes.byref(nb)), "csa2_sparse_attn_workspace_bytes")
     if ws is None:
@@ -297,12 +313,18 @@ class Plan:
         _check(lib().csa2_plan_workspace_bytes(self._h, B, N, ctypes.byref(nb)), "csa2_plan_workspace_bytes")
         return nb.value
 
-    def run_decode(self, cache, layers, ws=None, stream=None):
+    def decode_workspace(self, cache):
+        """The cached workspace run_decode uses for this cache's shape (zero-filled once)."""
+        return workspace(self.workspace_bytes(cache.B, cache.N), cache.codes.device, ("plan", id(self)))
+
+    def run_decode(self, cache, layers, ws=None, stream=None, check=True):
         """layers: list of dicts with 'q' [B][H][d] bf16, 'q_idx' [B][d_idx], 'out' [B][H][d] fp32 and
-        optional 'idx_out' [B][K] int32, 'pool_out' [B][P] int32."""
+        optional 'idx_out' [B][K] int32, 'pool_out' [B][P] int32.
+        check: synchronize and raise Csa2Error if the workspace status word is nonzero (pass False in
+        timing loops and read status_word(plan.decode_workspace(cache)) afterwards)."""
         B, N = cache.B, cache.N
         if ws is None:
-            ws = workspace(self.workspace_bytes(B, N), cache.codes.device, ("plan", id(self)))
+            ws = self.decode_workspace(cache)
         io = (LayerIO * len(layers))()
         for i, L in enumerate(layers):
             io[i] = LayerIO(L["q"].data_ptr(), L["q_idx"].data_ptr() if L.get("q_idx") is not None else None,
@@ -312,6 +334,8 @@ class Plan:
         desc = cache.desc()
         _check(lib().csa2_plan_run_decode(self._h, ctypes.byref(desc), io, B, N, _ptr(ws), ws.numel(),
                                           _stream(stream)), "csa2_plan_run_decode")
+        if check:
+            _check_status(ws, "csa2_plan_run_decode")
 
     def profile_begin(self, max_runs):
         """Record HIP events around every kernel of the next max_runs run_decode calls."""
@@ -330,16 +354,18 @@ class Plan:
         _check(lib().csa2_prefill_workspace_bytes(self._h, B, Q, N, ctypes.byref(nb)), "csa2_prefill_workspace_bytes")
         return nb.value
 
-    def prefill_status(self, cache, Q):
-        """Device status word of the cached prefill workspace (synchronizes): 0 = clean; bit 1 = more rows
-        failed the candidate check than the exact repair pass holds (their top-K is not guaranteed)."""
+    def prefill_workspace(self, cache, Q):
+        """The cached workspace prefill_full uses for this shape (zero-filled once)."""
         nb = self.prefill_workspace_bytes(cache.B, Q, cache.N)
-        ws = workspace(nb, cache.codes.device, ("prefill", id(self)))
-        torch.cuda.synchronize(ws.device)
-        return int(ws[:4].view(torch.int32).item())
+        return workspace(nb, cache.codes.device, ("prefill", id(self)))
 
-    def prefill_full(self, cache, q_idx, q, q_pos, idx_out=None, out=None, ws=None, stream=None):
-        """Full-layer prefill: q_idx [B][Q][d_idx], q [B][Q][H][d] bf16, q_pos [B][Q] int64."""
+    def prefill_status(self, cache, Q):
+        """Device status word of the cached prefill workspace (synchronizes); 0 = clean."""
+        return status_word(self.prefill_workspace(cache, Q))
+
+    def prefill_full(self, cache, q_idx, q, q_pos, idx_out=None, out=None, ws=None, stream=None, check=True):
+        """Full-layer prefill: q_idx [B][Q][d_idx], q [B][Q][H][d] bf16, q_pos [B][Q] int64.
+        check: synchronize and raise Csa2Error if the workspace status word is nonzero."""
         B, Q = q_pos.shape
         dev = q.device
         K = self.params.K
@@ -348,9 +374,11 @@ class Plan:
         if out is None:
             out = torch.empty(B, Q, q.shape[2], q.shape[3], dtype=torch.float32, device=dev)
         if ws is None:
-            ws = workspace(self.prefill_workspace_bytes(B, Q, cache.N), dev, ("prefill", id(self)))
+            ws = self.prefill_workspace(cache, Q)
         desc = cache.desc()
         _check(lib().csa2_prefill_full(self._h, ctypes.byref(desc), _ptr(q_idx), _ptr(q), _ptr(q_pos), B, Q, cache.N,
                                        _ptr(idx_out), _ptr(out), _ptr(ws), ws.numel(), _stream(stream)),
                "csa2_prefill_full")
+        if check:
+            _check_status(ws, "csa2_prefill_full")
         return idx_out, out

@@ -240,8 +240,9 @@ int csa2_sparse_attn_fp4(const uint16_t* q, int32_t B, int32_t Q, int32_t H, int
                            "csa2_sparse_attn_fp4"))
         return e;
     if (!idx || !out) return fail(INVALID, "csa2_sparse_attn_fp4: null pointer");
-    if (!(softmax_scale > 0.f) || !isfinite(softmax_scale))
-        return fail(INVALID, "csa2_sparse_attn_fp4: softmax_scale must be positive and finite");
+    if (!(softmax_scale >= 0.f) || !isfinite(softmax_scale))
+        return fail(INVALID, "csa2_sparse_attn_fp4: softmax_scale must be >= 0 and finite");
+    if (softmax_scale == 0.f) softmax_scale = 1.0f / sqrtf((float)d);
     const size_t need = kCtrlBytes + attn_data_bytes((int64_t)B * Q, K);
     if (int e = check_ws(ws, ws_bytes, need, "csa2_sparse_attn_fp4")) return e;
     AttnArgs a;
@@ -548,7 +549,7 @@ namespace {
 // data region shared by the three select calls (they run one after another)
 // and the attention data; or (exact path) one select region and the attention.
 constexpr int32_t kSampleStride = 64;           // every 64th position is sampled
-constexpr int32_t kRepairRows = 64;             // rows the exact repair pass holds
+constexpr int32_t kRepairRows = 64;             // queued rows the multi-workgroup exact repair pass takes
 constexpr int64_t kRthMaxSamples = 16384;       // sample rows the threshold kernel holds in registers
 
 struct PrefillLayout {
@@ -602,8 +603,8 @@ int prefill_layout(const csa2_plan* plan, int32_t B, int32_t Q, int64_t N, Prefi
         off += align_up((size_t)rows * p.K * 4);
         lay->off_cnt = off;
         off += align_up((size_t)rows * lay->nr * 4);
-        lay->off_rep = off;                     // [count][pad][kRepairRows rows][kRepairRows map]
-        off += align_up((size_t)(64 + 2 * kRepairRows) * 4);
+        lay->off_rep = off;                     // [count][pad][rows queue slots][kRepairRows map]
+        off += align_up((size_t)(64 + rows + kRepairRows) * 4);
         lay->off_sel = off;
         size_t sel = lay->sel_sample.data_bytes;
         if (lay->sel_cand.data_bytes > sel) sel = lay->sel_cand.data_bytes;
@@ -672,7 +673,7 @@ int csa2_prefill_full(const csa2_plan* plan, const csa2_cache* cache, const void
         uint32_t* cnt = reinterpret_cast<uint32_t*>(wsb + lay.off_cnt);
         uint32_t* rep_count = reinterpret_cast<uint32_t*>(wsb + lay.off_rep);
         int32_t* rep_rows = reinterpret_cast<int32_t*>(wsb + lay.off_rep) + 64;
-        int32_t* rep_map = rep_rows + kRepairRows;
+        int32_t* rep_map = rep_rows + rows;
         int32_t* cand = reinterpret_cast<int32_t*>(wsb + lay.off_dense);   // reuses the sample scores
         uint32_t* status = reinterpret_cast<uint32_t*>(wsb);
         if (int e = launch_pf_kmax(a.k, p.k_idx_dtype, B, N, kmax, stream)) return e;
@@ -719,12 +720,17 @@ int csa2_prefill_full(const csa2_plan* plan, const csa2_cache* cache, const void
         SelOutput oc{idx_out, csc, p.K, p.K};
         if (int e = run_select(lay.sel_cand, SRC_CAND, ca, none, &oc, 1, wsb, wsb + lay.off_sel, stream)) return e;
         if (int e = launch_pf_verify(rows, lay.nr, lay.cap, cnt, csc, thr, q_pos, N, p.K, rep_rows, rep_count,
-                                     kRepairRows, status, stream))
+                                     (int32_t)rows, status, stream))
             return e;
+        // queued rows: the first kRepairRows by the multi-workgroup exact select, any others by
+        // one workgroup each (that kernel returns at once when the queue is no longer)
         if (int e = launch_pf_repair_map(rep_rows, rep_count, 0, kRepairRows, rep_map, stream)) return e;
         ScanArgs ra = a;
         ra.rowmap = rep_map;
         if (int e = run_select(lay.sel_exact, SRC_SCAN, ra, none, &o, 1, wsb, wsb + lay.off_sel, stream)) return e;
+        if (int e = launch_pf_repair_rest(qb, a.k, p.k_idx_dtype, N, Q, q_pos, rep_rows, rep_count, kRepairRows, p.K,
+                                          idx_out, stream))
+            return e;
     }
     AttnArgs at;
     at.q = q;

@@ -24,10 +24,14 @@
 //      step 4 (no cross-lane movement), and output channel 8m + t of MFMA t
 //      lands in accumulator row m, so each lane dequantizes only the 8
 //      channels 8n..8n+7 of its 8 positions.
-// The query is converted to f16 once (exact for |q| in [2^-14, 65504]; smaller
-// magnitudes round to f16 subnormals, an absolute error below 2^-25). Each
-// softmax weight p (fp32) enters the matrix core as two f16 terms hi + lo
-// (about 22 significant bits together); accumulation is fp32.
+// Each head's query is scaled by a power of two 2^-e (e from the head's
+// largest |q|, so that element lands in [2^14, 2^15)) and converted to f16
+// once: exact for every element within 2^28 of the head's largest one, any
+// finite bf16 magnitude. The logits stay in these scaled units; the factor
+// 2^e is applied to the differences (logit - running maximum) inside the
+// exponent, so neither huge nor tiny queries overflow or lose the softmax.
+// Each softmax weight p (fp32) enters the matrix core as two f16 terms
+// hi + lo (about 22 significant bits together); accumulation is fp32.
 //
 // The waves of a workgroup are merged through LDS in wave order. With NS > 1
 // each workgroup writes its (max, sum, acc) state to the workspace with
@@ -139,6 +143,7 @@ struct MergeArea {
     float acc[W][kMaxHeads][kMergeStride];
     float m[W][kMaxHeads];
     float l[W][kMaxHeads];
+    float f[kMaxHeads];                         // per head: 2^e, the query's scale-back factor
 };
 
 template <int W>
@@ -185,7 +190,8 @@ __device__ __forceinline__ void gather(BlockRaw& r, const BlockPos& bp, int blk,
 }
 
 struct WaveState {
-    float m, l;                                 // head n (same in the 4 lane groups), log2 units
+    float m, l;                                 // head n (same in the 4 lane groups), scaled log2 units
+    float f;                                    // head n: 2^e, scaled log2 units -> log2 units
     f32x4 acc[8];                               // acc[t][i] = unnormalized out[n][8*(4g+i) + t]
 };
 
@@ -245,13 +251,13 @@ __device__ __forceinline__ void attend_block(WaveState& st, const BlockRaw& r, S
     mx = rows_max(mx);
     const float m_old = st.m;
     const float m_new = fmaxf(m_old, mx);
-    // weights 2^(lg - m_new): the hardware exp2 flushes results below 2^-126
-    // to zero, far below what can matter against the maximum weight 1
+    // weights 2^((lg - m_new) * 2^e): the hardware exp2 flushes results below
+    // 2^-126 to zero, far below what can matter against the maximum weight 1
     const float mref = m_new == -INFINITY ? 0.f : m_new;
     float p[8], psum = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        p[i] = __builtin_amdgcn_exp2f(lg[i] - mref);
+        p[i] = __builtin_amdgcn_exp2f((lg[i] - mref) * st.f);
         psum += p[i];
     }
     f16x8 pb_hi, pb_lo;                         // p = hi + lo, both f16: ~22 significant bits
@@ -265,7 +271,7 @@ __device__ __forceinline__ void attend_block(WaveState& st, const BlockRaw& r, S
         pb_lo[i + 1] = lo.y;
     }
     psum = rows_sum(psum);
-    const float alpha = m_old == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_old - mref);
+    const float alpha = m_old == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m_old - mref) * st.f);
     st.l = st.l * alpha + psum;
     st.m = m_new;
     // the running sums need rescaling only where the maximum grew after the
@@ -342,14 +348,26 @@ k_sparse_attn(const uint16_t* __restrict__ q, int32_t rows_per_seq, int32_t H, c
             qraw[s] = *reinterpret_cast<const uint4*>(q + (row * H + min(n, H - 1)) * (int64_t)kD + 32 * g + 8 * s);
     };
     f16x8 qb[4];
+    int qe = 0;                                 // head n's query is used as q * 2^-qe
     auto convert_q = [&]() {
+        uint32_t mb = 0;                        // largest |q| of this lane's 32 elements (bf16 bits)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const uint32_t w[4] = {qraw[s].x, qraw[s].y, qraw[s].z, qraw[s].w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) mb = max(mb, max(w[i] & 0x7FFFu, (w[i] >> 16) & 0x7FFFu));
+        }
+        const float qmax = rows_max(bf16_bits_to_f32(mb));   // over the head's 128 channels
+        int ex = 0;
+        (void)frexpf(qmax, &ex);                // qmax = m * 2^ex, m in [0.5, 1)
+        qe = qmax > 0.f ? ex - 15 : 0;
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             const uint32_t w[4] = {qraw[s].x, qraw[s].y, qraw[s].z, qraw[s].w};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                qb[s][2 * i + 0] = n < H ? (_Float16)bf16_bits_to_f32(w[i] & 0xFFFFu) : (_Float16)0.f;
-                qb[s][2 * i + 1] = n < H ? (_Float16)bf16_bits_to_f32(w[i] >> 16) : (_Float16)0.f;
+                qb[s][2 * i + 0] = n < H ? (_Float16)ldexpf(bf16_bits_to_f32(w[i] & 0xFFFFu), -qe) : (_Float16)0.f;
+                qb[s][2 * i + 1] = n < H ? (_Float16)ldexpf(bf16_bits_to_f32(w[i] >> 16), -qe) : (_Float16)0.f;
             }
         }
     };
@@ -361,6 +379,7 @@ k_sparse_attn(const uint16_t* __restrict__ q, int32_t rows_per_seq, int32_t H, c
     WaveState st;
     st.m = -INFINITY;
     st.l = 0.f;
+    st.f = 1.f;
 #pragma unroll
     for (int t = 0; t < 8; ++t) st.acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
@@ -380,6 +399,7 @@ k_sparse_attn(const uint16_t* __restrict__ q, int32_t rows_per_seq, int32_t H, c
         BlockPos p1 = load_pos(ip, first + min(1, nb - 1) * kAttnWaves, K, lane);
         gather(r0, p0, first, K, kv, N, lane, n, g);
         convert_q();
+        st.f = ldexpf(1.f, qe);
         int k = 0;
         for (; k + 3 < nb; k += 2) {
             const int bk = first + k * kAttnWaves;
@@ -406,6 +426,10 @@ k_sparse_attn(const uint16_t* __restrict__ q, int32_t rows_per_seq, int32_t H, c
             attend_block(st, r1, lds.st[wave], qb, sl2, lane, n, g);
             attend_block(st, r0, lds.st[wave], qb, sl2, lane, n, g);
         }
+    } else {                                    // no block: only the scale-back factor is needed
+        load_q();
+        convert_q();
+        st.f = ldexpf(1.f, qe);
     }
 
     // ---- merge the waves in wave order (the staging areas are reused)
@@ -419,12 +443,14 @@ k_sparse_attn(const uint16_t* __restrict__ q, int32_t rows_per_seq, int32_t H, c
     if (g == 0) {
         lds.mg.m[wave][n] = st.m;
         lds.mg.l[wave][n] = st.l;
+        if (wave == 0) lds.mg.f[n] = st.f;
     }
     __syncthreads();
 
     // this thread's head h and channels c0 .. c0 + kCh - 1
     const int h = tid / (kD / kCh);
     const int c0 = (tid % (kD / kCh)) * kCh;
+    const float fh = lds.mg.f[h];
     float M = -INFINITY;
 #pragma unroll
     for (int w = 0; w < kAttnWaves; ++w) M = fmaxf(M, lds.mg.m[w][h]);
@@ -436,7 +462,7 @@ k_sparse_attn(const uint16_t* __restrict__ q, int32_t rows_per_seq, int32_t H, c
 #pragma unroll
         for (int w = 0; w < kAttnWaves; ++w) {
             const float mw = lds.mg.m[w][h];
-            const float wt = (mw == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw - M);
+            const float wt = (mw == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((mw - M) * fh);
             L += wt * lds.mg.l[w][h];
 #pragma unroll
             for (int v = 0; v < kV4; ++v) o[v] += wt * *reinterpret_cast<const f32x4*>(&lds.mg.acc[w][h][c0 + 4 * v]);
@@ -495,7 +521,7 @@ k_sparse_attn(const uint16_t* __restrict__ q, int32_t rows_per_seq, int32_t H, c
 #pragma unroll
         for (int s = 0; s < kMaxSplits; ++s) {
             const float ms = __uint_as_float(pml[s].x);
-            const float wt = (s >= NS || ms == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ms - MM);
+            const float wt = (s >= NS || ms == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((ms - MM) * fh);
             LL += wt * __uint_as_float(pml[s].y);
 #pragma unroll
             for (int v = 0; v < kV4; ++v) oo[v] += wt * __builtin_bit_cast(f32x4, pa[s][v]);

@@ -16,7 +16,7 @@ template <int KT, int QT, int D>
 __global__ void __launch_bounds__(kIdxThreads)
 k_index_dense(const void* __restrict__ q, const uint8_t* __restrict__ k, int64_t N, int32_t Q,
               const int64_t* __restrict__ q_pos, float* __restrict__ scores) {
-    using KS = KeySlice<KT, D>;
+    using KS = KeySlice<KT, D, QT>;
     constexpr int QB = (QT == kBF16) ? 2 : 4;
     const int64_t row = blockIdx.y;                       // b*Q + i
     const int64_t seq = row / Q;
@@ -32,8 +32,8 @@ k_index_dense(const void* __restrict__ q, const uint8_t* __restrict__ k, int64_t
         KS s;
         if (t < N) s.load(kb + t * KS::ROW_BYTES, lq);
         else for (int w = 0; w < KS::RAW; ++w) s.raw[w] = make_uint4(0, 0, 0, 0);
-        const double v = quad_sum(s.dot(qd));
-        if (lq == 0 && t < N) out[t] = (t > qp) ? -INFINITY : (float)v;
+        const auto v = quad_sum(s.dot(qd));
+        if (lq == 0 && t < N) out[t] = (t > qp) ? -INFINITY : round_score(v);
     }
 }
 
@@ -41,7 +41,7 @@ template <int KT, int QT, int D>
 __global__ void __launch_bounds__(kIdxThreads)
 k_index_pool(const void* __restrict__ q, const uint8_t* __restrict__ k, int64_t N, const int32_t* __restrict__ pool,
              int32_t P, float* __restrict__ scores) {
-    using KS = KeySlice<KT, D>;
+    using KS = KeySlice<KT, D, QT>;
     constexpr int QB = (QT == kBF16) ? 2 : 4;
     const int64_t row = blockIdx.y;
     const int quad = threadIdx.x >> 2, lq = threadIdx.x & 3;
@@ -56,8 +56,8 @@ k_index_pool(const void* __restrict__ q, const uint8_t* __restrict__ k, int64_t 
         KS s;
         if (ok) s.load(kb + (int64_t)pos * KS::ROW_BYTES, lq);
         else for (int w = 0; w < KS::RAW; ++w) s.raw[w] = make_uint4(0, 0, 0, 0);
-        const double v = quad_sum(s.dot(qd));
-        if (lq == 0 && i < P) scores[row * P + i] = ok ? (float)v : -INFINITY;
+        const auto v = quad_sum(s.dot(qd));
+        if (lq == 0 && i < P) scores[row * P + i] = ok ? round_score(v) : -INFINITY;
     }
 }
 

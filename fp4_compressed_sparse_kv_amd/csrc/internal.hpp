@@ -140,6 +140,10 @@ int launch_pf_thresholds(const uint16_t* q, int64_t rows, int32_t Q, const float
 int launch_pf_verify(int64_t rows, int32_t nranges, int32_t cap, const uint32_t* cnt, const float* sel,
                      const float* thr, const int64_t* q_pos, int64_t N, int32_t K, int32_t* repair_rows,
                      uint32_t* repair_count, int32_t repair_cap, uint32_t* status, hipStream_t stream);
+// Exact top-K of the queued queries in queue slots [first, count): one workgroup per query.
+int launch_pf_repair_rest(const uint16_t* q, const uint8_t* k, int k_dtype, int64_t N, int32_t Q,
+                          const int64_t* q_pos, const int32_t* repair_rows, const uint32_t* repair_count, int32_t first,
+                          int32_t K, int32_t* idx_out, hipStream_t stream);
 int launch_pf_repair_map(const int32_t* repair_rows, const uint32_t* repair_count, int32_t first, int32_t n,
                          int32_t* map, hipStream_t stream);
 

@@ -97,7 +97,7 @@ __global__ void __launch_bounds__(kPsThreads) k_pool_select(const void* __restri
                                                             int64_t N, const int32_t* __restrict__ pool, PsDev g,
                                                             int32_t* __restrict__ idx_out, int64_t idx_stride,
                                                             float* __restrict__ sc_out) {
-    using KS = KeySlice<KT, D>;
+    using KS = KeySlice<KT, D, QT>;
     constexpr int QB = (QT == kBF16) ? 2 : 4;
     __shared__ PsLds L;
     const int tid = threadIdx.x;
@@ -137,16 +137,16 @@ __global__ void __launch_bounds__(kPsThreads) k_pool_select(const void* __restri
             // padding entries read key row 0 and are discarded
             s[u].load(kb + (int64_t)(ok[u] ? pv[u] : 0) * KS::ROW_BYTES, lq);
         }
-        double acc[4];
+        typename KS::Part acc[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) acc[u] = s[u].dot(qd);
-        const double v = quad_transpose_sum(acc, lq);
+        const auto v = quad_transpose_sum(acc, lq);
         const int i = lq * (kPsThreads / 4) + quad;
         const bool okl = lq == 0 ? ok[0] : lq == 1 ? ok[1] : lq == 2 ? ok[2] : ok[3];
         const int32_t pvl = lq == 0 ? pv[0] : lq == 1 ? pv[1] : lq == 2 ? pv[2] : pv[3];
         if (i < cnt) {
             const __amdgpu_buffer_rsrc_t ws = __builtin_amdgcn_make_buffer_rsrc(rkeys, (short)0, g.n4 * 4, kRsrcWord3);
-            __builtin_amdgcn_raw_buffer_store_b32(okl ? score_key((float)v) : 0u, ws, (begin + i) * 4, 0, kCoherent);
+            __builtin_amdgcn_raw_buffer_store_b32(okl ? score_key(round_score(v)) : 0u, ws, (begin + i) * 4, 0, kCoherent);
             L.pos[i] = (uint32_t)pvl;
         }
     }

@@ -27,7 +27,8 @@
 //      the top-K or tie with its last member, so the result is the exact
 //      top-K; so it is too when the lists hold every causal position. Queries
 //      that fail both tests, or whose lists overflowed, are queued for the
-//      exact full-scan select.
+//      exact full-scan select (all of them: the first 64 by the multi-
+//      workgroup select, any further ones by k_pf_repair_rest).
 // Matrix-core tiles: a workgroup of 4 waves owns 128 queries of one sequence
 // and one key range; wave w owns query rows 32w..32w+31 and runs
 // v_mfma_f32_32x32x16_bf16 over 128-key tiles staged in LDS as bf16 (E4M3
@@ -109,7 +110,7 @@ struct PfTileArgs {
     const int64_t* q_pos;                       // [rows] causal limit
     int64_t key_off, key_stride, nkeys;         // key j of the set is position key_off + j * key_stride
     int32_t nranges;
-    int64_t range_len;                          // keys per range (a multiple of kPfKeys)
+    int64_t range_len;                          // dense mode: keys per range (a multiple of kPfKeys)
     float* dense;                               // dense mode: [rows][nkeys] scores (s~, -inf past q_pos)
     const float* thr;                           // candidate mode: [rows][2] (lo, v)
     int32_t* cand;                              // [rows][nranges][cap] positions
@@ -177,8 +178,26 @@ __global__ void __launch_bounds__(kPfThreads, 2) k_pf_tiles(PfTileArgs a) {
     // candidate list of row rr(i): cand_base + (8*(i/4) + i%4) * row_step
     const size_t row_step = (size_t)a.nranges * a.cap;
     const size_t cand_base = ((size_t)(rbase + q0 + 4 * g) * a.nranges + range) * a.cap;
-    const int64_t j0 = (int64_t)range * a.range_len;
-    const int64_t j1 = min(a.nkeys, j0 + a.range_len);
+    // Candidate mode: the ranges split the causal span of this workgroup's 128
+    // queries, [0, largest q_pos], not the whole context, so every query's
+    // candidates spread over all of its lists wherever the chunk sits.
+    int64_t range_len = a.range_len;
+    if constexpr (!DENSE) {
+        int32_t tmax = -1;
+        for (int u = lane; u < kPfRows; u += kWave) {
+            const int qi = qt * kPfRows + u;
+            if (qi < a.Q) {
+                const int64_t pq = a.q_pos ? a.q_pos[rbase + qi] : a.N - 1;
+                tmax = max(tmax, (int32_t)(pq < 0 ? -1 : (pq >= a.N ? a.N - 1 : pq)));
+            }
+        }
+        for (int o = 32; o >= 1; o >>= 1) tmax = max(tmax, __shfl_xor(tmax, o));
+        const int64_t span = min(a.nkeys, (int64_t)tmax + 1);
+        range_len = (span + a.nranges - 1) / a.nranges;
+        range_len = (range_len + kPfKeys - 1) / kPfKeys * kPfKeys;
+    }
+    const int64_t j0 = (int64_t)range * range_len;
+    const int64_t j1 = min(a.nkeys, j0 + range_len);
     const int64_t ntile = j1 > j0 ? (j1 - j0 + kPfKeys - 1) / kPfKeys : 0;
 
     // Loads are unconditional (a tile past the range reloads the last one) so
@@ -457,8 +476,7 @@ k_pf_verify(int64_t rows, int32_t nranges, int32_t cap, const uint32_t* __restri
     const bool ok = !overflow && (total == valid || (n == (uint32_t)K && sk > thr[2 * r + 1]));
     if (!ok) {
         const uint32_t slot = atomicAdd(repair_count, 1u);
-        if (slot < (uint32_t)repair_cap) repair_rows[slot] = (int32_t)r;
-        else __hip_atomic_fetch_or(status, kStatusRepairOverflow, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (slot < (uint32_t)repair_cap) repair_rows[slot] = (int32_t)r;   // the queue holds every row
     }
 }
 
@@ -468,6 +486,176 @@ __global__ void k_pf_repair_map(const int32_t* __restrict__ repair_rows, const u
                                 int32_t first, int32_t n, int32_t* __restrict__ map) {
     const int i = threadIdx.x;
     if (i < n) map[i] = (uint32_t)(first + i) < *repair_count ? repair_rows[first + i] : -1;
+}
+
+// ------------------------------------------------- exact repair, any count
+
+// Queued queries past the fast repair pass (queue slots first .. count-1):
+// one workgroup per query, grid-stride over the queue, so every queued query
+// gets its exact top-K whatever the count (a count within the fast pass makes
+// this kernel return at once). A query's exact scores over its causal range
+// [0, q_pos] are recomputed in each of four passes instead of being stored:
+// three radix passes (11, 11, 10 key bits) narrow the threshold key T and the
+// number of keys equal to T to take, and the last pass writes the selected
+// positions in ascending order (keys above T, then the lowest-positioned
+// keys equal to T), then -1 padding. Only degenerate inputs (mass ties at a
+// query's threshold) queue more queries than the fast pass holds.
+constexpr int kRepThreads = 512;
+constexpr int kRepQuads = kRepThreads / 4;
+constexpr int kRepU = 8;                        // keys per quad in flight
+constexpr int kRepTile = kRepQuads * kRepU;     // keys per iteration
+
+// Bin holding the need-th largest key of a 2048-bin histogram (counted from
+// the top): returns the bin; `above` = keys in higher bins. need >= 1 and
+// the histogram holds at least need keys.
+__device__ uint32_t rep_find(const uint32_t* hist, int nb, uint32_t need, uint32_t& above, uint32_t* sm) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    constexpr int kPer = 2048 / kRepThreads;
+    // thread t owns bins nb-1-kPer*t .. nb-kPer*(t+1) (top down); nb <= 2048
+    uint32_t c[kPer], tot = 0;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        const int b = nb - 1 - kPer * tid - i;
+        c[i] = b >= 0 ? hist[b] : 0u;
+        tot += c[i];
+    }
+    const uint32_t inc = wave_incl_scan(tot);
+    if (lane == 63) sm[wave] = inc;
+    __syncthreads();
+    uint32_t before = inc - tot;
+    for (int w = 0; w < wave; ++w) before += sm[w];
+    uint32_t run = before;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        const int b = nb - 1 - kPer * tid - i;
+        if (b >= 0 && run < need && run + c[i] >= need) {
+            sm[16] = (uint32_t)b;
+            sm[17] = run;
+        }
+        run += c[i];
+    }
+    __syncthreads();
+    const uint32_t bin = sm[16];
+    above = sm[17];
+    __syncthreads();
+    return bin;
+}
+
+template <int KT>
+__global__ void __launch_bounds__(kRepThreads)
+k_pf_repair_rest(const uint16_t* __restrict__ q, const uint8_t* __restrict__ k, int64_t N, int32_t Q,
+                 const int64_t* __restrict__ q_pos, const int32_t* __restrict__ repair_rows,
+                 const uint32_t* __restrict__ repair_count, int32_t first, int32_t K, int32_t* __restrict__ idx_out) {
+    using KS = KeySlice<KT, kPfDim, kBF16>;
+    __shared__ uint32_t hist[2048];
+    __shared__ uint32_t sm[32];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int quad = tid >> 2, lq = tid & 3;
+    const uint32_t count = *repair_count;
+    for (uint32_t slot = (uint32_t)first + blockIdx.x; slot < count; slot += gridDim.x) {
+        const int64_t row = repair_rows[slot];
+        const int64_t seq = row / Q;
+        const int64_t pq = q_pos ? q_pos[row] : N - 1;
+        const int64_t L = pq < 0 ? 0 : (pq >= N ? N : pq + 1);
+        double qd[kPfDim / 4];
+        load_query_slice<kBF16, kPfDim>(q + row * kPfDim, lq, qd);
+        const uint8_t* kb = k + (size_t)seq * N * KS::ROW_BYTES;
+        // keys[u] of this quad: position base + u * kRepQuads + quad (0 = padding / not selectable)
+        auto scan = [&](auto&& visit) {
+            for (int64_t base = 0; base < L; base += kRepTile) {
+                KS sl[kRepU];
+#pragma unroll
+                for (int u = 0; u < kRepU; ++u) {
+                    const int64_t t = base + u * kRepQuads + quad;
+                    if (t < L) sl[u].load(kb + t * KS::ROW_BYTES, lq);
+                    else for (int j = 0; j < KS::RAW; ++j) sl[u].raw[j] = make_uint4(0, 0, 0, 0);
+                }
+#pragma unroll
+                for (int u = 0; u < kRepU; ++u) {
+                    const int64_t t = base + u * kRepQuads + quad;
+                    const auto v = quad_sum(sl[u].dot(qd));
+                    visit(t, t < L ? score_key(round_score(v)) : 0u, u);
+                }
+            }
+        };
+        // ---- pass 1: top 11 bits, and the number of selectable keys
+        for (int i = tid; i < 2048; i += kRepThreads) hist[i] = 0u;
+        if (tid == 0) sm[18] = 0u;
+        __syncthreads();
+        uint32_t nvalid = 0;
+        scan([&](int64_t, uint32_t key, int) {
+            if (lq == 0 && key) {
+                atomicAdd(&hist[key >> 21], 1u);
+                ++nvalid;
+            }
+        });
+        atomicAdd(&sm[18], nvalid);
+        __syncthreads();
+        const uint32_t need = min((uint32_t)K, sm[18]);
+        uint32_t T = 0xFFFFFFFFu, take_eq = 0;
+        if (need > 0) {
+            uint32_t above = 0, rem = need;
+            const uint32_t b1 = rep_find(hist, 2048, rem, above, sm);
+            rem -= above;
+            // ---- pass 2: bits 10..20 of the keys in bin b1
+            for (int i = tid; i < 2048; i += kRepThreads) hist[i] = 0u;
+            __syncthreads();
+            scan([&](int64_t, uint32_t key, int) {
+                if (lq == 0 && key && (key >> 21) == b1) atomicAdd(&hist[(key >> 10) & 0x7FFu], 1u);
+            });
+            __syncthreads();
+            const uint32_t b2 = rep_find(hist, 2048, rem, above, sm);
+            rem -= above;
+            const uint32_t pre = (b1 << 11) | b2;
+            // ---- pass 3: bits 0..9 of the keys with that 22-bit prefix
+            for (int i = tid; i < 2048; i += kRepThreads) hist[i] = 0u;
+            __syncthreads();
+            scan([&](int64_t, uint32_t key, int) {
+                if (lq == 0 && key && (key >> 10) == pre) atomicAdd(&hist[key & 0x3FFu], 1u);
+            });
+            __syncthreads();
+            const uint32_t b3 = rep_find(hist, 1024, rem, above, sm);
+            rem -= above;
+            T = (pre << 10) | b3;
+            take_eq = rem;                      // keys equal to T to take, lowest positions first
+        }
+        // ---- pass 4: selected positions in ascending order
+        int32_t* orow = idx_out + row * (int64_t)K;
+        uint32_t run_sel = 0, run_eq = 0;       // over the positions already visited (uniform)
+        if (need > 0) {
+            scan([&](int64_t t, uint32_t key, int) {
+                // positions of this step are base + u*kRepQuads + quad: ascending in (quad) for fixed u
+                const bool is_eq = lq == 0 && key == T;
+                const uint64_t me = __ballot(is_eq);
+                if (lane == 63) sm[wave] = (uint32_t)__popcll(me);
+                __syncthreads();
+                uint32_t eq_before = run_eq, eq_tot = 0;
+                for (int w = 0; w < kRepThreads / 64; ++w) {
+                    if (w < wave) eq_before += sm[w];
+                    eq_tot += sm[w];
+                }
+                eq_before += lanes_below(me);
+                // eq_before: this key's rank among the keys equal to T, in position order
+                const bool sel = lq == 0 && key != 0u && (key > T || (is_eq && eq_before < take_eq));
+                __syncthreads();
+                const uint64_t ms = __ballot(sel);
+                if (lane == 63) sm[wave] = (uint32_t)__popcll(ms);
+                __syncthreads();
+                uint32_t sel_before = run_sel, sel_tot = 0;
+                for (int w = 0; w < kRepThreads / 64; ++w) {
+                    if (w < wave) sel_before += sm[w];
+                    sel_tot += sm[w];
+                }
+                sel_before += lanes_below(ms);
+                if (sel && sel_before < (uint32_t)K) orow[sel_before] = (int32_t)t;
+                run_sel += sel_tot;
+                run_eq += eq_tot;
+                __syncthreads();
+            });
+        }
+        for (int i = (int)need + tid; i < K; i += kRepThreads) orow[i] = -1;
+        __syncthreads();
+    }
 }
 
 // ------------------------------------------------------------------- host
@@ -538,6 +726,22 @@ int launch_pf_verify(int64_t rows, int32_t nranges, int32_t cap, const uint32_t*
                        thr, q_pos, N, K, repair_rows, repair_count, repair_cap, status);
     const hipError_t e = hipGetLastError();
     return e == hipSuccess ? OK : hip_fail(e, "launch k_pf_verify");
+}
+
+int launch_pf_repair_rest(const uint16_t* q, const uint8_t* k, int k_dtype, int64_t N, int32_t Q,
+                          const int64_t* q_pos, const int32_t* repair_rows, const uint32_t* repair_count, int32_t first,
+                          int32_t K, int32_t* idx_out, hipStream_t stream) {
+    DeviceInfo di;
+    if (int e = device_info(&di)) return e;
+    const dim3 grid((unsigned)(di.num_cus > 0 ? di.num_cus : 1));
+    if (k_dtype == kE4M3)
+        hipLaunchKernelGGL(k_pf_repair_rest<kE4M3>, grid, dim3(kRepThreads), 0, stream, q, k, N, Q, q_pos, repair_rows,
+                           repair_count, first, K, idx_out);
+    else
+        hipLaunchKernelGGL(k_pf_repair_rest<kBF16>, grid, dim3(kRepThreads), 0, stream, q, k, N, Q, q_pos, repair_rows,
+                           repair_count, first, K, idx_out);
+    const hipError_t e = hipGetLastError();
+    return e == hipSuccess ? OK : hip_fail(e, "launch k_pf_repair_rest");
 }
 
 int launch_pf_repair_map(const int32_t* repair_rows, const uint32_t* repair_count, int32_t first, int32_t n,

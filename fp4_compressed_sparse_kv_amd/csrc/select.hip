@@ -115,7 +115,7 @@ struct SrcScan {
     static constexpr bool kPosLds = false;       // position = index
     __device__ __forceinline__ int fill(int64_t row, int64_t begin, int cnt, int cpad, uint32_t* keys,
                                         uint32_t* hist, uint32_t*) const {
-        using KS = KeySlice<KT, D>;
+        using KS = KeySlice<KT, D, QT>;
         constexpr int QB = (QT == kBF16) ? 2 : 4;
         constexpr int U = KS::RAW >= 4 ? 1 : 4 / KS::RAW;   // 64 bytes in flight per lane
         const int quad = threadIdx.x >> 2, lq = threadIdx.x & 3;
@@ -153,17 +153,17 @@ struct SrcScan {
                                                          kr, (bi * kB + u * 256) * KS::ROW_BYTES + qoff, 0, kStreaming));
             };
             auto score_batch = [&](const uint4 (&r)[4], int base, bool masked) {
-                double acc[4];
+                typename KS::Part acc[4];
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
                     KS sl;
                     sl.raw[0] = r[u];
                     acc[u] = sl.dot(qd);
                 }
-                const double v = quad_transpose_sum(acc, lq);
+                const auto v = quad_transpose_sum(acc, lq);
                 const int i = base + lq * 256 + quad;
-                if (!masked) put_key(keys, hist, i, score_key((float)v));
-                else if (i < cnt) put_key(keys, hist, i, (i < lim) ? score_key((float)v) : 0u);
+                if (!masked) put_key(keys, hist, i, score_key(round_score(v)));
+                else if (i < cnt) put_key(keys, hist, i, (i < lim) ? score_key(round_score(v)) : 0u);
             };
             if (nfull > 0) {
                 uint4 ra[4], rb[4], rc[4];
@@ -205,8 +205,8 @@ struct SrcScan {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int i = base + u * (kSelThreads / 4) + quad;
-                const double v = quad_sum(s[u].dot(qd));
-                if (lq == 0 && i < cnt) put_key(keys, hist, i, (i < lim) ? score_key((float)v) : 0u);
+                const auto v = quad_sum(s[u].dot(qd));
+                if (lq == 0 && i < cnt) put_key(keys, hist, i, (i < lim) ? score_key(round_score(v)) : 0u);
             }
         }
         pad_keys(keys, cnt, cpad);
@@ -227,7 +227,7 @@ struct SrcPool {
     static constexpr bool kPosLds = true;        // positions come from the pool: kept in LDS when they fit
     __device__ __forceinline__ int fill(int64_t row, int64_t begin, int cnt, int cpad, uint32_t* keys,
                                         uint32_t* hist, uint32_t* posl) const {
-        using KS = KeySlice<KT, D>;
+        using KS = KeySlice<KT, D, QT>;
         constexpr int QB = (QT == kBF16) ? 2 : 4;
         constexpr int U = KS::RAW >= 4 ? 1 : 4 / KS::RAW;
         const int quad = threadIdx.x >> 2, lq = threadIdx.x & 3;
@@ -249,24 +249,24 @@ struct SrcPool {
             }
             if constexpr (U == 4) {
                 // transposed quad reduction: lane lq ends with the sum of slot lq's key
-                double acc[4];
+                typename KS::Part acc[4];
 #pragma unroll
                 for (int u = 0; u < 4; ++u) acc[u] = s[u].dot(qd);
-                const double v = quad_transpose_sum(acc, lq);
+                const auto v = quad_transpose_sum(acc, lq);
                 const int i = base + lq * (kSelThreads / 4) + quad;
                 const bool okl = lq == 0 ? ok[0] : lq == 1 ? ok[1] : lq == 2 ? ok[2] : ok[3];
                 const int32_t pvl = lq == 0 ? pv[0] : lq == 1 ? pv[1] : lq == 2 ? pv[2] : pv[3];
                 if (i < cnt) {
-                    put_key(keys, hist, i, okl ? score_key((float)v) : 0u);
+                    put_key(keys, hist, i, okl ? score_key(round_score(v)) : 0u);
                     if (posl) posl[i] = (uint32_t)pvl;
                 }
             } else {
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
                     const int i = base + u * (kSelThreads / 4) + quad;
-                    const double v = quad_sum(s[u].dot(qd));
+                    const auto v = quad_sum(s[u].dot(qd));
                     if (lq == 0 && i < cnt) {
-                        put_key(keys, hist, i, ok[u] ? score_key((float)v) : 0u);
+                        put_key(keys, hist, i, ok[u] ? score_key(round_score(v)) : 0u);
                         if (posl) posl[i] = (uint32_t)pv[u];
                     }
                 }
@@ -305,7 +305,7 @@ struct SrcCand {
     static constexpr bool kPosLds = true;        // positions come from the lists: kept in LDS when they fit
     __device__ __forceinline__ int fill(int64_t row, int64_t begin, int cnt_, int cpad, uint32_t* keys,
                                         uint32_t* hist, uint32_t* posl) const {
-        using KS = KeySlice<KT, D>;
+        using KS = KeySlice<KT, D, QT>;
         constexpr int QB = (QT == kBF16) ? 2 : 4;
         constexpr int U = KS::RAW >= 4 ? 2 : 8 / KS::RAW;
         constexpr int kMaxLists = 16;
@@ -363,22 +363,22 @@ struct SrcCand {
                     // two groups of four slots, transposed quad reduction: lane lq writes slot 4h + lq
                     auto group = [&](const KS& a, const KS& b, const KS& c, const KS& d, int32_t p0, int32_t p1,
                                      int32_t p2, int32_t p3, int h) {
-                        const double acc[4] = {a.dot(qd), b.dot(qd), c.dot(qd), d.dot(qd)};
-                        const double sv = quad_transpose_sum(acc, lq);
+                        const typename KS::Part acc[4] = {a.dot(qd), b.dot(qd), c.dot(qd), d.dot(qd)};
+                        const auto sv = quad_transpose_sum(acc, lq);
                         const int32_t p = lq == 0 ? p0 : lq == 1 ? p1 : lq == 2 ? p2 : p3;
                         const uint32_t v = base + (4 * h + lq) * (kSelThreads / 4) + quad;
                         if (v < total)          // an entry without a valid position is padding (key 0)
-                            put_key(keys, hist, (int)v, (p >= 0 && (int64_t)p < N) ? score_key((float)sv) : 0u);
+                            put_key(keys, hist, (int)v, (p >= 0 && (int64_t)p < N) ? score_key(round_score(sv)) : 0u);
                     };
                     group(sk[0], sk[1], sk[2], sk[3], pv[0], pv[1], pv[2], pv[3], 0);
                     group(sk[4], sk[5], sk[6], sk[7], pv[4], pv[5], pv[6], pv[7], 1);
                 } else {
 #pragma unroll
                     for (int u = 0; u < U; ++u) {
-                        const double sv = quad_sum(sk[u].dot(qd));
+                        const auto sv = quad_sum(sk[u].dot(qd));
                         const uint32_t v = base + u * (kSelThreads / 4) + quad;
                         if (lq == 0 && v < total)
-                            put_key(keys, hist, (int)v, (pv[u] >= 0 && (int64_t)pv[u] < N) ? score_key((float)sv) : 0u);
+                            put_key(keys, hist, (int)v, (pv[u] >= 0 && (int64_t)pv[u] < N) ? score_key(round_score(sv)) : 0u);
                     }
                 }
             }
@@ -415,16 +415,16 @@ struct SrcCand {
             }
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const double sv = quad_sum(s[u].dot(qd));
+                const auto sv = quad_sum(s[u].dot(qd));
                 const uint32_t v = base + u * (kSelThreads / 4) + quad;
                 if (lq != 0) continue;
                 if (dense) {
                     if (v < total) {            // an entry without a valid position is padding (key 0)
-                        put_key(keys, hist, (int)v, ent[u] >= 0 ? score_key((float)sv) : 0u);
+                        put_key(keys, hist, (int)v, ent[u] >= 0 ? score_key(round_score(sv)) : 0u);
                         posl[v] = (uint32_t)pv[u];
                     }
                 } else if (ent[u] >= 0) {
-                    put_key(keys, hist, ent[u], score_key((float)sv));
+                    put_key(keys, hist, ent[u], score_key(round_score(sv)));
                 }
             }
         }

@@ -189,8 +189,8 @@ int csa2_topk(const float* scores, int64_t rows, int64_t n, int64_t score_stride
  * CSA2とFP4: dequantize before attention).
  *
  * R: all H query heads share the one KV head and one position list; logits
- * are (q_h . K_j) * softmax_scale; no mask beyond the position list; a query
- * whose list has no valid position gets zeros.
+ * are (q_h . K_j) * softmax_scale (0 selects 1/sqrt(d)); no mask beyond the
+ * position list; a query whose list has no valid position gets zeros.
  *
  *   q          device [B][Q][H][d] bf16 bit patterns
  *   H          1..16 query heads;  d = 128
@@ -202,9 +202,11 @@ int csa2_topk(const float* scores, int64_t rows, int64_t n, int64_t score_stride
  * Alignment: code pointers and code_stride_bytes to 16 bytes; scale
  * pointers and scale_stride_bytes to 8 bytes (each position's 8 K and 8 V
  * scale bytes are read as one 8-byte word each).
- * Numerics: the query is used in f16 (exact for |q| in [2^-14, 65504]), the
- * dequantized K and V are exact in f16, each softmax weight is carried as
- * two f16 terms (about 22 significant bits), products accumulate in fp32.
+ * Numerics: each head's query is scaled by a power of two into f16 range
+ * (exact for every element within 2^28 of the head's largest |q|; any finite
+ * bf16 query is accepted), the dequantized K and V are exact in f16, each
+ * softmax weight is carried as two f16 terms (about 22 significant bits),
+ * products accumulate in fp32.
  */
 int csa2_sparse_attn_workspace_bytes(int32_t B, int32_t Q, int32_t H, int32_t d, int32_t K, size_t* bytes);
 int csa2_sparse_attn_fp4(const uint16_t* q, int32_t B, int32_t Q, int32_t H, int32_t d,
@@ -295,10 +297,9 @@ int csa2_plan_profile_read(csa2_plan* plan, float* avg_ms, int32_t* runs);
  * the indexer runs on the matrix cores and only nominates candidates; their
  * exact scores decide the top-K. A query whose result the candidates cannot
  * certify (ties or near-ties at its threshold, an overflowing candidate list)
- * is re-selected by an exact scan of its whole causal range, up to 64 such
- * queries per call; beyond that, bit 1 (value 2) of the workspace status word
- * is set and the remaining ones keep the candidate result, which is then not
- * guaranteed to be the exact top-K.
+ * is re-selected by an exact scan of its whole causal range: every such
+ * query, however many (beyond 64 per call this fallback is slow: one
+ * workgroup per query). The result is always the exact top-K.
  */
 int csa2_prefill_workspace_bytes(const csa2_plan* plan, int32_t B, int32_t Q, int64_t N, size_t* bytes);
 int csa2_prefill_full(const csa2_plan* plan, const csa2_cache* cache, const void* q_idx,

@@ -16,7 +16,9 @@ import torch
 import bench
 import fp4_compressed_sparse_kv_amd as C
 import synth
+from oracle import formats as F
 from oracle import plan as OP
+from oracle import quant as OQ
 from oracle import scores as OS
 from oracle.attention import sparse_attn as o_attn
 from oracle.topk import topk as o_topk
@@ -101,3 +103,38 @@ def test_prefill_full_size_sampled():
             err = max_rel_err_rows(out[b, i], o_attn(qb[b, i], oc, idx[b, i], SCALE))
             assert err <= ATTN_TOL, (b, i, err)
     print(f"prefill: top-K sets {stats}")
+
+
+@pytest.mark.timeout(900)
+def test_quant_dequant_full_size_sampled():
+    """kv_quant_fp4 and kv_dequant_fp4 over the whole 1,048,576 x 512 quantize workload in the benchmark's
+    launch configuration, compared bit for bit with the oracle on row blocks chosen so that every
+    grid-stride slot of both kernels is checked in its first and last pass: the quantizer's grid of
+    16,384 x 256 lanes takes two 16-group slots per pass (131,072 rows each) over four passes, the
+    dequantizer four half-group slots (65,536 rows each) over four passes."""
+    cfg = dict(synth.WORKLOADS["quant_1m_x512"])
+    T, Cc, rb = cfg["T"], cfg["C"], cfg["row_block"]
+    dev = torch.device("cuda", 0)
+    x = bench.build_quant_input(cfg, dev)
+    codes, scales = C.kv_quant_fp4(x)
+    y = C.kv_dequant_fp4(codes, scales, Cc)
+    torch.cuda.synchronize()
+    q_slot, dq_slot = 131072, 65536
+    rows = set()
+    for p in (0, 3):                                        # first and last pass
+        for k in range(2):
+            rows |= {(2 * p + k) * q_slot, (2 * p + k + 1) * q_slot - 1}
+        for k in range(4):
+            rows |= {(4 * p + k) * dq_slot, (4 * p + k + 1) * dq_slot - 1}
+    blocks = sorted({r // rb for r in rows if r < T})
+    assert blocks[0] == 0 and blocks[-1] == T // rb - 1
+    for blk in blocks:
+        xb = synth.quant_rows(cfg, blk)
+        rc, rs = OQ.quant_fp4(xb)
+        sl = slice(blk * rb, (blk + 1) * rb)
+        assert np.array_equal(host(scales[sl]), rs), blk
+        assert np.array_equal(host(codes[sl]), rc), blk
+        got = F.bf16_decode(host(y[sl].view(torch.int16)).view(np.uint16))
+        ref = OQ.dequant_fp4(rc, rs, Cc)
+        assert np.array_equal(got, ref) and np.array_equal(np.signbit(got), np.signbit(ref)), blk
+    print(f"quant full size: {len(blocks)} row blocks of {rb} bit-exact")

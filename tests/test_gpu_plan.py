@@ -273,12 +273,39 @@ def test_prefill_repair_pass_takes_lowest_positions_on_ties():
         assert np.array_equal(idx[0, i], np.arange(K)), i          # ties go to the lowest positions
 
 
-def test_prefill_reports_rows_beyond_the_repair_pass():
+def test_prefill_exact_for_every_queued_row():
+    """100 queries whose candidates cannot be certified (all scores tie) - more than the 64 the
+    multi-workgroup repair pass takes: every one still gets the exact top-K (ties to the lowest positions)."""
     cfg = synth.small("stack_b4_n1m", B=1, N=70001, K=256, modes=("full",))
-    N, Q = cfg["N"], 100                                            # 100 failing rows > 64 repair slots
+    N, K, Q = cfg["N"], cfg["K"], 100
     cache = _tied_cache(N)
-    q_pos = np.full((1, Q), N - 1, dtype=np.int64)
+    q_pos = np.stack([np.concatenate([np.full(60, N - 1), N - 1 - 997 * np.arange(1, 41)])]).astype(np.int64)
     qi, qb, qp = _prefill_inputs(cfg, 1, Q, q_pos)
     plan = make_plan(cfg)
-    plan.prefill_full(cache, dev_key(qi, "bf16"), dev_bf16(qb), qp)
-    assert plan.prefill_status(cache, Q) & 2
+    idx, _ = plan.prefill_full(cache, dev_key(qi, "bf16"), dev_bf16(qb), qp)
+    assert plan.prefill_status(cache, Q) == 0
+    idx = host(idx)
+    for i in range(Q):
+        assert np.array_equal(idx[0, i], np.arange(K)), i
+
+
+@pytest.mark.timeout(600)
+def test_prefill_early_positions_in_a_long_context():
+    """A chunk of queries at early positions of a 524,288-position cache (K = 2048): each query's
+    candidates spread over the key ranges of its own causal span, so no list overflows and every
+    query's top-K is exact without the repair fallback."""
+    cfg = synth.small("stack_b4_n1m", B=1, N=524288, K=2048, modes=("full",))
+    N, K, Q = cfg["N"], cfg["K"], 160
+    cache, _, ocache, _ = build_case(cfg)
+    rng = np.random.default_rng(11)
+    q_pos = np.sort(np.concatenate([[0, 1, 2047, 2048, 4095, 4096, 65535, 65536],
+                                    rng.integers(0, N // 4, Q - 8)]))[None].astype(np.int64)
+    qi, qb, qp = _prefill_inputs(cfg, 1, Q, q_pos)
+    plan = make_plan(cfg)
+    idx, _ = plan.prefill_full(cache, dev_key(qi, cfg["q_idx_dtype"]), dev_bf16(qb), qp)
+    assert plan.prefill_status(cache, Q) == 0
+    idx = host(idx)
+    for i in range(Q):
+        s = OS.index_scores(qi[0, i], cfg["q_idx_dtype"], ocache[0]["k_idx"], cfg["k_idx_dtype"], q_pos=int(q_pos[0, i]))
+        r_idx, _ = o_topk(s, K)
+        assert compare_topk(idx[0, i], r_idx, lambda p: s[p], K) == "exact", i

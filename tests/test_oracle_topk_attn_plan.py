@@ -160,3 +160,31 @@ def test_prefill_causal_and_last_query_equals_decode():
     assert (idx[0] >= 0).sum() == 6                 # only 6 positions visible to query 0
     dec = PL.run_decode(["full"], cache, [dict(layers[0], q=qb[2], q_idx=qi[2])], cfg["K"])
     assert np.array_equal(idx[2], dec[0]["idx"]) and np.array_equal(out[2], dec[0]["out"])
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_attention_bf16_rows_equals_quantized_planes(seed):
+    """The oracle's bf16-rows input (only the listed rows are quantized) against the stored-planes input
+    (the whole plane quantized first, then the listed rows dequantized): bit-identical outputs on ragged,
+    unsorted, repeating and padded position lists, and each gathered row equals the plane's row."""
+    rng = np.random.default_rng(seed)
+    N, H, d = 257, 5, 128
+    kb = synth.to_bf16_bits((rng.standard_normal((N, d)) * np.exp(rng.uniform(-6, 6, (N, 1)))).astype(np.float32))
+    vb = synth.to_bf16_bits((rng.standard_normal((N, d)) * 3).astype(np.float32))
+    kc, ks = Q.quant_fp4(kb)
+    vc, vs = Q.quant_fp4(vb)
+    planes = dict(k_codes=kc, k_scales=ks, v_codes=vc, v_scales=vs)
+    rows = dict(k_bf16=kb, v_bf16=vb)
+    qb = synth.to_bf16_bits(rng.standard_normal((H, d)).astype(np.float32))
+    lists = [rng.permutation(N)[:37], np.array([N - 1, 0, 3, 3, 200, -1, -1]), rng.integers(0, N, 129),
+             np.array([-1, 42, -1]), np.arange(N)[::-1]]
+    for idx in lists:
+        a = A.sparse_attn(qb, rows, idx)
+        b = A.sparse_attn(qb, planes, idx)
+        assert np.array_equal(a, b)
+        sel = idx[idx >= 0]
+        for which, plane in (("k", Q.dequant_fp4(kc, ks, d)), ("v", Q.dequant_fp4(vc, vs, d))):
+            assert np.array_equal(A.kv_rows(rows, which, sel, d), plane[sel])
+    # a one-position list returns that row of V exactly, from either input form
+    out = A.sparse_attn(qb, rows, np.array([-1, 77, -1]))
+    assert np.array_equal(out, np.broadcast_to(Q.dequant_fp4(vc, vs, d)[77], (H, d)))
