@@ -19,7 +19,7 @@ import torch
 __all__ = [
     "Csa2Error", "lib", "F32", "BF16", "E4M3", "FULL", "REINDEX", "REUSE",
     "kv_quant_fp4", "kv_dequant_fp4", "index_full", "index_reindex", "topk",
-    "sparse_attn_fp4", "KVCache", "Plan", "status_word",
+    "sparse_attn_fp4", "sparse_attn_fp4_noalloc", "KVCache", "Plan", "status_word",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcsa2.so")
@@ -62,6 +62,8 @@ _SIGS = {
     "csa2_sparse_attn_workspace_bytes": (ctypes.c_int, [_c_i32, _c_i32, _c_i32, _c_i32, _c_i32, ctypes.POINTER(_c_sz)]),
     "csa2_sparse_attn_fp4": (ctypes.c_int, [_vp, _c_i32, _c_i32, _c_i32, _c_i32, _vp, _vp, _vp, _vp, _c_i64, _c_i64,
                                             _c_i64, _vp, _c_i32, _c_f32, _vp, _vp, _c_sz, _vp]),
+    "csa2_sparse_attn_fp4_noalloc": (ctypes.c_int, [_vp, _c_i32, _c_i32, _c_i32, _c_i32, _vp, _vp, _vp, _vp, _c_i64,
+                                                    _c_i64, _c_i64, _vp, _c_i32, _c_f32, _vp, _vp]),
     "csa2_plan_create": (ctypes.c_int, [ctypes.POINTER(_c_i32), _c_i32, ctypes.POINTER(PlanParams),
                                         ctypes.POINTER(_vp)]),
     "csa2_plan_destroy": (None, [_vp]),
@@ -285,6 +287,22 @@ def sparse_attn_fp4(q, cache, idx, softmax_scale=None, out=None, stream=None, ws
     _check(lib().csa2_sparse_attn_fp4(_ptr(q), B, Q, H, d, c.k_codes, c.k_scales, c.v_codes, c.v_scales, cache.N,
                                       c.code_stride_bytes, c.scale_stride_bytes, _ptr(idx), K, scale, _ptr(out),
                                       _ptr(ws), ws.numel(), _stream(stream)), "csa2_sparse_attn_fp4")
+    return out
+
+
+def sparse_attn_fp4_noalloc(q, cache, idx, softmax_scale=None, out=None, stream=None):
+    """sparse_attn_fp4 through the library's allocation-free entry point (scratch in a fixed device
+    array; calls that may overlap on one device race)."""
+    _need_cuda(q, idx)
+    B, Q, H, d = q.shape
+    K = idx.shape[-1]
+    if out is None:
+        out = torch.empty(B, Q, H, d, dtype=torch.float32, device=q.device)
+    scale = 0.0 if softmax_scale is None else softmax_scale
+    c = cache.desc()
+    _check(lib().csa2_sparse_attn_fp4_noalloc(_ptr(q), B, Q, H, d, c.k_codes, c.k_scales, c.v_codes, c.v_scales,
+                                              cache.N, c.code_stride_bytes, c.scale_stride_bytes, _ptr(idx), K, scale,
+                                              _ptr(out), _stream(stream)), "csa2_sparse_attn_fp4_noalloc")
     return out
 
 

@@ -104,6 +104,10 @@ int check_scan(const void* q_idx, int32_t q_dtype, const void* k_idx, int32_t k_
     return OK;
 }
 
+}  // namespace
+
+namespace csa2 {
+
 int check_attn(const uint16_t* q, int32_t H, int32_t d, const uint8_t* kc, const uint8_t* ks, const uint8_t* vc,
                const uint8_t* vs, int64_t N, int64_t cs, int64_t ss, int32_t K, const char* who) {
     const std::string w(who);
@@ -121,7 +125,7 @@ int check_attn(const uint16_t* q, int32_t H, int32_t d, const uint8_t* kc, const
     return OK;
 }
 
-}  // namespace
+}  // namespace csa2
 
 extern "C" {
 

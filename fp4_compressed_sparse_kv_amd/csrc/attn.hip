@@ -535,21 +535,25 @@ k_sparse_attn(const uint16_t* __restrict__ q, int32_t rows_per_seq, int32_t H, c
     if (tid == 0) st_rlx(ctr, 0u);              // ready for the next launch
 }
 
-int launch_attn(const AttnArgs& a, void* ws_ctrl, void* ws_data, size_t data_bytes, hipStream_t stream) {
+int launch_attn_scratch(const AttnArgs& a, uint32_t* counters, void* parts, size_t parts_bytes, hipStream_t stream) {
     if (a.rows == 0) return OK;
     const AttnShape sh = attn_shape(a.rows, a.K);
     const int ns = sh.ns;
-    if (data_bytes < attn_data_bytes(a.rows, a.K)) return fail(WORKSPACE, "attention workspace too small");
+    if (parts_bytes < attn_data_bytes(a.rows, a.K)) return fail(WORKSPACE, "attention workspace too small");
     if (ns > 1 && a.rows > kAttnCtrlWords) return fail(INVALID, "attention: split rows exceed the counter table");
     const int64_t groups = a.rows * ns;
     if (groups > 0x7FFFFFFFll) return fail(INVALID, "attention: too many query rows");
-    uint32_t* counters = reinterpret_cast<uint32_t*>(ws_ctrl) + kAttnCtrlOffsetWords;
     auto fn = sh.waves == 4 ? k_sparse_attn<4> : k_sparse_attn<8>;
     hipLaunchKernelGGL(fn, dim3((unsigned)groups), dim3(sh.waves * kWave), 0, stream, a.q, a.rows_per_seq,
                        a.H, a.k_codes, a.k_scales, a.v_codes, a.v_scales, a.N, a.code_stride, a.scale_stride, a.idx,
-                       a.idx_stride, a.K, a.scale, a.out, ns, counters, reinterpret_cast<float*>(ws_data), a.rows);
+                       a.idx_stride, a.K, a.scale, a.out, ns, counters, reinterpret_cast<float*>(parts), a.rows);
     const hipError_t e = hipGetLastError();
     return e == hipSuccess ? OK : hip_fail(e, "launch k_sparse_attn");
+}
+
+int launch_attn(const AttnArgs& a, void* ws_ctrl, void* ws_data, size_t data_bytes, hipStream_t stream) {
+    return launch_attn_scratch(a, reinterpret_cast<uint32_t*>(ws_ctrl) + kAttnCtrlOffsetWords, ws_data, data_bytes,
+                               stream);
 }
 
 }  // namespace csa2

@@ -170,5 +170,12 @@ struct AttnArgs {
 };
 size_t attn_data_bytes(int64_t rows, int32_t K);     // data region of one attention call
 int launch_attn(const AttnArgs& a, void* ws_ctrl, void* ws_data, size_t data_bytes, hipStream_t stream);
+// The same with the merge counters (kAttnCtrlWords words, zero between calls) and the partial
+// states given directly.
+int launch_attn_scratch(const AttnArgs& a, uint32_t* counters, void* parts, size_t parts_bytes, hipStream_t stream);
+
+// Host-side argument checks of the attention call (api.cpp).
+int check_attn(const uint16_t* q, int32_t H, int32_t d, const uint8_t* kc, const uint8_t* ks, const uint8_t* vc,
+               const uint8_t* vs, int64_t N, int64_t cs, int64_t ss, int32_t K, const char* who);
 
 }  // namespace csa2

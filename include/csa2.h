@@ -216,6 +216,32 @@ int csa2_sparse_attn_fp4(const uint16_t* q, int32_t B, int32_t Q, int32_t H, int
                          const int32_t* idx, int32_t K, float softmax_scale,
                          float* out, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/*
+ * csa2_sparse_attn_fp4_noalloc - csa2_sparse_attn_fp4 for callers that cannot
+ * allocate device memory or pass a workspace: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation. Same arguments,
+ * semantics and results (bit-identical outputs) without ws / ws_bytes.
+ *
+ * Scratch: a fixed device array inside the library (4,260,864 bytes per
+ * device, held until the process ends): 256 merge counters and up to 511
+ * partial softmax states, which covers every shape this call accepts (rows
+ * split over several workgroups times their splits stay below 512); a shape
+ * that would need more is rejected with CSA2_ERR_WORKSPACE. The array's
+ * device address is looked up on the first call on each device (that call
+ * also enqueues a small kernel clearing the counters); the call itself never
+ * allocates or frees memory.
+ * Concurrency: every call on one device shares that device's array and the
+ * counters must be zero when a call starts (each completed call leaves them
+ * zero), so calls that may overlap on one device - on two streams or from two
+ * host threads - race; the caller must order them.
+ */
+int csa2_sparse_attn_fp4_noalloc(const uint16_t* q, int32_t B, int32_t Q, int32_t H, int32_t d,
+                                 const uint8_t* k_codes, const uint8_t* k_scales,
+                                 const uint8_t* v_codes, const uint8_t* v_scales,
+                                 int64_t N, int64_t code_stride_bytes, int64_t scale_stride_bytes,
+                                 const int32_t* idx, int32_t K, float softmax_scale,
+                                 float* out, hipStream_t stream);
+
 /* ---------------------------------------------------------------------------
  * Layer plan - S6: a static per-layer mode table ([zaikei] CSA2とFP4: each
  * CSA2 layer is fixed to Full, Reindex or Reuse; [jiwasawa] CSA2: modes are

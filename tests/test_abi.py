@@ -82,6 +82,12 @@ def test_topk_and_attn_validation():
          1, "softmax_scale")
     sz = ctypes.c_size_t(0)
     _err(L.csa2_sparse_attn_workspace_bytes(1, 1, 0, 128, 4, ctypes.byref(sz)), 1, "bad sizes")
+    # the allocation-free variant checks the same arguments on the host before any HIP call
+    _err(L.csa2_sparse_attn_fp4_noalloc(p, 1, 1, 17, 128, p, p, p, p, 10, 128, 16, p, 4, 0.1, p, None), 1, "H must")
+    _err(L.csa2_sparse_attn_fp4_noalloc(p, 1, 1, 8, 128, p, p, p, p, 10, 128, 16, None, 4, 0.1, p, None), 1, "null")
+    _err(L.csa2_sparse_attn_fp4_noalloc(p, 1, 1, 8, 128, p, p, p, p, 10, 128, 16, p, 4, float("nan"), p, None),
+         1, "softmax_scale")
+    assert L.csa2_sparse_attn_fp4_noalloc(p, 0, 1, 8, 128, p, p, p, p, 10, 128, 16, p, 4, 0.0, p, None) == 0
 
 
 def _plan(modes, **kw):
