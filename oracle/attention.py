@@ -13,13 +13,19 @@ Everything in fp64.
 import numpy as np
 
 from .formats import bf16_decode
+from .mxfp4 import dequant_mxfp4, quant_mxfp4
 from .quant import dequant_fp4, quant_fp4
 
+# KV storage formats: FP4 E2M1 with an E4M3 scale per 16 channels ([ezic] key
+# points), or MXFP4 with an E8M0 scale per 32 channels ([jiwasawa] FP4 main KV).
+FORMATS = {"fp4_e4m3": (quant_fp4, dequant_fp4, 16), "mxfp4": (quant_mxfp4, dequant_mxfp4, 32)}
 
-def dequant_rows(codes, scales, rows, C):
-    """Dequantize only the listed rows of a (codes [N][>=C/2], scales [N][>=C/16]) plane."""
+
+def dequant_rows(codes, scales, rows, C, fmt="fp4_e4m3"):
+    """Dequantize only the listed rows of a (codes [N][>=C/2], scales [N][>=C/block]) plane."""
+    _, deq, blk = FORMATS[fmt]
     rows = np.asarray(rows, dtype=np.int64)
-    return dequant_fp4(np.asarray(codes)[rows][:, : C // 2], np.asarray(scales)[rows][:, : C // 16], C)
+    return deq(np.asarray(codes)[rows][:, : C // 2], np.asarray(scales)[rows][:, : C // blk], C)
 
 
 def kv_rows(kv, which, rows, C):
@@ -28,20 +34,24 @@ def kv_rows(kv, which, rows, C):
     The cache is given either as stored planes ('k_codes', 'k_scales', ...) or
     as the bf16 rows before quantization ('k_bf16', 'v_bf16'); in the second
     case only the listed rows are quantized here. Quantization works row by
-    row, so this equals quantizing the whole plane first.
+    row, so this equals quantizing the whole plane first. kv['format'] names
+    the storage format ('fp4_e4m3' when absent, or 'mxfp4').
     """
+    fmt = kv.get("format", "fp4_e4m3")
     if f"{which}_codes" in kv:
-        return dequant_rows(kv[f"{which}_codes"], kv[f"{which}_scales"], rows, C)
-    codes, scales = quant_fp4(np.asarray(kv[f"{which}_bf16"])[np.asarray(rows, dtype=np.int64)])
-    return dequant_fp4(codes, scales, C)
+        return dequant_rows(kv[f"{which}_codes"], kv[f"{which}_scales"], rows, C, fmt)
+    quant, deq, _ = FORMATS[fmt]
+    codes, scales = quant(np.asarray(kv[f"{which}_bf16"])[np.asarray(rows, dtype=np.int64)])
+    return deq(codes, scales, C)
 
 
 def sparse_attn(q_bits, kv, idx, softmax_scale=None):
     """One query.
 
     q_bits: (H, d) bf16 bit patterns. kv: dict with 'k_codes', 'k_scales',
-    'v_codes', 'v_scales' (planes over all N positions, [N][d/2] and [N][d/16]),
-    or 'k_bf16', 'v_bf16' (the rows before quantization; see kv_rows).
+    'v_codes', 'v_scales' (planes over all N positions, [N][d/2] and [N][d/16],
+    or [N][d/32] for 'format': 'mxfp4'), or 'k_bf16', 'v_bf16' (the rows before
+    quantization; see kv_rows).
     idx: (K,) positions, -1 = padding. Returns (H, d) fp64.
     """
     q = bf16_decode(q_bits)
