@@ -39,12 +39,13 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def alg_bytes(cfg):
+def alg_bytes(cfg, kv="fp4_e4m3"):
     """Algorithmic bytes of one step (per sequence sums x B) and of the Full selection kernel.
 
     Full    = 2*d_I + N*d_I*b_k + 4P (when a Reindex follows) + 4K + A
     Reindex = 2*d_I + 4P + P*d_I*b_k + 4K + A
-    Reuse   = A,  A = 4K + 2*H*d + K*2*(d/2 + d/16) + 4*H*d
+    Reuse   = A,  A = 4K + 2*H*d + K*2*(d/2 + d/g) + 4*H*d
+    with g = 16 channels per scale (E4M3 scales) or 32 (MXFP4).
     """
     B, N, K, H, d, dI = cfg["B"], cfg["N"], cfg["K"], cfg["H"], cfg["d"], cfg["d_idx"]
     P = cfg.get("P") or 0
@@ -52,7 +53,8 @@ def alg_bytes(cfg):
     bq = {"bf16": 2, "f32": 4}[cfg["q_idx_dtype"]]
     modes = list(cfg["modes"])
     has_re = "reindex" in modes
-    A = 4 * K + 2 * H * d + K * 2 * (d // 2 + d // 16) + 4 * H * d
+    g = 32 if kv == "mxfp4" else 16
+    A = 4 * K + 2 * H * d + K * 2 * (d // 2 + d // g) + 4 * H * d
     per_seq = 0
     full_sel = 0
     first_full = True
@@ -90,7 +92,7 @@ def measured_traffic(workload):
     return t.get("traffic_bytes_per_launch")
 
 
-def build_inputs(cfg, dev, query_set=0):
+def build_inputs(cfg, dev, query_set=0, kv="fp4_e4m3"):
     import numpy as np
     import torch
 
@@ -113,7 +115,7 @@ def build_inputs(cfg, dev, query_set=0):
     dI = cfg["d_idx"]
     kdt = {"e4m3": torch.uint8, "bf16": torch.int16, "f32": torch.float32}[cfg["k_idx_dtype"]]
     kidx = torch.empty(B, N, dI, dtype=kdt, device=dev)
-    cache = C.KVCache(B, N, device=dev)
+    cache = C.KVCache(B, N, device=dev, kv_format=kv)
     for b in range(B):
         kb, vb = synth.kv_bf16(cfg, b)
         cache.fill(bf(kb), bf(vb), row0=b * N)
@@ -187,7 +189,7 @@ def host_cores():
     return len(os.sched_getaffinity(0))
 
 
-def cpu_baseline(cfg, budget_s):
+def cpu_baseline(cfg, budget_s, kv="fp4_e4m3"):
     """The oracle, as it stands, on whole sequences of the same workload until ~budget_s of CPU work."""
     import numpy as np
     from threadpoolctl import threadpool_limits
@@ -202,7 +204,7 @@ def cpu_baseline(cfg, budget_s):
     with threadpool_limits(limits=cores):
         for b in range(cfg["B"]):
             kb, vb = synth.kv_bf16(cfg, b)                           # untimed: input generation
-            cache = dict(k_bf16=kb, v_bf16=vb, k_idx=synth.k_idx(cfg, b), k_idx_dtype=cfg["k_idx_dtype"])
+            cache = dict(k_bf16=kb, v_bf16=vb, k_idx=synth.k_idx(cfg, b), k_idx_dtype=cfg["k_idx_dtype"], format=kv)
             layers = [dict(q=synth.q_bf16(cfg, li, b)[0], q_idx=synth.q_idx(cfg, li, b)[0],
                            q_idx_dtype=cfg["q_idx_dtype"]) for li in range(len(modes))]
             t0 = time.perf_counter()
@@ -242,14 +244,19 @@ def run_quant(args, cfg, dev):
 
     import fp4_compressed_sparse_kv_amd as C
     import synth
+    from oracle import mxfp4 as OM
     from oracle import quant as OQ
 
+    mx = args.kv == "mxfp4"
     T, Cc, rb = cfg["T"], cfg["C"], cfg["row_block"]
+    blk = 32 if mx else 16
+    quant, dequant = (C.kv_quant_mxfp4, C.kv_dequant_mxfp4) if mx else (C.kv_quant_fp4, C.kv_dequant_fp4)
+    oquant = OM.quant_mxfp4 if mx else OQ.quant_fp4
     t0 = time.perf_counter()
     x = build_quant_input(cfg, dev)
     log(f"inputs ready in {time.perf_counter() - t0:.1f} s")
     codes = torch.empty(T, Cc // 2, dtype=torch.uint8, device=dev)
-    scales = torch.empty(T, Cc // 16, dtype=torch.uint8, device=dev)
+    scales = torch.empty(T, Cc // blk, dtype=torch.uint8, device=dev)
     y = torch.empty_like(x)
     stream = torch.cuda.current_stream()
 
@@ -265,22 +272,25 @@ def run_quant(args, cfg, dev):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / args.steps
 
-    q_ms = timed(lambda: C.kv_quant_fp4(x, codes, scales))
-    d_ms = timed(lambda: C.kv_dequant_fp4(codes, scales, Cc, y))
-    nbytes = T * Cc * 2 + T * (Cc // 2 + Cc // 16)            # bf16 rows + codes + scales, each direction
-    groups = T * Cc // 16
+    q_ms = timed(lambda: quant(x, codes, scales))
+    d_ms = timed(lambda: dequant(codes, scales, Cc, y))
+    nbytes = T * Cc * 2 + T * (Cc // 2 + Cc // blk)           # bf16 rows + codes + scales, each direction
+    groups = T * Cc // blk
     s_zero = int((scales == 0).sum().item())
-    s_sat = int((scales == 0x7E).sum().item())
+    s_sat = int((scales == 0x7E).sum().item()) if not mx else None
     out = {
-        "metric": "kv_quant_fp4 HBM GB/s (bf16 rows in, FP4 codes + E4M3 scales out)",
+        "metric": ("kv_quant_mxfp4 HBM GB/s (bf16 rows in, FP4 codes + E8M0 scales out)" if mx else
+                   "kv_quant_fp4 HBM GB/s (bf16 rows in, FP4 codes + E4M3 scales out)"),
         "value": round(nbytes / (q_ms * 1e-3) / 1e9, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(q_ms, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32 compares / u8", "data": "synthetic",
-        "config": {"workload": args.workload, "T": T, "C": Cc},
+        "config": {"workload": args.workload + (":mxfp4" if mx else ""), "T": T, "C": Cc,
+                   "kv": "mxfp4 (e2m1 + e8m0 per 32 ch)" if mx else "fp4_e2m1 + e4m3 scale per 16 ch"},
         "rows_per_s": round(T / (q_ms * 1e-3), 1),
         "dequant_ms": round(d_ms, 5), "dequant_gbs": round(nbytes / (d_ms * 1e-3) / 1e9, 1),
         "alg_bytes_per_call": nbytes, "groups": groups, "groups_scale_zero": s_zero, "groups_scale_448": s_sat,
-        "roofline": {"bound": "hbm", "kernel": "k_quant", "achieved": round(nbytes / (q_ms * 1e-3) / 1e9, 1),
+        "roofline": {"bound": "hbm", "kernel": "k_quant_mx" if mx else "k_quant",
+                     "achieved": round(nbytes / (q_ms * 1e-3) / 1e9, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(nbytes / (q_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                      "traffic": None},
     }
@@ -291,7 +301,7 @@ def run_quant(args, cfg, dev):
             for blk in range(T // rb):
                 xb = synth.quant_rows(cfg, blk)                   # untimed: input generation
                 t1 = time.perf_counter()
-                OQ.quant_fp4(xb)
+                oquant(xb)
                 spent += time.perf_counter() - t1
                 done += rb
                 if spent >= args.cpu_seconds:
@@ -401,6 +411,8 @@ def main():
     ap.add_argument("--workload", default="stack_b32_n262144")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--kv", default="fp4_e4m3", choices=["fp4_e4m3", "mxfp4"],
+                    help="main KV cache format: E4M3 scale per 16 channels, or MXFP4 (E8M0 per 32)")
     ap.add_argument("--query-sets", type=int, default=4,
                     help="decode: timed steps rotate through this many seeded query sets")
     ap.add_argument("--copy-calibration", action="store_true")
@@ -435,10 +447,10 @@ def main():
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     t0 = time.perf_counter()
-    cache, layers = build_inputs(cfg, dev)
+    cache, layers = build_inputs(cfg, dev, kv=args.kv)
     log(f"inputs ready in {time.perf_counter() - t0:.1f} s")
     plan = C.Plan(cfg["modes"], K=cfg["K"], P=cfg.get("P") or 0, H=cfg["H"], d=cfg["d"], d_idx=cfg["d_idx"],
-                  q_idx_dtype=cfg["q_idx_dtype"], k_idx_dtype=cfg["k_idx_dtype"])
+                  q_idx_dtype=cfg["q_idx_dtype"], k_idx_dtype=cfg["k_idx_dtype"], kv_format=args.kv)
     stream = torch.cuda.current_stream()
     sets = query_sets(cfg, dev, layers, args.query_sets)
     ws = plan.decode_workspace(cache)
@@ -504,7 +516,7 @@ def main():
         torch.cuda.synchronize()
         del x, y
 
-    step_bytes, sel_bytes = alg_bytes(cfg)
+    step_bytes, sel_bytes = alg_bytes(cfg, args.kv)
     qps = cfg["B"] / (ms * 1e-3)
     sel_ms = slot_ms[0]
     achieved = sel_bytes / (sel_ms * 1e-3) / 1e9
@@ -522,9 +534,11 @@ def main():
         "vs_baseline": None,
         "dtype": "f64/f32",
         "data": "synthetic",
-        "config": {"workload": args.workload, "B": cfg["B"], "N": cfg["N"], "modes": list(cfg["modes"]),
+        "config": {"workload": args.workload + (":mxfp4" if args.kv == "mxfp4" else ""), "B": cfg["B"],
+                   "N": cfg["N"], "modes": list(cfg["modes"]),
                    "H": cfg["H"], "d": cfg["d"], "d_idx": cfg["d_idx"], "K": cfg["K"], "P": cfg.get("P"),
-                   "kv": "fp4_e2m1 + e4m3 scale per 16 ch", "indexer_keys": cfg["k_idx_dtype"],
+                   "kv": "mxfp4 (e2m1 + e8m0 per 32 ch)" if args.kv == "mxfp4" else "fp4_e2m1 + e4m3 scale per 16 ch",
+                   "indexer_keys": cfg["k_idx_dtype"],
                    "indexer_query": cfg["q_idx_dtype"]},
         "status_word": status,
         "query_sets": len(sets),
@@ -544,7 +558,7 @@ def main():
     }
     if not args.no_cpu:
         t0 = time.perf_counter()
-        out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds, args.kv)
         log(f"cpu baseline in {time.perf_counter() - t0:.1f} s")
     print(json.dumps(out), flush=True)
 

@@ -18,7 +18,7 @@ import torch
 
 __all__ = [
     "Csa2Error", "lib", "F32", "BF16", "E4M3", "FULL", "REINDEX", "REUSE",
-    "kv_quant_fp4", "kv_dequant_fp4", "index_full", "index_reindex", "topk",
+    "kv_quant_fp4", "kv_dequant_fp4", "kv_quant_mxfp4", "kv_dequant_mxfp4", "index_full", "index_reindex", "topk",
     "sparse_attn_fp4", "sparse_attn_fp4_noalloc", "KVCache", "Plan", "status_word",
 ]
 
@@ -36,9 +36,13 @@ class Csa2Error(RuntimeError):
     pass
 
 
+KV_FP4_E4M3, KV_MXFP4 = 0, 1
+KV_FORMATS = {"fp4_e4m3": KV_FP4_E4M3, "mxfp4": KV_MXFP4}
+
+
 class PlanParams(ctypes.Structure):
     _fields_ = [("K", _c_i32), ("P", _c_i32), ("H", _c_i32), ("d", _c_i32), ("d_idx", _c_i32),
-                ("q_idx_dtype", _c_i32), ("k_idx_dtype", _c_i32), ("softmax_scale", _c_f32)]
+                ("q_idx_dtype", _c_i32), ("k_idx_dtype", _c_i32), ("softmax_scale", _c_f32), ("kv_format", _c_i32)]
 
 
 class CacheDesc(ctypes.Structure):
@@ -55,6 +59,8 @@ _SIGS = {
     "csa2_version": (ctypes.c_int, []),
     "kv_quant_fp4": (ctypes.c_int, [_vp, _c_i64, _c_i32, _c_i64, _vp, _c_i64, _vp, _c_i64, _vp]),
     "kv_dequant_fp4": (ctypes.c_int, [_vp, _c_i64, _vp, _c_i64, _c_i64, _c_i32, _vp, _c_i64, _vp]),
+    "kv_quant_mxfp4": (ctypes.c_int, [_vp, _c_i64, _c_i32, _c_i64, _vp, _c_i64, _vp, _c_i64, _vp]),
+    "kv_dequant_mxfp4": (ctypes.c_int, [_vp, _c_i64, _vp, _c_i64, _c_i64, _c_i32, _vp, _c_i64, _vp]),
     "csa2_index_full": (ctypes.c_int, [_vp, _c_i32, _vp, _c_i32, _c_i32, _c_i32, _c_i64, _c_i32, _vp, _vp, _vp]),
     "csa2_index_reindex": (ctypes.c_int, [_vp, _c_i32, _vp, _c_i32, _c_i32, _c_i64, _c_i32, _vp, _c_i32, _vp, _vp]),
     "csa2_topk_workspace_bytes": (ctypes.c_int, [_c_i64, _c_i64, _c_i32, ctypes.POINTER(_c_sz)]),
@@ -62,6 +68,8 @@ _SIGS = {
     "csa2_sparse_attn_workspace_bytes": (ctypes.c_int, [_c_i32, _c_i32, _c_i32, _c_i32, _c_i32, ctypes.POINTER(_c_sz)]),
     "csa2_sparse_attn_fp4": (ctypes.c_int, [_vp, _c_i32, _c_i32, _c_i32, _c_i32, _vp, _vp, _vp, _vp, _c_i64, _c_i64,
                                             _c_i64, _vp, _c_i32, _c_f32, _vp, _vp, _c_sz, _vp]),
+    "csa2_sparse_attn_mxfp4": (ctypes.c_int, [_vp, _c_i32, _c_i32, _c_i32, _c_i32, _vp, _vp, _vp, _vp, _c_i64, _c_i64,
+                                              _c_i64, _vp, _c_i32, _c_f32, _vp, _vp, _c_sz, _vp]),
     "csa2_sparse_attn_fp4_noalloc": (ctypes.c_int, [_vp, _c_i32, _c_i32, _c_i32, _c_i32, _vp, _vp, _vp, _vp, _c_i64,
                                                     _c_i64, _c_i64, _vp, _c_i32, _c_f32, _vp, _vp]),
     "csa2_plan_create": (ctypes.c_int, [ctypes.POINTER(_c_i32), _c_i32, ctypes.POINTER(PlanParams),
@@ -185,6 +193,30 @@ def kv_dequant_fp4(codes, scales, C, y=None, stream=None):
     return y
 
 
+def kv_quant_mxfp4(x, codes=None, scales=None, stream=None):
+    """MXFP4: quantize bf16 rows x [T][C] (C % 32 == 0) into (codes [T][C/2] u8, E8M0 scales [T][C/32] u8)."""
+    _need_cuda(x)
+    T, C = x.shape
+    if codes is None:
+        codes = torch.empty(T, C // 2, dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty(T, C // 32, dtype=torch.uint8, device=x.device)
+    _check(lib().kv_quant_mxfp4(_ptr(x), T, C, x.stride(0), _ptr(codes), codes.stride(0), _ptr(scales),
+                                scales.stride(0), _stream(stream)), "kv_quant_mxfp4")
+    return codes, scales
+
+
+def kv_dequant_mxfp4(codes, scales, C, y=None, stream=None):
+    """Dequantize MXFP4 (codes, E8M0 scales) of rows with C channels into bf16 y [T][C]."""
+    _need_cuda(codes, scales)
+    T = codes.shape[0]
+    if y is None:
+        y = torch.empty(T, C, dtype=torch.bfloat16, device=codes.device)
+    _check(lib().kv_dequant_mxfp4(_ptr(codes), codes.stride(0), _ptr(scales), scales.stride(0), T, C, _ptr(y),
+                                  y.stride(0), _stream(stream)), "kv_dequant_mxfp4")
+    return y
+
+
 def index_full(q_idx, k_idx, q_pos=None, scores=None, stream=None):
     """Dense indexer scores. q_idx [B][Q][d_idx], k_idx [B][N][d_idx] -> scores [B][Q][N] fp32."""
     _need_cuda(q_idx, k_idx, q_pos)
@@ -233,13 +265,16 @@ class KVCache:
     """Main KV cache of B sequences x N positions in the 144-byte record layout.
 
     codes [B*N][128] u8 = [K codes 64 | V codes 64], scales [B*N][16] u8 =
-    [K scales 8 | V scales 8]; k_idx [B][N][d_idx] indexer keys.
+    [K scales 8 | V scales 8] (E4M3 per 16 channels) or [B*N][8] u8 = [K 4 | V 4]
+    (MXFP4: E8M0 per 32 channels); k_idx [B][N][d_idx] indexer keys.
     """
 
-    def __init__(self, B, N, d=128, device="cuda", k_idx=None):
+    def __init__(self, B, N, d=128, device="cuda", k_idx=None, kv_format="fp4_e4m3"):
         self.B, self.N, self.d = B, N, d
+        self.kv_format = kv_format
+        self.block = 32 if kv_format == "mxfp4" else 16     # channels per scale
         self.codes = torch.empty(B * N, d, dtype=torch.uint8, device=device)
-        self.scales = torch.empty(B * N, d // 8, dtype=torch.uint8, device=device)
+        self.scales = torch.empty(B * N, 2 * d // self.block, dtype=torch.uint8, device=device)
         self.k_idx = k_idx
 
     @property
@@ -252,21 +287,22 @@ class KVCache:
 
     @property
     def k_scales(self):
-        return self.scales[:, : self.d // 16]
+        return self.scales[:, : self.d // self.block]
 
     @property
     def v_scales(self):
-        return self.scales[:, self.d // 16:]
+        return self.scales[:, self.d // self.block:]
 
     def fill(self, k_bf16, v_bf16, row0=0, stream=None):
         """Quantize bf16 K and V rows [n][d] into positions [row0, row0+n) (flat over B*N)."""
         n = k_bf16.shape[0]
-        kv_quant_fp4(k_bf16, self.k_codes[row0:row0 + n], self.k_scales[row0:row0 + n], stream)
-        kv_quant_fp4(v_bf16, self.v_codes[row0:row0 + n], self.v_scales[row0:row0 + n], stream)
+        quant = kv_quant_mxfp4 if self.kv_format == "mxfp4" else kv_quant_fp4
+        quant(k_bf16, self.k_codes[row0:row0 + n], self.k_scales[row0:row0 + n], stream)
+        quant(v_bf16, self.v_codes[row0:row0 + n], self.v_scales[row0:row0 + n], stream)
 
     def desc(self):
         return CacheDesc(self.codes.data_ptr(), self.scales.data_ptr(), self.codes.data_ptr() + self.d // 2,
-                         self.scales.data_ptr() + self.d // 16, self.codes.stride(0), self.scales.stride(0),
+                         self.scales.data_ptr() + self.d // self.block, self.codes.stride(0), self.scales.stride(0),
                          None if self.k_idx is None else self.k_idx.data_ptr())
 
 
@@ -284,9 +320,10 @@ def sparse_attn_fp4(q, cache, idx, softmax_scale=None, out=None, stream=None, ws
     if ws is None:
         ws = workspace(nb.value, q.device, "attn")
     c = cache.desc()
-    _check(lib().csa2_sparse_attn_fp4(_ptr(q), B, Q, H, d, c.k_codes, c.k_scales, c.v_codes, c.v_scales, cache.N,
-                                      c.code_stride_bytes, c.scale_stride_bytes, _ptr(idx), K, scale, _ptr(out),
-                                      _ptr(ws), ws.numel(), _stream(stream)), "csa2_sparse_attn_fp4")
+    name = "csa2_sparse_attn_mxfp4" if cache.kv_format == "mxfp4" else "csa2_sparse_attn_fp4"
+    _check(getattr(lib(), name)(_ptr(q), B, Q, H, d, c.k_codes, c.k_scales, c.v_codes, c.v_scales, cache.N,
+                                c.code_stride_bytes, c.scale_stride_bytes, _ptr(idx), K, scale, _ptr(out),
+                                _ptr(ws), ws.numel(), _stream(stream)), name)
     return out
 
 
@@ -310,12 +347,12 @@ class Plan:
     """A static Full / Reindex / Reuse layer plan (csa2_plan_*)."""
 
     def __init__(self, modes, K, P=0, H=16, d=128, d_idx=64, q_idx_dtype="bf16", k_idx_dtype="e4m3",
-                 softmax_scale=0.0):
+                 softmax_scale=0.0, kv_format="fp4_e4m3"):
         codes = [MODE_CODES[m] if isinstance(m, str) else int(m) for m in modes]
         arr = (_c_i32 * len(codes))(*codes)
         self.modes = list(codes)
         self.params = PlanParams(K, P or 0, H, d, d_idx, DTYPE_CODES[q_idx_dtype], DTYPE_CODES[k_idx_dtype],
-                                 softmax_scale)
+                                 softmax_scale, KV_FORMATS[kv_format])
         h = ctypes.c_void_p(None)
         _check(lib().csa2_plan_create(arr, len(codes), ctypes.byref(self.params), ctypes.byref(h)), "csa2_plan_create")
         self._h = h

@@ -93,6 +93,22 @@ int check_quant_layout(int64_t rows, int32_t C, int64_t x_stride, int64_t cs, in
     return OK;
 }
 
+int check_mx_layout(int64_t rows, int32_t C, int64_t x_stride, int64_t cs, int64_t ss, const void* x,
+                    const void* codes, const void* scales, int code_align, const char* who) {
+    const std::string w(who);
+    if (rows < 0) return fail(INVALID, w + ": rows < 0");
+    if (C <= 0 || C % 32 != 0) return fail(INVALID, w + ": C must be a positive multiple of 32");
+    if (x_stride < C) return fail(INVALID, w + ": bf16 row stride < C");
+    if (cs < C / 2) return fail(INVALID, w + ": code row stride < C/2 bytes");
+    if (ss < C / 32) return fail(INVALID, w + ": scale row stride < C/32 bytes");
+    if (rows == 0) return OK;
+    if (!x || !codes || !scales) return fail(INVALID, w + ": null pointer");
+    if (!aligned(x, 16) || (x_stride * 2) % 16 != 0) return fail(INVALID, w + ": bf16 rows must be 16-byte aligned");
+    if (!aligned(codes, code_align) || cs % code_align != 0)
+        return fail(INVALID, w + ": code rows must be " + std::to_string(code_align) + "-byte aligned");
+    return OK;
+}
+
 int check_scan(const void* q_idx, int32_t q_dtype, const void* k_idx, int32_t k_dtype, int32_t d_idx, const char* who) {
     const std::string w(who);
     if (!q_dtype_ok(q_dtype)) return fail(DTYPE, w + ": indexer query dtype must be CSA2_F32 or CSA2_BF16");
@@ -109,19 +125,20 @@ int check_scan(const void* q_idx, int32_t q_dtype, const void* k_idx, int32_t k_
 namespace csa2 {
 
 int check_attn(const uint16_t* q, int32_t H, int32_t d, const uint8_t* kc, const uint8_t* ks, const uint8_t* vc,
-               const uint8_t* vs, int64_t N, int64_t cs, int64_t ss, int32_t K, const char* who) {
+               const uint8_t* vs, int64_t N, int64_t cs, int64_t ss, int32_t K, const char* who, bool mx) {
     const std::string w(who);
     if (H < 1 || H > 16) return fail(INVALID, w + ": H must be in 1..16");
     if (d != 128) return fail(INVALID, w + ": head dim d must be 128");
     if (K < 1) return fail(INVALID, w + ": K must be >= 1");
     if (N < 1) return fail(INVALID, w + ": N must be >= 1");
-    if (cs < d / 2 || ss < d / 16) return fail(INVALID, w + ": KV code/scale stride smaller than one row");
+    if (cs < d / 2 || ss < (mx ? d / 32 : d / 16)) return fail(INVALID, w + ": KV code/scale stride smaller than one row");
     if (!q || !kc || !ks || !vc || !vs) return fail(INVALID, w + ": null pointer");
     if (!aligned(kc, 16) || !aligned(vc, 16) || cs % 16 != 0)
         return fail(INVALID, w + ": KV code rows must be 16-byte aligned");
     if (!aligned(q, 16)) return fail(INVALID, w + ": query must be 16-byte aligned");
-    if (!aligned(ks, 8) || !aligned(vs, 8) || ss % 8 != 0)
-        return fail(INVALID, w + ": KV scale rows must be 8-byte aligned");
+    const int sa = mx ? 4 : 8;                  // each position's K (V) scales are read as one word
+    if (!aligned(ks, sa) || !aligned(vs, sa) || ss % sa != 0)
+        return fail(INVALID, w + (mx ? ": KV scale rows must be 4-byte aligned" : ": KV scale rows must be 8-byte aligned"));
     return OK;
 }
 
@@ -149,6 +166,24 @@ int kv_dequant_fp4(const uint8_t* codes, int64_t code_stride_bytes, const uint8_
                                    "kv_dequant_fp4"))
         return e;
     return launch_dequant(codes, code_stride_bytes, scales, scale_stride_bytes, rows, C, y, y_stride, stream);
+}
+
+int kv_quant_mxfp4(const uint16_t* x, int64_t rows, int32_t C, int64_t x_stride, uint8_t* codes,
+                   int64_t code_stride_bytes, uint8_t* scales, int64_t scale_stride_bytes, hipStream_t stream) {
+    g_err.clear();
+    if (int e = check_mx_layout(rows, C, x_stride, code_stride_bytes, scale_stride_bytes, x, codes, scales, 16,
+                                "kv_quant_mxfp4"))
+        return e;
+    return launch_quant_mx(x, rows, C, x_stride, codes, code_stride_bytes, scales, scale_stride_bytes, stream);
+}
+
+int kv_dequant_mxfp4(const uint8_t* codes, int64_t code_stride_bytes, const uint8_t* scales, int64_t scale_stride_bytes,
+                     int64_t rows, int32_t C, uint16_t* y, int64_t y_stride, hipStream_t stream) {
+    g_err.clear();
+    if (int e = check_mx_layout(rows, C, y_stride, code_stride_bytes, scale_stride_bytes, y, codes, scales, 4,
+                                "kv_dequant_mxfp4"))
+        return e;
+    return launch_dequant_mx(codes, code_stride_bytes, scales, scale_stride_bytes, rows, C, y, y_stride, stream);
 }
 
 int csa2_index_full(const void* q_idx, int32_t q_dtype, const void* k_idx, int32_t k_dtype, int32_t B, int32_t Q,
@@ -241,7 +276,7 @@ int csa2_sparse_attn_fp4(const uint16_t* q, int32_t B, int32_t Q, int32_t H, int
     if (B < 0 || Q < 0) return fail(INVALID, "csa2_sparse_attn_fp4: negative size");
     if ((int64_t)B * Q == 0) return OK;
     if (int e = check_attn(q, H, d, k_codes, k_scales, v_codes, v_scales, N, code_stride_bytes, scale_stride_bytes, K,
-                           "csa2_sparse_attn_fp4"))
+                           "csa2_sparse_attn_fp4", false))
         return e;
     if (!idx || !out) return fail(INVALID, "csa2_sparse_attn_fp4: null pointer");
     if (!(softmax_scale >= 0.f) || !isfinite(softmax_scale))
@@ -267,6 +302,44 @@ int csa2_sparse_attn_fp4(const uint16_t* q, int32_t B, int32_t Q, int32_t H, int
     a.K = K;
     a.scale = softmax_scale;
     a.out = out;
+    return launch_attn(a, ws, static_cast<uint8_t*>(ws) + kCtrlBytes, ws_bytes - kCtrlBytes, stream);
+}
+
+int csa2_sparse_attn_mxfp4(const uint16_t* q, int32_t B, int32_t Q, int32_t H, int32_t d, const uint8_t* k_codes,
+                         const uint8_t* k_scales, const uint8_t* v_codes, const uint8_t* v_scales, int64_t N,
+                         int64_t code_stride_bytes, int64_t scale_stride_bytes, const int32_t* idx, int32_t K,
+                         float softmax_scale, float* out, void* ws, size_t ws_bytes, hipStream_t stream) {
+    g_err.clear();
+    if (B < 0 || Q < 0) return fail(INVALID, "csa2_sparse_attn_mxfp4: negative size");
+    if ((int64_t)B * Q == 0) return OK;
+    if (int e = check_attn(q, H, d, k_codes, k_scales, v_codes, v_scales, N, code_stride_bytes, scale_stride_bytes, K,
+                           "csa2_sparse_attn_mxfp4", true))
+        return e;
+    if (!idx || !out) return fail(INVALID, "csa2_sparse_attn_mxfp4: null pointer");
+    if (!(softmax_scale >= 0.f) || !isfinite(softmax_scale))
+        return fail(INVALID, "csa2_sparse_attn_mxfp4: softmax_scale must be >= 0 and finite");
+    if (softmax_scale == 0.f) softmax_scale = 1.0f / sqrtf((float)d);
+    const size_t need = kCtrlBytes + attn_data_bytes((int64_t)B * Q, K);
+    if (int e = check_ws(ws, ws_bytes, need, "csa2_sparse_attn_mxfp4")) return e;
+    AttnArgs a;
+    a.q = q;
+    a.rows = (int64_t)B * Q;
+    a.rows_per_seq = Q;
+    a.H = H;
+    a.d = d;
+    a.k_codes = k_codes;
+    a.k_scales = k_scales;
+    a.v_codes = v_codes;
+    a.v_scales = v_scales;
+    a.N = N;
+    a.code_stride = code_stride_bytes;
+    a.scale_stride = scale_stride_bytes;
+    a.idx = idx;
+    a.idx_stride = K;
+    a.K = K;
+    a.scale = softmax_scale;
+    a.out = out;
+    a.mx = true;
     return launch_attn(a, ws, static_cast<uint8_t*>(ws) + kCtrlBytes, ws_bytes - kCtrlBytes, stream);
 }
 
@@ -382,6 +455,8 @@ int csa2_plan_create(const int32_t* modes, int32_t L, const csa2_plan_params* pa
     if (!k_dtype_ok(p.k_idx_dtype)) return fail(DTYPE, "csa2_plan_create: indexer key dtype");
     if (!(p.softmax_scale >= 0.f) || !isfinite(p.softmax_scale))
         return fail(INVALID, "csa2_plan_create: softmax_scale must be >= 0 and finite");
+    if (p.kv_format != CSA2_KV_FP4_E4M3 && p.kv_format != CSA2_KV_MXFP4)
+        return fail(INVALID, "csa2_plan_create: kv_format must be CSA2_KV_FP4_E4M3 or CSA2_KV_MXFP4");
     csa2_plan* plan = new csa2_plan;
     plan->modes.assign(modes, modes + L);
     plan->p = p;
@@ -454,7 +529,8 @@ int csa2_plan_run_decode(const csa2_plan* plan, const csa2_cache* cache, const c
     const int L = (int)plan->modes.size();
     if (plan->has_reindex && p.P > N) return fail(INVALID, "csa2_plan_run_decode: pool size P exceeds N");
     if (int e = check_attn(io[0].q, p.H, p.d, cache->k_codes, cache->k_scales, cache->v_codes, cache->v_scales, N,
-                           cache->code_stride_bytes, cache->scale_stride_bytes, p.K, "csa2_plan_run_decode"))
+                           cache->code_stride_bytes, cache->scale_stride_bytes, p.K, "csa2_plan_run_decode",
+                           p.kv_format == CSA2_KV_MXFP4))
         return e;
     if (!cache->k_idx || !aligned(cache->k_idx, 16))
         return fail(INVALID, "csa2_plan_run_decode: indexer keys null or not 16-byte aligned");
@@ -536,6 +612,7 @@ int csa2_plan_run_decode(const csa2_plan* plan, const csa2_cache* cache, const c
         at.K = p.K;
         at.scale = p.softmax_scale;
         at.out = io[l].out;
+        at.mx = p.kv_format == CSA2_KV_MXFP4;
         SlotTimer timer(plan, 2 * l + 1, stream);
         if (int e = launch_attn(at, wsb, wsb + lay.off_attn, lay.off_idx - lay.off_attn, stream)) return e;
     }
@@ -643,7 +720,8 @@ int csa2_prefill_full(const csa2_plan* plan, const csa2_cache* cache, const void
     if (B < 1 || Q < 1 || N < 1) return fail(INVALID, "csa2_prefill_full: sizes must be >= 1");
     const csa2_plan_params& p = plan->p;
     if (int e = check_attn(q, p.H, p.d, cache->k_codes, cache->k_scales, cache->v_codes, cache->v_scales, N,
-                           cache->code_stride_bytes, cache->scale_stride_bytes, p.K, "csa2_prefill_full"))
+                           cache->code_stride_bytes, cache->scale_stride_bytes, p.K, "csa2_prefill_full",
+                           p.kv_format == CSA2_KV_MXFP4))
         return e;
     if (int e = check_scan(q_idx, p.q_idx_dtype, cache->k_idx, p.k_idx_dtype, p.d_idx, "csa2_prefill_full")) return e;
     if (!q_pos || !idx_out || !out) return fail(INVALID, "csa2_prefill_full: null pointer");
@@ -754,6 +832,7 @@ int csa2_prefill_full(const csa2_plan* plan, const csa2_cache* cache, const void
     at.K = p.K;
     at.scale = p.softmax_scale;
     at.out = out;
+    at.mx = p.kv_format == CSA2_KV_MXFP4;
     return launch_attn(at, wsb, wsb + lay.off_attn, lay.total - lay.off_attn, stream);
 }
 

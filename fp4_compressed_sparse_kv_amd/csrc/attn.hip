@@ -33,6 +33,14 @@
 // Each softmax weight p (fp32) enters the matrix core as two f16 terms
 // hi + lo (about 22 significant bits together); accumulation is fp32.
 //
+// MXFP4 caches (E2M1 with one E8M0 scale per 32 channels) take the same
+// path with bf16 operands: K is widened by the hardware scaled FP4 -> bf16
+// convert, which applies the block's power-of-two scale exactly (a lane's 32
+// K channels are one block); V by the FP4 -> fp32 convert times each
+// position's scale (exact) and the top halves; the query, scaled per head by
+// a power of two as below, stays bf16; each softmax weight enters as two bf16
+// terms hi + lo (16 bits).
+//
 // The waves of a workgroup are merged through LDS in wave order. With NS > 1
 // each workgroup writes its (max, sum, acc) state to the workspace with
 // device-coherent stores, and the last workgroup of the row to arrive (one
@@ -46,6 +54,8 @@
 namespace csa2 {
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -99,6 +109,34 @@ __device__ __forceinline__ f16x8 dq8(uint32_t w, _Float16 s) {
 }
 
 __device__ __forceinline__ _Float16 scale_f16(uint32_t b) { return (_Float16)e4m3_to_f32(b); }
+
+// 8 FP4 codes (one dword) of one 32-channel MXFP4 block -> 8 bf16 with the
+// block's E8M0 scale (an fp32 whose exponent field is the scale byte).
+__device__ __forceinline__ bf16x8 dq8_mx(uint32_t w, float X) {
+    const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, X, 0);
+    const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, X, 1);
+    const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, X, 2);
+    const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, X, 3);
+    return bf16x8{a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
+}
+
+__device__ __forceinline__ float e8m0_f32(uint32_t b) { return __uint_as_float((b & 0xFFu) << 23); }
+
+// Top halves of two fp32 whose values are exact in bf16, as a bf16 pair.
+__device__ __forceinline__ uint32_t pack_hi(float lo, float hi) {
+    return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);
+}
+
+__device__ __forceinline__ f32x4 mfma16(const f16x8& a, const f16x8& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Matrix-core operand type of a cache format: f16 (E4M3 scales), bf16 (MXFP4).
+template <bool MX> struct OpOf { using type = f16x8; };
+template <> struct OpOf<true> { using type = bf16x8; };
 
 // Over the four rows of 16 lanes (lanes n, 16 + n, 32 + n, 48 + n): the
 // maximum and the sum, in every lane of the group. v_permlane16_swap and
@@ -174,6 +212,7 @@ __device__ __forceinline__ BlockPos load_pos(const int32_t* ip, int blk, int K, 
 // is padding (past K, negative or >= N) reads position 0 of the sequence
 // instead, and its scales are zeroed when the block is staged, so it
 // dequantizes to exact zeros and is masked out of the softmax.
+template <bool MX>
 __device__ __forceinline__ void gather(BlockRaw& r, const BlockPos& bp, int blk, int K, const KvBase& kv, int64_t N,
                                        int lane, int n, int g) {
     const bool ok = lane < kBlk && blk * kBlk + lane < K && bp.s >= 0 && (int64_t)bp.s < N;
@@ -184,8 +223,13 @@ __device__ __forceinline__ void gather(BlockRaw& r, const BlockPos& bp, int blk,
     r.v[0] = *reinterpret_cast<const uint4*>(kv.vc + p0 * kv.cs + 16 * g);
     r.k[1] = *reinterpret_cast<const uint4*>(kv.kc + p1 * kv.cs + 16 * g);
     r.v[1] = *reinterpret_cast<const uint4*>(kv.vc + p1 * kv.cs + 16 * g);
-    r.ks = *reinterpret_cast<const uint2*>(kv.ks + safe * kv.ss);
-    r.vs = *reinterpret_cast<const uint2*>(kv.vs + safe * kv.ss);
+    if constexpr (MX) {                         // 4 E8M0 bytes per plane (128 channels)
+        r.ks = make_uint2(*reinterpret_cast<const uint32_t*>(kv.ks + safe * kv.ss), 0u);
+        r.vs = make_uint2(*reinterpret_cast<const uint32_t*>(kv.vs + safe * kv.ss), 0u);
+    } else {
+        r.ks = *reinterpret_cast<const uint2*>(kv.ks + safe * kv.ss);
+        r.vs = *reinterpret_cast<const uint2*>(kv.vs + safe * kv.ss);
+    }
     r.pos = ok ? bp.s : -1;
 }
 
@@ -202,8 +246,10 @@ __device__ __forceinline__ f16x2 e4m3x2_to_f16(uint32_t w) {
     return __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(f.x, f.y));
 }
 
-__device__ __forceinline__ void attend_block(WaveState& st, const BlockRaw& r, Stage& sg, const f16x8 (&qb)[4],
-                                             float sl2, int lane, int n, int g) {
+template <bool MX>
+__device__ __forceinline__ void attend_block(WaveState& st, const BlockRaw& r, Stage& sg,
+                                             const typename OpOf<MX>::type (&qb)[4], float sl2, int lane, int n, int g) {
+    using OpT = typename OpOf<MX>::type;
     // ---- stage V codes and scales; this wave alone uses `sg`, and its LDS
     // accesses complete in order, so no barrier is needed
     *reinterpret_cast<uint4*>(&sg.v[n][16 * g]) = r.v[0];
@@ -216,26 +262,30 @@ __device__ __forceinline__ void attend_block(WaveState& st, const BlockRaw& r, S
     // bit p: position p of the block is a real entry (padding is masked out of
     // the softmax; its codes and scales are those of position 0, all finite)
     const uint32_t vmask = (uint32_t)__builtin_amdgcn_ballot_w64(r.pos >= 0);
-    // this lane's softmax columns i: positions 4g + i (i < 4), 16 + 4g + i - 4 (i >= 4)
+    // this lane's softmax columns i: positions 4g + i (i < 4), 16 + 4g + i - 4 (i >= 4);
+    // its V channels 8n .. 8n+7 lie in scale group n/2 (16 channels) or block n/4 (32)
     uint32_t vw[8], vsb[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const int p = (i < 4) ? (4 * g + i) : (16 + 4 * g + i - 4);
         vw[i] = *reinterpret_cast<const uint32_t*>(&sg.v[p][4 * n]);
-        vsb[i] = sg.vs[p][n >> 1];
+        vsb[i] = MX ? sg.vs[p][n >> 2] : sg.vs[p][n >> 1];
     }
-    const f16x2 ks0 = e4m3x2_to_f16(*reinterpret_cast<const uint16_t*>(&sg.ks[n][2 * g]));
-    const f16x2 ks1 = e4m3x2_to_f16(*reinterpret_cast<const uint16_t*>(&sg.ks[16 + n][2 * g]));
 
-    // ---- S^T = K_hat Q^T
+    // ---- S^T = K_hat Q^T (a lane's K channels 32g .. 32g+31: two E4M3 groups, one MXFP4 block)
     f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
-        const f16x2 ks = mb == 0 ? ks0 : ks1;
         const uint32_t w[4] = {r.k[mb].x, r.k[mb].y, r.k[mb].z, r.k[mb].w};
+        if constexpr (MX) {
+            const float X = e8m0_f32(sg.ks[16 * mb + n][g]);
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
-            sacc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(dq8(w[s], s < 2 ? ks.x : ks.y), qb[s], sacc[mb], 0, 0, 0);
+            for (int s = 0; s < 4; ++s) sacc[mb] = mfma16(dq8_mx(w[s], X), qb[s], sacc[mb]);
+        } else {
+            const f16x2 ks = e4m3x2_to_f16(*reinterpret_cast<const uint16_t*>(&sg.ks[16 * mb + n][2 * g]));
+#pragma unroll
+            for (int s = 0; s < 4; ++s) sacc[mb] = mfma16(dq8(w[s], s < 2 ? ks.x : ks.y), qb[s], sacc[mb]);
+        }
     }
 
     // ---- online softmax for head n over the 8 positions this lane holds
@@ -260,16 +310,23 @@ __device__ __forceinline__ void attend_block(WaveState& st, const BlockRaw& r, S
         p[i] = __builtin_amdgcn_exp2f((lg[i] - mref) * st.f);
         psum += p[i];
     }
-    f16x8 pb_hi, pb_lo;                         // p = hi + lo, both f16: ~22 significant bits
+    uint32_t ph[4], pl[4];                      // p = hi + lo: f16 (~22 bits) or bf16 (16 bits) pairs
 #pragma unroll
     for (int i = 0; i < 8; i += 2) {
-        const f16x2 hi = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(p[i], p[i + 1]));
-        const f16x2 lo = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(p[i] - (float)hi.x, p[i + 1] - (float)hi.y));
-        pb_hi[i] = hi.x;
-        pb_hi[i + 1] = hi.y;
-        pb_lo[i] = lo.x;
-        pb_lo[i + 1] = lo.y;
+        if constexpr (MX) {
+            const float h0 = __uint_as_float(__float_as_uint(p[i]) & 0xFFFF0000u);
+            const float h1 = __uint_as_float(__float_as_uint(p[i + 1]) & 0xFFFF0000u);
+            ph[i / 2] = pack_hi(h0, h1);
+            pl[i / 2] = pack_hi(p[i] - h0, p[i + 1] - h1);
+        } else {
+            const f16x2 hi = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(p[i], p[i + 1]));
+            const f16x2 lo = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(p[i] - (float)hi.x, p[i + 1] - (float)hi.y));
+            ph[i / 2] = __builtin_bit_cast(uint32_t, hi);
+            pl[i / 2] = __builtin_bit_cast(uint32_t, lo);
+        }
     }
+    const OpT pb_hi = __builtin_bit_cast(OpT, make_uint4(ph[0], ph[1], ph[2], ph[3]));
+    const OpT pb_lo = __builtin_bit_cast(OpT, make_uint4(pl[0], pl[1], pl[2], pl[3]));
     psum = rows_sum(psum);
     const float alpha = m_old == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m_old - mref) * st.f);
     st.l = st.l * alpha + psum;
@@ -284,35 +341,48 @@ __device__ __forceinline__ void attend_block(WaveState& st, const BlockRaw& r, S
     // ---- out^T += V_hat^T P^T: MFMA t covers channels 8m + t; its operand
     // element i is channel 8n + t of position column i. Codes of columns
     // 2k and 2k+1 are interleaved nibble-wise so that one convert yields the
-    // (column 2k, column 2k+1) pair of a channel, scaled by the packed scale
-    // pair of the two positions.
-    f16x2 va[8][4];                             // va[t][k] = (V[2k][8n+t], V[2k+1][8n+t])
+    // (column 2k, column 2k+1) pair of a channel, then each value takes its
+    // own position's scale: a packed f16 product with the E4M3 scale pair, or
+    // fp32 products with the two E8M0 scales (exact) and the bf16 top halves.
+    uint32_t va[8][4];                          // va[t][k] = (V[2k][8n+t], V[2k+1][8n+t])
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
         const uint32_t wa = vw[2 * k], wb = vw[2 * k + 1];
-        const f16x2 sp = e4m3x2_to_f16(vsb[2 * k] | (vsb[2 * k + 1] << 8));
         const uint32_t ev = (wa & 0x0F0F0F0Fu) | ((wb << 4) & 0xF0F0F0F0u);   // byte j: channel 2j of a | of b
         const uint32_t od = ((wa >> 4) & 0x0F0F0F0Fu) | (wb & 0xF0F0F0F0u);  // byte j: channel 2j+1
-        va[0][k] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(ev, 1.0f, 0) * sp;
-        va[2][k] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(ev, 1.0f, 1) * sp;
-        va[4][k] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(ev, 1.0f, 2) * sp;
-        va[6][k] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(ev, 1.0f, 3) * sp;
-        va[1][k] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(od, 1.0f, 0) * sp;
-        va[3][k] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(od, 1.0f, 1) * sp;
-        va[5][k] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(od, 1.0f, 2) * sp;
-        va[7][k] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(od, 1.0f, 3) * sp;
+        if constexpr (MX) {
+            const float X0 = e8m0_f32(vsb[2 * k]), X1 = e8m0_f32(vsb[2 * k + 1]);
+            auto pair = [&](f32x2 e) { return pack_hi(e.x * X0, e.y * X1); };
+            va[0][k] = pair(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(ev, 1.0f, 0));
+            va[2][k] = pair(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(ev, 1.0f, 1));
+            va[4][k] = pair(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(ev, 1.0f, 2));
+            va[6][k] = pair(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(ev, 1.0f, 3));
+            va[1][k] = pair(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(od, 1.0f, 0));
+            va[3][k] = pair(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(od, 1.0f, 1));
+            va[5][k] = pair(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(od, 1.0f, 2));
+            va[7][k] = pair(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(od, 1.0f, 3));
+        } else {
+            const f16x2 sp = e4m3x2_to_f16(vsb[2 * k] | (vsb[2 * k + 1] << 8));
+            auto pair = [&](f16x2 e) { return __builtin_bit_cast(uint32_t, e * sp); };
+            va[0][k] = pair(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(ev, 1.0f, 0));
+            va[2][k] = pair(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(ev, 1.0f, 1));
+            va[4][k] = pair(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(ev, 1.0f, 2));
+            va[6][k] = pair(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(ev, 1.0f, 3));
+            va[1][k] = pair(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(od, 1.0f, 0));
+            va[3][k] = pair(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(od, 1.0f, 1));
+            va[5][k] = pair(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(od, 1.0f, 2));
+            va[7][k] = pair(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(od, 1.0f, 3));
+        }
     }
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-        const f16x8 a = __builtin_shufflevector(__builtin_shufflevector(va[t][0], va[t][1], 0, 1, 2, 3),
-                                                __builtin_shufflevector(va[t][2], va[t][3], 0, 1, 2, 3), 0, 1, 2, 3,
-                                                4, 5, 6, 7);
-        st.acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pb_hi, st.acc[t], 0, 0, 0);
-        st.acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pb_lo, st.acc[t], 0, 0, 0);
+        const OpT a = __builtin_bit_cast(OpT, make_uint4(va[t][0], va[t][1], va[t][2], va[t][3]));
+        st.acc[t] = mfma16(a, pb_hi, st.acc[t]);
+        st.acc[t] = mfma16(a, pb_lo, st.acc[t]);
     }
 }
 
-template <int W>
+template <int W, bool MX>
 __global__ void __launch_bounds__(W * kWave, W == 4 ? 2 : 1)
 k_sparse_attn(const uint16_t* __restrict__ q, int32_t rows_per_seq, int32_t H, const uint8_t* __restrict__ k_codes,
               const uint8_t* __restrict__ k_scales, const uint8_t* __restrict__ v_codes,
@@ -347,7 +417,7 @@ k_sparse_attn(const uint16_t* __restrict__ q, int32_t rows_per_seq, int32_t H, c
         for (int s = 0; s < 4; ++s)
             qraw[s] = *reinterpret_cast<const uint4*>(q + (row * H + min(n, H - 1)) * (int64_t)kD + 32 * g + 8 * s);
     };
-    f16x8 qb[4];
+    typename OpOf<MX>::type qb[4];
     int qe = 0;                                 // head n's query is used as q * 2^-qe
     auto convert_q = [&]() {
         uint32_t mb = 0;                        // largest |q| of this lane's 32 elements (bf16 bits)
@@ -363,12 +433,19 @@ k_sparse_attn(const uint16_t* __restrict__ q, int32_t rows_per_seq, int32_t H, c
         qe = qmax > 0.f ? ex - 15 : 0;
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-            const uint32_t w[4] = {qraw[s].x, qraw[s].y, qraw[s].z, qraw[s].w};
+            uint32_t w[4] = {qraw[s].x, qraw[s].y, qraw[s].z, qraw[s].w};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                qb[s][2 * i + 0] = n < H ? (_Float16)ldexpf(bf16_bits_to_f32(w[i] & 0xFFFFu), -qe) : (_Float16)0.f;
-                qb[s][2 * i + 1] = n < H ? (_Float16)ldexpf(bf16_bits_to_f32(w[i] >> 16), -qe) : (_Float16)0.f;
+                const float a = n < H ? ldexpf(bf16_bits_to_f32(w[i] & 0xFFFFu), -qe) : 0.f;
+                const float b = n < H ? ldexpf(bf16_bits_to_f32(w[i] >> 16), -qe) : 0.f;
+                if constexpr (MX) {             // a bf16 times a power of two: its top half (exact unless subnormal)
+                    w[i] = pack_hi(a, b);
+                } else {
+                    qb[s][2 * i + 0] = (_Float16)a;
+                    qb[s][2 * i + 1] = (_Float16)b;
+                }
             }
+            if constexpr (MX) qb[s] = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
         }
     };
 
@@ -397,34 +474,34 @@ k_sparse_attn(const uint16_t* __restrict__ q, int32_t rows_per_seq, int32_t H, c
         BlockPos p0 = load_pos(ip, first, K, lane);
         load_q();
         BlockPos p1 = load_pos(ip, first + min(1, nb - 1) * kAttnWaves, K, lane);
-        gather(r0, p0, first, K, kv, N, lane, n, g);
+        gather<MX>(r0, p0, first, K, kv, N, lane, n, g);
         convert_q();
         st.f = ldexpf(1.f, qe);
         int k = 0;
         for (; k + 3 < nb; k += 2) {
             const int bk = first + k * kAttnWaves;
             p0 = load_pos(ip, bk + 2 * kAttnWaves, K, lane);
-            gather(r1, p1, bk + kAttnWaves, K, kv, N, lane, n, g);
-            attend_block(st, r0, lds.st[wave], qb, sl2, lane, n, g);
+            gather<MX>(r1, p1, bk + kAttnWaves, K, kv, N, lane, n, g);
+            attend_block<MX>(st, r0, lds.st[wave], qb, sl2, lane, n, g);
             p1 = load_pos(ip, bk + 3 * kAttnWaves, K, lane);
-            gather(r0, p0, bk + 2 * kAttnWaves, K, kv, N, lane, n, g);
-            attend_block(st, r1, lds.st[wave], qb, sl2, lane, n, g);
+            gather<MX>(r0, p0, bk + 2 * kAttnWaves, K, kv, N, lane, n, g);
+            attend_block<MX>(st, r1, lds.st[wave], qb, sl2, lane, n, g);
         }
         const int bk = first + k * kAttnWaves;
         const int rem = nb - k;                 // 1, 2 or 3
         if (rem == 1) {
-            attend_block(st, r0, lds.st[wave], qb, sl2, lane, n, g);
+            attend_block<MX>(st, r0, lds.st[wave], qb, sl2, lane, n, g);
         } else if (rem == 2) {
-            gather(r1, p1, bk + kAttnWaves, K, kv, N, lane, n, g);
-            attend_block(st, r0, lds.st[wave], qb, sl2, lane, n, g);
-            attend_block(st, r1, lds.st[wave], qb, sl2, lane, n, g);
+            gather<MX>(r1, p1, bk + kAttnWaves, K, kv, N, lane, n, g);
+            attend_block<MX>(st, r0, lds.st[wave], qb, sl2, lane, n, g);
+            attend_block<MX>(st, r1, lds.st[wave], qb, sl2, lane, n, g);
         } else {
             p0 = load_pos(ip, bk + 2 * kAttnWaves, K, lane);
-            gather(r1, p1, bk + kAttnWaves, K, kv, N, lane, n, g);
-            attend_block(st, r0, lds.st[wave], qb, sl2, lane, n, g);
-            gather(r0, p0, bk + 2 * kAttnWaves, K, kv, N, lane, n, g);
-            attend_block(st, r1, lds.st[wave], qb, sl2, lane, n, g);
-            attend_block(st, r0, lds.st[wave], qb, sl2, lane, n, g);
+            gather<MX>(r1, p1, bk + kAttnWaves, K, kv, N, lane, n, g);
+            attend_block<MX>(st, r0, lds.st[wave], qb, sl2, lane, n, g);
+            gather<MX>(r0, p0, bk + 2 * kAttnWaves, K, kv, N, lane, n, g);
+            attend_block<MX>(st, r1, lds.st[wave], qb, sl2, lane, n, g);
+            attend_block<MX>(st, r0, lds.st[wave], qb, sl2, lane, n, g);
         }
     } else {                                    // no block: only the scale-back factor is needed
         load_q();
@@ -543,7 +620,8 @@ int launch_attn_scratch(const AttnArgs& a, uint32_t* counters, void* parts, size
     if (ns > 1 && a.rows > kAttnCtrlWords) return fail(INVALID, "attention: split rows exceed the counter table");
     const int64_t groups = a.rows * ns;
     if (groups > 0x7FFFFFFFll) return fail(INVALID, "attention: too many query rows");
-    auto fn = sh.waves == 4 ? k_sparse_attn<4> : k_sparse_attn<8>;
+    auto fn = a.mx ? (sh.waves == 4 ? k_sparse_attn<4, true> : k_sparse_attn<8, true>)
+                   : (sh.waves == 4 ? k_sparse_attn<4, false> : k_sparse_attn<8, false>);
     hipLaunchKernelGGL(fn, dim3((unsigned)groups), dim3(sh.waves * kWave), 0, stream, a.q, a.rows_per_seq,
                        a.H, a.k_codes, a.k_scales, a.v_codes, a.v_scales, a.N, a.code_stride, a.scale_stride, a.idx,
                        a.idx_stride, a.K, a.scale, a.out, ns, counters, reinterpret_cast<float*>(parts), a.rows);

@@ -152,6 +152,10 @@ int launch_quant(const uint16_t* x, int64_t rows, int32_t C, int64_t x_stride, u
                  int64_t cs, uint8_t* scales, int64_t ss, hipStream_t stream);
 int launch_dequant(const uint8_t* codes, int64_t cs, const uint8_t* scales, int64_t ss, int64_t rows,
                    int32_t C, uint16_t* y, int64_t y_stride, hipStream_t stream);
+int launch_quant_mx(const uint16_t* x, int64_t rows, int32_t C, int64_t x_stride, uint8_t* codes, int64_t cs,
+                    uint8_t* scales, int64_t ss, hipStream_t stream);
+int launch_dequant_mx(const uint8_t* codes, int64_t cs, const uint8_t* scales, int64_t ss, int64_t rows, int32_t C,
+                      uint16_t* y, int64_t y_stride, hipStream_t stream);
 int launch_index_dense(const ScanArgs& a, int32_t B, int32_t Q, float* scores, hipStream_t stream);
 int launch_index_pool(const ScanArgs& a, int32_t B, int32_t P, float* scores, hipStream_t stream);
 
@@ -167,6 +171,7 @@ struct AttnArgs {
     int32_t K = 0;
     float scale = 0.f;
     float* out = nullptr;           // [rows][H][d]
+    bool mx = false;                // cache format: E4M3 scale per 16 channels, or MXFP4 (E8M0 per 32)
 };
 size_t attn_data_bytes(int64_t rows, int32_t K);     // data region of one attention call
 int launch_attn(const AttnArgs& a, void* ws_ctrl, void* ws_data, size_t data_bytes, hipStream_t stream);
@@ -176,6 +181,6 @@ int launch_attn_scratch(const AttnArgs& a, uint32_t* counters, void* parts, size
 
 // Host-side argument checks of the attention call (api.cpp).
 int check_attn(const uint16_t* q, int32_t H, int32_t d, const uint8_t* kc, const uint8_t* ks, const uint8_t* vc,
-               const uint8_t* vs, int64_t N, int64_t cs, int64_t ss, int32_t K, const char* who);
+               const uint8_t* vs, int64_t N, int64_t cs, int64_t ss, int32_t K, const char* who, bool mx);
 
 }  // namespace csa2

@@ -79,7 +79,7 @@ extern "C" int csa2_sparse_attn_fp4_noalloc(const uint16_t* q, int32_t B, int32_
     if (B < 0 || Q < 0) return fail(INVALID, std::string(who) + ": negative size");
     if ((int64_t)B * Q == 0) return OK;
     if (int e = check_attn(q, H, d, k_codes, k_scales, v_codes, v_scales, N, code_stride_bytes, scale_stride_bytes, K,
-                           who))
+                           who, false))
         return e;
     if (!idx || !out) return fail(INVALID, std::string(who) + ": null pointer");
     if (!(softmax_scale >= 0.f) || !std::isfinite(softmax_scale))

@@ -171,6 +171,97 @@ k_dequant(const uint8_t* __restrict__ codes, int64_t cs, const uint8_t* __restri
     }
 }
 
+// ---------------------------------------------------------------- MXFP4
+// E2M1 elements with one E8M0 scale per 32 channels: the block's scale is
+// X = 2^(floor(log2(amax)) - 2) (2 = the exponent of E2M1's largest value 6),
+// stored as the E8M0 byte floor(log2(amax)) - 2 + 127 clamped to [0, 254];
+// for bf16 amax that is max(exponent field - 2, 0), which also gives byte 0
+// for a zero block. x / X = x * 2^(127 - byte) is exact (a power of two; a
+// product below fp32's range is far below E2M1's 0.25 rounding threshold and
+// keeps its sign), so the hardware FP4 convert at unit scale rounds it to
+// nearest even with saturation, as the E4M3-scaled path does. One lane owns
+// one 32-channel block: four 16-byte loads, one 16-byte store of codes and
+// one scale byte. Inputs must be finite.
+__global__ void __launch_bounds__(kQuantThreads)
+k_quant_mx(const uint16_t* __restrict__ x, int64_t rows, int32_t bpr, int32_t bshift, int64_t x_stride,
+           uint8_t* __restrict__ codes, int64_t cs, uint8_t* __restrict__ scales, int64_t ss) {
+    const int64_t total = rows * bpr;
+    const int64_t stride = (int64_t)gridDim.x * kQuantThreads;
+    for (int64_t bid = (int64_t)blockIdx.x * kQuantThreads + threadIdx.x; bid < total; bid += stride) {
+        int64_t r;
+        int32_t b;
+        row_group(bid, bpr, bshift, r, b);
+        const uint4* src = reinterpret_cast<const uint4*>(x + r * x_stride + (int64_t)b * 32);
+        uint32_t w[16];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const uint4 v = ld_stream16(src + k);
+            w[4 * k + 0] = v.x;
+            w[4 * k + 1] = v.y;
+            w[4 * k + 2] = v.z;
+            w[4 * k + 3] = v.w;
+        }
+        uint32_t amax_bits = 0;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) amax_bits = max(amax_bits, max(w[i] & 0x7FFFu, (w[i] >> 16) & 0x7FFFu));
+        const int32_t e = (int32_t)(amax_bits >> 7) - 2;     // bf16 exponent field - 2
+        const uint32_t sc = (uint32_t)(e > 0 ? e : 0);
+        const float inv = __uint_as_float((254u - sc) << 23);  // 2^(127 - byte), exact
+        uint32_t c[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const float y0 = bf16_bits_to_f32(w[i] & 0xFFFFu) * inv;
+            const float y1 = __uint_as_float(w[i] & 0xFFFF0000u) * inv;
+            switch (i & 3) {
+                case 0: c[i >> 2] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c[i >> 2], y0, y1, 1.0f, 0); break;
+                case 1: c[i >> 2] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c[i >> 2], y0, y1, 1.0f, 1); break;
+                case 2: c[i >> 2] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c[i >> 2], y0, y1, 1.0f, 2); break;
+                default: c[i >> 2] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c[i >> 2], y0, y1, 1.0f, 3); break;
+            }
+        }
+        *reinterpret_cast<uint4*>(codes + r * cs + (int64_t)b * 16) = make_uint4(c[0], c[1], c[2], c[3]);
+        scales[r * ss + b] = (uint8_t)sc;
+    }
+}
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// MXFP4 dequantization: the hardware scaled FP4 -> bf16 convert applies the
+// block's E8M0 scale (passed as an fp32 whose exponent field is the byte),
+// exactly for every byte (0xFF gives NaN; E2M1 x 2^(byte-127) beyond bf16's
+// range gives Inf, which bf16 inputs never produce). One lane owns 8
+// channels (4 code bytes in, 16 bytes of bf16 out; a wave's stores are one
+// contiguous KiB); four such units in flight per lane.
+__global__ void __launch_bounds__(kQuantThreads)
+k_dequant_mx(const uint8_t* __restrict__ codes, int64_t cs, const uint8_t* __restrict__ scales, int64_t ss,
+             int64_t rows, int32_t upr, int32_t ushift, uint16_t* __restrict__ y, int64_t y_stride) {
+    const int64_t total = rows * upr;           // 8-channel units
+    const int64_t stride = (int64_t)gridDim.x * kQuantThreads;
+    for (int64_t uid = (int64_t)blockIdx.x * kQuantThreads + threadIdx.x; uid < total; uid += kDqInFlight * stride) {
+        int64_t r[kDqInFlight];
+        int32_t u[kDqInFlight];
+        bool ok[kDqInFlight];
+        uint32_t c[kDqInFlight], sb[kDqInFlight];
+#pragma unroll
+        for (int k = 0; k < kDqInFlight; ++k) {
+            const int64_t id = uid + k * stride;
+            ok[k] = id < total;
+            row_group(ok[k] ? id : uid, upr, ushift, r[k], u[k]);
+            c[k] = *reinterpret_cast<const uint32_t*>(codes + r[k] * cs + (int64_t)u[k] * 4);
+            sb[k] = scales[r[k] * ss + (u[k] >> 2)];
+        }
+#pragma unroll
+        for (int k = 0; k < kDqInFlight; ++k) {
+            const float X = __uint_as_float(sb[k] << 23);
+            const uint4 o = make_uint4(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c[k], X, 0)),
+                                       __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c[k], X, 1)),
+                                       __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c[k], X, 2)),
+                                       __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c[k], X, 3)));
+            if (ok[k]) *reinterpret_cast<uint4*>(y + r[k] * y_stride + (int64_t)u[k] * 8) = o;
+        }
+    }
+}
+
 // log2(n) when n is a power of two, else -1.
 static int32_t pow2_shift(int32_t n) {
     if (n <= 0 || (n & (n - 1))) return -1;
@@ -194,6 +285,26 @@ int launch_quant(const uint16_t* x, int64_t rows, int32_t C, int64_t x_stride, u
                        gpr, pow2_shift(gpr), x_stride, codes, cs, scales, ss);
     const hipError_t e = hipGetLastError();
     return e == hipSuccess ? OK : hip_fail(e, "launch k_quant");
+}
+
+int launch_quant_mx(const uint16_t* x, int64_t rows, int32_t C, int64_t x_stride, uint8_t* codes, int64_t cs,
+                    uint8_t* scales, int64_t ss, hipStream_t stream) {
+    if (rows == 0) return OK;
+    const int32_t bpr = C / 32;
+    hipLaunchKernelGGL(k_quant_mx, dim3(grid_for(rows * bpr, kQuantThreads)), dim3(kQuantThreads), 0, stream, x, rows,
+                       bpr, pow2_shift(bpr), x_stride, codes, cs, scales, ss);
+    const hipError_t e = hipGetLastError();
+    return e == hipSuccess ? OK : hip_fail(e, "launch k_quant_mx");
+}
+
+int launch_dequant_mx(const uint8_t* codes, int64_t cs, const uint8_t* scales, int64_t ss, int64_t rows, int32_t C,
+                      uint16_t* y, int64_t y_stride, hipStream_t stream) {
+    if (rows == 0) return OK;
+    const int32_t upr = C / 8;
+    hipLaunchKernelGGL(k_dequant_mx, dim3(grid_for(rows * upr, kQuantThreads)), dim3(kQuantThreads), 0, stream, codes,
+                       cs, scales, ss, rows, upr, pow2_shift(upr), y, y_stride);
+    const hipError_t e = hipGetLastError();
+    return e == hipSuccess ? OK : hip_fail(e, "launch k_dequant_mx");
 }
 
 int launch_dequant(const uint8_t* codes, int64_t cs, const uint8_t* scales, int64_t ss, int64_t rows, int32_t C,

@@ -81,6 +81,12 @@ extern "C" {
 #define CSA2_BF16 1                 /* bfloat16, stored as uint16 bit patterns */
 #define CSA2_E4M3 2                 /* OCP E4M3FN byte, no scale */
 
+/* Main KV cache formats: FP4 E2M1 with one E4M3 scale per 16 channels
+ * ([ezic] key points), or MXFP4: FP4 E2M1 with one E8M0 (power-of-two) scale
+ * per 32 channels, the OCP MX format ([jiwasawa] FP4 main KV cache). */
+#define CSA2_KV_FP4_E4M3 0
+#define CSA2_KV_MXFP4 1
+
 /* Layer modes ([zaikei] CSA2とFP4; [jiwasawa] CSA2). */
 #define CSA2_FULL 0
 #define CSA2_REINDEX 1
@@ -123,6 +129,34 @@ int kv_quant_fp4(const uint16_t* x, int64_t rows, int32_t C, int64_t x_stride,
 int kv_dequant_fp4(const uint8_t* codes, int64_t code_stride_bytes,
                    const uint8_t* scales, int64_t scale_stride_bytes,
                    int64_t rows, int32_t C, uint16_t* y, int64_t y_stride, hipStream_t stream);
+
+/*
+ * kv_quant_mxfp4 - S1 in the MXFP4 reading of the format ([jiwasawa] "FP4
+ * メイン KV Cache と SWA Bounded Replay": OCP-standard MXFP4, E2M1 elements):
+ * per row r and 32-channel block b, the shared scale is X = 2^(floor(log2(
+ * amax)) - 2) stored as the E8M0 byte floor(log2(amax)) - 2 + 127 clamped to
+ * [0, 254] (byte 0 for an all-zero block); code_i = RNE_E2M1(x_i / X) with
+ * saturation at 6 and the sign of x_i kept (R).
+ *
+ *   x             device, bf16; row r starts at x + r*x_stride (16-byte aligned rows)
+ *   C             channels per row, a positive multiple of 32
+ *   codes         device; row r's C/2 code bytes (nibble order as kv_quant_fp4) at
+ *                 codes + r*code_stride_bytes (16-byte aligned rows)
+ *   scales        device; row r's C/32 E8M0 bytes at scales + r*scale_stride_bytes
+ * Inputs must be finite.
+ */
+int kv_quant_mxfp4(const uint16_t* x, int64_t rows, int32_t C, int64_t x_stride,
+                   uint8_t* codes, int64_t code_stride_bytes,
+                   uint8_t* scales, int64_t scale_stride_bytes, hipStream_t stream);
+
+/*
+ * kv_dequant_mxfp4 - inverse image of kv_quant_mxfp4: y = E2M1(code) *
+ * 2^(scale - 127), exact in bf16 (scale byte 0xFF gives NaN). Code rows
+ * 4-byte aligned, y rows 16-byte aligned.
+ */
+int kv_dequant_mxfp4(const uint8_t* codes, int64_t code_stride_bytes,
+                     const uint8_t* scales, int64_t scale_stride_bytes,
+                     int64_t rows, int32_t C, uint16_t* y, int64_t y_stride, hipStream_t stream);
 
 /*
  * csa2_index_full - S2a, dense form: indexer scores of Q queries per sequence
@@ -217,6 +251,24 @@ int csa2_sparse_attn_fp4(const uint16_t* q, int32_t B, int32_t Q, int32_t H, int
                          float* out, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * csa2_sparse_attn_mxfp4 - csa2_sparse_attn_fp4 over an MXFP4 cache (codes as
+ * kv_quant_fp4; 4 E8M0 scale bytes per position for K and 4 for V, one per 32
+ * channels). Same arguments and semantics; scale pointers and
+ * scale_stride_bytes must be 4-byte aligned (the recommended record is 8
+ * bytes: [K scales 4 | V scales 4], 136 bytes per token with the codes).
+ * Numerics: the dequantized K and V and the bf16 query are exact bf16 matrix
+ * core operands; each softmax weight is carried as two bf16 terms (16
+ * significant bits); products accumulate in fp32. Shares the workspace rules
+ * (and csa2_sparse_attn_workspace_bytes) of csa2_sparse_attn_fp4.
+ */
+int csa2_sparse_attn_mxfp4(const uint16_t* q, int32_t B, int32_t Q, int32_t H, int32_t d,
+                           const uint8_t* k_codes, const uint8_t* k_scales,
+                           const uint8_t* v_codes, const uint8_t* v_scales,
+                           int64_t N, int64_t code_stride_bytes, int64_t scale_stride_bytes,
+                           const int32_t* idx, int32_t K, float softmax_scale,
+                           float* out, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
  * csa2_sparse_attn_fp4_noalloc - csa2_sparse_attn_fp4 for callers that cannot
  * allocate device memory or pass a workspace: code under HIP graph capture,
  * tight serving loops, harnesses that forbid allocation. Same arguments,
@@ -266,10 +318,11 @@ typedef struct {
     int32_t q_idx_dtype;    /* CSA2_F32 or CSA2_BF16 */
     int32_t k_idx_dtype;    /* CSA2_F32, CSA2_BF16 or CSA2_E4M3 */
     float softmax_scale;    /* 0 selects 1/sqrt(d) */
+    int32_t kv_format;      /* CSA2_KV_FP4_E4M3 or CSA2_KV_MXFP4: the main KV cache's format */
 } csa2_plan_params;
 
 typedef struct {
-    const uint8_t* k_codes; /* main KV cache of B sequences x N positions */
+    const uint8_t* k_codes; /* main KV cache of B sequences x N positions, in the plan's kv_format */
     const uint8_t* k_scales;
     const uint8_t* v_codes;
     const uint8_t* v_scales;

@@ -26,7 +26,7 @@ def test_header_declares_the_boundary_calls():
     names = _declared_functions()
     for n in ["kv_quant_fp4", "kv_dequant_fp4", "csa2_index_full", "csa2_index_reindex", "csa2_topk",
               "csa2_sparse_attn_fp4", "csa2_plan_create", "csa2_plan_run_decode", "csa2_prefill_full",
-              "csa2_last_error"]:
+              "csa2_last_error", "kv_quant_mxfp4", "kv_dequant_mxfp4", "csa2_sparse_attn_mxfp4"]:
         assert n in names, n
 
 
@@ -52,6 +52,25 @@ def test_quant_validation():
     _err(L.kv_quant_fp4(p, -1, 32, 32, p, 16, p, 2, None), 1, "rows")
     assert L.kv_quant_fp4(None, 0, 32, 32, None, 16, None, 2, None) == 0          # empty: no-op
     _err(L.kv_dequant_fp4(p, 4, p, 2, 10, 32, p, 32, None), 1, "code row stride")
+
+
+def test_mxfp4_validation():
+    L = C.lib()
+    p = ctypes.c_void_p(4096)
+    _err(L.kv_quant_mxfp4(p, 10, 48, 48, p, 24, p, 2, None), 1, "multiple of 32")
+    _err(L.kv_quant_mxfp4(p, 10, 64, 64, ctypes.c_void_p(4104), 32, p, 2, None), 1, "16-byte aligned")
+    _err(L.kv_quant_mxfp4(p, 10, 64, 64, p, 32, p, 1, None), 1, "scale row stride")
+    assert L.kv_quant_mxfp4(None, 0, 64, 64, None, 32, None, 2, None) == 0
+    _err(L.kv_dequant_mxfp4(p, 16, p, 2, 10, 64, p, 64, None), 1, "code row stride")
+    _err(L.csa2_sparse_attn_mxfp4(p, 1, 1, 8, 128, p, ctypes.c_void_p(4098), p, p, 10, 128, 8, p, 4, 0.1, p, p,
+                                  1 << 20, None), 1, "4-byte aligned")
+    _err(L.csa2_sparse_attn_mxfp4(p, 1, 1, 8, 128, p, p, p, p, 10, 128, 2, p, 4, 0.1, p, p, 1 << 20, None),
+         1, "stride")
+    params = C.PlanParams(K=16, P=64, H=8, d=128, d_idx=64, q_idx_dtype=1, k_idx_dtype=2, softmax_scale=0.0,
+                          kv_format=7)
+    arr = (ctypes.c_int32 * 1)(C.FULL)
+    h = ctypes.c_void_p(None)
+    _err(L.csa2_plan_create(arr, 1, ctypes.byref(params), ctypes.byref(h)), 1, "kv_format")
 
 
 def test_index_validation():
