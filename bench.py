@@ -16,6 +16,8 @@ oracle timed on a bounded sample of the same workload (cpu_baseline).
   python bench.py --copy-calibration   # also runs a known-size copy kernel (for PMC scaling)
   python bench.py --workload stack_b4_n1m --prefill --steps 3 --warmup 1   # the prefill chunk
   python bench.py --workload quant_1m_x512 --steps 20                       # kv_quant_fp4 / dequant
+  python bench.py --workload kvproj_t16384_d4096 --steps 50                 # KV write path (projection + FP4)
+  python bench.py --kv mxfp4 ...                                            # MXFP4 cache (E8M0 per 32 channels)
 """
 
 import argparse
@@ -235,6 +237,90 @@ def build_quant_input(cfg, dev):
     return x
 
 
+def build_proj_input(cfg, dev):
+    """The projection workload's hidden state [T][D] and transposed weights [C][D] on the device (bf16)."""
+    import numpy as np
+    import torch
+
+    import synth
+
+    T, D, rb = cfg["T"], cfg["D"], cfg["row_block"]
+    h = torch.empty(T, D, dtype=torch.bfloat16, device=dev)
+    for blk in range(T // rb):
+        h[blk * rb:(blk + 1) * rb].copy_(torch.from_numpy(synth.proj_hidden(cfg, blk).view(np.int16)).view(torch.bfloat16))
+    wt = torch.from_numpy(synth.proj_weights_t(cfg).view(np.int16)).view(torch.bfloat16).to(dev)
+    torch.cuda.synchronize()
+    return h, wt
+
+
+def run_proj(args, cfg, dev):
+    """The KV write path: C = H W (bf16, matrix cores) rounded to bf16 and quantized to FP4 in one kernel,
+    T tokens x D hidden into the 256 channels of one KV head; the oracle on a bounded sample of rows."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_limits
+
+    import fp4_compressed_sparse_kv_amd as C
+    import synth
+    from oracle import mxfp4 as OM
+    from oracle import project as PJ
+    from oracle import quant as OQ
+
+    T, D, Cc, rb = cfg["T"], cfg["D"], cfg["C"], cfg["row_block"]
+    mx = args.kv == "mxfp4"
+    t0 = time.perf_counter()
+    h, wt = build_proj_input(cfg, dev)
+    log(f"inputs ready in {time.perf_counter() - t0:.1f} s")
+    codes = torch.empty(T, 128, dtype=torch.uint8, device=dev)
+    scales = torch.empty(T, 8 if mx else 16, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        C.kv_project(h, wt, args.kv, codes=codes, scales=scales)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        C.kv_project(h, wt, args.kv, codes=codes, scales=scales)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    nbytes = T * D * 2 + Cc * D * 2 + T * (Cc // 2 + Cc // (32 if mx else 16))
+    flop = 2.0 * T * D * Cc
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    tflops = flop / (ms * 1e-3) / 1e12
+    out = {
+        "metric": "KV write path tokens/s (CED projection GEMM + fused FP4 quantize) + HBM GB/s",
+        "value": round(T / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16 MFMA (fp32 accumulate)", "data": "synthetic",
+        "config": {"workload": args.workload + (":mxfp4" if mx else ""), "T": T, "D": D, "C": Cc,
+                   "kv": "mxfp4 (e2m1 + e8m0 per 32 ch)" if mx else "fp4_e2m1 + e4m3 scale per 16 ch"},
+        "alg_bytes_per_call": nbytes, "flop_per_call": flop, "tflops": round(tflops, 1),
+        "mfma_frac": round(tflops / 2500.0, 4),
+        # the HBM floor (bytes / 8 TB/s) is above the matrix-core floor (FLOP / 2.5 PFLOP/s) at C = 256
+        "roofline": {"bound": "hbm", "kernel": "k_kv_project", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
+    }
+    if not args.no_cpu:
+        done, spent = 0, 0.0
+        cores = host_cores()
+        wt_h = synth.proj_weights_t(cfg)
+        quant = OM.quant_mxfp4 if mx else OQ.quant_fp4
+        with threadpool_limits(limits=cores):
+            for blk in range(T // rb):
+                hb = synth.proj_hidden(cfg, blk)                 # untimed: input generation
+                t1 = time.perf_counter()
+                quant(PJ.round_to_bf16(PJ.project_exact(hb, wt_h.T)))
+                spent += time.perf_counter() - t1
+                done += rb
+                if spent >= args.cpu_seconds:
+                    break
+        out["cpu_baseline"] = {"value": round(done / spent, 1), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+                               "sample": f"{done} of {T} tokens ({done // rb} blocks of {rb}), {spent:.1f} s with "
+                                         f"BLAS on {cores} host threads"}
+    print(json.dumps(out), flush=True)
+
+
 def run_quant(args, cfg, dev):
     """The quantize workload: kv_quant_fp4 and kv_dequant_fp4 over T x C bf16 rows (each call timed alone,
     back to back, K calls between two events), with the oracle's quantizer on a bounded sample of rows."""
@@ -439,6 +525,9 @@ def main():
             raise SystemExit(f"{args.workload} has no prefill chunk")
         torch.cuda.set_device(0)
         return run_prefill(args, cfg, torch.device("cuda", 0))
+    if "D" in cfg:
+        torch.cuda.set_device(0)
+        return run_proj(args, cfg, torch.device("cuda", 0))
     if "T" in cfg:
         torch.cuda.set_device(0)
         return run_quant(args, cfg, torch.device("cuda", 0))

@@ -18,7 +18,7 @@ import torch
 
 __all__ = [
     "Csa2Error", "lib", "F32", "BF16", "E4M3", "FULL", "REINDEX", "REUSE",
-    "kv_quant_fp4", "kv_dequant_fp4", "kv_quant_mxfp4", "kv_dequant_mxfp4", "index_full", "index_reindex", "topk",
+    "kv_quant_fp4", "kv_dequant_fp4", "kv_quant_mxfp4", "kv_dequant_mxfp4", "kv_project", "index_full", "index_reindex", "topk",
     "sparse_attn_fp4", "sparse_attn_fp4_noalloc", "KVCache", "Plan", "status_word",
 ]
 
@@ -61,6 +61,8 @@ _SIGS = {
     "kv_dequant_fp4": (ctypes.c_int, [_vp, _c_i64, _vp, _c_i64, _c_i64, _c_i32, _vp, _c_i64, _vp]),
     "kv_quant_mxfp4": (ctypes.c_int, [_vp, _c_i64, _c_i32, _c_i64, _vp, _c_i64, _vp, _c_i64, _vp]),
     "kv_dequant_mxfp4": (ctypes.c_int, [_vp, _c_i64, _vp, _c_i64, _c_i64, _c_i32, _vp, _c_i64, _vp]),
+    "csa2_kv_project": (ctypes.c_int, [_vp, _c_i64, _c_i32, _c_i64, _vp, _c_i64, _c_i32, _vp, _c_i64, _vp, _c_i64,
+                                       _vp, _c_i64, _vp]),
     "csa2_index_full": (ctypes.c_int, [_vp, _c_i32, _vp, _c_i32, _c_i32, _c_i32, _c_i64, _c_i32, _vp, _vp, _vp]),
     "csa2_index_reindex": (ctypes.c_int, [_vp, _c_i32, _vp, _c_i32, _c_i32, _c_i64, _c_i32, _vp, _c_i32, _vp, _vp]),
     "csa2_topk_workspace_bytes": (ctypes.c_int, [_c_i64, _c_i64, _c_i32, ctypes.POINTER(_c_sz)]),
@@ -215,6 +217,23 @@ def kv_dequant_mxfp4(codes, scales, C, y=None, stream=None):
     _check(lib().kv_dequant_mxfp4(_ptr(codes), codes.stride(0), _ptr(scales), scales.stride(0), T, C, _ptr(y),
                                   y.stride(0), _stream(stream)), "kv_dequant_mxfp4")
     return y
+
+
+def kv_project(h, w_t, kv_format="fp4_e4m3", codes=None, scales=None, c_out=None, stream=None):
+    """KV write path: C = h [T][D] @ w_t[256][D]^T (bf16), rounded to bf16 and quantized in one kernel into
+    codes [T][128] u8 and scales [T][16 or 8] u8 (the cache record layout; views of a KVCache's planes
+    work); c_out [T][256] bf16 receives the rounded C when given."""
+    _need_cuda(h, w_t)
+    T, D = h.shape
+    blk = 32 if kv_format == "mxfp4" else 16
+    if codes is None:
+        codes = torch.empty(T, 128, dtype=torch.uint8, device=h.device)
+    if scales is None:
+        scales = torch.empty(T, 256 // blk, dtype=torch.uint8, device=h.device)
+    _check(lib().csa2_kv_project(_ptr(h), T, D, h.stride(0), _ptr(w_t), w_t.stride(0), KV_FORMATS[kv_format],
+                                 _ptr(codes), codes.stride(0), _ptr(scales), scales.stride(0), _ptr(c_out),
+                                 c_out.stride(0) if c_out is not None else 0, _stream(stream)), "csa2_kv_project")
+    return codes, scales
 
 
 def index_full(q_idx, k_idx, q_pos=None, scores=None, stream=None):

@@ -186,6 +186,33 @@ int kv_dequant_mxfp4(const uint8_t* codes, int64_t code_stride_bytes, const uint
     return launch_dequant_mx(codes, code_stride_bytes, scales, scale_stride_bytes, rows, C, y, y_stride, stream);
 }
 
+int csa2_kv_project(const uint16_t* h, int64_t T, int32_t D, int64_t h_stride, const uint16_t* w_t, int64_t w_stride,
+                    int32_t kv_format, uint8_t* codes, int64_t code_stride_bytes, uint8_t* scales,
+                    int64_t scale_stride_bytes, uint16_t* c_out, int64_t c_stride, hipStream_t stream) {
+    g_err.clear();
+    const char* w = "csa2_kv_project";
+    if (T < 0) return fail(INVALID, std::string(w) + ": T < 0");
+    if (D <= 0 || D % 64 != 0) return fail(INVALID, std::string(w) + ": D must be a positive multiple of 64");
+    if (kv_format != CSA2_KV_FP4_E4M3 && kv_format != CSA2_KV_MXFP4)
+        return fail(INVALID, std::string(w) + ": kv_format must be CSA2_KV_FP4_E4M3 or CSA2_KV_MXFP4");
+    const bool mx = kv_format == CSA2_KV_MXFP4;
+    if (h_stride < D || w_stride < D) return fail(INVALID, std::string(w) + ": row stride < D");
+    if (code_stride_bytes < 128) return fail(INVALID, std::string(w) + ": code row stride < 128 bytes");
+    if (scale_stride_bytes < (mx ? 8 : 16)) return fail(INVALID, std::string(w) + ": scale row stride too small");
+    if (c_out && c_stride < 256) return fail(INVALID, std::string(w) + ": c_out row stride < 256");
+    if (T == 0) return OK;
+    if (!h || !w_t || !codes || !scales) return fail(INVALID, std::string(w) + ": null pointer");
+    if (!aligned(h, 16) || (h_stride * 2) % 16 || !aligned(w_t, 16) || (w_stride * 2) % 16)
+        return fail(INVALID, std::string(w) + ": h and w_t rows must be 16-byte aligned");
+    const int ca = mx ? 16 : 8;
+    if (!aligned(codes, ca) || code_stride_bytes % ca)
+        return fail(INVALID, std::string(w) + ": code rows must be " + std::to_string(ca) + "-byte aligned");
+    if (c_out && (!aligned(c_out, 16) || (c_stride * 2) % 16))
+        return fail(INVALID, std::string(w) + ": c_out rows must be 16-byte aligned");
+    return launch_kv_project(h, T, D, h_stride, w_t, w_stride, mx, codes, code_stride_bytes, scales,
+                             scale_stride_bytes, c_out, c_stride, stream);
+}
+
 int csa2_index_full(const void* q_idx, int32_t q_dtype, const void* k_idx, int32_t k_dtype, int32_t B, int32_t Q,
                     int64_t N, int32_t d_idx, const int64_t* q_pos, float* scores, hipStream_t stream) {
     g_err.clear();

@@ -156,6 +156,9 @@ int launch_quant_mx(const uint16_t* x, int64_t rows, int32_t C, int64_t x_stride
                     uint8_t* scales, int64_t ss, hipStream_t stream);
 int launch_dequant_mx(const uint8_t* codes, int64_t cs, const uint8_t* scales, int64_t ss, int64_t rows, int32_t C,
                       uint16_t* y, int64_t y_stride, hipStream_t stream);
+int launch_kv_project(const uint16_t* h, int64_t T, int32_t D, int64_t hs, const uint16_t* wt, int64_t wsd, bool mx,
+                      uint8_t* codes, int64_t cs, uint8_t* scales, int64_t ss, uint16_t* cout, int64_t cos,
+                      hipStream_t stream);
 int launch_index_dense(const ScanArgs& a, int32_t B, int32_t Q, float* scores, hipStream_t stream);
 int launch_index_pool(const ScanArgs& a, int32_t B, int32_t P, float* scores, hipStream_t stream);
 

@@ -159,6 +159,33 @@ int kv_dequant_mxfp4(const uint8_t* codes, int64_t code_stride_bytes,
                      int64_t rows, int32_t C, uint16_t* y, int64_t y_stride, hipStream_t stream);
 
 /*
+ * csa2_kv_project - the KV write path ([jiwasawa] "Causal Encoder-Decoder
+ * (CED) アーキテクチャ", its projection equation; [zaikei] "■CEDで入力処理の
+ * 計算量を削減"): a decoder layer's global KV rows are projected from the
+ * encoder's last hidden state, C = H W, and stored in FP4 in the same kernel.
+ *
+ * R: C has 256 channels, one shared KV head with K in channels 0..127 and V in
+ * 128..255; each element is the product-sum (bf16 inputs, fp32 accumulation)
+ * rounded once to bf16 (nearest even), then quantized per group exactly as
+ * kv_quant_fp4 (kv_format CSA2_KV_FP4_E4M3) or kv_quant_mxfp4 (CSA2_KV_MXFP4)
+ * would quantize that bf16 row.
+ *
+ *   h       device [T][D] bf16 (row r at h + r*h_stride), D a positive multiple of 64
+ *   w_t     device [256][D] bf16: W transposed, row c holds the D weights of output
+ *           channel c (row c at w_t + c*w_stride)
+ *   codes   device; token r's 128 code bytes [K 64 | V 64] at codes + r*code_stride_bytes
+ *           (8-byte aligned rows; 16-byte for MXFP4) - the main KV cache record layout
+ *   scales  device; token r's scale bytes [K | V] (8 + 8 E4M3, or 4 + 4 E8M0) at
+ *           scales + r*scale_stride_bytes
+ *   c_out   device [T][256] bf16 (row r at c_out + r*c_stride), the rounded C itself, or NULL
+ * h, w_t and c_out rows must be 16-byte aligned.
+ */
+int csa2_kv_project(const uint16_t* h, int64_t T, int32_t D, int64_t h_stride,
+                    const uint16_t* w_t, int64_t w_stride, int32_t kv_format,
+                    uint8_t* codes, int64_t code_stride_bytes, uint8_t* scales, int64_t scale_stride_bytes,
+                    uint16_t* c_out, int64_t c_stride, hipStream_t stream);
+
+/*
  * csa2_index_full - S2a, dense form: indexer scores of Q queries per sequence
  * against all N indexer keys of that sequence ([jiwasawa] CSA2: a Full layer
  * computes its own indexer Q and scores the whole context; [zaikei] CSA2とFP4:

@@ -20,6 +20,10 @@ Workloads (one decode query per sequence and layer; context positions 0..N-1):
   stack_b4_n1m       the stack at B=4, N=1,048,576 plus a prefill chunk of the
                      last 4096 positions of each sequence through the Full
                      layer (causal), K=2048.
+  kvproj_t16384_d4096  the KV write path of that prefill chunk: 4 x 4096 tokens
+                     of encoder hidden state (D = 4096, bf16 N(0,1)) projected
+                     by one decoder layer's KV weights (256 x 4096 bf16,
+                     N(0, 1/D)) into K and V of the shared head.
 """
 
 import numpy as np
@@ -36,13 +40,14 @@ WORKLOADS = {
     "stack_b32_n262144": dict(wid=3, B=32, N=262144, H=16, d=128, d_idx=64, K=2048, P=8192,
                               modes=("full", "reindex", "reuse", "reuse"), q_idx_dtype="bf16",
                               k_idx_dtype="e4m3", outlier_frac=0.005, seed=0),
+    "kvproj_t16384_d4096": dict(wid=5, T=16384, D=4096, C=256, seed=0, row_block=1024),
     "stack_b4_n1m": dict(wid=4, B=4, N=1048576, H=16, d=128, d_idx=64, K=2048, P=8192,
                          modes=("full", "reindex", "reuse", "reuse"), q_idx_dtype="bf16",
                          k_idx_dtype="e4m3", outlier_frac=0.005, seed=0, prefill_Q=4096),
 }
 
 # tensor ids for the substreams
-_T_K, _T_V, _T_KOUT, _T_VOUT, _T_Q, _T_QIDX, _T_KIDX, _T_ROWS, _T_PQ, _T_PQIDX = range(10)
+_T_K, _T_V, _T_KOUT, _T_VOUT, _T_Q, _T_QIDX, _T_KIDX, _T_ROWS, _T_PQ, _T_PQIDX, _T_HID, _T_WKV = range(12)
 
 
 def rng(seed, wid, tensor, index=0):
@@ -136,6 +141,19 @@ def quant_rows(cfg, block):
     g = rng(cfg["seed"], cfg["wid"], _T_ROWS, block)
     scale = np.power(np.float32(10.0), g.uniform(-3.0, 3.0, size=(rb, 1)).astype(np.float32))
     x = g.standard_normal((rb, C), dtype=np.float32) * scale.astype(np.float32)
+    return to_bf16_bits(x)
+
+
+def proj_hidden(cfg, block):
+    """Rows [block*row_block, (block+1)*row_block) of the projection workload's hidden state: bf16 N(0,1)."""
+    g = rng(cfg["seed"], cfg["wid"], _T_HID, block)
+    return to_bf16_bits(g.standard_normal((cfg["row_block"], cfg["D"]), dtype=np.float32))
+
+
+def proj_weights_t(cfg):
+    """The KV projection weights, transposed ([C][D], row c = output channel c): bf16 N(0, 1/D)."""
+    g = rng(cfg["seed"], cfg["wid"], _T_WKV, 0)
+    x = g.standard_normal((cfg["C"], cfg["D"]), dtype=np.float32) * np.float32(1.0 / np.sqrt(cfg["D"]))
     return to_bf16_bits(x)
 
 

@@ -26,7 +26,7 @@ def test_header_declares_the_boundary_calls():
     names = _declared_functions()
     for n in ["kv_quant_fp4", "kv_dequant_fp4", "csa2_index_full", "csa2_index_reindex", "csa2_topk",
               "csa2_sparse_attn_fp4", "csa2_plan_create", "csa2_plan_run_decode", "csa2_prefill_full",
-              "csa2_last_error", "kv_quant_mxfp4", "kv_dequant_mxfp4", "csa2_sparse_attn_mxfp4"]:
+              "csa2_last_error", "kv_quant_mxfp4", "kv_dequant_mxfp4", "csa2_sparse_attn_mxfp4", "csa2_kv_project"]:
         assert n in names, n
 
 
@@ -71,6 +71,18 @@ def test_mxfp4_validation():
     arr = (ctypes.c_int32 * 1)(C.FULL)
     h = ctypes.c_void_p(None)
     _err(L.csa2_plan_create(arr, 1, ctypes.byref(params), ctypes.byref(h)), 1, "kv_format")
+
+
+def test_kv_project_validation():
+    L = C.lib()
+    p = ctypes.c_void_p(4096)
+    _err(L.csa2_kv_project(p, 10, 96, 96, p, 96, 0, p, 128, p, 16, None, 0, None), 1, "multiple of 64")
+    _err(L.csa2_kv_project(p, 10, 128, 128, p, 128, 3, p, 128, p, 16, None, 0, None), 1, "kv_format")
+    _err(L.csa2_kv_project(p, 10, 128, 128, p, 128, 0, p, 64, p, 16, None, 0, None), 1, "code row stride")
+    _err(L.csa2_kv_project(p, 10, 128, 128, p, 128, 1, ctypes.c_void_p(4104), 128, p, 8, None, 0, None), 1,
+         "16-byte aligned")
+    _err(L.csa2_kv_project(None, 10, 128, 128, p, 128, 0, p, 128, p, 16, None, 0, None), 1, "null")
+    assert L.csa2_kv_project(None, 0, 128, 128, None, 128, 0, None, 128, None, 16, None, 0, None) == 0
 
 
 def test_index_validation():
