@@ -66,3 +66,36 @@ def sparse_attn(q_bits, kv, idx, softmax_scale=None):
     logits = (q @ K_hat.T) * scale                                   # (H, k)
     w = np.exp(logits - logits.max(axis=1, keepdims=True))
     return (w @ V_hat) / w.sum(axis=1, keepdims=True)
+
+
+def sparse_attn_swa(q_bits, kv, idx, win_k_bits, win_v_bits, softmax_scale=None):
+    """One query of a decoder layer with a sliding-window branch beside CSA2: one softmax over the
+    selected positions of the FP4 main KV cache and the window's own KV rows.
+
+    [zaikei] "■CEDで入力処理の計算量を削減": each decoder layer keeps a sliding-window attention over the
+    most recent tokens; [jiwasawa] "FP4 メイン KV Cache と SWA Bounded Replay": the window's KV is kept
+    apart from the FP4 main cache. Readings: the window KV is bf16 (win_k_bits, win_v_bits: (W, d) bit
+    patterns, the valid rows of the window), attended by every head with the same scale as the sparse
+    part; its rows are separate keys of the same softmax (no position is merged with a main-cache one).
+    Returns (H, d) fp64; zeros when there is neither a valid position nor a window row.
+    """
+    q = bf16_decode(q_bits)
+    H, d = q.shape
+    scale = 1.0 / np.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    idx = np.asarray(idx, dtype=np.int64)
+    sel = idx[idx >= 0]
+    Ks, Vs = [], []
+    if sel.size:
+        Ks.append(kv_rows(kv, "k", sel, d))
+        Vs.append(kv_rows(kv, "v", sel, d))
+    wk = bf16_decode(np.asarray(win_k_bits, dtype=np.uint16).reshape(-1, d))
+    wv = bf16_decode(np.asarray(win_v_bits, dtype=np.uint16).reshape(-1, d))
+    if wk.shape[0]:
+        Ks.append(wk)
+        Vs.append(wv)
+    if not Ks:
+        return np.zeros((H, d))
+    K_all, V_all = np.concatenate(Ks), np.concatenate(Vs)
+    logits = (q @ K_all.T) * scale
+    w = np.exp(logits - logits.max(axis=1, keepdims=True))
+    return (w @ V_all) / w.sum(axis=1, keepdims=True)

@@ -23,7 +23,7 @@ Readings:
 
 import numpy as np
 
-from .attention import sparse_attn
+from .attention import sparse_attn, sparse_attn_swa
 from .scores import index_scores, pool_scores
 from .topk import topk
 
@@ -49,7 +49,9 @@ def run_decode(modes, cache, layers, K, P=None, softmax_scale=None):
     cache: dict with 'k_codes', 'k_scales', 'v_codes', 'v_scales' (main KV,
     [N][d/2] and [N][d/16]), 'k_idx' ([N][d_idx] stored), 'k_idx_dtype'.
     layers: list (one per layer) of dicts with 'q' ((H, d) bf16 bits) and, for
-    Full and Reindex layers, 'q_idx' ((d_idx,) stored) and 'q_idx_dtype'.
+    Full and Reindex layers, 'q_idx' ((d_idx,) stored) and 'q_idx_dtype'; a
+    layer with a sliding-window branch also has 'win_k', 'win_v' ((w, d) bf16
+    bits: its window's valid rows).
     Returns a list of dicts per layer: 'idx' (K,), 'out' (H, d) fp64 and, for
     the first Full layer when the plan has a Reindex, 'pool' (P,).
     """
@@ -72,7 +74,10 @@ def run_decode(modes, cache, layers, K, P=None, softmax_scale=None):
         else:
             idx = prev_idx.copy()
         res["idx"] = idx
-        res["out"] = sparse_attn(layer["q"], cache, idx, softmax_scale)
+        if layer.get("win_k") is not None:      # the layer's sliding-window branch, in the same softmax
+            res["out"] = sparse_attn_swa(layer["q"], cache, idx, layer["win_k"], layer["win_v"], softmax_scale)
+        else:
+            res["out"] = sparse_attn(layer["q"], cache, idx, softmax_scale)
         results.append(res)
         prev_idx = idx
     return results

@@ -188,3 +188,33 @@ def test_attention_bf16_rows_equals_quantized_planes(seed):
     # a one-position list returns that row of V exactly, from either input form
     out = A.sparse_attn(qb, rows, np.array([-1, 77, -1]))
     assert np.array_equal(out, np.broadcast_to(Q.dequant_fp4(vc, vs, d)[77], (H, d)))
+
+
+def test_swa_attention_pins():
+    """Sliding-window branch: with no window rows it is the sparse attention; with no sparse positions it is
+    dense attention over the window (torch SDPA in fp64); a window row equal to a selected main-cache row
+    counts twice (two keys of one softmax); both parts together equal SDPA over the concatenated keys."""
+    rng = np.random.default_rng(7)
+    N, H, d, Wn = 60, 4, 128, 24
+    kv = _kv(rng, N, d)
+    qb = synth.to_bf16_bits(rng.standard_normal((H, d)).astype(np.float32))
+    wk = synth.to_bf16_bits(rng.standard_normal((Wn, d)).astype(np.float32))
+    wv = synth.to_bf16_bits(rng.standard_normal((Wn, d)).astype(np.float32))
+    idx = np.array([3, 17, -1, 40, 41])
+    empty = np.zeros((0, d), dtype=np.uint16)
+    assert np.array_equal(A.sparse_attn_swa(qb, kv, idx, empty, empty), A.sparse_attn(qb, kv, idx))
+    q = torch.from_numpy(F.bf16_decode(qb))
+    Kw, Vw = torch.from_numpy(F.bf16_decode(wk)), torch.from_numpy(F.bf16_decode(wv))
+    ref = torch.nn.functional.scaled_dot_product_attention(q[None], Kw[None], Vw[None])[0].numpy()
+    np.testing.assert_allclose(A.sparse_attn_swa(qb, kv, np.array([-1, -1]), wk, wv), ref, rtol=1e-12, atol=1e-12)
+    Kh = torch.from_numpy(Q.dequant_fp4(kv["k_codes"], kv["k_scales"], d))[[3, 17, 40, 41]]
+    Vh = torch.from_numpy(Q.dequant_fp4(kv["v_codes"], kv["v_scales"], d))[[3, 17, 40, 41]]
+    ref = torch.nn.functional.scaled_dot_product_attention(q[None], torch.cat([Kh, Kw])[None],
+                                                           torch.cat([Vh, Vw])[None])[0].numpy()
+    np.testing.assert_allclose(A.sparse_attn_swa(qb, kv, idx, wk, wv), ref, rtol=1e-12, atol=1e-12)
+    # a window row identical to main-cache row 3 (as bf16 of its dequantized values) is a second key
+    k3 = synth.to_bf16_bits(Q.dequant_fp4(kv["k_codes"], kv["k_scales"], d)[3:4].astype(np.float32))
+    v3 = synth.to_bf16_bits(Q.dequant_fp4(kv["v_codes"], kv["v_scales"], d)[3:4].astype(np.float32))
+    two = A.sparse_attn_swa(qb, kv, np.array([3]), k3, v3)
+    np.testing.assert_allclose(two, A.sparse_attn(qb, kv, np.array([3])), rtol=1e-12)
+    assert np.all(A.sparse_attn_swa(qb, kv, np.array([-1]), empty, empty) == 0)
