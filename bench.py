@@ -41,13 +41,14 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def alg_bytes(cfg, kv="fp4_e4m3"):
+def alg_bytes(cfg, kv="fp4_e4m3", swa=0):
     """Algorithmic bytes of one step (per sequence sums x B) and of the Full selection kernel.
 
     Full    = 2*d_I + N*d_I*b_k + 4P (when a Reindex follows) + 4K + A
     Reindex = 2*d_I + 4P + P*d_I*b_k + 4K + A
     Reuse   = A,  A = 4K + 2*H*d + K*2*(d/2 + d/g) + 4*H*d
-    with g = 16 channels per scale (E4M3 scales) or 32 (MXFP4).
+    with g = 16 channels per scale (E4M3 scales) or 32 (MXFP4); a sliding window of W bf16 rows
+    per layer adds 2*W*d*2 (its K and V rows) to A.
     """
     B, N, K, H, d, dI = cfg["B"], cfg["N"], cfg["K"], cfg["H"], cfg["d"], cfg["d_idx"]
     P = cfg.get("P") or 0
@@ -56,7 +57,7 @@ def alg_bytes(cfg, kv="fp4_e4m3"):
     modes = list(cfg["modes"])
     has_re = "reindex" in modes
     g = 32 if kv == "mxfp4" else 16
-    A = 4 * K + 2 * H * d + K * 2 * (d // 2 + d // g) + 4 * H * d
+    A = 4 * K + 2 * H * d + K * 2 * (d // 2 + d // g) + 4 * H * d + 2 * swa * d * 2
     per_seq = 0
     full_sel = 0
     first_full = True
@@ -94,7 +95,7 @@ def measured_traffic(workload):
     return t.get("traffic_bytes_per_launch")
 
 
-def build_inputs(cfg, dev, query_set=0, kv="fp4_e4m3"):
+def build_inputs(cfg, dev, query_set=0, kv="fp4_e4m3", swa=0):
     import numpy as np
     import torch
 
@@ -138,6 +139,9 @@ def build_inputs(cfg, dev, query_set=0, kv="fp4_e4m3"):
         layers.append(dict(q=bf(q), q_idx=key_t(qi, cfg["q_idx_dtype"]),
                            out=torch.empty(B, cfg["H"], cfg["d"], dtype=torch.float32, device=dev),
                            idx_out=torch.empty(B, cfg["K"], dtype=torch.int32, device=dev)))
+        if swa:
+            wk, wv = synth.window_kv(cfg, ql, swa)
+            layers[-1]["win_k"], layers[-1]["win_v"] = bf(wk), bf(wv)
     if cfg.get("P") and "reindex" in cfg["modes"]:
         layers[0]["pool_out"] = torch.empty(B, cfg["P"], dtype=torch.int32, device=dev)
     torch.cuda.synchronize()
@@ -164,6 +168,9 @@ def query_sets(cfg, dev, layers, nsets):
             d = dict(layers[li])
             d["q"] = _to_dev_bf16(q, dev)
             d["q_idx"] = _to_dev_key(qi, cfg["q_idx_dtype"], dev)
+            if "win_k" in d:
+                wk, wv = synth.window_kv(cfg, ql, d["win_k"].shape[1])
+                d["win_k"], d["win_v"] = _to_dev_bf16(wk, dev), _to_dev_bf16(wv, dev)
             cur.append(d)
         sets.append(cur)
     return sets
@@ -191,7 +198,7 @@ def host_cores():
     return len(os.sched_getaffinity(0))
 
 
-def cpu_baseline(cfg, budget_s, kv="fp4_e4m3"):
+def cpu_baseline(cfg, budget_s, kv="fp4_e4m3", swa=0):
     """The oracle, as it stands, on whole sequences of the same workload until ~budget_s of CPU work."""
     import numpy as np
     from threadpoolctl import threadpool_limits
@@ -209,6 +216,10 @@ def cpu_baseline(cfg, budget_s, kv="fp4_e4m3"):
             cache = dict(k_bf16=kb, v_bf16=vb, k_idx=synth.k_idx(cfg, b), k_idx_dtype=cfg["k_idx_dtype"], format=kv)
             layers = [dict(q=synth.q_bf16(cfg, li, b)[0], q_idx=synth.q_idx(cfg, li, b)[0],
                            q_idx_dtype=cfg["q_idx_dtype"]) for li in range(len(modes))]
+            if swa:
+                for li, L in enumerate(layers):
+                    wk, wv = synth.window_kv(cfg, li, swa)
+                    L["win_k"], L["win_v"] = wk[b], wv[b]
             t0 = time.perf_counter()
             OP.run_decode(modes, cache, layers, cfg["K"], cfg.get("P"), softmax_scale=scale)
             spent += time.perf_counter() - t0
@@ -499,6 +510,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--kv", default="fp4_e4m3", choices=["fp4_e4m3", "mxfp4"],
                     help="main KV cache format: E4M3 scale per 16 channels, or MXFP4 (E8M0 per 32)")
+    ap.add_argument("--swa", type=int, default=0,
+                    help="decode: every layer also attends to a sliding window of this many bf16 rows")
     ap.add_argument("--query-sets", type=int, default=4,
                     help="decode: timed steps rotate through this many seeded query sets")
     ap.add_argument("--copy-calibration", action="store_true")
@@ -536,10 +549,11 @@ def main():
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     t0 = time.perf_counter()
-    cache, layers = build_inputs(cfg, dev, kv=args.kv)
+    cache, layers = build_inputs(cfg, dev, kv=args.kv, swa=args.swa)
     log(f"inputs ready in {time.perf_counter() - t0:.1f} s")
     plan = C.Plan(cfg["modes"], K=cfg["K"], P=cfg.get("P") or 0, H=cfg["H"], d=cfg["d"], d_idx=cfg["d_idx"],
-                  q_idx_dtype=cfg["q_idx_dtype"], k_idx_dtype=cfg["k_idx_dtype"], kv_format=args.kv)
+                  q_idx_dtype=cfg["q_idx_dtype"], k_idx_dtype=cfg["k_idx_dtype"], kv_format=args.kv,
+                  swa_window=args.swa)
     stream = torch.cuda.current_stream()
     sets = query_sets(cfg, dev, layers, args.query_sets)
     ws = plan.decode_workspace(cache)
@@ -605,7 +619,7 @@ def main():
         torch.cuda.synchronize()
         del x, y
 
-    step_bytes, sel_bytes = alg_bytes(cfg, args.kv)
+    step_bytes, sel_bytes = alg_bytes(cfg, args.kv, args.swa)
     qps = cfg["B"] / (ms * 1e-3)
     sel_ms = slot_ms[0]
     achieved = sel_bytes / (sel_ms * 1e-3) / 1e9
@@ -623,7 +637,8 @@ def main():
         "vs_baseline": None,
         "dtype": "f64/f32",
         "data": "synthetic",
-        "config": {"workload": args.workload + (":mxfp4" if args.kv == "mxfp4" else ""), "B": cfg["B"],
+        "config": {"workload": args.workload + (":mxfp4" if args.kv == "mxfp4" else "") +
+                               (f":swa{args.swa}" if args.swa else ""), "B": cfg["B"], "swa_window": args.swa,
                    "N": cfg["N"], "modes": list(cfg["modes"]),
                    "H": cfg["H"], "d": cfg["d"], "d_idx": cfg["d_idx"], "K": cfg["K"], "P": cfg.get("P"),
                    "kv": "mxfp4 (e2m1 + e8m0 per 32 ch)" if args.kv == "mxfp4" else "fp4_e2m1 + e4m3 scale per 16 ch",
@@ -647,7 +662,7 @@ def main():
     }
     if not args.no_cpu:
         t0 = time.perf_counter()
-        out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds, args.kv)
+        out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds, args.kv, args.swa)
         log(f"cpu baseline in {time.perf_counter() - t0:.1f} s")
     print(json.dumps(out), flush=True)
 

@@ -19,7 +19,7 @@ import torch
 __all__ = [
     "Csa2Error", "lib", "F32", "BF16", "E4M3", "FULL", "REINDEX", "REUSE",
     "kv_quant_fp4", "kv_dequant_fp4", "kv_quant_mxfp4", "kv_dequant_mxfp4", "kv_project", "index_full", "index_reindex", "topk",
-    "sparse_attn_fp4", "sparse_attn_fp4_noalloc", "KVCache", "Plan", "status_word",
+    "sparse_attn_fp4", "sparse_attn_swa", "sparse_attn_fp4_noalloc", "KVCache", "Plan", "status_word",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcsa2.so")
@@ -42,7 +42,8 @@ KV_FORMATS = {"fp4_e4m3": KV_FP4_E4M3, "mxfp4": KV_MXFP4}
 
 class PlanParams(ctypes.Structure):
     _fields_ = [("K", _c_i32), ("P", _c_i32), ("H", _c_i32), ("d", _c_i32), ("d_idx", _c_i32),
-                ("q_idx_dtype", _c_i32), ("k_idx_dtype", _c_i32), ("softmax_scale", _c_f32), ("kv_format", _c_i32)]
+                ("q_idx_dtype", _c_i32), ("k_idx_dtype", _c_i32), ("softmax_scale", _c_f32), ("kv_format", _c_i32),
+                ("swa_window", _c_i32)]
 
 
 class CacheDesc(ctypes.Structure):
@@ -51,7 +52,8 @@ class CacheDesc(ctypes.Structure):
 
 
 class LayerIO(ctypes.Structure):
-    _fields_ = [("q", _vp), ("q_idx", _vp), ("out", _vp), ("idx_out", _vp), ("pool_out", _vp)]
+    _fields_ = [("q", _vp), ("q_idx", _vp), ("out", _vp), ("idx_out", _vp), ("pool_out", _vp),
+                ("win_k", _vp), ("win_v", _vp), ("win_len", _vp)]
 
 
 _SIGS = {
@@ -72,6 +74,11 @@ _SIGS = {
                                             _c_i64, _vp, _c_i32, _c_f32, _vp, _vp, _c_sz, _vp]),
     "csa2_sparse_attn_mxfp4": (ctypes.c_int, [_vp, _c_i32, _c_i32, _c_i32, _c_i32, _vp, _vp, _vp, _vp, _c_i64, _c_i64,
                                               _c_i64, _vp, _c_i32, _c_f32, _vp, _vp, _c_sz, _vp]),
+    "csa2_sparse_attn_swa_workspace_bytes": (ctypes.c_int, [_c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
+                                                            ctypes.POINTER(_c_sz)]),
+    "csa2_sparse_attn_swa": (ctypes.c_int, [_vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _vp, _vp, _vp, _vp, _c_i64,
+                                            _c_i64, _c_i64, _vp, _c_i32, _vp, _vp, _c_i64, _c_i32, _vp, _c_f32, _vp,
+                                            _vp, _c_sz, _vp]),
     "csa2_sparse_attn_fp4_noalloc": (ctypes.c_int, [_vp, _c_i32, _c_i32, _c_i32, _c_i32, _vp, _vp, _vp, _vp, _c_i64,
                                                     _c_i64, _c_i64, _vp, _c_i32, _c_f32, _vp, _vp]),
     "csa2_plan_create": (ctypes.c_int, [ctypes.POINTER(_c_i32), _c_i32, ctypes.POINTER(PlanParams),
@@ -346,6 +353,30 @@ def sparse_attn_fp4(q, cache, idx, softmax_scale=None, out=None, stream=None, ws
     return out
 
 
+def sparse_attn_swa(q, cache, idx, win_k, win_v, win_len=None, softmax_scale=None, out=None, stream=None, ws=None):
+    """Sparse attention plus a sliding-window branch in one softmax. q [B][Q][H][d] bf16, idx [B][Q][K];
+    win_k, win_v [B][Q][W][d] bf16 (each query row's window rows); win_len [B*Q] int32 or None (all W)."""
+    _need_cuda(q, idx, win_k, win_v, win_len)
+    B, Q, H, d = q.shape
+    K = idx.shape[-1]
+    W = win_k.shape[-2]
+    if out is None:
+        out = torch.empty(B, Q, H, d, dtype=torch.float32, device=q.device)
+    scale = 0.0 if softmax_scale is None else softmax_scale
+    nb = ctypes.c_size_t(0)
+    _check(lib().csa2_sparse_attn_swa_workspace_bytes(B, Q, H, d, K, W, ctypes.byref(nb)),
+           "csa2_sparse_attn_swa_workspace_bytes")
+    if ws is None:
+        ws = workspace(nb.value, q.device, "attn")
+    c = cache.desc()
+    rs = win_k.stride(-3) if win_k.dim() >= 3 else W * d
+    _check(lib().csa2_sparse_attn_swa(_ptr(q), B, Q, H, d, KV_FORMATS[cache.kv_format], c.k_codes, c.k_scales,
+                                      c.v_codes, c.v_scales, cache.N, c.code_stride_bytes, c.scale_stride_bytes,
+                                      _ptr(idx), K, _ptr(win_k), _ptr(win_v), rs, W, _ptr(win_len), scale,
+                                      _ptr(out), _ptr(ws), ws.numel(), _stream(stream)), "csa2_sparse_attn_swa")
+    return out
+
+
 def sparse_attn_fp4_noalloc(q, cache, idx, softmax_scale=None, out=None, stream=None):
     """sparse_attn_fp4 through the library's allocation-free entry point (scratch in a fixed device
     array; calls that may overlap on one device race)."""
@@ -366,12 +397,12 @@ class Plan:
     """A static Full / Reindex / Reuse layer plan (csa2_plan_*)."""
 
     def __init__(self, modes, K, P=0, H=16, d=128, d_idx=64, q_idx_dtype="bf16", k_idx_dtype="e4m3",
-                 softmax_scale=0.0, kv_format="fp4_e4m3"):
+                 softmax_scale=0.0, kv_format="fp4_e4m3", swa_window=0):
         codes = [MODE_CODES[m] if isinstance(m, str) else int(m) for m in modes]
         arr = (_c_i32 * len(codes))(*codes)
         self.modes = list(codes)
         self.params = PlanParams(K, P or 0, H, d, d_idx, DTYPE_CODES[q_idx_dtype], DTYPE_CODES[k_idx_dtype],
-                                 softmax_scale, KV_FORMATS[kv_format])
+                                 softmax_scale, KV_FORMATS[kv_format], swa_window)
         h = ctypes.c_void_p(None)
         _check(lib().csa2_plan_create(arr, len(codes), ctypes.byref(self.params), ctypes.byref(h)), "csa2_plan_create")
         self._h = h
@@ -393,7 +424,8 @@ class Plan:
 
     def run_decode(self, cache, layers, ws=None, stream=None, check=True):
         """layers: list of dicts with 'q' [B][H][d] bf16, 'q_idx' [B][d_idx], 'out' [B][H][d] fp32 and
-        optional 'idx_out' [B][K] int32, 'pool_out' [B][P] int32.
+        optional 'idx_out' [B][K] int32, 'pool_out' [B][P] int32; with swa_window W > 0 also 'win_k',
+        'win_v' [B][W][d] bf16 and optional 'win_len' [B] int32.
         check: synchronize and raise Csa2Error if the workspace status word is nonzero (pass False in
         timing loops and read status_word(plan.decode_workspace(cache)) afterwards)."""
         B, N = cache.B, cache.N
@@ -401,10 +433,11 @@ class Plan:
             ws = self.decode_workspace(cache)
         io = (LayerIO * len(layers))()
         for i, L in enumerate(layers):
-            io[i] = LayerIO(L["q"].data_ptr(), L["q_idx"].data_ptr() if L.get("q_idx") is not None else None,
-                            L["out"].data_ptr(),
-                            L["idx_out"].data_ptr() if L.get("idx_out") is not None else None,
-                            L["pool_out"].data_ptr() if L.get("pool_out") is not None else None)
+            def p(key):
+                t = L.get(key)
+                return t.data_ptr() if t is not None else None
+            io[i] = LayerIO(L["q"].data_ptr(), p("q_idx"), L["out"].data_ptr(), p("idx_out"), p("pool_out"),
+                            p("win_k"), p("win_v"), p("win_len"))
         desc = cache.desc()
         _check(lib().csa2_plan_run_decode(self._h, ctypes.byref(desc), io, B, N, _ptr(ws), ws.numel(),
                                           _stream(stream)), "csa2_plan_run_decode")

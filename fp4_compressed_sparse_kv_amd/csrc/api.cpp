@@ -370,6 +370,71 @@ int csa2_sparse_attn_mxfp4(const uint16_t* q, int32_t B, int32_t Q, int32_t H, i
     return launch_attn(a, ws, static_cast<uint8_t*>(ws) + kCtrlBytes, ws_bytes - kCtrlBytes, stream);
 }
 
+int csa2_sparse_attn_swa_workspace_bytes(int32_t B, int32_t Q, int32_t H, int32_t d, int32_t K, int32_t W,
+                                         size_t* bytes) {
+    g_err.clear();
+    if (!bytes) return fail(INVALID, "csa2_sparse_attn_swa_workspace_bytes: bytes is null");
+    if (B < 0 || Q < 0 || H < 1 || H > 16 || d != 128 || K < 1 || W < 0)
+        return fail(INVALID, "csa2_sparse_attn_swa_workspace_bytes: bad sizes");
+    *bytes = align_up(kCtrlBytes + attn_data_bytes((int64_t)B * Q, K, W));
+    return OK;
+}
+
+int csa2_sparse_attn_swa(const uint16_t* q, int32_t B, int32_t Q, int32_t H, int32_t d, int32_t kv_format,
+                         const uint8_t* k_codes, const uint8_t* k_scales, const uint8_t* v_codes,
+                         const uint8_t* v_scales, int64_t N, int64_t code_stride_bytes, int64_t scale_stride_bytes,
+                         const int32_t* idx, int32_t K, const uint16_t* win_k, const uint16_t* win_v,
+                         int64_t win_row_stride, int32_t W, const int32_t* win_len, float softmax_scale, float* out,
+                         void* ws, size_t ws_bytes, hipStream_t stream) {
+    g_err.clear();
+    const char* who = "csa2_sparse_attn_swa";
+    if (B < 0 || Q < 0 || W < 0) return fail(INVALID, std::string(who) + ": negative size");
+    if ((int64_t)B * Q == 0) return OK;
+    if (kv_format != CSA2_KV_FP4_E4M3 && kv_format != CSA2_KV_MXFP4)
+        return fail(INVALID, std::string(who) + ": kv_format must be CSA2_KV_FP4_E4M3 or CSA2_KV_MXFP4");
+    const bool mx = kv_format == CSA2_KV_MXFP4;
+    if (int e = check_attn(q, H, d, k_codes, k_scales, v_codes, v_scales, N, code_stride_bytes, scale_stride_bytes, K,
+                           who, mx))
+        return e;
+    if (!idx || !out) return fail(INVALID, std::string(who) + ": null pointer");
+    if (W > 0) {
+        if (!win_k || !win_v) return fail(INVALID, std::string(who) + ": window pointers are null");
+        if (!aligned(win_k, 16) || !aligned(win_v, 16)) return fail(INVALID, std::string(who) + ": window rows must be 16-byte aligned");
+        if (win_row_stride < (int64_t)W * d) return fail(INVALID, std::string(who) + ": window row stride < W*d");
+        if (win_row_stride % 8) return fail(INVALID, std::string(who) + ": window row stride must keep 16-byte alignment");
+    }
+    if (!(softmax_scale >= 0.f) || !isfinite(softmax_scale))
+        return fail(INVALID, std::string(who) + ": softmax_scale must be >= 0 and finite");
+    if (softmax_scale == 0.f) softmax_scale = 1.0f / sqrtf((float)d);
+    const size_t need = kCtrlBytes + attn_data_bytes((int64_t)B * Q, K, W);
+    if (int e = check_ws(ws, ws_bytes, need, who)) return e;
+    AttnArgs a;
+    a.q = q;
+    a.rows = (int64_t)B * Q;
+    a.rows_per_seq = Q;
+    a.H = H;
+    a.d = d;
+    a.k_codes = k_codes;
+    a.k_scales = k_scales;
+    a.v_codes = v_codes;
+    a.v_scales = v_scales;
+    a.N = N;
+    a.code_stride = code_stride_bytes;
+    a.scale_stride = scale_stride_bytes;
+    a.idx = idx;
+    a.idx_stride = K;
+    a.K = K;
+    a.scale = softmax_scale;
+    a.out = out;
+    a.mx = mx;
+    a.win_k = win_k;
+    a.win_v = win_v;
+    a.win_rs = win_row_stride;
+    a.Wn = W;
+    a.win_len = win_len;
+    return launch_attn(a, ws, static_cast<uint8_t*>(ws) + kCtrlBytes, ws_bytes - kCtrlBytes, stream);
+}
+
 // ------------------------------------------------------------------- plan
 
 struct csa2_plan {
@@ -484,6 +549,8 @@ int csa2_plan_create(const int32_t* modes, int32_t L, const csa2_plan_params* pa
         return fail(INVALID, "csa2_plan_create: softmax_scale must be >= 0 and finite");
     if (p.kv_format != CSA2_KV_FP4_E4M3 && p.kv_format != CSA2_KV_MXFP4)
         return fail(INVALID, "csa2_plan_create: kv_format must be CSA2_KV_FP4_E4M3 or CSA2_KV_MXFP4");
+    if (p.swa_window < 0 || p.swa_window > 65536)
+        return fail(INVALID, "csa2_plan_create: swa_window must be in 0..65536");
     csa2_plan* plan = new csa2_plan;
     plan->modes.assign(modes, modes + L);
     plan->p = p;
@@ -527,7 +594,7 @@ int plan_layout(const csa2_plan* plan, int32_t B, int64_t N, PlanLayout* lay) {
         off += align_up((size_t)B * plan->p.P * 4);
     }
     lay->off_attn = off;
-    off += align_up(attn_data_bytes(B, plan->p.K));
+    off += align_up(attn_data_bytes(B, plan->p.K, plan->p.swa_window));
     lay->off_idx = off;
     off += align_up((size_t)B * plan->p.K * 4);
     lay->total = off;
@@ -565,6 +632,9 @@ int csa2_plan_run_decode(const csa2_plan* plan, const csa2_cache* cache, const c
         if (!io[l].q || !io[l].out) return fail(INVALID, "csa2_plan_run_decode: layer " + std::to_string(l) + " needs q and out");
         if (plan->modes[l] != CSA2_REUSE && !io[l].q_idx)
             return fail(INVALID, "csa2_plan_run_decode: layer " + std::to_string(l) + " needs q_idx");
+        if (p.swa_window > 0 && (!io[l].win_k || !io[l].win_v || !aligned(io[l].win_k, 16) || !aligned(io[l].win_v, 16)))
+            return fail(INVALID, "csa2_plan_run_decode: layer " + std::to_string(l) +
+                                     " needs 16-byte aligned window rows win_k and win_v (the plan has swa_window > 0)");
     }
     PlanLayout lay;
     if (int e = plan_layout(plan, B, N, &lay)) return e;
@@ -640,6 +710,13 @@ int csa2_plan_run_decode(const csa2_plan* plan, const csa2_cache* cache, const c
         at.scale = p.softmax_scale;
         at.out = io[l].out;
         at.mx = p.kv_format == CSA2_KV_MXFP4;
+        if (p.swa_window > 0) {
+            at.win_k = io[l].win_k;
+            at.win_v = io[l].win_v;
+            at.win_rs = (int64_t)p.swa_window * p.d;
+            at.Wn = p.swa_window;
+            at.win_len = io[l].win_len;
+        }
         SlotTimer timer(plan, 2 * l + 1, stream);
         if (int e = launch_attn(at, wsb, wsb + lay.off_attn, lay.off_idx - lay.off_attn, stream)) return e;
     }

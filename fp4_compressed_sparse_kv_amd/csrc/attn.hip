@@ -41,6 +41,12 @@
 // a power of two as below, stays bf16; each softmax weight enters as two bf16
 // terms hi + lo (16 bits).
 //
+// A sliding-window branch (the decoder's window of recent tokens, kept as
+// bf16 K and V rows beside the FP4 cache) joins the same softmax: its rows are
+// extra blocks of 32 positions after the sparse ones, multiplied on the bf16
+// matrix cores (K rows are the operands as loaded; V rows are staged in LDS
+// and each lane reads its channel columns back transposed).
+//
 // The waves of a workgroup are merged through LDS in wave order. With NS > 1
 // each workgroup writes its (max, sum, acc) state to the workspace with
 // device-coherent stores, and the last workgroup of the row to arrive (one
@@ -71,6 +77,7 @@ constexpr int kVRowBytes = 80;                  // staged V row: 64 code bytes +
 constexpr int kMergeStride = kD + 4;
 constexpr float kLog2e = 1.4426950408889634f;
 
+// K: positions per row, counting the window's rows too (blocks of 32 each).
 static int attn_splits(int64_t rows, int32_t K, int waves) {
     const int64_t nblk = (K + kBlk - 1) / kBlk;
     int64_t ns = (kAttnTargetGroups + rows - 1) / (rows > 0 ? rows : 1);
@@ -93,8 +100,12 @@ static AttnShape attn_shape(int64_t rows, int32_t K) {
     return AttnShape{8, attn_splits(rows, K, 8)};
 }
 
-size_t attn_data_bytes(int64_t rows, int32_t K) {
-    const int ns = attn_shape(rows, K).ns;
+static int32_t attn_blocks_positions(int32_t K, int32_t W) {
+    return ((K + kBlk - 1) / kBlk + (W + kBlk - 1) / kBlk) * kBlk;
+}
+
+size_t attn_data_bytes(int64_t rows, int32_t K, int32_t W) {
+    const int ns = attn_shape(rows, attn_blocks_positions(K, W)).ns;
     return ns > 1 ? (size_t)rows * ns * kPartFloats * 4 : 0;
 }
 
@@ -176,6 +187,12 @@ struct Stage {                                  // one wave's LDS staging area
     uint8_t vs[kBlk][8];
 };
 
+constexpr int kWinRow = kD + 8;                 // staged window V row (bf16): 128 channels + pad
+union WaveStage {                               // a wave's area: FP4 blocks, or a window block's V rows
+    Stage sp;
+    uint16_t wv[kBlk][kWinRow];
+};
+
 template <int W>
 struct MergeArea {
     float acc[W][kMaxHeads][kMergeStride];
@@ -186,7 +203,7 @@ struct MergeArea {
 
 template <int W>
 union AttnLds {
-    Stage st[W];
+    WaveStage st[W];
     MergeArea<W> mg;
 };
 
@@ -382,13 +399,111 @@ __device__ __forceinline__ void attend_block(WaveState& st, const BlockRaw& r, S
     }
 }
 
+// One block of 32 window rows (rows 32 wb .. of this query row's window; rows
+// at or past `len` are masked). Lane (n, g) loads channels 32g..32g+31 of K
+// rows n and 16 + n (its S^T operands as they are) and of the same V rows,
+// which it stages in LDS; the softmax is attend_block's; each lane then reads
+// channels 8n..8n+7 of its 8 position columns and transposes them into the
+// PV operands. qw: the query (scaled by 2^-qe like the sparse part) in bf16.
+__device__ __forceinline__ void attend_window_block(WaveState& st, const uint16_t* wk, const uint16_t* wv, int wb,
+                                                    int len, WaveStage& sg, const bf16x8 (&qw)[4], float sl2,
+                                                    int n, int g) {
+    const int lim = max(len - 1, 0);
+    const int r0 = min(32 * wb + n, lim), r1 = min(32 * wb + 16 + n, lim);
+    uint4 kq[2][4], vq[2][4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        kq[0][s] = *reinterpret_cast<const uint4*>(wk + (int64_t)r0 * kD + 32 * g + 8 * s);
+        kq[1][s] = *reinterpret_cast<const uint4*>(wk + (int64_t)r1 * kD + 32 * g + 8 * s);
+        vq[0][s] = *reinterpret_cast<const uint4*>(wv + (int64_t)r0 * kD + 32 * g + 8 * s);
+        vq[1][s] = *reinterpret_cast<const uint4*>(wv + (int64_t)r1 * kD + 32 * g + 8 * s);
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        *reinterpret_cast<uint4*>(&sg.wv[n][32 * g + 8 * s]) = vq[0][s];
+        *reinterpret_cast<uint4*>(&sg.wv[16 + n][32 * g + 8 * s]) = vq[1][s];
+    }
+    __builtin_amdgcn_wave_barrier();
+    const int nvalid = min(max(len - 32 * wb, 0), kBlk);
+    const uint32_t vmask = nvalid >= kBlk ? 0xFFFFFFFFu : ((1u << nvalid) - 1u);
+
+    f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) sacc[mb] = mfma16(__builtin_bit_cast(bf16x8, kq[mb][s]), qw[s], sacc[mb]);
+
+    const uint32_t mlo = vmask >> (4 * g), mhi = vmask >> (16 + 4 * g);
+    float lg[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float sv = (i < 4) ? sacc[0][i] : sacc[1][i - 4];
+        const uint32_t bit = (i < 4) ? (mlo >> i) & 1u : (mhi >> (i - 4)) & 1u;
+        lg[i] = bit ? sv * sl2 : -INFINITY;
+    }
+    float mx = fmaxf(fmaxf(fmaxf(lg[0], lg[1]), fmaxf(lg[2], lg[3])), fmaxf(fmaxf(lg[4], lg[5]), fmaxf(lg[6], lg[7])));
+    mx = rows_max(mx);
+    const float m_old = st.m;
+    const float m_new = fmaxf(m_old, mx);
+    const float mref = m_new == -INFINITY ? 0.f : m_new;
+    float p[8], psum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        p[i] = __builtin_amdgcn_exp2f((lg[i] - mref) * st.f);
+        psum += p[i];
+    }
+    uint32_t ph[4], pl[4];                      // p = hi + lo as bf16 pairs (16 bits)
+#pragma unroll
+    for (int i = 0; i < 8; i += 2) {
+        const float h0 = __uint_as_float(__float_as_uint(p[i]) & 0xFFFF0000u);
+        const float h1 = __uint_as_float(__float_as_uint(p[i + 1]) & 0xFFFF0000u);
+        ph[i / 2] = pack_hi(h0, h1);
+        pl[i / 2] = pack_hi(p[i] - h0, p[i + 1] - h1);
+    }
+    const bf16x8 pb_hi = __builtin_bit_cast(bf16x8, make_uint4(ph[0], ph[1], ph[2], ph[3]));
+    const bf16x8 pb_lo = __builtin_bit_cast(bf16x8, make_uint4(pl[0], pl[1], pl[2], pl[3]));
+    psum = rows_sum(psum);
+    const float alpha = m_old == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m_old - mref) * st.f);
+    st.l = st.l * alpha + psum;
+    st.m = m_new;
+    if (__builtin_amdgcn_ballot_w64(m_old != -INFINITY && alpha != 1.f) != 0) {
+#pragma unroll
+        for (int t = 0; t < 8; ++t) st.acc[t] = st.acc[t] * alpha;
+    }
+
+    // V: channels 8n..8n+7 (16 bytes) of each of this lane's 8 position columns
+    uint4 vr[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int pp = (i < 4) ? (4 * g + i) : (16 + 4 * g + i - 4);
+        vr[i] = *reinterpret_cast<const uint4*>(&sg.wv[pp][8 * n]);
+    }
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        uint32_t va[4];                         // (V[2k][8n+t], V[2k+1][8n+t]) bf16 pairs
+        const uint32_t sel = (t & 1) ? 0x07060302u : 0x05040100u;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const uint4 a = vr[2 * k], b = vr[2 * k + 1];
+            const uint32_t wa = (t >> 1) == 0 ? a.x : (t >> 1) == 1 ? a.y : (t >> 1) == 2 ? a.z : a.w;
+            const uint32_t wb2 = (t >> 1) == 0 ? b.x : (t >> 1) == 1 ? b.y : (t >> 1) == 2 ? b.z : b.w;
+            va[k] = __builtin_amdgcn_perm(wb2, wa, sel);
+        }
+        const bf16x8 a8 = __builtin_bit_cast(bf16x8, make_uint4(va[0], va[1], va[2], va[3]));
+        st.acc[t] = mfma16(a8, pb_hi, st.acc[t]);
+        st.acc[t] = mfma16(a8, pb_lo, st.acc[t]);
+    }
+}
+
 template <int W, bool MX>
 __global__ void __launch_bounds__(W * kWave, W == 4 ? 2 : 1)
 k_sparse_attn(const uint16_t* __restrict__ q, int32_t rows_per_seq, int32_t H, const uint8_t* __restrict__ k_codes,
               const uint8_t* __restrict__ k_scales, const uint8_t* __restrict__ v_codes,
               const uint8_t* __restrict__ v_scales, int64_t N, int64_t cs, int64_t ss, const int32_t* __restrict__ idx,
               int64_t idx_stride, int32_t K, float scale, float* __restrict__ out, int32_t NS,
-              uint32_t* __restrict__ counters, float* __restrict__ parts, int64_t rows) {
+              uint32_t* __restrict__ counters, float* __restrict__ parts, int64_t rows,
+              const uint16_t* __restrict__ win_k, const uint16_t* __restrict__ win_v, int64_t win_rs, int32_t Wn,
+              const int32_t* __restrict__ win_len) {
     constexpr int kAttnWaves = W;
     constexpr int kAttnThreads = W * kWave;
     constexpr int kCh = kMaxHeads * kD / kAttnThreads;  // output channels per thread in the merges
@@ -402,7 +517,8 @@ k_sparse_attn(const uint16_t* __restrict__ q, int32_t rows_per_seq, int32_t H, c
     const int64_t row = (int64_t)blockIdx.x % rows;            // row fastest: a row's slices share an XCD
     const int split = (int)((int64_t)blockIdx.x / rows);
     const int64_t seq = row / rows_per_seq;
-    const int nblk = (K + kBlk - 1) / kBlk;
+    const int nblk_s = (K + kBlk - 1) / kBlk;                   // blocks of the sparse positions
+    const int nblk = nblk_s + (Wn + kBlk - 1) / kBlk;           // then the window's blocks
     const int bps = (nblk + NS - 1) / NS;                       // blocks per slice
     const int b0 = split * bps, b1 = min(nblk, b0 + bps);
     const float sl2 = scale * kLog2e;
@@ -418,6 +534,7 @@ k_sparse_attn(const uint16_t* __restrict__ q, int32_t rows_per_seq, int32_t H, c
             qraw[s] = *reinterpret_cast<const uint4*>(q + (row * H + min(n, H - 1)) * (int64_t)kD + 32 * g + 8 * s);
     };
     typename OpOf<MX>::type qb[4];
+    bf16x8 qw[4];                               // the same scaled query in bf16 (window blocks)
     int qe = 0;                                 // head n's query is used as q * 2^-qe
     auto convert_q = [&]() {
         uint32_t mb = 0;                        // largest |q| of this lane's 32 elements (bf16 bits)
@@ -438,14 +555,14 @@ k_sparse_attn(const uint16_t* __restrict__ q, int32_t rows_per_seq, int32_t H, c
             for (int i = 0; i < 4; ++i) {
                 const float a = n < H ? ldexpf(bf16_bits_to_f32(w[i] & 0xFFFFu), -qe) : 0.f;
                 const float b = n < H ? ldexpf(bf16_bits_to_f32(w[i] >> 16), -qe) : 0.f;
-                if constexpr (MX) {             // a bf16 times a power of two: its top half (exact unless subnormal)
-                    w[i] = pack_hi(a, b);
-                } else {
+                w[i] = pack_hi(a, b);           // a bf16 times a power of two: its top half (exact unless subnormal)
+                if constexpr (!MX) {
                     qb[s][2 * i + 0] = (_Float16)a;
                     qb[s][2 * i + 1] = (_Float16)b;
                 }
             }
-            if constexpr (MX) qb[s] = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
+            qw[s] = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
+            if constexpr (MX) qb[s] = qw[s];
         }
     };
 
@@ -468,7 +585,9 @@ k_sparse_attn(const uint16_t* __restrict__ q, int32_t rows_per_seq, int32_t H, c
     // unconditional, so nothing in flight is copied and the compiler's wait
     // counts stay exact; the last one to three blocks are peeled.
     const int first = b0 + wave;
-    const int nb = first < b1 ? (b1 - first + kAttnWaves - 1) / kAttnWaves : 0;
+    const int nb_all = first < b1 ? (b1 - first + kAttnWaves - 1) / kAttnWaves : 0;
+    const int b1s = min(b1, nblk_s);
+    const int nb = first < b1s ? (b1s - first + kAttnWaves - 1) / kAttnWaves : 0;   // sparse blocks first
     if (nb > 0) {
         BlockRaw r0, r1;
         BlockPos p0 = load_pos(ip, first, K, lane);
@@ -482,31 +601,38 @@ k_sparse_attn(const uint16_t* __restrict__ q, int32_t rows_per_seq, int32_t H, c
             const int bk = first + k * kAttnWaves;
             p0 = load_pos(ip, bk + 2 * kAttnWaves, K, lane);
             gather<MX>(r1, p1, bk + kAttnWaves, K, kv, N, lane, n, g);
-            attend_block<MX>(st, r0, lds.st[wave], qb, sl2, lane, n, g);
+            attend_block<MX>(st, r0, lds.st[wave].sp, qb, sl2, lane, n, g);
             p1 = load_pos(ip, bk + 3 * kAttnWaves, K, lane);
             gather<MX>(r0, p0, bk + 2 * kAttnWaves, K, kv, N, lane, n, g);
-            attend_block<MX>(st, r1, lds.st[wave], qb, sl2, lane, n, g);
+            attend_block<MX>(st, r1, lds.st[wave].sp, qb, sl2, lane, n, g);
         }
         const int bk = first + k * kAttnWaves;
         const int rem = nb - k;                 // 1, 2 or 3
         if (rem == 1) {
-            attend_block<MX>(st, r0, lds.st[wave], qb, sl2, lane, n, g);
+            attend_block<MX>(st, r0, lds.st[wave].sp, qb, sl2, lane, n, g);
         } else if (rem == 2) {
             gather<MX>(r1, p1, bk + kAttnWaves, K, kv, N, lane, n, g);
-            attend_block<MX>(st, r0, lds.st[wave], qb, sl2, lane, n, g);
-            attend_block<MX>(st, r1, lds.st[wave], qb, sl2, lane, n, g);
+            attend_block<MX>(st, r0, lds.st[wave].sp, qb, sl2, lane, n, g);
+            attend_block<MX>(st, r1, lds.st[wave].sp, qb, sl2, lane, n, g);
         } else {
             p0 = load_pos(ip, bk + 2 * kAttnWaves, K, lane);
             gather<MX>(r1, p1, bk + kAttnWaves, K, kv, N, lane, n, g);
-            attend_block<MX>(st, r0, lds.st[wave], qb, sl2, lane, n, g);
+            attend_block<MX>(st, r0, lds.st[wave].sp, qb, sl2, lane, n, g);
             gather<MX>(r0, p0, bk + 2 * kAttnWaves, K, kv, N, lane, n, g);
-            attend_block<MX>(st, r1, lds.st[wave], qb, sl2, lane, n, g);
-            attend_block<MX>(st, r0, lds.st[wave], qb, sl2, lane, n, g);
+            attend_block<MX>(st, r1, lds.st[wave].sp, qb, sl2, lane, n, g);
+            attend_block<MX>(st, r0, lds.st[wave].sp, qb, sl2, lane, n, g);
         }
-    } else {                                    // no block: only the scale-back factor is needed
+    } else {                                    // no sparse block: the query is needed as it stands
         load_q();
         convert_q();
         st.f = ldexpf(1.f, qe);
+    }
+    if (nb_all > nb) {                          // then this wave's window blocks
+        const uint16_t* wkr = win_k + row * win_rs;
+        const uint16_t* wvr = win_v + row * win_rs;
+        const int len = win_len ? min(max(win_len[row], 0), Wn) : Wn;
+        for (int k = nb; k < nb_all; ++k)
+            attend_window_block(st, wkr, wvr, first + k * kAttnWaves - nblk_s, len, lds.st[wave], qw, sl2, n, g);
     }
 
     // ---- merge the waves in wave order (the staging areas are reused)
@@ -614,9 +740,9 @@ k_sparse_attn(const uint16_t* __restrict__ q, int32_t rows_per_seq, int32_t H, c
 
 int launch_attn_scratch(const AttnArgs& a, uint32_t* counters, void* parts, size_t parts_bytes, hipStream_t stream) {
     if (a.rows == 0) return OK;
-    const AttnShape sh = attn_shape(a.rows, a.K);
+    const AttnShape sh = attn_shape(a.rows, attn_blocks_positions(a.K, a.Wn));
     const int ns = sh.ns;
-    if (parts_bytes < attn_data_bytes(a.rows, a.K)) return fail(WORKSPACE, "attention workspace too small");
+    if (parts_bytes < attn_data_bytes(a.rows, a.K, a.Wn)) return fail(WORKSPACE, "attention workspace too small");
     if (ns > 1 && a.rows > kAttnCtrlWords) return fail(INVALID, "attention: split rows exceed the counter table");
     const int64_t groups = a.rows * ns;
     if (groups > 0x7FFFFFFFll) return fail(INVALID, "attention: too many query rows");
@@ -624,7 +750,8 @@ int launch_attn_scratch(const AttnArgs& a, uint32_t* counters, void* parts, size
                    : (sh.waves == 4 ? k_sparse_attn<4, false> : k_sparse_attn<8, false>);
     hipLaunchKernelGGL(fn, dim3((unsigned)groups), dim3(sh.waves * kWave), 0, stream, a.q, a.rows_per_seq,
                        a.H, a.k_codes, a.k_scales, a.v_codes, a.v_scales, a.N, a.code_stride, a.scale_stride, a.idx,
-                       a.idx_stride, a.K, a.scale, a.out, ns, counters, reinterpret_cast<float*>(parts), a.rows);
+                       a.idx_stride, a.K, a.scale, a.out, ns, counters, reinterpret_cast<float*>(parts), a.rows,
+                       a.win_k, a.win_v, a.win_rs, a.Wn, a.win_len);
     const hipError_t e = hipGetLastError();
     return e == hipSuccess ? OK : hip_fail(e, "launch k_sparse_attn");
 }

@@ -175,8 +175,13 @@ struct AttnArgs {
     float scale = 0.f;
     float* out = nullptr;           // [rows][H][d]
     bool mx = false;                // cache format: E4M3 scale per 16 channels, or MXFP4 (E8M0 per 32)
+    const uint16_t* win_k = nullptr;// sliding window: row r's Wn bf16 K rows at win_k + r*win_rs (d each)
+    const uint16_t* win_v = nullptr;
+    int64_t win_rs = 0;
+    int32_t Wn = 0;                 // window rows per query row (0: no window)
+    const int32_t* win_len = nullptr;   // [rows] valid window rows, or null (all Wn)
 };
-size_t attn_data_bytes(int64_t rows, int32_t K);     // data region of one attention call
+size_t attn_data_bytes(int64_t rows, int32_t K, int32_t W = 0);  // data region of one attention call
 int launch_attn(const AttnArgs& a, void* ws_ctrl, void* ws_data, size_t data_bytes, hipStream_t stream);
 // The same with the merge counters (kAttnCtrlWords words, zero between calls) and the partial
 // states given directly.

@@ -296,6 +296,37 @@ int csa2_sparse_attn_mxfp4(const uint16_t* q, int32_t B, int32_t Q, int32_t H, i
                            float* out, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * csa2_sparse_attn_swa - the sparse attention of a decoder layer together
+ * with its sliding-window branch, in one softmax ([zaikei] "■CEDで入力処理の
+ * 計算量を削減": each decoder layer attends to a window of recent tokens;
+ * [jiwasawa] "FP4 メイン KV Cache と SWA Bounded Replay": the window's KV
+ * is kept apart from the FP4 main cache).
+ *
+ * R: the window KV is bf16; query row r (of B*Q) has W window rows of d = 128
+ * channels, K at win_k + r*win_row_stride + j*128 and V likewise at win_v,
+ * j < W, of which the first win_len[r] (all W when win_len is NULL) are valid.
+ * They are keys of the same softmax as the selected main-cache positions (a
+ * window row is never merged with a main-cache position). Everything else -
+ * main cache in kv_format (CSA2_KV_FP4_E4M3 or CSA2_KV_MXFP4), idx, scale,
+ * out, numerics - as csa2_sparse_attn_fp4 / csa2_sparse_attn_mxfp4; window
+ * rows are bf16 matrix-core operands (exact), the query scaled per head by a
+ * power of two as for the sparse part.
+ *   win_k, win_v     device bf16, 16-byte aligned; win_row_stride >= W*128, a multiple of 8
+ *   win_len          device [B*Q] int32 or NULL
+ *   ws               workspace of csa2_sparse_attn_swa_workspace_bytes(B, Q, H, d, K, W) bytes
+ */
+int csa2_sparse_attn_swa_workspace_bytes(int32_t B, int32_t Q, int32_t H, int32_t d, int32_t K, int32_t W,
+                                         size_t* bytes);
+int csa2_sparse_attn_swa(const uint16_t* q, int32_t B, int32_t Q, int32_t H, int32_t d, int32_t kv_format,
+                         const uint8_t* k_codes, const uint8_t* k_scales,
+                         const uint8_t* v_codes, const uint8_t* v_scales,
+                         int64_t N, int64_t code_stride_bytes, int64_t scale_stride_bytes,
+                         const int32_t* idx, int32_t K,
+                         const uint16_t* win_k, const uint16_t* win_v, int64_t win_row_stride, int32_t W,
+                         const int32_t* win_len, float softmax_scale,
+                         float* out, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
  * csa2_sparse_attn_fp4_noalloc - csa2_sparse_attn_fp4 for callers that cannot
  * allocate device memory or pass a workspace: code under HIP graph capture,
  * tight serving loops, harnesses that forbid allocation. Same arguments,
@@ -346,6 +377,8 @@ typedef struct {
     int32_t k_idx_dtype;    /* CSA2_F32, CSA2_BF16 or CSA2_E4M3 */
     float softmax_scale;    /* 0 selects 1/sqrt(d) */
     int32_t kv_format;      /* CSA2_KV_FP4_E4M3 or CSA2_KV_MXFP4: the main KV cache's format */
+    int32_t swa_window;     /* W > 0: every layer also attends to its W-row sliding window (see
+                               csa2_sparse_attn_swa) in the same softmax; 0: no window */
 } csa2_plan_params;
 
 typedef struct {
@@ -365,6 +398,9 @@ typedef struct {
     int32_t* idx_out;       /* device [B][K] positions selected by this layer (Full, Reindex)
                                or NULL to keep them in the workspace; ignored for Reuse */
     int32_t* pool_out;      /* device [B][P] pool of the first Full layer, or NULL */
+    const uint16_t* win_k;  /* swa_window > 0: device [B][W][d] bf16 window K rows of this layer */
+    const uint16_t* win_v;  /*                 device [B][W][d] bf16 window V rows */
+    const int32_t* win_len; /*                 device [B] valid window rows, or NULL (all W) */
 } csa2_layer_io;
 
 int csa2_plan_create(const int32_t* modes, int32_t L, const csa2_plan_params* params, csa2_plan** out);

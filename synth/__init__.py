@@ -47,7 +47,7 @@ WORKLOADS = {
 }
 
 # tensor ids for the substreams
-_T_K, _T_V, _T_KOUT, _T_VOUT, _T_Q, _T_QIDX, _T_KIDX, _T_ROWS, _T_PQ, _T_PQIDX, _T_HID, _T_WKV = range(12)
+_T_K, _T_V, _T_KOUT, _T_VOUT, _T_Q, _T_QIDX, _T_KIDX, _T_ROWS, _T_PQ, _T_PQIDX, _T_HID, _T_WKV, _T_WIN = range(13)
 
 
 def rng(seed, wid, tensor, index=0):
@@ -142,6 +142,14 @@ def quant_rows(cfg, block):
     scale = np.power(np.float32(10.0), g.uniform(-3.0, 3.0, size=(rb, 1)).astype(np.float32))
     x = g.standard_normal((rb, C), dtype=np.float32) * scale.astype(np.float32)
     return to_bf16_bits(x)
+
+
+def window_kv(cfg, layer, W):
+    """A layer's sliding-window K and V rows for all B sequences: ([B][W][d], [B][W][d]) bf16 bits, N(0,1)."""
+    g = rng(cfg["seed"], cfg["wid"], _T_WIN, layer)
+    k = g.standard_normal((cfg["B"], W, cfg["d"]), dtype=np.float32)
+    v = g.standard_normal((cfg["B"], W, cfg["d"]), dtype=np.float32)
+    return to_bf16_bits(k), to_bf16_bits(v)
 
 
 def proj_hidden(cfg, block):
