@@ -16,7 +16,11 @@ Readings:
   * a Reindex layer scores the pool positions with its own indexer query and
     the first Full layer's indexer keys, and selects top-K from the pool;
   * a Reuse layer takes the positions of the immediately preceding layer;
-  * all layers read the one shared main KV cache (one KV head);
+  * every Full layer computes KV afresh, so it opens a group: its main KV
+    cache and indexer keys, and the pool it picks (when a Reindex layer
+    follows in the group), serve the Reindex and Reuse layers after it up to
+    the next Full layer; with one Full layer this is the single shared cache
+    and "the first Full layer's pool";
   * plan validity: the first layer is Full; a Reindex needs an earlier Full
     (and a pool, so P >= K); a Reuse needs a predecessor.
 """
@@ -43,11 +47,30 @@ def validate_plan(modes, K, P=None):
     return modes
 
 
+def groups(modes):
+    """Group index of each layer: the number of Full layers up to and including it, minus one."""
+    out, gi = [], -1
+    for m in modes:
+        gi += m == FULL
+        out.append(gi)
+    return out
+
+
+def _group_needs_pool(modes):
+    """Per group: whether a Reindex layer follows its Full layer."""
+    g = groups(modes)
+    need = [False] * (g[-1] + 1)
+    for m, gi in zip(modes, g):
+        need[gi] |= m == REINDEX
+    return need
+
+
 def run_decode(modes, cache, layers, K, P=None, softmax_scale=None):
     """One decode step of the stack for ONE sequence.
 
     cache: dict with 'k_codes', 'k_scales', 'v_codes', 'v_scales' (main KV,
-    [N][d/2] and [N][d/16]), 'k_idx' ([N][d_idx] stored), 'k_idx_dtype'.
+    [N][d/2] and [N][d/16]), 'k_idx' ([N][d_idx] stored), 'k_idx_dtype' - or a
+    list of such dicts, one per Full layer (group).
     layers: list (one per layer) of dicts with 'q' ((H, d) bf16 bits) and, for
     Full and Reindex layers, 'q_idx' ((d_idx,) stored) and 'q_idx_dtype'; a
     layer with a sliding-window branch also has 'win_k', 'win_v' ((w, d) bf16
@@ -56,15 +79,18 @@ def run_decode(modes, cache, layers, K, P=None, softmax_scale=None):
     the first Full layer when the plan has a Reindex, 'pool' (P,).
     """
     modes = validate_plan(modes, K, P)
-    need_pool = REINDEX in modes
+    caches = cache if isinstance(cache, (list, tuple)) else [cache]
+    grp, need_pool = groups(modes), _group_needs_pool(modes)
     pool = None
     prev_idx = None
     results = []
-    for mode, layer in zip(modes, layers):
+    for mode, layer, gi in zip(modes, layers, grp):
         res = {}
+        cache = caches[gi]
         if mode == FULL:
             s = index_scores(layer["q_idx"], layer["q_idx_dtype"], cache["k_idx"], cache["k_idx_dtype"])
-            if need_pool and pool is None:
+            pool = None
+            if need_pool[gi]:
                 pool, _ = topk(s, P)
                 res["pool"] = pool
             idx, _ = topk(s, K)
@@ -81,6 +107,41 @@ def run_decode(modes, cache, layers, K, P=None, softmax_scale=None):
         results.append(res)
         prev_idx = idx
     return results
+
+
+def run_prefill(modes, cache, layers, q_pos, K, P=None, softmax_scale=None, queries=None):
+    """A prefill chunk of Q queries of ONE sequence through every layer of the plan.
+
+    Each query is a decode step at its own position: the causal rule of
+    prefill_full (positions <= q_pos[i]) in its Full layers, and its own pool,
+    Reindex selection and Reuse inheritance. cache: as run_decode. layers: one
+    dict per layer with 'q' ((Q, H, d) bf16 bits) and, for Full and Reindex
+    layers, 'q_idx' ((Q, d_idx) stored) and 'q_idx_dtype'. Returns per layer
+    (idx (Q', K), out (Q', H, d)) for the queries taken (all, or `queries`).
+    """
+    modes = validate_plan(modes, K, P)
+    caches = cache if isinstance(cache, (list, tuple)) else [cache]
+    grp, need_pool = groups(modes), _group_needs_pool(modes)
+    rows = range(len(q_pos)) if queries is None else list(queries)
+    res = [([], []) for _ in modes]
+    for i in rows:
+        pool, prev_idx = None, None
+        for li, (mode, layer, gi) in enumerate(zip(modes, layers, grp)):
+            cache = caches[gi]
+            if mode == FULL:
+                s = index_scores(layer["q_idx"][i], layer["q_idx_dtype"], cache["k_idx"], cache["k_idx_dtype"],
+                                 q_pos=int(q_pos[i]))
+                pool = topk(s, P)[0] if need_pool[gi] else None
+                idx, _ = topk(s, K)
+            elif mode == REINDEX:
+                s = pool_scores(layer["q_idx"][i], layer["q_idx_dtype"], cache["k_idx"], cache["k_idx_dtype"], pool)
+                idx, _ = topk(s, K, positions=pool)
+            else:
+                idx = prev_idx.copy()
+            res[li][0].append(idx)
+            res[li][1].append(sparse_attn(layer["q"][i], cache, idx, softmax_scale))
+            prev_idx = idx
+    return [(np.stack(a), np.stack(b)) for a, b in res]
 
 
 def prefill_full(q_idx, q_idx_dtype, q_pos, q, cache, K, softmax_scale=None, queries=None):

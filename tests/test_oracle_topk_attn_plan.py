@@ -218,3 +218,48 @@ def test_swa_attention_pins():
     two = A.sparse_attn_swa(qb, kv, np.array([3]), k3, v3)
     np.testing.assert_allclose(two, A.sparse_attn(qb, kv, np.array([3])), rtol=1e-12)
     assert np.all(A.sparse_attn_swa(qb, kv, np.array([-1]), empty, empty) == 0)
+
+
+def _group_cache(cfg, b, seed_shift):
+    c2 = dict(cfg, seed=cfg["seed"] + seed_shift)
+    kb, vb = synth.kv_bf16(c2, b)
+    kc, ks = Q.quant_fp4(kb)
+    vc, vs = Q.quant_fp4(vb)
+    return dict(k_codes=kc, k_scales=ks, v_codes=vc, v_scales=vs, k_idx=synth.k_idx(c2, b), k_idx_dtype=cfg["k_idx_dtype"])
+
+
+def test_plan_with_several_full_layers_runs_groups_on_their_own_caches():
+    """[Full, Reindex, Reuse, Full, Reindex, Reuse] over two caches (one per Full layer): each half equals
+    the three-layer plan on its own cache, so a later Full layer's pool and KV replace the first's."""
+    modes = ["full", "reindex", "reuse", "full", "reindex", "reuse"]
+    cfg, _, layers = _stack_case(modes, N=700, K=16, P=64)
+    caches = [_group_cache(cfg, 0, 0), _group_cache(cfg, 0, 1)]
+    res = PL.run_decode(modes, caches, layers, cfg["K"], cfg["P"])
+    a = PL.run_decode(modes[:3], caches[0], layers[:3], cfg["K"], cfg["P"])
+    b = PL.run_decode(modes[3:], caches[1], layers[3:], cfg["K"], cfg["P"])
+    for got, ref in zip(res, a + b):
+        assert np.array_equal(got["idx"], ref["idx"]) and np.array_equal(got["out"], ref["out"])
+    assert not np.array_equal(res[3]["pool"], res[0]["pool"])
+    assert PL.groups(modes) == [0, 0, 0, 1, 1, 1]
+
+
+def test_prefill_plan_query_equals_decode_on_its_causal_prefix():
+    """Every query of a prefill chunk through [Full, Reindex, Reuse, Reuse] equals a decode step of the
+    same plan whose context is the query's causal prefix (positions 0..q_pos), layer by layer - including
+    queries whose prefix is shorter than the pool (padded pools) or than K."""
+    modes = ["full", "reindex", "reuse", "reuse"]
+    cfg, cache, _ = _stack_case(modes, N=400, K=12, P=40)
+    Qn = 6
+    q_pos = np.array([3, 11, 39, 40, 200, 399])
+    layers = [dict(q=np.stack([synth.q_bf16(cfg, li * 10 + i, 0)[0] for i in range(Qn)]),
+                   q_idx=np.stack([synth.q_idx(cfg, li * 10 + i, 0)[0] for i in range(Qn)]),
+                   q_idx_dtype=cfg["q_idx_dtype"]) for li in range(len(modes))]
+    res = PL.run_prefill(modes, cache, layers, q_pos, cfg["K"], cfg["P"])
+    for i, qp in enumerate(q_pos):
+        pre = {k: (v[: qp + 1] if k != "k_idx_dtype" else v) for k, v in cache.items()}
+        dec = PL.run_decode(modes, pre, [dict(q=L["q"][i], q_idx=L["q_idx"][i], q_idx_dtype=L["q_idx_dtype"])
+                                         for L in layers], cfg["K"], cfg["P"])
+        for li in range(len(modes)):
+            assert np.array_equal(res[li][0][i], dec[li]["idx"]), (i, li)
+            assert np.array_equal(res[li][1][i], dec[li]["out"]), (i, li)
+        assert np.all(res[1][0][i][res[1][0][i] >= 0] <= qp)
