@@ -465,6 +465,85 @@ def run_prefill(args, cfg, dev):
     print(json.dumps(res), flush=True)
 
 
+def run_prefill_plan(args, cfg, dev):
+    """The workload's prefill chunk through every layer of its plan (csa2_plan_run_prefill): per query a
+    causal Full layer with its own pool, Reindex over that pool, Reuse, and attention in every layer."""
+    import numpy as np
+    import torch
+
+    import fp4_compressed_sparse_kv_amd as C
+    import synth
+
+    B, N, Q, K, P = cfg["B"], cfg["N"], cfg["prefill_Q"], cfg["K"], cfg["P"]
+    modes = list(cfg["modes"])
+    t0 = time.perf_counter()
+    cache, _ = build_inputs(cfg, dev)
+    layers = []
+    for li in range(len(modes)):
+        qi = np.stack([synth.q_idx(cfg, 100 + li, b, Q=Q) for b in range(B)])
+        qb = np.stack([synth.q_bf16(cfg, 100 + li, b, Q=Q) for b in range(B)])
+        layers.append(dict(q=_to_dev_bf16(qb, dev), q_idx=_to_dev_key(qi, cfg["q_idx_dtype"], dev),
+                           out=torch.empty(B, Q, cfg["H"], cfg["d"], dtype=torch.float32, device=dev)))
+    q_pos = torch.arange(N - Q, N, dtype=torch.int64, device=dev).repeat(B, 1).contiguous()
+    log(f"inputs ready in {time.perf_counter() - t0:.1f} s")
+    plan = C.Plan(modes, K=K, P=P, H=cfg["H"], d=cfg["d"], d_idx=cfg["d_idx"], q_idx_dtype=cfg["q_idx_dtype"],
+                  k_idx_dtype=cfg["k_idx_dtype"])
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        plan.run_prefill(cache, layers, q_pos, check=False)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        plan.run_prefill(cache, layers, q_pos, check=False)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    ws = C.workspace(0, dev, ("plan_prefill", id(plan)))
+    status = C.status_word(ws)
+    res = {
+        "metric": "prefill queries/s through the CSA2 layer stack (per-query pools, Reindex, Reuse, attention)",
+        "value": round(B * Q / (ms * 1e-3), 1) if status == 0 else None, "unit": "queries/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16 MFMA (candidates) / f64 (exact scores) / f32",
+        "data": "synthetic",
+        "config": {"workload": args.workload + ":prefill_plan", "B": B, "N": N, "Q": Q, "K": K, "P": P,
+                   "modes": modes},
+        "status_word": status,
+    }
+    causal = float((q_pos + 1).sum().item())
+    flop = 2.0 * cfg["d_idx"] * causal * modes.count("full")      # the Full layers' indexer dot products
+    res["indexer_tflop"] = round(flop / 1e12, 3)
+    # conservative: the Full layers' indexer FLOP over the whole prefill time (all layers), dense bf16 peak
+    res["roofline"] = {"bound": "mfma", "kernel": "k_pf_tiles (indexer candidates), whole-plan prefill time",
+                       "achieved": round(flop / (ms * 1e-3) / 1e12, 1), "peak": 2500.0, "unit": "TFLOP/s",
+                       "frac": round(flop / (ms * 1e-3) / 2.5e15, 4), "traffic": None}
+    if not args.no_cpu:
+        from threadpoolctl import threadpool_limits
+
+        from oracle import plan as OP
+        scale = float(np.float32(1 / math.sqrt(cfg["d"])))
+        kb, vb = synth.kv_bf16(cfg, 0)                               # untimed: input generation
+        oc = dict(k_bf16=kb, v_bf16=vb, k_idx=synth.k_idx(cfg, 0), k_idx_dtype=cfg["k_idx_dtype"])
+        ol = [dict(q=synth.q_bf16(cfg, 100 + li, 0, Q=Q), q_idx=synth.q_idx(cfg, 100 + li, 0, Q=Q),
+                   q_idx_dtype=cfg["q_idx_dtype"]) for li in range(len(modes))]
+        qp = np.arange(N - Q, N)
+        cores = host_cores()
+        done, spent = 0, 0.0
+        with threadpool_limits(limits=cores):
+            for i in range(0, Q, 97):
+                t1 = time.perf_counter()
+                OP.run_prefill(modes, oc, ol, qp, K, P, softmax_scale=scale, queries=[i])
+                spent += time.perf_counter() - t1
+                done += 1
+                if spent >= args.cpu_seconds:
+                    break
+        res["cpu_baseline"] = {"value": done / spent, "unit": "queries/s", "cores": cores, "kind": "oracle",
+                               "sample": f"{done} of {Q} queries of sequence 0 (every 97th position) through all "
+                                         f"{len(modes)} layers, N={N}, {spent:.1f} s with BLAS on {cores} host threads"}
+    print(json.dumps(res), flush=True)
+
+
 def prefill_cpu_baseline(cfg, budget_s):
     """The oracle on sampled prefill queries of sequence 0 (exact causal scores over the whole context,
     top-K, fp64 attention) until ~budget_s of CPU work."""
@@ -517,6 +596,8 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--prefill", action="store_true",
                     help="time the workload's Full-layer prefill chunk instead of the decode step")
+    ap.add_argument("--prefill-plan", action="store_true",
+                    help="time the workload's prefill chunk through every layer of its plan")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -533,10 +614,12 @@ def main():
     import synth
 
     cfg = dict(synth.WORKLOADS[args.workload])
-    if args.prefill:
+    if args.prefill or args.prefill_plan:
         if "prefill_Q" not in cfg:
             raise SystemExit(f"{args.workload} has no prefill chunk")
         torch.cuda.set_device(0)
+        if args.prefill_plan:
+            return run_prefill_plan(args, cfg, torch.device("cuda", 0))
         return run_prefill(args, cfg, torch.device("cuda", 0))
     if "D" in cfg:
         torch.cuda.set_device(0)

@@ -51,6 +51,10 @@ class CacheDesc(ctypes.Structure):
                 ("code_stride_bytes", _c_i64), ("scale_stride_bytes", _c_i64), ("k_idx", _vp)]
 
 
+class PrefillIO(ctypes.Structure):
+    _fields_ = [("q", _vp), ("q_idx", _vp), ("out", _vp), ("idx_out", _vp)]
+
+
 class LayerIO(ctypes.Structure):
     _fields_ = [("q", _vp), ("q_idx", _vp), ("out", _vp), ("idx_out", _vp), ("pool_out", _vp),
                 ("win_k", _vp), ("win_v", _vp), ("win_len", _vp)]
@@ -90,6 +94,9 @@ _SIGS = {
     "csa2_plan_profile_begin": (ctypes.c_int, [_vp, _c_i32]),
     "csa2_plan_profile_read": (ctypes.c_int, [_vp, ctypes.POINTER(_c_f32), ctypes.POINTER(_c_i32)]),
     "csa2_prefill_workspace_bytes": (ctypes.c_int, [_vp, _c_i32, _c_i32, _c_i64, ctypes.POINTER(_c_sz)]),
+    "csa2_plan_prefill_workspace_bytes": (ctypes.c_int, [_vp, _c_i32, _c_i32, _c_i64, ctypes.POINTER(_c_sz)]),
+    "csa2_plan_run_prefill": (ctypes.c_int, [_vp, ctypes.POINTER(CacheDesc), ctypes.POINTER(PrefillIO), _vp, _c_i32,
+                                             _c_i32, _c_i64, _vp, _c_sz, _vp]),
     "csa2_prefill_full": (ctypes.c_int, [_vp, ctypes.POINTER(CacheDesc), _vp, _vp, _vp, _c_i32, _c_i32, _c_i64, _vp,
                                          _vp, _vp, _c_sz, _vp]),
 }
@@ -418,9 +425,17 @@ class Plan:
         _check(lib().csa2_plan_workspace_bytes(self._h, B, N, ctypes.byref(nb)), "csa2_plan_workspace_bytes")
         return nb.value
 
+    @staticmethod
+    def _caches(cache):
+        """One KVCache or a list of them (one per Full layer) -> (first cache, ctypes array of descriptors)."""
+        cs = list(cache) if isinstance(cache, (list, tuple)) else [cache]
+        arr = (CacheDesc * len(cs))(*[c.desc() for c in cs])
+        return cs[0], arr
+
     def decode_workspace(self, cache):
         """The cached workspace run_decode uses for this cache's shape (zero-filled once)."""
-        return workspace(self.workspace_bytes(cache.B, cache.N), cache.codes.device, ("plan", id(self)))
+        c0 = cache[0] if isinstance(cache, (list, tuple)) else cache
+        return workspace(self.workspace_bytes(c0.B, c0.N), c0.codes.device, ("plan", id(self)))
 
     def run_decode(self, cache, layers, ws=None, stream=None, check=True):
         """layers: list of dicts with 'q' [B][H][d] bf16, 'q_idx' [B][d_idx], 'out' [B][H][d] fp32 and
@@ -428,7 +443,8 @@ class Plan:
         'win_v' [B][W][d] bf16 and optional 'win_len' [B] int32.
         check: synchronize and raise Csa2Error if the workspace status word is nonzero (pass False in
         timing loops and read status_word(plan.decode_workspace(cache)) afterwards)."""
-        B, N = cache.B, cache.N
+        c0, descs = self._caches(cache)
+        B, N = c0.B, c0.N
         if ws is None:
             ws = self.decode_workspace(cache)
         io = (LayerIO * len(layers))()
@@ -438,8 +454,7 @@ class Plan:
                 return t.data_ptr() if t is not None else None
             io[i] = LayerIO(L["q"].data_ptr(), p("q_idx"), L["out"].data_ptr(), p("idx_out"), p("pool_out"),
                             p("win_k"), p("win_v"), p("win_len"))
-        desc = cache.desc()
-        _check(lib().csa2_plan_run_decode(self._h, ctypes.byref(desc), io, B, N, _ptr(ws), ws.numel(),
+        _check(lib().csa2_plan_run_decode(self._h, descs, io, B, N, _ptr(ws), ws.numel(),
                                           _stream(stream)), "csa2_plan_run_decode")
         if check:
             _check_status(ws, "csa2_plan_run_decode")
@@ -460,6 +475,26 @@ class Plan:
         nb = ctypes.c_size_t(0)
         _check(lib().csa2_prefill_workspace_bytes(self._h, B, Q, N, ctypes.byref(nb)), "csa2_prefill_workspace_bytes")
         return nb.value
+
+    def run_prefill(self, cache, layers, q_pos, ws=None, stream=None, check=True):
+        """A prefill chunk through every layer (csa2_plan_run_prefill). cache: a KVCache or one per Full
+        layer; layers: dicts with 'q' [B][Q][H][d] bf16, 'q_idx' [B][Q][d_idx] (Full, Reindex), 'out'
+        [B][Q][H][d] fp32 and optional 'idx_out' [B][Q][K] int32; q_pos [B][Q] int64."""
+        c0, descs = self._caches(cache)
+        B, Q = q_pos.shape
+        nb = ctypes.c_size_t(0)
+        _check(lib().csa2_plan_prefill_workspace_bytes(self._h, B, Q, c0.N, ctypes.byref(nb)),
+               "csa2_plan_prefill_workspace_bytes")
+        if ws is None:
+            ws = workspace(nb.value, c0.codes.device, ("plan_prefill", id(self)))
+        io = (PrefillIO * len(layers))()
+        for i, L in enumerate(layers):
+            io[i] = PrefillIO(L["q"].data_ptr(), L["q_idx"].data_ptr() if L.get("q_idx") is not None else None,
+                              L["out"].data_ptr(), L["idx_out"].data_ptr() if L.get("idx_out") is not None else None)
+        _check(lib().csa2_plan_run_prefill(self._h, descs, io, _ptr(q_pos), B, Q, c0.N, _ptr(ws), ws.numel(),
+                                           _stream(stream)), "csa2_plan_run_prefill")
+        if check:
+            _check_status(ws, "csa2_plan_run_prefill")
 
     def prefill_workspace(self, cache, Q):
         """The cached workspace prefill_full uses for this shape (zero-filled once)."""

@@ -439,6 +439,9 @@ int csa2_sparse_attn_swa(const uint16_t* q, int32_t B, int32_t Q, int32_t H, int
 
 struct csa2_plan {
     std::vector<int32_t> modes;
+    std::vector<int32_t> group;         // per layer: index of its Full layer's group (its cache)
+    std::vector<uint8_t> group_pool;    // per group: a Reindex layer follows its Full layer
+    int32_t groups = 0;
     csa2_plan_params p;
     bool has_reindex = false;
     // timing aid: events[(run * 2L + slot) * 2 + {0 start, 1 stop}]
@@ -556,6 +559,14 @@ int csa2_plan_create(const int32_t* modes, int32_t L, const csa2_plan_params* pa
     plan->p = p;
     if (plan->p.softmax_scale == 0.f) plan->p.softmax_scale = 1.0f / sqrtf((float)p.d);
     plan->has_reindex = has_reindex;
+    for (int32_t l = 0; l < L; ++l) {
+        if (modes[l] == CSA2_FULL) {
+            plan->groups += 1;
+            plan->group_pool.push_back(0);
+        }
+        plan->group.push_back(plan->groups - 1);
+        if (modes[l] == CSA2_REINDEX) plan->group_pool.back() = 1;
+    }
     *out = plan;
     return OK;
 }
@@ -622,12 +633,15 @@ int csa2_plan_run_decode(const csa2_plan* plan, const csa2_cache* cache, const c
     const csa2_plan_params& p = plan->p;
     const int L = (int)plan->modes.size();
     if (plan->has_reindex && p.P > N) return fail(INVALID, "csa2_plan_run_decode: pool size P exceeds N");
-    if (int e = check_attn(io[0].q, p.H, p.d, cache->k_codes, cache->k_scales, cache->v_codes, cache->v_scales, N,
-                           cache->code_stride_bytes, cache->scale_stride_bytes, p.K, "csa2_plan_run_decode",
-                           p.kv_format == CSA2_KV_MXFP4))
-        return e;
-    if (!cache->k_idx || !aligned(cache->k_idx, 16))
-        return fail(INVALID, "csa2_plan_run_decode: indexer keys null or not 16-byte aligned");
+    for (int32_t gi = 0; gi < plan->groups; ++gi) {      // one cache per Full layer
+        const csa2_cache* c = &cache[gi];
+        if (int e = check_attn(io[0].q, p.H, p.d, c->k_codes, c->k_scales, c->v_codes, c->v_scales, N,
+                               c->code_stride_bytes, c->scale_stride_bytes, p.K, "csa2_plan_run_decode",
+                               p.kv_format == CSA2_KV_MXFP4))
+            return e;
+        if (!c->k_idx || !aligned(c->k_idx, 16))
+            return fail(INVALID, "csa2_plan_run_decode: indexer keys null or not 16-byte aligned");
+    }
     for (int l = 0; l < L; ++l) {
         if (!io[l].q || !io[l].out) return fail(INVALID, "csa2_plan_run_decode: layer " + std::to_string(l) + " needs q and out");
         if (plan->modes[l] != CSA2_REUSE && !io[l].q_idx)
@@ -645,11 +659,12 @@ int csa2_plan_run_decode(const csa2_plan* plan, const csa2_cache* cache, const c
     const int32_t* pool = nullptr;
     for (int l = 0; l < L; ++l) {
         const int32_t mode = plan->modes[l];
+        const csa2_cache* gc = &cache[plan->group[l]];
         if (mode == CSA2_FULL || mode == CSA2_REINDEX) {
             int32_t* idx_dst = io[l].idx_out ? io[l].idx_out : reinterpret_cast<int32_t*>(wsb + lay.off_idx);
             ScanArgs a;
             a.q = io[l].q_idx;
-            a.k = reinterpret_cast<const uint8_t*>(cache->k_idx);
+            a.k = reinterpret_cast<const uint8_t*>(gc->k_idx);
             a.N = N;
             a.q_dtype = p.q_idx_dtype;
             a.k_dtype = p.k_idx_dtype;
@@ -660,7 +675,8 @@ int csa2_plan_run_decode(const csa2_plan* plan, const csa2_cache* cache, const c
             int e;
             SlotTimer timer(plan, 2 * l, stream);
             if (mode == CSA2_FULL) {
-                if (plan->has_reindex && !pool) {
+                pool = nullptr;                 // a Full layer opens a group: its own pool, if any
+                if (plan->group_pool[plan->group[l]]) {
                     int32_t* pool_dst = io[l].pool_out ? io[l].pool_out : reinterpret_cast<int32_t*>(wsb + lay.off_poolbuf);
                     o[0] = SelOutput{pool_dst, nullptr, p.P, p.P};
                     o[1] = SelOutput{idx_dst, nullptr, p.K, p.K};
@@ -697,13 +713,13 @@ int csa2_plan_run_decode(const csa2_plan* plan, const csa2_cache* cache, const c
         at.rows_per_seq = 1;
         at.H = p.H;
         at.d = p.d;
-        at.k_codes = cache->k_codes;
-        at.k_scales = cache->k_scales;
-        at.v_codes = cache->v_codes;
-        at.v_scales = cache->v_scales;
+        at.k_codes = gc->k_codes;
+        at.k_scales = gc->k_scales;
+        at.v_codes = gc->v_codes;
+        at.v_scales = gc->v_scales;
         at.N = N;
-        at.code_stride = cache->code_stride_bytes;
-        at.scale_stride = cache->scale_stride_bytes;
+        at.code_stride = gc->code_stride_bytes;
+        at.scale_stride = gc->scale_stride_bytes;
         at.idx = cur_idx;
         at.idx_stride = p.K;
         at.K = p.K;
@@ -728,34 +744,37 @@ int csa2_plan_run_decode(const csa2_plan* plan, const csa2_cache* cache, const c
 
 namespace {
 
-// Prefill workspace: the control region, then (matrix-core indexer path) the
-// key maxima, the sample scores (later reused for the candidate lists), the
-// sample top-R, the thresholds and counters, the repair list and map, one
-// data region shared by the three select calls (they run one after another)
-// and the attention data; or (exact path) one select region and the attention.
+// Prefill selection workspace (one region, at the start of the data area):
+// (matrix-core indexer path) the key maxima, the sample scores (later reused
+// for the candidate lists), the sample top-R, the thresholds and counters,
+// the repair queue and map, one data region shared by the three select calls
+// (they run one after another); or (exact path) one select region.
 constexpr int32_t kSampleStride = 64;           // every 64th position is sampled
 constexpr int32_t kRepairRows = 64;             // queued rows the multi-workgroup exact repair pass takes
 constexpr int64_t kRthMaxSamples = 16384;       // sample rows the threshold kernel holds in registers
 
 struct PrefillLayout {
     bool mfma = false;
+    int32_t M = 0;                              // the (larger) number of positions selected per query
     int64_t rows = 0, ns = 0;
     int32_t R = 0, nr = 0, nrd = 0, cap = 0;
     SelPlan sel_sample, sel_cand, sel_exact;
     size_t off_kmax = 0, off_dense = 0, off_sidx = 0, off_ssc = 0, off_thr = 0, off_csc = 0, off_cnt = 0,
-           off_rep = 0, off_sel = 0, off_attn = 0, total = 0;
+           off_rep = 0, off_sel = 0, end = 0;   // end: first byte after the selection region
 };
 
-bool prefill_uses_mfma(const csa2_plan_params& p, int64_t N) {
+bool prefill_uses_mfma(const csa2_plan_params& p, int64_t N, int32_t M) {
     return p.q_idx_dtype == CSA2_BF16 && (p.k_idx_dtype == CSA2_E4M3 || p.k_idx_dtype == CSA2_BF16) && p.d_idx == 64 &&
-           N >= 65536 && (int64_t)p.K * 16 <= N;
+           N >= 65536 && (int64_t)M * 16 <= N;
 }
 
-int prefill_layout(const csa2_plan* plan, int32_t B, int32_t Q, int64_t N, PrefillLayout* lay) {
+// Selection region for the top-M positions of B*Q queries, starting at `base`.
+int prefill_layout(const csa2_plan* plan, int32_t B, int32_t Q, int64_t N, int32_t M, size_t base, PrefillLayout* lay) {
     const csa2_plan_params& p = plan->p;
+    lay->M = M;
     lay->rows = (int64_t)B * Q;
-    lay->mfma = prefill_uses_mfma(p, N);
-    size_t off = align_up(kCtrlBytes);
+    lay->mfma = prefill_uses_mfma(p, N, M);
+    size_t off = base;
     if (!lay->mfma) {
         if (int e = plan_select(lay->rows, N, 1024, &lay->sel_exact)) return e;
         lay->off_sel = off;
@@ -763,11 +782,11 @@ int prefill_layout(const csa2_plan* plan, int32_t B, int32_t Q, int64_t N, Prefi
     } else {
         const int64_t rows = lay->rows;
         lay->ns = (N - kSampleStride / 2 + kSampleStride - 1) / kSampleStride;
-        lay->R = (int32_t)((2 * (int64_t)p.K * lay->ns + N - 1) / N);
+        lay->R = (int32_t)((2 * (int64_t)M * lay->ns + N - 1) / N);
         if (lay->R < 1) lay->R = 1;
         lay->nr = (int32_t)(N / 65536 < 1 ? 1 : (N / 65536 > 16 ? 16 : N / 65536));
         lay->nrd = (int32_t)(lay->ns / 2048 < 1 ? 1 : (lay->ns / 2048 > 8 ? 8 : lay->ns / 2048));
-        int64_t cap = 4 * 2 * (int64_t)p.K / lay->nr;
+        int64_t cap = 4 * 2 * (int64_t)M / lay->nr;
         if (cap < 512) cap = 512;
         lay->cap = (int32_t)((cap + 63) / 64 * 64);
         if (int e = plan_select(rows, lay->ns, 1024, &lay->sel_sample)) return e;
@@ -785,7 +804,7 @@ int prefill_layout(const csa2_plan* plan, int32_t B, int32_t Q, int64_t N, Prefi
         lay->off_thr = off;
         off += align_up((size_t)rows * 2 * 4);
         lay->off_csc = off;                     // exact scores of the selected candidates
-        off += align_up((size_t)rows * p.K * 4);
+        off += align_up((size_t)rows * M * 4);
         lay->off_cnt = off;
         off += align_up((size_t)rows * lay->nr * 4);
         lay->off_rep = off;                     // [count][pad][rows queue slots][kRepairRows map]
@@ -796,8 +815,171 @@ int prefill_layout(const csa2_plan* plan, int32_t B, int32_t Q, int64_t N, Prefi
         if (lay->sel_exact.data_bytes > sel) sel = lay->sel_exact.data_bytes;
         off += align_up(sel);
     }
+    lay->end = off;
+    return OK;
+}
+
+// The exact top-M positions (out[0], M = out[0].M) of B*Q prefill queries
+// under the causal rule, and with nt = 2 also their top-out[1].M (a prefix of
+// the same order, out[1].M <= M). Matrix-core candidates + exact re-scoring +
+// verification + repair, or the exact scan select.
+int prefill_select(const csa2_plan* plan, const PrefillLayout& lay, const csa2_cache* cache, const void* q_idx,
+                   const int64_t* q_pos, int32_t B, int32_t Q, int64_t N, SelOutput* o, int nt, uint8_t* wsb,
+                   hipStream_t stream) {
+    const csa2_plan_params& p = plan->p;
+    const int64_t rows = lay.rows;
+    ScanArgs a;
+    a.q = q_idx;
+    a.k = reinterpret_cast<const uint8_t*>(cache->k_idx);
+    a.N = N;
+    a.rows_per_seq = Q;
+    a.q_pos = q_pos;
+    a.q_dtype = p.q_idx_dtype;
+    a.k_dtype = p.k_idx_dtype;
+    a.d_idx = p.d_idx;
+    ScoresArgs none;
+    if (!lay.mfma) return run_select(lay.sel_exact, SRC_SCAN, a, none, o, nt, wsb, wsb + lay.off_sel, stream);
+    const uint16_t* qb = reinterpret_cast<const uint16_t*>(q_idx);
+    float* kmax = reinterpret_cast<float*>(wsb + lay.off_kmax);
+    float* dense = reinterpret_cast<float*>(wsb + lay.off_dense);
+    int32_t* sidx = reinterpret_cast<int32_t*>(wsb + lay.off_sidx);
+    float* ssc = reinterpret_cast<float*>(wsb + lay.off_ssc);
+    float* thr = reinterpret_cast<float*>(wsb + lay.off_thr);
+    float* csc = reinterpret_cast<float*>(wsb + lay.off_csc);
+    uint32_t* cnt = reinterpret_cast<uint32_t*>(wsb + lay.off_cnt);
+    uint32_t* rep_count = reinterpret_cast<uint32_t*>(wsb + lay.off_rep);
+    int32_t* rep_rows = reinterpret_cast<int32_t*>(wsb + lay.off_rep) + 64;
+    int32_t* rep_map = rep_rows + rows;
+    int32_t* cand = reinterpret_cast<int32_t*>(wsb + lay.off_dense);   // reuses the sample scores
+    uint32_t* status = reinterpret_cast<uint32_t*>(wsb);
+    if (int e = launch_pf_kmax(a.k, p.k_idx_dtype, B, N, kmax, stream)) return e;
+    PfTiles t;
+    t.q = qb;
+    t.k = a.k;
+    t.N = N;
+    t.B = B;
+    t.Q = Q;
+    t.q_pos = q_pos;
+    t.key_off = kSampleStride / 2;
+    t.key_stride = kSampleStride;
+    t.nkeys = lay.ns;
+    t.nranges = lay.nrd;
+    t.dense = dense;
+    if (int e = launch_pf_tiles(t, p.k_idx_dtype, true, stream)) return e;
+    if (lay.ns <= kRthMaxSamples) {
+        // the R-th largest sample score of each row (exact) straight from the dense scores
+        if (int e = launch_pf_rth(dense, rows, (int32_t)lay.ns, lay.R, ssc, stream)) return e;
+        if (int e = launch_pf_thresholds(qb, rows, Q, ssc, 1, kmax, thr, rep_count, stream)) return e;
+    } else {
+        ScoresArgs sa;
+        sa.scores = dense;
+        sa.stride = lay.ns;
+        SelOutput so{sidx, ssc, lay.R, lay.R};
+        if (int e = run_select(lay.sel_sample, SRC_SCORES, a, sa, &so, 1, wsb, wsb + lay.off_sel, stream)) return e;
+        if (int e = launch_pf_thresholds(qb, rows, Q, ssc, lay.R, kmax, thr, rep_count, stream)) return e;
+    }
+    t.key_off = 0;
+    t.key_stride = 1;
+    t.nkeys = N;
+    t.nranges = lay.nr;
+    t.dense = nullptr;
+    t.thr = thr;
+    t.cand = cand;
+    t.cap = lay.cap;
+    t.cnt = cnt;
+    if (int e = launch_pf_tiles(t, p.k_idx_dtype, false, stream)) return e;
+    ScanArgs ca = a;
+    ca.cand = cand;
+    ca.cnt = cnt;
+    ca.nranges = lay.nr;
+    ca.cap = lay.cap;
+    SelOutput oc[2] = {o[0], nt > 1 ? o[1] : o[0]};
+    oc[0].score = csc;                          // the M-th exact score decides the verification
+    if (int e = run_select(lay.sel_cand, SRC_CAND, ca, none, oc, nt, wsb, wsb + lay.off_sel, stream)) return e;
+    if (int e = launch_pf_verify(rows, lay.nr, lay.cap, cnt, csc, thr, q_pos, N, lay.M, rep_rows, rep_count,
+                                 (int32_t)rows, status, stream))
+        return e;
+    // queued rows: the first kRepairRows by the multi-workgroup exact select, any others by one
+    // workgroup each per target (that kernel returns at once when the queue is no longer)
+    if (int e = launch_pf_repair_map(rep_rows, rep_count, 0, kRepairRows, rep_map, stream)) return e;
+    ScanArgs ra = a;
+    ra.rowmap = rep_map;
+    if (int e = run_select(lay.sel_exact, SRC_SCAN, ra, none, o, nt, wsb, wsb + lay.off_sel, stream)) return e;
+    for (int j = 0; j < nt; ++j)
+        if (int e = launch_pf_repair_rest(qb, a.k, p.k_idx_dtype, N, Q, q_pos, rep_rows, rep_count, kRepairRows,
+                                          o[j].M, o[j].idx, stream))
+            return e;
+    return OK;
+}
+
+AttnArgs prefill_attn_args(const csa2_plan_params& p, const csa2_cache* c, const uint16_t* q, int64_t rows, int32_t Q,
+                           int64_t N, const int32_t* idx, float* out) {
+    AttnArgs at;
+    at.q = q;
+    at.rows = rows;
+    at.rows_per_seq = Q;
+    at.H = p.H;
+    at.d = p.d;
+    at.k_codes = c->k_codes;
+    at.k_scales = c->k_scales;
+    at.v_codes = c->v_codes;
+    at.v_scales = c->v_scales;
+    at.N = N;
+    at.code_stride = c->code_stride_bytes;
+    at.scale_stride = c->scale_stride_bytes;
+    at.idx = idx;
+    at.idx_stride = p.K;
+    at.K = p.K;
+    at.scale = p.softmax_scale;
+    at.out = out;
+    at.mx = p.kv_format == CSA2_KV_MXFP4;
+    return at;
+}
+
+// Full-layer prefill workspace: selection region (top-K), then the attention data.
+int full_prefill_layout(const csa2_plan* plan, int32_t B, int32_t Q, int64_t N, PrefillLayout* lay, size_t* off_attn,
+                        size_t* total) {
+    if (int e = prefill_layout(plan, B, Q, N, plan->p.K, align_up(kCtrlBytes), lay)) return e;
+    *off_attn = lay->end;
+    *total = lay->end + align_up(attn_data_bytes(lay->rows, plan->p.K));
+    return OK;
+}
+
+// Prefill through the whole plan: the Full layers' selection region (sized
+// for top-P when a group needs a pool, else top-K), the per-query pools, the
+// per-query positions, the Reindex select's data region and the attention's.
+struct PlanPrefillLayout {
+    PrefillLayout full;                         // selection of a Full layer that picks a pool (M = P), or top-K
+    PrefillLayout full_k;                       // selection of a Full layer without a pool (M = K)
+    SelPlan reidx;                              // Reindex selection: top-K of each query's pool
+    size_t off_pool = 0, off_idx = 0, off_reidx = 0, off_attn = 0, total = 0;
+};
+
+int plan_prefill_layout(const csa2_plan* plan, int32_t B, int32_t Q, int64_t N, PlanPrefillLayout* lay) {
+    const csa2_plan_params& p = plan->p;
+    const size_t base = align_up(kCtrlBytes);
+    bool any_pool = false;
+    for (uint8_t g : plan->group_pool) any_pool |= g != 0;
+    size_t end = base;
+    if (any_pool) {
+        if (int e = prefill_layout(plan, B, Q, N, p.P, base, &lay->full)) return e;
+        end = lay->full.end;
+    }
+    if (int e = prefill_layout(plan, B, Q, N, p.K, base, &lay->full_k)) return e;
+    if (lay->full_k.end > end) end = lay->full_k.end;
+    const int64_t rows = (int64_t)B * Q;
+    size_t off = end;
+    if (any_pool) {
+        lay->off_pool = off;
+        off += align_up((size_t)rows * p.P * 4);
+        if (int e = plan_select(rows, p.P, 1024, &lay->reidx)) return e;
+        lay->off_reidx = off;
+        off += align_up(lay->reidx.data_bytes);
+    }
+    lay->off_idx = off;
+    off += align_up((size_t)rows * p.K * 4);
     lay->off_attn = off;
-    off += align_up(attn_data_bytes(lay->rows, p.K));
+    off += align_up(attn_data_bytes(rows, p.K));
     lay->total = off;
     return OK;
 }
@@ -811,8 +993,9 @@ int csa2_prefill_workspace_bytes(const csa2_plan* plan, int32_t B, int32_t Q, in
     if (!plan || !bytes) return fail(INVALID, "csa2_prefill_workspace_bytes: null pointer");
     if (B < 1 || Q < 1 || N < 1) return fail(INVALID, "csa2_prefill_workspace_bytes: sizes must be >= 1");
     PrefillLayout lay;
-    if (int e = prefill_layout(plan, B, Q, N, &lay)) return e;
-    *bytes = lay.total;
+    size_t off_attn = 0, total = 0;
+    if (int e = full_prefill_layout(plan, B, Q, N, &lay, &off_attn, &total)) return e;
+    *bytes = total;
     return OK;
 }
 
@@ -830,114 +1013,93 @@ int csa2_prefill_full(const csa2_plan* plan, const csa2_cache* cache, const void
     if (int e = check_scan(q_idx, p.q_idx_dtype, cache->k_idx, p.k_idx_dtype, p.d_idx, "csa2_prefill_full")) return e;
     if (!q_pos || !idx_out || !out) return fail(INVALID, "csa2_prefill_full: null pointer");
     PrefillLayout lay;
-    if (int e = prefill_layout(plan, B, Q, N, &lay)) return e;
-    if (int e = check_ws(ws, ws_bytes, lay.total, "csa2_prefill_full")) return e;
+    size_t off_attn = 0, total = 0;
+    if (int e = full_prefill_layout(plan, B, Q, N, &lay, &off_attn, &total)) return e;
+    if (int e = check_ws(ws, ws_bytes, total, "csa2_prefill_full")) return e;
     if (lay.mfma && !aligned(q_idx, 16)) return fail(INVALID, "csa2_prefill_full: indexer query must be 16-byte aligned");
     uint8_t* wsb = reinterpret_cast<uint8_t*>(ws);
-    const int64_t rows = lay.rows;
-    ScanArgs a;
-    a.q = q_idx;
-    a.k = reinterpret_cast<const uint8_t*>(cache->k_idx);
-    a.N = N;
-    a.rows_per_seq = Q;
-    a.q_pos = q_pos;
-    a.q_dtype = p.q_idx_dtype;
-    a.k_dtype = p.k_idx_dtype;
-    a.d_idx = p.d_idx;
-    ScoresArgs none;
     SelOutput o{idx_out, nullptr, p.K, p.K};
-    if (!lay.mfma) {
-        if (int e = run_select(lay.sel_exact, SRC_SCAN, a, none, &o, 1, wsb, wsb + lay.off_sel, stream)) return e;
-    } else {
-        const uint16_t* qb = reinterpret_cast<const uint16_t*>(q_idx);
-        float* kmax = reinterpret_cast<float*>(wsb + lay.off_kmax);
-        float* dense = reinterpret_cast<float*>(wsb + lay.off_dense);
-        int32_t* sidx = reinterpret_cast<int32_t*>(wsb + lay.off_sidx);
-        float* ssc = reinterpret_cast<float*>(wsb + lay.off_ssc);
-        float* thr = reinterpret_cast<float*>(wsb + lay.off_thr);
-        float* csc = reinterpret_cast<float*>(wsb + lay.off_csc);
-        uint32_t* cnt = reinterpret_cast<uint32_t*>(wsb + lay.off_cnt);
-        uint32_t* rep_count = reinterpret_cast<uint32_t*>(wsb + lay.off_rep);
-        int32_t* rep_rows = reinterpret_cast<int32_t*>(wsb + lay.off_rep) + 64;
-        int32_t* rep_map = rep_rows + rows;
-        int32_t* cand = reinterpret_cast<int32_t*>(wsb + lay.off_dense);   // reuses the sample scores
-        uint32_t* status = reinterpret_cast<uint32_t*>(wsb);
-        if (int e = launch_pf_kmax(a.k, p.k_idx_dtype, B, N, kmax, stream)) return e;
-        PfTiles t;
-        t.q = qb;
-        t.k = a.k;
-        t.N = N;
-        t.B = B;
-        t.Q = Q;
-        t.q_pos = q_pos;
-        t.key_off = kSampleStride / 2;
-        t.key_stride = kSampleStride;
-        t.nkeys = lay.ns;
-        t.nranges = lay.nrd;
-        t.dense = dense;
-        if (int e = launch_pf_tiles(t, p.k_idx_dtype, true, stream)) return e;
-        if (lay.ns <= kRthMaxSamples) {
-            // the R-th largest sample score of each row (exact) straight from the dense scores
-            if (int e = launch_pf_rth(dense, rows, (int32_t)lay.ns, lay.R, ssc, stream)) return e;
-            if (int e = launch_pf_thresholds(qb, rows, Q, ssc, 1, kmax, thr, rep_count, stream)) return e;
-        } else {
-            ScoresArgs sa;
-            sa.scores = dense;
-            sa.stride = lay.ns;
-            SelOutput so{sidx, ssc, lay.R, lay.R};
-            if (int e = run_select(lay.sel_sample, SRC_SCORES, a, sa, &so, 1, wsb, wsb + lay.off_sel, stream)) return e;
-            if (int e = launch_pf_thresholds(qb, rows, Q, ssc, lay.R, kmax, thr, rep_count, stream)) return e;
-        }
-        t.key_off = 0;
-        t.key_stride = 1;
-        t.nkeys = N;
-        t.nranges = lay.nr;
-        t.dense = nullptr;
-        t.thr = thr;
-        t.cand = cand;
-        t.cap = lay.cap;
-        t.cnt = cnt;
-        if (int e = launch_pf_tiles(t, p.k_idx_dtype, false, stream)) return e;
-        ScanArgs ca = a;
-        ca.cand = cand;
-        ca.cnt = cnt;
-        ca.nranges = lay.nr;
-        ca.cap = lay.cap;
-        SelOutput oc{idx_out, csc, p.K, p.K};
-        if (int e = run_select(lay.sel_cand, SRC_CAND, ca, none, &oc, 1, wsb, wsb + lay.off_sel, stream)) return e;
-        if (int e = launch_pf_verify(rows, lay.nr, lay.cap, cnt, csc, thr, q_pos, N, p.K, rep_rows, rep_count,
-                                     (int32_t)rows, status, stream))
-            return e;
-        // queued rows: the first kRepairRows by the multi-workgroup exact select, any others by
-        // one workgroup each (that kernel returns at once when the queue is no longer)
-        if (int e = launch_pf_repair_map(rep_rows, rep_count, 0, kRepairRows, rep_map, stream)) return e;
-        ScanArgs ra = a;
-        ra.rowmap = rep_map;
-        if (int e = run_select(lay.sel_exact, SRC_SCAN, ra, none, &o, 1, wsb, wsb + lay.off_sel, stream)) return e;
-        if (int e = launch_pf_repair_rest(qb, a.k, p.k_idx_dtype, N, Q, q_pos, rep_rows, rep_count, kRepairRows, p.K,
-                                          idx_out, stream))
+    if (int e = prefill_select(plan, lay, cache, q_idx, q_pos, B, Q, N, &o, 1, wsb, stream)) return e;
+    const AttnArgs at = prefill_attn_args(p, cache, q, lay.rows, Q, N, idx_out, out);
+    return launch_attn(at, wsb, wsb + off_attn, total - off_attn, stream);
+}
+
+int csa2_plan_prefill_workspace_bytes(const csa2_plan* plan, int32_t B, int32_t Q, int64_t N, size_t* bytes) {
+    g_err.clear();
+    if (!plan || !bytes) return fail(INVALID, "csa2_plan_prefill_workspace_bytes: null pointer");
+    if (B < 1 || Q < 1 || N < 1) return fail(INVALID, "csa2_plan_prefill_workspace_bytes: sizes must be >= 1");
+    PlanPrefillLayout lay;
+    if (int e = plan_prefill_layout(plan, B, Q, N, &lay)) return e;
+    *bytes = lay.total;
+    return OK;
+}
+
+int csa2_plan_run_prefill(const csa2_plan* plan, const csa2_cache* cache, const csa2_prefill_io* io,
+                          const int64_t* q_pos, int32_t B, int32_t Q, int64_t N, void* ws, size_t ws_bytes,
+                          hipStream_t stream) {
+    g_err.clear();
+    const char* who = "csa2_plan_run_prefill";
+    if (!plan || !cache || !io || !q_pos) return fail(INVALID, std::string(who) + ": null pointer");
+    if (B < 1 || Q < 1 || N < 1) return fail(INVALID, std::string(who) + ": sizes must be >= 1");
+    const csa2_plan_params& p = plan->p;
+    if (plan->has_reindex && p.P > N) return fail(INVALID, std::string(who) + ": pool size P exceeds N");
+    if (p.swa_window > 0) return fail(INVALID, std::string(who) + ": the sliding window is a decode-time branch here");
+    const int L = (int)plan->modes.size();
+    for (int32_t gi = 0; gi < plan->groups; ++gi) {
+        const csa2_cache* c = &cache[gi];
+        if (int e = check_attn(io[0].q, p.H, p.d, c->k_codes, c->k_scales, c->v_codes, c->v_scales, N,
+                               c->code_stride_bytes, c->scale_stride_bytes, p.K, who, p.kv_format == CSA2_KV_MXFP4))
             return e;
     }
-    AttnArgs at;
-    at.q = q;
-    at.rows = rows;
-    at.rows_per_seq = Q;
-    at.H = p.H;
-    at.d = p.d;
-    at.k_codes = cache->k_codes;
-    at.k_scales = cache->k_scales;
-    at.v_codes = cache->v_codes;
-    at.v_scales = cache->v_scales;
-    at.N = N;
-    at.code_stride = cache->code_stride_bytes;
-    at.scale_stride = cache->scale_stride_bytes;
-    at.idx = idx_out;
-    at.idx_stride = p.K;
-    at.K = p.K;
-    at.scale = p.softmax_scale;
-    at.out = out;
-    at.mx = p.kv_format == CSA2_KV_MXFP4;
-    return launch_attn(at, wsb, wsb + lay.off_attn, lay.total - lay.off_attn, stream);
+    for (int l = 0; l < L; ++l) {
+        if (!io[l].q || !io[l].out) return fail(INVALID, std::string(who) + ": layer " + std::to_string(l) + " needs q and out");
+        if (plan->modes[l] != CSA2_REUSE) {
+            const csa2_cache* c = &cache[plan->group[l]];
+            if (int e = check_scan(io[l].q_idx, p.q_idx_dtype, c->k_idx, p.k_idx_dtype, p.d_idx, who)) return e;
+            if (!aligned(io[l].q_idx, 16)) return fail(INVALID, std::string(who) + ": indexer queries must be 16-byte aligned");
+        }
+    }
+    PlanPrefillLayout lay;
+    if (int e = plan_prefill_layout(plan, B, Q, N, &lay)) return e;
+    if (int e = check_ws(ws, ws_bytes, lay.total, who)) return e;
+    uint8_t* wsb = reinterpret_cast<uint8_t*>(ws);
+    const int64_t rows = (int64_t)B * Q;
+    int32_t* pool = reinterpret_cast<int32_t*>(wsb + lay.off_pool);
+    const int32_t* cur_idx = nullptr;
+    for (int l = 0; l < L; ++l) {
+        const int32_t mode = plan->modes[l];
+        const int32_t gi = plan->group[l];
+        const csa2_cache* gc = &cache[gi];
+        int32_t* idx_dst = io[l].idx_out ? io[l].idx_out : reinterpret_cast<int32_t*>(wsb + lay.off_idx);
+        if (mode == CSA2_FULL) {
+            if (plan->group_pool[gi]) {         // the group's per-query pools and top-K in one selection
+                SelOutput o[2] = {SelOutput{pool, nullptr, p.P, p.P}, SelOutput{idx_dst, nullptr, p.K, p.K}};
+                if (int e = prefill_select(plan, lay.full, gc, io[l].q_idx, q_pos, B, Q, N, o, 2, wsb, stream)) return e;
+            } else {
+                SelOutput o{idx_dst, nullptr, p.K, p.K};
+                if (int e = prefill_select(plan, lay.full_k, gc, io[l].q_idx, q_pos, B, Q, N, &o, 1, wsb, stream))
+                    return e;
+            }
+            cur_idx = idx_dst;
+        } else if (mode == CSA2_REINDEX) {      // each query's top-K of its own pool, with this layer's query
+            ScanArgs a;
+            a.q = io[l].q_idx;
+            a.k = reinterpret_cast<const uint8_t*>(gc->k_idx);
+            a.N = N;
+            a.rows_per_seq = Q;
+            a.pool = pool;
+            a.q_dtype = p.q_idx_dtype;
+            a.k_dtype = p.k_idx_dtype;
+            a.d_idx = p.d_idx;
+            ScoresArgs none;
+            SelOutput o{idx_dst, nullptr, p.K, p.K};
+            if (int e = run_select(lay.reidx, SRC_POOL, a, none, &o, 1, wsb, wsb + lay.off_reidx, stream)) return e;
+            cur_idx = idx_dst;
+        }
+        const AttnArgs at = prefill_attn_args(p, gc, io[l].q, rows, Q, N, cur_idx, io[l].out);
+        if (int e = launch_attn(at, wsb, wsb + lay.off_attn, lay.total - lay.off_attn, stream)) return e;
+    }
+    return OK;
 }
 
 }  // extern "C"

@@ -223,6 +223,7 @@ struct SrcPool {
     int64_t N;
     const int32_t* pool;
     int64_t P;
+    int32_t rows_per_seq;                        // row r reads sequence r / rows_per_seq
 
     static constexpr bool kPosLds = true;        // positions come from the pool: kept in LDS when they fit
     __device__ __forceinline__ int fill(int64_t row, int64_t begin, int cnt, int cpad, uint32_t* keys,
@@ -233,7 +234,7 @@ struct SrcPool {
         const int quad = threadIdx.x >> 2, lq = threadIdx.x & 3;
         double qd[D / 4];
         load_query_slice<QT, D>(reinterpret_cast<const uint8_t*>(q) + row * (int64_t)(D * QB), lq, qd);
-        const uint8_t* kb = k + row * N * (int64_t)KS::ROW_BYTES;
+        const uint8_t* kb = k + (row / rows_per_seq) * N * (int64_t)KS::ROW_BYTES;
         const int32_t* pr = pool + row * P + begin;
         for (int base = 0; base < cnt; base += (kSelThreads / 4) * U) {
             KS s[U];
@@ -1354,7 +1355,7 @@ int run_scan_typed(const SelPlan& p, int source, const ScanArgs& a, const SelOut
             return fail(INVALID, "candidate select needs bf16 queries, 64 channels and E4M3 or bf16 keys");
         }
     }
-    SrcPool<KT, QT, D> s{a.q, a.k, a.N, a.pool, p.n};
+    SrcPool<KT, QT, D> s{a.q, a.k, a.N, a.pool, p.n, a.rows_per_seq};
     return launch_rows(p, s, out, nt, wc, wd, stream);
 }
 

@@ -403,11 +403,24 @@ typedef struct {
     const int32_t* win_len; /*                 device [B] valid window rows, or NULL (all W) */
 } csa2_layer_io;
 
+/* One layer's inputs and outputs for csa2_plan_run_prefill (a chunk of Q queries per sequence). */
+typedef struct {
+    const uint16_t* q;      /* device [B][Q][H][d] bf16 attention queries of this layer */
+    const void* q_idx;      /* device [B][Q][d_idx] indexer queries (Full, Reindex; 16-byte aligned);
+                               ignored for Reuse */
+    float* out;             /* device [B][Q][H][d] fp32 attention output */
+    int32_t* idx_out;       /* device [B][Q][K] positions this layer attends, or NULL */
+} csa2_prefill_io;
+
 int csa2_plan_create(const int32_t* modes, int32_t L, const csa2_plan_params* params, csa2_plan** out);
 void csa2_plan_destroy(csa2_plan* plan);
 int csa2_plan_workspace_bytes(const csa2_plan* plan, int32_t B, int64_t N, size_t* bytes);
 /* One decode step of the whole stack for B sequences, one query each; layers
- * run in order on `stream`. io has one entry per layer. */
+ * run in order on `stream`. io has one entry per layer. `cache` points to one
+ * csa2_cache per Full layer, in layer order (R: a Full layer computes KV
+ * afresh, so each Full layer opens a group - its own main KV cache, indexer
+ * keys and pool - that the Reindex and Reuse layers after it share, up to the
+ * next Full layer; a one-Full plan reads one cache). */
 int csa2_plan_run_decode(const csa2_plan* plan, const csa2_cache* cache, const csa2_layer_io* io,
                          int32_t B, int64_t N, void* ws, size_t ws_bytes, hipStream_t stream);
 
@@ -444,6 +457,25 @@ int csa2_plan_profile_read(csa2_plan* plan, float* avg_ms, int32_t* runs);
  * workgroup per query). The result is always the exact top-K.
  */
 int csa2_prefill_workspace_bytes(const csa2_plan* plan, int32_t B, int32_t Q, int64_t N, size_t* bytes);
+/*
+ * csa2_plan_run_prefill - a prefill chunk of Q queries per sequence through
+ * every layer of the plan ([jiwasawa] CSA2, Hierarchical Sparse Indexer:
+ * the pool of a Full layer is what later Reindex layers search; each query
+ * of a chunk is one step of the stack at its own position): per query, each
+ * Full layer selects under the causal rule (positions <= q_pos) its top-K and,
+ * when a Reindex layer follows in its group, its own pool (top-P); a Reindex
+ * layer takes the top-K of that query's pool with its own indexer query; a
+ * Reuse layer takes the preceding layer's positions; every layer runs sparse
+ * FP4 attention for all B*Q queries. Every selection is the exact top-K (or
+ * top-P), as csa2_prefill_full. `cache`: one per Full layer, as
+ * csa2_plan_run_decode; io: one csa2_prefill_io per layer; q_pos: device
+ * [B][Q] int64. The plan's sliding window (swa_window) is not applied here
+ * (the call rejects a plan that has one).
+ */
+int csa2_plan_prefill_workspace_bytes(const csa2_plan* plan, int32_t B, int32_t Q, int64_t N, size_t* bytes);
+int csa2_plan_run_prefill(const csa2_plan* plan, const csa2_cache* cache, const csa2_prefill_io* io,
+                          const int64_t* q_pos, int32_t B, int32_t Q, int64_t N, void* ws, size_t ws_bytes,
+                          hipStream_t stream);
 int csa2_prefill_full(const csa2_plan* plan, const csa2_cache* cache, const void* q_idx,
                       const uint16_t* q, const int64_t* q_pos, int32_t B, int32_t Q, int64_t N,
                       int32_t* idx_out, float* out, void* ws, size_t ws_bytes, hipStream_t stream);
