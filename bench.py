@@ -33,8 +33,15 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 METRIC = "decode queries/s per CSA2 layer stack + achieved HBM GB/s (% of peak)"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_full_select_stack_b32_n262144.json")
-KERNEL_SOURCES = ["select.hip", "dot.hpp", "device.hpp"]
+# HBM traffic per launch from committed rocprofv3 PMC passes (profiles/traffic_<kernel>_<workload>.json),
+# each tied to a hash of the sources its kernel is built from and ignored once they change.
+TRAFFIC_KERNELS = {
+    "full_select": ["select.hip", "dot.hpp", "device.hpp"],
+    "quant": ["quant.hip", "fp4q.hpp", "device.hpp"],
+    "quant_mx": ["quant.hip", "fp4q.hpp", "device.hpp"],
+    "kv_project": ["project.hip", "fp4q.hpp", "device.hpp"],
+    "kv_project_mx": ["project.hip", "fp4q.hpp", "device.hpp"],
+}
 
 
 def log(*a):
@@ -75,24 +82,35 @@ def alg_bytes(cfg, kv="fp4_e4m3", swa=0):
     return B * per_seq, B * full_sel
 
 
-def kernel_hash():
+def kernel_hash(kernel="full_select"):
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in TRAFFIC_KERNELS[kernel]:
         with open(os.path.join(ROOT, "fp4_compressed_sparse_kv_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload):
-    """HBM bytes per launch of the Full selection kernel from the committed PMC runs, or None
-    when they were taken on other kernel sources or another workload."""
-    if not os.path.exists(TRAFFIC_FILE):
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` on `workload` from the committed PMC runs, or None when
+    there are none or they were taken on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+    if not os.path.exists(path):
         return None
-    with open(TRAFFIC_FILE) as fh:
+    with open(path) as fh:
         t = json.load(fh)
-    if t.get("kernel_hash") != kernel_hash() or t.get("workload") != workload:
+    if t.get("kernel_hash") != kernel_hash(kernel) or t.get("workload") != workload:
         return None
     return t.get("traffic_bytes_per_launch")
+
+
+def copy_calibration(dev):
+    """A known-size copy kernel for scaling the PMC byte counters: reads and writes 1 GiB."""
+    import torch
+    x = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    y = torch.empty_like(x)
+    torch.add(x, 0.0, out=y)
+    torch.cuda.synchronize()
+    del x, y
 
 
 def build_inputs(cfg, dev, query_set=0, kv="fp4_e4m3", swa=0):
@@ -295,6 +313,8 @@ def run_proj(args, cfg, dev):
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
+    if args.copy_calibration:
+        copy_calibration(dev)
     nbytes = T * D * 2 + Cc * D * 2 + T * (Cc // 2 + Cc // (32 if mx else 16))
     flop = 2.0 * T * D * Cc
     gbs = nbytes / (ms * 1e-3) / 1e9
@@ -310,7 +330,8 @@ def run_proj(args, cfg, dev):
         "mfma_frac": round(tflops / 2500.0, 4),
         # the HBM floor (bytes / 8 TB/s) is above the matrix-core floor (FLOP / 2.5 PFLOP/s) at C = 256
         "roofline": {"bound": "hbm", "kernel": "k_kv_project", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic("kv_project_mx" if mx else "kv_project", args.workload)},
     }
     if not args.no_cpu:
         done, spent = 0, 0.0
@@ -371,6 +392,8 @@ def run_quant(args, cfg, dev):
 
     q_ms = timed(lambda: quant(x, codes, scales))
     d_ms = timed(lambda: dequant(codes, scales, Cc, y))
+    if args.copy_calibration:
+        copy_calibration(dev)
     nbytes = T * Cc * 2 + T * (Cc // 2 + Cc // blk)           # bf16 rows + codes + scales, each direction
     groups = T * Cc // blk
     s_zero = int((scales == 0).sum().item())
@@ -389,7 +412,7 @@ def run_quant(args, cfg, dev):
         "roofline": {"bound": "hbm", "kernel": "k_quant_mx" if mx else "k_quant",
                      "achieved": round(nbytes / (q_ms * 1e-3) / 1e9, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(nbytes / (q_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                     "traffic": None},
+                     "traffic": measured_traffic("quant_mx" if mx else "quant", args.workload)},
     }
     if not args.no_cpu:
         done, spent = 0, 0.0
@@ -695,18 +718,13 @@ def main():
     del src, dst
 
     if args.copy_calibration:
-        # known-size copy kernel for scaling PMC byte counters: reads and writes 1 GiB
-        x = torch.ones(1 << 28, dtype=torch.float32, device=dev)
-        y = torch.empty_like(x)
-        torch.add(x, 0.0, out=y)
-        torch.cuda.synchronize()
-        del x, y
+        copy_calibration(dev)
 
     step_bytes, sel_bytes = alg_bytes(cfg, args.kv, args.swa)
     qps = cfg["B"] / (ms * 1e-3)
     sel_ms = slot_ms[0]
     achieved = sel_bytes / (sel_ms * 1e-3) / 1e9
-    traffic = measured_traffic(args.workload)
+    traffic = measured_traffic("full_select", args.workload)
     out = {
         "metric": METRIC,
         "value": round(qps, 1) if status == 0 else None,
