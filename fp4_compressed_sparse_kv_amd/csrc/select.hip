@@ -19,7 +19,7 @@
 // than CUs, and the kernel fits one per CU) every chunk knows the bin b1 that
 // holds the M-th largest key, and every chunk's count of keys above b1 and
 // in it.
-//   List path (S > 1 and at most kCandCap keys in bin b1 row-wide): each
+//   List path (S > 1 and at most kListCap keys in bin b1 row-wide): each
 //     wave first copies its keys in bin b1 or above (a few percent of them)
 //     with their indices, in index order, to the start of its own LDS span;
 //     the later steps visit only these. Each chunk writes its bin-b1 keys to
@@ -27,7 +27,9 @@
 //     counts). After a second barrier every chunk reads the short list and
 //     resolves the exact threshold key T, how many entries equal to T are
 //     taken, and the counts of entries > T and == T in earlier chunks and in
-//     all chunks, with no further exchange.
+//     all chunks, with no further exchange. A list of up to kListBatch
+//     entries stays in registers for all of these passes; a longer one is
+//     read again, batch by batch, in each pass.
 //   Radix path (otherwise): two more radix passes over the LDS keys (11 and
 //     10 bits), each with a row-wide histogram exchange, then an exchange of
 //     the per-chunk counts of keys > T and == T.
@@ -46,7 +48,8 @@ constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / kWave;
 constexpr int kB1 = 2048, kB2 = 2048, kB3 = 1024;   // radix digits 11 | 11 | 10 bits
 constexpr int kRowHdr = 16;                          // control words of a row: [0] barrier, [1] exit
-constexpr int kCandCap = 16384;                      // list entries per (row, target)
+constexpr int kListCap = 32768;                      // list entries per (row, target)
+constexpr int kListBatch = 16384;                    // list entries held in registers at once
 constexpr int kMaxS = 256;                           // chunks per row (<= CUs)
 constexpr int kScratchWords = 256;
 constexpr int kLdsFixedWords = kB1 + 2 * kB2 + 4 * kMaxS + kScratchWords;
@@ -587,7 +590,7 @@ __global__ void __launch_bounds__(kSelThreads) k_select(Src src, SelDev g, SelTg
     uint32_t* rw = g.data + (size_t)lrow * g.row_words;                              // data, any content
     uint32_t* gcnt = rw;                        // [S][2][> T, == T]
     uint32_t* gsuf = gcnt + 4 * S;              // [S][kB1] per-chunk suffix sums of the top-digit histogram
-    uint32_t* glist = gsuf + (size_t)S * kB1;  // [2][kCandCap] bin-b1 keys, one segment per chunk in chunk order
+    uint32_t* glist = gsuf + (size_t)S * kB1;  // [2][kListCap] bin-b1 keys, one segment per chunk in chunk order
     uint32_t gen = 0;
 
     const uint32_t M[2] = {(uint32_t)t0.M, (uint32_t)t1.M};
@@ -638,7 +641,7 @@ __global__ void __launch_bounds__(kSelThreads) k_select(Src src, SelDev g, SelTg
                 b1[j] = f[j].bin;
                 rem[j] = f[j].rem;
                 C[j] = G[f[j].bin];
-                path[j] = (multi && C[j] <= (uint32_t)kCandCap) ? kPathList : kPathRadix;
+                path[j] = (multi && C[j] <= (uint32_t)kListCap) ? kPathList : kPathRadix;
             }
         }
     }
@@ -786,8 +789,8 @@ __global__ void __launch_bounds__(kSelThreads) k_select(Src src, SelDev g, SelTg
                 const bool c = v && k != 0u && (k >> 21) == b1[j];
                 const uint64_t m = __ballot(c);
                 const uint32_t slot = run[j] + lanes_below(m);
-                if (c && slot < hi[j] && slot < (uint32_t)kCandCap)   // holds: the waves' counts sum to hi - lo
-                    st_rlx(&glist[(size_t)j * kCandCap + slot], k);
+                if (c && slot < hi[j] && slot < (uint32_t)kListCap)   // holds: the waves' counts sum to hi - lo
+                    st_rlx(&glist[(size_t)j * kListCap + slot], k);
                 run[j] += (uint32_t)__popcll(m);
             }
         });
@@ -854,36 +857,55 @@ __global__ void __launch_bounds__(kSelThreads) k_select(Src src, SelDev g, SelTg
     uint32_t lgt_all[2] = {0u, 0u}, leq_all[2] = {0u, 0u};   // list entries > T and == T (list targets)
     if (any_list) {
         row_barrier(ctrl, S, gen, status);
-        constexpr int R = kCandCap / kSelThreads;
+        constexpr int R = kListBatch / kSelThreads;
         uint32_t ent[2][R];
-        int rn[2] = {0, 0};                     // list slots per thread in use (uniform)
-        // coherent buffer loads: entries past C read 0 (a padding key) without
-        // a branch, so all of a thread's loads are in flight together
+        int rn[2] = {0, 0};                     // list slots per thread in use in the current batch (uniform)
+        int nbat = 0;                           // batches of the longest list (uniform)
 #pragma unroll
-        for (int j = 0; j < NT; ++j) {
-            if (path[j] == kPathList) rn[j] = ((int)C[j] + kSelThreads - 1) / kSelThreads;
-            const __amdgpu_buffer_rsrc_t lr = __builtin_amdgcn_make_buffer_rsrc(
-                glist + (size_t)j * kCandCap, (short)0, (int)(path[j] == kPathList ? C[j] * 4u : 0u), kRsrcWord3);
-            // (ent[j][r] is read only for r < rn[j]; left unset otherwise, so
-            // the loads need no merge with a default and stay in flight)
+        for (int j = 0; j < NT; ++j)
+            if (path[j] == kPathList) nbat = max(nbat, (int)((C[j] + kListBatch - 1) / kListBatch));
+        // Batch bi of the list targets: entry tid + r * kSelThreads of the batch
+        // is list entry bi * kListBatch + tid + r * kSelThreads. Coherent buffer
+        // loads: entries past the list's end read 0 (a padding key) without a
+        // branch, so all of a thread's loads are in flight together; ent[j][r]
+        // is read only for r < rn[j] and left unset otherwise, so the loads need
+        // no merge with a default.
+        auto ld_batch = [&](int bi) {
 #pragma unroll
-            for (int r = 0; r < R; ++r)
-                if (r < rn[j])                  // uniform
-                    ent[j][r] = __builtin_amdgcn_raw_buffer_load_b32(lr, (tid + r * kSelThreads) * 4, 0, kCoherent);
-        }
+            for (int j = 0; j < NT; ++j) {
+                const uint32_t cj = path[j] == kPathList ? C[j] : 0u;
+                const uint32_t base = (uint32_t)bi * kListBatch;
+                const uint32_t nb = cj > base ? min(cj - base, (uint32_t)kListBatch) : 0u;
+                rn[j] = (int)((nb + kSelThreads - 1) / kSelThreads);
+                const __amdgpu_buffer_rsrc_t lr = __builtin_amdgcn_make_buffer_rsrc(
+                    glist + (size_t)j * kListCap + base, (short)0, (int)(nb * 4u), kRsrcWord3);
+#pragma unroll
+                for (int r = 0; r < R; ++r)
+                    if (r < rn[j])              // uniform
+                        ent[j][r] = __builtin_amdgcn_raw_buffer_load_b32(lr, (tid + r * kSelThreads) * 4, 0, kCoherent);
+            }
+        };
+        // a pass over the list: one batch in registers is reused, longer lists are read again
+        auto reload = [&](int bi) {
+            if (nbat > 1) ld_batch(bi);
+        };
+        ld_batch(0);
         // both targets' digit histograms side by side: bits 10..20, then bits 0..9
         uint32_t nd[2] = {0u, 0u};
 #pragma unroll
         for (int j = 0; j < NT; ++j) nd[j] = path[j] == kPathList ? rem[j] : 0u;
         for (int i = tid; i < NT * kB2; i += kSelThreads) lh2[i] = 0u;
         __syncthreads();
+        for (int bi = 0; bi < nbat; ++bi) {
+            if (bi > 0) ld_batch(bi);
 #pragma unroll
-        for (int j = 0; j < NT; ++j) {
+            for (int j = 0; j < NT; ++j) {
 #pragma unroll
-            for (int r = 0; r < R; ++r) {
-                if (r >= rn[j]) break;
-                const uint32_t k = ent[j][r];
-                if (k) atomicAdd(&lh2[j * kB2 + ((k >> 10) & 2047u)], 1u);
+                for (int r = 0; r < R; ++r) {
+                    if (r >= rn[j]) break;
+                    const uint32_t k = ent[j][r];
+                    if (k) atomicAdd(&lh2[j * kB2 + ((k >> 10) & 2047u)], 1u);
+                }
             }
         }
         __syncthreads();
@@ -894,15 +916,18 @@ __global__ void __launch_bounds__(kSelThreads) k_select(Src src, SelDev g, SelTg
         // target with more of them than one per thread takes a histogram of
         // the low 10 bits instead.
         uint32_t* tie = lh2;                    // [2][kSelThreads] (the histogram is no longer read)
+        for (int bi = 0; bi < nbat; ++bi) {
+            reload(bi);
 #pragma unroll
-        for (int j = 0; j < NT; ++j) {
+            for (int j = 0; j < NT; ++j) {
 #pragma unroll
-            for (int r = 0; r < R; ++r) {
-                if (r >= rn[j]) break;
-                const uint32_t k = ent[j][r];
-                if (k && ((k >> 10) & 2047u) == f2[j].bin) {
-                    const uint32_t slot = atomicAdd(&sm[206 + j], 1u);
-                    if (slot < (uint32_t)kSelThreads) tie[j * kSelThreads + slot] = k;
+                for (int r = 0; r < R; ++r) {
+                    if (r >= rn[j]) break;
+                    const uint32_t k = ent[j][r];
+                    if (k && ((k >> 10) & 2047u) == f2[j].bin) {
+                        const uint32_t slot = atomicAdd(&sm[206 + j], 1u);
+                        if (slot < (uint32_t)kSelThreads) tie[j * kSelThreads + slot] = k;
+                    }
                 }
             }
         }
@@ -946,13 +971,17 @@ __global__ void __launch_bounds__(kSelThreads) k_select(Src src, SelDev g, SelTg
             for (int i = tid; i < NT * kB3; i += kSelThreads) lh2[i] = 0u;
             __syncthreads();
 #pragma unroll
-            for (int j = 0; j < NT; ++j) {
-                nd[j] = path[j] == kPathList ? f2[j].rem : 0u;
+            for (int j = 0; j < NT; ++j) nd[j] = path[j] == kPathList ? f2[j].rem : 0u;
+            for (int bi = 0; bi < nbat; ++bi) {
+                reload(bi);
 #pragma unroll
-                for (int r = 0; r < R; ++r) {
-                    if (r >= rn[j]) break;
-                    const uint32_t k = ent[j][r];
-                    if (k && ((k >> 10) & 2047u) == f2[j].bin) atomicAdd(&lh2[j * kB3 + (k & 1023u)], 1u);
+                for (int j = 0; j < NT; ++j) {
+#pragma unroll
+                    for (int r = 0; r < R; ++r) {
+                        if (r >= rn[j]) break;
+                        const uint32_t k = ent[j][r];
+                        if (k && ((k >> 10) & 2047u) == f2[j].bin) atomicAdd(&lh2[j * kB3 + (k & 1023u)], 1u);
+                    }
                 }
             }
             __syncthreads();
@@ -970,28 +999,42 @@ __global__ void __launch_bounds__(kSelThreads) k_select(Src src, SelDev g, SelTg
         // above b2, then the ranking inside it); those before this chunk's
         // segment (earlier chunks) are counted by list position with ballots.
         // The per-wave sums go to lh2 (free once T is known).
+        uint32_t gt_before[2] = {0u, 0u}, eq_before[2] = {0u, 0u};
 #pragma unroll
         for (int j = 0; j < NT; ++j) {
             if (path[j] != kPathList) continue;
             T[j] = (b1[j] << 21) | (f2[j].bin << 10) | tbin[j];
             lgt_all[j] = (rem[j] - f2[j].rem) + gt_t[j];
             leq_all[j] = eq_t[j];
-            const uint32_t lo = sm[200 + 2 * j];
-            const int rlo = ((int)lo + kSelThreads - 1) / kSelThreads;
-            uint32_t gt_before = 0, eq_before = 0;
+        }
+        for (int bi = 0; bi < nbat; ++bi) {
+            const uint32_t base = (uint32_t)bi * kListBatch;
+            bool more = false;                  // entries of earlier chunks left in this batch (uniform)
 #pragma unroll
-            for (int r = 0; r < R; ++r) {
-                if (r >= rlo) break;
-                const uint32_t e = (uint32_t)(tid + r * kSelThreads);
-                const uint32_t k = ent[j][r];
-                const bool b = e < lo;
-                gt_before += (uint32_t)__popcll(__ballot(b && k > T[j]));   // padding keys are 0 < T
-                eq_before += (uint32_t)__popcll(__ballot(b && k == T[j]));
+            for (int j = 0; j < NT; ++j) more = more || (path[j] == kPathList && sm[200 + 2 * j] > base);
+            if (!more) break;
+            reload(bi);
+#pragma unroll
+            for (int j = 0; j < NT; ++j) {
+                if (path[j] != kPathList) continue;
+                const uint32_t lo = sm[200 + 2 * j];
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    if (r >= rn[j] || base + (uint32_t)(r * kSelThreads) >= lo) break;
+                    const uint32_t e = base + (uint32_t)(tid + r * kSelThreads);
+                    const uint32_t k = ent[j][r];
+                    const bool b = e < lo;
+                    gt_before[j] += (uint32_t)__popcll(__ballot(b && k > T[j]));   // padding keys are 0 < T
+                    eq_before[j] += (uint32_t)__popcll(__ballot(b && k == T[j]));
+                }
             }
-            if (lane == 0) {
+        }
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+            if (path[j] == kPathList && lane == 0) {
                 uint32_t* agg = lh2 + (j * kSelWaves + wave) * 2;
-                agg[0] = gt_before;
-                agg[1] = eq_before;
+                agg[0] = gt_before[j];
+                agg[1] = eq_before[j];
             }
         }
     }
@@ -1267,7 +1310,7 @@ int plan_select(int64_t rows, int64_t n, int32_t min_chunk, SelPlan* out) {
     if (rows > 0 && p.rows_per_launch > rows) p.rows_per_launch = (int32_t)rows;
     if (p.rows_per_launch < 1) p.rows_per_launch = 1;
     p.launches = rows > 0 ? (int32_t)((rows + p.rows_per_launch - 1) / p.rows_per_launch) : 0;
-    p.row_words = S == 1 ? 0 : 4 * (int32_t)S + (int32_t)S * kB1 + 2 * kCandCap;
+    p.row_words = S == 1 ? 0 : 4 * (int32_t)S + (int32_t)S * kB1 + 2 * kListCap;
     p.row_words = (p.row_words + 63) / 64 * 64;
     p.chunk_pad = (int32_t)((chunk + kPadTo - 1) / kPadTo * kPadTo);
     p.lds_bytes = (size_t)(p.chunk_pad + kLdsFixedWords) * 4;

@@ -198,6 +198,13 @@ def _scores_with_ties(rng, rows, n, kind):
         s = rng.integers(-3, 4, (rows, n)).astype(np.float32)
     elif kind == "equal":
         s = np.full((rows, n), 1.25, dtype=np.float32)
+    elif kind.startswith("bin"):                            # bin20k: 20,000 keys in [1, 1.25), one top-digit bin
+        c = int(kind[3:].split("k")[0]) * 1000
+        s = (rng.standard_normal((rows, n)) * 0.1).astype(np.float32)
+        for r in range(rows):
+            at = rng.choice(n, c, replace=False)
+            s[r, at] = (1.0 + rng.integers(0, 16, c) / 64.0 if kind.endswith("kt")     # 16 values, many ties
+                        else rng.uniform(1.0, 1.25, c)).astype(np.float32)
     elif kind == "inf":                                     # the top-K is a subset of many +inf
         s = rng.standard_normal((rows, n)).astype(np.float32)
         s[rng.random((rows, n)) < 0.3] = np.inf
@@ -219,7 +226,10 @@ def _scores_with_ties(rng, rows, n, kind):
     (2, 70001, 2048, "few"),        # > 1024 keys equal to the threshold: low-bit histogram fallback
     # rows of 2..16 chunks, which exchange suffix sums only
     (32, 70001, 2048, "normal"), (32, 70001, 50000, "normal"), (32, 70001, 2048, "few"),
-    (32, 70001, 2048, "inf"), (16, 262144, 100, "equal"), (20, 100000, 3000, "ties")])
+    (32, 70001, 2048, "inf"), (16, 262144, 100, "equal"), (20, 100000, 3000, "ties"),
+    # 16K..32K keys in the threshold's top-digit bin: the row list is resolved in two batches
+    (2, 300000, 8192, "bin20k"), (1, 1000000, 2048, "bin30k"), (3, 262144, 8192, "bin24kt"),
+    (1, 300000, 8192, "bin40k")])   # more than the list holds: the radix path
 def test_topk_matches_oracle(rows, n, K, kind):
     rng = np.random.default_rng(rows * 1000 + n + K)
     s = _scores_with_ties(rng, rows, n, kind)
