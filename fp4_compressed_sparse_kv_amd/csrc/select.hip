@@ -651,17 +651,21 @@ __global__ void __launch_bounds__(kSelThreads) k_select(Src src, SelDev g, SelTg
     const bool any_other = path[0] != kPathList || (NT > 1 && path[1] != kPathList);
 
     // ---- each wave owns a contiguous span of kPadTo-key steps; its lanes keep
-    // the span's keys in registers (4 per lane per step) for the passes below
+    // the span's keys in registers for the passes below: component u of lane
+    // l's word for step t is the key of chunk index w0 + t*kPadTo + 64u + l,
+    // so one ballot per component covers 64 consecutive indices in order
     int span = (cpad + kSelWaves - 1) / kSelWaves;
     span = (span + kPadTo - 1) / kPadTo * kPadTo;
     const int w0 = min(cpad, wave * span), w1 = min(cpad, w0 + span);
     const int nst = (w1 - w0) / kPadTo;         // steps of this wave (<= kMaxSteps)
+    static_assert(kPadTo == 4 * kWave, "four components of 64 keys per step");
     uint4 kreg[kMaxSteps];
     auto load_kreg = [&]() {
 #pragma unroll
-        for (int t = 0; t < kMaxSteps; ++t)
-            kreg[t] = (t < nst) ? *reinterpret_cast<const uint4*>(&keys[w0 + t * kPadTo + 4 * lane])
-                                : make_uint4(0, 0, 0, 0);
+        for (int t = 0; t < kMaxSteps; ++t) {
+            const uint32_t* kp = &keys[w0 + t * kPadTo + lane];
+            kreg[t] = (t < nst) ? make_uint4(kp[0], kp[kWave], kp[2 * kWave], kp[3 * kWave]) : make_uint4(0, 0, 0, 0);
+        }
     };
     uint32_t* wcnt = sm + 64;                   // [2][16][gt, eq] per-wave counts of this chunk
 
@@ -698,30 +702,30 @@ __global__ void __launch_bounds__(kSelThreads) k_select(Src src, SelDev g, SelTg
 #pragma unroll
         for (int t = 0; t < kMaxSteps; ++t) {
             if (t >= nst) break;
-            const int ib = w0 + t * kPadTo + 4 * lane;
+            const int ib = w0 + t * kPadTo + lane;
             const uint32_t kv[4] = {kreg[t].x, kreg[t].y, kreg[t].z, kreg[t].w};
-            // this lane's candidates (bit u: key 4*lane + u), their count, and the
-            // count in lower lanes by one wave scan: slots follow index order
-            uint32_t cm = 0;
+            // candidates of component u (indices ib + 64u over the lanes) take
+            // consecutive slots in lane order: slots follow index order
 #pragma unroll
-            for (int u = 0; u < 4; ++u) cm |= (uint32_t)(kv[u] >= lowk) << u;
-            const uint32_t mine = (uint32_t)__popc(cm);
-            const uint32_t incl = wave_incl_scan(mine);
-            const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)incl, kWave - 1);
-            uint32_t slot = npair + incl - mine;
-            while (cm) {
-                const int u = __builtin_ctz(cm);
-                cm &= cm - 1u;
-                if (slot < cap) pairs[slot] = make_uint2(u == 0 ? kv[0] : u == 1 ? kv[1] : u == 2 ? kv[2] : kv[3], (uint32_t)(ib + u));
-                ++slot;
+            for (int u = 0; u < 4; ++u) {
+                const bool c = kv[u] >= lowk;
+                const uint64_t m = __ballot(c);
+                const uint32_t slot = npair + lanes_below(m);
+                if (c && slot < cap) pairs[slot] = make_uint2(kv[u], (uint32_t)(ib + kWave * u));
+                npair += (uint32_t)__popcll(m);
             }
-            npair += total;
         }
         ext = npair <= cap;
         if (!ext) {
 #pragma unroll
-            for (int t = 0; t < kMaxSteps; ++t)
-                if (t < nst) *reinterpret_cast<uint4*>(&keys[w0 + t * kPadTo + 4 * lane]) = kreg[t];
+            for (int t = 0; t < kMaxSteps; ++t) {
+                if (t >= nst) continue;
+                uint32_t* kp = &keys[w0 + t * kPadTo + lane];
+                kp[0] = kreg[t].x;
+                kp[kWave] = kreg[t].y;
+                kp[2 * kWave] = kreg[t].z;
+                kp[3 * kWave] = kreg[t].w;
+            }
         }
     }
     // Visit this wave's keys in index order, 64 at a time: f(key, chunk index,
@@ -738,11 +742,11 @@ __global__ void __launch_bounds__(kSelThreads) k_select(Src src, SelDev g, SelTg
 #pragma unroll
             for (int t = 0; t < kMaxSteps; ++t) {
                 if (t >= nst) break;
-                const int ib = w0 + t * kPadTo + 4 * lane;
-                f(kreg[t].x, (uint32_t)ib, true);
-                f(kreg[t].y, (uint32_t)ib + 1u, true);
-                f(kreg[t].z, (uint32_t)ib + 2u, true);
-                f(kreg[t].w, (uint32_t)ib + 3u, true);
+                const uint32_t ib = (uint32_t)(w0 + t * kPadTo + lane);
+                f(kreg[t].x, ib, true);
+                f(kreg[t].y, ib + kWave, true);
+                f(kreg[t].z, ib + 2u * kWave, true);
+                f(kreg[t].w, ib + 3u * kWave, true);
             }
         }
     };
@@ -1170,88 +1174,26 @@ __global__ void __launch_bounds__(kSelThreads) k_select(Src src, SelDev g, SelTg
         uint32_t run_eq = wbase[(j * kSelWaves + wave) * 2 + 1];
         int32_t* out_idx = t.idx + row * t.stride;
         float* out_sc = t.score ? t.score + row * t.stride : nullptr;
-        if (ext) {
-            for (uint32_t i0 = 0; i0 < npair; i0 += kWave) {
-                const uint32_t i = i0 + (uint32_t)lane;
-                const bool v = i < npair;
-                const uint2 pr = v ? pairs[i] : make_uint2(0u, 0u);
-                bool s = v && pr.x > Tj;
-                if (eq_all) {
-                    s = s || (v && pr.x == Tj);
-                } else if (take_eq) {           // ties at T split inside this chunk: ranked in index order
-                    const bool e = v && pr.x == Tj;
-                    const uint64_t me = __ballot(e);
-                    s = s || (e && run_eq + lanes_below(me) < take_eq);
-                    run_eq += (uint32_t)__popcll(me);
-                }
-                const uint64_t m = __ballot(s);
-                const uint32_t slot = run_sel + lanes_below(m);
-                if (s && slot < M[j]) {         // the bound holds whenever the counts agree
-                    out_idx[slot] = pos_lds ? (int32_t)posl[pr.y] : src.position(row, begin + (int64_t)pr.y);
-                    if (out_sc) out_sc[slot] = key_score(pr.x);
-                }
-                run_sel += (uint32_t)__popcll(m);
+        // 64 consecutive entries in index order, one per lane (v: the entry exists)
+        auto emit = [&](uint32_t k, uint32_t ci, bool v) {
+            bool s = v && k > Tj;
+            if (eq_all) {
+                s = s || (v && k == Tj && k != 0u);
+            } else if (take_eq) {               // ties at T split inside this chunk: ranked in index order
+                const bool e = v && k == Tj && k != 0u;
+                const uint64_t me = __ballot(e);
+                s = s || (e && run_eq + lanes_below(me) < take_eq);
+                run_eq += (uint32_t)__popcll(me);
             }
-        } else {
-            load_kreg();
-            // Entry (lane, u) of a step has index i0 + 4*lane + u; its rank among the
-            // step's selected entries is the count over all u of selected entries in
-            // lower lanes (one ballot per u, counted with mbcnt) plus those at u' < u
-            // in its own lane - no cross-lane data movement.
-#pragma unroll
-            for (int t = 0; t < kMaxSteps; ++t) {
-                if (t >= nst) break;
-                const int ib = w0 + t * kPadTo + 4 * lane;
-                const uint32_t kv[4] = {kreg[t].x, kreg[t].y, kreg[t].z, kreg[t].w};
-                uint32_t selm = 0, below = 0, total = 0;
-                if (eq_all || take_eq == 0) {
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        const bool s = kv[u] > Tj || (eq_all && kv[u] == Tj && kv[u] != 0u);
-                        const uint64_t m = __ballot(s);
-                        selm |= (uint32_t)s << u;
-                        below += lanes_below(m);
-                        total += (uint32_t)__popcll(m);
-                    }
-                } else {                        // ties at T split inside this chunk: rank them in index order
-                    uint32_t eqm = 0, eq_below = 0, eq_total = 0;
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        const bool e = kv[u] == Tj && kv[u] != 0u;
-                        const uint64_t m = __ballot(e);
-                        eqm |= (uint32_t)e << u;
-                        eq_below += lanes_below(m);
-                        eq_total += (uint32_t)__popcll(m);
-                    }
-                    uint32_t r = run_eq + eq_below;
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        bool s = kv[u] > Tj;
-                        if ((eqm >> u) & 1u) {
-                            s = r < take_eq;
-                            ++r;
-                        }
-                        const uint64_t m = __ballot(s);
-                        selm |= (uint32_t)s << u;
-                        below += lanes_below(m);
-                        total += (uint32_t)__popcll(m);
-                    }
-                    run_eq += eq_total;
-                }
-                // one store per selected entry of the lane (usually none or one)
-                uint32_t slot = run_sel + below;
-                while (selm) {
-                    const int u = __builtin_ctz(selm);
-                    selm &= selm - 1u;
-                    if (slot < M[j]) {          // the bound holds whenever the counts agree
-                        out_idx[slot] = pos_lds ? (int32_t)posl[ib + u] : src.position(row, begin + ib + u);
-                        if (out_sc) out_sc[slot] = key_score(u == 0 ? kv[0] : u == 1 ? kv[1] : u == 2 ? kv[2] : kv[3]);
-                    }
-                    ++slot;
-                }
-                run_sel += total;
+            const uint64_t m = __ballot(s);
+            const uint32_t slot = run_sel + lanes_below(m);
+            if (s && slot < M[j]) {             // the bound holds whenever the counts agree
+                out_idx[slot] = pos_lds ? (int32_t)posl[ci] : src.position(row, begin + (int64_t)ci);
+                if (out_sc) out_sc[slot] = key_score(k);
             }
-        }
+            run_sel += (uint32_t)__popcll(m);
+        };
+        for_keys(emit);
         if (split == S - 1) {
             for (uint32_t s = tinfo[j * 4 + 1] + tid; s < M[j]; s += kSelThreads) {
                 out_idx[s] = -1;
