@@ -581,6 +581,7 @@ struct PlanLayout {
     SelPlan full, pool;
     PoolSelPlan psel;               // Reindex select when the pool has at most kPoolSelMaxN entries
     bool use_psel = false;
+    bool fuse_reindex = false;      // the Reindex layers' attention runs inside the pool select
     size_t off_full = 0, off_pool = 0, off_attn = 0, off_idx = 0, off_poolbuf = 0, total = 0;
 };
 
@@ -594,7 +595,9 @@ int plan_layout(const csa2_plan* plan, int32_t B, int64_t N, PlanLayout* lay) {
         size_t pool_data = 0;
         if (lay->use_psel) {
             if (int e = plan_pool_select(B, plan->p.P, &lay->psel)) return e;
-            pool_data = lay->psel.data_bytes;
+            // the fused attention covers the E4M3-scaled cache without a sliding window
+            lay->fuse_reindex = plan->p.kv_format == CSA2_KV_FP4_E4M3 && plan->p.swa_window == 0;
+            pool_data = lay->fuse_reindex ? pool_select_fused_bytes(lay->psel) : lay->psel.data_bytes;
         } else {
             if (int e = plan_select(B, plan->p.P, 512, &lay->pool)) return e;
             pool_data = lay->pool.data_bytes;
@@ -698,7 +701,24 @@ int csa2_plan_run_decode(const csa2_plan* plan, const csa2_cache* cache, const c
                 ps.K = p.K;
                 ps.idx = idx_dst;
                 ps.idx_stride = p.K;
-                e = run_pool_select(lay.psel, ps, wsb, wsb + lay.off_pool, lay.psel.data_bytes, stream);
+                AttnFuse af{};
+                if (lay.fuse_reindex) {
+                    af.q = io[l].q;
+                    af.k_codes = gc->k_codes;
+                    af.k_scales = gc->k_scales;
+                    af.v_codes = gc->v_codes;
+                    af.v_scales = gc->v_scales;
+                    af.N = N;
+                    af.cs = gc->code_stride_bytes;
+                    af.ss = gc->scale_stride_bytes;
+                    af.H = p.H;
+                    af.rows_per_seq = 1;
+                    af.scale = p.softmax_scale;
+                    af.out = io[l].out;
+                    ps.attn = &af;
+                }
+                e = run_pool_select(lay.psel, ps, wsb, wsb + lay.off_pool,
+                                    lay.fuse_reindex ? pool_select_fused_bytes(lay.psel) : lay.psel.data_bytes, stream);
             } else {
                 a.pool = pool;
                 o[0] = SelOutput{idx_dst, nullptr, p.K, p.K};
@@ -706,6 +726,7 @@ int csa2_plan_run_decode(const csa2_plan* plan, const csa2_cache* cache, const c
             }
             if (e) return e;
             cur_idx = idx_dst;
+            if (mode == CSA2_REINDEX && lay.use_psel && lay.fuse_reindex) continue;   // attended in the select
         }
         AttnArgs at;
         at.q = io[l].q;

@@ -100,6 +100,18 @@ struct PoolSelPlan {
     int32_t n = 0, n4 = 0, S = 1, rows_per_launch = 0;
     size_t data_bytes = 0;          // published keys, rows_per_launch rows of n4 words
 };
+// An attention fused into a selection kernel, for an FP4 cache with E4M3
+// scales (128 channels, at most 16 heads, no sliding window).
+struct AttnFuse {
+    const uint16_t* q;                          // [rows][H][128] bf16 attention queries
+    const uint8_t *k_codes, *k_scales, *v_codes, *v_scales;   // sequence s starts at + s * N * stride
+    int64_t N, cs, ss;                          // positions per sequence, code and scale row strides
+    int32_t H, rows_per_seq;
+    float scale;                                // softmax scale
+    float* out;                                 // [rows][H][128] fp32
+    float* parts;                               // [launch rows][S][partial state] (set by the launcher)
+};
+
 struct PoolSelArgs {
     const void* q = nullptr;        // [rows][d_idx] indexer queries (q_dtype)
     const uint8_t* k = nullptr;     // [rows][N][d_idx] keys (k_dtype); row r reads sequence r
@@ -109,9 +121,12 @@ struct PoolSelArgs {
     int32_t* idx = nullptr;         // [rows][idx_stride] ascending positions, -1 padding
     int64_t idx_stride = 0;
     float* score = nullptr;         // optional selected scores
+    const AttnFuse* attn = nullptr; // attend to the selected positions in the same launch
 };
 constexpr int64_t kPoolSelMaxN = 16384;
 int plan_pool_select(int64_t rows, int64_t n, PoolSelPlan* out);
+// Data bytes of a pool select with the attention fused in (the key buffer, then the partial states).
+size_t pool_select_fused_bytes(const PoolSelPlan& p);
 int run_pool_select(const PoolSelPlan& p, const PoolSelArgs& a, void* ws_ctrl, void* ws_data, size_t data_bytes,
                     hipStream_t stream);
 

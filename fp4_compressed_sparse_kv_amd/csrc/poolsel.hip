@@ -22,8 +22,17 @@
 //      order; its slot is the number of selected entries before it, from one
 //      block scan of per-thread counts. Pool order is position order, so the
 //      output is ascending. Slots past the number selected hold -1.
+//   5. (with the attention fused in) attends to its own selected positions,
+//      which it keeps in LDS in output order, publishes its partial softmax
+//      state, and after a second row barrier writes the output of heads
+//      split, split + S, ... as the merge of the row's S states in slice
+//      order - so the layer's attention needs no launch, position read-back
+//      or merge of its own.
 // NaN and -inf scores map to key 0 and are never selected; -0 ranks as +0.
 // Ties at T go to the lowest pool entry, which is the lowest position.
+#include <type_traits>
+
+#include "attn_core.hpp"
 #include "dot.hpp"
 #include "internal.hpp"
 
@@ -92,14 +101,23 @@ __device__ __forceinline__ void ps_find(const uint32_t* h, uint32_t M_req, PsLds
     M = m;
 }
 
-template <int KT, int QT, int D, int NK>
+// LDS of the fused attention: its positions (this chunk's selected entries in
+// output order) and the waves' staging and merge areas.
+struct alignas(16) PsAttnLds {
+    AttnLds<kFuseWaves> a;
+    int32_t apos[kPsChunk];
+    uint32_t span[2];                           // this chunk's output slots [span[0], span[1])
+};
+
+template <int KT, int QT, int D, int NK, bool FA>
 __global__ void __launch_bounds__(kPsThreads) k_pool_select(const void* __restrict__ q, const uint8_t* __restrict__ k,
                                                             int64_t N, const int32_t* __restrict__ pool, PsDev g,
                                                             int32_t* __restrict__ idx_out, int64_t idx_stride,
-                                                            float* __restrict__ sc_out) {
+                                                            float* __restrict__ sc_out, AttnFuse af) {
     using KS = KeySlice<KT, D, QT>;
     constexpr int QB = (QT == kBF16) ? 2 : 4;
     __shared__ PsLds L;
+    __shared__ typename std::conditional<FA, PsAttnLds, char>::type FL;
     const int tid = threadIdx.x;
     const int S = g.S, n = g.n;
     const int lrow = blockIdx.x / S;
@@ -175,7 +193,7 @@ __global__ void __launch_bounds__(kPsThreads) k_pool_select(const void* __restri
         for (int j = 0; j < NK; ++j)
             if (tid * NK + j >= n) kv[j] = 0u;
     }
-    if (S > 1) {                                // the last workgroup past the barrier resets the row's words
+    if (S > 1 && !FA) {                         // the last workgroup past the barrier resets the row's words
         if (tid == 0 && add_rlx(exitc, 1u) == (uint32_t)S - 1) {
             st_rlx(exitc, 0u);
             st_rlx(bar, 0u);
@@ -236,6 +254,18 @@ __global__ void __launch_bounds__(kPsThreads) k_pool_select(const void* __restri
         uint32_t tot;
         const uint32_t before = ps_block_scan((c_gt << 16) | c_eq, L.wsum, tot);   // both < 2^15
         uint32_t bgt = before >> 16, beq = before & 0xFFFFu;
+        if constexpr (FA) {
+            // output slots of this chunk: the entries selected before its first entry and
+            // before the next chunk's (chunk starts are multiples of NK: a thread's first entry)
+            const uint32_t sel_before = bgt + (beq < need ? beq : need);
+            if (tid * NK == begin) FL.span[0] = sel_before;
+            if (split == S - 1) {
+                if (tid == 0) FL.span[1] = M;
+            } else if (tid * NK == begin + kPsChunk) {
+                FL.span[1] = sel_before;
+            }
+            __syncthreads();
+        }
         const int e0 = tid * NK;
         if (e0 < begin + cnt && e0 + NK > begin) {
 #pragma unroll
@@ -246,6 +276,7 @@ __global__ void __launch_bounds__(kPsThreads) k_pool_select(const void* __restri
                     const uint32_t slot = bgt + (beq < need ? beq : need);
                     orow[slot] = (int32_t)L.pos[e - begin];
                     if (srow) srow[slot] = key_score(kv[j]);
+                    if constexpr (FA) FL.apos[slot - FL.span[0]] = (int32_t)L.pos[e - begin];
                 }
                 bgt += kv[j] > T ? 1u : 0u;
                 beq += kv[j] == T ? 1u : 0u;
@@ -256,6 +287,20 @@ __global__ void __launch_bounds__(kPsThreads) k_pool_select(const void* __restri
         for (int s = (int)M + tid; s < g.K; s += kPsThreads) {
             orow[s] = -1;
             if (srow) srow[s] = __uint_as_float(0x7FC00000u);
+        }
+    }
+    if constexpr (FA) {
+        // ---- 5. this chunk's share of the row's attention, then the merge
+        __syncthreads();                        // the positions are in LDS
+        const int nsel = M > 0 ? (int)(FL.span[1] - FL.span[0]) : 0;
+        float* parts_row = af.parts + (size_t)lrow * S * kPartFloats;
+        fused_attn_partial(af, row, FL.apos, nsel, FL.a, parts_row + (size_t)split * kPartFloats);
+        if (S > 1) row_barrier(bar, (uint32_t)S, gen, status);
+        else __syncthreads();
+        fused_attn_merge<NK>(af, row, parts_row, S, split, S, FL.a.mg.f);   // S <= NK: n <= NK * kPsChunk
+        if (S > 1 && tid == 0 && add_rlx(exitc, 1u) == (uint32_t)S - 1) {   // every chunk is past both barriers
+            st_rlx(exitc, 0u);
+            st_rlx(bar, 0u);
         }
     }
 }
@@ -286,10 +331,12 @@ namespace {
 
 template <int KT, int QT, int D>
 int launch_ps_typed(const PoolSelPlan& p, const PoolSelArgs& a, void* ws_ctrl, void* ws_data, hipStream_t stream) {
-    auto fn = p.n <= 8 * kPsThreads ? k_pool_select<KT, QT, D, 8> : k_pool_select<KT, QT, D, 16>;
+    const bool fa = a.attn != nullptr;
+    auto fn = p.n <= 8 * kPsThreads ? (fa ? k_pool_select<KT, QT, D, 8, true> : k_pool_select<KT, QT, D, 8, false>)
+                                    : (fa ? k_pool_select<KT, QT, D, 16, true> : k_pool_select<KT, QT, D, 16, false>);
     // the chunks of a row wait for each other: check once that a workgroup fits on a CU
-    static bool fits[2] = {false, false};
-    const int which = p.n <= 8 * kPsThreads ? 0 : 1;
+    static bool fits[4] = {false, false, false, false};
+    const int which = (p.n <= 8 * kPsThreads ? 0 : 1) + (fa ? 2 : 0);
     if (!fits[which]) {
         int per_cu = 0;
         const hipError_t he = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kPsThreads, 0);
@@ -304,11 +351,16 @@ int launch_ps_typed(const PoolSelPlan& p, const PoolSelArgs& a, void* ws_ctrl, v
     g.K = a.K;
     g.ctrl = reinterpret_cast<uint32_t*>(ws_ctrl);
     g.keys = reinterpret_cast<uint32_t*>(ws_data);
+    AttnFuse af{};
+    if (fa) {
+        af = *a.attn;
+        af.parts = reinterpret_cast<float*>(static_cast<uint8_t*>(ws_data) + p.data_bytes);
+    }
     for (int64_t r0 = 0; r0 < p.rows; r0 += p.rows_per_launch) {
         const int64_t nr = (p.rows - r0) < p.rows_per_launch ? (p.rows - r0) : p.rows_per_launch;
         g.row0 = (int32_t)r0;
         hipLaunchKernelGGL(fn, dim3((unsigned)(nr * p.S)), dim3(kPsThreads), 0, stream, a.q, a.k, a.N, a.pool, g,
-                           a.idx, a.idx_stride, a.score);
+                           a.idx, a.idx_stride, a.score, af);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return hip_fail(e, "launch k_pool_select");
     }
@@ -331,10 +383,15 @@ int launch_ps_q(const PoolSelPlan& p, const PoolSelArgs& a, void* wc, void* wd, 
 
 }  // namespace
 
+size_t pool_select_fused_bytes(const PoolSelPlan& p) {
+    return p.data_bytes + (size_t)p.rows_per_launch * p.S * kPartFloats * 4;
+}
+
 int run_pool_select(const PoolSelPlan& p, const PoolSelArgs& a, void* ws_ctrl, void* ws_data, size_t data_bytes,
                     hipStream_t stream) {
     if (p.rows == 0) return OK;
-    if (data_bytes < p.data_bytes) return fail(WORKSPACE, "pool select workspace too small");
+    if (data_bytes < (a.attn ? pool_select_fused_bytes(p) : p.data_bytes))
+        return fail(WORKSPACE, "pool select workspace too small");
     if (a.K < 1) return fail(INVALID, "pool select: K must be >= 1");
     switch (a.k_dtype) {
         case kF32: return launch_ps_q<kF32>(p, a, ws_ctrl, ws_data, stream);
