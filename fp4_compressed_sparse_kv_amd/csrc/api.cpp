@@ -582,6 +582,7 @@ struct PlanLayout {
     PoolSelPlan psel;               // Reindex select when the pool has at most kPoolSelMaxN entries
     bool use_psel = false;
     bool fuse_reindex = false;      // the Reindex layers' attention runs inside the pool select
+    bool fuse_full = false;         // the Full layers' attention runs inside their select
     size_t off_full = 0, off_pool = 0, off_attn = 0, off_idx = 0, off_poolbuf = 0, total = 0;
 };
 
@@ -607,8 +608,15 @@ int plan_layout(const csa2_plan* plan, int32_t B, int64_t N, PlanLayout* lay) {
         lay->off_poolbuf = off;
         off += align_up((size_t)B * plan->p.P * 4);
     }
+    // the fused attention covers the E4M3-scaled cache without a sliding window, up to 4096 positions,
+    // in rows of at most 8 chunks (their states merge in one batch of loads; longer rows keep the
+    // attention kernel, which spreads a row over at most 8 workgroups)
+    lay->fuse_full = plan->p.kv_format == CSA2_KV_FP4_E4M3 && plan->p.swa_window == 0 && plan->p.K <= 4096 &&
+                     lay->full.S <= 8;
     lay->off_attn = off;
-    off += align_up(attn_data_bytes(B, plan->p.K, plan->p.swa_window));
+    size_t attn_bytes = attn_data_bytes(B, plan->p.K, plan->p.swa_window);
+    if (lay->fuse_full && select_fused_part_bytes(lay->full) > attn_bytes) attn_bytes = select_fused_part_bytes(lay->full);
+    off += align_up(attn_bytes);
     lay->off_idx = off;
     off += align_up((size_t)B * plan->p.K * 4);
     lay->total = off;
@@ -677,6 +685,19 @@ int csa2_plan_run_decode(const csa2_plan* plan, const csa2_cache* cache, const c
             int nt = 1;
             int e;
             SlotTimer timer(plan, 2 * l, stream);
+            AttnFuse fa{};                      // the layer's attention, when it runs inside the select
+            fa.q = io[l].q;
+            fa.k_codes = gc->k_codes;
+            fa.k_scales = gc->k_scales;
+            fa.v_codes = gc->v_codes;
+            fa.v_scales = gc->v_scales;
+            fa.N = N;
+            fa.cs = gc->code_stride_bytes;
+            fa.ss = gc->scale_stride_bytes;
+            fa.H = p.H;
+            fa.rows_per_seq = 1;
+            fa.scale = p.softmax_scale;
+            fa.out = io[l].out;
             if (mode == CSA2_FULL) {
                 pool = nullptr;                 // a Full layer opens a group: its own pool, if any
                 if (plan->group_pool[plan->group[l]]) {
@@ -687,6 +708,10 @@ int csa2_plan_run_decode(const csa2_plan* plan, const csa2_cache* cache, const c
                     pool = pool_dst;
                 } else {
                     o[0] = SelOutput{idx_dst, nullptr, p.K, p.K};
+                }
+                if (lay.fuse_full) {
+                    fa.parts = reinterpret_cast<float*>(wsb + lay.off_attn);
+                    a.attn = &fa;
                 }
                 e = run_select(lay.full, SRC_SCAN, a, none, o, nt, wsb, wsb + lay.off_full, stream);
             } else if (lay.use_psel) {
@@ -701,22 +726,7 @@ int csa2_plan_run_decode(const csa2_plan* plan, const csa2_cache* cache, const c
                 ps.K = p.K;
                 ps.idx = idx_dst;
                 ps.idx_stride = p.K;
-                AttnFuse af{};
-                if (lay.fuse_reindex) {
-                    af.q = io[l].q;
-                    af.k_codes = gc->k_codes;
-                    af.k_scales = gc->k_scales;
-                    af.v_codes = gc->v_codes;
-                    af.v_scales = gc->v_scales;
-                    af.N = N;
-                    af.cs = gc->code_stride_bytes;
-                    af.ss = gc->scale_stride_bytes;
-                    af.H = p.H;
-                    af.rows_per_seq = 1;
-                    af.scale = p.softmax_scale;
-                    af.out = io[l].out;
-                    ps.attn = &af;
-                }
+                if (lay.fuse_reindex) ps.attn = &fa;
                 e = run_pool_select(lay.psel, ps, wsb, wsb + lay.off_pool,
                                     lay.fuse_reindex ? pool_select_fused_bytes(lay.psel) : lay.psel.data_bytes, stream);
             } else {
@@ -726,7 +736,8 @@ int csa2_plan_run_decode(const csa2_plan* plan, const csa2_cache* cache, const c
             }
             if (e) return e;
             cur_idx = idx_dst;
-            if (mode == CSA2_REINDEX && lay.use_psel && lay.fuse_reindex) continue;   // attended in the select
+            if ((mode == CSA2_REINDEX && lay.use_psel && lay.fuse_reindex) || (mode == CSA2_FULL && lay.fuse_full))
+                continue;                       // attended in the select
         }
         AttnArgs at;
         at.q = io[l].q;

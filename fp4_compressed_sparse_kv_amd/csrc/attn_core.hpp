@@ -22,6 +22,7 @@ constexpr int kBlk = 32;
 constexpr int kMaxHeads = 16;
 constexpr int kD = 128;
 constexpr int kPartFloats = kMaxHeads * kD + 2 * kMaxHeads;   // per (row, slice): acc [16][128], (m, l) [16][2]
+static_assert(kPartFloats == kAttnPartFloats, "partial state size");
 constexpr int kVRowBytes = 80;                  // staged V row: 64 code bytes + pad (conflict-free dword reads)
 constexpr int kMergeStride = kD + 4;
 constexpr float kLog2e = 1.4426950408889634f;
@@ -476,11 +477,12 @@ constexpr int kFuseWaves = 8;                   // waves of a workgroup that att
 // 0..kFuseWaves-1 take blocks of 32 (wave w: blocks w, w + kFuseWaves, ...),
 // their states are merged in wave order, and the result - per head the
 // running maximum and sum (scaled log2 units) and the unnormalized output -
-// is written to `part` with device-coherent stores. All threads of the
+// is written to `part` with device-coherent stores, or (direct: the row has
+// no other workgroup) normalized straight to the output. All threads of the
 // workgroup (at least kFuseWaves waves) call it; it ends with the stores
-// drained. fh[h] receives head h's scale-back factor 2^qe.
+// drained. lds.mg.f[h] keeps head h's scale-back factor 2^qe.
 __device__ __forceinline__ void fused_attn_partial(const AttnFuse& af, int64_t row, const int32_t* pos, int n,
-                                                   AttnLds<kFuseWaves>& lds, float* part) {
+                                                   AttnLds<kFuseWaves>& lds, float* part, bool direct = false) {
     constexpr int W = kFuseWaves;
     constexpr int kCh = kMaxHeads * kD / (W * kWave);   // output channels per merging thread
     constexpr int kV4 = kCh / 4;
@@ -557,15 +559,25 @@ __device__ __forceinline__ void fused_attn_partial(const AttnFuse& af, int64_t r
                 for (int v = 0; v < kV4; ++v) o[v] += wt * *reinterpret_cast<const f32x4*>(&lds.mg.acc[w][h][c0 + 4 * v]);
             }
         }
-        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(part, (short)0, kPartFloats * 4, kRsrcWord3);
+        if (direct) {
+            if (h < af.H) {
+                const float inv = L > 0.f ? 1.f / L : 0.f;
 #pragma unroll
-        for (int v = 0; v < kV4; ++v)
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o[v]), rs, (h * kD + c0 + 4 * v) * 4, 0,
-                                                   kCoherent);
-        if (c0 == 0) {
-            const f32x2 ml = {M, L};
-            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, ml), rs, (kMaxHeads * kD + 2 * h) * 4, 0,
-                                                 kCoherent);
+                for (int v = 0; v < kV4; ++v)
+                    *reinterpret_cast<f32x4*>(af.out + (row * af.H + h) * (int64_t)kD + c0 + 4 * v) = o[v] * inv;
+            }
+        } else {
+            const __amdgpu_buffer_rsrc_t rs =
+                __builtin_amdgcn_make_buffer_rsrc(part, (short)0, kPartFloats * 4, kRsrcWord3);
+#pragma unroll
+            for (int v = 0; v < kV4; ++v)
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o[v]), rs, (h * kD + c0 + 4 * v) * 4,
+                                                       0, kCoherent);
+            if (c0 == 0) {
+                const f32x2 ml = {M, L};
+                __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, ml), rs, (kMaxHeads * kD + 2 * h) * 4,
+                                                     0, kCoherent);
+            }
         }
     }
     wave_drain();
@@ -573,40 +585,50 @@ __device__ __forceinline__ void fused_attn_partial(const AttnFuse& af, int64_t r
 
 // After every workgroup of the row has published its partial state: the
 // output rows of heads h = first, first + step, ... (< H), each the merge of
-// the S <= MAXS states in slice order, normalized. fh: the heads' scale-back
-// factors (those of this workgroup's own query conversion; every workgroup
-// converts the same query the same way). 32 threads per head, 4 channels each.
+// the row's S states in slice order, normalized - in batches of MAXS slices
+// whose loads are in flight together, each batch folded into the running
+// state with the usual rescale (a fixed order: the result does not depend on
+// scheduling). fh: the heads' scale-back factors (those of this workgroup's
+// own query conversion; every workgroup converts the same query the same
+// way). 32 threads per head, 4 channels each.
 template <int MAXS>
 __device__ __forceinline__ void fused_attn_merge(const AttnFuse& af, int64_t row, const float* parts_row, int S,
                                                  int first, int step, const float* fh) {
-    constexpr int kMaxS = MAXS;
     const int tid = threadIdx.x;
     const int h = first + (tid >> 5) * step;
     const int c0 = (tid & 31) * 4;
     if (h >= af.H || (tid >> 5) * step >= kMaxHeads) return;
     const __amdgpu_buffer_rsrc_t rs =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(parts_row), (short)0, S * kPartFloats * 4, kRsrcWord3);
-    u32x4 pa[kMaxS];
-    u32x2 pml[kMaxS];
-#pragma unroll
-    for (int s = 0; s < kMaxS; ++s) {           // slices past S read past the resource: zeros, no access
-        pa[s] = __builtin_amdgcn_raw_buffer_load_b128(rs, (s * kPartFloats + h * kD + c0) * 4, 0, kCoherent);
-        pml[s] = __builtin_amdgcn_raw_buffer_load_b64(rs, (s * kPartFloats + kMaxHeads * kD + 2 * h) * 4, 0, kCoherent);
-    }
-    float MM = -INFINITY;
-#pragma unroll
-    for (int s = 0; s < kMaxS; ++s) MM = fmaxf(MM, s < S ? __uint_as_float(pml[s].x) : -INFINITY);
-    float LL = 0.f;
+    const float f = fh[h];
+    float MM = -INFINITY, LL = 0.f;
     f32x4 oo = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (MM != -INFINITY) {
-        const float f = fh[h];
+    for (int s0 = 0; s0 < S; s0 += MAXS) {
+        u32x4 pa[MAXS];
+        u32x2 pml[MAXS];
 #pragma unroll
-        for (int s = 0; s < kMaxS; ++s) {
-            const float ms = __uint_as_float(pml[s].x);
-            const float wt = (s >= S || ms == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((ms - MM) * f);
-            LL += wt * __uint_as_float(pml[s].y);
-            oo += wt * __builtin_bit_cast(f32x4, pa[s]);
+        for (int i = 0; i < MAXS; ++i) {        // slices past S read past the resource: zeros, no access
+            const int s = s0 + i;
+            pa[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, (s * kPartFloats + h * kD + c0) * 4, 0, kCoherent);
+            pml[i] = __builtin_amdgcn_raw_buffer_load_b64(rs, (s * kPartFloats + kMaxHeads * kD + 2 * h) * 4, 0,
+                                                          kCoherent);
         }
+        float bm = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < MAXS; ++i) bm = fmaxf(bm, s0 + i < S ? __uint_as_float(pml[i].x) : -INFINITY);
+        const float Mn = fmaxf(MM, bm);
+        if (Mn == -INFINITY) continue;          // nothing attended so far
+        const float a = MM == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((MM - Mn) * f);
+        LL *= a;
+        oo *= a;
+#pragma unroll
+        for (int i = 0; i < MAXS; ++i) {
+            const float ms = __uint_as_float(pml[i].x);
+            const float wt = (s0 + i >= S || ms == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((ms - Mn) * f);
+            LL += wt * __uint_as_float(pml[i].y);
+            oo += wt * __builtin_bit_cast(f32x4, pa[i]);
+        }
+        MM = Mn;
     }
     const float inv = LL > 0.f ? 1.f / LL : 0.f;
     *reinterpret_cast<f32x4*>(af.out + (row * af.H + h) * (int64_t)kD + c0) = oo * inv;

@@ -66,6 +66,19 @@ struct SelOutput {
     int32_t M = 0;
 };
 
+// An attention fused into a selection kernel, for an FP4 cache with E4M3
+// scales (128 channels, at most 16 heads, no sliding window).
+struct AttnFuse {
+    const uint16_t* q;                          // [rows][H][128] bf16 attention queries
+    const uint8_t *k_codes, *k_scales, *v_codes, *v_scales;   // sequence s starts at + s * N * stride
+    int64_t N, cs, ss;                          // positions per sequence, code and scale row strides
+    int32_t H, rows_per_seq;
+    float scale;                                // softmax scale
+    float* out;                                 // [rows][H][128] fp32
+    float* parts;                               // [launch rows][S][kAttnPartFloats] partial states
+};
+constexpr int kAttnPartFloats = 16 * 128 + 2 * 16;   // one partial state: acc [16][128], (max, sum) [16][2]
+
 struct ScanArgs {                   // indexer keys scored inside the select kernel
     const void* q = nullptr;        // [rows][d_idx] indexer queries (q_dtype)
     const uint8_t* k = nullptr;     // [seqs][N][d_idx] keys (k_dtype)
@@ -78,7 +91,10 @@ struct ScanArgs {                   // indexer keys scored inside the select ker
     int32_t nranges = 0, cap = 0;
     const int32_t* rowmap = nullptr;// scan sources: launch row -> query row (-1: none), or null
     int32_t q_dtype = 0, k_dtype = 0, d_idx = 64;
+    const AttnFuse* attn = nullptr; // SRC_SCAN: attend to the last target's positions in the same launch
 };
+// Workspace bytes of the partial states of a select launch with the attention fused in.
+size_t select_fused_part_bytes(const SelPlan& p);
 
 struct ScoresArgs {                 // precomputed scores
     const float* scores = nullptr;
@@ -100,18 +116,6 @@ struct PoolSelPlan {
     int32_t n = 0, n4 = 0, S = 1, rows_per_launch = 0;
     size_t data_bytes = 0;          // published keys, rows_per_launch rows of n4 words
 };
-// An attention fused into a selection kernel, for an FP4 cache with E4M3
-// scales (128 channels, at most 16 heads, no sliding window).
-struct AttnFuse {
-    const uint16_t* q;                          // [rows][H][128] bf16 attention queries
-    const uint8_t *k_codes, *k_scales, *v_codes, *v_scales;   // sequence s starts at + s * N * stride
-    int64_t N, cs, ss;                          // positions per sequence, code and scale row strides
-    int32_t H, rows_per_seq;
-    float scale;                                // softmax scale
-    float* out;                                 // [rows][H][128] fp32
-    float* parts;                               // [launch rows][S][partial state] (set by the launcher)
-};
-
 struct PoolSelArgs {
     const void* q = nullptr;        // [rows][d_idx] indexer queries (q_dtype)
     const uint8_t* k = nullptr;     // [rows][N][d_idx] keys (k_dtype); row r reads sequence r

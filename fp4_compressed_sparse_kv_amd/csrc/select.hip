@@ -39,6 +39,14 @@
 // two targets (pool size P and K) are selected from the same keys in one
 // launch. The last workgroup of a row to leave resets the row's counters and
 // histograms, so the workspace is ready for the next launch without a memset.
+//
+// A Full layer's attention can run in the same launch (scan source, FA): each
+// chunk also writes its positions of the last target to LDS in output order,
+// attends to them with the attention's per-block step once the keys' LDS
+// area is free, publishes its partial softmax state, and after one more row
+// barrier writes heads split, split + S, ... as the merge of the row's states
+// in slice order (a row of one chunk writes its output directly).
+#include "attn_core.hpp"
 #include "dot.hpp"
 #include "internal.hpp"
 
@@ -56,6 +64,10 @@ constexpr int kLdsFixedWords = kB1 + 2 * kB2 + 4 * kMaxS + kScratchWords;
 constexpr int kMaxChunk = 32768;
 constexpr int kPadTo = 256;                          // keys per wave step of the count/compaction passes
 constexpr int kMaxSteps = kMaxChunk / kSelWaves / kPadTo;   // steps per wave (8)
+// LDS words the fused attention needs at the start of the keys' area, and the
+// most positions its list (the histogram area lh2) holds.
+constexpr int kFuseLdsWords = (int)((sizeof(AttnLds<kFuseWaves>) + 255) / 256 * 64);
+constexpr int kFuseMaxK = 2 * kB2;
 
 struct SelDev {
     int64_t n;
@@ -559,8 +571,8 @@ __device__ __forceinline__ T pick(T a0, T a1, int j) {
     return (NT > 1 && j) ? a1 : a0;
 }
 
-template <class Src, int NT>
-__global__ void __launch_bounds__(kSelThreads) k_select(Src src, SelDev g, SelTgt t0, SelTgt t1) {
+template <class Src, int NT, bool FA>
+__global__ void __launch_bounds__(kSelThreads) k_select(Src src, SelDev g, SelTgt t0, SelTgt t1, AttnFuse af) {
     extern __shared__ uint32_t lds[];
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
     const int S = g.S;
@@ -576,7 +588,8 @@ __global__ void __launch_bounds__(kSelThreads) k_select(Src src, SelDev g, SelTg
     uint32_t* keys = lds;                       // [cpad] score keys, 0 past cnt
     const bool pos_lds = Src::kPosLds && g.pos_lds;
     uint32_t* posl = pos_lds ? lds + cpad : nullptr;     // [cpad] positions of the keys (sources that keep them)
-    uint32_t* lh1 = lds + cpad * (pos_lds ? 2 : 1);     // [kB1] this chunk's top-digit histogram
+    // (the fused attention reuses the keys' area, at least kFuseLdsWords)
+    uint32_t* lh1 = lds + (pos_lds ? 2 * cpad : (FA && cpad < kFuseLdsWords ? kFuseLdsWords : cpad));   // [kB1] this chunk's top-digit histogram
     uint32_t* lh2 = lh1 + kB1;                  // [2*kB2] row histogram, then later histograms
     uint32_t* cnts = lh2 + 2 * kB2;             // [S][2 targets][> T, == T]
     uint32_t* sm = cnts + 4 * kMaxS;            // scratch
@@ -1174,6 +1187,10 @@ __global__ void __launch_bounds__(kSelThreads) k_select(Src src, SelDev g, SelTg
         uint32_t run_eq = wbase[(j * kSelWaves + wave) * 2 + 1];
         int32_t* out_idx = t.idx + row * t.stride;
         float* out_sc = t.score ? t.score + row * t.stride : nullptr;
+        // fused attention: this chunk's positions of the last target, in output order, from its first slot
+        const bool fa_j = FA && j == NT - 1;
+        int32_t* apos = reinterpret_cast<int32_t*>(lh2);
+        const uint32_t cbase = wbase[(j * kSelWaves) * 2 + 0];
         // 64 consecutive entries in index order, one per lane (v: the entry exists)
         auto emit = [&](uint32_t k, uint32_t ci, bool v) {
             bool s = v && k > Tj;
@@ -1188,17 +1205,35 @@ __global__ void __launch_bounds__(kSelThreads) k_select(Src src, SelDev g, SelTg
             const uint64_t m = __ballot(s);
             const uint32_t slot = run_sel + lanes_below(m);
             if (s && slot < M[j]) {             // the bound holds whenever the counts agree
-                out_idx[slot] = pos_lds ? (int32_t)posl[ci] : src.position(row, begin + (int64_t)ci);
+                const int32_t pos = pos_lds ? (int32_t)posl[ci] : src.position(row, begin + (int64_t)ci);
+                out_idx[slot] = pos;
                 if (out_sc) out_sc[slot] = key_score(k);
+                if (fa_j) apos[slot - cbase] = pos;
             }
             run_sel += (uint32_t)__popcll(m);
         };
         for_keys(emit);
+        // the last wave ends at the chunk's last slot: the number of positions it selected
+        if (fa_j && wave == kSelWaves - 1 && lane == 0) sm[216] = min(run_sel, M[j]) - cbase;
         if (split == S - 1) {
             for (uint32_t s = tinfo[j * 4 + 1] + tid; s < M[j]; s += kSelThreads) {
                 out_idx[s] = -1;
                 if (out_sc) out_sc[s] = __uint_as_float(0x7FC00000u);
             }
+        }
+    }
+
+    // ---- fused attention over this chunk's positions, then the merge
+    if constexpr (FA) {
+        __syncthreads();                        // positions and count written; the keys' area is free
+        const int nsel = (int)sm[216];
+        AttnLds<kFuseWaves>& al = *reinterpret_cast<AttnLds<kFuseWaves>*>(lds);
+        float* parts_row = af.parts + (size_t)lrow * S * kPartFloats;
+        fused_attn_partial(af, row, reinterpret_cast<const int32_t*>(lh2), nsel, al,
+                           parts_row + (size_t)split * kPartFloats, !multi);
+        if (multi) {
+            row_barrier(ctrl, S, gen, status);
+            fused_attn_merge<8>(af, row, parts_row, S, split, S, al.mg.f);
         }
     }
 
@@ -1222,6 +1257,10 @@ __global__ void __launch_bounds__(kSelThreads) k_select(Src src, SelDev g, SelTg
 }
 
 // ------------------------------------------------------------------- host
+
+size_t select_fused_part_bytes(const SelPlan& p) {
+    return p.S > 1 ? (size_t)p.rows_per_launch * p.S * kPartFloats * 4 : 0;
+}
 
 int plan_select(int64_t rows, int64_t n, int32_t min_chunk, SelPlan* out) {
     DeviceInfo di;
@@ -1265,23 +1304,36 @@ int plan_select(int64_t rows, int64_t n, int32_t min_chunk, SelPlan* out) {
 
 namespace {
 
-template <class Src>
+template <class Src, bool CAN_FA = false>
 int launch_rows(const SelPlan& p, const Src& src, const SelOutput* out, int nt, void* ws_ctrl, void* ws_data,
-                hipStream_t stream, const int32_t* rowmap = nullptr) {
-    auto fn = nt == 2 ? reinterpret_cast<const void*>(&k_select<Src, 2>) : reinterpret_cast<const void*>(&k_select<Src, 1>);
-    static bool attr_set[2] = {false, false};
-    if (!attr_set[nt - 1]) {
+                hipStream_t stream, const int32_t* rowmap = nullptr, const AttnFuse* attn = nullptr) {
+    const bool fa = CAN_FA && attn != nullptr;
+    const void* fn;
+    if constexpr (CAN_FA) {
+        fn = fa ? (nt == 2 ? reinterpret_cast<const void*>(&k_select<Src, 2, true>)
+                           : reinterpret_cast<const void*>(&k_select<Src, 1, true>))
+                : (nt == 2 ? reinterpret_cast<const void*>(&k_select<Src, 2, false>)
+                           : reinterpret_cast<const void*>(&k_select<Src, 1, false>));
+    } else {
+        fn = nt == 2 ? reinterpret_cast<const void*>(&k_select<Src, 2, false>)
+                     : reinterpret_cast<const void*>(&k_select<Src, 1, false>);
+    }
+    const int ki = (nt - 1) + (fa ? 2 : 0);
+    static bool attr_set[4] = {false, false, false, false};
+    if (!attr_set[ki]) {
         DeviceInfo di;
         if (int e = device_info(&di)) return e;
         hipError_t he = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)di.max_lds);
         if (he != hipSuccess) return hip_fail(he, "hipFuncSetAttribute(select)");
-        attr_set[nt - 1] = true;
+        attr_set[ki] = true;
     }
+    if (fa && out[nt - 1].M > kFuseMaxK) return fail(INVALID, "select: fused attention takes at most 4096 positions");
     // Sources whose positions are indirect keep them in LDS next to the keys when both fit.
     DeviceInfo dinfo;
     if (int e = device_info(&dinfo)) return e;
     const bool pos_lds = Src::kPosLds && (size_t)(2 * p.chunk_pad + kLdsFixedWords) * 4 <= dinfo.max_lds;
-    const size_t lds_bytes = (size_t)(p.chunk_pad * (pos_lds ? 2 : 1) + kLdsFixedWords) * 4;
+    const int key_words = fa && p.chunk_pad < kFuseLdsWords ? kFuseLdsWords : p.chunk_pad;
+    const size_t lds_bytes = (size_t)(pos_lds ? 2 * p.chunk_pad : key_words) * 4 + (size_t)kLdsFixedWords * 4;
     SelTgt t[2];
     for (int j = 0; j < 2; ++j) {
         const SelOutput& o = out[j < nt ? j : 0];
@@ -1305,19 +1357,21 @@ int launch_rows(const SelPlan& p, const Src& src, const SelOutput* out, int nt, 
     // Kernels on one stream run one after another, so the CUs are free when
     // the launch starts; a wait that still cannot finish gives up after a
     // bounded number of polls and flags the workspace status word.
-    static size_t checked_lds[2] = {0, 0};
-    if (checked_lds[nt - 1] != lds_bytes) {
+    static size_t checked_lds[4] = {0, 0, 0, 0};
+    if (checked_lds[ki] != lds_bytes) {
         int per_cu = 0;
         hipError_t he = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kSelThreads, lds_bytes);
         if (he != hipSuccess) return hip_fail(he, "hipOccupancyMaxActiveBlocksPerMultiprocessor(select)");
         if (per_cu < 1) return fail(INVALID, "select: kernel does not fit on a CU with this LDS size");
-        checked_lds[nt - 1] = lds_bytes;
+        checked_lds[ki] = lds_bytes;
     }
+    AttnFuse af{};
+    if (fa) af = *attn;
     Src s = src;
     for (int64_t r0 = 0; r0 < p.rows; r0 += p.rows_per_launch) {
         const int64_t nr = (p.rows - r0) < p.rows_per_launch ? (p.rows - r0) : p.rows_per_launch;
         g.row0 = (int32_t)r0;
-        void* args[] = {&s, &g, &t[0], &t[1]};
+        void* args[] = {&s, &g, &t[0], &t[1], &af};
         hipError_t he = hipLaunchKernel(fn, dim3((unsigned)(nr * p.S)), dim3(kSelThreads), args,
                                         (unsigned)lds_bytes, stream);
         if (he != hipSuccess) return hip_fail(he, "hipLaunchKernel(select)");
@@ -1330,7 +1384,7 @@ int run_scan_typed(const SelPlan& p, int source, const ScanArgs& a, const SelOut
                    void* wd, hipStream_t stream) {
     if (source == SRC_SCAN) {
         SrcScan<KT, QT, D> s{a.q, a.k, a.N, a.rows_per_seq, a.q_pos};
-        return launch_rows(p, s, out, nt, wc, wd, stream, a.rowmap);
+        return launch_rows<SrcScan<KT, QT, D>, true>(p, s, out, nt, wc, wd, stream, a.rowmap, a.attn);
     }
     if (source == SRC_CAND) {
         if constexpr (D == 64 && KT != kF32 && QT == kBF16) {      // the matrix-core prefill path's inputs
