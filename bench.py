@@ -36,7 +36,7 @@ METRIC = "decode queries/s per CSA2 layer stack + achieved HBM GB/s (% of peak)"
 # HBM traffic per launch from committed rocprofv3 PMC passes (profiles/traffic_<kernel>_<workload>.json),
 # each tied to a hash of the sources its kernel is built from and ignored once they change.
 TRAFFIC_KERNELS = {
-    "full_select": ["select.hip", "dot.hpp", "device.hpp"],
+    "full_select": ["select.hip", "dot.hpp", "device.hpp", "attn_core.hpp"],
     "quant": ["quant.hip", "fp4q.hpp", "device.hpp"],
     "quant_mx": ["quant.hip", "fp4q.hpp", "device.hpp"],
     "kv_project": ["project.hip", "fp4q.hpp", "device.hpp"],
@@ -721,6 +721,13 @@ def main():
         copy_calibration(dev)
 
     step_bytes, sel_bytes = alg_bytes(cfg, args.kv, args.swa)
+    # the Full layer's attention runs inside its select when its own slot stays empty: that launch
+    # then also reads the query, the selected KV rows and writes the output (its positions stay on chip)
+    full_fused = len(slot_ms) > 1 and slot_ms[1] == 0.0
+    if full_fused:
+        H, d, K = cfg["H"], cfg["d"], cfg["K"]
+        g = 32 if args.kv == "mxfp4" else 16
+        sel_bytes += cfg["B"] * (2 * H * d + K * 2 * (d // 2 + d // g) + 4 * H * d)
     qps = cfg["B"] / (ms * 1e-3)
     sel_ms = slot_ms[0]
     achieved = sel_bytes / (sel_ms * 1e-3) / 1e9
@@ -756,7 +763,8 @@ def main():
         "achievable_copy_gbs": round(copy_gbs, 1),
         "kernel_ms": {"full_select": round(sel_ms, 5),
                       **{f"slot{i}": round(v, 5) for i, v in enumerate(slot_ms) if i > 0 and v > 0}},
-        "roofline": {"bound": "hbm", "kernel": "k_select<SrcScan> (Full layer: scan + pool/top-K select)",
+        "roofline": {"bound": "hbm", "kernel": "k_select<SrcScan> (Full layer: scan + pool/top-K select" +
+                               (" + attention)" if full_fused else ")"),
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "alg_bytes_per_launch": sel_bytes,
                      "traffic": traffic},
