@@ -41,8 +41,9 @@ def _plan(cfg, modes):
 
 
 @pytest.mark.timeout(1500)
-@pytest.mark.parametrize("workload,seqs", [("full_b64_n131072", (0, 63)), ("stack_b32_n262144", (0, 31)),
-                                           ("stack_b4_n1m", (2,))])
+@pytest.mark.parametrize("workload,seqs", [("full_b64_n131072", (0, 21, 42, 63)),
+                                           ("stack_b32_n262144", (0, 9, 18, 31)),
+                                           ("stack_b4_n1m", (0, 2))])
 def test_decode_step_full_size_sampled(workload, seqs):
     cfg = dict(synth.WORKLOADS[workload])
     modes = list(cfg["modes"])
@@ -94,7 +95,7 @@ def test_prefill_full_size_sampled():
     assert plan.prefill_status(cache, Q) == 0
     idx, out = host(idx), host(out)
     stats = {"exact": 0, "excused": 0}
-    for b, queries in ((0, (0, 2049)), (3, (1, 4095))):
+    for b, queries in ((0, (0, 1000, 2049, 4095)), (1, (7, 3333)), (2, (512, 4094)), (3, (1, 2222, 4095))):
         oc = _oracle_sequence(cfg, b)
         for i in queries:
             s = OS.index_scores(qi[b, i], cfg["q_idx_dtype"], oc["k_idx"], cfg["k_idx_dtype"], q_pos=int(q_pos[b, i]))
