@@ -117,32 +117,56 @@ k_dequant(const uint8_t* __restrict__ codes, int64_t cs, const uint8_t* __restri
 // for a zero block. x / X = x * 2^(127 - byte) is exact (a power of two; a
 // product below fp32's range is far below E2M1's 0.25 rounding threshold and
 // keeps its sign), so the hardware FP4 convert at unit scale rounds it to
-// nearest even with saturation, as the E4M3-scaled path does. One lane owns
-// one 32-channel block: four 16-byte loads, one 16-byte store of codes and
-// one scale byte. Inputs must be finite.
+// nearest even with saturation, as the E4M3-scaled path does. Four lanes (a
+// quad) own one 32-channel block, 8 channels each: a wave's 16-byte loads
+// cover one contiguous KiB, the block maximum comes from two quad exchanges,
+// and each lane writes the 4 code bytes of its 8 channels (lane 0 of the
+// quad also the scale byte); four units in flight per lane. Inputs must be
+// finite.
 __global__ void __launch_bounds__(kQuantThreads)
-k_quant_mx(const uint16_t* __restrict__ x, int64_t rows, int32_t bpr, int32_t bshift, int64_t x_stride,
+k_quant_mx(const uint16_t* __restrict__ x, int64_t rows, int32_t upr, int32_t ushift, int64_t x_stride,
            uint8_t* __restrict__ codes, int64_t cs, uint8_t* __restrict__ scales, int64_t ss) {
-    const int64_t total = rows * bpr;
+    const int64_t total = rows * upr;           // 8-channel units; a quad's four units form one block
     const int64_t stride = (int64_t)gridDim.x * kQuantThreads;
-    for (int64_t bid = (int64_t)blockIdx.x * kQuantThreads + threadIdx.x; bid < total; bid += stride) {
-        int64_t r;
-        int32_t b;
-        row_group(bid, bpr, bshift, r, b);
-        const uint4* src = reinterpret_cast<const uint4*>(x + r * x_stride + (int64_t)b * 32);
-        uint32_t w[16];
+    // units per row are a multiple of 4, so a quad's units are all valid or all
+    // past the end: the quads stay whole for the exchanges
+    for (int64_t uid = (int64_t)blockIdx.x * kQuantThreads + threadIdx.x; uid < total; uid += kDqInFlight * stride) {
+        int64_t r[kDqInFlight];
+        int32_t u[kDqInFlight];
+        bool ok[kDqInFlight];
+        uint4 v[kDqInFlight];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const uint4 v = ld_stream16(src + k);
-            w[4 * k + 0] = v.x;
-            w[4 * k + 1] = v.y;
-            w[4 * k + 2] = v.z;
-            w[4 * k + 3] = v.w;
+        for (int k = 0; k < kDqInFlight; ++k) {
+            const int64_t id = uid + k * stride;
+            ok[k] = id < total;
+            row_group(ok[k] ? id : 0, upr, ushift, r[k], u[k]);
+            v[k] = ld_stream16(x + r[k] * x_stride + (int64_t)u[k] * 8);
         }
-        uint32_t c[4];
-        const uint32_t sc = quant_block_mx(w, c);
-        *reinterpret_cast<uint4*>(codes + r * cs + (int64_t)b * 16) = make_uint4(c[0], c[1], c[2], c[3]);
-        scales[r * ss + b] = (uint8_t)sc;
+#pragma unroll
+        for (int k = 0; k < kDqInFlight; ++k) {
+            const uint32_t w[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+            uint32_t am = 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) am = max(am, max(w[i] & 0x7FFFu, (w[i] >> 16) & 0x7FFFu));
+            am = max(am, (uint32_t)__builtin_amdgcn_mov_dpp((int)am, 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
+            am = max(am, (uint32_t)__builtin_amdgcn_mov_dpp((int)am, 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
+            const int32_t e = (int32_t)(am >> 7) - 2;      // bf16 exponent field of the block max - 2
+            const uint32_t sc = (uint32_t)(e > 0 ? e : 0);
+            const float inv = __uint_as_float((254u - sc) << 23);   // 2^(127 - byte), exact
+            uint32_t c = 0u;
+            c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, bf16_bits_to_f32(w[0] & 0xFFFFu) * inv,
+                                                         __uint_as_float(w[0] & 0xFFFF0000u) * inv, 1.0f, 0);
+            c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, bf16_bits_to_f32(w[1] & 0xFFFFu) * inv,
+                                                         __uint_as_float(w[1] & 0xFFFF0000u) * inv, 1.0f, 1);
+            c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, bf16_bits_to_f32(w[2] & 0xFFFFu) * inv,
+                                                         __uint_as_float(w[2] & 0xFFFF0000u) * inv, 1.0f, 2);
+            c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, bf16_bits_to_f32(w[3] & 0xFFFFu) * inv,
+                                                         __uint_as_float(w[3] & 0xFFFF0000u) * inv, 1.0f, 3);
+            if (ok[k]) {
+                *reinterpret_cast<uint32_t*>(codes + r[k] * cs + (int64_t)u[k] * 4) = c;
+                if ((u[k] & 3) == 0) scales[r[k] * ss + (u[k] >> 2)] = (uint8_t)sc;
+            }
+        }
     }
 }
 
@@ -212,9 +236,9 @@ int launch_quant(const uint16_t* x, int64_t rows, int32_t C, int64_t x_stride, u
 int launch_quant_mx(const uint16_t* x, int64_t rows, int32_t C, int64_t x_stride, uint8_t* codes, int64_t cs,
                     uint8_t* scales, int64_t ss, hipStream_t stream) {
     if (rows == 0) return OK;
-    const int32_t bpr = C / 32;
-    hipLaunchKernelGGL(k_quant_mx, dim3(grid_for(rows * bpr, kQuantThreads)), dim3(kQuantThreads), 0, stream, x, rows,
-                       bpr, pow2_shift(bpr), x_stride, codes, cs, scales, ss);
+    const int32_t upr = C / 8;
+    hipLaunchKernelGGL(k_quant_mx, dim3(grid_for(rows * upr, kQuantThreads)), dim3(kQuantThreads), 0, stream, x, rows,
+                       upr, pow2_shift(upr), x_stride, codes, cs, scales, ss);
     const hipError_t e = hipGetLastError();
     return e == hipSuccess ? OK : hip_fail(e, "launch k_quant_mx");
 }
