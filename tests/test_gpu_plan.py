@@ -188,6 +188,35 @@ def test_reindex_over_whole_context_equals_full():
             assert max_rel_err_rows(host(got), ref) <= ATTN_TOL, b
 
 
+def _oracle_seq(cfg, b):
+    kb, vb = synth.kv_bf16(cfg, b)
+    kc, ks = OQ.quant_fp4(kb)
+    vc, vs = OQ.quant_fp4(vb)
+    return dict(k_codes=kc, k_scales=ks, v_codes=vc, v_scales=vs, k_idx=synth.k_idx(cfg, b),
+                k_idx_dtype=cfg["k_idx_dtype"])
+
+
+@pytest.mark.parametrize("B,N,K,seqs", [
+    (40, 32768, 256, (0, 17, 35, 36, 39)),   # 7 chunks per row, 36 rows per launch: two launches of the fused select
+    (300, 4096, 64, (0, 150, 299))])        # one chunk per row: the fused attention writes its output directly
+def test_full_layer_fused_attention_launch_shapes(B, N, K, seqs):
+    """The Full layer's attention runs inside its select: across launches (partial states indexed by
+    the launch's rows) and for rows of one chunk (no partial state); positions and outputs against
+    the oracle on sampled sequences, including the first and last rows of each launch."""
+    cfg = synth.small("stack_b32_n262144", B=B, N=N, K=K, modes=("full",))
+    cache, layers, _, olayers = build_case(cfg, with_oracle=False)
+    plan = make_plan(cfg)
+    plan.run_decode(cache, layers)
+    torch.cuda.synchronize()
+    ocache = {b: _oracle_seq(cfg, b) for b in seqs}
+    for b in seqs:
+        res = OP.run_decode(["full"], ocache[b], [olayers[0][b]], K, None, softmax_scale=SCALE)
+        s = OS.index_scores(olayers[0][b]["q_idx"], cfg["q_idx_dtype"], ocache[b]["k_idx"], cfg["k_idx_dtype"])
+        g_idx = host(layers[0]["idx_out"][b])
+        assert compare_topk(g_idx, res[0]["idx"], lambda p: s[p], K) == "exact", b
+        assert max_rel_err_rows(host(layers[0]["out"][b]), res[0]["out"]) <= ATTN_TOL, b
+
+
 def test_plan_is_deterministic():
     cfg = synth.small("stack_b32_n262144", B=4, N=40000, K=256, P=1024)
     cache, layers, _, _ = build_case(cfg, with_oracle=False)
