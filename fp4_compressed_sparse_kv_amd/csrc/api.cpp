@@ -818,7 +818,13 @@ int prefill_layout(const csa2_plan* plan, int32_t B, int32_t Q, int64_t N, int32
         if (lay->R < 1) lay->R = 1;
         lay->nr = (int32_t)(N / 65536 < 1 ? 1 : (N / 65536 > 16 ? 16 : N / 65536));
         lay->nrd = (int32_t)(lay->ns / 2048 < 1 ? 1 : (lay->ns / 2048 > 8 ? 8 : lay->ns / 2048));
+        // slots per (query, range): four times the expected share of the ~2M candidates, or - when
+        // that still leaves twice the share - as many as keep a query's lists within one select
+        // chunk (32,768 slots: one workgroup per query, no row exchanges). A range that overflows
+        // sends its query to the exact repair.
         int64_t cap = 4 * 2 * (int64_t)M / lay->nr;
+        const int64_t one_chunk = 32768 / lay->nr;
+        if (cap > one_chunk && one_chunk >= 2 * 2 * (int64_t)M / lay->nr) cap = one_chunk;
         if (cap < 512) cap = 512;
         lay->cap = (int32_t)((cap + 63) / 64 * 64);
         if (int e = plan_select(rows, lay->ns, 1024, &lay->sel_sample)) return e;
