@@ -7,16 +7,18 @@
 // KV head), so both matrix-core operands are contiguous 16-byte runs along D.
 // A workgroup of 4 waves owns 64 tokens and all 256 channels: wave w computes
 // channels 64w..64w+63 of the 64 tokens with v_mfma_f32_32x32x16_bf16 (two
-// token halves x two channel halves), over k-tiles of 64. The H tile is
-// shared by the four waves, so it is staged in LDS; each wave's W operands
-// are its own, so they go from global memory (L2) straight into registers in
-// the matrix-core layout and never touch LDS. Three register sets and three
-// LDS buffers rotate: while tile k is multiplied (LDS buffer k % 3, W from
-// set k % 3), tile k+2 is being requested into set (k+2) % 3 and tile k+1's H
-// part is written from its set into LDS buffer (k+1) % 3, so every load has
-// two tiles' worth of matrix-core work to arrive. Every workgroup streams its own 64 rows of H
-// once; W (2 MiB at D = 4096) is read by every workgroup and stays in each
-// XCD's L2. The epilogue rounds the fp32 sums to bf16 (nearest even) into an
+// token halves x two channel halves), over k-tiles of 64. Both tiles go
+// through LDS: the H tile is shared by the four waves, and the W tile is
+// loaded with 8 lanes per 128-byte channel row, so each load instruction of a
+// wave reads 8 whole rows (loading each wave's operands straight into the
+// matrix-core layout touched 32 rows per instruction, 32 bytes of each, and
+// the rows were evicted from L1 before the rest was read: 68 against 53 us at
+// 16384 x 4096). Three register sets and three LDS buffers rotate: while tile
+// k is multiplied from LDS buffer k % 3, tile k+2 is being requested into set
+// (k+2) % 3 and tile k+1 is written from its set into LDS buffer (k+1) % 3,
+// so every load has two tiles' worth of matrix-core work to arrive. Every
+// workgroup streams its own 64 rows of H once; W (2 MiB at D = 4096) is read
+// by every workgroup and stays in each XCD's L2. The epilogue rounds the fp32 sums to bf16 (nearest even) into an
 // LDS tile, then each thread quantizes whole 16-channel groups (E4M3 scale)
 // or 32-channel blocks (E8M0 scale) with the same per-group code as
 // kv_quant_fp4 / kv_quant_mxfp4, and writes the cache records directly:
@@ -38,6 +40,7 @@ constexpr int kPjCRow = kPjN + 8;               // epilogue row of bf16
 
 struct PjStage {
     uint16_t a[3][kPjM * kPjRow];
+    uint16_t b[3][kPjN * kPjRow];               // the weight tile, [channel][k]
 };
 union PjLds {
     PjStage st;
@@ -66,10 +69,11 @@ k_kv_project(const uint16_t* __restrict__ h, int64_t T, int32_t D, int64_t hs, c
     const int lr = tid >> 3, lk = (tid & 7) * 8;
     const uint16_t* ap0 = h + min(m0 + lr, T - 1) * hs + lk;          // rows past T reload the last one
     const uint16_t* ap1 = h + min(m0 + lr + 32, T - 1) * hs + lk;     // (never stored)
-    const uint16_t* bp0 = wt + (int64_t)(64 * wave + ln) * wsd + 8 * g;
-    const uint16_t* bp1 = bp0 + (int64_t)32 * wsd;
+    // W: thread t takes 16-byte chunk (t & 7) of channel rows (t >> 3) + 32 j,
+    // j = 0..7: a wave's load covers 8 whole 128-byte rows of the tile
+    const uint16_t* bp = wt + (int64_t)lr * wsd + lk;
     struct Regs {                               // named registers: nothing indexed at run time
-        uint4 a0, a1, b00, b01, b02, b03, b10, b11, b12, b13;
+        uint4 a0, a1, b0, b1, b2, b3, b4, b5, b6, b7;
     };
     Regs r0, r1, r2;
     auto ld16 = [](const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); };
@@ -77,18 +81,28 @@ k_kv_project(const uint16_t* __restrict__ h, int64_t T, int32_t D, int64_t hs, c
         const int o = kt * kPjK;
         r.a0 = ld16(ap0 + o);
         r.a1 = ld16(ap1 + o);
-        r.b00 = ld16(bp0 + o);
-        r.b01 = ld16(bp0 + o + 16);
-        r.b02 = ld16(bp0 + o + 32);
-        r.b03 = ld16(bp0 + o + 48);
-        r.b10 = ld16(bp1 + o);
-        r.b11 = ld16(bp1 + o + 16);
-        r.b12 = ld16(bp1 + o + 32);
-        r.b13 = ld16(bp1 + o + 48);
+        const int64_t w32 = (int64_t)32 * wsd;
+        r.b0 = ld16(bp + o);
+        r.b1 = ld16(bp + w32 + o);
+        r.b2 = ld16(bp + 2 * w32 + o);
+        r.b3 = ld16(bp + 3 * w32 + o);
+        r.b4 = ld16(bp + 4 * w32 + o);
+        r.b5 = ld16(bp + 5 * w32 + o);
+        r.b6 = ld16(bp + 6 * w32 + o);
+        r.b7 = ld16(bp + 7 * w32 + o);
     };
     auto store = [&](int buf, const Regs& r) {
         *reinterpret_cast<uint4*>(&lds.st.a[buf][lr * kPjRow + lk]) = r.a0;
         *reinterpret_cast<uint4*>(&lds.st.a[buf][(lr + 32) * kPjRow + lk]) = r.a1;
+        uint16_t* wb = &lds.st.b[buf][lr * kPjRow + lk];
+        *reinterpret_cast<uint4*>(wb) = r.b0;
+        *reinterpret_cast<uint4*>(wb + 32 * kPjRow) = r.b1;
+        *reinterpret_cast<uint4*>(wb + 64 * kPjRow) = r.b2;
+        *reinterpret_cast<uint4*>(wb + 96 * kPjRow) = r.b3;
+        *reinterpret_cast<uint4*>(wb + 128 * kPjRow) = r.b4;
+        *reinterpret_cast<uint4*>(wb + 160 * kPjRow) = r.b5;
+        *reinterpret_cast<uint4*>(wb + 192 * kPjRow) = r.b6;
+        *reinterpret_cast<uint4*>(wb + 224 * kPjRow) = r.b7;
     };
 
     f32x16p acc[2][2];
@@ -97,21 +111,23 @@ k_kv_project(const uint16_t* __restrict__ h, int64_t T, int32_t D, int64_t hs, c
 #pragma unroll
         for (int ni = 0; ni < 2; ++ni) acc[mi][ni] = f32x16p{};
 
-    auto compute = [&](int cur, const Regs& r) {
-        const uint4 bq[2][4] = {{r.b00, r.b01, r.b02, r.b03}, {r.b10, r.b11, r.b12, r.b13}};
+    auto compute = [&](int cur) {
 #pragma unroll
         for (int s = 0; s < kPjK / 16; ++s) {   // k-step s, lane group g: k = 16 s + 8 g .. + 7
-            bf16x8p a[2];
+            bf16x8p a[2], bq[2];
 #pragma unroll
             for (int mi = 0; mi < 2; ++mi)
                 a[mi] = __builtin_bit_cast(bf16x8p, *reinterpret_cast<const uint4*>(
                                                         &lds.st.a[cur][(32 * mi + ln) * kPjRow + 16 * s + 8 * g]));
 #pragma unroll
+            for (int ni = 0; ni < 2; ++ni)
+                bq[ni] = __builtin_bit_cast(bf16x8p, *reinterpret_cast<const uint4*>(
+                                                         &lds.st.b[cur][(64 * wave + 32 * ni + ln) * kPjRow + 16 * s + 8 * g]));
+#pragma unroll
             for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
                 for (int ni = 0; ni < 2; ++ni)
-                    acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mi], __builtin_bit_cast(bf16x8p, bq[ni][s]),
-                                                                        acc[mi][ni], 0, 0, 0);
+                    acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mi], bq[ni], acc[mi][ni], 0, 0, 0);
         }
     };
 
@@ -120,9 +136,10 @@ k_kv_project(const uint16_t* __restrict__ h, int64_t T, int32_t D, int64_t hs, c
     // counts exact) and are never used.
     const int nk = D / kPjK;
     auto step = [&](int k, Regs& rl, Regs& rc, Regs& rs, int bc, int bs) {
+        (void)rc;
         load(min(k + 2, nk - 1), rl);           // tile k+2
-        compute(bc, rc);                        // tile k
-        if (k + 1 < nk) store(bs, rs);          // tile k+1's H part
+        compute(bc);                            // tile k
+        if (k + 1 < nk) store(bs, rs);          // tile k+1
         __syncthreads();
     };
     load(0, r0);
