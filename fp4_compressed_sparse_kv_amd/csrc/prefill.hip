@@ -32,7 +32,9 @@
 // Matrix-core tiles: a workgroup of 4 waves owns 128 queries of one sequence
 // and one key range; wave w owns query rows 32w..32w+31 and runs
 // v_mfma_f32_32x32x16_bf16 over 128-key tiles staged in LDS as bf16 (E4M3
-// keys convert exactly). The K dimension is permuted (lane group g holds
+// keys convert exactly), one 64-key half at a time, three workgroups per CU
+// (the candidate appends are the VALU-bound part; more resident waves hide
+// them behind each other's matrix-core work). The K dimension is permuted (lane group g holds
 // channels 32g..32g+31) so each lane reads 32 contiguous key bytes; the dot
 // product does not depend on the order of its terms beyond the bound above.
 #include "dot.hpp"
@@ -126,9 +128,10 @@ struct TileRaw {
 };
 
 template <int KT, bool DENSE>
-__global__ void __launch_bounds__(kPfThreads, 2) k_pf_tiles(PfTileArgs a) {
+__global__ void __launch_bounds__(kPfThreads, 3) k_pf_tiles(PfTileArgs a) {
     constexpr int EB = ElemBytes<KT>::v;
     __shared__ __attribute__((aligned(16))) uint16_t tile[2][kPfKeys * kPfLdsStride];
+    __shared__ int32_t s_qp[kPfThreads / kWave][32];     // causal limit of each query row of a wave
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 5, ln = lane & 31;
     const int qtiles = (a.Q + kPfRows - 1) / kPfRows;
@@ -151,8 +154,7 @@ __global__ void __launch_bounds__(kPfThreads, 2) k_pf_tiles(PfTileArgs a) {
     }
     // accumulator element i of this lane is query row rr(i) = 8*(i/4) + 4g + i%4 of the wave
     float tlo[16];
-    int32_t qp[16];
-    uint32_t cur0[16], cur1[16];                // list lengths of the rows rr(i) of lane group 0 and 1 (uniform)
+    uint32_t curv[16];                          // list length of this lane's row rr(i) (uniform per lane group)
     int32_t qmin = INT32_MAX, qmax = -1;        // over this wave's valid rows
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -160,14 +162,14 @@ __global__ void __launch_bounds__(kPfThreads, 2) k_pf_tiles(PfTileArgs a) {
         const bool ok = qi < a.Q;
         const int64_t r = rbase + (ok ? qi : 0);
         const int64_t pq = a.q_pos ? a.q_pos[r] : INT64_MAX;
-        qp[i] = ok ? (int32_t)(pq < 0 ? -1 : (pq >= a.N ? a.N - 1 : pq)) : -1;
+        const int32_t qpi = ok ? (int32_t)(pq < 0 ? -1 : (pq >= a.N ? a.N - 1 : pq)) : -1;
         if (ok) {
-            qmin = min(qmin, qp[i]);
-            qmax = max(qmax, qp[i]);
+            qmin = min(qmin, qpi);
+            qmax = max(qmax, qpi);
         }
+        if (ln == 0) s_qp[wave][8 * (i / 4) + 4 * g + (i % 4)] = qpi;
         if constexpr (!DENSE) tlo[i] = ok ? a.thr[2 * r + 0] : INFINITY;
-        cur0[i] = 0u;
-        cur1[i] = 0u;
+        curv[i] = 0u;
     }
     for (int o = 32; o >= 1; o >>= 1) {
         qmin = min(qmin, __shfl_xor(qmin, o));
@@ -175,9 +177,10 @@ __global__ void __launch_bounds__(kPfThreads, 2) k_pf_tiles(PfTileArgs a) {
     }
 
     const uint8_t* kbase = a.k + (size_t)seq * a.N * kPfDim * EB;
-    // candidate list of row rr(i): cand_base + (8*(i/4) + i%4) * row_step
-    const size_t row_step = (size_t)a.nranges * a.cap;
-    const size_t cand_base = ((size_t)(rbase + q0 + 4 * g) * a.nranges + range) * a.cap;
+    // candidate list of row rr(i): clist + (8*(i/4) + i%4) * row_step (32-bit offsets: the
+    // launcher keeps 32 * nranges * cap below 2^31)
+    const uint32_t row_step = (uint32_t)a.nranges * (uint32_t)a.cap;
+    int32_t* const clist = a.cand + ((size_t)(rbase + q0 + 4 * g) * a.nranges + range) * a.cap;
     // Candidate mode: the ranges split the causal span of this workgroup's 128
     // queries, [0, largest q_pos], not the whole context, so every query's
     // candidates spread over all of its lists wherever the chunk sits.
@@ -217,11 +220,9 @@ __global__ void __launch_bounds__(kPfThreads, 2) k_pf_tiles(PfTileArgs a) {
             uint32_t o[16];
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
-                const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)ws[u], false);
-                const f32x2 hi2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)ws[u], true);
-                // E4M3 values are exact in bf16: keep the top 16 bits of each fp32
-                o[2 * u + 0] = (__float_as_uint(lo.x) >> 16) | (__float_as_uint(lo.y) & 0xFFFF0000u);
-                o[2 * u + 1] = (__float_as_uint(hi2.x) >> 16) | (__float_as_uint(hi2.y) & 0xFFFF0000u);
+                // E4M3 values are exact in bf16; the scale 1.0 leaves them as they are
+                o[2 * u + 0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(ws[u], 1.0f, false));
+                o[2 * u + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(ws[u], 1.0f, true));
             }
 #pragma unroll
             for (int u = 0; u < 4; ++u) dst[u] = make_uint4(o[4 * u], o[4 * u + 1], o[4 * u + 2], o[4 * u + 3]);
@@ -237,61 +238,67 @@ __global__ void __launch_bounds__(kPfThreads, 2) k_pf_tiles(PfTileArgs a) {
         if (!DENSE && p_first > (int64_t)qmax) return;           // no causal key for any row of the wave
         const bool masked = p_last > (int64_t)qmin;              // some key is past some row's limit
         const bool full = jt + kPfKeys <= j1;                    // every key of the tile is in the range
-        // all B operands of the tile first, then the four 32-key blocks' MFMA
-        // chains interleaved (independent accumulators keep the matrix core busy)
-        constexpr int NC = kPfKeys / 32;
-        bf16x8 bop[NC][4];
+        // the tile in two halves of 64 keys: the two 32-key blocks' MFMA chains
+        // interleaved (independent accumulators), then their candidates - half
+        // the accumulators live at a time, so three workgroups fit on a CU
+        constexpr int NC = 2;                   // 32-key blocks per half tile
 #pragma unroll
-        for (int c = 0; c < NC; ++c)
+        for (int hh = 0; hh < kPfKeys / 64; ++hh) {
+            f32x16 accs[NC];
 #pragma unroll
-            for (int s = 0; s < 4; ++s)
-                bop[c][s] = __builtin_bit_cast(
-                    bf16x8, *reinterpret_cast<const uint4*>(&buf[(32 * c + ln) * kPfLdsStride + 32 * g + 8 * s]));
-        f32x16 accs[NC];
+            for (int c = 0; c < NC; ++c) accs[c] = f32x16{};
 #pragma unroll
-        for (int c = 0; c < NC; ++c) accs[c] = f32x16{};
+            for (int s = 0; s < 4; ++s) {
+                bf16x8 bop[NC];
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
+                for (int c = 0; c < NC; ++c)
+                    bop[c] = __builtin_bit_cast(
+                        bf16x8, *reinterpret_cast<const uint4*>(&buf[(64 * hh + 32 * c + ln) * kPfLdsStride + 32 * g + 8 * s]));
 #pragma unroll
-            for (int c = 0; c < NC; ++c) accs[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[s], bop[c][s], accs[c], 0, 0, 0);
+                for (int c = 0; c < NC; ++c) accs[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[s], bop[c], accs[c], 0, 0, 0);
+            }
 #pragma unroll
-        for (int c = 0; c < NC; ++c) {
-            const f32x16 acc = accs[c];
-            const int64_t jk = jt + 32 * c + ln;
-            const bool kvalid = jk < j1;
-            const int32_t pos = (int32_t)(a.key_off + jk * a.key_stride);
-            if constexpr (DENSE) {
-                if (kvalid) {
+            for (int c = 0; c < NC; ++c) {
+                const f32x16 acc = accs[c];
+                const int64_t jk = jt + 64 * hh + 32 * c + ln;
+                const bool kvalid = jk < j1;
+                const int32_t pos = (int32_t)(a.key_off + jk * a.key_stride);
+                if constexpr (DENSE) {
+                    if (kvalid) {
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const int qi = q0 + 8 * (i / 4) + 4 * g + (i % 4);
-                        if (qi < a.Q) a.dense[(size_t)(rbase + qi) * a.nkeys + jk] = pos <= qp[i] ? acc[i] : -INFINITY;
-                    }
-                }
-            } else {
-                // lanes 0..31 hold row rr(i) of lane group 0, lanes 32..63 that of group 1;
-                // each half appends its passing keys in lane (= position) order
-                auto emit = [&](int i, uint64_t m, bool pass) {
-                    const uint32_t n0 = (uint32_t)__popc((uint32_t)m), n1 = (uint32_t)__popc((uint32_t)(m >> 32));
-                    const uint32_t slot = (g ? cur1[i] : cur0[i]) + lanes_below(m) - (g ? n0 : 0u);
-                    if (pass && slot < (uint32_t)a.cap)
-                        a.cand[cand_base + (size_t)(8 * (i / 4) + (i % 4)) * row_step + slot] = pos;
-                    cur0[i] += n0;
-                    cur1[i] += n1;
-                };
-                if (full && !masked) {          // every key valid and causal for every row: one compare each
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const bool pass = acc[i] >= tlo[i];
-                        const uint64_t m = __ballot(pass);
-                        if (m != 0ull) emit(i, m, pass);
+                        for (int i = 0; i < 16; ++i) {
+                            const int qi = q0 + 8 * (i / 4) + 4 * g + (i % 4);
+                            if (qi < a.Q)
+                                a.dense[(size_t)(rbase + qi) * a.nkeys + jk] =
+                                    pos <= s_qp[wave][8 * (i / 4) + 4 * g + (i % 4)] ? acc[i] : -INFINITY;
+                        }
                     }
                 } else {
+                    // lanes 0..31 hold row rr(i) of lane group 0, lanes 32..63 that of group 1;
+                    // each half appends its passing keys in lane (= position) order
+                    auto emit = [&](int i, uint64_t m, bool pass) {
+                        const uint32_t mlo = (uint32_t)m, mhi = (uint32_t)(m >> 32);
+                        // the list length plus the passing lanes below this one in its half
+                        const uint32_t slot = __builtin_amdgcn_mbcnt_hi(mhi, __builtin_amdgcn_mbcnt_lo(g ? 0u : mlo, curv[i]));
+                        if (pass && slot < (uint32_t)a.cap)
+                            clist[(8 * (i / 4) + (i % 4)) * row_step + slot] = pos;
+                        curv[i] += (uint32_t)__popc(g ? mhi : mlo);
+                    };
+                    if (full && !masked) {          // every key valid and causal for every row: one compare each
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const bool pass = (int)kvalid & (int)(pos <= qp[i]) & (int)(acc[i] >= tlo[i]);
-                        const uint64_t m = __ballot(pass);
-                        if (m != 0ull) emit(i, m, pass);
+                        for (int i = 0; i < 16; ++i) {
+                            const bool pass = acc[i] >= tlo[i];
+                            const uint64_t m = __ballot(pass);
+                            if (__builtin_expect(m != 0ull, 0)) emit(i, m, pass);
+                        }
+                    } else {
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) {
+                            const bool pass = (int)kvalid & (int)(pos <= s_qp[wave][8 * (i / 4) + 4 * g + (i % 4)]) &
+                                              (int)(acc[i] >= tlo[i]);
+                            const uint64_t m = __ballot(pass);
+                            if (__builtin_expect(m != 0ull, 0)) emit(i, m, pass);
+                        }
                     }
                 }
             }
@@ -324,7 +331,7 @@ __global__ void __launch_bounds__(kPfThreads, 2) k_pf_tiles(PfTileArgs a) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const int qi = q0 + 8 * (i / 4) + 4 * g + (i % 4);
-                if (qi < a.Q) a.cnt[(size_t)(rbase + qi) * a.nranges + range] = g ? cur1[i] : cur0[i];
+                if (qi < a.Q) a.cnt[(size_t)(rbase + qi) * a.nranges + range] = curv[i];
             }
         }
     }
@@ -688,6 +695,9 @@ int launch_pf_tiles(const PfTiles& t, int k_dtype, bool dense, hipStream_t strea
     a.cand = t.cand;
     a.cap = t.cap;
     a.cnt = t.cnt;
+    // the kernel addresses a row's lists with 32-bit offsets of up to 32 * nranges * cap
+    if (!dense && (int64_t)32 * t.nranges * t.cap >= ((int64_t)1 << 31))
+        return fail(INVALID, "prefill candidate lists: nranges * cap too large");
     const int qtiles = (t.Q + kPfRows - 1) / kPfRows;
     const dim3 grid((unsigned)((int64_t)t.B * qtiles), (unsigned)t.nranges);
     if (k_dtype == kE4M3) {
