@@ -5,20 +5,22 @@
 // H is [T][D] bf16; W is given transposed, one row of D weights per output
 // channel ([256][D]: channels 0..127 are K, 128..255 are V of the one shared
 // KV head), so both matrix-core operands are contiguous 16-byte runs along D.
-// A workgroup of 4 waves owns 64 tokens and all 256 channels: wave w computes
-// channels 64w..64w+63 of the 64 tokens with v_mfma_f32_32x32x16_bf16 (two
-// token halves x two channel halves), over k-tiles of 64. Both tiles go
-// through LDS: the H tile is shared by the four waves, and the W tile is
-// loaded with 8 lanes per 128-byte channel row, so each load instruction of a
-// wave reads 8 whole rows (loading each wave's operands straight into the
-// matrix-core layout touched 32 rows per instruction, 32 bytes of each, and
-// the rows were evicted from L1 before the rest was read: 68 against 53 us at
-// 16384 x 4096). Three register sets and three LDS buffers rotate: while tile
-// k is multiplied from LDS buffer k % 3, tile k+2 is being requested into set
-// (k+2) % 3 and tile k+1 is written from its set into LDS buffer (k+1) % 3,
-// so every load has two tiles' worth of matrix-core work to arrive. Every
-// workgroup streams its own 64 rows of H once; W (2 MiB at D = 4096) is read
-// by every workgroup and stays in each XCD's L2. The epilogue rounds the fp32 sums to bf16 (nearest even) into an
+// A workgroup of 8 waves owns 64 tokens and all 256 channels: wave w computes
+// channels 32w..32w+31 of the 64 tokens with v_mfma_f32_32x32x16_bf16 (two
+// token halves), over k-tiles of 64; two waves per SIMD let one wave's matrix
+// work overlap the other's staging (4 waves of 64 channels each: 53 against
+// 47 us at 16384 x 4096). Both tiles go through LDS: the H tile is shared by
+// the eight waves, and the W tile is loaded with 8 lanes per 128-byte channel
+// row, so each load instruction of a wave reads 8 whole rows (loading each
+// wave's operands straight into the matrix-core layout touched 32 rows per
+// instruction, 32 bytes of each, and the rows were evicted from L1 before the
+// rest was read: 68 against 53 us). Three register sets and three LDS
+// buffers rotate: while tile k is multiplied from LDS buffer k % 3, tile k+2
+// is being requested into set (k+2) % 3 and tile k+1 is written from its set
+// into LDS buffer (k+1) % 3, so every load has two tiles' worth of
+// matrix-core work to arrive. Every workgroup streams its own 64 rows of H
+// once; W (2 MiB at D = 4096) is read by every workgroup and stays in each
+// XCD's L2. The epilogue rounds the fp32 sums to bf16 (nearest even) into an
 // LDS tile, then each thread quantizes whole 16-channel groups (E4M3 scale)
 // or 32-channel blocks (E8M0 scale) with the same per-group code as
 // kv_quant_fp4 / kv_quant_mxfp4, and writes the cache records directly:
@@ -31,7 +33,7 @@ namespace csa2 {
 typedef __bf16 bf16x8p __attribute__((ext_vector_type(8)));
 typedef float f32x16p __attribute__((ext_vector_type(16)));
 
-constexpr int kPjThreads = 256;
+constexpr int kPjThreads = 512;
 constexpr int kPjM = 64;                        // tokens per workgroup
 constexpr int kPjN = 256;                       // output channels (K | V)
 constexpr int kPjK = 64;                        // k-tile
@@ -62,72 +64,53 @@ k_kv_project(const uint16_t* __restrict__ h, int64_t T, int32_t D, int64_t hs, c
     const int ln = lane & 31, g = lane >> 5;
     const int64_t m0 = (int64_t)blockIdx.x * kPjM;
 
-    // global -> register loads of one k-tile. H: thread t takes 16-byte chunk
-    // (t & 7) of rows (t >> 3) and (t >> 3) + 32. W: lane (ln, g) of wave w
-    // takes, for channel half ni and k-step s, the 8 weights k = 16 s + 8 g ..
-    // of channel 64 w + 32 ni + ln - its own B operand.
+    // global -> register loads of one k-tile: thread t takes 16-byte chunk
+    // (t & 7) of H row (t >> 3) and of W^T rows (t >> 3) + 64 j, j = 0..3: a
+    // wave's load instruction reads 8 whole 128-byte rows
     const int lr = tid >> 3, lk = (tid & 7) * 8;
-    const uint16_t* ap0 = h + min(m0 + lr, T - 1) * hs + lk;          // rows past T reload the last one
-    const uint16_t* ap1 = h + min(m0 + lr + 32, T - 1) * hs + lk;     // (never stored)
-    // W: thread t takes 16-byte chunk (t & 7) of channel rows (t >> 3) + 32 j,
-    // j = 0..7: a wave's load covers 8 whole 128-byte rows of the tile
+    const uint16_t* ap0 = h + min(m0 + lr, T - 1) * hs + lk;          // rows past T reload the last one (never stored)
     const uint16_t* bp = wt + (int64_t)lr * wsd + lk;
     struct Regs {                               // named registers: nothing indexed at run time
-        uint4 a0, a1, b0, b1, b2, b3, b4, b5, b6, b7;
+        uint4 a0, b0, b1, b2, b3;
     };
     Regs r0, r1, r2;
     auto ld16 = [](const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); };
     auto load = [&](int kt, Regs& r) {
         const int o = kt * kPjK;
         r.a0 = ld16(ap0 + o);
-        r.a1 = ld16(ap1 + o);
-        const int64_t w32 = (int64_t)32 * wsd;
+        const int64_t w64 = (int64_t)64 * wsd;
         r.b0 = ld16(bp + o);
-        r.b1 = ld16(bp + w32 + o);
-        r.b2 = ld16(bp + 2 * w32 + o);
-        r.b3 = ld16(bp + 3 * w32 + o);
-        r.b4 = ld16(bp + 4 * w32 + o);
-        r.b5 = ld16(bp + 5 * w32 + o);
-        r.b6 = ld16(bp + 6 * w32 + o);
-        r.b7 = ld16(bp + 7 * w32 + o);
+        r.b1 = ld16(bp + w64 + o);
+        r.b2 = ld16(bp + 2 * w64 + o);
+        r.b3 = ld16(bp + 3 * w64 + o);
     };
     auto store = [&](int buf, const Regs& r) {
         *reinterpret_cast<uint4*>(&lds.st.a[buf][lr * kPjRow + lk]) = r.a0;
-        *reinterpret_cast<uint4*>(&lds.st.a[buf][(lr + 32) * kPjRow + lk]) = r.a1;
         uint16_t* wb = &lds.st.b[buf][lr * kPjRow + lk];
         *reinterpret_cast<uint4*>(wb) = r.b0;
-        *reinterpret_cast<uint4*>(wb + 32 * kPjRow) = r.b1;
-        *reinterpret_cast<uint4*>(wb + 64 * kPjRow) = r.b2;
-        *reinterpret_cast<uint4*>(wb + 96 * kPjRow) = r.b3;
-        *reinterpret_cast<uint4*>(wb + 128 * kPjRow) = r.b4;
-        *reinterpret_cast<uint4*>(wb + 160 * kPjRow) = r.b5;
-        *reinterpret_cast<uint4*>(wb + 192 * kPjRow) = r.b6;
-        *reinterpret_cast<uint4*>(wb + 224 * kPjRow) = r.b7;
+        *reinterpret_cast<uint4*>(wb + 64 * kPjRow) = r.b1;
+        *reinterpret_cast<uint4*>(wb + 128 * kPjRow) = r.b2;
+        *reinterpret_cast<uint4*>(wb + 192 * kPjRow) = r.b3;
     };
 
-    f32x16p acc[2][2];
+    // wave w: channels 32 w .. 32 w + 31 of the 64 tokens (two 32x32 tiles)
+    f32x16p acc[2][1];
 #pragma unroll
-    for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < 2; ++ni) acc[mi][ni] = f32x16p{};
+    for (int mi = 0; mi < 2; ++mi) acc[mi][0] = f32x16p{};
 
     auto compute = [&](int cur) {
 #pragma unroll
         for (int s = 0; s < kPjK / 16; ++s) {   // k-step s, lane group g: k = 16 s + 8 g .. + 7
-            bf16x8p a[2], bq[2];
+            bf16x8p a[2], bq[1];
 #pragma unroll
             for (int mi = 0; mi < 2; ++mi)
                 a[mi] = __builtin_bit_cast(bf16x8p, *reinterpret_cast<const uint4*>(
                                                         &lds.st.a[cur][(32 * mi + ln) * kPjRow + 16 * s + 8 * g]));
-#pragma unroll
-            for (int ni = 0; ni < 2; ++ni)
-                bq[ni] = __builtin_bit_cast(bf16x8p, *reinterpret_cast<const uint4*>(
-                                                         &lds.st.b[cur][(64 * wave + 32 * ni + ln) * kPjRow + 16 * s + 8 * g]));
+            bq[0] = __builtin_bit_cast(bf16x8p, *reinterpret_cast<const uint4*>(
+                                                    &lds.st.b[cur][(32 * wave + ln) * kPjRow + 16 * s + 8 * g]));
 #pragma unroll
             for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-                for (int ni = 0; ni < 2; ++ni)
-                    acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mi], bq[ni], acc[mi][ni], 0, 0, 0);
+                acc[mi][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mi], bq[0], acc[mi][0], 0, 0, 0);
         }
     };
 
@@ -158,13 +141,11 @@ k_kv_project(const uint16_t* __restrict__ h, int64_t T, int32_t D, int64_t hs, c
 #pragma unroll
     for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
-        for (int ni = 0; ni < 2; ++ni)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int m = 32 * mi + 8 * (i / 4) + 4 * g + (i % 4);
-                const int n = 64 * wave + 32 * ni + ln;
-                lds.c[m * kPjCRow + n] = (uint16_t)bf16_rne_bits(acc[mi][ni][i]);
-            }
+        for (int i = 0; i < 16; ++i) {
+            const int m = 32 * mi + 8 * (i / 4) + 4 * g + (i % 4);
+            const int n = 32 * wave + ln;
+            lds.c[m * kPjCRow + n] = (uint16_t)bf16_rne_bits(acc[mi][0][i]);
+        }
     __syncthreads();
     constexpr int kGroup = MX ? 32 : 16;
     constexpr int kUnits = kPjM * kPjN / kGroup;
