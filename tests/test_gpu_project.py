@@ -86,8 +86,9 @@ def test_kv_project_into_cache_then_attention(fmt):
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("fmt", ["fp4_e4m3", "mxfp4"])
 def test_kv_project_full_size_sampled(fmt):
-    """The 16,384 x 4096 projection workload in the benchmark's launch configuration; sampled row blocks
-    (the first, a middle and the last tile of 64 rows, plus ragged picks) against the oracle."""
+    """The 16,384 x 4096 projection workload in the benchmark's launch configuration; sampled rows (the
+    first and the last 64, 64 across the middle tile boundary, plus random picks; both channel halves of
+    each) against the oracle."""
     cfg = dict(synth.WORKLOADS["kvproj_t16384_d4096"])
     dev = torch.device("cuda", 0)
     h_t, wt_t = bench.build_proj_input(cfg, dev)
