@@ -67,27 +67,40 @@ __global__ void __launch_bounds__(256) k_pf_kmax(const uint8_t* __restrict__ k, 
 #pragma unroll
     for (int i = 0; i < 16; ++i) m[i] = 0.f;
     const uint8_t* base = k + (size_t)seq * N * kPfDim * EB;
-    for (int64_t r = t0 + (t >> 2); r < t1; r += 64) {
-        const uint8_t* p = base + (size_t)r * kPfDim * EB + cg * 16 * EB;
-        if constexpr (KT == kE4M3) {
-            const uint4 w = *reinterpret_cast<const uint4*>(p);
-            const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+    // four rows per step (r, r + 64, r + 128, r + 192; past the range the last
+    // row again, which leaves a maximum unchanged), their loads in flight together
+    static_assert(EB == 1 || EB == 2, "E4M3 or bf16 keys");
+    constexpr int W = EB;                       // 16-byte words per thread and row
+    for (int64_t r = t0 + (t >> 2); r < t1; r += 256) {
+        uint4 w[4][W];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)ws[j], false);
-                const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)ws[j], true);
-                m[4 * j + 0] = fmaxf(m[4 * j + 0], fabsf(a.x));
-                m[4 * j + 1] = fmaxf(m[4 * j + 1], fabsf(a.y));
-                m[4 * j + 2] = fmaxf(m[4 * j + 2], fabsf(b.x));
-                m[4 * j + 3] = fmaxf(m[4 * j + 3], fabsf(b.y));
-            }
-        } else {
-            const uint4 w0 = *reinterpret_cast<const uint4*>(p), w1 = *reinterpret_cast<const uint4*>(p + 16);
-            const uint32_t ws[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+        for (int u = 0; u < 4; ++u) {
+            const int64_t rr = min(r + 64 * u, t1 - 1);
+            const uint8_t* p = base + (size_t)rr * kPfDim * EB + cg * 16 * EB;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                m[2 * j + 0] = fmaxf(m[2 * j + 0], fabsf(__uint_as_float(ws[j] << 16)));
-                m[2 * j + 1] = fmaxf(m[2 * j + 1], fabsf(__uint_as_float(ws[j] & 0xFFFF0000u)));
+            for (int v = 0; v < W; ++v) w[u][v] = *reinterpret_cast<const uint4*>(p + 16 * v);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            if constexpr (KT == kE4M3) {
+                const uint32_t ws[4] = {w[u][0].x, w[u][0].y, w[u][0].z, w[u][0].w};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)ws[j], false);
+                    const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)ws[j], true);
+                    m[4 * j + 0] = fmaxf(m[4 * j + 0], fabsf(a.x));
+                    m[4 * j + 1] = fmaxf(m[4 * j + 1], fabsf(a.y));
+                    m[4 * j + 2] = fmaxf(m[4 * j + 2], fabsf(b.x));
+                    m[4 * j + 3] = fmaxf(m[4 * j + 3], fabsf(b.y));
+                }
+            } else {
+                const uint32_t ws[8] = {w[u][0].x, w[u][0].y, w[u][0].z, w[u][0].w,
+                                        w[u][W - 1].x, w[u][W - 1].y, w[u][W - 1].z, w[u][W - 1].w};
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    m[2 * j + 0] = fmaxf(m[2 * j + 0], fabsf(__uint_as_float(ws[j] << 16)));
+                    m[2 * j + 1] = fmaxf(m[2 * j + 1], fabsf(__uint_as_float(ws[j] & 0xFFFF0000u)));
+                }
             }
         }
     }
@@ -343,21 +356,89 @@ __global__ void __launch_bounds__(kPfThreads, 3) k_pf_tiles(PfTileArgs a) {
 // than R are finite): the row's order-preserving keys stay in registers (256
 // threads, up to kRthPer keys each) and three radix passes over 11, 11 and 10
 // key bits narrow the bin that holds the R-th key, counting from the top.
+// With R <= 256 the first pass counts only the keys at or above a floor: the
+// lower edge of the 11-bit bin that holds the R-th largest of the threads'
+// maxima. Those maxima are R distinct keys at or above the floor, so the R-th
+// largest key of the row is too, and every key below the floor ranks after
+// it; the floor leaves out most of the row, whose keys would otherwise crowd
+// a few histogram bins with conflicting atomic adds.
 constexpr int kRthThreads = 256;
 constexpr int kRthPer = 64;                     // rows of up to 16384 samples
+
+// Over nb = 2^w bins h[0..nb) scanned from the top: the bin holding the
+// need-th key and how many of its keys are still needed (res[0], res[1]);
+// returns the total count. Every thread calls it; it ends with a barrier.
+__device__ __forceinline__ uint32_t rth_find(const uint32_t* hist, int nb, uint32_t need, uint32_t* wsum,
+                                             uint32_t* res) {
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
+    // thread t owns bins top - per + 1 .. top (top = nb - 1 - per * t), scanned from the top
+    const int per = nb / kRthThreads;
+    const int top = nb - 1 - tid * per;
+    uint32_t sum = 0;
+    for (int i = 0; i < per; ++i) sum += hist[top - i];
+    const uint32_t inc = wave_incl_scan(sum);
+    if (lane == kWave - 1) wsum[wave] = inc;
+    __syncthreads();
+    uint32_t before = inc - sum, total = 0;
+#pragma unroll
+    for (int v = 0; v < kRthThreads / kWave; ++v) {
+        total += wsum[v];
+        if (v < wave) before += wsum[v];
+    }
+    if (before < need && need <= before + sum) {
+        uint32_t c = before;
+        for (int i = 0; i < per; ++i) {
+            const uint32_t h = hist[top - i];
+            if (c + h >= need) {
+                res[0] = (uint32_t)(top - i);
+                res[1] = need - c;
+                break;
+            }
+            c += h;
+        }
+    }
+    __syncthreads();
+    return total;
+}
 
 __global__ void __launch_bounds__(kRthThreads)
 k_pf_rth(const float* __restrict__ dense, int32_t n, int32_t R, float* __restrict__ tval) {
     __shared__ uint32_t hist[2048];
     __shared__ uint32_t wsum[kRthThreads / kWave];
     __shared__ uint32_t res[2];
-    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
+    const int tid = threadIdx.x;
     const float* p = dense + (size_t)blockIdx.x * n;
-    uint32_t kv[kRthPer];
+    uint32_t kv[kRthPer];                       // the order of a row's keys does not matter here
+    if ((n & 3) == 0) {                         // 16-byte rows: thread t holds entries 4(256j + t) .. + 3
 #pragma unroll
-    for (int j = 0; j < kRthPer; ++j) {
-        const int i = j * kRthThreads + tid;
-        kv[j] = i < n ? score_key(p[i]) : 0u;
+        for (int j = 0; j < kRthPer / 4; ++j) {
+            const int i = 4 * (j * kRthThreads + tid);
+            const float4 v = i < n ? *reinterpret_cast<const float4*>(p + i) : make_float4(NAN, NAN, NAN, NAN);
+            kv[4 * j + 0] = score_key(v.x);
+            kv[4 * j + 1] = score_key(v.y);
+            kv[4 * j + 2] = score_key(v.z);
+            kv[4 * j + 3] = score_key(v.w);
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < kRthPer; ++j) {
+            const int i = j * kRthThreads + tid;
+            kv[j] = i < n ? score_key(p[i]) : 0u;
+        }
+    }
+    uint32_t floor_key = 1u;                    // key 0 (NaN, -inf, padding) never counts
+    if (R <= kRthThreads) {
+        uint32_t mx = 0u;
+#pragma unroll
+        for (int j = 0; j < kRthPer; ++j) mx = max(mx, kv[j]);
+        for (int b = tid; b < 2048; b += kRthThreads) hist[b] = 0u;
+        __syncthreads();
+        if (mx != 0u) atomicAdd(&hist[mx >> 21], 1u);
+        __syncthreads();
+        const uint32_t tot = rth_find(hist, 2048, (uint32_t)R, wsum, res);
+        // fewer than R nonzero maxima: no floor beyond the nonzero keys
+        if (tot >= (uint32_t)R && res[0] != 0u) floor_key = res[0] << 21;
+        __syncthreads();                        // res is rewritten by the first pass
     }
     uint32_t prefix = 0, need = (uint32_t)R;
 #pragma unroll
@@ -370,40 +451,15 @@ k_pf_rth(const float* __restrict__ dense, int32_t n, int32_t R, float* __restric
 #pragma unroll
         for (int j = 0; j < kRthPer; ++j) {
             const uint32_t k = kv[j];
-            if (k != 0u && (d == 0 || (k >> (lo + w)) == prefix)) atomicAdd(&hist[(k >> lo) & (uint32_t)(nb - 1)], 1u);
+            if (d == 0 ? k >= floor_key : (k != 0u && (k >> (lo + w)) == prefix))
+                atomicAdd(&hist[(k >> lo) & (uint32_t)(nb - 1)], 1u);
         }
         __syncthreads();
-        // thread t owns bins top - per + 1 .. top (top = nb - 1 - per * t), scanned from the top
-        const int per = nb / kRthThreads;
-        const int top = nb - 1 - tid * per;
-        uint32_t sum = 0;
-        for (int i = 0; i < per; ++i) sum += hist[top - i];
-        const uint32_t inc = wave_incl_scan(sum);
-        if (lane == kWave - 1) wsum[wave] = inc;
-        __syncthreads();
-        uint32_t before = inc - sum, total = 0;
-#pragma unroll
-        for (int v = 0; v < kRthThreads / kWave; ++v) {
-            total += wsum[v];
-            if (v < wave) before += wsum[v];
-        }
+        const uint32_t total = rth_find(hist, nb, need, wsum, res);
         if (d == 0 && total < need) {           // the same for every thread
             if (tid == 0) tval[blockIdx.x] = -INFINITY;
             return;
         }
-        if (before < need && need <= before + sum) {
-            uint32_t c = before;
-            for (int i = 0; i < per; ++i) {
-                const uint32_t h = hist[top - i];
-                if (c + h >= need) {
-                    res[0] = (uint32_t)(top - i);
-                    res[1] = need - c;
-                    break;
-                }
-                c += h;
-            }
-        }
-        __syncthreads();
         prefix = (prefix << w) | res[0];
         need = res[1];
         __syncthreads();                        // hist, wsum and res are rewritten by the next pass
