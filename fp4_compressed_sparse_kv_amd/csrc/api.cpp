@@ -790,6 +790,7 @@ struct PrefillLayout {
     int32_t M = 0;                              // the (larger) number of positions selected per query
     int64_t rows = 0, ns = 0;
     int32_t R = 0, nr = 0, nrd = 0, cap = 0;
+    int64_t cand_dense = 0;                     // most candidates per query the exact select holds
     SelPlan sel_sample, sel_cand, sel_exact;
     size_t off_kmax = 0, off_dense = 0, off_sidx = 0, off_ssc = 0, off_thr = 0, off_csc = 0, off_cnt = 0,
            off_rep = 0, off_sel = 0, end = 0;   // end: first byte after the selection region
@@ -814,7 +815,13 @@ int prefill_layout(const csa2_plan* plan, int32_t B, int32_t Q, int64_t N, int32
     } else {
         const int64_t rows = lay->rows;
         lay->ns = (N - kSampleStride / 2 + kSampleStride - 1) / kSampleStride;
-        lay->R = (int32_t)((2 * (int64_t)M * lay->ns + N - 1) / N);
+        // R: f times the expected share of the top-M in the sample, f = 2 or (for M >= 7776) 1.5. The
+        // R-th largest sample score t ranks about 64R = f*M among all positions, with a standard
+        // deviation of about sqrt(64 f M) positions; a query needs a second, exact pass when t ranks
+        // below M, which lies (f - 1) * sqrt(M / (64 f)) deviations away: 4 at f = 2 and M = 2048,
+        // 4.6 at f = 1.5 and M = 8192. A smaller f leaves fewer candidates to list and score exactly.
+        const int64_t f2 = M >= 7776 ? 3 : 4;  // 2f
+        lay->R = (int32_t)((f2 * (int64_t)M * lay->ns + 2 * N - 1) / (2 * N));
         if (lay->R < 1) lay->R = 1;
         lay->nr = (int32_t)(N / 65536 < 1 ? 1 : (N / 65536 > 16 ? 16 : N / 65536));
         lay->nrd = (int32_t)(lay->ns / 2048 < 1 ? 1 : (lay->ns / 2048 > 8 ? 8 : lay->ns / 2048));
@@ -829,6 +836,9 @@ int prefill_layout(const csa2_plan* plan, int32_t B, int32_t Q, int64_t N, int32
         lay->cap = (int32_t)((cap + 63) / 64 * 64);
         if (int e = plan_select(rows, lay->ns, 1024, &lay->sel_sample)) return e;
         if (int e = plan_select(rows, (int64_t)lay->nr * lay->cap, 1024, &lay->sel_cand)) return e;
+        // the candidates' keys and positions in LDS for at most cand_dense candidates per query (a
+        // query with more goes to the exact repair; the lists' slots exceed the candidates ~4 times)
+        lay->cand_dense = plan_select_dense(&lay->sel_cand);
         if (int e = plan_select(kRepairRows, N, 1024, &lay->sel_exact)) return e;
         lay->off_kmax = off;
         off += align_up(pf_kmax_floats(B) * 4);
@@ -934,7 +944,7 @@ int prefill_select(const csa2_plan* plan, const PrefillLayout& lay, const csa2_c
     SelOutput oc[2] = {o[0], nt > 1 ? o[1] : o[0]};
     oc[0].score = csc;                          // the M-th exact score decides the verification
     if (int e = run_select(lay.sel_cand, SRC_CAND, ca, none, oc, nt, wsb, wsb + lay.off_sel, stream)) return e;
-    if (int e = launch_pf_verify(rows, lay.nr, lay.cap, cnt, csc, thr, q_pos, N, lay.M, rep_rows, rep_count,
+    if (int e = launch_pf_verify(rows, lay.nr, lay.cap, lay.cand_dense, cnt, csc, thr, q_pos, N, lay.M, rep_rows, rep_count,
                                  (int32_t)rows, status, stream))
         return e;
     // queued rows: the first kRepairRows by the multi-workgroup exact select, any others by one

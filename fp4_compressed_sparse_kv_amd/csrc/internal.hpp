@@ -52,12 +52,20 @@ struct SelPlan {
     size_t lds_bytes = 0;
     size_t data_bytes = 0;          // data region bytes (rows_per_launch rows)
     size_t ws_bytes = 0;            // control region + data region
+    int32_t dense_cap = 0;          // > 0: a source that stores only its valid entries densely holds at
+                                    // most this many per row (LDS sized for them, not for the chunk)
 };
 
 enum SelSource : int { SRC_SCORES = 0, SRC_SCAN = 1, SRC_POOL = 2, SRC_CAND = 3 };
 
 // Plan a selection. `min_chunk` bounds how finely a row may be split.
 int plan_select(int64_t rows, int64_t n, int32_t min_chunk, SelPlan* out);
+// For a one-chunk candidate selection whose keys and positions would not both
+// fit in LDS at the chunk's size: size LDS for the most valid entries that do
+// (p->dense_cap); rows with more valid entries are left to the caller (the
+// select writes nothing for them). Returns the number of valid entries a row
+// may hold.
+int64_t plan_select_dense(SelPlan* p);
 
 struct SelOutput {
     int32_t* idx = nullptr;         // [rows][stride] positions
@@ -156,7 +164,7 @@ int launch_pf_tiles(const PfTiles& t, int k_dtype, bool dense, hipStream_t strea
 int launch_pf_rth(const float* dense, int64_t rows, int32_t n, int32_t R, float* tval, hipStream_t stream);
 int launch_pf_thresholds(const uint16_t* q, int64_t rows, int32_t Q, const float* sel, int32_t R,
                          const float* kmax_partial, float* thr, uint32_t* repair_count, hipStream_t stream);
-int launch_pf_verify(int64_t rows, int32_t nranges, int32_t cap, const uint32_t* cnt, const float* sel,
+int launch_pf_verify(int64_t rows, int32_t nranges, int32_t cap, int64_t dense_cap, const uint32_t* cnt, const float* sel,
                      const float* thr, const int64_t* q_pos, int64_t N, int32_t K, int32_t* repair_rows,
                      uint32_t* repair_count, int32_t repair_cap, uint32_t* status, hipStream_t stream);
 // Exact top-K of the queued queries in queue slots [first, count): one workgroup per query.

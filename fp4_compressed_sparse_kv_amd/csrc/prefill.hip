@@ -26,7 +26,9 @@
 //      score among the candidates is above v, no other position can enter
 //      the top-K or tie with its last member, so the result is the exact
 //      top-K; so it is too when the lists hold every causal position. Queries
-//      that fail both tests, or whose lists overflowed, are queued for the
+//      that fail both tests, whose lists overflowed, or with more candidates
+//      than the select holds (its LDS is sized for the candidates a query
+//      nominates, not for every list slot), are queued for the
 //      exact full-scan select (all of them: the first 64 by the multi-
 //      workgroup select, any further ones by k_pf_repair_rest).
 // Matrix-core tiles: a workgroup of 4 waves owns 128 queries of one sequence
@@ -506,7 +508,8 @@ k_pf_thresholds(const uint16_t* __restrict__ q, int64_t rows, int32_t Q, const f
 // See step 6 above; sel holds the exact scores the select returned ([rows][K],
 // NaN past the selected ones). One wave per query row.
 __global__ void __launch_bounds__(256)
-k_pf_verify(int64_t rows, int32_t nranges, int32_t cap, const uint32_t* __restrict__ cnt, const float* __restrict__ sel,
+k_pf_verify(int64_t rows, int32_t nranges, int32_t cap, int64_t dense_cap, const uint32_t* __restrict__ cnt,
+            const float* __restrict__ sel,
             const float* __restrict__ thr, const int64_t* __restrict__ q_pos, int64_t N, int32_t K,
             int32_t* __restrict__ repair_rows, uint32_t* __restrict__ repair_count, int32_t repair_cap,
             uint32_t* __restrict__ status) {
@@ -536,6 +539,7 @@ k_pf_verify(int64_t rows, int32_t nranges, int32_t cap, const uint32_t* __restri
         total += c;
         overflow = overflow || c > (uint32_t)cap;
     }
+    overflow = overflow || total > dense_cap;  // more candidates than the exact select holds: it left the row alone
     const bool ok = !overflow && (total == valid || (n == (uint32_t)K && sk > thr[2 * r + 1]));
     if (!ok) {
         const uint32_t slot = atomicAdd(repair_count, 1u);
@@ -784,11 +788,11 @@ int launch_pf_thresholds(const uint16_t* q, int64_t rows, int32_t Q, const float
     return e == hipSuccess ? OK : hip_fail(e, "launch k_pf_thresholds");
 }
 
-int launch_pf_verify(int64_t rows, int32_t nranges, int32_t cap, const uint32_t* cnt, const float* sel,
+int launch_pf_verify(int64_t rows, int32_t nranges, int32_t cap, int64_t dense_cap, const uint32_t* cnt, const float* sel,
                      const float* thr, const int64_t* q_pos, int64_t N, int32_t K, int32_t* repair_rows,
                      uint32_t* repair_count, int32_t repair_cap, uint32_t* status, hipStream_t stream) {
     const unsigned blocks = (unsigned)((rows + 3) / 4);
-    hipLaunchKernelGGL(k_pf_verify, dim3(blocks > 0 ? blocks : 1), dim3(256), 0, stream, rows, nranges, cap, cnt, sel,
+    hipLaunchKernelGGL(k_pf_verify, dim3(blocks > 0 ? blocks : 1), dim3(256), 0, stream, rows, nranges, cap, dense_cap, cnt, sel,
                        thr, q_pos, N, K, repair_rows, repair_count, repair_cap, status);
     const hipError_t e = hipGetLastError();
     return e == hipSuccess ? OK : hip_fail(e, "launch k_pf_verify");

@@ -348,6 +348,9 @@ struct SrcCand {
             }
             total += nv[r];
         }
+        // more valid entries than the dense LDS area holds (its size may be below the chunk's):
+        // the row is left alone, every thread returns -1 (total is the same in all of them)
+        if (dense && total > (uint32_t)cpad) return -1;
         {
             const int zfrom = dense ? (int)total : 0;
             const int zto = dense ? (int)((total + kPadTo - 1) / kPadTo * kPadTo) : cpad;
@@ -612,6 +615,7 @@ __global__ void __launch_bounds__(kSelThreads) k_select(Src src, SelDev g, SelTg
     if (tid < 4) sm[204 + tid] = 0u;          // list slot cursors and tie counters of the two targets
     __syncthreads();
     cnt = src.fill(row, begin, cnt, cpad, keys, lh1, posl);   // keys + lh1 (+ positions); ends with a block barrier
+    if (cnt < 0) return;                        // a row over the dense capacity (one chunk per row): left to the caller
     cpad = (cnt + kPadTo - 1) / kPadTo * kPadTo;
 
     // ---- row histogram of the top 11 bits; each chunk also publishes the
@@ -1302,6 +1306,18 @@ int plan_select(int64_t rows, int64_t n, int32_t min_chunk, SelPlan* out) {
     return OK;
 }
 
+int64_t plan_select_dense(SelPlan* p) {
+    DeviceInfo di;
+    if (device_info(&di) != OK || p->S != 1) return p->chunk;
+    if ((size_t)(2 * p->chunk_pad + kLdsFixedWords) * 4 <= di.max_lds) return p->chunk;   // positions fit already
+    int64_t cap = ((int64_t)(di.max_lds / 4) - kLdsFixedWords) / 2;
+    cap = cap / kPadTo * kPadTo;
+    if (cap < kPadTo) return p->chunk;
+    p->dense_cap = (int32_t)cap;
+    p->lds_bytes = (size_t)(2 * cap + kLdsFixedWords) * 4;
+    return cap;
+}
+
 namespace {
 
 template <class Src, bool CAN_FA = false>
@@ -1331,9 +1347,14 @@ int launch_rows(const SelPlan& p, const Src& src, const SelOutput* out, int nt, 
     // Sources whose positions are indirect keep them in LDS next to the keys when both fit.
     DeviceInfo dinfo;
     if (int e = device_info(&dinfo)) return e;
-    const bool pos_lds = Src::kPosLds && (size_t)(2 * p.chunk_pad + kLdsFixedWords) * 4 <= dinfo.max_lds;
-    const int key_words = fa && p.chunk_pad < kFuseLdsWords ? kFuseLdsWords : p.chunk_pad;
-    const size_t lds_bytes = (size_t)(pos_lds ? 2 * p.chunk_pad : key_words) * 4 + (size_t)kLdsFixedWords * 4;
+    // A dense capacity below the chunk (one chunk per row, a source that stores its valid entries
+    // densely) sizes the key and position areas for that many entries.
+    const bool use_dense = Src::kPosLds && p.dense_cap > 0 && p.S == 1 && !fa;
+    const int32_t chunk_pad = use_dense && p.dense_cap < p.chunk_pad ? p.dense_cap : p.chunk_pad;
+    const bool pos_lds = Src::kPosLds && (size_t)(2 * chunk_pad + kLdsFixedWords) * 4 <= dinfo.max_lds;
+    if (chunk_pad < p.chunk_pad && !pos_lds) return fail(INVALID, "select: dense capacity does not fit in LDS");
+    const int key_words = fa && chunk_pad < kFuseLdsWords ? kFuseLdsWords : chunk_pad;
+    const size_t lds_bytes = (size_t)(pos_lds ? 2 * chunk_pad : key_words) * 4 + (size_t)kLdsFixedWords * 4;
     SelTgt t[2];
     for (int j = 0; j < 2; ++j) {
         const SelOutput& o = out[j < nt ? j : 0];
@@ -1343,7 +1364,7 @@ int launch_rows(const SelPlan& p, const Src& src, const SelOutput* out, int nt, 
     g.n = p.n;
     g.S = p.S;
     g.chunk = p.chunk;
-    g.chunk_pad = p.chunk_pad;
+    g.chunk_pad = chunk_pad;
     g.pos_lds = pos_lds ? 1 : 0;
     g.nt = nt;
     g.row_words = p.row_words;

@@ -144,3 +144,60 @@ def test_prefill_plan_two_groups():
     cfg, caches, ocaches, layers, olayers = _prefill_case(modes, B, N, K, P, q_pos, ngroups=2)
     stats = _check_prefill(modes, cfg, ocaches, layers, olayers, q_pos, list(range(q_pos.shape[1])))
     assert stats["exact"] == 2 * B * q_pos.shape[1], stats
+
+
+@pytest.mark.timeout(900)
+def test_prefill_plan_large_pool():
+    """P = 8192 at N = 262,144: the Full layer samples at 1.5 times the pool's share, and the exact
+    candidate select keeps keys and positions in LDS for the candidates a query nominates (fewer than its
+    lists' slots). Pools, Reindex and Reuse layers and attention match the oracle."""
+    modes = ["full", "reindex", "reuse", "reuse"]
+    B, N, K, P = 1, 262144, 2048, 8192
+    q_pos = np.array([[0, 100, 8191, 8192, 20000, 65535, 65536, 131071, 200000, N - 4097, N - 2, N - 1]],
+                     dtype=np.int64)
+    cfg, caches, ocaches, layers, olayers = _prefill_case(modes, B, N, K, P, q_pos)
+    stats = _check_prefill(modes, cfg, ocaches, layers, olayers, q_pos, [0, 2, 3, 5, 8, 10, 11])
+    assert stats["exact"] + stats["excused"] == 7 and stats["excused"] <= 1, stats
+
+
+@pytest.mark.timeout(900)
+def test_prefill_plan_more_candidates_than_the_select_holds():
+    """20,000 positions share the indexer key that scores highest for the Full layer's query, so every
+    query nominates them all: more candidates than the exact candidate select holds (the lists do not
+    overflow). Those queries take the exact repair; the pool is the lowest 8192 tied positions and the
+    top-K the lowest 2048, and every layer matches the oracle."""
+    modes = ["full", "reindex", "reuse", "reuse"]
+    B, N, K, P, Q = 1, 262144, 2048, 8192, 6
+    cfg = synth.small("stack_b4_n1m", B=B, N=N, K=K, P=P, modes=tuple(modes))
+    rng = np.random.default_rng(21)
+    tied = np.sort(rng.choice(N, 20000, replace=False))
+    q0 = synth.q_idx(cfg, 100, 0, Q=1)[0]                       # the Full layer's query, shared by the chunk
+    q0f = (np.ascontiguousarray(q0).astype(np.uint32) << 16).view(np.float32)
+    key = synth.to_e4m3_bytes(np.where(q0f >= 0, 4.0, -4.0).astype(np.float32))
+    kidx = synth.k_idx(cfg, 0)
+    kidx[tied] = key
+    cache = C.KVCache(B, N, k_idx=dev_key(kidx[None], cfg["k_idx_dtype"]))
+    kb, vb = synth.kv_bf16(cfg, 0)
+    cache.fill(dev_bf16(kb), dev_bf16(vb))
+    kc, ks = OQ.quant_fp4(kb)
+    vc, vs = OQ.quant_fp4(vb)
+    oc = dict(k_codes=kc, k_scales=ks, v_codes=vc, v_scales=vs, k_idx=kidx, k_idx_dtype=cfg["k_idx_dtype"])
+    q_pos = np.array([[N - 1, N - 1, N - 2, N - 100, N - 1000, N - 5000]], dtype=np.int64)
+    layers, olayers = [], []
+    for li in range(len(modes)):
+        q = synth.q_bf16(dict(cfg, H=16), 100 + li, 0, Q=Q)[None]
+        qi = synth.q_idx(cfg, 100 + li, 0, Q=Q)[None]
+        if li == 0:
+            qi = np.repeat(q0[None, None], Q, axis=1)
+        layers.append(dict(q=dev_bf16(q), q_idx=dev_key(qi, cfg["q_idx_dtype"]),
+                           out=torch.empty(B, Q, 16, 128, dtype=torch.float32, device="cuda"),
+                           idx_out=torch.empty(B, Q, K, dtype=torch.int32, device="cuda")))
+        olayers.append((q, qi))
+    plan = C.Plan(modes, K=K, P=P)
+    plan.run_prefill(cache, layers, torch.from_numpy(q_pos).cuda())
+    full_idx = host(layers[0]["idx_out"][0])
+    for i in range(Q):
+        causal_tied = tied[tied <= q_pos[0, i]]
+        assert np.array_equal(full_idx[i], causal_tied[:K]), i
+    stats = _check_prefill(modes, cfg, [[oc]], layers, olayers, q_pos, list(range(Q)))
+    assert stats["exact"] == Q, stats
