@@ -209,7 +209,7 @@ k_sparse_attn(const uint16_t* __restrict__ q, int32_t rows_per_seq, int32_t H, c
         *reinterpret_cast<f32x4*>(dst + 4) = f32x4{st.acc[4][i], st.acc[5][i], st.acc[6][i], st.acc[7][i]};
     }
     if (g == 0) {
-        lds.mg.m[wave][n] = st.m;
+        lds.mg.m[wave][n] = st.m * sl2;         // scaled log2 units
         lds.mg.l[wave][n] = st.l;
         if (wave == 0) lds.mg.f[n] = st.f;
     }

@@ -169,10 +169,58 @@ __device__ __forceinline__ void gather(BlockRaw& r, const BlockPos& bp, int blk,
 }
 
 struct WaveState {
-    float m, l;                                 // head n (same in the 4 lane groups), scaled log2 units
+    float m;                                    // head n (same in the 4 lane groups): running maximum score,
+                                                // in the units of q * 2^-e (times scale * log2(e): scaled log2 units)
+    float l;                                    // running sum of the weights
     float f;                                    // head n: 2^e, scaled log2 units -> log2 units
     f32x4 acc[8];                               // acc[t][i] = unnormalized out[n][8*(4g+i) + t]
 };
+
+// Online softmax of one block of 32 positions for head n: lanes n, 16 + n,
+// 32 + n and 48 + n hold its scores s (units of q * 2^-e) at positions
+// 4g + i (i < 4) and 16 + 4g + i - 4 (i >= 4). Weights p = 2^((s - m) * c)
+// with c = scale * log2(e) * 2^e (a product with a power of two: exact); the
+// difference is formed before the product, so neither huge nor tiny queries
+// overflow. vmask bit p: position p is real (all set: nothing to mask). Sets
+// p, their sum over the head's 32 positions, and rescales the running state.
+__device__ __forceinline__ void block_softmax(WaveState& st, const f32x4 (&sacc)[2], uint32_t vmask, float sl2, int g,
+                                              float (&p)[8], float& psum) {
+    float sc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) sc[i] = (i < 4) ? sacc[0][i] : sacc[1][i - 4];
+    if (vmask != 0xFFFFFFFFu) {                 // the same in every lane: a block with padding
+        const uint32_t mlo = vmask >> (4 * g), mhi = vmask >> (16 + 4 * g);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t bit = (i < 4) ? (mlo >> i) & 1u : (mhi >> (i - 4)) & 1u;
+            sc[i] = bit ? sc[i] : -INFINITY;
+        }
+    }
+    float mx = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])), fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
+    mx = rows_max(mx);
+    const float c = sl2 * st.f;
+    const float m_old = st.m;
+    const float m_new = fmaxf(m_old, mx);
+    // the hardware exp2 flushes results below 2^-126 to zero, far below what
+    // can matter against the maximum weight 1
+    const float mref = m_new == -INFINITY ? 0.f : m_new;
+    psum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        p[i] = __builtin_amdgcn_exp2f((sc[i] - mref) * c);
+        psum += p[i];
+    }
+    psum = rows_sum(psum);
+    const float alpha = m_old == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m_old - mref) * c);
+    st.l = st.l * alpha + psum;
+    st.m = m_new;
+    // the running sums need rescaling only where the maximum grew after the
+    // first block (before it they are zero)
+    if (__builtin_amdgcn_ballot_w64(m_old != -INFINITY && alpha != 1.f) != 0) {
+#pragma unroll
+        for (int t = 0; t < 8; ++t) st.acc[t] = st.acc[t] * alpha;
+    }
+}
 
 // Two E4M3 bytes (bits 0..15 of w) -> two f16, exactly (the hardware decode
 // to fp32 is exact and every E4M3 value is an f16 value).
@@ -224,27 +272,8 @@ __device__ __forceinline__ void attend_block(WaveState& st, const BlockRaw& r, S
     }
 
     // ---- online softmax for head n over the 8 positions this lane holds
-    const uint32_t mlo = vmask >> (4 * g), mhi = vmask >> (16 + 4 * g);
-    float lg[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const float sv = (i < 4) ? sacc[0][i] : sacc[1][i - 4];
-        const uint32_t bit = (i < 4) ? (mlo >> i) & 1u : (mhi >> (i - 4)) & 1u;
-        lg[i] = bit ? sv * sl2 : -INFINITY;
-    }
-    float mx = fmaxf(fmaxf(fmaxf(lg[0], lg[1]), fmaxf(lg[2], lg[3])), fmaxf(fmaxf(lg[4], lg[5]), fmaxf(lg[6], lg[7])));
-    mx = rows_max(mx);
-    const float m_old = st.m;
-    const float m_new = fmaxf(m_old, mx);
-    // weights 2^((lg - m_new) * 2^e): the hardware exp2 flushes results below
-    // 2^-126 to zero, far below what can matter against the maximum weight 1
-    const float mref = m_new == -INFINITY ? 0.f : m_new;
-    float p[8], psum = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        p[i] = __builtin_amdgcn_exp2f((lg[i] - mref) * st.f);
-        psum += p[i];
-    }
+    float p[8], psum;
+    block_softmax(st, sacc, vmask, sl2, g, p, psum);
     uint32_t ph[4], pl[4];                      // p = hi + lo: f16 (~22 bits) or bf16 (16 bits) pairs
 #pragma unroll
     for (int i = 0; i < 8; i += 2) {
@@ -262,16 +291,6 @@ __device__ __forceinline__ void attend_block(WaveState& st, const BlockRaw& r, S
     }
     const OpT pb_hi = __builtin_bit_cast(OpT, make_uint4(ph[0], ph[1], ph[2], ph[3]));
     const OpT pb_lo = __builtin_bit_cast(OpT, make_uint4(pl[0], pl[1], pl[2], pl[3]));
-    psum = rows_sum(psum);
-    const float alpha = m_old == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m_old - mref) * st.f);
-    st.l = st.l * alpha + psum;
-    st.m = m_new;
-    // the running sums need rescaling only where the maximum grew after the
-    // first block (before it they are zero)
-    if (__builtin_amdgcn_ballot_w64(m_old != -INFINITY && alpha != 1.f) != 0) {
-#pragma unroll
-        for (int t = 0; t < 8; ++t) st.acc[t] = st.acc[t] * alpha;
-    }
 
     // ---- out^T += V_hat^T P^T: MFMA t covers channels 8m + t; its operand
     // element i is channel 8n + t of position column i. Codes of columns
@@ -351,25 +370,8 @@ __device__ __forceinline__ void attend_window_block(WaveState& st, const uint16_
 #pragma unroll
         for (int s = 0; s < 4; ++s) sacc[mb] = mfma16(__builtin_bit_cast(bf16x8, kq[mb][s]), qw[s], sacc[mb]);
 
-    const uint32_t mlo = vmask >> (4 * g), mhi = vmask >> (16 + 4 * g);
-    float lg[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const float sv = (i < 4) ? sacc[0][i] : sacc[1][i - 4];
-        const uint32_t bit = (i < 4) ? (mlo >> i) & 1u : (mhi >> (i - 4)) & 1u;
-        lg[i] = bit ? sv * sl2 : -INFINITY;
-    }
-    float mx = fmaxf(fmaxf(fmaxf(lg[0], lg[1]), fmaxf(lg[2], lg[3])), fmaxf(fmaxf(lg[4], lg[5]), fmaxf(lg[6], lg[7])));
-    mx = rows_max(mx);
-    const float m_old = st.m;
-    const float m_new = fmaxf(m_old, mx);
-    const float mref = m_new == -INFINITY ? 0.f : m_new;
-    float p[8], psum = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        p[i] = __builtin_amdgcn_exp2f((lg[i] - mref) * st.f);
-        psum += p[i];
-    }
+    float p[8], psum;
+    block_softmax(st, sacc, vmask, sl2, g, p, psum);
     uint32_t ph[4], pl[4];                      // p = hi + lo as bf16 pairs (16 bits)
 #pragma unroll
     for (int i = 0; i < 8; i += 2) {
@@ -380,14 +382,6 @@ __device__ __forceinline__ void attend_window_block(WaveState& st, const uint16_
     }
     const bf16x8 pb_hi = __builtin_bit_cast(bf16x8, make_uint4(ph[0], ph[1], ph[2], ph[3]));
     const bf16x8 pb_lo = __builtin_bit_cast(bf16x8, make_uint4(pl[0], pl[1], pl[2], pl[3]));
-    psum = rows_sum(psum);
-    const float alpha = m_old == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m_old - mref) * st.f);
-    st.l = st.l * alpha + psum;
-    st.m = m_new;
-    if (__builtin_amdgcn_ballot_w64(m_old != -INFINITY && alpha != 1.f) != 0) {
-#pragma unroll
-        for (int t = 0; t < 8; ++t) st.acc[t] = st.acc[t] * alpha;
-    }
 
     // V: channels 8n..8n+7 (16 bytes) of each of this lane's 8 position columns
     uint4 vr[8];
@@ -532,7 +526,7 @@ __device__ __forceinline__ void fused_attn_partial(const AttnFuse& af, int64_t r
             *reinterpret_cast<f32x4*>(dst + 4) = f32x4{st.acc[4][i], st.acc[5][i], st.acc[6][i], st.acc[7][i]};
         }
         if (g == 0) {
-            lds.mg.m[wave][nn] = st.m;
+            lds.mg.m[wave][nn] = st.m * sl2;    // scaled log2 units
             lds.mg.l[wave][nn] = st.l;
             if (wave == 0) lds.mg.f[nn] = st.f;
         }
