@@ -52,6 +52,7 @@ struct SelPlan {
     size_t lds_bytes = 0;
     size_t data_bytes = 0;          // data region bytes (rows_per_launch rows)
     size_t ws_bytes = 0;            // control region + data region
+    int32_t skew = 0;               // even chunks take chunk + skew entries, odd ones chunk - skew
     int32_t dense_cap = 0;          // > 0: a source that stores only its valid entries densely holds at
                                     // most this many per row (LDS sized for them, not for the chunk)
 };

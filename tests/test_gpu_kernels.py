@@ -229,7 +229,9 @@ def _scores_with_ties(rng, rows, n, kind):
     (32, 70001, 2048, "inf"), (16, 262144, 100, "equal"), (20, 100000, 3000, "ties"),
     # 16K..32K keys in the threshold's top-digit bin: the row list is resolved in two batches
     (2, 300000, 8192, "bin20k"), (1, 1000000, 2048, "bin30k"), (3, 262144, 8192, "bin24kt"),
-    (1, 300000, 8192, "bin40k")])   # more than the list holds: the radix path
+    (1, 300000, 8192, "bin40k"),    # more than the list holds: the radix path
+    # rows of 16 or more chunks (a multiple of 8): even chunks take more entries than odd ones
+    (4, 1043576, 2048, "normal"), (16, 262144, 2048, "ties"), (4, 1048576, 8192, "bin20k")])
 def test_topk_matches_oracle(rows, n, K, kind):
     rng = np.random.default_rng(rows * 1000 + n + K)
     s = _scores_with_ties(rng, rows, n, kind)
