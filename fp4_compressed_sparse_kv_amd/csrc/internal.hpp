@@ -65,7 +65,7 @@ int plan_select(int64_t rows, int64_t n, int32_t min_chunk, SelPlan* out);
 // fit in LDS at the chunk's size: size LDS for the most valid entries that do
 // (p->dense_cap); rows with more valid entries are left to the caller (the
 // select writes nothing for them). Returns the number of valid entries a row
-// may hold.
+// may hold: all n of them unless a dense capacity is set.
 int64_t plan_select_dense(SelPlan* p);
 
 struct SelOutput {

@@ -1320,8 +1320,9 @@ int plan_select(int64_t rows, int64_t n, int32_t min_chunk, SelPlan* out) {
 
 int64_t plan_select_dense(SelPlan* p) {
     DeviceInfo di;
-    if (device_info(&di) != OK || p->S != 1) return p->chunk;
-    if ((size_t)(2 * p->chunk_pad + kLdsFixedWords) * 4 <= di.max_lds) return p->chunk;   // positions fit already
+    // several chunks per row, or keys and positions that fit for the whole chunk: a row holds all n
+    if (device_info(&di) != OK || p->S != 1) return p->n;
+    if ((size_t)(2 * p->chunk_pad + kLdsFixedWords) * 4 <= di.max_lds) return p->n;
     int64_t cap = ((int64_t)(di.max_lds / 4) - kLdsFixedWords) / 2;
     cap = cap / kPadTo * kPadTo;
     if (cap < kPadTo) return p->chunk;

@@ -148,26 +148,30 @@ def test_prefill_plan_two_groups():
 
 @pytest.mark.timeout(900)
 def test_prefill_plan_large_pool():
-    """P = 8192 at N = 262,144: the Full layer samples at 1.5 times the pool's share, and the exact
-    candidate select keeps keys and positions in LDS for the candidates a query nominates (fewer than its
-    lists' slots). Pools, Reindex and Reuse layers and attention match the oracle."""
+    """P = 8192 at N = 262,144 with 256 queries: the Full layer samples at 1.5 times the pool's share, and
+    the exact candidate select (one workgroup per query at this many queries) keeps keys and positions in
+    LDS for the candidates a query nominates, fewer than its lists' slots. Pools, Reindex and Reuse layers
+    and attention match the oracle."""
     modes = ["full", "reindex", "reuse", "reuse"]
-    B, N, K, P = 1, 262144, 2048, 8192
-    q_pos = np.array([[0, 100, 8191, 8192, 20000, 65535, 65536, 131071, 200000, N - 4097, N - 2, N - 1]],
-                     dtype=np.int64)
+    B, N, K, P, Q = 1, 262144, 2048, 8192, 256
+    rng = np.random.default_rng(31)
+    q_pos = np.sort(np.concatenate([[0, 100, 8191, 8192, 20000, 65535, 65536, 131071, N - 4097, N - 2, N - 1],
+                                    rng.integers(0, N, Q - 11)]))[None].astype(np.int64)
     cfg, caches, ocaches, layers, olayers = _prefill_case(modes, B, N, K, P, q_pos)
-    stats = _check_prefill(modes, cfg, ocaches, layers, olayers, q_pos, [0, 2, 3, 5, 8, 10, 11])
-    assert stats["exact"] + stats["excused"] == 7 and stats["excused"] <= 1, stats
+    check = [0, 2, 3, 5, 60, 130, 200, 250, 254, 255]
+    stats = _check_prefill(modes, cfg, ocaches, layers, olayers, q_pos, check)
+    assert stats["exact"] + stats["excused"] == len(check) and stats["excused"] <= 1, stats
 
 
 @pytest.mark.timeout(900)
 def test_prefill_plan_more_candidates_than_the_select_holds():
-    """20,000 positions share the indexer key that scores highest for the Full layer's query, so every
-    query nominates them all: more candidates than the exact candidate select holds (the lists do not
-    overflow). Those queries take the exact repair; the pool is the lowest 8192 tied positions and the
-    top-K the lowest 2048, and every layer matches the oracle."""
+    """20,000 positions share the indexer key that scores highest for the Full layer's query, so every one
+    of 256 queries nominates them all: more candidates than the exact candidate select holds (one
+    workgroup per query, its LDS sized below the lists' slots; the lists do not overflow). Those queries
+    take the exact repair (64 by the multi-workgroup select, the rest one workgroup each); the pool is the
+    lowest 8192 tied positions and the top-K the lowest 2048, and every layer matches the oracle."""
     modes = ["full", "reindex", "reuse", "reuse"]
-    B, N, K, P, Q = 1, 262144, 2048, 8192, 6
+    B, N, K, P, Q = 1, 262144, 2048, 8192, 256
     cfg = synth.small("stack_b4_n1m", B=B, N=N, K=K, P=P, modes=tuple(modes))
     rng = np.random.default_rng(21)
     tied = np.sort(rng.choice(N, 20000, replace=False))
@@ -182,7 +186,7 @@ def test_prefill_plan_more_candidates_than_the_select_holds():
     kc, ks = OQ.quant_fp4(kb)
     vc, vs = OQ.quant_fp4(vb)
     oc = dict(k_codes=kc, k_scales=ks, v_codes=vc, v_scales=vs, k_idx=kidx, k_idx_dtype=cfg["k_idx_dtype"])
-    q_pos = np.array([[N - 1, N - 1, N - 2, N - 100, N - 1000, N - 5000]], dtype=np.int64)
+    q_pos = (N - 1 - 20 * np.arange(Q))[None].astype(np.int64)
     layers, olayers = [], []
     for li in range(len(modes)):
         q = synth.q_bf16(dict(cfg, H=16), 100 + li, 0, Q=Q)[None]
@@ -199,5 +203,6 @@ def test_prefill_plan_more_candidates_than_the_select_holds():
     for i in range(Q):
         causal_tied = tied[tied <= q_pos[0, i]]
         assert np.array_equal(full_idx[i], causal_tied[:K]), i
-    stats = _check_prefill(modes, cfg, [[oc]], layers, olayers, q_pos, list(range(Q)))
-    assert stats["exact"] == Q, stats
+    check = [0, 1, 63, 64, 65, 200, 255]
+    stats = _check_prefill(modes, cfg, [[oc]], layers, olayers, q_pos, check)
+    assert stats["exact"] == len(check), stats
