@@ -451,7 +451,9 @@ int csa2_plan_profile_read(csa2_plan* plan, float* avg_ms, int32_t* runs);
  * With bf16 indexer queries, E4M3 or bf16 keys, d_idx = 64 and long contexts
  * the indexer runs on the matrix cores and only nominates candidates; their
  * exact scores decide the top-K. A query whose result the candidates cannot
- * certify (ties or near-ties at its threshold, an overflowing candidate list)
+ * certify (ties or near-ties at its threshold, an overflowing candidate list,
+ * more candidates than the exact select holds: 16,640 per query when its
+ * lists have more slots than LDS holds keys and positions for)
  * is re-selected by an exact scan of its whole causal range: every such
  * query, however many (beyond 64 per call this fallback is slow: one
  * workgroup per query). The result is always the exact top-K.
