@@ -109,10 +109,10 @@ def test_prefill_full_size_sampled():
 @pytest.mark.timeout(900)
 def test_quant_dequant_full_size_sampled():
     """kv_quant_fp4 and kv_dequant_fp4 over the whole 1,048,576 x 512 quantize workload in the benchmark's
-    launch configuration, compared bit for bit with the oracle on row blocks chosen so that every
-    grid-stride slot of both kernels is checked in its first and last pass: the quantizer's grid of
-    16,384 x 256 lanes takes two 16-group slots per pass (131,072 rows each) over four passes, the
-    dequantizer four half-group slots (65,536 rows each) over four passes."""
+    launch configuration, compared bit for bit with the oracle on row blocks at the start, the end and
+    between: each of the 16,384 workgroups of both kernels owns 64 consecutive rows (2048 groups or
+    4096 half-groups, four passes of 256 lanes), so every block spans the ranges of several workgroups,
+    the first and the last included."""
     cfg = dict(synth.WORKLOADS["quant_1m_x512"])
     T, Cc, rb = cfg["T"], cfg["C"], cfg["row_block"]
     dev = torch.device("cuda", 0)
@@ -120,15 +120,8 @@ def test_quant_dequant_full_size_sampled():
     codes, scales = C.kv_quant_fp4(x)
     y = C.kv_dequant_fp4(codes, scales, Cc)
     torch.cuda.synchronize()
-    q_slot, dq_slot = 131072, 65536
-    rows = set()
-    for p in (0, 3):                                        # first and last pass
-        for k in range(2):
-            rows |= {(2 * p + k) * q_slot, (2 * p + k + 1) * q_slot - 1}
-        for k in range(4):
-            rows |= {(4 * p + k) * dq_slot, (4 * p + k + 1) * dq_slot - 1}
-    blocks = sorted({r // rb for r in rows if r < T})
-    assert blocks[0] == 0 and blocks[-1] == T // rb - 1
+    nb = T // rb
+    blocks = sorted({0, 1, nb // 4, nb // 2, nb // 2 + 1, 3 * nb // 4, nb - 2, nb - 1})
     for blk in blocks:
         xb = synth.quant_rows(cfg, blk)
         rc, rs = OQ.quant_fp4(xb)
