@@ -473,12 +473,41 @@ k_pf_rth(const float* __restrict__ dense, int32_t n, int32_t R, float* __restric
 
 // One thread per query row: t = R-th largest sample score (the minimum of the
 // select's R outputs; -inf if fewer than R samples are causal), the margin
-// from the query and the per-channel key maxima, lo and v.
-__global__ void __launch_bounds__(256)
+// from the query and the per-channel key maxima, lo and v. The key maxima of
+// the (at most two) sequences a workgroup's rows belong to are reduced from
+// the partials once per workgroup, in LDS; with fewer than 256 queries per
+// sequence each thread reduces its own.
+constexpr int kThrThreads = 256;
+
+__global__ void __launch_bounds__(kThrThreads)
 k_pf_thresholds(const uint16_t* __restrict__ q, int64_t rows, int32_t Q, const float* __restrict__ sel, int32_t R,
                 const float* __restrict__ kmax_partial, float* __restrict__ thr, uint32_t* __restrict__ repair_count) {
-    const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    __shared__ float part[kThrThreads / kPfDim][kPfDim];
+    __shared__ float skm[2][kPfDim];
+    const int tid = threadIdx.x;
+    const int64_t r0 = (int64_t)blockIdx.x * kThrThreads;
+    const int64_t r = r0 + tid;
     if (r == 0) *repair_count = 0u;
+    const int64_t seq0 = r0 / Q;
+    const int64_t nseq = r0 < rows ? (min(rows, r0 + kThrThreads) - 1) / Q - seq0 + 1 : 0;
+    const bool shared_km = nseq >= 1 && nseq <= 2;      // the same in every thread
+    if (shared_km) {
+        const int c = tid % kPfDim, gq = tid / kPfDim;
+        for (int sq = 0; sq < nseq; ++sq) {
+            const float* kp = kmax_partial + (size_t)(seq0 + sq) * kKmaxBlocks * kPfDim;
+            float m = 0.f;
+            for (int b = gq; b < kKmaxBlocks; b += kThrThreads / kPfDim) m = fmaxf(m, kp[b * kPfDim + c]);
+            part[gq][c] = m;
+            __syncthreads();
+            if (tid < kPfDim) {
+                float km = 0.f;
+#pragma unroll
+                for (int u = 0; u < kThrThreads / kPfDim; ++u) km = fmaxf(km, part[u][tid]);
+                skm[sq][tid] = km;
+            }
+            __syncthreads();
+        }
+    }
     if (r >= rows) return;
     const int64_t seq = r / Q;
     float t = INFINITY;
@@ -492,11 +521,25 @@ k_pf_thresholds(const uint16_t* __restrict__ q, int64_t rows, int32_t Q, const f
     }
     if (n < R) t = -INFINITY;
     const float* kp = kmax_partial + (size_t)seq * kKmaxBlocks * kPfDim;
+    const uint4* qr = reinterpret_cast<const uint4*>(q + r * kPfDim);
     double s = 0.0;
-    for (int i = 0; i < kPfDim; ++i) {
-        float km = 0.f;
-        for (int b = 0; b < kKmaxBlocks; ++b) km = fmaxf(km, kp[b * kPfDim + i]);
-        s += fabs((double)bf16_bits_to_f32(q[r * kPfDim + i])) * (double)km;
+#pragma unroll
+    for (int v = 0; v < kPfDim / 8; ++v) {
+        const uint4 w = qr[v];
+        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int h = 0; h < 8; ++h) {
+            const int i = 8 * v + h;
+            float km;
+            if (shared_km) {
+                km = skm[seq - seq0][i];
+            } else {
+                km = 0.f;
+                for (int b = 0; b < kKmaxBlocks; ++b) km = fmaxf(km, kp[b * kPfDim + i]);
+            }
+            const uint32_t bits = (h & 1) ? (ws[h >> 1] >> 16) : (ws[h >> 1] & 0xFFFFu);
+            s += fabs((double)bf16_bits_to_f32(bits)) * (double)km;
+        }
     }
     const double e = s * 0x1p-14 + 0x1p-120;
     thr[2 * r + 0] = t == -INFINITY ? -INFINITY : (float)((double)t - e);
