@@ -1,6 +1,8 @@
 """GPU parity at the full sizes of the decode and prefill workloads, in the launch
 configuration the benchmark times (the same input builder and the same plan
-calls), on sampled sequences and queries that the oracle computes one by one.
+calls), on sampled sequences and queries that the oracle computes one by one; the
+decode index sets (Full top-K and pool, Reindex top-K) of every sequence of the
+batch, which need only the indexer keys, are checked too.
 
 Top-K position sets must match bit for bit; a mismatch is excused (and counted)
 only for near-ties at the K-th score. Attention is compared stage-wise, on the
@@ -40,6 +42,40 @@ def _plan(cfg, modes):
                   q_idx_dtype=cfg["q_idx_dtype"], k_idx_dtype=cfg["k_idx_dtype"])
 
 
+def _check_index_sets_every_sequence(cfg, modes, layers):
+    """Every sequence of the batch, not only the sampled ones: the Full layer's top-K (and pool) and the
+    Reindex layer's top-K against the oracle's exact selection from the indexer scores alone (these need
+    no KV rows, so the whole batch stays cheap). Stage-wise: the Reindex reference scores the GPU's own
+    pool. Returns the counts of exact and excused sets."""
+    K, P = cfg["K"], cfg.get("P")
+    stats = {"exact": 0, "excused": 0}
+    for b in range(cfg["B"]):
+        kidx = synth.k_idx(cfg, b)
+        pool = None
+        for li, mode in enumerate(modes):
+            if mode == "reuse":
+                continue
+            qi = synth.q_idx(cfg, li, b)[0]
+            g_idx = host(layers[li]["idx_out"][b])
+            if mode == "full":
+                s = OS.index_scores(qi, cfg["q_idx_dtype"], kidx, cfg["k_idx_dtype"])
+                r_idx, _ = o_topk(s, K)
+                stats[compare_topk(g_idx, r_idx, lambda p: s[p], K)] += 1
+                if "pool_out" in layers[li]:
+                    pool = host(layers[li]["pool_out"][b])
+                    r_pool, _ = o_topk(s, P)
+                    stats[compare_topk(pool, r_pool, lambda p: s[p], P)] += 1
+                    # the pool holds the layer's own top-K
+                    assert np.isin(g_idx, pool).all(), (b, li)
+            else:
+                sp = OS.pool_scores(qi, cfg["q_idx_dtype"], kidx, cfg["k_idx_dtype"], pool)
+                r_idx, _ = o_topk(sp, K, positions=pool)
+                at = dict(zip(pool.tolist(), sp.tolist()))
+                stats[compare_topk(g_idx, r_idx, lambda p: at[int(p)], K)] += 1
+                assert np.isin(g_idx, pool).all(), (b, li)
+    return stats
+
+
 @pytest.mark.timeout(1500)
 @pytest.mark.parametrize("workload,seqs", [("full_b64_n131072", (0, 21, 42, 63)),
                                            ("stack_b32_n262144", (0, 9, 18, 31)),
@@ -52,6 +88,9 @@ def test_decode_step_full_size_sampled(workload, seqs):
     plan = _plan(cfg, cfg["modes"])
     plan.run_decode(cache, layers)
     torch.cuda.synchronize()
+    for li in range(len(modes)):
+        assert torch.isfinite(layers[li]["out"]).all(), (workload, li)
+    print(f"{workload}: top-K sets of every sequence {_check_index_sets_every_sequence(cfg, modes, layers)}")
     K, P = cfg["K"], cfg.get("P")
     stats = {"exact": 0, "excused": 0}
     for b in seqs:
