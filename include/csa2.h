@@ -192,8 +192,13 @@ int csa2_kv_project(const uint16_t* h, int64_t T, int32_t D, int64_t h_stride,
  * the retrieval keys are shared across layers).
  *
  * Score (R: the pages give no formula) = the exact dot product q . k rounded
- * once to fp32 (nearest-even); the kernel accumulates exact products in fp64,
- * which is exact whenever the terms share a 2^53-wide window. With q_pos
+ * once to fp32 (nearest-even). A bf16 query against E4M3 keys accumulates its
+ * exact products with fp64 FMAs (exact while the query's nonzero elements span
+ * at most 2^21 in magnitude); every other dtype pair accumulates a double-double
+ * sum, exact while the query's and key's exponents together span less than
+ * about 46 binades, rounded once to fp32. A key with an E4M3 NaN byte scores
+ * NaN; infinite fp32 / bf16 operands give NaN or an infinity (not specified:
+ * the error-free sums turn inf - inf into NaN). With q_pos
  * given, positions t > q_pos[b*Q + i] score -inf (causal prefill).
  *
  *   q_idx    device [B][Q][d_idx] of q_dtype (CSA2_F32 or CSA2_BF16)

@@ -21,6 +21,10 @@ Computation here:
      multiple of u below 2^53 * u, hence representable, so no addition rounds;
   4. keys without that certificate are summed as exact rationals
      (fractions.Fraction) and rounded to fp32 by hand.
+Non-finite inputs (NaN keys, or infinities in fp32 / bf16 operands) follow
+IEEE-754 addition: a score is NaN when any product is NaN or products of
+both signs are infinite, otherwise the infinity; the fp64 sum of such a row
+gives exactly that, whatever the order.
 """
 
 from fractions import Fraction
@@ -81,9 +85,12 @@ def exact_dot_f32(q64, k64):
     n = k64.shape[0]
     out = np.empty(n, dtype=np.float32)
     for s in range(0, n, _CHUNK):
-        prods = k64[s:s + _CHUNK] * q64[None, :]
-        sums = prods.sum(axis=1)
-        ok = _certified_exact(prods)
+        with np.errstate(invalid="ignore"):     # inf - inf and inf * 0 are NaN by intent
+            prods = k64[s:s + _CHUNK] * q64[None, :]
+            sums = prods.sum(axis=1)
+        finite = np.isfinite(prods).all(axis=1)
+        # a row with a non-finite product keeps its fp64 sum (IEEE: NaN or the infinity)
+        ok = ~finite | _certified_exact(np.where(finite[:, None], prods, 0.0))
         out[s:s + _CHUNK] = sums.astype(np.float32)
         for i in np.nonzero(~ok)[0]:
             total = sum((Fraction(float(p)) for p in prods[i]), Fraction(0))

@@ -75,3 +75,26 @@ def test_causal_mask_and_pool_scores():
     ps = S.pool_scores(q, "f32", k, "f32", pool)
     full = S.index_scores(q, "f32", k, "f32")
     assert ps[:3].tolist() == full[[3, 7, 50]].tolist() and np.isneginf(ps[3])
+
+
+def test_non_finite_keys_follow_ieee_addition():
+    """IEEE-754 addition on non-finite terms: one NaN product makes the score NaN; infinite products of
+    one sign give that infinity; of both signs, NaN. The finite rows of the same call are unaffected."""
+    rng = np.random.default_rng(9)
+    q = rng.uniform(0.5, 1.0, 64).astype(np.float32)                # positive: products keep the keys' signs
+    k = rng.standard_normal((6, 64)).astype(np.float32)
+    k[1, 7] = np.nan                                                 # one NaN among finite terms
+    k[2, 3] = np.inf                                                 # +inf among finite terms
+    k[3, 3], k[3, 9] = np.inf, -np.inf                               # both infinities
+    k[4, :] = np.nan                                                 # a whole NaN row
+    k[5, 0] = -np.inf
+    s = S.index_scores(q, "f32", k, "f32")
+    assert np.isnan(s[1]) and np.isnan(s[3]) and np.isnan(s[4])
+    assert s[2] == np.inf and s[5] == -np.inf
+    assert s[0] == S.index_scores(q, "f32", k[:1], "f32")[0]
+    # an E4M3 NaN byte (0x7F) in one channel of a key
+    kb = to_e4m3_bytes(rng.standard_normal((3, 64)).astype(np.float32))
+    kb[1, 10] = 0x7F
+    qb = to_bf16_bits(rng.standard_normal(64).astype(np.float32))
+    sb = S.index_scores(qb, "bf16", kb, "e4m3")
+    assert np.isfinite(sb[0]) and np.isnan(sb[1]) and np.isfinite(sb[2])
