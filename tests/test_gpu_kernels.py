@@ -144,6 +144,23 @@ def test_index_full_scores(qd, kd, d):
             assert np.array_equal(got[b, i].view(np.uint32), ref.view(np.uint32)), (b, i)
 
 
+def test_index_full_scores_with_one_nan_channel():
+    """Keys with an E4M3 NaN byte (0x7F or 0xFF) in one channel among finite ones score NaN, as IEEE
+    addition gives; every other key keeps its bit-exact score."""
+    cfg = synth.small("full_b64_n131072", N=1000, d_idx=64)
+    rng = np.random.default_rng(13)
+    q = synth.q_idx(cfg, 0, 0, Q=2)
+    k = synth.k_idx(cfg, 0).copy()
+    rows = rng.choice(1000, size=37, replace=False)
+    k[rows, rng.integers(0, 64, 37)] = rng.choice(np.array([0x7F, 0xFF], dtype=np.uint8), 37)
+    got = host(C.index_full(dev_key(q[None], "bf16"), dev_key(k[None], "e4m3")))[0]
+    for i in range(2):
+        ref = OS.index_scores(q[i], "bf16", k, "e4m3")
+        nan = np.isnan(ref)
+        assert nan.sum() == 37 and np.array_equal(np.isnan(got[i]), nan), i
+        assert np.array_equal(got[i][~nan].view(np.uint32), ref[~nan].view(np.uint32)), i
+
+
 def _near_midpoint_f32_keys(q, n, rng, mode):
     """fp32 keys whose exact dot product with q sits on, or a hair off, a rounding midpoint between two
     fp32 values (built with exact rationals): a plain fp64 sum of 48-bit products rounds these wrongly."""
