@@ -761,8 +761,10 @@ def main():
         "cold_ms_per_step": round(sorted(cold)[len(cold) // 2], 5) if cold else None,
         "cold_ms_p10_p90": [round(float(np.percentile(cold, 10)), 5), round(float(np.percentile(cold, 90)), 5)] if cold else None,
         "achievable_copy_gbs": round(copy_gbs, 1),
+        # per-kernel slots: 2l is layer l's select launch, 2l + 1 its attention launch (empty when fused)
         "kernel_ms": {"full_select": round(sel_ms, 5),
-                      **{f"slot{i}": round(v, 5) for i, v in enumerate(slot_ms) if i > 0 and v > 0}},
+                      **{f"L{i // 2}_{cfg['modes'][i // 2]}_{'attn' if i % 2 else 'select'}": round(v, 5)
+                         for i, v in enumerate(slot_ms) if i > 0 and v > 0 and i // 2 < len(cfg["modes"])}},
         "roofline": {"bound": "hbm", "kernel": "k_select<SrcScan> (Full layer: scan + pool/top-K select" +
                                (" + attention)" if full_fused else ")"),
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
