@@ -119,7 +119,8 @@ def test_decode_step_full_size_sampled(workload, seqs):
 @pytest.mark.timeout(1500)
 def test_prefill_full_size_sampled():
     """The 4 x 1M-context prefill chunk (4096 queries per sequence at the last positions) through the
-    matrix-core indexer path; sampled queries against the oracle's exact causal top-K and attention."""
+    matrix-core indexer path; 59 sampled queries (both ends of the chunk and 12 seeded random ones per
+    sequence) against the oracle's exact causal top-K and attention."""
     cfg = dict(synth.WORKLOADS["stack_b4_n1m"])
     B, N, Q, K = cfg["B"], cfg["N"], cfg["prefill_Q"], cfg["K"]
     dev = torch.device("cuda", 0)
@@ -134,7 +135,11 @@ def test_prefill_full_size_sampled():
     assert plan.prefill_status(cache, Q) == 0
     idx, out = host(idx), host(out)
     stats = {"exact": 0, "excused": 0}
-    for b, queries in ((0, (0, 1000, 2049, 4095)), (1, (7, 3333)), (2, (512, 4094)), (3, (1, 2222, 4095))):
+    fixed = {0: (0, 1000, 2049, 4095), 1: (7, 3333), 2: (512, 4094), 3: (1, 2222, 4095)}
+    for b in range(B):
+        # the fixed queries (both ends of the chunk) plus 12 seeded random ones per sequence
+        extra = np.random.default_rng([7, b]).choice(Q, 12, replace=False)
+        queries = sorted(set(fixed[b]) | set(int(i) for i in extra))
         oc = _oracle_sequence(cfg, b)
         for i in queries:
             s = OS.index_scores(qi[b, i], cfg["q_idx_dtype"], oc["k_idx"], cfg["k_idx_dtype"], q_pos=int(q_pos[b, i]))
